@@ -1,0 +1,211 @@
+"""Seeded synthetic inputs shaped like audio-LLM prefill KV caches.
+
+This module holds input generation only -- none of the compression method's
+arithmetic -- and is the single source of inputs for both the HIP path and
+the CPU oracle, so both sides read identical bit patterns.
+
+The pages measure on speech corpora (LibriSpeech, MLS, long-form recordings)
+that are not available here; these generators stand in for their *shapes*:
+keys and window queries carry a smooth temporal drift (audio frames are
+continuous in time, AudioKV article section 1), an attention sink at the first
+audio position (the WnW digest reports prefill attention concentrated on the
+start of the audio), and 15-20 % of heads are audio-critical (AudioKV article
+section 1.1).  No item of any corpus is reproduced.
+
+Recipe, per (sequence, layer, KV head) unit, from its own spawned seed:
+  periods P_1..P_3 ~ U[50, 400], phases phi[i, c] ~ U[0, 2 pi),
+  drift[t, c] = sum_i 0.5 sin(2 pi t / P_i + phi[i, c]),
+  sink direction v = normalise(N(0, I_d)),
+  K[t] = N(0, I) + drift[t] + [t == 0] * beta * sqrt(d) * v,      beta = 8
+  Q[g, q] = N(0, I) + drift[L + q] + v                 (g over the GQA group)
+  V[t] = N(0, I)
+then rounded to bf16 (round to nearest even) unless the config is fp32.
+Head scores: U(0, 1) for the tiny config; otherwise round(0.18 N) randomly
+chosen heads ~ U(0.6, 1) and the rest ~ U(0, 0.2).
+"""
+from __future__ import annotations
+
+import concurrent.futures as _cf
+import dataclasses
+import math
+import os
+
+import numpy as np
+
+SINK_BETA = 8.0
+DRIFT_AMP = 0.5
+N_SINUSOIDS = 3
+AUDIO_HEAD_FRACTION = 0.18
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    index: int               # seeds SeedSequence(1000 + index)
+    n_seq: int
+    n_layers: int
+    n_kv_heads: int
+    gqa: int
+    head_dim: int
+    dtype: str               # "bf16" | "f32"
+    n_window: int = 32
+    alpha: float = 0.5
+    rho: float = 0.7
+    window: int = 32
+    base_ratio: float = 0.5
+    lengths: tuple = ()      # fixed per-sequence L, or () for the ragged draw
+    retention: tuple = ()    # fixed per-sequence retention, or () for U(0.2,0.6)
+    length_choices: tuple = ()
+    sink_beta: float = SINK_BETA
+
+
+CONFIGS = {
+    "tiny": Config("tiny", 0, 1, 1, 4, 1, 64, "f32", lengths=(1024,),
+                   retention=(0.6,)),
+    "qwen7b": Config("qwen7b", 1, 1, 28, 4, 7, 128, "bf16", lengths=(8192,),
+                     retention=(0.6,)),
+    "omni30b": Config("omni30b", 2, 1, 48, 4, 8, 128, "bf16", alpha=0.6,
+                      lengths=(32768,), retention=(0.4,)),
+    "ragged": Config("ragged", 3, 8, 28, 4, 7, 128, "bf16",
+                     length_choices=(4096, 8192, 16384, 32768)),
+    "long64k": Config("long64k", 4, 1, 48, 4, 8, 128, "bf16",
+                      lengths=(65536,), retention=(0.2,)),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounding = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    return ((u + rounding) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclasses.dataclass
+class Header:
+    """Per-config draws shared by all units: lengths, retentions, head scores."""
+    cfg: Config
+    lengths: np.ndarray      # int64 [n_seq]
+    retention: np.ndarray    # float64 [n_seq]
+    head_scores: np.ndarray  # float32 [n_layers, n_kv_heads]
+
+    @property
+    def seq_start(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lengths)]).astype(np.int64)
+
+    @property
+    def n_units(self) -> int:
+        c = self.cfg
+        return c.n_seq * c.n_layers * c.n_kv_heads
+
+
+def _root(cfg: Config, n_units: int):
+    return np.random.SeedSequence(1000 + cfg.index).spawn(1 + n_units)
+
+
+def header(cfg: Config) -> Header:
+    n_units = cfg.n_seq * cfg.n_layers * cfg.n_kv_heads
+    rng = np.random.default_rng(_root(cfg, n_units)[0])
+    if cfg.lengths:
+        lengths = np.array(cfg.lengths, dtype=np.int64)
+    else:
+        lengths = rng.choice(np.array(cfg.length_choices, dtype=np.int64),
+                             size=cfg.n_seq)
+    if cfg.retention:
+        retention = np.array(cfg.retention, dtype=np.float64)
+    else:
+        retention = rng.uniform(0.2, 0.6, size=cfg.n_seq)
+    nh = cfg.n_layers * cfg.n_kv_heads
+    if cfg.name == "tiny":
+        S = rng.uniform(0.0, 1.0, size=nh)
+    else:
+        n_audio = int(round(AUDIO_HEAD_FRACTION * nh))
+        audio = rng.choice(nh, size=n_audio, replace=False)
+        S = rng.uniform(0.0, 0.2, size=nh)
+        S[audio] = rng.uniform(0.6, 1.0, size=n_audio)
+    return Header(cfg, lengths, retention,
+                  S.astype(np.float32).reshape(cfg.n_layers, cfg.n_kv_heads))
+
+
+def unit(cfg: Config, hdr: Header, seq: int, layer: int, head: int,
+         *, sink_beta=None):
+    """Generate one unit's (q [G, W, d], k [L, d], v [L, d]).
+
+    Returns float32 arrays for fp32 configs and uint16 bf16 bit arrays
+    otherwise.
+    """
+    beta = cfg.sink_beta if sink_beta is None else sink_beta
+    u = (seq * cfg.n_layers + layer) * cfg.n_kv_heads + head
+    rng = np.random.default_rng(_root(cfg, hdr.n_units)[1 + u])
+    L, d, G, W = int(hdr.lengths[seq]), cfg.head_dim, cfg.gqa, cfg.n_window
+    periods = rng.uniform(50.0, 400.0, size=N_SINUSOIDS)
+    phases = rng.uniform(0.0, 2.0 * math.pi, size=(N_SINUSOIDS, d))
+    v = rng.standard_normal(d)
+    v /= np.linalg.norm(v)
+    kn = rng.standard_normal((L, d), dtype=np.float32)
+    qn = rng.standard_normal((G, W, d), dtype=np.float32)
+    vv = rng.standard_normal((L, d), dtype=np.float32)
+    # sum_i a sin(w_i t + phi_ic) = sum_i a [sin(w_i t) cos(phi_ic) + cos(w_i t) sin(phi_ic)]
+    t = np.arange(L + W, dtype=np.float64)
+    w = 2.0 * math.pi / periods
+    A = np.concatenate([np.sin(np.outer(t, w)), np.cos(np.outer(t, w))], axis=1)
+    B = DRIFT_AMP * np.concatenate([np.cos(phases), np.sin(phases)], axis=0)
+    drift = (A @ B).astype(np.float32)
+    k = kn + drift[:L]
+    k[0] += np.float32(beta * math.sqrt(d)) * v.astype(np.float32)
+    q = qn + drift[L:L + W][None, :, :] + v.astype(np.float32)[None, None, :]
+    if cfg.dtype == "f32":
+        return q.astype(np.float32), k.astype(np.float32), vv
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(vv)
+
+
+@dataclasses.dataclass
+class Problem:
+    """A whole batch in the packed layout the library takes.
+
+    q: [n_seq, n_layers, n_kv_heads * gqa, W, d]
+    k, v: [n_layers, n_kv_heads, T, d] with T = sum of lengths; sequence i
+          occupies tokens seq_start[i] .. seq_start[i+1].
+    """
+    hdr: Header
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+
+    @property
+    def cfg(self) -> Config:
+        return self.hdr.cfg
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def problem(cfg: Config, *, sink_beta=None, hdr: Header | None = None) -> Problem:
+    hdr = hdr or header(cfg)
+    dt = np.float32 if cfg.dtype == "f32" else np.uint16
+    T = int(hdr.lengths.sum())
+    NL, H, G, W, d = cfg.n_layers, cfg.n_kv_heads, cfg.gqa, cfg.n_window, cfg.head_dim
+    q = np.empty((cfg.n_seq, NL, H * G, W, d), dtype=dt)
+    k = np.empty((NL, H, T, d), dtype=dt)
+    v = np.empty((NL, H, T, d), dtype=dt)
+    starts = hdr.seq_start
+
+    def fill(args):
+        i, l, h = args
+        qu, ku, vu = unit(cfg, hdr, i, l, h, sink_beta=sink_beta)
+        q[i, l, h * G:(h + 1) * G] = qu
+        k[l, h, starts[i]:starts[i + 1]] = ku
+        v[l, h, starts[i]:starts[i + 1]] = vu
+
+    jobs = [(i, l, h) for i in range(cfg.n_seq) for l in range(NL) for h in range(H)]
+    with _cf.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, jobs))
+    return Problem(hdr, q, k, v)
