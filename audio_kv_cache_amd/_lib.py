@@ -1,0 +1,91 @@
+"""ctypes binding of libkvc.so (the C ABI declared in include/kvc.h).
+
+Argument marshalling only: every step of the method runs in the library's
+HIP kernels.  torch is imported before the library is loaded so that the
+process has a single HIP runtime (torch's), which libkvc.so then binds to.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+import threading
+
+import torch  # noqa: F401  (loads the HIP runtime libkvc.so binds to)
+
+_PKG = pathlib.Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libkvc.so"
+
+KVC_OK = 0
+KVC_ERR_INVALID_ARG = 1
+KVC_ERR_UNSUPPORTED = 2
+KVC_ERR_BUDGET = 3
+KVC_ERR_WORKSPACE = 4
+KVC_ERR_HIP = 5
+KVC_BF16 = 0
+KVC_F32 = 1
+
+EXPORTS = ("kvc_plan", "kvc_compress", "kvc_scores", "kvc_smooth", "kvc_budget",
+           "kvc_select", "kvc_gather", "kvc_status_str", "kvc_last_hip_error")
+
+
+class kvc_params(ctypes.Structure):
+    _fields_ = [("alpha", ctypes.c_double), ("rho", ctypes.c_double),
+                ("window", ctypes.c_int32), ("base_ratio", ctypes.c_double)]
+
+
+class kvc_problem(ctypes.Structure):
+    _fields_ = [("n_seq", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("gqa_group", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("n_window_q", ctypes.c_int32),
+                ("dtype", ctypes.c_int32),
+                ("seq_start", ctypes.POINTER(ctypes.c_int64)),
+                ("retention", ctypes.POINTER(ctypes.c_double)),
+                ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3)]
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().kvc_status_str(status).decode()
+        if status == KVC_ERR_HIP:
+            msg += f" (hipError {lib().kvc_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [status {status}]")
+
+
+_lib = None
+_lock = threading.Lock()
+_P = ctypes.POINTER
+_vp = ctypes.c_void_p
+
+
+def lib():
+    """Load libkvc.so (building it first only if it has never been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not LIB_PATH.exists():
+                from audio_kv_cache_amd import build as _b
+                _b.build()
+            L = ctypes.CDLL(str(LIB_PATH))
+            prob, prm = _P(kvc_problem), _P(kvc_params)
+            L.kvc_plan.argtypes = [prob, prm, _P(ctypes.c_int64), _P(ctypes.c_size_t)]
+            L.kvc_compress.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, ctypes.c_size_t, _vp]
+            L.kvc_scores.argtypes = [prob, prm, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+            L.kvc_smooth.argtypes = [prob, prm, _vp, _vp, _vp, _vp]
+            L.kvc_budget.argtypes = [prob, prm, _vp, _vp, _vp, _vp]
+            L.kvc_select.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp]
+            L.kvc_gather.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+            for name in EXPORTS[:7]:
+                getattr(L, name).restype = ctypes.c_int
+            L.kvc_status_str.argtypes = [ctypes.c_int]
+            L.kvc_status_str.restype = ctypes.c_char_p
+            L.kvc_last_hip_error.argtypes = []
+            L.kvc_last_hip_error.restype = ctypes.c_int
+            _lib = L
+    return _lib
+
+
+def check(status: int, where: str):
+    if status != KVC_OK:
+        raise KvcError(status, where)

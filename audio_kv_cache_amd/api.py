@@ -1,0 +1,185 @@
+"""torch-facing wrappers of the C ABI (same names as include/kvc.h).
+
+Only argument marshalling lives here: tensor pointers, strides, the stream,
+and output allocation through torch.  The computation is the library's.
+
+Layouts (see include/kvc.h):
+  q        [n_seq, n_layers, n_kv_heads * gqa, n_window, head_dim]
+  k, v     [n_layers, n_kv_heads, T, head_dim] (any strides with head_dim
+           contiguous), sequence i = tokens seq_start[i] .. seq_start[i+1]-1
+  S        float32 [n_layers, n_kv_heads]
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+
+import numpy as np
+import torch
+
+from audio_kv_cache_amd import _lib as C
+
+
+@dataclasses.dataclass
+class Params:
+    alpha: float = 0.5
+    rho: float = 0.7
+    window: int = 32
+    base_ratio: float = 0.5
+
+    def c(self) -> C.kvc_params:
+        return C.kvc_params(float(self.alpha), float(self.rho), int(self.window),
+                            float(self.base_ratio))
+
+
+class Spec:
+    """Host-side problem description (kvc_problem) and the arrays it points to."""
+
+    def __init__(self, *, n_layers, n_kv_heads, gqa, head_dim, seq_lens, retention,
+                 dtype, n_window=32, k_stride=None, v_stride=None):
+        self.n_layers, self.n_kv_heads, self.gqa = int(n_layers), int(n_kv_heads), int(gqa)
+        self.head_dim, self.n_window = int(head_dim), int(n_window)
+        self.dtype = dtype if isinstance(dtype, str) else ("bf16" if dtype == torch.bfloat16 else "f32")
+        self.seq_lens = np.asarray(seq_lens, dtype=np.int64).reshape(-1)
+        self.n_seq = int(self.seq_lens.shape[0])
+        self._seq_start = np.ascontiguousarray(
+            np.concatenate([[0], np.cumsum(self.seq_lens)]).astype(np.int64))
+        self._retention = np.ascontiguousarray(np.broadcast_to(
+            np.asarray(retention, dtype=np.float64), (self.n_seq,)).copy())
+        T = int(self._seq_start[-1])
+        dense = (self.n_kv_heads * T * self.head_dim, T * self.head_dim, self.head_dim)
+        self.k_stride = tuple(int(x) for x in (k_stride or dense))
+        self.v_stride = tuple(int(x) for x in (v_stride or dense))
+
+    @property
+    def n_units(self) -> int:
+        return self.n_seq * self.n_layers * self.n_kv_heads
+
+    @property
+    def seq_start(self) -> np.ndarray:
+        return self._seq_start
+
+    def c(self) -> C.kvc_problem:
+        p = C.kvc_problem()
+        p.n_seq, p.n_layers, p.n_kv_heads = self.n_seq, self.n_layers, self.n_kv_heads
+        p.gqa_group, p.head_dim, p.n_window_q = self.gqa, self.head_dim, self.n_window
+        p.dtype = C.KVC_BF16 if self.dtype == "bf16" else C.KVC_F32
+        p.seq_start = self._seq_start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        p.retention = self._retention.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+        for a in range(3):
+            p.k_stride[a] = self.k_stride[a]
+            p.v_stride[a] = self.v_stride[a]
+        return p
+
+    def score_rows(self) -> int:
+        return int(self.n_layers * self.n_kv_heads * self._seq_start[-1])
+
+    def row_offset(self, i: int, l: int, h: int) -> int:
+        """First element of unit (i, l, h)'s score row."""
+        L = int(self.seq_lens[i])
+        return int(self.n_layers * self.n_kv_heads * self._seq_start[i]
+                   + (l * self.n_kv_heads + h) * L)
+
+    @staticmethod
+    def for_tensors(k, v, *, gqa, seq_lens, retention, n_window=32):
+        """Spec for k/v tensors shaped [n_layers, n_kv_heads, T, head_dim]."""
+        NL, H, T, d = k.shape
+        dtype = "bf16" if k.dtype == torch.bfloat16 else "f32"
+        return Spec(n_layers=NL, n_kv_heads=H, gqa=gqa, head_dim=d, seq_lens=seq_lens,
+                    retention=retention, dtype=dtype, n_window=n_window,
+                    k_stride=k.stride()[:3], v_stride=v.stride()[:3])
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# The entry points, one to one.
+# ---------------------------------------------------------------------------
+def kvc_plan(spec: Spec, params: Params):
+    """-> (total_rows, workspace_bytes); host only."""
+    rows = ctypes.c_int64(0)
+    ws = ctypes.c_size_t(0)
+    C.check(C.lib().kvc_plan(ctypes.byref(spec.c()), ctypes.byref(params.c()),
+                             ctypes.byref(rows), ctypes.byref(ws)), "kvc_plan")
+    return int(rows.value), int(ws.value)
+
+
+def kvc_compress(spec, params, q, k, v, head_scores, k_out, v_out, idx_out, seg_offsets,
+                 budgets, workspace, stream=None):
+    C.check(C.lib().kvc_compress(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(head_scores), _ptr(k_out), _ptr(v_out),
+                                 _ptr(idx_out), _ptr(seg_offsets), _ptr(budgets),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)), "kvc_compress")
+
+
+def kvc_scores(spec, params, q, k, s_out, workspace, stream=None):
+    C.check(C.lib().kvc_scores(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(q),
+                               _ptr(k), _ptr(s_out), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)),
+            "kvc_scores")
+
+
+def kvc_smooth(spec, params, s, s_hat, kstar, stream=None):
+    C.check(C.lib().kvc_smooth(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(s),
+                               _ptr(s_hat), _ptr(kstar), _stream(stream)), "kvc_smooth")
+
+
+def kvc_budget(spec, params, head_scores, budgets, seg_offsets, stream=None):
+    C.check(C.lib().kvc_budget(ctypes.byref(spec.c()), ctypes.byref(params.c()),
+                               _ptr(head_scores), _ptr(budgets), _ptr(seg_offsets),
+                               _stream(stream)), "kvc_budget")
+
+
+def kvc_select(spec, params, s_hat, budgets, seg_offsets, idx_out, stream=None):
+    C.check(C.lib().kvc_select(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(s_hat),
+                               _ptr(budgets), _ptr(seg_offsets), _ptr(idx_out),
+                               _stream(stream)), "kvc_select")
+
+
+def kvc_gather(spec, params, k, v, idx, seg_offsets, k_out, v_out, stream=None):
+    C.check(C.lib().kvc_gather(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(k),
+                               _ptr(v), _ptr(idx), _ptr(seg_offsets), _ptr(k_out), _ptr(v_out),
+                               _stream(stream)), "kvc_gather")
+
+
+# ---------------------------------------------------------------------------
+# Convenience: allocate outputs with torch and run the whole path.
+# ---------------------------------------------------------------------------
+def _require_gpu(*ts):
+    for t in ts:
+        if not (isinstance(t, torch.Tensor) and t.is_cuda):
+            raise ValueError("audio_kv_cache_amd needs its tensors in GPU memory")
+
+
+def allocate(spec: Spec, params: Params, device):
+    rows, ws = kvc_plan(spec, params)
+    tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    return dict(
+        k_out=torch.empty((rows, spec.head_dim), dtype=tdt, device=device),
+        v_out=torch.empty((rows, spec.head_dim), dtype=tdt, device=device),
+        idx=torch.empty((rows,), dtype=torch.int32, device=device),
+        offsets=torch.empty((spec.n_units + 1,), dtype=torch.int64, device=device),
+        budgets=torch.empty((spec.n_units,), dtype=torch.int32, device=device),
+        workspace=torch.empty((max(ws, 256),), dtype=torch.uint8, device=device),
+    )
+
+
+def compress(q, k, v, head_scores, *, gqa, seq_lens, retention, alpha=0.5, rho=0.7,
+             window=32, base_ratio=0.5, out=None, stream=None):
+    """Whole path; returns dict(k_out, v_out, idx, offsets, budgets, workspace)."""
+    _require_gpu(q, k, v, head_scores)
+    spec = Spec.for_tensors(k, v, gqa=gqa, seq_lens=seq_lens, retention=retention,
+                            n_window=q.shape[-2])
+    params = Params(alpha, rho, window, base_ratio)
+    o = out if out is not None else allocate(spec, params, k.device)
+    kvc_compress(spec, params, q, k, v, head_scores, o["k_out"], o["v_out"], o["idx"],
+                 o["offsets"], o["budgets"], o["workspace"], stream)
+    return o

@@ -1,0 +1,175 @@
+// budget.hip -- head-aware token budget (step 3), one workgroup per sequence.
+//
+// AudioKV article, section 3.1 (layered cache allocation): every head keeps
+// a local window w plus a uniform base share r, and the remaining budget
+// B_score is split in proportion to the head's audio score S_{l,h}; the
+// section 5.1 config gives min_window 32 and base_ratio 0.5.  Here:
+//   kbar = floor(retention * L), r = floor(base_ratio * kbar), fixed = w + r
+//   R = n*kbar - n*fixed split as R*S_u/sum(S) (uniform if sum(S) == 0)
+// A share may not exceed cap = L - fixed (a head cannot keep more than L
+// tokens): shares at or above the cap are fixed there and the remaining pool
+// is split again among the other heads.  Integer budgets by largest
+// remainder, equal remainders to the lower head index.  kbar >= L keeps all.
+//
+// The arithmetic is IEEE fp64 in a fixed order (sums ascending in u) with no
+// fused multiply-add, so the budgets are bit-identical to any other
+// implementation of the same definition.
+#include "kvc_internal.h"
+
+#pragma clang fp contract(off)
+
+#define BUDGET_THREADS 1024
+
+__global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
+    KvcDesc D, const float* __restrict__ S, int32_t* __restrict__ budgets,
+    int64_t* __restrict__ offsets, uint32_t* __restrict__ zero_ptr, int zero_count) {
+  // Side job: clear the score kernels' per-unit arrival counters.
+  for (int i = blockIdx.x * BUDGET_THREADS + threadIdx.x; i < zero_count;
+       i += gridDim.x * BUDGET_THREADS)
+    zero_ptr[i] = 0u;
+
+  __shared__ double q[KVC_MAX_UNITS_PER_SEQ];
+  __shared__ int32_t extra[KVC_MAX_UNITS_PER_SEQ];
+  __shared__ uint8_t active[KVC_MAX_UNITS_PER_SEQ];
+  __shared__ double s_sum;
+  __shared__ int64_t s_R;
+  __shared__ int s_nA, s_capped;
+  __shared__ int64_t s_wsum[BUDGET_THREADS / 64];
+  __shared__ int s_wcnt[BUDGET_THREADS / 64];
+
+  const int seq = blockIdx.x;
+  const int n = D.upseq;
+  const int L = D.L[seq];
+  const int tid = threadIdx.x;
+  const int64_t u0 = (int64_t)seq * n;
+
+  const int64_t kbar = (int64_t)floor(D.retention[seq] * (double)L);
+  if (kbar >= L) {
+    for (int u = tid; u < n; u += BUDGET_THREADS) {
+      budgets[u0 + u] = L;
+      offsets[u0 + u] = D.row_base[seq] + (int64_t)u * L;
+    }
+    if (seq == D.n_seq - 1 && tid == 0) offsets[u0 + n] = D.row_base[seq] + (int64_t)n * L;
+    return;
+  }
+  const int64_t r = (int64_t)floor(D.base_ratio * (double)kbar);
+  const int64_t fixed = (int64_t)D.window + r;
+  const int64_t cap = (int64_t)L - fixed;
+
+  for (int u = tid; u < n; u += BUDGET_THREADS) {
+    active[u] = 1;
+    extra[u] = 0;
+  }
+  if (tid == 0) s_R = (int64_t)n * kbar - (int64_t)n * fixed;
+  __syncthreads();
+
+  // Water-filling rounds.
+  for (;;) {
+    if (tid == 0) {
+      double acc = 0.0;
+      int nA = 0;
+      for (int u = 0; u < n; ++u)
+        if (active[u]) {
+          acc += (double)S[u];
+          ++nA;
+        }
+      s_sum = acc;
+      s_nA = nA;
+      s_capped = 0;
+    }
+    __syncthreads();
+    const double sumA = s_sum;
+    const int nA = s_nA;
+    const double Rd = (double)s_R;
+    int my_capped = 0;
+    for (int u = tid; u < n; u += BUDGET_THREADS) {
+      if (!active[u]) continue;
+      const double qu = sumA > 0.0 ? (Rd * (double)S[u]) / sumA : Rd / (double)nA;
+      q[u] = qu;
+      if (qu >= (double)cap) ++my_capped;
+    }
+    if (my_capped) atomicAdd(&s_capped, my_capped);
+    __syncthreads();
+    const int capped = s_capped;
+    if (capped == 0 || nA == 0) break;
+    for (int u = tid; u < n; u += BUDGET_THREADS)
+      if (active[u] && q[u] >= (double)cap) {
+        active[u] = 0;
+        extra[u] = (int32_t)cap;
+      }
+    __syncthreads();
+    if (tid == 0) s_R -= cap * (int64_t)capped;
+    __syncthreads();
+  }
+
+  // Largest remainder over the heads still active.
+  int64_t my_floor = 0;
+  for (int u = tid; u < n; u += BUDGET_THREADS)
+    if (active[u]) my_floor += (int64_t)floor(q[u]);
+  for (int o = 32; o > 0; o >>= 1) my_floor += __shfl_xor(my_floor, o);
+  if ((tid & 63) == 0) s_wsum[tid >> 6] = my_floor;
+  __syncthreads();
+  int64_t floors = 0;
+  for (int w = 0; w < BUDGET_THREADS / 64; ++w) floors += s_wsum[w];
+  const int64_t deficit = s_R - floors;  // 0 <= deficit <= active count
+
+  for (int u = tid; u < n; u += BUDGET_THREADS) {
+    if (!active[u]) continue;
+    const double fu = floor(q[u]);
+    const double ru = q[u] - fu;
+    int64_t rank = 0;
+    for (int v = 0; v < n; ++v) {
+      if (!active[v]) continue;
+      const double rv = q[v] - floor(q[v]);
+      rank += (rv > ru) || (rv == ru && v < u);
+    }
+    extra[u] = (int32_t)fu + (rank < deficit ? 1 : 0);
+  }
+  __syncthreads();
+
+  // Budgets and the exclusive prefix of row offsets, in u order.
+  const int per = (n + BUDGET_THREADS - 1) / BUDGET_THREADS;
+  const int lo = tid * per, hi = min(n, lo + per);
+  int64_t part = 0;
+  for (int u = lo; u < hi; ++u) part += fixed + extra[u];
+  // inclusive scan of per-thread parts: wave scan then across waves
+  int64_t incl = part;
+  const int lane = tid & 63;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  __syncthreads();
+  if (lane == 63) s_wsum[tid >> 6] = incl;
+  __syncthreads();
+  int64_t before = 0;
+  for (int w = 0; w < (tid >> 6); ++w) before += s_wsum[w];
+  int64_t run = D.row_base[seq] + before + incl - part;
+  for (int u = lo; u < hi; ++u) {
+    const int64_t bu = fixed + extra[u];
+    budgets[u0 + u] = (int32_t)bu;
+    offsets[u0 + u] = run;
+    run += bu;
+  }
+  if (seq == D.n_seq - 1 && hi == n && lo < hi) offsets[u0 + n] = run;
+}
+
+hipError_t kvc_launch_budget(const KvcDesc& D, const float* S, int32_t* budgets,
+                             int64_t* offsets, uint32_t* zero_ptr, int zero_count,
+                             hipStream_t st) {
+  hipLaunchKernelGGL(kvc_budget_kernel, dim3(D.n_seq), dim3(BUDGET_THREADS), 0, st, D, S,
+                     budgets, offsets, zero_ptr, zero_count);
+  return hipGetLastError();
+}
+
+__global__ void kvc_fill_u32_kernel(uint32_t* p, int count, uint32_t value) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = value;
+}
+
+hipError_t kvc_launch_fill_u32(uint32_t* p, int count, uint32_t value, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kvc_fill_u32_kernel, dim3((count + 255) / 256), dim3(256), 0, st, p,
+                     count, value);
+  return hipGetLastError();
+}

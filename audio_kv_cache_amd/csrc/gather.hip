@@ -1,0 +1,95 @@
+// gather.hip -- compaction of the kept K/V rows (step 5).
+//
+// K_out[t] = K[idx[t]], V_out[t] = V[idx[t]] for every compacted row t; the
+// rows of unit u are seg_offsets[u] .. seg_offsets[u+1]-1 (the VoxZip
+// digest writes the same compaction as K_{t+1} = Concat(K[:T], K[I_hist],
+// K[-M:])).  Pure data movement: each lane moves 16-byte pieces, a 256-thread
+// workgroup moves a contiguous run of output rows, loads are issued for K and
+// V together so several 16-byte requests per lane are in flight, and the
+// output is written with non-temporal stores (it is not read again here).
+#include "kvc_internal.h"
+
+#define GATHER_THREADS 256
+
+template <int ROWB>
+__global__ __launch_bounds__(GATHER_THREADS) void kvc_gather_kernel(
+    KvcDesc D, const char* __restrict__ k, const char* __restrict__ v,
+    const int32_t* __restrict__ idx, const int64_t* __restrict__ offsets,
+    char* __restrict__ k_out, char* __restrict__ v_out, int64_t total_rows) {
+  constexpr int CH = ROWB / 16;                    // 16-byte chunks per row
+  constexpr int ROWS_PER_PASS = GATHER_THREADS / CH;
+  constexpr int PASSES = 4;
+  constexpr int ROWS_PER_BLOCK = ROWS_PER_PASS * PASSES;
+  const int64_t r0 = (int64_t)blockIdx.x * ROWS_PER_BLOCK;
+  if (r0 >= total_rows) return;
+
+  // Unit owning the block's first row: largest u with offsets[u] <= r0.
+  __shared__ int s_u0;
+  if (threadIdx.x == 0) {
+    int lo = 0, hi = D.n_units - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offsets[mid] <= r0) lo = mid; else hi = mid - 1;
+    }
+    s_u0 = lo;
+  }
+  __syncthreads();
+
+  const int esz = D.dtype == 0 ? 2 : 4;
+  const int chunk = threadIdx.x % CH;
+  int u = s_u0;
+  uint4 kv[PASSES], vv[PASSES];
+  int64_t rows[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int64_t t = r0 + p * ROWS_PER_PASS + threadIdx.x / CH;
+    rows[p] = t;
+    if (t >= total_rows) continue;
+    while (u + 1 < D.n_units && offsets[u + 1] <= t) ++u;
+    const int seq = u / D.upseq;
+    const int within = u - seq * D.upseq;
+    const int l = within / D.n_heads, h = within - l * D.n_heads;
+    int pos = idx[t];
+    if ((unsigned)pos >= (unsigned)D.L[seq]) pos = 0;  // never read outside the row
+    const int64_t tok = D.tok0[seq] + pos;
+    const char* ks = k + (l * D.ks[0] + h * D.ks[1] + tok * D.ks[2]) * esz;
+    const char* vs = v + (l * D.vs[0] + h * D.vs[1] + tok * D.vs[2]) * esz;
+    kv[p] = *reinterpret_cast<const uint4*>(ks + chunk * 16);
+    vv[p] = *reinterpret_cast<const uint4*>(vs + chunk * 16);
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int64_t t = rows[p];
+    if (t >= total_rows) continue;
+    uint4* ko = reinterpret_cast<uint4*>(k_out + t * ROWB + chunk * 16);
+    uint4* vo = reinterpret_cast<uint4*>(v_out + t * ROWB + chunk * 16);
+    __builtin_nontemporal_store(kv[p].x, &ko->x);
+    __builtin_nontemporal_store(kv[p].y, &ko->y);
+    __builtin_nontemporal_store(kv[p].z, &ko->z);
+    __builtin_nontemporal_store(kv[p].w, &ko->w);
+    __builtin_nontemporal_store(vv[p].x, &vo->x);
+    __builtin_nontemporal_store(vv[p].y, &vo->y);
+    __builtin_nontemporal_store(vv[p].z, &vo->z);
+    __builtin_nontemporal_store(vv[p].w, &vo->w);
+  }
+}
+
+hipError_t kvc_launch_gather(const KvcDesc& D, const void* k, const void* v,
+                             const int32_t* idx, const int64_t* offsets, void* k_out,
+                             void* v_out, int64_t total_rows, hipStream_t st) {
+  if (total_rows <= 0) return hipSuccess;
+  const int rowb = D.d * (D.dtype == 0 ? 2 : 4);
+  auto go = [&](auto kern, int rows_per_block) {
+    const int64_t blocks = (total_rows + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(GATHER_THREADS), 0, st, D,
+                       (const char*)k, (const char*)v, idx, offsets, (char*)k_out,
+                       (char*)v_out, total_rows);
+  };
+  switch (rowb) {
+    case 128: go(kvc_gather_kernel<128>, GATHER_THREADS / 8 * 4); break;
+    case 256: go(kvc_gather_kernel<256>, GATHER_THREADS / 16 * 4); break;
+    case 512: go(kvc_gather_kernel<512>, GATHER_THREADS / 32 * 4); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}

@@ -1,0 +1,262 @@
+// kvc_host.hip -- the C ABI of include/kvc.h: validation, sizing, workspace
+// carving and kernel launches.  No allocation, no synchronisation: every
+// entry point enqueues on the caller's stream and returns.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/kvc.h"
+#include "kvc_internal.h"
+
+static thread_local int g_last_hip_error = 0;
+
+static kvc_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return KVC_OK;
+  g_last_hip_error = (int)e;
+  return KVC_ERR_HIP;
+}
+
+extern "C" const char* kvc_status_str(kvc_status s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_INVALID_ARG: return "invalid argument";
+    case KVC_ERR_UNSUPPORTED: return "unsupported problem shape";
+    case KVC_ERR_BUDGET: return "infeasible budget (L <= window or window + base share > mean budget)";
+    case KVC_ERR_WORKSPACE: return "workspace too small";
+    case KVC_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+extern "C" int kvc_last_hip_error(void) { return g_last_hip_error; }
+
+static bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+static size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// kbar = floor(retention * L) in fp64, as the budget kernel computes it.
+static int64_t kbar_of(double retention, int64_t L) {
+  return (int64_t)floor(retention * (double)L);
+}
+
+// Validate and fill the kernel descriptor.
+static kvc_status make_desc(const kvc_problem* p, const kvc_params* prm, KvcDesc* D) {
+  if (!p || !prm || !D) return KVC_ERR_INVALID_ARG;
+  if (!p->seq_start || !p->retention) return KVC_ERR_INVALID_ARG;
+  if (p->n_seq < 1 || p->n_layers < 1 || p->n_kv_heads < 1 || p->gqa_group < 1 ||
+      p->head_dim < 1 || p->n_window_q < 1)
+    return KVC_ERR_INVALID_ARG;
+  if (p->dtype != KVC_BF16 && p->dtype != KVC_F32) return KVC_ERR_INVALID_ARG;
+  if (!(prm->alpha >= 0.0 && prm->alpha <= 1.0)) return KVC_ERR_INVALID_ARG;
+  if (!(prm->rho > 0.0 && prm->rho <= 1.0)) return KVC_ERR_INVALID_ARG;
+  if (!(prm->base_ratio >= 0.0 && prm->base_ratio <= 1.0)) return KVC_ERR_INVALID_ARG;
+  if (prm->window < 0) return KVC_ERR_INVALID_ARG;
+  const int esz = p->dtype == KVC_BF16 ? 2 : 4;
+  for (int a = 0; a < 3; ++a)
+    if (p->k_stride[a] < 0 || p->v_stride[a] < 0) return KVC_ERR_INVALID_ARG;
+  if (p->k_stride[2] < p->head_dim || p->v_stride[2] < p->head_dim) return KVC_ERR_INVALID_ARG;
+  for (int a = 0; a < 3; ++a)
+    if ((p->k_stride[a] * esz) % 16 || (p->v_stride[a] * esz) % 16) return KVC_ERR_INVALID_ARG;
+  for (int i = 0; i < p->n_seq && i < KVC_MAX_SEQ; ++i) {
+    if (!(p->retention[i] > 0.0 && p->retention[i] <= 1.0)) return KVC_ERR_INVALID_ARG;
+    if (p->seq_start[i + 1] < p->seq_start[i] || p->seq_start[i] < 0) return KVC_ERR_INVALID_ARG;
+  }
+
+  if (p->n_seq > KVC_MAX_SEQ) return KVC_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return KVC_ERR_UNSUPPORTED;
+  const int64_t gw = (int64_t)p->gqa_group * p->n_window_q;
+  if (gw % 32 != 0 || gw > KVC_MAX_GW) return KVC_ERR_UNSUPPORTED;
+  const int64_t upseq = (int64_t)p->n_layers * p->n_kv_heads;
+  if (upseq > KVC_MAX_UNITS_PER_SEQ) return KVC_ERR_UNSUPPORTED;
+  if (upseq * p->n_seq > (int64_t)1 << 30) return KVC_ERR_UNSUPPORTED;
+
+  memset(D, 0, sizeof(*D));
+  D->n_seq = p->n_seq;
+  D->n_layers = p->n_layers;
+  D->n_heads = p->n_kv_heads;
+  D->gqa = p->gqa_group;
+  D->d = p->head_dim;
+  D->nwin = p->n_window_q;
+  D->gw = (int)gw;
+  D->upseq = (int)upseq;
+  D->window = prm->window;
+  D->dtype = p->dtype == KVC_BF16 ? 0 : 1;
+  D->alpha = (float)prm->alpha;
+  D->rho = (float)prm->rho;
+  D->base_ratio = prm->base_ratio;
+  for (int a = 0; a < 3; ++a) {
+    D->ks[a] = p->k_stride[a];
+    D->vs[a] = p->v_stride[a];
+  }
+  int64_t rows = 0, srows = 0;
+  int64_t tiles = 0;
+  for (int i = 0; i < p->n_seq; ++i) {
+    const int64_t L = p->seq_start[i + 1] - p->seq_start[i];
+    if (!is_pow2(L) || L < KVC_MIN_L || L > KVC_MAX_L) return KVC_ERR_UNSUPPORTED;
+    if (L <= prm->window) return KVC_ERR_BUDGET;
+    const int64_t kbar = kbar_of(p->retention[i], L);
+    if (kbar < L) {
+      const int64_t r = (int64_t)floor(prm->base_ratio * (double)kbar);
+      if ((int64_t)prm->window + r > kbar) return KVC_ERR_BUDGET;
+    }
+    D->tok0[i] = p->seq_start[i];
+    D->L[i] = (int32_t)L;
+    D->log2L[i] = 63 - __builtin_clzll((unsigned long long)L);
+    D->retention[i] = p->retention[i];
+    D->row_base[i] = rows;
+    D->srow_base[i] = srows;
+    D->tile_base[i] = (int32_t)tiles;
+    rows += upseq * std::min(kbar, L);
+    srows += upseq * L;
+    tiles += upseq * kvc_tiles_per_unit((int)L);
+  }
+  if (tiles > INT32_MAX / 2) return KVC_ERR_UNSUPPORTED;
+  D->tok0[p->n_seq] = p->seq_start[p->n_seq];
+  D->row_base[p->n_seq] = rows;
+  D->srow_base[p->n_seq] = srows;
+  D->tile_base[p->n_seq] = (int32_t)tiles;
+  D->n_units = (int)(upseq * p->n_seq);
+  D->total_tiles = (int)tiles;
+  // Longest sequences first, so the longest units start earliest.
+  int order[KVC_MAX_SEQ];
+  for (int i = 0; i < p->n_seq; ++i) order[i] = i;
+  std::stable_sort(order, order + p->n_seq, [&](int a, int b) { return D->L[a] > D->L[b]; });
+  for (int i = 0; i < p->n_seq; ++i) D->seq_order[i] = order[i];
+  return KVC_OK;
+}
+
+static size_t score_rows_bytes(const KvcDesc& D) {
+  return sizeof(float) * (size_t)D.srow_base[D.n_seq];
+}
+
+extern "C" kvc_status kvc_plan(const kvc_problem* prob, const kvc_params* params,
+                               int64_t* total_rows, size_t* workspace_bytes) {
+  KvcDesc D;
+  const kvc_status st = make_desc(prob, params, &D);
+  if (st != KVC_OK) return st;
+  if (total_rows) *total_rows = D.row_base[D.n_seq];
+  if (workspace_bytes) *workspace_bytes = kvc_scores_workspace(D) + up256(score_rows_bytes(D));
+  return KVC_OK;
+}
+
+// Workspace layout: [counters | lse2 | partials] (kvc_scores_workspace) then
+// the score rows.
+struct Carve {
+  uint32_t* counters;
+  float* lse2;
+  float2* partials;
+  float* srows;
+};
+
+static Carve carve(const KvcDesc& D, void* ws) {
+  char* p = (char*)ws;
+  Carve c;
+  c.counters = (uint32_t*)p;
+  p += up256(sizeof(uint32_t) * (size_t)D.n_units);
+  c.lse2 = (float*)p;
+  p += up256(sizeof(float) * (size_t)D.n_units * D.gw);
+  c.partials = (float2*)p;
+  p += up256(sizeof(float2) * (size_t)D.total_tiles * D.gw);
+  c.srows = (float*)p;
+  return c;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+extern "C" kvc_status kvc_compress(const kvc_problem* prob, const kvc_params* params,
+                                   const void* q_window, const void* k, const void* v,
+                                   const float* head_scores, void* k_out, void* v_out,
+                                   int32_t* idx_out, int64_t* seg_offsets, int32_t* budgets,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  KvcDesc D;
+  kvc_status st = make_desc(prob, params, &D);
+  if (st != KVC_OK) return st;
+  if (!q_window || !k || !v || !head_scores || !k_out || !v_out || !idx_out || !seg_offsets ||
+      !budgets || !workspace)
+    return KVC_ERR_INVALID_ARG;
+  if (!aligned16(q_window) || !aligned16(k) || !aligned16(v) || !aligned16(k_out) ||
+      !aligned16(v_out) || ((uintptr_t)workspace & 255u))
+    return KVC_ERR_INVALID_ARG;
+  const size_t need = kvc_scores_workspace(D) + up256(score_rows_bytes(D));
+  if (workspace_bytes < need) return KVC_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const Carve c = carve(D, workspace);
+  hipError_t e;
+  e = kvc_launch_budget(D, head_scores, budgets, seg_offsets, c.counters, D.n_units, s);
+  if (e != hipSuccess) return hip_status(e);
+  e = kvc_launch_scores(D, q_window, k, c.srows, c.partials, c.lse2, c.counters, s);
+  if (e != hipSuccess) return hip_status(e);
+  e = kvc_launch_sss_select(D, 1 | 2, c.srows, nullptr, nullptr, budgets, seg_offsets, idx_out, s);
+  if (e != hipSuccess) return hip_status(e);
+  e = kvc_launch_gather(D, k, v, idx_out, seg_offsets, k_out, v_out, D.row_base[D.n_seq], s);
+  return hip_status(e);
+}
+
+extern "C" kvc_status kvc_scores(const kvc_problem* prob, const kvc_params* params,
+                                 const void* q_window, const void* k, float* s_out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  KvcDesc D;
+  kvc_status st = make_desc(prob, params, &D);
+  if (st != KVC_OK) return st;
+  if (!q_window || !k || !s_out || !workspace) return KVC_ERR_INVALID_ARG;
+  if (!aligned16(q_window) || !aligned16(k) || ((uintptr_t)workspace & 255u) ||
+      ((uintptr_t)s_out & 7u))
+    return KVC_ERR_INVALID_ARG;
+  if (workspace_bytes < kvc_scores_workspace(D)) return KVC_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const Carve c = carve(D, workspace);
+  hipError_t e = kvc_launch_fill_u32(c.counters, D.n_units, 0u, s);
+  if (e != hipSuccess) return hip_status(e);
+  e = kvc_launch_scores(D, q_window, k, s_out, c.partials, c.lse2, c.counters, s);
+  return hip_status(e);
+}
+
+extern "C" kvc_status kvc_smooth(const kvc_problem* prob, const kvc_params* params,
+                                 const float* s_in, float* s_hat, int32_t* kstar,
+                                 void* stream) {
+  KvcDesc D;
+  kvc_status st = make_desc(prob, params, &D);
+  if (st != KVC_OK) return st;
+  if (!s_in || !s_hat || !kstar) return KVC_ERR_INVALID_ARG;
+  if (((uintptr_t)s_in & 7u) || ((uintptr_t)s_hat & 7u)) return KVC_ERR_INVALID_ARG;
+  return hip_status(kvc_launch_sss_select(D, 1 | 4, s_in, s_hat, kstar, nullptr, nullptr,
+                                          nullptr, (hipStream_t)stream));
+}
+
+extern "C" kvc_status kvc_budget(const kvc_problem* prob, const kvc_params* params,
+                                 const float* head_scores, int32_t* budgets,
+                                 int64_t* seg_offsets, void* stream) {
+  KvcDesc D;
+  kvc_status st = make_desc(prob, params, &D);
+  if (st != KVC_OK) return st;
+  if (!head_scores || !budgets || !seg_offsets) return KVC_ERR_INVALID_ARG;
+  return hip_status(kvc_launch_budget(D, head_scores, budgets, seg_offsets, nullptr, 0,
+                                      (hipStream_t)stream));
+}
+
+extern "C" kvc_status kvc_select(const kvc_problem* prob, const kvc_params* params,
+                                 const float* s_hat, const int32_t* budgets,
+                                 const int64_t* seg_offsets, int32_t* idx_out, void* stream) {
+  KvcDesc D;
+  kvc_status st = make_desc(prob, params, &D);
+  if (st != KVC_OK) return st;
+  if (!s_hat || !budgets || !seg_offsets || !idx_out) return KVC_ERR_INVALID_ARG;
+  if ((uintptr_t)s_hat & 7u) return KVC_ERR_INVALID_ARG;
+  return hip_status(kvc_launch_sss_select(D, 2, s_hat, nullptr, nullptr, budgets, seg_offsets,
+                                          idx_out, (hipStream_t)stream));
+}
+
+extern "C" kvc_status kvc_gather(const kvc_problem* prob, const kvc_params* params,
+                                 const void* k, const void* v, const int32_t* idx,
+                                 const int64_t* seg_offsets, void* k_out, void* v_out,
+                                 void* stream) {
+  KvcDesc D;
+  kvc_status st = make_desc(prob, params, &D);
+  if (st != KVC_OK) return st;
+  if (!k || !v || !idx || !seg_offsets || !k_out || !v_out) return KVC_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out))
+    return KVC_ERR_INVALID_ARG;
+  return hip_status(kvc_launch_gather(D, k, v, idx, seg_offsets, k_out, v_out,
+                                      D.row_base[D.n_seq], (hipStream_t)stream));
+}

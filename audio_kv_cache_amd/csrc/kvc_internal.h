@@ -1,0 +1,66 @@
+// kvc_internal.h -- definitions shared by libkvc's host code and its gfx950
+// kernels (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define KVC_MAX_SEQ 64
+#define KVC_MAX_UNITS_PER_SEQ 4096
+#define KVC_MIN_L 64
+#define KVC_MAX_L 65536
+#define KVC_MAX_GW 256
+
+// Keys covered by one score workgroup (a "tile"); shorter rows use one tile.
+#define KVC_TILE_KEYS 1024
+// Threads of the smoothing/selection workgroup (one workgroup per unit).
+#define KVC_SSS_THREADS 1024
+
+// Everything a kernel needs to know about the problem, passed by value as a
+// kernel argument (about 2.7 KiB, under the 4 KiB argument limit).
+struct KvcDesc {
+  int32_t n_seq, n_layers, n_heads, gqa, d, nwin, gw, upseq;  // upseq = n_layers*n_heads
+  int32_t window, dtype;                                      // dtype: 0 bf16, 1 f32
+  float alpha, rho;
+  double base_ratio;
+  int64_t ks[3], vs[3];                 // element strides: layer, head, token
+  int64_t tok0[KVC_MAX_SEQ + 1];        // sequence i = tokens tok0[i] .. tok0[i+1]-1
+  int64_t row_base[KVC_MAX_SEQ + 1];    // first compacted row of sequence i
+  int64_t srow_base[KVC_MAX_SEQ + 1];   // first score-row element of sequence i
+  double retention[KVC_MAX_SEQ];
+  int32_t L[KVC_MAX_SEQ];
+  int32_t log2L[KVC_MAX_SEQ];
+  int32_t tile_base[KVC_MAX_SEQ + 1];   // first score tile of sequence i
+  int32_t seq_order[KVC_MAX_SEQ];       // sequences by descending L (ties: index)
+  int32_t n_units;
+  int32_t total_tiles;
+};
+
+// Unit u -> (sequence, unit within sequence).
+__host__ __device__ inline int kvc_seq_of_unit(const KvcDesc& D, int u) { return u / D.upseq; }
+
+__host__ __device__ inline int kvc_tiles_per_unit(int L) {
+  return L > KVC_TILE_KEYS ? L / KVC_TILE_KEYS : 1;
+}
+
+// Kernel launchers (defined next to each kernel).
+hipError_t kvc_launch_budget(const KvcDesc& D, const float* S, int32_t* budgets,
+                             int64_t* offsets, uint32_t* zero_ptr, int zero_count,
+                             hipStream_t st);
+hipError_t kvc_launch_fill_u32(uint32_t* p, int count, uint32_t value, hipStream_t st);
+hipError_t kvc_launch_scores(const KvcDesc& D, const void* q, const void* k,
+                             float* s, float2* partials, float* lse2,
+                             uint32_t* counters, hipStream_t st);
+// mode bit 0: smooth (else read s_hat from s_in); bit 1: select;
+// bit 2: export s_hat and kstar.
+hipError_t kvc_launch_sss_select(const KvcDesc& D, int mode, const float* s_in,
+                                 float* s_hat_out, int32_t* kstar_out,
+                                 const int32_t* budgets, const int64_t* offsets,
+                                 int32_t* idx_out, hipStream_t st);
+hipError_t kvc_launch_gather(const KvcDesc& D, const void* k, const void* v,
+                             const int32_t* idx, const int64_t* offsets,
+                             void* k_out, void* v_out, int64_t total_rows,
+                             hipStream_t st);
+
+// Workspace needed by the score kernels.
+size_t kvc_scores_workspace(const KvcDesc& D);

@@ -1,0 +1,344 @@
+// score.hip -- observation-window importance scores (step 1) on MFMA.
+//
+// AudioKV article, section 1.2: the raw importance score of each audio
+// position is the attention it receives from the observation window; with
+// the softmax(q K^T / sqrt(d)) form written in the VoxZip digest's
+// decayed-eviction equation, per unit (sequence, layer, KV head):
+//   s[j] = 1/(G W) * sum_{g,q} exp(l[gq,j] - LSE[gq]),  l = q . k_j / sqrt(d),
+// the softmax taken over all L audio keys.
+//
+// Two passes over K, both GEMM-shaped (Q [G W, d] x K^T [d, keys]):
+//   stats  per query (max, sum of exp) of each 1024-key tile; the last tile of
+//          a unit to finish folds the unit's partials into LSE (log2 units)
+//   pool   recompute the logits, p = exp2(l*c - LSE2), sum over the G*W
+//          queries inside the lane, write s.
+// Q of the unit sits in LDS (rows padded by 16 bytes against bank
+// conflicts); each wave streams its own K rows straight into MFMA operand
+// registers.  Inside a lane's 128-byte half row the head dimension is read in
+// a permuted order (lane group g owns d in [g*d/G, (g+1)*d/G)); the same
+// permutation is applied to Q and K, so the contraction is unchanged and
+// every lane reads contiguous memory.
+//
+// bf16 inputs: v_mfma_f32_32x32x16_bf16 (fp32 accumulate).  fp32 inputs:
+// widened to fp64 and contracted with v_mfma_f64_16x16x4f64, which keeps the
+// logits exact to ~1e-15 so the 1e-5 fp32 tolerance is met with margin.
+#include "kvc_internal.h"
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float floatx16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef double doublex4 __attribute__((__vector_size__(4 * sizeof(double))));
+
+#define SCORE_THREADS 256
+#define SCORE_WAVES 4
+
+static constexpr float kLog2e = 1.4426950408889634f;
+
+struct TBf16 {
+  using elem_t = uint16_t;
+  using frag_t = bf16x8;
+  using acc_t = floatx16;
+  static constexpr int M = 32, KS = 16, E = 8, NOUT = 16, G = 2;
+  __device__ static acc_t zero() { return acc_t{}; }
+  __device__ static acc_t mma(frag_t a, frag_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // Output element i of a lane sits at row out_row(i, lane), column lane % M.
+  __device__ static int out_row(int i, int lane) { return (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3); }
+  __device__ static float val(const acc_t& a, int i) { return a[i]; }
+  // NK fragments covering the lane's D/G contiguous elements at p.
+  template <int NK>
+  __device__ static void load(frag_t (&f)[NK], const elem_t* p) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const uint4 raw = reinterpret_cast<const uint4*>(p)[kk];
+      __builtin_memcpy(&f[kk], &raw, 16);
+    }
+  }
+};
+
+struct TF64 {
+  using elem_t = float;
+  using frag_t = double;
+  using acc_t = doublex4;
+  static constexpr int M = 16, KS = 4, E = 1, NOUT = 4, G = 4;
+  __device__ static acc_t zero() { return acc_t{}; }
+  __device__ static acc_t mma(frag_t a, frag_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+  }
+  __device__ static int out_row(int i, int lane) { return (lane >> 4) * 4 + i; }
+  __device__ static float val(const acc_t& a, int i) { return (float)a[i]; }
+  template <int NK>
+  __device__ static void load(frag_t (&f)[NK], const elem_t* p) {
+#pragma unroll
+    for (int kk = 0; kk < NK; kk += 4) {
+      const float4 raw = reinterpret_cast<const float4*>(p)[kk / 4];
+      f[kk + 0] = raw.x;
+      f[kk + 1] = raw.y;
+      f[kk + 2] = raw.z;
+      f[kk + 3] = raw.w;
+    }
+  }
+};
+
+// Per-instance tiling: RB key row blocks per wave step in the stats pass,
+// CB key column blocks per wave step in the pooling pass.
+template <class T, int D> struct Tiling;
+template <> struct Tiling<TBf16, 64> { static constexpr int RB = 2, CB = 2; };
+template <> struct Tiling<TBf16, 128> { static constexpr int RB = 2, CB = 2; };
+template <> struct Tiling<TF64, 64> { static constexpr int RB = 2, CB = 1; };
+template <> struct Tiling<TF64, 128> { static constexpr int RB = 1, CB = 1; };
+
+struct TileInfo {
+  int seq, u, l, h, t, tpu, L, keys, key0;
+};
+
+__device__ inline TileInfo tile_info(const KvcDesc& Dsc, int tile) {
+  TileInfo ti;
+  int seq = 0;
+  while (seq + 1 < Dsc.n_seq && Dsc.tile_base[seq + 1] <= tile) ++seq;
+  ti.seq = seq;
+  ti.L = Dsc.L[seq];
+  ti.tpu = kvc_tiles_per_unit(ti.L);
+  const int rel = tile - Dsc.tile_base[seq];
+  const int uin = rel / ti.tpu;
+  ti.t = rel - uin * ti.tpu;
+  ti.u = seq * Dsc.upseq + uin;
+  ti.l = uin / Dsc.n_heads;
+  ti.h = uin - ti.l * Dsc.n_heads;
+  ti.keys = ti.L < KVC_TILE_KEYS ? ti.L : KVC_TILE_KEYS;
+  ti.key0 = ti.t * ti.keys;
+  return ti;
+}
+
+// Copy the unit's G*W window queries into LDS rows of stride QS elements.
+template <class T, int D, int QS>
+__device__ inline void stage_q(typename T::elem_t* sQ, const typename T::elem_t* qg, int gw) {
+  using elem_t = typename T::elem_t;
+  constexpr int CPR = D * (int)sizeof(elem_t) / 16;  // 16-byte chunks per row
+  for (int c = threadIdx.x; c < gw * CPR; c += SCORE_THREADS) {
+    const int row = c / CPR, col = c - row * CPR;
+    const uint4 v = reinterpret_cast<const uint4*>(qg + (size_t)row * D)[col];
+    *reinterpret_cast<uint4*>(sQ + row * QS + col * (16 / (int)sizeof(elem_t))) = v;
+  }
+}
+
+__device__ inline void merge_stat(float& m, float& z, float m2, float z2, float c) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) return;
+  const float a = (m == -INFINITY) ? 0.f : z * __builtin_amdgcn_exp2f((m - mm) * c);
+  const float b = (m2 == -INFINITY) ? 0.f : z2 * __builtin_amdgcn_exp2f((m2 - mm) * c);
+  m = mm;
+  z = a + b;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: per-query softmax statistics of each tile, folded per unit.
+// ---------------------------------------------------------------------------
+template <class T, int D>
+__global__ __launch_bounds__(SCORE_THREADS) void kvc_score_stats_kernel(
+    KvcDesc Dsc, const typename T::elem_t* __restrict__ q,
+    const typename T::elem_t* __restrict__ k, float2* __restrict__ partials,
+    float* __restrict__ lse2, uint32_t* __restrict__ counters) {
+  using elem_t = typename T::elem_t;
+  using frag_t = typename T::frag_t;
+  using acc_t = typename T::acc_t;
+  constexpr int M = T::M, G = T::G, NK = D / T::KS, RB = Tiling<T, D>::RB;
+  constexpr int QS = D + 16 / (int)sizeof(elem_t);
+  constexpr int MAXCB = KVC_MAX_GW / M;
+  constexpr int KW = RB * M;
+
+  __shared__ __attribute__((aligned(16))) elem_t sQ[KVC_MAX_GW * QS];
+  __shared__ float2 sStat[SCORE_WAVES][KVC_MAX_GW];
+  __shared__ int sLast;
+
+  const TileInfo ti = tile_info(Dsc, blockIdx.x);
+  const int gw = Dsc.gw, ncb = gw / M;
+  const float c = kLog2e / sqrtf((float)D);
+  const elem_t* qg =
+      q + ((size_t)((int64_t)ti.seq * Dsc.n_layers + ti.l) * Dsc.n_heads * Dsc.gqa +
+           (size_t)ti.h * Dsc.gqa) * Dsc.nwin * D;
+  const elem_t* ku = k + ti.l * Dsc.ks[0] + ti.h * Dsc.ks[1] + Dsc.tok0[ti.seq] * Dsc.ks[2];
+  stage_q<T, D, QS>(sQ, qg, gw);
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lrow = lane % M, lgrp = lane / M;
+  float m[MAXCB], z[MAXCB];
+#pragma unroll
+  for (int cb = 0; cb < MAXCB; ++cb) {
+    m[cb] = -INFINITY;
+    z[cb] = 0.f;
+  }
+
+  const int ngroups = ti.keys / KW;
+  for (int grp = wave; grp < ngroups; grp += SCORE_WAVES) {
+    const int kb = ti.key0 + grp * KW;
+    frag_t a[RB][NK];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      T::template load<NK>(a[rb], ku + (int64_t)(kb + rb * M + lrow) * Dsc.ks[2] + lgrp * (D / G));
+#pragma unroll
+    for (int cb = 0; cb < MAXCB; ++cb) {
+      if (cb >= ncb) break;
+      frag_t b[NK];
+      T::template load<NK>(b, sQ + (cb * M + lrow) * QS + lgrp * (D / G));
+      acc_t acc[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        acc[rb] = T::zero();
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) acc[rb] = T::mma(a[rb][kk], b[kk], acc[rb]);
+      }
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < T::NOUT; ++i) mloc = fmaxf(mloc, T::val(acc[rb], i));
+      const float mnew = fmaxf(m[cb], mloc);
+      const float nmc = -mnew * c;
+      float zz = (m[cb] == -INFINITY) ? 0.f : z[cb] * __builtin_amdgcn_exp2f((m[cb] - mnew) * c);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < T::NOUT; ++i)
+          zz += __builtin_amdgcn_exp2f(fmaf(T::val(acc[rb], i), c, nmc));
+      m[cb] = mnew;
+      z[cb] = zz;
+    }
+  }
+
+  // Fold the lane groups holding the same query, then the waves.
+#pragma unroll
+  for (int cb = 0; cb < MAXCB; ++cb) {
+    if (cb >= ncb) break;
+#pragma unroll
+    for (int o = M; o < 64; o <<= 1) {
+      const float m2 = __shfl_xor(m[cb], o);
+      const float z2 = __shfl_xor(z[cb], o);
+      merge_stat(m[cb], z[cb], m2, z2, c);
+    }
+    if (lgrp == 0) sStat[wave][cb * M + lrow] = make_float2(m[cb], z[cb]);
+  }
+  __syncthreads();
+  const int tile0 = blockIdx.x - ti.t;  // first tile of this unit
+  if (threadIdx.x < gw) {
+    float mm = -INFINITY, zz = 0.f;
+#pragma unroll
+    for (int w = 0; w < SCORE_WAVES; ++w) merge_stat(mm, zz, sStat[w][threadIdx.x].x, sStat[w][threadIdx.x].y, c);
+    partials[(size_t)blockIdx.x * gw + threadIdx.x] = make_float2(mm, zz);
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) sLast = (atomicAdd(&counters[ti.u], 1u) == (uint32_t)(ti.tpu - 1));
+  __syncthreads();
+  if (!sLast) return;
+  __threadfence();
+  if (threadIdx.x < gw) {
+    float mm = -INFINITY, zz = 0.f;
+    for (int t = 0; t < ti.tpu; ++t) {
+      const float2 p = partials[(size_t)(tile0 + t) * gw + threadIdx.x];
+      merge_stat(mm, zz, p.x, p.y, c);
+    }
+    lse2[(size_t)ti.u * gw + threadIdx.x] = mm * c + __builtin_amdgcn_logf(zz);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: probabilities pooled over the window queries and the GQA group.
+// ---------------------------------------------------------------------------
+template <class T, int D>
+__global__ __launch_bounds__(SCORE_THREADS) void kvc_score_pool_kernel(
+    KvcDesc Dsc, const typename T::elem_t* __restrict__ q,
+    const typename T::elem_t* __restrict__ k, const float* __restrict__ lse2,
+    float* __restrict__ s) {
+  using elem_t = typename T::elem_t;
+  using frag_t = typename T::frag_t;
+  using acc_t = typename T::acc_t;
+  constexpr int M = T::M, G = T::G, NK = D / T::KS, CB = Tiling<T, D>::CB;
+  constexpr int QS = D + 16 / (int)sizeof(elem_t);
+  constexpr int MAXRB = KVC_MAX_GW / M;
+  constexpr int KW = CB * M;
+
+  __shared__ __attribute__((aligned(16))) elem_t sQ[KVC_MAX_GW * QS];
+  __shared__ float sL[KVC_MAX_GW];
+
+  const TileInfo ti = tile_info(Dsc, blockIdx.x);
+  const int gw = Dsc.gw, nrb = gw / M;
+  const float c = kLog2e / sqrtf((float)D);
+  const float inv_gw = 1.0f / (float)gw;
+  const elem_t* qg =
+      q + ((size_t)((int64_t)ti.seq * Dsc.n_layers + ti.l) * Dsc.n_heads * Dsc.gqa +
+           (size_t)ti.h * Dsc.gqa) * Dsc.nwin * D;
+  const elem_t* ku = k + ti.l * Dsc.ks[0] + ti.h * Dsc.ks[1] + Dsc.tok0[ti.seq] * Dsc.ks[2];
+  stage_q<T, D, QS>(sQ, qg, gw);
+  if (threadIdx.x < gw) sL[threadIdx.x] = lse2[(size_t)ti.u * gw + threadIdx.x];
+  __syncthreads();
+
+  float* srow = s + Dsc.srow_base[ti.seq] + (int64_t)(ti.u - ti.seq * Dsc.upseq) * ti.L;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lrow = lane % M, lgrp = lane / M;
+  const int ngroups = ti.keys / KW;
+  for (int grp = wave; grp < ngroups; grp += SCORE_WAVES) {
+    const int kb = ti.key0 + grp * KW;
+    frag_t b[CB][NK];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      T::template load<NK>(b[cb], ku + (int64_t)(kb + cb * M + lrow) * Dsc.ks[2] + lgrp * (D / G));
+    float acc_s[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc_s[cb] = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < MAXRB; ++rb) {
+      if (rb >= nrb) break;
+      frag_t a[NK];
+      T::template load<NK>(a, sQ + (rb * M + lrow) * QS + lgrp * (D / G));
+      float nl[T::NOUT];
+#pragma unroll
+      for (int i = 0; i < T::NOUT; ++i) nl[i] = -sL[rb * M + T::out_row(i, lane)];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        acc_t acc = T::zero();
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) acc = T::mma(a[kk], b[cb][kk], acc);
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < T::NOUT; ++i) sum += __builtin_amdgcn_exp2f(fmaf(T::val(acc, i), c, nl[i]));
+        acc_s[cb] += sum;
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      float v = acc_s[cb];
+#pragma unroll
+      for (int o = M; o < 64; o <<= 1) v += __shfl_xor(v, o);
+      if (lgrp == 0) srow[kb + cb * M + lrow] = v * inv_gw;
+    }
+  }
+}
+
+size_t kvc_scores_workspace(const KvcDesc& D) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  return up(sizeof(uint32_t) * (size_t)D.n_units) +
+         up(sizeof(float) * (size_t)D.n_units * D.gw) +
+         up(sizeof(float2) * (size_t)D.total_tiles * D.gw);
+}
+
+template <class T, int Dm>
+static void launch_pair(const KvcDesc& D, const void* q, const void* k, float* s,
+                        float2* partials, float* lse2, uint32_t* counters, hipStream_t st) {
+  using elem_t = typename T::elem_t;
+  hipLaunchKernelGGL((kvc_score_stats_kernel<T, Dm>), dim3(D.total_tiles), dim3(SCORE_THREADS), 0,
+                     st, D, (const elem_t*)q, (const elem_t*)k, partials, lse2, counters);
+  hipLaunchKernelGGL((kvc_score_pool_kernel<T, Dm>), dim3(D.total_tiles), dim3(SCORE_THREADS), 0,
+                     st, D, (const elem_t*)q, (const elem_t*)k, (const float*)lse2, s);
+}
+
+hipError_t kvc_launch_scores(const KvcDesc& D, const void* q, const void* k, float* s,
+                             float2* partials, float* lse2, uint32_t* counters, hipStream_t st) {
+  if (D.dtype == 0 && D.d == 128) launch_pair<TBf16, 128>(D, q, k, s, partials, lse2, counters, st);
+  else if (D.dtype == 0 && D.d == 64) launch_pair<TBf16, 64>(D, q, k, s, partials, lse2, counters, st);
+  else if (D.dtype == 1 && D.d == 128) launch_pair<TF64, 128>(D, q, k, s, partials, lse2, counters, st);
+  else if (D.dtype == 1 && D.d == 64) launch_pair<TF64, 64>(D, q, k, s, partials, lse2, counters, st);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}

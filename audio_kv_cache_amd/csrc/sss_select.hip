@@ -1,0 +1,594 @@
+// sss_select.hip -- Spectral Score Smoothing (step 2) and per-head top-k
+// selection (step 4), one 1024-thread workgroup per unit.
+//
+// AudioKV article, section 2.2: F = rfft(s) of the length-L score row; the
+// cumulative energy E(k) = sum_{i<=k} |F_i|^2; the smallest k* with
+// E(k*) >= rho E(L/2); a low-pass mask keeping bins 0..k*; the blend
+// s_hat = (1 - alpha) s + alpha irfft(F masked).  The article runs the FFTs
+// with cuFFT; here they are hand-written for one gfx950 workgroup:
+//
+//  * The real length-L transform is a complex length-N = L/2 transform of
+//    z_m = s_{2m} + i s_{2m+1}, split into the real spectrum afterwards
+//    (and merged back before the inverse).
+//  * Complex FFTs use the Stockham autosort formulation (each radix-R pass
+//    reads x[j + r N/R] and writes its R outputs to (j - j mod Ns) R +
+//    j mod Ns + m Ns, natural order after the last pass; Govindaraju et al.,
+//    SC 2008).  Every thread keeps V = 8, 16 or 32 values in registers and
+//    runs radix-V butterflies on them; passes exchange data through one
+//    LDS buffer of N floats (real and imaginary parts in turn), padded by one
+//    float per 32 so strided passes do not collide on banks.  N = 32768 (L =
+//    65536) thus fits in 132 KiB of LDS without a multi-pass global variant.
+//  * E(k) is summed in fp64 from the fp32 spectrum; k* is the first bin
+//    whose prefix reaches rho E(N), found with a block scan.
+//
+// Selection (step 4): the b_u - w largest s_hat among positions [0, L-w)
+// plus the window [L-w, L), ascending.  s_hat is mapped to order-preserving
+// 32-bit keys (-0 folded into +0); a bitwise search for the largest key T
+// with count(key >= T) >= k finds the k-th largest value, positions equal to
+// T are taken from the lowest position upward, and a block scan writes the
+// kept positions in ascending order.
+#include "kvc_internal.h"
+
+#define SSS_T KVC_SSS_THREADS
+#define SSS_WAVES (SSS_T / 64)
+
+// e^{-2 pi i m / 32} for m = 0..15: cos and sin of 2 pi m / 32.
+static constexpr float kCos32[16] = {
+    1.0f, 0.98078528040323044913f, 0.92387953251128675613f, 0.83146961230254523708f,
+    0.70710678118654752440f, 0.55557023301960222474f, 0.38268343236508977173f,
+    0.19509032201612826785f, 0.0f, -0.19509032201612826785f, -0.38268343236508977173f,
+    -0.55557023301960222474f, -0.70710678118654752440f, -0.83146961230254523708f,
+    -0.92387953251128675613f, -0.98078528040323044913f};
+static constexpr float kSin32[16] = {
+    0.0f, 0.19509032201612826785f, 0.38268343236508977173f, 0.55557023301960222474f,
+    0.70710678118654752440f, 0.83146961230254523708f, 0.92387953251128675613f,
+    0.98078528040323044913f, 1.0f, 0.98078528040323044913f, 0.92387953251128675613f,
+    0.83146961230254523708f, 0.70710678118654752440f, 0.55557023301960222474f,
+    0.38268343236508977173f, 0.19509032201612826785f};
+
+__device__ __forceinline__ int phys(int a) { return a; }
+
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+  return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+
+template <int R>
+__host__ __device__ constexpr int bitrev(int i) {
+  int r = 0;
+  for (int b = 1; b < R; b <<= 1) {
+    r = (r << 1) | (i & 1);
+    i >>= 1;
+  }
+  return r;
+}
+
+// In-register forward DFT of size R (power of two <= 32), natural order.
+template <int R>
+__device__ __forceinline__ void dft_small(float2 (&v)[R]) {
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int j = bitrev<R>(i);
+    if (j > i) {
+      const float2 t = v[i];
+      v[i] = v[j];
+      v[j] = t;
+    }
+  }
+#pragma unroll
+  for (int len = 2; len <= R; len <<= 1) {
+#pragma unroll
+    for (int i = 0; i < R; i += len) {
+#pragma unroll
+      for (int m = 0; m < len / 2; ++m) {
+        const int ti = m * (32 / len);
+        const float2 w = make_float2(kCos32[ti], -kSin32[ti]);
+        const float2 a = v[i + m];
+        const float2 b = cmul(v[i + m + len / 2], w);
+        v[i + m] = make_float2(a.x + b.x, a.y + b.y);
+        v[i + m + len / 2] = make_float2(a.x - b.x, a.y - b.y);
+      }
+    }
+  }
+}
+
+// One Stockham pass of radix R on the V values a thread holds (V/R
+// butterflies j = t + b T, T = N/V threads).
+template <int V, int R, int T, int Ns>
+__device__ __forceinline__ void fft_pass(float (&re)[V], float (&im)[V], int t) {
+#pragma unroll
+  for (int b = 0; b < V / R; ++b) {
+    const int j = t + b * T;
+    int k = j & (Ns - 1);
+    // The forward and inverse transforms use the same twiddles; an empty asm
+    // keeps the compiler from carrying them across the whole kernel.
+    asm volatile("" : "+v"(k));
+    float2 v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = make_float2(re[b * R + r], im[b * R + r]);
+    if constexpr (Ns > 1) {
+      // w^r, w = e^{-2 pi i k / (Ns R)}: v_sin/v_cos (which take revolutions;
+      // k r / (Ns R) is an exact dyadic fraction) at every 8th power, the
+      // powers in between by one complex multiply each.
+      constexpr float inv = 1.0f / (float)(Ns * R);
+      const float x1 = (float)k * inv;
+      const float2 w1 = make_float2(__builtin_amdgcn_cosf(x1), -__builtin_amdgcn_sinf(x1));
+      float2 w = w1;
+#pragma unroll
+      for (int r = 1; r < R; ++r) {
+        if (r > 1) {
+          if (r % 8 == 0) {
+            const float x = (float)(k * r) * inv;
+            w = make_float2(__builtin_amdgcn_cosf(x), -__builtin_amdgcn_sinf(x));
+          } else {
+            w = cmul(w, w1);
+          }
+        }
+        v[r] = cmul(v[r], w);
+      }
+    }
+    dft_small<R>(v);
+#pragma unroll
+    for (int m = 0; m < R; ++m) {
+      re[b * R + m] = v[m].x;
+      im[b * R + m] = v[m].y;
+    }
+  }
+}
+
+// Position of value slot s in the input of a radix-R pass, and in the output
+// of a radix-R pass whose sub-transforms have length Ns.
+template <int R, int T, int N>
+__device__ __forceinline__ int in_index(int s, int t) {
+  return t + (s / R) * T + (s % R) * (N / R);
+}
+template <int R, int T, int Ns>
+__device__ __forceinline__ int out_index(int s, int t) {
+  const int j = t + (s / R) * T;
+  const int k = j & (Ns - 1);
+  return (j - k) * R + k + (s % R) * Ns;
+}
+
+// Exchange through LDS: the value in slot s moves from position widx(s) to
+// the slot whose position is ridx(s).  Real parts first, then imaginary
+// parts.  One optional extra value per thread is written at position xw and
+// one read from position xr (-1: none).
+struct Extra {
+  int xw, xr;
+  float wre, wim, rre, rim;
+};
+
+template <int V, class WF, class RF>
+__device__ __forceinline__ void exchange(float (&re)[V], float (&im)[V], float* lds, bool act,
+                                         WF widx, RF ridx, Extra& x) {
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < V; ++s) lds[phys(widx(s))] = re[s];
+    if (x.xw >= 0) lds[phys(x.xw)] = x.wre;
+  }
+  __syncthreads();
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < V; ++s) re[s] = lds[phys(ridx(s))];
+    if (x.xr >= 0) x.rre = lds[phys(x.xr)];
+  }
+  __syncthreads();
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < V; ++s) lds[phys(widx(s))] = im[s];
+    if (x.xw >= 0) lds[phys(x.xw)] = x.wim;
+  }
+  __syncthreads();
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < V; ++s) im[s] = lds[phys(ridx(s))];
+    if (x.xr >= 0) x.rim = lds[phys(x.xr)];
+  }
+  __syncthreads();
+}
+
+// Forward complex FFT of length N = T V, passes from sub-length Ns on.  On
+// entry slot s holds x[in_index<V, T, N>(s)]; on exit slot s holds
+// X[ridx_final(s)] (plus the extra read of `xf`, if any).
+template <int N, int V, int Ns, class RF>
+__device__ __forceinline__ void fft_stages(float (&re)[V], float (&im)[V], float* lds, int t,
+                                           bool act, RF ridx_final, Extra& xf) {
+  constexpr int T = N / V;
+  constexpr int R = (N / Ns) < V ? (N / Ns) : V;
+  constexpr int Nn = Ns * R;
+  if (act) fft_pass<V, R, T, Ns>(re, im, t);
+  auto wf = [&](int s) { return out_index<R, T, Ns>(s, t); };
+  if constexpr (Nn >= N) {
+    exchange<V>(re, im, lds, act, wf, ridx_final, xf);
+  } else {
+    constexpr int R2 = (N / Nn) < V ? (N / Nn) : V;
+    Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
+    exchange<V>(re, im, lds, act, wf, [&](int s) { return in_index<R2, T, N>(s, t); }, none);
+    fft_stages<N, V, Nn>(re, im, lds, t, act, ridx_final, xf);
+  }
+}
+
+// Block-wide exclusive scan (sum) over all SSS_T threads; *total gets the sum.
+template <class X>
+__device__ __forceinline__ X block_scan(X v, X* sw, X* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  X incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const X y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) sw[w] = incl;
+  __syncthreads();
+  X before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < SSS_WAVES; ++i) {
+    const X x = sw[i];
+    if (i < w) before += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + incl - v;
+}
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f == 0.0f) f = 0.0f;  // -0 and +0 are equal
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+struct SssShared {
+  double sd[SSS_WAVES];
+  int si[SSS_WAVES];
+  int kstar;
+};
+
+// e^{i pi x} as (cos, sin); v_sin/v_cos take revolutions (x/2).
+__device__ __forceinline__ float2 cispi(float x) {
+  const float rev = 0.5f * x;
+  return make_float2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+}
+
+// ---------------------------------------------------------------------------
+// Smoothing of one unit's row.  On return re[s], im[s] hold s_hat at
+// positions 2(tV + s) and 2(tV + s) + 1.
+// ---------------------------------------------------------------------------
+template <int N, int V>
+__device__ __forceinline__ void smooth_unit(const KvcDesc& D, int mode, int u, const float* srow,
+                            float* shrow, int32_t* kstar_out, float (&re)[V], float (&im)[V],
+                            float* lds, SssShared& sh, int t, bool act) {
+  constexpr int T = N / V;
+  constexpr int L = 2 * N;
+  const int hv = V / 2;
+  // z_m = s_{2m} + i s_{2m+1}, in the order of the first radix-V pass.
+  if (act) {
+    const float2* z = reinterpret_cast<const float2*>(srow);
+#pragma unroll
+    for (int s = 0; s < V; ++s) {
+      const float2 v = z[in_index<V, T, N>(s, t)];
+      re[s] = v.x;
+      im[s] = v.y;
+    }
+  }
+  if (t == 0) sh.kstar = N;
+
+  // Forward FFT; end in the pair layout: slot s < V/2 holds Z_k with
+  // k = t V/2 + s, slot V/2 + s holds Z_{(N - k) mod N}; thread 0 also reads
+  // the self-paired bin N/2.
+  auto pair_idx = [&](int s) {
+    const int k = t * hv + (s % hv);
+    return s < hv ? k : ((N - k) & (N - 1));
+  };
+  Extra xf{-1, (t == 0) ? N / 2 : -1, 0.f, 0.f, 0.f, 0.f};
+  fft_stages<N, V, 1>(re, im, lds, t, act, pair_idx, xf);
+
+  // Real spectrum: F_k = A_k + e^{-2 pi i k/L} B_k with
+  // A_k = (Z_k + conj Z_{N-k})/2, B_k = (Z_k - conj Z_{N-k})/(2i); the mirror
+  // bin N-k uses the same pair.  Energies |F|^2 in fp64.
+  double lo_sum = 0.0, hi_sum = 0.0, pmid = 0.0;
+  float2 fmid = make_float2(0.f, 0.f);
+  if (act) {
+    const float2 Wstep = cispi(-2.0f / (float)L);
+    float2 W = make_float2(1.f, 0.f);
+#pragma unroll
+    for (int s = 0; s < hv; ++s) {
+      const int k = t * hv + s;
+      const float2 zk = make_float2(re[s], im[s]);
+      const float2 zm = make_float2(re[hv + s], im[hv + s]);
+      const float2 A = make_float2(0.5f * (zk.x + zm.x), 0.5f * (zk.y - zm.y));
+      const float2 B = make_float2(0.5f * (zk.y + zm.y), -0.5f * (zk.x - zm.x));
+      if (s % 8 == 0) W = cispi(-2.0f * (float)k / (float)L);
+      else W = cmul(W, Wstep);
+      const float2 WB = cmul(W, B);
+      const float2 Fk = make_float2(A.x + WB.x, A.y + WB.y);
+      // mirror: A' = conj(A), B' = (Z_{N-k} - conj Z_k)/(2i) = conj(B)... with
+      // twiddle e^{-2 pi i (N-k)/L} = -conj(W)
+      const float2 Bm = make_float2(B.x, -B.y);
+      const float2 Wm = make_float2(-W.x, W.y);
+      const float2 WBm = cmul(Wm, Bm);
+      const float2 Fm = make_float2(A.x + WBm.x, -A.y + WBm.y);
+      re[s] = Fk.x;
+      im[s] = Fk.y;
+      re[hv + s] = Fm.x;
+      im[hv + s] = Fm.y;
+      lo_sum += (double)Fk.x * Fk.x + (double)Fk.y * Fk.y;
+      hi_sum += (double)Fm.x * Fm.x + (double)Fm.y * Fm.y;
+    }
+    if (t == 0) {
+      fmid = make_float2(xf.rre, -xf.rim);  // F_{N/2} = conj(Z_{N/2})
+      pmid = (double)fmid.x * fmid.x + (double)fmid.y * fmid.y;
+    }
+  }
+  // Natural bin order: lower chunks (t ascending), bin N/2, upper chunks
+  // (t descending).  Prefix energies from two block scans.
+  double lo_tot, hi_tot;
+  const double lo_before = block_scan<double>(lo_sum, sh.sd, &lo_tot);
+  const double hi_incl = block_scan<double>(hi_sum, sh.sd, &hi_tot) + hi_sum;
+  if (t == 0) sh.sd[0] = pmid;
+  __syncthreads();
+  const double pm = sh.sd[0];
+  __syncthreads();
+  const double total = lo_tot + pm + hi_tot;
+  const double target = (double)D.rho * total;
+  if (act) {
+    // Recompute the bin energies below rather than keeping 2V doubles live.
+#pragma unroll
+    for (int s = 0; s < V; ++s) asm volatile("" : "+v"(re[s]), "+v"(im[s]));
+    int cand = N;
+    double e = lo_before;
+#pragma unroll
+    for (int s = 0; s < hv; ++s) {
+      e += (double)re[s] * re[s] + (double)im[s] * im[s];
+      if (e >= target && cand == N) cand = t * hv + s;
+    }
+    if (t == 0 && cand == N && lo_tot + pm >= target) cand = N / 2;
+    if (cand == N) {
+      e = lo_tot + pm + (hi_tot - hi_incl);
+#pragma unroll
+      for (int s = hv - 1; s >= 0; --s) {
+        e += (double)re[hv + s] * re[hv + s] + (double)im[hv + s] * im[hv + s];
+        const int kk = N - (t * hv + s);
+        if (e >= target && cand == N) cand = kk;
+      }
+    }
+    if (cand < N) atomicMin(&sh.kstar, cand);
+  }
+  __syncthreads();
+  const int kstar = sh.kstar;
+  if ((mode & 4) && t == 0) kstar_out[u] = kstar;
+
+  // Mask bins above k*, then merge back to the half-length sequence:
+  // Z'_k = A'_k + i B'_k, A'_k = (F_k + conj F_{N-k})/2,
+  // B'_k = e^{+2 pi i k/L} (F_k - conj F_{N-k})/2.
+  Extra xi{-1, -1, 0.f, 0.f, 0.f, 0.f};
+  if (act) {
+    const float2 Wstep = cispi(2.0f / (float)L);
+    float2 W = make_float2(1.f, 0.f);
+#pragma unroll
+    for (int s = 0; s < hv; ++s) {
+      const int k = t * hv + s;
+      const int km = N - k;  // N when k == 0
+      const float2 Fk = (k <= kstar) ? make_float2(re[s], im[s]) : make_float2(0.f, 0.f);
+      const float2 Fm =
+          (km <= kstar) ? make_float2(re[hv + s], im[hv + s]) : make_float2(0.f, 0.f);
+      const float2 A = make_float2(0.5f * (Fk.x + Fm.x), 0.5f * (Fk.y - Fm.y));
+      const float2 Dd = make_float2(0.5f * (Fk.x - Fm.x), 0.5f * (Fk.y + Fm.y));
+      if (s % 8 == 0) W = cispi(2.0f * (float)k / (float)L);
+      else W = cmul(W, Wstep);
+      const float2 B = cmul(W, Dd);
+      // Z'_k = A + i B
+      re[s] = A.x - B.y;
+      im[s] = A.y + B.x;
+      // Z'_{N-k}: A'' = conj(A), B'' = e^{+2 pi i (N-k)/L} (F_{N-k} - conj F_k)/2
+      //         = (-conj W) * (-conj Dd) = conj(W Dd) = conj(B)
+      re[hv + s] = A.x - (-B.y);
+      im[hv + s] = -A.y + B.x;
+    }
+    if (t == 0) {
+      // Z'_{N/2} = conj(F'_{N/2})
+      const bool keep = (N / 2) <= kstar;
+      xi.xw = N / 2;
+      xi.wre = keep ? fmid.x : 0.f;
+      xi.wim = keep ? -fmid.y : 0.f;
+    }
+  }
+  // To the inverse's first-pass order.  Slot V/2 of thread 0 (k = 0) maps to
+  // index 0 again and carries the same value as slot 0.
+  exchange<V>(re, im, lds, act, pair_idx, [&](int s) { return in_index<V, T, N>(s, t); }, xi);
+
+  // Inverse FFT as conj(FFT(conj(x))) / N, ending in natural chunks
+  // (slot s holds index tV + s).
+#pragma unroll
+  for (int s = 0; s < V; ++s) im[s] = -im[s];
+  Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
+  fft_stages<N, V, 1>(re, im, lds, t, act, [&](int s) { return t * V + s; }, none);
+
+  // Blend with the raw row: s_hat = (1 - alpha) s + alpha lowpass.
+  const float invN = 1.0f / (float)N;
+  const float a = D.alpha, oma = 1.0f - D.alpha;
+  if (act) {
+    const float2* sr = reinterpret_cast<const float2*>(srow);
+#pragma unroll
+    for (int s = 0; s < V; ++s) {
+      const float2 sv = sr[t * V + s];
+      const float lpe = re[s] * invN, lpo = -im[s] * invN;
+      re[s] = oma * sv.x + a * lpe;
+      im[s] = oma * sv.y + a * lpo;
+    }
+    if (mode & 4) {
+      float2* o = reinterpret_cast<float2*>(shrow);
+#pragma unroll
+      for (int s = 0; s < V; ++s) o[t * V + s] = make_float2(re[s], im[s]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Selection for one unit from s_hat held as in smooth_unit's output.
+// ---------------------------------------------------------------------------
+template <int N, int V>
+__device__ __forceinline__ void select_unit(const KvcDesc& D, int u, float (&re)[V], float (&im)[V],
+                            const int32_t* budgets, const int64_t* offsets, int32_t* idx_out,
+                            SssShared& sh, int t, bool act) {
+  constexpr int L = 2 * N;
+  const int w = D.window;
+  const int ncand = L - w;
+  const int b = budgets[u];
+  const int k = b - w;
+  const int64_t off = offsets[u];
+  // Order-preserving keys, stored in place of the values: position
+  // p0 + 2s is re[s], p0 + 2s + 1 is im[s].
+#pragma unroll
+  for (int s = 0; s < V; ++s) {
+    re[s] = __uint_as_float(order_key(re[s]));
+    im[s] = __uint_as_float(order_key(im[s]));
+  }
+#define KEY(s) __float_as_uint(((s) & 1) ? im[(s) >> 1] : re[(s) >> 1])
+  const int p0 = 2 * V * t;  // first position held by this thread
+
+  // Largest T with #{key >= T} >= k, bit by bit from the top.
+  uint32_t thr = 0;
+  int tot;
+  if (k > 0 && k < ncand) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = thr | (1u << bit);
+      int cnt = 0;
+      if (act) {
+#pragma unroll
+        for (int s = 0; s < 2 * V; ++s) cnt += (p0 + s < ncand) && (KEY(s) >= c);
+      }
+      block_scan<int>(cnt, sh.si, &tot);
+      if (tot >= k) thr = c;
+    }
+  }
+  // Counts above and at the threshold.
+  int ngt = 0, neq = 0;
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < 2 * V; ++s) {
+      const bool cd = p0 + s < ncand;
+      ngt += cd && KEY(s) > thr;
+      neq += cd && KEY(s) == thr;
+    }
+  }
+  int gt_total, eq_total;
+  const int eq_before = block_scan<int>(neq, sh.si, &eq_total);
+  block_scan<int>(ngt, sh.si, &gt_total);
+  (void)eq_total;
+  const bool take_all = k >= ncand;
+  const bool take_none = k <= 0;
+  const int need = k - gt_total;  // positions equal to thr to keep, lowest first
+
+  int nsel = 0, er = eq_before;
+  uint32_t selmask_lo = 0, selmask_hi = 0;
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < 2 * V; ++s) {
+      const int p = p0 + s;
+      bool sel;
+      if (p >= ncand) sel = true;
+      else if (take_all) sel = true;
+      else if (take_none) sel = false;
+      else if (KEY(s) > thr) sel = true;
+      else if (KEY(s) == thr) sel = (er++ < need);
+      else sel = false;
+      if (sel) {
+        if (s < 32) selmask_lo |= 1u << s;
+        else selmask_hi |= 1u << (s - 32);
+        ++nsel;
+      }
+    }
+  }
+  int nsel_total;
+  const int base = block_scan<int>(nsel, sh.si, &nsel_total);
+  if (act) {
+    int o = 0;
+#pragma unroll
+    for (int s = 0; s < 2 * V; ++s) {
+      const bool sel = (s < 32) ? ((selmask_lo >> s) & 1u) : ((selmask_hi >> (s - 32)) & 1u);
+      // (base + o < b always holds for finite input; the guard keeps a
+      // non-finite row from writing past the unit's segment)
+      if (sel && base + o < b) idx_out[off + base + (o++)] = p0 + s;
+    }
+  }
+#undef KEY
+}
+
+// Values per thread for a half-length N: at most 1024 threads, at least 8
+// values each.
+__host__ __device__ constexpr int kvc_sss_v(int N) {
+  return N >= 32 * SSS_T ? 32 : N >= 16 * SSS_T ? 16 : 8;
+}
+
+template <int LOG2N>
+__global__ __launch_bounds__(SSS_T) void kvc_sss_select_kernel(
+    KvcDesc D, int mode, int unit0, const float* __restrict__ s_in, float* __restrict__ s_hat_out,
+    int32_t* __restrict__ kstar_out, const int32_t* __restrict__ budgets,
+    const int64_t* __restrict__ offsets, int32_t* __restrict__ idx_out) {
+  constexpr int N = 1 << LOG2N;
+  constexpr int L = 2 * N;
+  constexpr int V = kvc_sss_v(N);
+  constexpr int T = N / V;
+  __shared__ float lds[N];
+  __shared__ SssShared sh;
+  // Units in descending-L order (sequences sorted on the host); this launch
+  // covers the ones of length L, starting at position unit0.
+  const int pos = unit0 + blockIdx.x;
+  const int rank = pos / D.upseq;
+  const int within = pos - rank * D.upseq;
+  const int seq = D.seq_order[rank];
+  const int u = seq * D.upseq + within;
+  const int64_t row = D.srow_base[seq] + (int64_t)within * L;
+  const int t = threadIdx.x;
+  const bool act = t < T;
+  float re[V], im[V];
+  if (mode & 1) {
+    smooth_unit<N, V>(D, mode, u, s_in + row, s_hat_out ? s_hat_out + row : nullptr, kstar_out,
+                      re, im, lds, sh, t, act);
+  } else if (act) {
+    const float2* z = reinterpret_cast<const float2*>(s_in + row);
+#pragma unroll
+    for (int s = 0; s < V; ++s) {
+      const float2 v = z[t * V + s];
+      re[s] = v.x;
+      im[s] = v.y;
+    }
+  }
+  if (mode & 2) select_unit<N, V>(D, u, re, im, budgets, offsets, idx_out, sh, t, act);
+}
+
+hipError_t kvc_launch_sss_select(const KvcDesc& D, int mode, const float* s_in,
+                                 float* s_hat_out, int32_t* kstar_out, const int32_t* budgets,
+                                 const int64_t* offsets, int32_t* idx_out, hipStream_t st) {
+  // Sequences are ordered by descending L, so each length is a contiguous
+  // range of unit positions: one launch per distinct length.
+  int r = 0;
+  while (r < D.n_seq) {
+    const int L = D.L[D.seq_order[r]];
+    int r2 = r;
+    while (r2 < D.n_seq && D.L[D.seq_order[r2]] == L) ++r2;
+    const int unit0 = r * D.upseq, nunits = (r2 - r) * D.upseq;
+    void (*kern)(KvcDesc, int, int, const float*, float*, int32_t*, const int32_t*,
+                 const int64_t*, int32_t*) = nullptr;
+    switch (L) {
+      case 64: kern = kvc_sss_select_kernel<5>; break;
+      case 128: kern = kvc_sss_select_kernel<6>; break;
+      case 256: kern = kvc_sss_select_kernel<7>; break;
+      case 512: kern = kvc_sss_select_kernel<8>; break;
+      case 1024: kern = kvc_sss_select_kernel<9>; break;
+      case 2048: kern = kvc_sss_select_kernel<10>; break;
+      case 4096: kern = kvc_sss_select_kernel<11>; break;
+      case 8192: kern = kvc_sss_select_kernel<12>; break;
+      case 16384: kern = kvc_sss_select_kernel<13>; break;
+      case 32768: kern = kvc_sss_select_kernel<14>; break;
+      case 65536: kern = kvc_sss_select_kernel<15>; break;
+      default: return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL(kern, dim3(nunits), dim3(SSS_T), 0, st, D, mode, unit0, s_in, s_hat_out,
+                       kstar_out, budgets, offsets, idx_out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    r = r2;
+  }
+  return hipSuccess;
+}

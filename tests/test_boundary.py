@@ -1,0 +1,109 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+entry point include/kvc.h declares, sizes problems on the host, and rejects
+invalid problems before launching anything."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from audio_kv_cache_amd import _lib as C
+from audio_kv_cache_amd import api
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kvc.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = C.lib()
+    names = declared_symbols()
+    assert set(names) == set(C.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = C.lib()
+    for s in range(6):
+        assert L.kvc_status_str(s)
+    assert L.kvc_status_str(99) == b"unknown status"
+    assert L.kvc_last_hip_error() == 0
+
+
+def spec(**kw):
+    base = dict(n_layers=48, n_kv_heads=4, gqa=8, head_dim=128, seq_lens=[32768],
+                retention=0.4, dtype="bf16")
+    base.update(kw)
+    return api.Spec(**base)
+
+
+def test_plan_total_rows_closed_form():
+    for lens, ret in [([32768], 0.4), ([8192], 0.6), ([1024], 0.6), ([65536], 0.2),
+                      ([4096, 32768, 8192], [0.2, 0.55, 1.0])]:
+        sp = spec(seq_lens=lens, retention=ret)
+        rows, ws = api.kvc_plan(sp, api.Params())
+        rets = np.broadcast_to(np.asarray(ret, float), (len(lens),))
+        want = sum(48 * 4 * min(math.floor(r * L), L) for L, r in zip(lens, rets))
+        assert rows == want
+        # score rows + per-unit statistics fit in the workspace
+        assert ws >= 4 * 48 * 4 * sum(lens)
+
+
+def status(sp, prm=None, **ptrs):
+    """Call kvc_compress with dummy (never dereferenced) pointers."""
+    L = C.lib()
+    prm = prm or api.Params()
+    fake = ctypes.c_void_p(1 << 20)   # 16-byte and 256-byte aligned, never touched
+    args = dict(q=fake, k=fake, v=fake, S=fake, ko=fake, vo=fake, idx=fake, off=fake,
+                b=fake, ws=fake)
+    args.update(ptrs)
+    return L.kvc_compress(ctypes.byref(sp.c()), ctypes.byref(prm.c()), args["q"], args["k"],
+                          args["v"], args["S"], args["ko"], args["vo"], args["idx"],
+                          args["off"], args["b"], args["ws"], ptrs.get("ws_bytes", 0), None)
+
+
+def test_invalid_problems_rejected_before_launch():
+    assert status(spec(seq_lens=[3000])) == C.KVC_ERR_UNSUPPORTED          # not a power of two
+    assert status(spec(seq_lens=[131072])) == C.KVC_ERR_UNSUPPORTED        # too long
+    assert status(spec(seq_lens=[32])) == C.KVC_ERR_UNSUPPORTED            # too short
+    assert status(spec(head_dim=96)) == C.KVC_ERR_UNSUPPORTED
+    assert status(spec(n_window=5)) == C.KVC_ERR_UNSUPPORTED               # G*W = 40, not a multiple of 32
+    assert status(spec(gqa=9)) == C.KVC_ERR_UNSUPPORTED                    # G*W = 288 > 256
+    assert status(spec(seq_lens=[64], retention=0.5)) == C.KVC_ERR_BUDGET  # w + r > kbar
+    assert status(spec(retention=0.0)) == C.KVC_ERR_INVALID_ARG
+    assert status(spec(retention=1.5)) == C.KVC_ERR_INVALID_ARG
+    assert status(spec(), api.Params(alpha=1.5)) == C.KVC_ERR_INVALID_ARG
+    assert status(spec(), api.Params(rho=0.0)) == C.KVC_ERR_INVALID_ARG
+    assert status(spec(), api.Params(base_ratio=-0.1)) == C.KVC_ERR_INVALID_ARG
+    assert status(spec(), api.Params(window=-1)) == C.KVC_ERR_INVALID_ARG
+    assert status(spec(), q=None) == C.KVC_ERR_INVALID_ARG
+    assert status(spec(), ko=ctypes.c_void_p((1 << 20) + 8)) == C.KVC_ERR_INVALID_ARG
+    assert status(spec(), ws=ctypes.c_void_p((1 << 20) + 64)) == C.KVC_ERR_INVALID_ARG
+    assert status(spec(k_stride=(0, 0, 100))) == C.KVC_ERR_INVALID_ARG    # rows not 16-B aligned
+    assert status(spec(k_stride=(0, 0, 64))) == C.KVC_ERR_INVALID_ARG     # stride < head_dim
+    assert status(spec()) == C.KVC_ERR_WORKSPACE                           # 0 bytes given
+    assert C.lib().kvc_last_hip_error() == 0
+
+
+def test_gqa_96_window_queries_is_supported():
+    # 3 * 32 = 96 window queries: a multiple of 32, so it is accepted.
+    sp = spec(gqa=3)
+    assert api.kvc_plan(sp, api.Params())[0] > 0
+
+
+def test_too_many_sequences_and_units():
+    assert status(spec(seq_lens=[64] * 65, retention=0.9,
+                       n_layers=1, n_kv_heads=1)) == C.KVC_ERR_UNSUPPORTED
+    assert status(spec(n_layers=1025, n_kv_heads=4)) == C.KVC_ERR_UNSUPPORTED
+
+
+def test_full_retention_plans_every_row():
+    sp = spec(seq_lens=[1024], retention=1.0, n_layers=2, n_kv_heads=2)
+    assert api.kvc_plan(sp, api.Params())[0] == 4 * 1024
