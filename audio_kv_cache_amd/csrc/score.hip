@@ -65,7 +65,8 @@ struct TF64 {
   __device__ static acc_t mma(frag_t a, frag_t b, acc_t c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
   }
-  __device__ static int out_row(int i, int lane) { return (lane >> 4) * 4 + i; }
+  // (measured: element i of lane l is row 4 i + l / 16)
+  __device__ static int out_row(int i, int lane) { return 4 * i + (lane >> 4); }
   __device__ static float val(const acc_t& a, int i) { return (float)a[i]; }
   template <int NK>
   __device__ static void load(frag_t (&f)[NK], const elem_t* p) {
