@@ -22,20 +22,15 @@
 
 __global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
     KvcDesc D, const float* __restrict__ S, int32_t* __restrict__ budgets,
-    int64_t* __restrict__ offsets, uint32_t* __restrict__ zero_ptr, int zero_count) {
-  // Side job: clear the score kernels' per-unit arrival counters.
-  for (int i = blockIdx.x * BUDGET_THREADS + threadIdx.x; i < zero_count;
-       i += gridDim.x * BUDGET_THREADS)
-    zero_ptr[i] = 0u;
-
+    int64_t* __restrict__ offsets) {
   __shared__ double q[KVC_MAX_UNITS_PER_SEQ];
+  __shared__ float sS[KVC_MAX_UNITS_PER_SEQ];
   __shared__ int32_t extra[KVC_MAX_UNITS_PER_SEQ];
   __shared__ uint8_t active[KVC_MAX_UNITS_PER_SEQ];
   __shared__ double s_sum;
   __shared__ int64_t s_R;
   __shared__ int s_nA, s_capped;
   __shared__ int64_t s_wsum[BUDGET_THREADS / 64];
-  __shared__ int s_wcnt[BUDGET_THREADS / 64];
 
   const int seq = blockIdx.x;
   const int n = D.upseq;
@@ -59,6 +54,7 @@ __global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
   for (int u = tid; u < n; u += BUDGET_THREADS) {
     active[u] = 1;
     extra[u] = 0;
+    sS[u] = S[u];
   }
   if (tid == 0) s_R = (int64_t)n * kbar - (int64_t)n * fixed;
   __syncthreads();
@@ -70,7 +66,7 @@ __global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
       int nA = 0;
       for (int u = 0; u < n; ++u)
         if (active[u]) {
-          acc += (double)S[u];
+          acc += (double)sS[u];
           ++nA;
         }
       s_sum = acc;
@@ -84,7 +80,7 @@ __global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
     int my_capped = 0;
     for (int u = tid; u < n; u += BUDGET_THREADS) {
       if (!active[u]) continue;
-      const double qu = sumA > 0.0 ? (Rd * (double)S[u]) / sumA : Rd / (double)nA;
+      const double qu = sumA > 0.0 ? (Rd * (double)sS[u]) / sumA : Rd / (double)nA;
       q[u] = qu;
       if (qu >= (double)cap) ++my_capped;
     }
@@ -155,21 +151,8 @@ __global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
 }
 
 hipError_t kvc_launch_budget(const KvcDesc& D, const float* S, int32_t* budgets,
-                             int64_t* offsets, uint32_t* zero_ptr, int zero_count,
-                             hipStream_t st) {
+                             int64_t* offsets, hipStream_t st) {
   hipLaunchKernelGGL(kvc_budget_kernel, dim3(D.n_seq), dim3(BUDGET_THREADS), 0, st, D, S,
-                     budgets, offsets, zero_ptr, zero_count);
-  return hipGetLastError();
-}
-
-__global__ void kvc_fill_u32_kernel(uint32_t* p, int count, uint32_t value) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) p[i] = value;
-}
-
-hipError_t kvc_launch_fill_u32(uint32_t* p, int count, uint32_t value, hipStream_t st) {
-  if (count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kvc_fill_u32_kernel, dim3((count + 255) / 256), dim3(256), 0, st, p,
-                     count, value);
+                     budgets, offsets);
   return hipGetLastError();
 }

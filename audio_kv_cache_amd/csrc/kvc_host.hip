@@ -140,10 +140,9 @@ extern "C" kvc_status kvc_plan(const kvc_problem* prob, const kvc_params* params
   return KVC_OK;
 }
 
-// Workspace layout: [counters | lse2 | partials] (kvc_scores_workspace) then
-// the score rows.
+// Workspace layout: [lse2 | partials] (kvc_scores_workspace) then the score
+// rows.
 struct Carve {
-  uint32_t* counters;
   float* lse2;
   float2* partials;
   float* srows;
@@ -152,8 +151,6 @@ struct Carve {
 static Carve carve(const KvcDesc& D, void* ws) {
   char* p = (char*)ws;
   Carve c;
-  c.counters = (uint32_t*)p;
-  p += up256(sizeof(uint32_t) * (size_t)D.n_units);
   c.lse2 = (float*)p;
   p += up256(sizeof(float) * (size_t)D.n_units * D.gw);
   c.partials = (float2*)p;
@@ -183,9 +180,9 @@ extern "C" kvc_status kvc_compress(const kvc_problem* prob, const kvc_params* pa
   hipStream_t s = (hipStream_t)stream;
   const Carve c = carve(D, workspace);
   hipError_t e;
-  e = kvc_launch_budget(D, head_scores, budgets, seg_offsets, c.counters, D.n_units, s);
+  e = kvc_launch_budget(D, head_scores, budgets, seg_offsets, s);
   if (e != hipSuccess) return hip_status(e);
-  e = kvc_launch_scores(D, q_window, k, c.srows, c.partials, c.lse2, c.counters, s);
+  e = kvc_launch_scores(D, q_window, k, c.srows, c.partials, c.lse2, s);
   if (e != hipSuccess) return hip_status(e);
   e = kvc_launch_sss_select(D, 1 | 2, c.srows, nullptr, nullptr, budgets, seg_offsets, idx_out, s);
   if (e != hipSuccess) return hip_status(e);
@@ -206,9 +203,7 @@ extern "C" kvc_status kvc_scores(const kvc_problem* prob, const kvc_params* para
   if (workspace_bytes < kvc_scores_workspace(D)) return KVC_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const Carve c = carve(D, workspace);
-  hipError_t e = kvc_launch_fill_u32(c.counters, D.n_units, 0u, s);
-  if (e != hipSuccess) return hip_status(e);
-  e = kvc_launch_scores(D, q_window, k, s_out, c.partials, c.lse2, c.counters, s);
+  const hipError_t e = kvc_launch_scores(D, q_window, k, s_out, c.partials, c.lse2, s);
   return hip_status(e);
 }
 
@@ -231,8 +226,7 @@ extern "C" kvc_status kvc_budget(const kvc_problem* prob, const kvc_params* para
   kvc_status st = make_desc(prob, params, &D);
   if (st != KVC_OK) return st;
   if (!head_scores || !budgets || !seg_offsets) return KVC_ERR_INVALID_ARG;
-  return hip_status(kvc_launch_budget(D, head_scores, budgets, seg_offsets, nullptr, 0,
-                                      (hipStream_t)stream));
+  return hip_status(kvc_launch_budget(D, head_scores, budgets, seg_offsets, (hipStream_t)stream));
 }
 
 extern "C" kvc_status kvc_select(const kvc_problem* prob, const kvc_params* params,

@@ -45,12 +45,9 @@ __host__ __device__ inline int kvc_tiles_per_unit(int L) {
 
 // Kernel launchers (defined next to each kernel).
 hipError_t kvc_launch_budget(const KvcDesc& D, const float* S, int32_t* budgets,
-                             int64_t* offsets, uint32_t* zero_ptr, int zero_count,
-                             hipStream_t st);
-hipError_t kvc_launch_fill_u32(uint32_t* p, int count, uint32_t value, hipStream_t st);
+                             int64_t* offsets, hipStream_t st);
 hipError_t kvc_launch_scores(const KvcDesc& D, const void* q, const void* k,
-                             float* s, float2* partials, float* lse2,
-                             uint32_t* counters, hipStream_t st);
+                             float* s, float2* partials, float* lse2, hipStream_t st);
 // mode bit 0: smooth (else read s_hat from s_in); bit 1: select;
 // bit 2: export s_hat and kstar.
 hipError_t kvc_launch_sss_select(const KvcDesc& D, int mode, const float* s_in,

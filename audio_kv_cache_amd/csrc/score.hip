@@ -8,8 +8,8 @@
 // the softmax taken over all L audio keys.
 //
 // Two passes over K, both GEMM-shaped (Q [G W, d] x K^T [d, keys]):
-//   stats  per query (max, sum of exp) of each 1024-key tile; the last tile of
-//          a unit to finish folds the unit's partials into LSE (log2 units)
+//   stats  per query (max, sum of exp) of each 1024-key tile, folded per
+//          unit into LSE (log2 units) by a small kernel after it
 //   pool   recompute the logits, p = exp2(l*c - LSE2), sum over the G*W
 //          queries inside the lane, write s.
 // Q of the unit sits in LDS (rows padded by 16 bytes against bank
@@ -38,6 +38,7 @@ struct TBf16 {
   using frag_t = bf16x8;
   using acc_t = floatx16;
   static constexpr int M = 32, KS = 16, E = 8, NOUT = 16, G = 2;
+  static constexpr int MINB = 2;  // workgroups per CU the registers are sized for
   __device__ static acc_t zero() { return acc_t{}; }
   __device__ static acc_t mma(frag_t a, frag_t b, acc_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -61,6 +62,7 @@ struct TF64 {
   using frag_t = double;
   using acc_t = doublex4;
   static constexpr int M = 16, KS = 4, E = 1, NOUT = 4, G = 4;
+  static constexpr int MINB = 1;
   __device__ static acc_t zero() { return acc_t{}; }
   __device__ static acc_t mma(frag_t a, frag_t b, acc_t c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
@@ -84,9 +86,9 @@ struct TF64 {
 // Per-instance tiling: RB key row blocks per wave step in the stats pass,
 // CB key column blocks per wave step in the pooling pass.
 template <class T, int D> struct Tiling;
-template <> struct Tiling<TBf16, 64> { static constexpr int RB = 2, CB = 2; };
-template <> struct Tiling<TBf16, 128> { static constexpr int RB = 2, CB = 2; };
-template <> struct Tiling<TF64, 64> { static constexpr int RB = 2, CB = 1; };
+template <> struct Tiling<TBf16, 64> { static constexpr int RB = 2, CB = 1; };
+template <> struct Tiling<TBf16, 128> { static constexpr int RB = 2, CB = 1; };
+template <> struct Tiling<TF64, 64> { static constexpr int RB = 1, CB = 1; };
 template <> struct Tiling<TF64, 128> { static constexpr int RB = 1, CB = 1; };
 
 struct TileInfo {
@@ -135,25 +137,27 @@ __device__ inline void merge_stat(float& m, float& z, float m2, float z2, float 
 // ---------------------------------------------------------------------------
 // Pass 1: per-query softmax statistics of each tile, folded per unit.
 // ---------------------------------------------------------------------------
-template <class T, int D>
-__global__ __launch_bounds__(SCORE_THREADS) void kvc_score_stats_kernel(
+// NBC: number of 32/16-query blocks (G W / M) when fixed at compile time,
+// 0 to read it from the descriptor (a runtime bound costs the compiler the
+// freedom to overlap one block's exponentials with the next block's MFMAs).
+template <class T, int D, int NBC>
+__global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_stats_kernel(
     KvcDesc Dsc, const typename T::elem_t* __restrict__ q,
-    const typename T::elem_t* __restrict__ k, float2* __restrict__ partials,
-    float* __restrict__ lse2, uint32_t* __restrict__ counters) {
+    const typename T::elem_t* __restrict__ k, float2* __restrict__ partials) {
   using elem_t = typename T::elem_t;
   using frag_t = typename T::frag_t;
   using acc_t = typename T::acc_t;
   constexpr int M = T::M, G = T::G, NK = D / T::KS, RB = Tiling<T, D>::RB;
   constexpr int QS = D + 16 / (int)sizeof(elem_t);
-  constexpr int MAXCB = KVC_MAX_GW / M;
+  constexpr int MAXCB = NBC > 0 ? NBC : KVC_MAX_GW / M;
   constexpr int KW = RB * M;
 
-  __shared__ __attribute__((aligned(16))) elem_t sQ[KVC_MAX_GW * QS];
-  __shared__ float2 sStat[SCORE_WAVES][KVC_MAX_GW];
-  __shared__ int sLast;
+  __shared__ __attribute__((aligned(16))) elem_t sQ[MAXCB * M * QS];
+  __shared__ float2 sStat[SCORE_WAVES][MAXCB * M];
 
   const TileInfo ti = tile_info(Dsc, blockIdx.x);
-  const int gw = Dsc.gw, ncb = gw / M;
+  const int gw = NBC > 0 ? NBC * M : Dsc.gw;
+  const int ncb = NBC > 0 ? NBC : gw / M;
   const float c = kLog2e / sqrtf((float)D);
   const elem_t* qg =
       q + ((size_t)((int64_t)ti.seq * Dsc.n_layers + ti.l) * Dsc.n_heads * Dsc.gqa +
@@ -172,99 +176,146 @@ __global__ __launch_bounds__(SCORE_THREADS) void kvc_score_stats_kernel(
   }
 
   const int ngroups = ti.keys / KW;
-  for (int grp = wave; grp < ngroups; grp += SCORE_WAVES) {
+  // Software pipeline over query blocks: the MFMAs of block cb+1 are issued
+  // before the exponentials of block cb, and a scheduling barrier per stage
+  // keeps the compiler from hoisting further blocks (which would exhaust
+  // the registers).
+  auto mma_blk = [&](acc_t (&acc)[RB], const frag_t (&a)[RB][NK], int cb, int qoff) {
+    frag_t b[NK];
+    int qo = cb * M * QS + qoff;
+    asm volatile("" : "+v"(qo));  // load this block's Q here, not earlier
+    T::template load<NK>(b, sQ + qo);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      acc[rb] = T::zero();
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) acc[rb] = T::mma(a[rb][kk], b[kk], acc[rb]);
+    }
+  };
+  auto stat_blk = [&](const acc_t (&acc)[RB], float& mref, float& zref) {
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < T::NOUT; ++i) mloc = fmaxf(mloc, T::val(acc[rb], i));
+    const float mnew = fmaxf(mref, mloc);
+    const float nmc = -mnew * c;
+    float zz = (mref == -INFINITY) ? 0.f : zref * __builtin_amdgcn_exp2f((mref - mnew) * c);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < T::NOUT; ++i) zz += __builtin_amdgcn_exp2f(fmaf(T::val(acc[rb], i), c, nmc));
+    mref = mnew;
+    zref = zz;
+  };
+  auto load_keys = [&](frag_t (&a)[RB][NK], int grp) {
     const int kb = ti.key0 + grp * KW;
-    frag_t a[RB][NK];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
       T::template load<NK>(a[rb], ku + (int64_t)(kb + rb * M + lrow) * Dsc.ks[2] + lgrp * (D / G));
+  };
+  auto group = [&](const frag_t (&a)[RB][NK]) {
+    // Q fragments do not change between key groups; an opaque lane index
+    // keeps the compiler from hoisting them all out of the loop.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int qoff = (ln % M) * QS + (ln / M) * (D / G);
+    if constexpr (NBC > 0) {
+      acc_t X[RB], Y[RB];
+      mma_blk(X, a, 0, qoff);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int cb = 0; cb < MAXCB; ++cb) {
-      if (cb >= ncb) break;
-      frag_t b[NK];
-      T::template load<NK>(b, sQ + (cb * M + lrow) * QS + lgrp * (D / G));
-      acc_t acc[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        acc[rb] = T::zero();
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) acc[rb] = T::mma(a[rb][kk], b[kk], acc[rb]);
+      for (int cb = 0; cb < NBC; ++cb) {
+        if (cb + 1 < NBC) mma_blk((cb & 1) ? X : Y, a, cb + 1, qoff);
+        stat_blk((cb & 1) ? Y : X, m[cb], z[cb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      float mloc = -INFINITY;
+    } else {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int i = 0; i < T::NOUT; ++i) mloc = fmaxf(mloc, T::val(acc[rb], i));
-      const float mnew = fmaxf(m[cb], mloc);
-      const float nmc = -mnew * c;
-      float zz = (m[cb] == -INFINITY) ? 0.f : z[cb] * __builtin_amdgcn_exp2f((m[cb] - mnew) * c);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int i = 0; i < T::NOUT; ++i)
-          zz += __builtin_amdgcn_exp2f(fmaf(T::val(acc[rb], i), c, nmc));
-      m[cb] = mnew;
-      z[cb] = zz;
+      for (int cb = 0; cb < MAXCB; ++cb) {
+        if (cb < ncb) {
+          acc_t X[RB];
+          mma_blk(X, a, cb, qoff);
+          stat_blk(X, m[cb], z[cb]);
+        }
+      }
     }
+  };
+  // Two register buffers: the next group's keys load while this one computes.
+  frag_t a0[RB][NK], a1[RB][NK];
+  if (wave < ngroups) load_keys(a0, wave);
+  for (int grp = wave; grp < ngroups; grp += 2 * SCORE_WAVES) {
+    const bool more = grp + SCORE_WAVES < ngroups;
+    if (more) load_keys(a1, grp + SCORE_WAVES);
+    group(a0);
+    if (!more) break;
+    if (grp + 2 * SCORE_WAVES < ngroups) load_keys(a0, grp + 2 * SCORE_WAVES);
+    group(a1);
   }
 
   // Fold the lane groups holding the same query, then the waves.
 #pragma unroll
   for (int cb = 0; cb < MAXCB; ++cb) {
-    if (cb >= ncb) break;
+    if (cb < ncb) {
 #pragma unroll
-    for (int o = M; o < 64; o <<= 1) {
-      const float m2 = __shfl_xor(m[cb], o);
-      const float z2 = __shfl_xor(z[cb], o);
-      merge_stat(m[cb], z[cb], m2, z2, c);
+      for (int o = M; o < 64; o <<= 1) {
+        const float m2 = __shfl_xor(m[cb], o);
+        const float z2 = __shfl_xor(z[cb], o);
+        merge_stat(m[cb], z[cb], m2, z2, c);
+      }
+      if (lgrp == 0) sStat[wave][cb * M + lrow] = make_float2(m[cb], z[cb]);
     }
-    if (lgrp == 0) sStat[wave][cb * M + lrow] = make_float2(m[cb], z[cb]);
   }
   __syncthreads();
-  const int tile0 = blockIdx.x - ti.t;  // first tile of this unit
   if (threadIdx.x < gw) {
     float mm = -INFINITY, zz = 0.f;
 #pragma unroll
     for (int w = 0; w < SCORE_WAVES; ++w) merge_stat(mm, zz, sStat[w][threadIdx.x].x, sStat[w][threadIdx.x].y, c);
     partials[(size_t)blockIdx.x * gw + threadIdx.x] = make_float2(mm, zz);
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) sLast = (atomicAdd(&counters[ti.u], 1u) == (uint32_t)(ti.tpu - 1));
-  __syncthreads();
-  if (!sLast) return;
-  __threadfence();
-  if (threadIdx.x < gw) {
-    float mm = -INFINITY, zz = 0.f;
-    for (int t = 0; t < ti.tpu; ++t) {
-      const float2 p = partials[(size_t)(tile0 + t) * gw + threadIdx.x];
-      merge_stat(mm, zz, p.x, p.y, c);
-    }
-    lse2[(size_t)ti.u * gw + threadIdx.x] = mm * c + __builtin_amdgcn_logf(zz);
+}
+
+// Fold the per-tile statistics of each unit into LSE (log2 units): one
+// workgroup per unit, one thread per window query.
+__global__ __launch_bounds__(KVC_MAX_GW) void kvc_score_lse_kernel(KvcDesc Dsc, float c,
+                                                                   const float2* __restrict__ partials,
+                                                                   float* __restrict__ lse2) {
+  const int u = blockIdx.x;
+  const int seq = u / Dsc.upseq;
+  const int tpu = kvc_tiles_per_unit(Dsc.L[seq]);
+  const int tile0 = Dsc.tile_base[seq] + (u - seq * Dsc.upseq) * tpu;
+  const int gw = Dsc.gw;
+  if ((int)threadIdx.x >= gw) return;
+  float mm = -INFINITY, zz = 0.f;
+  for (int t = 0; t < tpu; ++t) {
+    const float2 p = partials[(size_t)(tile0 + t) * gw + threadIdx.x];
+    merge_stat(mm, zz, p.x, p.y, c);
   }
+  lse2[(size_t)u * gw + threadIdx.x] = mm * c + __builtin_amdgcn_logf(zz);
 }
 
 // ---------------------------------------------------------------------------
 // Pass 2: probabilities pooled over the window queries and the GQA group.
 // ---------------------------------------------------------------------------
-template <class T, int D>
-__global__ __launch_bounds__(SCORE_THREADS) void kvc_score_pool_kernel(
+template <class T, int D, int NBC, int CBT = Tiling<T, D>::CB, bool PIPE = true>
+__global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_pool_kernel(
     KvcDesc Dsc, const typename T::elem_t* __restrict__ q,
     const typename T::elem_t* __restrict__ k, const float* __restrict__ lse2,
     float* __restrict__ s) {
   using elem_t = typename T::elem_t;
   using frag_t = typename T::frag_t;
   using acc_t = typename T::acc_t;
-  constexpr int M = T::M, G = T::G, NK = D / T::KS, CB = Tiling<T, D>::CB;
+  constexpr int M = T::M, G = T::G, NK = D / T::KS, CB = CBT;
   constexpr int QS = D + 16 / (int)sizeof(elem_t);
-  constexpr int MAXRB = KVC_MAX_GW / M;
+  constexpr int MAXRB = NBC > 0 ? NBC : KVC_MAX_GW / M;
   constexpr int KW = CB * M;
 
-  __shared__ __attribute__((aligned(16))) elem_t sQ[KVC_MAX_GW * QS];
-  __shared__ float sL[KVC_MAX_GW];
+  __shared__ __attribute__((aligned(16))) elem_t sQ[MAXRB * M * QS];
+  __shared__ float sL[MAXRB * M];
 
   const TileInfo ti = tile_info(Dsc, blockIdx.x);
-  const int gw = Dsc.gw, nrb = gw / M;
+  const int gw = NBC > 0 ? NBC * M : Dsc.gw;
+  const int nrb = NBC > 0 ? NBC : gw / M;
   const float c = kLog2e / sqrtf((float)D);
   const float inv_gw = 1.0f / (float)gw;
   const elem_t* qg =
@@ -279,32 +330,69 @@ __global__ __launch_bounds__(SCORE_THREADS) void kvc_score_pool_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lrow = lane % M, lgrp = lane / M;
   const int ngroups = ti.keys / KW;
-  for (int grp = wave; grp < ngroups; grp += SCORE_WAVES) {
+  // Same two-stage pipeline as the statistics pass, over query row blocks.
+  auto mma_blk = [&](acc_t (&acc)[CB], const frag_t (&b)[CB][NK], int rb, int qoff) {
+    frag_t a[NK];
+    int qo = rb * M * QS + qoff;
+    asm volatile("" : "+v"(qo));  // load this block's Q here, not earlier
+    T::template load<NK>(a, sQ + qo);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      acc[cb] = T::zero();
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) acc[cb] = T::mma(a[kk], b[cb][kk], acc[cb]);
+    }
+  };
+  auto pool_blk = [&](const acc_t (&acc)[CB], float (&acc_s)[CB], int rb, int ln) {
+    float nl[T::NOUT];
+    int lb = rb * M;
+    asm volatile("" : "+v"(lb));  // load this block's LSE here, not earlier
+#pragma unroll
+    for (int i = 0; i < T::NOUT; ++i) nl[i] = -sL[lb + T::out_row(i, ln)];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < T::NOUT; ++i) sum += __builtin_amdgcn_exp2f(fmaf(T::val(acc[cb], i), c, nl[i]));
+      acc_s[cb] += sum;
+    }
+  };
+  auto load_keys = [&](frag_t (&b)[CB][NK], int grp) {
     const int kb = ti.key0 + grp * KW;
-    frag_t b[CB][NK];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       T::template load<NK>(b[cb], ku + (int64_t)(kb + cb * M + lrow) * Dsc.ks[2] + lgrp * (D / G));
+  };
+  auto group = [&](const frag_t (&b)[CB][NK], int grp) {
+    const int kb = ti.key0 + grp * KW;
+    // The Q fragments and LSE values of a query block do not change from one
+    // key group to the next; an opaque lane index keeps the compiler from
+    // hoisting all of them out of the loop (they would not fit in registers).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int qoff = (ln % M) * QS + (ln / M) * (D / G);
     float acc_s[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc_s[cb] = 0.f;
+    if constexpr (NBC > 0 && PIPE) {
+      acc_t X[CB], Y[CB];
+      mma_blk(X, b, 0, qoff);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rb = 0; rb < MAXRB; ++rb) {
-      if (rb >= nrb) break;
-      frag_t a[NK];
-      T::template load<NK>(a, sQ + (rb * M + lrow) * QS + lgrp * (D / G));
-      float nl[T::NOUT];
+      for (int rb = 0; rb < NBC; ++rb) {
+        if (rb + 1 < NBC) mma_blk((rb & 1) ? X : Y, b, rb + 1, qoff);
+        pool_blk((rb & 1) ? Y : X, acc_s, rb, ln);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
-      for (int i = 0; i < T::NOUT; ++i) nl[i] = -sL[rb * M + T::out_row(i, lane)];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        acc_t acc = T::zero();
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) acc = T::mma(a[kk], b[cb][kk], acc);
-        float sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < T::NOUT; ++i) sum += __builtin_amdgcn_exp2f(fmaf(T::val(acc, i), c, nl[i]));
-        acc_s[cb] += sum;
+      for (int rb = 0; rb < MAXRB; ++rb) {
+        if (rb < nrb) {
+          acc_t X[CB];
+          mma_blk(X, b, rb, qoff);
+          pool_blk(X, acc_s, rb, ln);
+          if constexpr (!PIPE) __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
 #pragma unroll
@@ -314,32 +402,58 @@ __global__ __launch_bounds__(SCORE_THREADS) void kvc_score_pool_kernel(
       for (int o = M; o < 64; o <<= 1) v += __shfl_xor(v, o);
       if (lgrp == 0) srow[kb + cb * M + lrow] = v * inv_gw;
     }
+  };
+  frag_t b0[CB][NK], b1[CB][NK];
+  if (wave < ngroups) load_keys(b0, wave);
+  for (int grp = wave; grp < ngroups; grp += 2 * SCORE_WAVES) {
+    const bool more = grp + SCORE_WAVES < ngroups;
+    if (more) load_keys(b1, grp + SCORE_WAVES);
+    group(b0, grp);
+    if (!more) break;
+    if (grp + 2 * SCORE_WAVES < ngroups) load_keys(b0, grp + 2 * SCORE_WAVES);
+    group(b1, grp + SCORE_WAVES);
   }
 }
 
 size_t kvc_scores_workspace(const KvcDesc& D) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  return up(sizeof(uint32_t) * (size_t)D.n_units) +
-         up(sizeof(float) * (size_t)D.n_units * D.gw) +
+  return up(sizeof(float) * (size_t)D.n_units * D.gw) +
          up(sizeof(float2) * (size_t)D.total_tiles * D.gw);
 }
 
-template <class T, int Dm>
+template <class T, int Dm, int NBC>
 static void launch_pair(const KvcDesc& D, const void* q, const void* k, float* s,
-                        float2* partials, float* lse2, uint32_t* counters, hipStream_t st) {
+                        float2* partials, float* lse2, hipStream_t st) {
   using elem_t = typename T::elem_t;
-  hipLaunchKernelGGL((kvc_score_stats_kernel<T, Dm>), dim3(D.total_tiles), dim3(SCORE_THREADS), 0,
-                     st, D, (const elem_t*)q, (const elem_t*)k, partials, lse2, counters);
-  hipLaunchKernelGGL((kvc_score_pool_kernel<T, Dm>), dim3(D.total_tiles), dim3(SCORE_THREADS), 0,
-                     st, D, (const elem_t*)q, (const elem_t*)k, (const float*)lse2, s);
+  hipLaunchKernelGGL((kvc_score_stats_kernel<T, Dm, NBC>), dim3(D.total_tiles), dim3(SCORE_THREADS),
+                     0, st, D, (const elem_t*)q, (const elem_t*)k, partials);
+  hipLaunchKernelGGL(kvc_score_lse_kernel, dim3(D.n_units), dim3(KVC_MAX_GW), 0, st, D,
+                     kLog2e / sqrtf((float)Dm), (const float2*)partials, lse2);
+  hipLaunchKernelGGL((kvc_score_pool_kernel<T, Dm, NBC>), dim3(D.total_tiles), dim3(SCORE_THREADS),
+                     0, st, D, (const elem_t*)q, (const elem_t*)k, (const float*)lse2, s);
+}
+
+template <int Dm>
+static void launch_bf16(const KvcDesc& D, const void* q, const void* k, float* s,
+                        float2* partials, float* lse2, hipStream_t st) {
+  switch (D.gw / 32) {
+    case 1: launch_pair<TBf16, Dm, 1>(D, q, k, s, partials, lse2, st); break;
+    case 2: launch_pair<TBf16, Dm, 2>(D, q, k, s, partials, lse2, st); break;
+    case 3: launch_pair<TBf16, Dm, 3>(D, q, k, s, partials, lse2, st); break;
+    case 4: launch_pair<TBf16, Dm, 4>(D, q, k, s, partials, lse2, st); break;
+    case 5: launch_pair<TBf16, Dm, 5>(D, q, k, s, partials, lse2, st); break;
+    case 6: launch_pair<TBf16, Dm, 6>(D, q, k, s, partials, lse2, st); break;
+    case 7: launch_pair<TBf16, Dm, 7>(D, q, k, s, partials, lse2, st); break;
+    default: launch_pair<TBf16, Dm, 8>(D, q, k, s, partials, lse2, st); break;
+  }
 }
 
 hipError_t kvc_launch_scores(const KvcDesc& D, const void* q, const void* k, float* s,
-                             float2* partials, float* lse2, uint32_t* counters, hipStream_t st) {
-  if (D.dtype == 0 && D.d == 128) launch_pair<TBf16, 128>(D, q, k, s, partials, lse2, counters, st);
-  else if (D.dtype == 0 && D.d == 64) launch_pair<TBf16, 64>(D, q, k, s, partials, lse2, counters, st);
-  else if (D.dtype == 1 && D.d == 128) launch_pair<TF64, 128>(D, q, k, s, partials, lse2, counters, st);
-  else if (D.dtype == 1 && D.d == 64) launch_pair<TF64, 64>(D, q, k, s, partials, lse2, counters, st);
+                             float2* partials, float* lse2, hipStream_t st) {
+  if (D.dtype == 0 && D.d == 128) launch_bf16<128>(D, q, k, s, partials, lse2, st);
+  else if (D.dtype == 0 && D.d == 64) launch_bf16<64>(D, q, k, s, partials, lse2, st);
+  else if (D.dtype == 1 && D.d == 128) launch_pair<TF64, 128, 0>(D, q, k, s, partials, lse2, st);
+  else if (D.dtype == 1 && D.d == 64) launch_pair<TF64, 64, 0>(D, q, k, s, partials, lse2, st);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -1,0 +1,233 @@
+"""Throughput of audio prefill KV-cache compression on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config omni30b]
+
+One step = one kvc_compress call over the whole batch (all layers, KV heads
+and sequences): scores -> spectral smoothing -> budget -> top-k -> gather,
+inputs resident in HBM.  Prints one JSON line on stdout; progress on stderr.
+
+Metric: compressed tokens*heads per second (sum of L * layers * KV heads per
+step time) and the fraction of HBM peak that the path's algorithmic bytes
+reach.  Algorithmic bytes per (sequence, layer, KV head) unit:
+    L d e            K read once for the scores
+  + 2 b d e          kept K and V rows read
+  + 2 b d e          kept K and V rows written
+  + 4 b              kept positions written
+  + G W d e          window queries read
+(e = element size, b = the unit's budget); V is never read for the scores and
+the score rows are workspace.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import pathlib
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+ROOT = pathlib.Path(__file__).resolve().parent
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, hdr, budgets):
+    e = 2 if cfg.dtype == "bf16" else 4
+    d = cfg.head_dim
+    gwde = cfg.gqa * cfg.n_window * d * e
+    per_seq_units = cfg.n_layers * cfg.n_kv_heads
+    k_read = sum(int(L) * d * e * per_seq_units for L in hdr.lengths)
+    b = np.asarray(budgets, dtype=np.int64)
+    kept = int(b.sum())
+    return dict(k_scores=k_read, gather=4 * kept * d * e + 4 * kept,
+                q=gwde * per_seq_units * cfg.n_seq, total=k_read + 4 * kept * d * e + 4 * kept
+                + gwde * per_seq_units * cfg.n_seq)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        h.update((ROOT / "audio_kv_cache_amd" / "csrc" / n).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel_file: str, kernel: str, workload: str):
+    """HBM bytes per launch from a committed counter summary, if it matches the
+    current kernel source; None otherwise."""
+    p = ROOT / "profiles" / "traffic.json"
+    if not p.exists():
+        return None
+    try:
+        rec = json.loads(p.read_text()).get(f"{workload}:{kernel}")
+    except json.JSONDecodeError:
+        return None
+    if not rec or rec.get("source_sha") != source_hash(kernel_file):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, hdr, prob_units, budgets, max_units=8):
+    """The fp64 oracle, as it stands, on a bounded sample of units."""
+    from oracle import oracle as O
+    from audio_kv_cache_amd import synth
+    cores = min(max_units, O.threads())
+    units = prob_units[:max_units]
+    # regenerate only the sampled units (each is seeded on its own)
+    inputs = [synth.unit(cfg, hdr, i, l, h) for (i, l, h) in units]
+    import concurrent.futures as cf
+
+    def run(j):
+        (i, l, h), (qu, ku, _) = units[j], inputs[j]
+        u = (i * cfg.n_layers + l) * cfg.n_kv_heads + h
+        O.unit_compress(qu, ku, cfg.dtype, int(budgets[u]), cfg.alpha, cfg.rho, cfg.window)
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(cores) as ex:
+        list(ex.map(run, range(len(units))))
+    dt = time.perf_counter() - t0
+    toks = sum(int(hdr.lengths[i]) for (i, l, h) in units)
+    return dict(value=toks / dt, unit="tokens·heads/s", cores=cores, kind="oracle",
+                sample=f"{len(units)} units (seq, layer, KV head) of the same workload, "
+                       f"scores+smoothing+selection in fp64, {dt:.1f} s wall")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="omni30b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stages", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by (sequence, layer, KV head) unit with no exchange; "
+              "multi-GPU runs are out of scope here)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from audio_kv_cache_amd import api, synth
+
+    cfg = synth.CONFIGS[args.config]
+    log(f"[bench] generating {cfg.name} inputs")
+    t0 = time.perf_counter()
+    prob = synth.problem(cfg)
+    hdr = prob.hdr
+    log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; copying to the GPU")
+
+    def dev(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q, k, v = dev(prob.q), dev(prob.k), dev(prob.v)
+    S = torch.from_numpy(hdr.head_scores).cuda()
+    units = [(i, l, h) for i in range(cfg.n_seq) for l in range(cfg.n_layers)
+             for h in range(cfg.n_kv_heads)]
+    del prob
+    spec = api.Spec.for_tensors(k, v, gqa=cfg.gqa, seq_lens=hdr.lengths,
+                                retention=hdr.retention, n_window=cfg.n_window)
+    prm = api.Params(cfg.alpha, cfg.rho, cfg.window, cfg.base_ratio)
+    out = api.allocate(spec, prm, k.device)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        api.kvc_compress(spec, prm, q, k, v, S, out["k_out"], out["v_out"], out["idx"],
+                         out["offsets"], out["budgets"], out["workspace"], stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    budgets = out["budgets"].cpu().numpy()
+    ab = algorithmic_bytes(cfg, hdr, budgets)
+    tokheads = sum(int(L) for L in hdr.lengths) * cfg.n_layers * cfg.n_kv_heads
+    value = tokheads / (ms * 1e-3)
+    path_gbs = ab["total"] / (ms * 1e-3) / 1e9
+    log(f"[bench] {ms:.3f} ms/step, {value:.4g} tokens·heads/s, path {path_gbs:.0f} GB/s "
+        f"({100 * path_gbs / HBM_PEAK_GBS:.1f} % of HBM peak)")
+
+    # Per-stage timing with events on the same stream (each stage entry point
+    # launches that step's kernels only).
+    stages = {}
+    if not args.no_stages:
+        s_rows = torch.empty(spec.score_rows(), dtype=torch.float32, device="cuda")
+        sh_rows = torch.empty_like(s_rows)
+        kst = torch.empty(spec.n_units, dtype=torch.int32, device="cuda")
+        api.kvc_scores(spec, prm, q, k, s_rows, out["workspace"], stream)
+        api.kvc_smooth(spec, prm, s_rows, sh_rows, kst, stream)
+        calls = {
+            "budget": lambda: api.kvc_budget(spec, prm, S, out["budgets"], out["offsets"], stream),
+            "scores": lambda: api.kvc_scores(spec, prm, q, k, s_rows, out["workspace"], stream),
+            "smooth": lambda: api.kvc_smooth(spec, prm, s_rows, sh_rows, kst, stream),
+            "select": lambda: api.kvc_select(spec, prm, sh_rows, out["budgets"], out["offsets"],
+                                             out["idx"], stream),
+            "gather": lambda: api.kvc_gather(spec, prm, k, v, out["idx"], out["offsets"],
+                                             out["k_out"], out["v_out"], stream),
+        }
+        for name, fn in calls.items():
+            fn()
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            stages[name] = ev0.elapsed_time(ev1) / args.steps
+        log("[bench] stage ms: " + ", ".join(f"{n} {t:.3f}" for n, t in stages.items()))
+
+    # Roofline of the dominant kernel: the gather (bytes only, HBM bound).
+    roof = None
+    if stages:
+        g_ms = stages["gather"]
+        g_gbs = ab["gather"] / (g_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "kvc_gather_kernel<256>", "achieved": round(g_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
+                "traffic": committed_traffic("gather.hip", "kvc_gather_kernel", cfg.name)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample of units")
+        cpu = cpu_baseline(cfg, hdr, units, budgets)
+        log(f"[bench] oracle {cpu['value']:.4g} tokens·heads/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": "compressed tokens·heads/s and % of HBM peak, L=32K audio tokens, 1 GPU",
+        "value": value, "unit": "tokens·heads/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.n_seq} seq x L={int(hdr.lengths[0]) if cfg.n_seq == 1 else 'ragged'}"
+                               f", {cfg.n_layers} layers x {cfg.n_kv_heads} KV heads, GQA {cfg.gqa}, "
+                               f"head_dim {cfg.head_dim}, {cfg.dtype}, retention "
+                               f"{float(hdr.retention[0]) if cfg.n_seq == 1 else 'U(0.2,0.6)'}, "
+                               f"alpha {cfg.alpha}, rho {cfg.rho}, w {cfg.window}",
+                   "tokens_heads_per_step": tokheads,
+                   "algorithmic_bytes_per_step": ab["total"]},
+        "path_hbm": {"achieved": round(path_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(path_gbs / HBM_PEAK_GBS, 4)},
+        "stage_ms": {k2: round(v2, 4) for k2, v2 in stages.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
