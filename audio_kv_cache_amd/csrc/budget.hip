@@ -62,13 +62,23 @@ __global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
   // Water-filling rounds.
   for (;;) {
     if (tid == 0) {
+      // Sequential in u (the order fixes the rounding); branch-free so the
+      // LDS loads pipeline: adding +0.0 for an inactive head changes nothing.
       double acc = 0.0;
       int nA = 0;
-      for (int u = 0; u < n; ++u)
-        if (active[u]) {
-          acc += (double)sS[u];
-          ++nA;
+      for (int u0 = 0; u0 < n; u0 += 16) {
+        // 16 independent LDS loads first, then the adds in u order.
+        double x[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int u = u0 + j;
+          const bool a = u < n && active[u] != 0;
+          x[j] = a ? (double)sS[u] : 0.0;
+          nA += a;
         }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc += x[j];
+      }
       s_sum = acc;
       s_nA = nA;
       s_capped = 0;
@@ -101,7 +111,11 @@ __global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
   // Largest remainder over the heads still active.
   int64_t my_floor = 0;
   for (int u = tid; u < n; u += BUDGET_THREADS)
-    if (active[u]) my_floor += (int64_t)floor(q[u]);
+    if (active[u]) {
+      const double fu = floor(q[u]);
+      extra[u] = (int32_t)fu;
+      my_floor += (int64_t)fu;
+    }
   for (int o = 32; o > 0; o >>= 1) my_floor += __shfl_xor(my_floor, o);
   if ((tid & 63) == 0) s_wsum[tid >> 6] = my_floor;
   __syncthreads();
@@ -109,17 +123,19 @@ __global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
   for (int w = 0; w < BUDGET_THREADS / 64; ++w) floors += s_wsum[w];
   const int64_t deficit = s_R - floors;  // 0 <= deficit <= active count
 
+  // Fractional parts once (inactive heads get -1, below every real one).
+  for (int u = tid; u < n; u += BUDGET_THREADS) q[u] = active[u] ? q[u] - floor(q[u]) : -1.0;
+  __syncthreads();
   for (int u = tid; u < n; u += BUDGET_THREADS) {
     if (!active[u]) continue;
-    const double fu = floor(q[u]);
-    const double ru = q[u] - fu;
-    int64_t rank = 0;
+    const double ru = q[u];
+    int rank = 0;
+#pragma unroll 8
     for (int v = 0; v < n; ++v) {
-      if (!active[v]) continue;
-      const double rv = q[v] - floor(q[v]);
-      rank += (rv > ru) || (rv == ru && v < u);
+      const double rv = q[v];
+      rank += (rv > ru) | ((rv == ru) & (v < u));
     }
-    extra[u] = (int32_t)fu + (rank < deficit ? 1 : 0);
+    extra[u] += (rank < deficit ? 1 : 0);
   }
   __syncthreads();
 

@@ -13,77 +13,77 @@
 
 template <int ROWB>
 __global__ __launch_bounds__(GATHER_THREADS) void kvc_gather_kernel(
-    KvcDesc D, const char* __restrict__ k, const char* __restrict__ v,
+    KvcDesc D, int u0, int u1, const char* __restrict__ k, const char* __restrict__ v,
     const int32_t* __restrict__ idx, const int64_t* __restrict__ offsets,
-    char* __restrict__ k_out, char* __restrict__ v_out, int64_t total_rows) {
+    char* __restrict__ k_out, char* __restrict__ v_out) {
   constexpr int CH = ROWB / 16;                    // 16-byte chunks per row
   constexpr int ROWS_PER_PASS = GATHER_THREADS / CH;
   constexpr int PASSES = 4;
   constexpr int ROWS_PER_BLOCK = ROWS_PER_PASS * PASSES;
-  const int64_t r0 = (int64_t)blockIdx.x * ROWS_PER_BLOCK;
-  if (r0 >= total_rows) return;
-
-  // Unit owning the block's first row: largest u with offsets[u] <= r0.
-  __shared__ int s_u0;
-  if (threadIdx.x == 0) {
-    int lo = 0, hi = D.n_units - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (offsets[mid] <= r0) lo = mid; else hi = mid - 1;
-    }
-    s_u0 = lo;
-  }
-  __syncthreads();
-
+  // Rows of units [u0, u1) are offsets[u0] .. offsets[u1]-1; the grid
+  // strides over them.
+  const int64_t rbeg = offsets[u0], rend = offsets[u1];
   const int esz = D.dtype == 0 ? 2 : 4;
   const int chunk = threadIdx.x % CH;
-  int u = s_u0;
-  uint4 kv[PASSES], vv[PASSES];
-  int64_t rows[PASSES];
+  for (int64_t r0 = rbeg + (int64_t)blockIdx.x * ROWS_PER_BLOCK; r0 < rend;
+       r0 += (int64_t)gridDim.x * ROWS_PER_BLOCK) {
+    // Unit owning this thread's first row: largest u with offsets[u] <= row.
+    const int64_t t0 = r0 + threadIdx.x / CH;
+    int lo = u0, hi = u1 - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offsets[mid] <= t0) lo = mid; else hi = mid - 1;
+    }
+    int u = lo;
+    uint4 kv[PASSES], vv[PASSES];
+    int64_t rows[PASSES];
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int64_t t = r0 + p * ROWS_PER_PASS + threadIdx.x / CH;
-    rows[p] = t;
-    if (t >= total_rows) continue;
-    while (u + 1 < D.n_units && offsets[u + 1] <= t) ++u;
-    const int seq = u / D.upseq;
-    const int within = u - seq * D.upseq;
-    const int l = within / D.n_heads, h = within - l * D.n_heads;
-    int pos = idx[t];
-    if ((unsigned)pos >= (unsigned)D.L[seq]) pos = 0;  // never read outside the row
-    const int64_t tok = D.tok0[seq] + pos;
-    const char* ks = k + (l * D.ks[0] + h * D.ks[1] + tok * D.ks[2]) * esz;
-    const char* vs = v + (l * D.vs[0] + h * D.vs[1] + tok * D.vs[2]) * esz;
-    kv[p] = *reinterpret_cast<const uint4*>(ks + chunk * 16);
-    vv[p] = *reinterpret_cast<const uint4*>(vs + chunk * 16);
-  }
+    for (int p = 0; p < PASSES; ++p) {
+      const int64_t t = r0 + p * ROWS_PER_PASS + threadIdx.x / CH;
+      rows[p] = t;
+      if (t >= rend) continue;
+      while (u + 1 < u1 && offsets[u + 1] <= t) ++u;
+      const int seq = u / D.upseq;
+      const int within = u - seq * D.upseq;
+      const int l = within / D.n_heads, h = within - l * D.n_heads;
+      int pos = idx[t];
+      if ((unsigned)pos >= (unsigned)D.L[seq]) pos = 0;  // never read outside the row
+      const int64_t tok = D.tok0[seq] + pos;
+      const char* ks = k + (l * D.ks[0] + h * D.ks[1] + tok * D.ks[2]) * esz;
+      const char* vs = v + (l * D.vs[0] + h * D.vs[1] + tok * D.vs[2]) * esz;
+      kv[p] = *reinterpret_cast<const uint4*>(ks + chunk * 16);
+      vv[p] = *reinterpret_cast<const uint4*>(vs + chunk * 16);
+    }
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int64_t t = rows[p];
-    if (t >= total_rows) continue;
-    uint4* ko = reinterpret_cast<uint4*>(k_out + t * ROWB + chunk * 16);
-    uint4* vo = reinterpret_cast<uint4*>(v_out + t * ROWB + chunk * 16);
-    __builtin_nontemporal_store(kv[p].x, &ko->x);
-    __builtin_nontemporal_store(kv[p].y, &ko->y);
-    __builtin_nontemporal_store(kv[p].z, &ko->z);
-    __builtin_nontemporal_store(kv[p].w, &ko->w);
-    __builtin_nontemporal_store(vv[p].x, &vo->x);
-    __builtin_nontemporal_store(vv[p].y, &vo->y);
-    __builtin_nontemporal_store(vv[p].z, &vo->z);
-    __builtin_nontemporal_store(vv[p].w, &vo->w);
+    for (int p = 0; p < PASSES; ++p) {
+      const int64_t t = rows[p];
+      if (t >= rend) continue;
+      uint4* ko = reinterpret_cast<uint4*>(k_out + t * ROWB + chunk * 16);
+      uint4* vo = reinterpret_cast<uint4*>(v_out + t * ROWB + chunk * 16);
+      __builtin_nontemporal_store(kv[p].x, &ko->x);
+      __builtin_nontemporal_store(kv[p].y, &ko->y);
+      __builtin_nontemporal_store(kv[p].z, &ko->z);
+      __builtin_nontemporal_store(kv[p].w, &ko->w);
+      __builtin_nontemporal_store(vv[p].x, &vo->x);
+      __builtin_nontemporal_store(vv[p].y, &vo->y);
+      __builtin_nontemporal_store(vv[p].z, &vo->z);
+      __builtin_nontemporal_store(vv[p].w, &vo->w);
+    }
   }
 }
 
-hipError_t kvc_launch_gather(const KvcDesc& D, const void* k, const void* v,
-                             const int32_t* idx, const int64_t* offsets, void* k_out,
-                             void* v_out, int64_t total_rows, hipStream_t st) {
-  if (total_rows <= 0) return hipSuccess;
+// Units [u0, u1); est_rows sizes the grid (the kernel strides over any excess).
+hipError_t kvc_launch_gather(const KvcDesc& D, int u0, int u1, const void* k, const void* v,
+                             const int32_t* idx, const int64_t* offsets, void* k_out, void* v_out,
+                             int64_t est_rows, hipStream_t st) {
+  if (u1 <= u0) return hipSuccess;
   const int rowb = D.d * (D.dtype == 0 ? 2 : 4);
   auto go = [&](auto kern, int rows_per_block) {
-    const int64_t blocks = (total_rows + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(GATHER_THREADS), 0, st, D,
-                       (const char*)k, (const char*)v, idx, offsets, (char*)k_out,
-                       (char*)v_out, total_rows);
+    int64_t blocks = (est_rows + rows_per_block - 1) / rows_per_block;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(GATHER_THREADS), 0, st, D, u0, u1,
+                       (const char*)k, (const char*)v, idx, offsets, (char*)k_out, (char*)v_out);
   };
   switch (rowb) {
     case 128: go(kvc_gather_kernel<128>, GATHER_THREADS / 8 * 4); break;

@@ -118,11 +118,6 @@ static kvc_status make_desc(const kvc_problem* p, const kvc_params* prm, KvcDesc
   D->tile_base[p->n_seq] = (int32_t)tiles;
   D->n_units = (int)(upseq * p->n_seq);
   D->total_tiles = (int)tiles;
-  // Longest sequences first, so the longest units start earliest.
-  int order[KVC_MAX_SEQ];
-  for (int i = 0; i < p->n_seq; ++i) order[i] = i;
-  std::stable_sort(order, order + p->n_seq, [&](int a, int b) { return D->L[a] > D->L[b]; });
-  for (int i = 0; i < p->n_seq; ++i) D->seq_order[i] = order[i];
   return KVC_OK;
 }
 
@@ -177,16 +172,26 @@ extern "C" kvc_status kvc_compress(const kvc_problem* prob, const kvc_params* pa
     return KVC_ERR_INVALID_ARG;
   const size_t need = kvc_scores_workspace(D) + up256(score_rows_bytes(D));
   if (workspace_bytes < need) return KVC_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
   const Carve c = carve(D, workspace);
-  hipError_t e;
-  e = kvc_launch_budget(D, head_scores, budgets, seg_offsets, s);
+  hipStream_t s = (hipStream_t)stream;
+  // One launch per step and sequence over all of the sequence's units (more,
+  // smaller launches cost more in launch and queue latency than they save).
+  hipError_t e = kvc_launch_budget(D, head_scores, budgets, seg_offsets, s);
   if (e != hipSuccess) return hip_status(e);
-  e = kvc_launch_scores(D, q_window, k, c.srows, c.partials, c.lse2, s);
-  if (e != hipSuccess) return hip_status(e);
-  e = kvc_launch_sss_select(D, 1 | 2, c.srows, nullptr, nullptr, budgets, seg_offsets, idx_out, s);
-  if (e != hipSuccess) return hip_status(e);
-  e = kvc_launch_gather(D, k, v, idx_out, seg_offsets, k_out, v_out, D.row_base[D.n_seq], s);
+  for (int seq = 0; seq < D.n_seq; ++seq) {
+    const int u0 = seq * D.upseq, u1 = u0 + D.upseq;
+    if ((e = kvc_launch_scores(D, u0, u1, q_window, k, c.srows, c.partials, c.lse2, s)) !=
+        hipSuccess)
+      return hip_status(e);
+  }
+  for (int seq = 0; seq < D.n_seq; ++seq) {
+    const int u0 = seq * D.upseq, u1 = u0 + D.upseq;
+    if ((e = kvc_launch_sss_select(D, u0, u1, 1 | 2, c.srows, nullptr, nullptr, budgets,
+                                   seg_offsets, idx_out, s)) != hipSuccess)
+      return hip_status(e);
+  }
+  e = kvc_launch_gather(D, 0, D.n_units, k, v, idx_out, seg_offsets, k_out, v_out,
+                        D.row_base[D.n_seq], s);
   return hip_status(e);
 }
 
@@ -201,10 +206,13 @@ extern "C" kvc_status kvc_scores(const kvc_problem* prob, const kvc_params* para
       ((uintptr_t)s_out & 7u))
     return KVC_ERR_INVALID_ARG;
   if (workspace_bytes < kvc_scores_workspace(D)) return KVC_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
   const Carve c = carve(D, workspace);
-  const hipError_t e = kvc_launch_scores(D, q_window, k, s_out, c.partials, c.lse2, s);
-  return hip_status(e);
+  for (int seq = 0; seq < D.n_seq; ++seq) {
+    const hipError_t e = kvc_launch_scores(D, seq * D.upseq, (seq + 1) * D.upseq, q_window, k,
+                                           s_out, c.partials, c.lse2, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return KVC_OK;
 }
 
 extern "C" kvc_status kvc_smooth(const kvc_problem* prob, const kvc_params* params,
@@ -215,8 +223,13 @@ extern "C" kvc_status kvc_smooth(const kvc_problem* prob, const kvc_params* para
   if (st != KVC_OK) return st;
   if (!s_in || !s_hat || !kstar) return KVC_ERR_INVALID_ARG;
   if (((uintptr_t)s_in & 7u) || ((uintptr_t)s_hat & 7u)) return KVC_ERR_INVALID_ARG;
-  return hip_status(kvc_launch_sss_select(D, 1 | 4, s_in, s_hat, kstar, nullptr, nullptr,
-                                          nullptr, (hipStream_t)stream));
+  for (int seq = 0; seq < D.n_seq; ++seq) {
+    const hipError_t e =
+        kvc_launch_sss_select(D, seq * D.upseq, (seq + 1) * D.upseq, 1 | 4, s_in, s_hat, kstar,
+                              nullptr, nullptr, nullptr, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return KVC_OK;
 }
 
 extern "C" kvc_status kvc_budget(const kvc_problem* prob, const kvc_params* params,
@@ -237,8 +250,13 @@ extern "C" kvc_status kvc_select(const kvc_problem* prob, const kvc_params* para
   if (st != KVC_OK) return st;
   if (!s_hat || !budgets || !seg_offsets || !idx_out) return KVC_ERR_INVALID_ARG;
   if ((uintptr_t)s_hat & 7u) return KVC_ERR_INVALID_ARG;
-  return hip_status(kvc_launch_sss_select(D, 2, s_hat, nullptr, nullptr, budgets, seg_offsets,
-                                          idx_out, (hipStream_t)stream));
+  for (int seq = 0; seq < D.n_seq; ++seq) {
+    const hipError_t e =
+        kvc_launch_sss_select(D, seq * D.upseq, (seq + 1) * D.upseq, 2, s_hat, nullptr, nullptr,
+                              budgets, seg_offsets, idx_out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return KVC_OK;
 }
 
 extern "C" kvc_status kvc_gather(const kvc_problem* prob, const kvc_params* params,
@@ -251,6 +269,6 @@ extern "C" kvc_status kvc_gather(const kvc_problem* prob, const kvc_params* para
   if (!k || !v || !idx || !seg_offsets || !k_out || !v_out) return KVC_ERR_INVALID_ARG;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out))
     return KVC_ERR_INVALID_ARG;
-  return hip_status(kvc_launch_gather(D, k, v, idx, seg_offsets, k_out, v_out,
+  return hip_status(kvc_launch_gather(D, 0, D.n_units, k, v, idx, seg_offsets, k_out, v_out,
                                       D.row_base[D.n_seq], (hipStream_t)stream));
 }

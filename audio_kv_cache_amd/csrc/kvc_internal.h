@@ -31,14 +31,11 @@ struct KvcDesc {
   int32_t L[KVC_MAX_SEQ];
   int32_t log2L[KVC_MAX_SEQ];
   int32_t tile_base[KVC_MAX_SEQ + 1];   // first score tile of sequence i
-  int32_t seq_order[KVC_MAX_SEQ];       // sequences by descending L (ties: index)
   int32_t n_units;
   int32_t total_tiles;
 };
 
 // Unit u -> (sequence, unit within sequence).
-__host__ __device__ inline int kvc_seq_of_unit(const KvcDesc& D, int u) { return u / D.upseq; }
-
 __host__ __device__ inline int kvc_tiles_per_unit(int L) {
   return L > KVC_TILE_KEYS ? L / KVC_TILE_KEYS : 1;
 }
@@ -46,18 +43,18 @@ __host__ __device__ inline int kvc_tiles_per_unit(int L) {
 // Kernel launchers (defined next to each kernel).
 hipError_t kvc_launch_budget(const KvcDesc& D, const float* S, int32_t* budgets,
                              int64_t* offsets, hipStream_t st);
-hipError_t kvc_launch_scores(const KvcDesc& D, const void* q, const void* k,
+// Range launches: units [u0, u1) (natural (seq, layer, head) order) must lie
+// within one sequence for the score and smoothing/selection launches.
+hipError_t kvc_launch_scores(const KvcDesc& D, int u0, int u1, const void* q, const void* k,
                              float* s, float2* partials, float* lse2, hipStream_t st);
 // mode bit 0: smooth (else read s_hat from s_in); bit 1: select;
 // bit 2: export s_hat and kstar.
-hipError_t kvc_launch_sss_select(const KvcDesc& D, int mode, const float* s_in,
-                                 float* s_hat_out, int32_t* kstar_out,
-                                 const int32_t* budgets, const int64_t* offsets,
-                                 int32_t* idx_out, hipStream_t st);
-hipError_t kvc_launch_gather(const KvcDesc& D, const void* k, const void* v,
-                             const int32_t* idx, const int64_t* offsets,
-                             void* k_out, void* v_out, int64_t total_rows,
-                             hipStream_t st);
+hipError_t kvc_launch_sss_select(const KvcDesc& D, int u0, int u1, int mode, const float* s_in,
+                                 float* s_hat_out, int32_t* kstar_out, const int32_t* budgets,
+                                 const int64_t* offsets, int32_t* idx_out, hipStream_t st);
+hipError_t kvc_launch_gather(const KvcDesc& D, int u0, int u1, const void* k, const void* v,
+                             const int32_t* idx, const int64_t* offsets, void* k_out, void* v_out,
+                             int64_t est_rows, hipStream_t st);
 
 // Workspace needed by the score kernels.
 size_t kvc_scores_workspace(const KvcDesc& D);

@@ -142,7 +142,7 @@ __device__ inline void merge_stat(float& m, float& z, float m2, float z2, float 
 // freedom to overlap one block's exponentials with the next block's MFMAs).
 template <class T, int D, int NBC>
 __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_stats_kernel(
-    KvcDesc Dsc, const typename T::elem_t* __restrict__ q,
+    KvcDesc Dsc, int tile0, const typename T::elem_t* __restrict__ q,
     const typename T::elem_t* __restrict__ k, float2* __restrict__ partials) {
   using elem_t = typename T::elem_t;
   using frag_t = typename T::frag_t;
@@ -155,7 +155,8 @@ __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_stats_kernel
   __shared__ __attribute__((aligned(16))) elem_t sQ[MAXCB * M * QS];
   __shared__ float2 sStat[SCORE_WAVES][MAXCB * M];
 
-  const TileInfo ti = tile_info(Dsc, blockIdx.x);
+  const int tile = tile0 + (int)blockIdx.x;
+  const TileInfo ti = tile_info(Dsc, tile);
   const int gw = NBC > 0 ? NBC * M : Dsc.gw;
   const int ncb = NBC > 0 ? NBC : gw / M;
   const float c = kLog2e / sqrtf((float)D);
@@ -271,16 +272,16 @@ __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_stats_kernel
     float mm = -INFINITY, zz = 0.f;
 #pragma unroll
     for (int w = 0; w < SCORE_WAVES; ++w) merge_stat(mm, zz, sStat[w][threadIdx.x].x, sStat[w][threadIdx.x].y, c);
-    partials[(size_t)blockIdx.x * gw + threadIdx.x] = make_float2(mm, zz);
+    partials[(size_t)tile * gw + threadIdx.x] = make_float2(mm, zz);
   }
 }
 
 // Fold the per-tile statistics of each unit into LSE (log2 units): one
 // workgroup per unit, one thread per window query.
-__global__ __launch_bounds__(KVC_MAX_GW) void kvc_score_lse_kernel(KvcDesc Dsc, float c,
+__global__ __launch_bounds__(KVC_MAX_GW) void kvc_score_lse_kernel(KvcDesc Dsc, int unit0, float c,
                                                                    const float2* __restrict__ partials,
                                                                    float* __restrict__ lse2) {
-  const int u = blockIdx.x;
+  const int u = unit0 + (int)blockIdx.x;
   const int seq = u / Dsc.upseq;
   const int tpu = kvc_tiles_per_unit(Dsc.L[seq]);
   const int tile0 = Dsc.tile_base[seq] + (u - seq * Dsc.upseq) * tpu;
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(KVC_MAX_GW) void kvc_score_lse_kernel(KvcDesc Dsc, 
 // ---------------------------------------------------------------------------
 template <class T, int D, int NBC, int CBT = Tiling<T, D>::CB, bool PIPE = true>
 __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_pool_kernel(
-    KvcDesc Dsc, const typename T::elem_t* __restrict__ q,
+    KvcDesc Dsc, int tile0, const typename T::elem_t* __restrict__ q,
     const typename T::elem_t* __restrict__ k, const float* __restrict__ lse2,
     float* __restrict__ s) {
   using elem_t = typename T::elem_t;
@@ -313,7 +314,8 @@ __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_pool_kernel(
   __shared__ __attribute__((aligned(16))) elem_t sQ[MAXRB * M * QS];
   __shared__ float sL[MAXRB * M];
 
-  const TileInfo ti = tile_info(Dsc, blockIdx.x);
+  const int tile = tile0 + (int)blockIdx.x;
+  const TileInfo ti = tile_info(Dsc, tile);
   const int gw = NBC > 0 ? NBC * M : Dsc.gw;
   const int nrb = NBC > 0 ? NBC : gw / M;
   const float c = kLog2e / sqrtf((float)D);
@@ -421,39 +423,45 @@ size_t kvc_scores_workspace(const KvcDesc& D) {
          up(sizeof(float2) * (size_t)D.total_tiles * D.gw);
 }
 
+// Units [u0, u1) must lie in one sequence.
 template <class T, int Dm, int NBC>
-static void launch_pair(const KvcDesc& D, const void* q, const void* k, float* s,
+static void launch_pair(const KvcDesc& D, int u0, int u1, const void* q, const void* k, float* s,
                         float2* partials, float* lse2, hipStream_t st) {
   using elem_t = typename T::elem_t;
-  hipLaunchKernelGGL((kvc_score_stats_kernel<T, Dm, NBC>), dim3(D.total_tiles), dim3(SCORE_THREADS),
-                     0, st, D, (const elem_t*)q, (const elem_t*)k, partials);
-  hipLaunchKernelGGL(kvc_score_lse_kernel, dim3(D.n_units), dim3(KVC_MAX_GW), 0, st, D,
+  const int seq = u0 / D.upseq;
+  const int tpu = kvc_tiles_per_unit(D.L[seq]);
+  const int t0 = D.tile_base[seq] + (u0 - seq * D.upseq) * tpu;
+  const int nt = (u1 - u0) * tpu;
+  hipLaunchKernelGGL((kvc_score_stats_kernel<T, Dm, NBC>), dim3(nt), dim3(SCORE_THREADS), 0, st, D,
+                     t0, (const elem_t*)q, (const elem_t*)k, partials);
+  hipLaunchKernelGGL(kvc_score_lse_kernel, dim3(u1 - u0), dim3(KVC_MAX_GW), 0, st, D, u0,
                      kLog2e / sqrtf((float)Dm), (const float2*)partials, lse2);
-  hipLaunchKernelGGL((kvc_score_pool_kernel<T, Dm, NBC>), dim3(D.total_tiles), dim3(SCORE_THREADS),
-                     0, st, D, (const elem_t*)q, (const elem_t*)k, (const float*)lse2, s);
+  hipLaunchKernelGGL((kvc_score_pool_kernel<T, Dm, NBC>), dim3(nt), dim3(SCORE_THREADS), 0, st, D,
+                     t0, (const elem_t*)q, (const elem_t*)k, (const float*)lse2, s);
 }
 
 template <int Dm>
-static void launch_bf16(const KvcDesc& D, const void* q, const void* k, float* s,
+static void launch_bf16(const KvcDesc& D, int u0, int u1, const void* q, const void* k, float* s,
                         float2* partials, float* lse2, hipStream_t st) {
   switch (D.gw / 32) {
-    case 1: launch_pair<TBf16, Dm, 1>(D, q, k, s, partials, lse2, st); break;
-    case 2: launch_pair<TBf16, Dm, 2>(D, q, k, s, partials, lse2, st); break;
-    case 3: launch_pair<TBf16, Dm, 3>(D, q, k, s, partials, lse2, st); break;
-    case 4: launch_pair<TBf16, Dm, 4>(D, q, k, s, partials, lse2, st); break;
-    case 5: launch_pair<TBf16, Dm, 5>(D, q, k, s, partials, lse2, st); break;
-    case 6: launch_pair<TBf16, Dm, 6>(D, q, k, s, partials, lse2, st); break;
-    case 7: launch_pair<TBf16, Dm, 7>(D, q, k, s, partials, lse2, st); break;
-    default: launch_pair<TBf16, Dm, 8>(D, q, k, s, partials, lse2, st); break;
+    case 1: launch_pair<TBf16, Dm, 1>(D, u0, u1, q, k, s, partials, lse2, st); break;
+    case 2: launch_pair<TBf16, Dm, 2>(D, u0, u1, q, k, s, partials, lse2, st); break;
+    case 3: launch_pair<TBf16, Dm, 3>(D, u0, u1, q, k, s, partials, lse2, st); break;
+    case 4: launch_pair<TBf16, Dm, 4>(D, u0, u1, q, k, s, partials, lse2, st); break;
+    case 5: launch_pair<TBf16, Dm, 5>(D, u0, u1, q, k, s, partials, lse2, st); break;
+    case 6: launch_pair<TBf16, Dm, 6>(D, u0, u1, q, k, s, partials, lse2, st); break;
+    case 7: launch_pair<TBf16, Dm, 7>(D, u0, u1, q, k, s, partials, lse2, st); break;
+    default: launch_pair<TBf16, Dm, 8>(D, u0, u1, q, k, s, partials, lse2, st); break;
   }
 }
 
-hipError_t kvc_launch_scores(const KvcDesc& D, const void* q, const void* k, float* s,
-                             float2* partials, float* lse2, hipStream_t st) {
-  if (D.dtype == 0 && D.d == 128) launch_bf16<128>(D, q, k, s, partials, lse2, st);
-  else if (D.dtype == 0 && D.d == 64) launch_bf16<64>(D, q, k, s, partials, lse2, st);
-  else if (D.dtype == 1 && D.d == 128) launch_pair<TF64, 128, 0>(D, q, k, s, partials, lse2, st);
-  else if (D.dtype == 1 && D.d == 64) launch_pair<TF64, 64, 0>(D, q, k, s, partials, lse2, st);
+hipError_t kvc_launch_scores(const KvcDesc& D, int u0, int u1, const void* q, const void* k,
+                             float* s, float2* partials, float* lse2, hipStream_t st) {
+  if (u1 <= u0) return hipSuccess;
+  if (D.dtype == 0 && D.d == 128) launch_bf16<128>(D, u0, u1, q, k, s, partials, lse2, st);
+  else if (D.dtype == 0 && D.d == 64) launch_bf16<64>(D, u0, u1, q, k, s, partials, lse2, st);
+  else if (D.dtype == 1 && D.d == 128) launch_pair<TF64, 128, 0>(D, u0, u1, q, k, s, partials, lse2, st);
+  else if (D.dtype == 1 && D.d == 64) launch_pair<TF64, 64, 0>(D, u0, u1, q, k, s, partials, lse2, st);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -186,6 +186,50 @@ __device__ __forceinline__ void exchange(float (&re)[V], float (&im)[V], float* 
   __syncthreads();
 }
 
+// Same exchange with real and imaginary parts moved together (when the LDS
+// buffer holds N complex values): two barriers instead of four.
+template <int V, class WF, class RF>
+__device__ __forceinline__ void exchange2(float (&re)[V], float (&im)[V], float2* lds, bool act,
+                                          WF widx, RF ridx, Extra& x) {
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < V; ++s) lds[widx(s)] = make_float2(re[s], im[s]);
+    if (x.xw >= 0) lds[x.xw] = make_float2(x.wre, x.wim);
+  }
+  __syncthreads();
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < V; ++s) {
+      const float2 v = lds[ridx(s)];
+      re[s] = v.x;
+      im[s] = v.y;
+    }
+    if (x.xr >= 0) {
+      const float2 v = lds[x.xr];
+      x.rre = v.x;
+      x.rim = v.y;
+    }
+  }
+  __syncthreads();
+}
+
+// LDS buffer: N complex values when they fit (N <= 16384, 128 KiB), else N
+// floats with the two parts exchanged in turn.
+template <int N>
+struct Xbuf {
+  static constexpr bool kPair = N <= 16384;
+  static constexpr int kFloats = kPair ? 2 * N : N;
+};
+
+template <int N, int V, class WF, class RF>
+__device__ __forceinline__ void xchg(float (&re)[V], float (&im)[V], float* lds, bool act, WF widx,
+                                     RF ridx, Extra& x) {
+  if constexpr (Xbuf<N>::kPair)
+    exchange2<V>(re, im, reinterpret_cast<float2*>(lds), act, widx, ridx, x);
+  else
+    exchange<V>(re, im, lds, act, widx, ridx, x);
+}
+
 // Forward complex FFT of length N = T V, passes from sub-length Ns on.  On
 // entry slot s holds x[in_index<V, T, N>(s)]; on exit slot s holds
 // X[ridx_final(s)] (plus the extra read of `xf`, if any).
@@ -198,11 +242,11 @@ __device__ __forceinline__ void fft_stages(float (&re)[V], float (&im)[V], float
   if (act) fft_pass<V, R, T, Ns>(re, im, t);
   auto wf = [&](int s) { return out_index<R, T, Ns>(s, t); };
   if constexpr (Nn >= N) {
-    exchange<V>(re, im, lds, act, wf, ridx_final, xf);
+    xchg<N, V>(re, im, lds, act, wf, ridx_final, xf);
   } else {
     constexpr int R2 = (N / Nn) < V ? (N / Nn) : V;
     Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
-    exchange<V>(re, im, lds, act, wf, [&](int s) { return in_index<R2, T, N>(s, t); }, none);
+    xchg<N, V>(re, im, lds, act, wf, [&](int s) { return in_index<R2, T, N>(s, t); }, none);
     fft_stages<N, V, Nn>(re, im, lds, t, act, ridx_final, xf);
   }
 }
@@ -240,6 +284,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 struct SssShared {
   double sd[SSS_WAVES];
   int si[SSS_WAVES];
+  int s3[2][3][SSS_WAVES];
   int kstar;
 };
 
@@ -394,7 +439,7 @@ __device__ __forceinline__ void smooth_unit(const KvcDesc& D, int mode, int u, c
   }
   // To the inverse's first-pass order.  Slot V/2 of thread 0 (k = 0) maps to
   // index 0 again and carries the same value as slot 0.
-  exchange<V>(re, im, lds, act, pair_idx, [&](int s) { return in_index<V, T, N>(s, t); }, xi);
+  xchg<N, V>(re, im, lds, act, pair_idx, [&](int s) { return in_index<V, T, N>(s, t); }, xi);
 
   // Inverse FFT as conj(FFT(conj(x))) / N, ending in natural chunks
   // (slot s holds index tV + s).
@@ -429,7 +474,8 @@ __device__ __forceinline__ void smooth_unit(const KvcDesc& D, int mode, int u, c
 template <int N, int V>
 __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, float (&re)[V], float (&im)[V],
                             const int32_t* budgets, const int64_t* offsets, int32_t* idx_out,
-                            SssShared& sh, int t, bool act) {
+                            SssShared& sh, int* stage, int t, bool act) {
+  constexpr int kStage = Xbuf<N>::kFloats;  // the FFT exchange buffer, free by now
   constexpr int L = 2 * N;
   const int w = D.window;
   const int ncand = L - w;
@@ -446,18 +492,23 @@ __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, float (&re)
 #define KEY(s) __float_as_uint(((s) & 1) ? im[(s) >> 1] : re[(s) >> 1])
   const int p0 = 2 * V * t;  // first position held by this thread
 
-  // Largest T with #{key >= T} >= k, bit by bit from the top.
+  // Largest T with #{key >= T} >= k, bit by bit from the top; one barrier
+  // per bit (the reduction slots alternate between bits).
   uint32_t thr = 0;
-  int tot;
   if (k > 0 && k < ncand) {
+    const int nval = act ? min(2 * V, max(0, ncand - p0)) : 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t c = thr | (1u << bit);
       int cnt = 0;
-      if (act) {
 #pragma unroll
-        for (int s = 0; s < 2 * V; ++s) cnt += (p0 + s < ncand) && (KEY(s) >= c);
-      }
-      block_scan<int>(cnt, sh.si, &tot);
+      for (int s = 0; s < 2 * V; ++s) cnt += (s < nval) & (KEY(s) >= c);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+      if ((threadIdx.x & 63) == 0) sh.s3[bit & 1][0][threadIdx.x >> 6] = cnt;
+      __syncthreads();
+      int tot = 0;
+#pragma unroll
+      for (int i = 0; i < SSS_WAVES; ++i) tot += sh.s3[bit & 1][0][i];
       if (tot >= k) thr = c;
     }
   }
@@ -501,7 +552,19 @@ __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, float (&re)
   }
   int nsel_total;
   const int base = block_scan<int>(nsel, sh.si, &nsel_total);
-  if (act) {
+  if (b <= kStage) {
+    // Compact into LDS, then one coalesced copy of the b positions.
+    if (act) {
+      int o = 0;
+#pragma unroll
+      for (int s = 0; s < 2 * V; ++s) {
+        const bool sel = (s < 32) ? ((selmask_lo >> s) & 1u) : ((selmask_hi >> (s - 32)) & 1u);
+        if (sel && base + o < b) stage[base + (o++)] = p0 + s;
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < b; i += SSS_T) idx_out[off + i] = stage[i];
+  } else if (act) {
     int o = 0;
 #pragma unroll
     for (int s = 0; s < 2 * V; ++s) {
@@ -529,15 +592,12 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_select_kernel(
   constexpr int L = 2 * N;
   constexpr int V = kvc_sss_v(N);
   constexpr int T = N / V;
-  __shared__ float lds[N];
+  __shared__ __attribute__((aligned(16))) float lds[Xbuf<N>::kFloats];
   __shared__ SssShared sh;
-  // Units in descending-L order (sequences sorted on the host); this launch
-  // covers the ones of length L, starting at position unit0.
-  const int pos = unit0 + blockIdx.x;
-  const int rank = pos / D.upseq;
-  const int within = pos - rank * D.upseq;
-  const int seq = D.seq_order[rank];
-  const int u = seq * D.upseq + within;
+  // This launch covers units unit0 .. unit0 + gridDim.x - 1 of one sequence.
+  const int u = unit0 + (int)blockIdx.x;
+  const int seq = u / D.upseq;
+  const int within = u - seq * D.upseq;
   const int64_t row = D.srow_base[seq] + (int64_t)within * L;
   const int t = threadIdx.x;
   const bool act = t < T;
@@ -554,41 +614,36 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_select_kernel(
       im[s] = v.y;
     }
   }
-  if (mode & 2) select_unit<N, V>(D, u, re, im, budgets, offsets, idx_out, sh, t, act);
+  if (mode & 2) {
+    __syncthreads();  // the exchange buffer becomes the output staging area
+    select_unit<N, V>(D, u, re, im, budgets, offsets, idx_out, sh, reinterpret_cast<int*>(lds), t,
+                      act);
+  }
 }
 
-hipError_t kvc_launch_sss_select(const KvcDesc& D, int mode, const float* s_in,
+// Units [u0, u1) must lie in one sequence.
+hipError_t kvc_launch_sss_select(const KvcDesc& D, int u0, int u1, int mode, const float* s_in,
                                  float* s_hat_out, int32_t* kstar_out, const int32_t* budgets,
                                  const int64_t* offsets, int32_t* idx_out, hipStream_t st) {
-  // Sequences are ordered by descending L, so each length is a contiguous
-  // range of unit positions: one launch per distinct length.
-  int r = 0;
-  while (r < D.n_seq) {
-    const int L = D.L[D.seq_order[r]];
-    int r2 = r;
-    while (r2 < D.n_seq && D.L[D.seq_order[r2]] == L) ++r2;
-    const int unit0 = r * D.upseq, nunits = (r2 - r) * D.upseq;
-    void (*kern)(KvcDesc, int, int, const float*, float*, int32_t*, const int32_t*,
-                 const int64_t*, int32_t*) = nullptr;
-    switch (L) {
-      case 64: kern = kvc_sss_select_kernel<5>; break;
-      case 128: kern = kvc_sss_select_kernel<6>; break;
-      case 256: kern = kvc_sss_select_kernel<7>; break;
-      case 512: kern = kvc_sss_select_kernel<8>; break;
-      case 1024: kern = kvc_sss_select_kernel<9>; break;
-      case 2048: kern = kvc_sss_select_kernel<10>; break;
-      case 4096: kern = kvc_sss_select_kernel<11>; break;
-      case 8192: kern = kvc_sss_select_kernel<12>; break;
-      case 16384: kern = kvc_sss_select_kernel<13>; break;
-      case 32768: kern = kvc_sss_select_kernel<14>; break;
-      case 65536: kern = kvc_sss_select_kernel<15>; break;
-      default: return hipErrorInvalidValue;
-    }
-    hipLaunchKernelGGL(kern, dim3(nunits), dim3(SSS_T), 0, st, D, mode, unit0, s_in, s_hat_out,
-                       kstar_out, budgets, offsets, idx_out);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    r = r2;
+  if (u1 <= u0) return hipSuccess;
+  const int L = D.L[u0 / D.upseq];
+  void (*kern)(KvcDesc, int, int, const float*, float*, int32_t*, const int32_t*, const int64_t*,
+               int32_t*) = nullptr;
+  switch (L) {
+    case 64: kern = kvc_sss_select_kernel<5>; break;
+    case 128: kern = kvc_sss_select_kernel<6>; break;
+    case 256: kern = kvc_sss_select_kernel<7>; break;
+    case 512: kern = kvc_sss_select_kernel<8>; break;
+    case 1024: kern = kvc_sss_select_kernel<9>; break;
+    case 2048: kern = kvc_sss_select_kernel<10>; break;
+    case 4096: kern = kvc_sss_select_kernel<11>; break;
+    case 8192: kern = kvc_sss_select_kernel<12>; break;
+    case 16384: kern = kvc_sss_select_kernel<13>; break;
+    case 32768: kern = kvc_sss_select_kernel<14>; break;
+    case 65536: kern = kvc_sss_select_kernel<15>; break;
+    default: return hipErrorInvalidValue;
   }
-  return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(u1 - u0), dim3(SSS_T), 0, st, D, mode, u0, s_in, s_hat_out,
+                     kstar_out, budgets, offsets, idx_out);
+  return hipGetLastError();
 }

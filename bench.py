@@ -105,6 +105,8 @@ def main():
     ap.add_argument("--config", default="omni30b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -163,6 +165,16 @@ def main():
     path_gbs = ab["total"] / (ms * 1e-3) / 1e9
     log(f"[bench] {ms:.3f} ms/step, {value:.4g} tokens·heads/s, path {path_gbs:.0f} GB/s "
         f"({100 * path_gbs / HBM_PEAK_GBS:.1f} % of HBM peak)")
+
+    if args.calib_copy:
+        # A plain copy of known size: what HBM counters read for it scales
+        # the counters of the path's kernels to bytes.
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # Per-stage timing with events on the same stream (each stage entry point
     # launches that step's kernels only).
