@@ -24,8 +24,9 @@ KVC_ERR_HIP = 5
 KVC_BF16 = 0
 KVC_F32 = 1
 
-EXPORTS = ("kvc_plan", "kvc_compress", "kvc_scores", "kvc_smooth", "kvc_budget",
-           "kvc_select", "kvc_gather", "kvc_status_str", "kvc_last_hip_error")
+EXPORTS = ("kvc_plan", "kvc_compress", "kvc_scores", "kvc_score_stats", "kvc_score_pool",
+           "kvc_smooth", "kvc_budget", "kvc_select", "kvc_gather", "kvc_status_str",
+           "kvc_last_hip_error")
 
 
 class kvc_params(ctypes.Structure):
@@ -72,11 +73,13 @@ def lib():
             L.kvc_compress.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, ctypes.c_size_t, _vp]
             L.kvc_scores.argtypes = [prob, prm, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+            L.kvc_score_stats.argtypes = [prob, prm, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+            L.kvc_score_pool.argtypes = [prob, prm, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
             L.kvc_smooth.argtypes = [prob, prm, _vp, _vp, _vp, _vp]
             L.kvc_budget.argtypes = [prob, prm, _vp, _vp, _vp, _vp]
             L.kvc_select.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp]
             L.kvc_gather.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
-            for name in EXPORTS[:7]:
+            for name in EXPORTS[:9]:
                 getattr(L, name).restype = ctypes.c_int
             L.kvc_status_str.argtypes = [ctypes.c_int]
             L.kvc_status_str.restype = ctypes.c_char_p

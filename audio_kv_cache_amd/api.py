@@ -127,6 +127,20 @@ def kvc_scores(spec, params, q, k, s_out, workspace, stream=None):
             "kvc_scores")
 
 
+def kvc_score_stats(spec, params, q, k, workspace, stream=None):
+    C.check(C.lib().kvc_score_stats(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(q),
+                                    _ptr(k), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)),
+            "kvc_score_stats")
+
+
+def kvc_score_pool(spec, params, q, k, s_out, workspace, stream=None):
+    C.check(C.lib().kvc_score_pool(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(q),
+                                   _ptr(k), _ptr(s_out), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+            "kvc_score_pool")
+
+
 def kvc_smooth(spec, params, s, s_hat, kstar, stream=None):
     C.check(C.lib().kvc_smooth(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(s),
                                _ptr(s_hat), _ptr(kstar), _stream(stream)), "kvc_smooth")

@@ -195,13 +195,13 @@ extern "C" kvc_status kvc_compress(const kvc_problem* prob, const kvc_params* pa
   return hip_status(e);
 }
 
-extern "C" kvc_status kvc_scores(const kvc_problem* prob, const kvc_params* params,
-                                 const void* q_window, const void* k, float* s_out,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+static kvc_status scores_common(const kvc_problem* prob, const kvc_params* params,
+                                const void* q_window, const void* k, float* s_out,
+                                void* workspace, size_t workspace_bytes, void* stream, int which) {
   KvcDesc D;
   kvc_status st = make_desc(prob, params, &D);
   if (st != KVC_OK) return st;
-  if (!q_window || !k || !s_out || !workspace) return KVC_ERR_INVALID_ARG;
+  if (!q_window || !k || !workspace || ((which & 2) && !s_out)) return KVC_ERR_INVALID_ARG;
   if (!aligned16(q_window) || !aligned16(k) || ((uintptr_t)workspace & 255u) ||
       ((uintptr_t)s_out & 7u))
     return KVC_ERR_INVALID_ARG;
@@ -209,10 +209,28 @@ extern "C" kvc_status kvc_scores(const kvc_problem* prob, const kvc_params* para
   const Carve c = carve(D, workspace);
   for (int seq = 0; seq < D.n_seq; ++seq) {
     const hipError_t e = kvc_launch_scores(D, seq * D.upseq, (seq + 1) * D.upseq, q_window, k,
-                                           s_out, c.partials, c.lse2, (hipStream_t)stream);
+                                           s_out, c.partials, c.lse2, (hipStream_t)stream, which);
     if (e != hipSuccess) return hip_status(e);
   }
   return KVC_OK;
+}
+
+extern "C" kvc_status kvc_scores(const kvc_problem* prob, const kvc_params* params,
+                                 const void* q_window, const void* k, float* s_out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return scores_common(prob, params, q_window, k, s_out, workspace, workspace_bytes, stream, 3);
+}
+
+extern "C" kvc_status kvc_score_stats(const kvc_problem* prob, const kvc_params* params,
+                                      const void* q_window, const void* k, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return scores_common(prob, params, q_window, k, nullptr, workspace, workspace_bytes, stream, 1);
+}
+
+extern "C" kvc_status kvc_score_pool(const kvc_problem* prob, const kvc_params* params,
+                                     const void* q_window, const void* k, float* s_out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return scores_common(prob, params, q_window, k, s_out, workspace, workspace_bytes, stream, 2);
 }
 
 extern "C" kvc_status kvc_smooth(const kvc_problem* prob, const kvc_params* params,

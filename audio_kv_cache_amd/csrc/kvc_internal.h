@@ -45,8 +45,10 @@ hipError_t kvc_launch_budget(const KvcDesc& D, const float* S, int32_t* budgets,
                              int64_t* offsets, hipStream_t st);
 // Range launches: units [u0, u1) (natural (seq, layer, head) order) must lie
 // within one sequence for the score and smoothing/selection launches.
+// which: 1 = statistics pass (+ LSE fold), 2 = pooling pass, 3 = both.
 hipError_t kvc_launch_scores(const KvcDesc& D, int u0, int u1, const void* q, const void* k,
-                             float* s, float2* partials, float* lse2, hipStream_t st);
+                             float* s, float2* partials, float* lse2, hipStream_t st,
+                             int which = 3);
 // mode bit 0: smooth (else read s_hat from s_in); bit 1: select;
 // bit 2: export s_hat and kstar.
 hipError_t kvc_launch_sss_select(const KvcDesc& D, int u0, int u1, int mode, const float* s_in,

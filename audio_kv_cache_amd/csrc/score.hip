@@ -91,6 +91,17 @@ template <> struct Tiling<TBf16, 128> { static constexpr int RB = 2, CB = 1; };
 template <> struct Tiling<TF64, 64> { static constexpr int RB = 1, CB = 1; };
 template <> struct Tiling<TF64, 128> { static constexpr int RB = 1, CB = 1; };
 
+// The dispatcher hands workgroup b of a launch to XCD b % 8, and each XCD
+// has its own L2.  Renumber so that XCD x runs one contiguous range of tiles:
+// the tiles of a unit then share one L2, which serves the unit's window
+// queries after the first read instead of every XCD fetching them again.
+// A bijection on [0, n) for any n.
+__device__ inline int xcd_local_tile(int b, int n) {
+  constexpr int kXcds = 8;
+  const int x = b % kXcds, per = n / kXcds, rem = n % kXcds;
+  return x * per + (x < rem ? x : rem) + b / kXcds;
+}
+
 struct TileInfo {
   int seq, u, l, h, t, tpu, L, keys, key0;
 };
@@ -155,7 +166,7 @@ __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_stats_kernel
   __shared__ __attribute__((aligned(16))) elem_t sQ[MAXCB * M * QS];
   __shared__ float2 sStat[SCORE_WAVES][MAXCB * M];
 
-  const int tile = tile0 + (int)blockIdx.x;
+  const int tile = tile0 + xcd_local_tile((int)blockIdx.x, (int)gridDim.x);
   const TileInfo ti = tile_info(Dsc, tile);
   const int gw = NBC > 0 ? NBC * M : Dsc.gw;
   const int ncb = NBC > 0 ? NBC : gw / M;
@@ -314,7 +325,7 @@ __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_pool_kernel(
   __shared__ __attribute__((aligned(16))) elem_t sQ[MAXRB * M * QS];
   __shared__ float sL[MAXRB * M];
 
-  const int tile = tile0 + (int)blockIdx.x;
+  const int tile = tile0 + xcd_local_tile((int)blockIdx.x, (int)gridDim.x);
   const TileInfo ti = tile_info(Dsc, tile);
   const int gw = NBC > 0 ? NBC * M : Dsc.gw;
   const int nrb = NBC > 0 ? NBC : gw / M;
@@ -426,42 +437,45 @@ size_t kvc_scores_workspace(const KvcDesc& D) {
 // Units [u0, u1) must lie in one sequence.
 template <class T, int Dm, int NBC>
 static void launch_pair(const KvcDesc& D, int u0, int u1, const void* q, const void* k, float* s,
-                        float2* partials, float* lse2, hipStream_t st) {
+                        float2* partials, float* lse2, hipStream_t st, int which) {
   using elem_t = typename T::elem_t;
   const int seq = u0 / D.upseq;
   const int tpu = kvc_tiles_per_unit(D.L[seq]);
   const int t0 = D.tile_base[seq] + (u0 - seq * D.upseq) * tpu;
   const int nt = (u1 - u0) * tpu;
-  hipLaunchKernelGGL((kvc_score_stats_kernel<T, Dm, NBC>), dim3(nt), dim3(SCORE_THREADS), 0, st, D,
-                     t0, (const elem_t*)q, (const elem_t*)k, partials);
-  hipLaunchKernelGGL(kvc_score_lse_kernel, dim3(u1 - u0), dim3(KVC_MAX_GW), 0, st, D, u0,
-                     kLog2e / sqrtf((float)Dm), (const float2*)partials, lse2);
-  hipLaunchKernelGGL((kvc_score_pool_kernel<T, Dm, NBC>), dim3(nt), dim3(SCORE_THREADS), 0, st, D,
-                     t0, (const elem_t*)q, (const elem_t*)k, (const float*)lse2, s);
+  if (which & 1) {
+    hipLaunchKernelGGL((kvc_score_stats_kernel<T, Dm, NBC>), dim3(nt), dim3(SCORE_THREADS), 0, st,
+                       D, t0, (const elem_t*)q, (const elem_t*)k, partials);
+    hipLaunchKernelGGL(kvc_score_lse_kernel, dim3(u1 - u0), dim3(KVC_MAX_GW), 0, st, D, u0,
+                       kLog2e / sqrtf((float)Dm), (const float2*)partials, lse2);
+  }
+  if (which & 2)
+    hipLaunchKernelGGL((kvc_score_pool_kernel<T, Dm, NBC>), dim3(nt), dim3(SCORE_THREADS), 0, st,
+                       D, t0, (const elem_t*)q, (const elem_t*)k, (const float*)lse2, s);
 }
 
 template <int Dm>
 static void launch_bf16(const KvcDesc& D, int u0, int u1, const void* q, const void* k, float* s,
-                        float2* partials, float* lse2, hipStream_t st) {
+                        float2* partials, float* lse2, hipStream_t st, int which) {
   switch (D.gw / 32) {
-    case 1: launch_pair<TBf16, Dm, 1>(D, u0, u1, q, k, s, partials, lse2, st); break;
-    case 2: launch_pair<TBf16, Dm, 2>(D, u0, u1, q, k, s, partials, lse2, st); break;
-    case 3: launch_pair<TBf16, Dm, 3>(D, u0, u1, q, k, s, partials, lse2, st); break;
-    case 4: launch_pair<TBf16, Dm, 4>(D, u0, u1, q, k, s, partials, lse2, st); break;
-    case 5: launch_pair<TBf16, Dm, 5>(D, u0, u1, q, k, s, partials, lse2, st); break;
-    case 6: launch_pair<TBf16, Dm, 6>(D, u0, u1, q, k, s, partials, lse2, st); break;
-    case 7: launch_pair<TBf16, Dm, 7>(D, u0, u1, q, k, s, partials, lse2, st); break;
-    default: launch_pair<TBf16, Dm, 8>(D, u0, u1, q, k, s, partials, lse2, st); break;
+    case 1: launch_pair<TBf16, Dm, 1>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 2: launch_pair<TBf16, Dm, 2>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 3: launch_pair<TBf16, Dm, 3>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 4: launch_pair<TBf16, Dm, 4>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 5: launch_pair<TBf16, Dm, 5>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 6: launch_pair<TBf16, Dm, 6>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 7: launch_pair<TBf16, Dm, 7>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    default: launch_pair<TBf16, Dm, 8>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
   }
 }
 
 hipError_t kvc_launch_scores(const KvcDesc& D, int u0, int u1, const void* q, const void* k,
-                             float* s, float2* partials, float* lse2, hipStream_t st) {
+                             float* s, float2* partials, float* lse2, hipStream_t st, int which) {
   if (u1 <= u0) return hipSuccess;
-  if (D.dtype == 0 && D.d == 128) launch_bf16<128>(D, u0, u1, q, k, s, partials, lse2, st);
-  else if (D.dtype == 0 && D.d == 64) launch_bf16<64>(D, u0, u1, q, k, s, partials, lse2, st);
-  else if (D.dtype == 1 && D.d == 128) launch_pair<TF64, 128, 0>(D, u0, u1, q, k, s, partials, lse2, st);
-  else if (D.dtype == 1 && D.d == 64) launch_pair<TF64, 64, 0>(D, u0, u1, q, k, s, partials, lse2, st);
+  if (D.dtype == 0 && D.d == 128) launch_bf16<128>(D, u0, u1, q, k, s, partials, lse2, st, which);
+  else if (D.dtype == 0 && D.d == 64) launch_bf16<64>(D, u0, u1, q, k, s, partials, lse2, st, which);
+  else if (D.dtype == 1 && D.d == 128) launch_pair<TF64, 128, 0>(D, u0, u1, q, k, s, partials, lse2, st, which);
+  else if (D.dtype == 1 && D.d == 64) launch_pair<TF64, 64, 0>(D, u0, u1, q, k, s, partials, lse2, st, which);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

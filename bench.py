@@ -30,6 +30,9 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+# MI355X dense matrix peaks, TFLOP/s: bf16 MFMA; fp32 inputs run on the fp64
+# MFMA (78.6 TFLOP/s dense fp64)
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 78.6}
 ROOT = pathlib.Path(__file__).resolve().parent
 
 
@@ -40,14 +43,26 @@ def log(*a):
 def algorithmic_bytes(cfg, hdr, budgets):
     e = 2 if cfg.dtype == "bf16" else 4
     d = cfg.head_dim
-    gwde = cfg.gqa * cfg.n_window * d * e
+    gw = cfg.gqa * cfg.n_window
     per_seq_units = cfg.n_layers * cfg.n_kv_heads
-    k_read = sum(int(L) * d * e * per_seq_units for L in hdr.lengths)
+    n_units = per_seq_units * cfg.n_seq
+    tok = sum(int(L) for L in hdr.lengths) * per_seq_units      # sum of L over units
+    k_read = tok * d * e
+    q_read = gw * d * e * n_units
     b = np.asarray(budgets, dtype=np.int64)
     kept = int(b.sum())
-    return dict(k_scores=k_read, gather=4 * kept * d * e + 4 * kept,
-                q=gwde * per_seq_units * cfg.n_seq, total=k_read + 4 * kept * d * e + 4 * kept
-                + gwde * per_seq_units * cfg.n_seq)
+    gather = 4 * kept * d * e + 4 * kept
+    return dict(
+        total=k_read + gather + q_read, gather=gather,
+        # pooling pass: K and the window queries read, one LSE per query read,
+        # the fp32 score rows written
+        pool=k_read + q_read + 4 * gw * n_units + 4 * tok,
+        # statistics pass: K and queries read, one (max, sum) pair per query
+        # and 1024-key tile written
+        stats=k_read + q_read + 8 * gw * sum(-(-int(L) // 1024) for L in hdr.lengths)
+        * per_seq_units,
+        # both passes: one G*W x d by d x L product per unit
+        score_flops=2 * gw * d * tok)
 
 
 def source_hash(*names):
@@ -176,18 +191,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # Per-stage timing with events on the same stream (each stage entry point
-    # launches that step's kernels only).
+    # Per-kernel timing with events on the stream the kernels run on: each
+    # stage entry point launches that step's kernels only (kvc_score_stats
+    # launches the statistics kernel and the small LSE fold).
     stages = {}
     if not args.no_stages:
         s_rows = torch.empty(spec.score_rows(), dtype=torch.float32, device="cuda")
         sh_rows = torch.empty_like(s_rows)
         kst = torch.empty(spec.n_units, dtype=torch.int32, device="cuda")
-        api.kvc_scores(spec, prm, q, k, s_rows, out["workspace"], stream)
+        ws = out["workspace"]
+        api.kvc_scores(spec, prm, q, k, s_rows, ws, stream)
         api.kvc_smooth(spec, prm, s_rows, sh_rows, kst, stream)
         calls = {
             "budget": lambda: api.kvc_budget(spec, prm, S, out["budgets"], out["offsets"], stream),
-            "scores": lambda: api.kvc_scores(spec, prm, q, k, s_rows, out["workspace"], stream),
+            "score_stats": lambda: api.kvc_score_stats(spec, prm, q, k, ws, stream),
+            "score_pool": lambda: api.kvc_score_pool(spec, prm, q, k, s_rows, ws, stream),
             "smooth": lambda: api.kvc_smooth(spec, prm, s_rows, sh_rows, kst, stream),
             "select": lambda: api.kvc_select(spec, prm, sh_rows, out["budgets"], out["offsets"],
                                              out["idx"], stream),
@@ -205,14 +223,39 @@ def main():
             stages[name] = ev0.elapsed_time(ev1) / args.steps
         log("[bench] stage ms: " + ", ".join(f"{n} {t:.3f}" for n, t in stages.items()))
 
-    # Roofline of the dominant kernel: the gather (bytes only, HBM bound).
-    roof = None
+    # Rooflines.  The dominant kernel is the pooling pass of the scores; its
+    # tighter bound is HBM (K must be streamed) unless the MFMA work takes
+    # longer at peak.  One launch per sequence; per-launch figures are the
+    # step's totals divided by the launches.
+    roof, others = None, {}
     if stages:
-        g_ms = stages["gather"]
-        g_gbs = ab["gather"] / (g_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "kvc_gather_kernel<256>", "achieved": round(g_gbs, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
-                "traffic": committed_traffic("gather.hip", "kvc_gather_kernel", cfg.name)}
+        launches = cfg.n_seq
+
+        def hbm(name, kernel, nbytes, ms, src):
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "traffic": committed_traffic(src, kernel.split("<")[0], cfg.name),
+                    "algorithmic_bytes": nbytes // launches, "avg_launch_us":
+                        round(ms * 1e3 / launches, 1)}
+
+        t_hbm = ab["pool"] / (HBM_PEAK_GBS * 1e9)
+        t_mfma = ab["score_flops"] / (MFMA_PEAK_TFLOPS[cfg.dtype] * 1e12)
+        pool_kernel = f"kvc_score_pool_kernel<{cfg.dtype}, d={cfg.head_dim}, GW={cfg.gqa * cfg.n_window}>"
+        if t_hbm >= t_mfma:
+            roof = hbm("score_pool", pool_kernel, ab["pool"], stages["score_pool"], "score.hip")
+        else:
+            tf = ab["score_flops"] / (stages["score_pool"] * 1e-3) / 1e12
+            roof = {"bound": "mfma", "kernel": pool_kernel, "achieved": round(tf, 2),
+                    "peak": MFMA_PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s",
+                    "frac": round(tf / MFMA_PEAK_TFLOPS[cfg.dtype], 4),
+                    "traffic": committed_traffic("score.hip", "kvc_score_pool_kernel", cfg.name)}
+        roof["mfma_frac"] = round(ab["score_flops"] / (stages["score_pool"] * 1e-3) / 1e12
+                                  / MFMA_PEAK_TFLOPS[cfg.dtype], 4)
+        others["score_stats"] = hbm("score_stats", "kvc_score_stats_kernel", ab["stats"],
+                                    stages["score_stats"], "score.hip")
+        others["gather"] = hbm("gather", "kvc_gather_kernel<256>", ab["gather"], stages["gather"],
+                               "gather.hip")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -236,6 +279,7 @@ def main():
                      "frac": round(path_gbs / HBM_PEAK_GBS, 4)},
         "stage_ms": {k2: round(v2, 4) for k2, v2 in stages.items()},
         "roofline": roof,
+        "roofline_other_kernels": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

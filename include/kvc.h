@@ -123,6 +123,18 @@ kvc_status kvc_compress(const kvc_problem *prob, const kvc_params *params,
 kvc_status kvc_scores(const kvc_problem *prob, const kvc_params *params,
                       const void *q_window, const void *k, float *s,
                       void *workspace, size_t workspace_bytes, void *stream);
+/* The two passes of step 1, as kvc_scores runs them:
+ * kvc_score_stats: per window query, the log-sum-exp of its logits over the
+ *                  L keys, left in `workspace` (log2 units) for
+ * kvc_score_pool:  the pooled softmax rows s, given that workspace.
+ * kvc_score_stats followed by kvc_score_pool on the same workspace equals
+ * kvc_scores. */
+kvc_status kvc_score_stats(const kvc_problem *prob, const kvc_params *params,
+                           const void *q_window, const void *k, void *workspace,
+                           size_t workspace_bytes, void *stream);
+kvc_status kvc_score_pool(const kvc_problem *prob, const kvc_params *params,
+                          const void *q_window, const void *k, float *s,
+                          void *workspace, size_t workspace_bytes, void *stream);
 kvc_status kvc_smooth(const kvc_problem *prob, const kvc_params *params,
                       const float *s, float *s_hat, int32_t *kstar,
                       void *stream);

@@ -86,6 +86,15 @@ class Dev:
         torch.cuda.synchronize()
         return s.cpu().numpy()
 
+    def scores_two_pass(self):
+        """Step 1 through kvc_score_stats then kvc_score_pool."""
+        s = torch.empty(self.spec.score_rows(), dtype=torch.float32, device="cuda")
+        ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        api.kvc_score_stats(self.spec, self.params, self.q, self.k, ws)
+        api.kvc_score_pool(self.spec, self.params, self.q, self.k, s, ws)
+        torch.cuda.synchronize()
+        return s.cpu().numpy()
+
     def smooth(self, s_flat: np.ndarray):
         s = torch.from_numpy(np.ascontiguousarray(s_flat, dtype=np.float32)).cuda()
         sh = torch.empty_like(s)

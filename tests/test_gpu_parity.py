@@ -244,6 +244,19 @@ def test_scores_qwen7b_sampled():
     _check_scores(D, [(0, 0, 0), (0, 13, 2), (0, 27, 3)])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_scores_two_pass_entry_points(dtype):
+    say(f"[scores] stats + pool entry points, {dtype}")
+    cfg = small(dtype=dtype, n_seq=2, lengths=(4096, 1024), retention=(0.5, 0.5), base_ratio=0.0)
+    D = Dev(synth.problem(cfg))
+    s2 = D.scores_two_pass()
+    assert np.array_equal(s2, D.scores())
+    for (i, l, h) in D.units():
+        qu, ku, _ = O.unit_inputs(D.prob, i, l, h)
+        ref = O.scores(O.widen(qu, D.dtype).reshape(-1, D.cfg.head_dim), O.widen(ku, D.dtype))
+        assert rel_err(D.row(s2, i, l, h), ref) <= TOL[D.dtype]
+
+
 def test_scores_no_sink_variant():
     say("[scores] qwen7b-shaped, no sink")
     cfg = dataclasses.replace(synth.CONFIGS["qwen7b"], n_layers=2, sink_beta=0.0)
