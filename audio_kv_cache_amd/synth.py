@@ -209,3 +209,118 @@ def problem(cfg: Config, *, sink_beta=None, hdr: Header | None = None) -> Proble
     with _cf.ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(fill, jobs))
     return Problem(hdr, q, k, v)
+
+
+# ---------------------------------------------------------------------------
+# Decode-step inputs (decayed-eviction path)
+# ---------------------------------------------------------------------------
+# One cache per (sequence, layer, KV head) holding n rows, the last being the
+# new token.  Rows carry the same drift + first-position sink as the prefill
+# keys; the new token's G query heads are N(0, I) + drift[n - 1] + v.  The
+# running importance A_prev of the n - 1 older rows stands in for what
+# earlier decode steps accumulated: Exp(1) * 20 / n per row (a total near
+# 1 / (1 - gamma) = 20) plus U(1, 4) on the four leading rows.  Capacity
+# padding rows are zero.
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    index: int
+    n_seq: int
+    n_layers: int
+    n_kv_heads: int
+    gqa: int
+    head_dim: int
+    dtype: str
+    lens: tuple              # rows per cache, new token included, per sequence
+    budgets: tuple           # cache budget B per sequence
+    capacity: int
+    gamma: float = 0.95
+    n_sink: int = 4
+    recent_frac: float = 0.2
+    sink_beta: float = SINK_BETA
+
+
+DECODE_CONFIGS = {
+    # parity-sized, fp32
+    "vz_tiny": DecodeConfig("vz_tiny", 10, 1, 1, 4, 1, 64, "f32", lens=(300,), budgets=(200,),
+                            capacity=320),
+    # Omni30B-shaped steady state: a 32768-token context held at a 25 %
+    # budget (8192 rows); each step appends one row and evicts one
+    "vz_omni30b": DecodeConfig("vz_omni30b", 11, 1, 48, 4, 8, 128, "bf16", lens=(8193,),
+                               budgets=(8192,), capacity=8200),
+    # first decode step after a 40 %-retention prefill of 32768 tokens
+    # (13107 rows + the new token) brought down to the 25 % budget
+    "vz_first": DecodeConfig("vz_first", 12, 1, 48, 4, 8, 128, "bf16", lens=(13108,),
+                             budgets=(8192,), capacity=13120),
+    # mixed batch: steady state, first step after prefill, still filling,
+    # exactly at budget
+    "vz_ragged": DecodeConfig("vz_ragged", 13, 4, 28, 4, 7, 128, "bf16",
+                              lens=(4097, 13108, 2000, 1024), budgets=(4096, 8192, 4096, 1024),
+                              capacity=13120),
+}
+
+
+@dataclasses.dataclass
+class DecodeProblem:
+    """q [units, G, d]; k, v [units, capacity, d]; a_prev float32
+    [units, capacity] (entries 0..n-2 meaningful)."""
+    cfg: DecodeConfig
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    a_prev: np.ndarray
+
+    @property
+    def n_units(self) -> int:
+        c = self.cfg
+        return c.n_seq * c.n_layers * c.n_kv_heads
+
+    def seq_of(self, u: int) -> int:
+        return u // (self.cfg.n_layers * self.cfg.n_kv_heads)
+
+
+def decode_cache(cfg: DecodeConfig, u: int):
+    """One cache's (q [G, d], k [n, d], v [n, d], a_prev [n - 1])."""
+    n_units = cfg.n_seq * cfg.n_layers * cfg.n_kv_heads
+    rng = np.random.default_rng(np.random.SeedSequence(2000 + cfg.index).spawn(n_units)[u])
+    seq = u // (cfg.n_layers * cfg.n_kv_heads)
+    n, d, G = int(cfg.lens[seq]), cfg.head_dim, cfg.gqa
+    periods = rng.uniform(50.0, 400.0, size=N_SINUSOIDS)
+    phases = rng.uniform(0.0, 2.0 * math.pi, size=(N_SINUSOIDS, d))
+    v = rng.standard_normal(d)
+    v /= np.linalg.norm(v)
+    kn = rng.standard_normal((n, d), dtype=np.float32)
+    qn = rng.standard_normal((G, d), dtype=np.float32)
+    vv = rng.standard_normal((n, d), dtype=np.float32)
+    a_prev = (rng.exponential(1.0, size=n - 1) * (20.0 / n)).astype(np.float32)
+    a_prev[:min(4, n - 1)] += rng.uniform(1.0, 4.0, size=min(4, n - 1)).astype(np.float32)
+    t = np.arange(n, dtype=np.float64)
+    w = 2.0 * math.pi / periods
+    A = np.concatenate([np.sin(np.outer(t, w)), np.cos(np.outer(t, w))], axis=1)
+    B = DRIFT_AMP * np.concatenate([np.cos(phases), np.sin(phases)], axis=0)
+    drift = (A @ B).astype(np.float32)
+    k = kn + drift
+    k[0] += np.float32(cfg.sink_beta * math.sqrt(d)) * v.astype(np.float32)
+    q = qn + drift[n - 1][None, :] + v.astype(np.float32)[None, :]
+    if cfg.dtype == "f32":
+        return q, k, vv, a_prev
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(vv), a_prev
+
+
+def decode_problem(cfg: DecodeConfig) -> DecodeProblem:
+    dt = np.float32 if cfg.dtype == "f32" else np.uint16
+    U = cfg.n_seq * cfg.n_layers * cfg.n_kv_heads
+    G, d, cap = cfg.gqa, cfg.head_dim, cfg.capacity
+    q = np.zeros((U, G, d), dtype=dt)
+    k = np.zeros((U, cap, d), dtype=dt)
+    v = np.zeros((U, cap, d), dtype=dt)
+    a = np.zeros((U, cap), dtype=np.float32)
+
+    def fill(u):
+        qu, ku, vu, au = decode_cache(cfg, u)
+        n = ku.shape[0]
+        q[u], k[u, :n], v[u, :n], a[u, :n - 1] = qu, ku, vu, au
+
+    with _cf.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, range(U)))
+    return DecodeProblem(cfg, q, k, v, a)
