@@ -27,6 +27,9 @@ KVC_F32 = 1
 EXPORTS = ("kvc_plan", "kvc_compress", "kvc_scores", "kvc_score_stats", "kvc_score_pool",
            "kvc_smooth", "kvc_budget", "kvc_select", "kvc_gather", "kvc_status_str",
            "kvc_last_hip_error")
+# include/kvc_voxzip.h
+VZ_EXPORTS = ("kvc_vz_plan", "kvc_vz_step", "kvc_vz_accumulate", "kvc_vz_evict",
+              "kvc_vz_gather")
 
 
 class kvc_params(ctypes.Structure):
@@ -42,6 +45,21 @@ class kvc_problem(ctypes.Structure):
                 ("seq_start", ctypes.POINTER(ctypes.c_int64)),
                 ("retention", ctypes.POINTER(ctypes.c_double)),
                 ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3)]
+
+
+class kvc_vz_params(ctypes.Structure):
+    _fields_ = [("gamma", ctypes.c_double), ("n_sink", ctypes.c_int32),
+                ("recent_frac", ctypes.c_double)]
+
+
+class kvc_vz_problem(ctypes.Structure):
+    _fields_ = [("n_seq", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("gqa_group", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("capacity", ctypes.c_int64),
+                ("len", ctypes.POINTER(ctypes.c_int64)),
+                ("budget", ctypes.POINTER(ctypes.c_int64)),
+                ("k_stride", ctypes.c_int64 * 2), ("v_stride", ctypes.c_int64 * 2)]
 
 
 class KvcError(RuntimeError):
@@ -80,6 +98,16 @@ def lib():
             L.kvc_select.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp]
             L.kvc_gather.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
             for name in EXPORTS[:9]:
+                getattr(L, name).restype = ctypes.c_int
+            vp, vq = _P(kvc_vz_problem), _P(kvc_vz_params)
+            L.kvc_vz_plan.argtypes = [vp, vq, _P(ctypes.c_int64), _P(ctypes.c_size_t)]
+            L.kvc_vz_step.argtypes = [vp, vq, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      ctypes.c_size_t, _vp]
+            L.kvc_vz_accumulate.argtypes = [vp, vq, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                            _vp]
+            L.kvc_vz_evict.argtypes = [vp, vq, _vp, _vp, _vp]
+            L.kvc_vz_gather.argtypes = [vp, vq, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+            for name in VZ_EXPORTS:
                 getattr(L, name).restype = ctypes.c_int
             L.kvc_status_str.argtypes = [ctypes.c_int]
             L.kvc_status_str.restype = ctypes.c_char_p

@@ -197,3 +197,97 @@ def compress(q, k, v, head_scores, *, gqa, seq_lens, retention, alpha=0.5, rho=0
     kvc_compress(spec, params, q, k, v, head_scores, o["k_out"], o["v_out"], o["idx"],
                  o["offsets"], o["budgets"], o["workspace"], stream)
     return o
+
+
+# ---------------------------------------------------------------------------
+# Decode-time decayed eviction (include/kvc_voxzip.h)
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class VzParams:
+    gamma: float = 0.95
+    n_sink: int = 4
+    recent_frac: float = 0.2
+
+    def c(self) -> C.kvc_vz_params:
+        return C.kvc_vz_params(float(self.gamma), int(self.n_sink), float(self.recent_frac))
+
+
+class VzSpec:
+    """Host-side kvc_vz_problem: caches [units][capacity][head_dim] for K and V
+    (or any strides with head_dim contiguous), per-sequence lengths and
+    budgets."""
+
+    def __init__(self, *, n_layers, n_kv_heads, gqa, head_dim, lens, budgets, capacity,
+                 dtype, k_stride=None, v_stride=None):
+        self.n_layers, self.n_kv_heads, self.gqa = int(n_layers), int(n_kv_heads), int(gqa)
+        self.head_dim, self.capacity = int(head_dim), int(capacity)
+        self.dtype = dtype if isinstance(dtype, str) else ("bf16" if dtype == torch.bfloat16 else "f32")
+        self._len = np.ascontiguousarray(np.asarray(lens, dtype=np.int64).reshape(-1))
+        self.n_seq = int(self._len.shape[0])
+        self._budget = np.ascontiguousarray(np.broadcast_to(
+            np.asarray(budgets, dtype=np.int64), (self.n_seq,)).copy())
+        dense = (self.capacity * self.head_dim, self.head_dim)
+        self.k_stride = tuple(int(x) for x in (k_stride or dense))
+        self.v_stride = tuple(int(x) for x in (v_stride or dense))
+
+    @property
+    def n_units(self) -> int:
+        return self.n_seq * self.n_layers * self.n_kv_heads
+
+    @property
+    def lens(self) -> np.ndarray:
+        return self._len
+
+    @property
+    def budgets(self) -> np.ndarray:
+        return self._budget
+
+    def c(self) -> C.kvc_vz_problem:
+        p = C.kvc_vz_problem()
+        p.n_seq, p.n_layers, p.n_kv_heads = self.n_seq, self.n_layers, self.n_kv_heads
+        p.gqa_group, p.head_dim = self.gqa, self.head_dim
+        p.dtype = C.KVC_BF16 if self.dtype == "bf16" else C.KVC_F32
+        p.capacity = self.capacity
+        p.len = self._len.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        p.budget = self._budget.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        for a in range(2):
+            p.k_stride[a] = self.k_stride[a]
+            p.v_stride[a] = self.v_stride[a]
+        return p
+
+
+def kvc_vz_plan(spec: VzSpec, params: VzParams):
+    """-> (new_len [n_seq] int64, workspace_bytes); host only."""
+    nl = np.zeros(spec.n_seq, dtype=np.int64)
+    ws = ctypes.c_size_t(0)
+    C.check(C.lib().kvc_vz_plan(ctypes.byref(spec.c()), ctypes.byref(params.c()),
+                                nl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                ctypes.byref(ws)), "kvc_vz_plan")
+    return nl, int(ws.value)
+
+
+def kvc_vz_step(spec, params, q, k, v, a_prev, k_out, v_out, a_out, idx_out, workspace,
+                stream=None):
+    C.check(C.lib().kvc_vz_step(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(q),
+                                _ptr(k), _ptr(v), _ptr(a_prev), _ptr(k_out), _ptr(v_out),
+                                _ptr(a_out), _ptr(idx_out), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)),
+            "kvc_vz_step")
+
+
+def kvc_vz_accumulate(spec, params, q, k, a_prev, a, workspace, stream=None):
+    C.check(C.lib().kvc_vz_accumulate(ctypes.byref(spec.c()), ctypes.byref(params.c()),
+                                      _ptr(q), _ptr(k), _ptr(a_prev), _ptr(a), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream)), "kvc_vz_accumulate")
+
+
+def kvc_vz_evict(spec, params, a, idx_out, stream=None):
+    C.check(C.lib().kvc_vz_evict(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(a),
+                                 _ptr(idx_out), _stream(stream)), "kvc_vz_evict")
+
+
+def kvc_vz_gather(spec, params, k, v, a, idx, k_out, v_out, a_out, stream=None):
+    C.check(C.lib().kvc_vz_gather(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(k),
+                                  _ptr(v), _ptr(a), _ptr(idx), _ptr(k_out), _ptr(v_out),
+                                  _ptr(a_out), _stream(stream)), "kvc_vz_gather")

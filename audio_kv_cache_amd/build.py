@@ -14,7 +14,8 @@ PKG = pathlib.Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 BUILD = PKG / "_build"
 LIB = PKG / "libkvc.so"
-SOURCES = ["kvc_host.hip", "budget.hip", "score.hip", "sss_select.hip", "gather.hip"]
+SOURCES = ["kvc_host.hip", "budget.hip", "score.hip", "sss_select.hip", "gather.hip",
+           "voxzip.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -22,7 +22,9 @@ extern "C" const char* kvc_status_str(kvc_status s) {
     case KVC_OK: return "ok";
     case KVC_ERR_INVALID_ARG: return "invalid argument";
     case KVC_ERR_UNSUPPORTED: return "unsupported problem shape";
-    case KVC_ERR_BUDGET: return "infeasible budget (L <= window or window + base share > mean budget)";
+    case KVC_ERR_BUDGET:
+      return "infeasible budget (prefill: L <= window or window + base share > mean budget; "
+             "decode: sinks + recent window > budget)";
     case KVC_ERR_WORKSPACE: return "workspace too small";
     case KVC_ERR_HIP: return "HIP launch failure";
   }
@@ -30,6 +32,8 @@ extern "C" const char* kvc_status_str(kvc_status s) {
 }
 
 extern "C" int kvc_last_hip_error(void) { return g_last_hip_error; }
+
+void kvc_note_hip_error(int e) { g_last_hip_error = e; }
 
 static bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 

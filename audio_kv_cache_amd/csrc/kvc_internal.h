@@ -58,5 +58,8 @@ hipError_t kvc_launch_gather(const KvcDesc& D, int u0, int u1, const void* k, co
                              const int32_t* idx, const int64_t* offsets, void* k_out, void* v_out,
                              int64_t est_rows, hipStream_t st);
 
+// Record a HIP error for kvc_last_hip_error() (calling thread).
+void kvc_note_hip_error(int e);
+
 // Workspace needed by the score kernels.
 size_t kvc_scores_workspace(const KvcDesc& D);

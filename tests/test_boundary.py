@@ -12,20 +12,22 @@ import pytest
 from audio_kv_cache_amd import _lib as C
 from audio_kv_cache_amd import api
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kvc.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 
 
-def declared_symbols():
-    text = open(HEADER).read()
+def declared_symbols(name):
+    text = open(os.path.join(INCLUDE, name)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     L = C.lib()
-    names = declared_symbols()
-    assert set(names) == set(C.EXPORTS)
-    for n in names:
+    headers = sorted(f for f in os.listdir(INCLUDE) if f.endswith(".h"))
+    assert headers == ["kvc.h", "kvc_voxzip.h"]
+    assert set(declared_symbols("kvc.h")) == set(C.EXPORTS)
+    assert set(declared_symbols("kvc_voxzip.h")) == set(C.VZ_EXPORTS)
+    for n in C.EXPORTS + C.VZ_EXPORTS:
         assert hasattr(L, n), n
 
 
@@ -107,3 +109,48 @@ def test_too_many_sequences_and_units():
 def test_full_retention_plans_every_row():
     sp = spec(seq_lens=[1024], retention=1.0, n_layers=2, n_kv_heads=2)
     assert api.kvc_plan(sp, api.Params())[0] == 4 * 1024
+
+
+# ---------------------------------------------------------------------------
+# include/kvc_voxzip.h
+# ---------------------------------------------------------------------------
+def vz_spec(**kw):
+    base = dict(n_layers=48, n_kv_heads=4, gqa=8, head_dim=128, lens=[8193], budgets=[8192],
+                capacity=8200, dtype="bf16")
+    base.update(kw)
+    return api.VzSpec(**base)
+
+
+def vz_status(sp, prm=None, ws_bytes=1 << 40):
+    L = C.lib()
+    prm = prm or api.VzParams()
+    fake = ctypes.c_void_p(1 << 20)
+    return L.kvc_vz_step(ctypes.byref(sp.c()), ctypes.byref(prm.c()), fake, fake, fake, fake,
+                         fake, fake, fake, fake, fake, ws_bytes, None)
+
+
+def test_vz_plan_closed_form():
+    sp = vz_spec(lens=[8193, 100, 4096, 13108], budgets=[8192, 200, 4096, 8192], capacity=13120)
+    nl, ws = api.kvc_vz_plan(sp, api.VzParams())
+    assert nl.tolist() == [8192, 100, 4096, 8192]
+    units = 4 * 48 * 4
+    # logits (G per row), chunk statistics, and A before eviction
+    assert ws >= units * 13120 * 4 * (8 + 1)
+
+
+def test_vz_invalid_problems_rejected_before_launch():
+    # Every call below fails validation, so the fake pointers are never used;
+    # a huge workspace figure makes every shape check reachable.
+    assert vz_status(vz_spec(lens=[8201])) == C.KVC_ERR_INVALID_ARG           # n > capacity
+    assert vz_status(vz_spec(lens=[0])) == C.KVC_ERR_INVALID_ARG
+    assert vz_status(vz_spec(budgets=[0])) == C.KVC_ERR_INVALID_ARG
+    assert vz_status(vz_spec(head_dim=96)) == C.KVC_ERR_UNSUPPORTED
+    assert vz_status(vz_spec(gqa=33)) == C.KVC_ERR_UNSUPPORTED
+    assert vz_status(vz_spec(capacity=70000, lens=[8193])) == C.KVC_ERR_UNSUPPORTED
+    assert vz_status(vz_spec(budgets=[4]), api.VzParams(n_sink=4, recent_frac=0.5)) \
+        == C.KVC_ERR_BUDGET                                                       # T + M > B
+    assert vz_status(vz_spec(), api.VzParams(gamma=-0.1)) == C.KVC_ERR_INVALID_ARG
+    assert vz_status(vz_spec(), api.VzParams(recent_frac=1.5)) == C.KVC_ERR_INVALID_ARG
+    assert vz_status(vz_spec(), api.VzParams(n_sink=-1)) == C.KVC_ERR_INVALID_ARG
+    assert vz_status(vz_spec(), ws_bytes=16) == C.KVC_ERR_WORKSPACE
+    assert vz_status(vz_spec(k_stride=(8200 * 128, 100))) == C.KVC_ERR_INVALID_ARG  # row < d

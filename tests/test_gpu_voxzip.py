@@ -1,0 +1,354 @@
+"""GPU parity of decode-time decayed eviction against the fp64 oracle
+(oracle/voxzip.py), through the C ABI of include/kvc_voxzip.h.
+
+Criteria:
+  * A (before eviction): max|A - A_ref| / max|A_ref| <= TOL[dtype] per cache
+    (the same norm-wise tolerances as the prefill scores);
+  * eviction on the GPU's own A values: kept positions bit-exact;
+  * gather: K, V rows and A entries bit-exact for the GPU's positions;
+  * whole step: a kept/dropped disagreement only where the oracle's A lies
+    within TOL * max|A_ref| of the N-th largest middle value.
+Capacity padding of K, V and A_prev holds NaN, so a read past a cache's n
+rows shows up in A.
+"""
+import dataclasses
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from audio_kv_cache_amd import api, synth  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+from oracle import voxzip as VZ  # noqa: E402
+from tests.gpu_helpers import TOL, rel_err, to_numpy, to_torch  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def poison(prob: synth.DecodeProblem):
+    """NaN in every capacity row past n (bf16 0x7FC0 / fp32 NaN)."""
+    cfg = prob.cfg
+    for u in range(prob.n_units):
+        n = int(cfg.lens[prob.seq_of(u)])
+        if cfg.dtype == "bf16":
+            prob.k[u, n:] = 0x7FC0
+            prob.v[u, n:] = 0x7FC0
+        else:
+            prob.k[u, n:] = np.nan
+            prob.v[u, n:] = np.nan
+        prob.a_prev[u, n - 1:] = np.nan
+    return prob
+
+
+class VzDev:
+    def __init__(self, prob: synth.DecodeProblem):
+        self.prob = prob
+        c = prob.cfg
+        self.cfg, self.dtype = c, c.dtype
+        self.q = to_torch(prob.q, c.dtype)
+        self.k = to_torch(prob.k, c.dtype)
+        self.v = to_torch(prob.v, c.dtype)
+        self.a_prev = torch.from_numpy(prob.a_prev).cuda()
+        self.spec = api.VzSpec(n_layers=c.n_layers, n_kv_heads=c.n_kv_heads, gqa=c.gqa,
+                               head_dim=c.head_dim, lens=c.lens, budgets=c.budgets,
+                               capacity=c.capacity, dtype=c.dtype)
+        self.params = api.VzParams(c.gamma, c.n_sink, c.recent_frac)
+        self.new_len, self.ws_bytes = api.kvc_vz_plan(self.spec, self.params)
+        U, cap = prob.n_units, c.capacity
+        self.shape = (U, cap)
+
+    def n(self, u):
+        return int(self.cfg.lens[self.prob.seq_of(u)])
+
+    def B(self, u):
+        return int(self.cfg.budgets[self.prob.seq_of(u)])
+
+    def ws(self):
+        return torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+
+    def accumulate(self):
+        a = torch.full(self.shape, float("nan"), dtype=torch.float32, device="cuda")
+        api.kvc_vz_accumulate(self.spec, self.params, self.q, self.k, self.a_prev, a, self.ws())
+        torch.cuda.synchronize()
+        return a.cpu().numpy()
+
+    def evict(self, a_np):
+        a = torch.from_numpy(np.ascontiguousarray(a_np, dtype=np.float32)).cuda()
+        idx = torch.full(self.shape, -1, dtype=torch.int32, device="cuda")
+        api.kvc_vz_evict(self.spec, self.params, a, idx)
+        torch.cuda.synchronize()
+        return idx.cpu().numpy()
+
+    def gather(self, a_np, idx_np):
+        a = torch.from_numpy(np.ascontiguousarray(a_np, dtype=np.float32)).cuda()
+        idx = torch.from_numpy(np.ascontiguousarray(idx_np, dtype=np.int32)).cuda()
+        ko, vo = torch.zeros_like(self.k), torch.zeros_like(self.v)
+        ao = torch.zeros(self.shape, dtype=torch.float32, device="cuda")
+        api.kvc_vz_gather(self.spec, self.params, self.k, self.v, a, idx, ko, vo, ao)
+        torch.cuda.synchronize()
+        return to_numpy(ko, self.dtype), to_numpy(vo, self.dtype), ao.cpu().numpy()
+
+    def step(self):
+        ko, vo = torch.zeros_like(self.k), torch.zeros_like(self.v)
+        ao = torch.zeros(self.shape, dtype=torch.float32, device="cuda")
+        idx = torch.full(self.shape, -1, dtype=torch.int32, device="cuda")
+        api.kvc_vz_step(self.spec, self.params, self.q, self.k, self.v, self.a_prev, ko, vo, ao,
+                        idx, self.ws())
+        torch.cuda.synchronize()
+        return dict(k_out=to_numpy(ko, self.dtype), v_out=to_numpy(vo, self.dtype),
+                    a_out=ao.cpu().numpy(), idx=idx.cpu().numpy())
+
+    def ref_A(self, u):
+        n = self.n(u)
+        q = O.widen(self.prob.q[u], self.dtype)
+        k = O.widen(self.prob.k[u, :n], self.dtype)
+        return VZ.accumulate(self.prob.a_prev[u, :n - 1].astype(np.float64), q, k,
+                             self.cfg.gamma)
+
+
+def make(name, **kw):
+    cfg = synth.DECODE_CONFIGS[name]
+    if kw:
+        cfg = dataclasses.replace(cfg, **kw)
+    say(f"[vz gen] {name} {kw}")
+    return VzDev(poison(synth.decode_problem(cfg)))
+
+
+def small(**kw):
+    base = dict(name="vz_small", index=40, n_seq=1, n_layers=1, n_kv_heads=2, gqa=4,
+                head_dim=128, dtype="bf16", lens=(700,), budgets=(500,), capacity=704)
+    base.update(kw)
+    return VzDev(poison(synth.decode_problem(synth.DecodeConfig(**base))))
+
+
+def check_accumulate(D, units):
+    a = D.accumulate()
+    worst = 0.0
+    for u in units:
+        n = D.n(u)
+        ref = D.ref_A(u)
+        assert np.isfinite(a[u, :n]).all(), u
+        err = rel_err(a[u, :n], ref)
+        worst = max(worst, err)
+        assert err <= TOL[D.dtype], (u, err)
+    say(f"    worst A error {worst:.2e}")
+    return a
+
+
+def check_evict(D, a, units):
+    idx = D.evict(a)
+    for u in units:
+        n, B = D.n(u), D.B(u)
+        want = VZ.evict(a[u, :n].astype(np.float64), B, D.cfg.n_sink, D.cfg.recent_frac)
+        assert np.array_equal(idx[u, :len(want)], want), u
+    return idx
+
+
+def check_step_unit(D, out, u):
+    n, B = D.n(u), D.B(u)
+    c = D.cfg
+    ref = VZ.step(O.widen(D.prob.q[u], D.dtype), O.widen(D.prob.k[u, :n], D.dtype),
+                  D.prob.v[u, :n], D.prob.a_prev[u, :n - 1].astype(np.float64), B, c.gamma,
+                  c.n_sink, c.recent_frac)
+    nl = min(n, B)
+    idx = out["idx"][u, :nl]
+    assert np.all(np.diff(idx) > 0) and idx[0] >= 0 and idx[-1] < n
+    A_ref = ref["A"]
+    diff = np.setxor1d(idx, ref["kept"])
+    if len(diff):
+        T, M, N = VZ.split(B, c.n_sink, c.recent_frac)
+        theta = np.sort(A_ref[T:n - M])[::-1][N - 1]
+        tol = TOL[D.dtype] * np.max(np.abs(A_ref))
+        bad = [j for j in diff if abs(A_ref[j] - theta) > tol]
+        assert not bad, (u, len(diff), bad[:8])
+    # rows and A entries follow the GPU's own positions
+    assert np.array_equal(out["k_out"][u, :nl], D.prob.k[u, idx])
+    assert np.array_equal(out["v_out"][u, :nl], D.prob.v[u, idx])
+    assert rel_err(out["a_out"][u, :nl], A_ref[idx]) <= TOL[D.dtype]
+    return len(diff)
+
+
+# ---------------------------------------------------------------------------
+# Step 1: accumulation
+# ---------------------------------------------------------------------------
+def test_vz_accumulate_tiny_all():
+    say("[vz] accumulate tiny")
+    D = make("vz_tiny")
+    check_accumulate(D, range(D.prob.n_units))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("gqa", [1, 7, 8, 12, 32])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_vz_accumulate_shapes(dtype, gqa, d):
+    say(f"[vz] accumulate {dtype} G={gqa} d={d}")
+    D = small(dtype=dtype, gqa=gqa, head_dim=d, n_seq=3, lens=(1, 33, 2085),
+              budgets=(10, 40, 1500), capacity=2090)
+    check_accumulate(D, range(D.prob.n_units))
+
+
+def test_vz_accumulate_full_size_sampled():
+    say("[vz] accumulate vz_omni30b")
+    D = make("vz_omni30b")
+    check_accumulate(D, [0, 77, 191])
+
+
+# ---------------------------------------------------------------------------
+# Step 2: eviction on identical A (bit-exact)
+# ---------------------------------------------------------------------------
+def test_vz_evict_on_gpu_values():
+    say("[vz] evict on GPU A, vz_ragged")
+    D = make("vz_ragged")
+    a = D.accumulate()
+    check_evict(D, a, range(D.prob.n_units))
+
+
+@pytest.mark.parametrize("case", ["ties", "zeros", "two_values", "negzero"])
+def test_vz_evict_ties(case):
+    say(f"[vz] evict ties {case}")
+    D = small(n_seq=2, lens=(3000, 999), budgets=(1000, 600), capacity=3008)
+    r = np.random.default_rng(7)
+    a = np.zeros(D.shape, dtype=np.float32)
+    for u in range(D.prob.n_units):
+        n = D.n(u)
+        if case == "ties":
+            a[u, :n] = r.integers(0, 5, n).astype(np.float32) * 0.25
+        elif case == "two_values":
+            a[u, :n] = np.where(r.random(n) < 0.5, 1.0, 2.0).astype(np.float32)
+        elif case == "negzero":
+            a[u, :n] = np.where(r.random(n) < 0.5, -0.0, 0.0).astype(np.float32)
+    check_evict(D, a, range(D.prob.n_units))
+
+
+@pytest.mark.parametrize("n_sink,frac,B", [(4, 0.2, 500), (0, 0.2, 500), (4, 0.0, 500),
+                                           (4, 0.2, 5), (4, 0.0, 4), (64, 0.5, 128),
+                                           (0, 1.0, 100)])
+def test_vz_evict_splits(n_sink, frac, B):
+    say(f"[vz] evict T={n_sink} frac={frac} B={B}")
+    D = small(lens=(700,), budgets=(B,), n_sink=n_sink, recent_frac=frac)
+    a = D.accumulate()
+    check_evict(D, a, range(D.prob.n_units))
+
+
+# ---------------------------------------------------------------------------
+# Step 3: gather (bit-exact)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+def test_vz_gather_bitexact(dtype, d):
+    say(f"[vz] gather {dtype} d={d}")
+    D = small(dtype=dtype, head_dim=d, n_seq=2, lens=(900, 130), budgets=(600, 200), capacity=904)
+    r = np.random.default_rng(3)
+    a = r.random(D.shape).astype(np.float32)
+    idx = np.zeros(D.shape, dtype=np.int32)
+    for u in range(D.prob.n_units):
+        n, nl = D.n(u), min(D.n(u), D.B(u))
+        idx[u, :nl] = np.sort(r.choice(n, nl, replace=False))
+    ko, vo, ao = D.gather(a, idx)
+    for u in range(D.prob.n_units):
+        nl = min(D.n(u), D.B(u))
+        assert np.array_equal(ko[u, :nl], D.prob.k[u, idx[u, :nl]])
+        assert np.array_equal(vo[u, :nl], D.prob.v[u, idx[u, :nl]])
+        assert np.array_equal(ao[u, :nl], a[u, idx[u, :nl]])
+
+
+# ---------------------------------------------------------------------------
+# Whole step
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["vz_tiny", "vz_ragged"])
+def test_vz_step_all_units(name):
+    say(f"[vz] step {name}")
+    D = make(name)
+    out = D.step()
+    nd = sum(check_step_unit(D, out, u) for u in range(D.prob.n_units))
+    say(f"    {nd} positions in the tie band")
+
+
+@pytest.mark.parametrize("name", ["vz_omni30b", "vz_first"])
+def test_vz_step_full_size_sampled(name):
+    say(f"[vz] step {name}")
+    D = make(name)
+    out = D.step()
+    for u in (0, 50, 101, 191):
+        check_step_unit(D, out, u)
+
+
+def test_vz_step_matches_stage_entry_points():
+    say("[vz] step == accumulate + evict + gather")
+    D = make("vz_ragged")
+    out = D.step()
+    a = D.accumulate()
+    idx = D.evict(a)
+    ko, vo, ao = D.gather(a, idx)
+    for u in range(D.prob.n_units):
+        nl = min(D.n(u), D.B(u))
+        assert np.array_equal(out["idx"][u, :nl], idx[u, :nl])
+        assert np.array_equal(out["k_out"][u, :nl], ko[u, :nl])
+        assert np.array_equal(out["a_out"][u, :nl], ao[u, :nl])
+
+
+def test_vz_decode_loop_tracks_the_oracle():
+    # Five consecutive steps: each appends a new row and query to the
+    # compacted cache (GPU) and to the oracle's own cache; fp32 inputs keep
+    # the two kept sets identical step after step.
+    say("[vz] five chained steps, fp32")
+    r = np.random.default_rng(11)
+    G, d, B, cap = 4, 64, 150, 208
+    n = 200
+    k = r.standard_normal((1, cap, d)).astype(np.float32)
+    v = r.standard_normal((1, cap, d)).astype(np.float32)
+    a_prev = np.zeros((1, cap), dtype=np.float32)
+    ref_k, ref_v, ref_a = k[0, :n].astype(np.float64), v[0, :n].copy(), np.zeros(n - 1)
+    for t in range(5):
+        q = r.standard_normal((1, G, d)).astype(np.float32)
+        spec = api.VzSpec(n_layers=1, n_kv_heads=1, gqa=G, head_dim=d, lens=[n], budgets=[B],
+                          capacity=cap, dtype="f32")
+        prm = api.VzParams()
+        nl, wsb = api.kvc_vz_plan(spec, prm)
+        kt, vt, at = (torch.from_numpy(x).cuda() for x in (k, v, a_prev))
+        ko, vo = torch.zeros_like(kt), torch.zeros_like(vt)
+        ao = torch.zeros_like(at)
+        idx = torch.full((1, cap), -1, dtype=torch.int32, device="cuda")
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        api.kvc_vz_step(spec, prm, torch.from_numpy(q).cuda(), kt, vt, at, ko, vo, ao, idx, ws)
+        torch.cuda.synchronize()
+        ref = VZ.step(q[0].astype(np.float64), ref_k, ref_v, ref_a, B)
+        m = int(nl[0])
+        assert np.array_equal(idx.cpu().numpy()[0, :m], ref["kept"]), t
+        assert rel_err(ao.cpu().numpy()[0, :m], ref["a_out"]) <= TOL["f32"]
+        # next step: append one new row to both caches
+        k, v, a_prev = ko.cpu().numpy(), vo.cpu().numpy(), ao.cpu().numpy()
+        newk, newv = r.standard_normal(d).astype(np.float32), r.standard_normal(d).astype(np.float32)
+        k[0, m], v[0, m] = newk, newv
+        n = m + 1
+        ref_k = np.vstack([ref["k_out"], newk.astype(np.float64)])
+        ref_v = np.vstack([ref["v_out"], newv])
+        ref_a = ref["a_out"]
+
+
+def test_vz_within_budget_is_identity():
+    say("[vz] no eviction while within budget")
+    D = small(n_seq=2, lens=(257, 64), budgets=(257, 1000), capacity=260)
+    out = D.step()
+    for u in range(D.prob.n_units):
+        n = D.n(u)
+        assert out["idx"][u, :n].tolist() == list(range(n))
+        assert np.array_equal(out["k_out"][u, :n], D.prob.k[u, :n])
+
+
+def test_vz_invalid_arguments():
+    D = small()
+    bad = api.VzSpec(n_layers=1, n_kv_heads=2, gqa=4, head_dim=128, lens=[705], budgets=[500],
+                     capacity=704, dtype="bf16")
+    with pytest.raises(Exception):
+        api.kvc_vz_plan(bad, api.VzParams())
+    with pytest.raises(Exception):
+        api.kvc_vz_accumulate(D.spec, D.params, D.q, D.k, D.a_prev,
+                              torch.empty(D.shape, device="cuda"),
+                              torch.empty(16, dtype=torch.uint8, device="cuda"))
