@@ -108,34 +108,53 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_logits_bf16_kernel(
   }
   const uint16_t* kc = k + (int64_t)u * V.ks[0];
   float* lgu = lg + (size_t)u * G * V.cap;
-  // The wave's 256 rows of the chunk, 32 per MFMA block.
-  for (int blk = 0; blk < 8; ++blk) {
-    const int r0 = row0 + wave * 256 + blk * 32;
-    if (r0 >= n) break;
+  // The wave's (up to) 256 rows of the chunk, 32 per MFMA block; the next
+  // block's rows load while this block computes.
+  const int wrow0 = row0 + wave * 256;
+  const int nblk = wrow0 >= n ? 0 : min(8, (n - wrow0 + 31) / 32);
+  auto load_blk = [&](vz_bf16x8 (&b)[NK], int blk) {
+    const int r0 = wrow0 + blk * 32;
     const int r = r0 + col;
-    const bool live = r < n;
-    const uint16_t* kp = kc + (int64_t)(live ? r : r0) * V.ks[1] + half * (D / 2);
-    vz_floatx16 acc = {};
+    const uint16_t* kp = kc + (int64_t)(r < n ? r : r0) * V.ks[1] + half * (D / 2);
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const uint4 raw = reinterpret_cast<const uint4*>(kp)[kk];
-      vz_bf16x8 b;
-      __builtin_memcpy(&b, &raw, 16);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], b, acc, 0, 0, 0);
+      __builtin_memcpy(&b[kk], &raw, 16);
     }
+  };
+  auto compute_blk = [&](const vz_bf16x8 (&b)[NK], int blk) {
+    const int r = wrow0 + blk * 32 + col;
+    vz_floatx16 acc = {};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], b[kk], acc, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int g = (i >> 2) * 8 + half * 4 + (i & 3);
-      if (g < G && live) {
+      if (g < G && r < n) {
         const float l2 = acc[i] * c;
         lgu[(size_t)g * V.cap + r] = l2;
-        if (l2 > m[i]) {
-          z[i] = (m[i] == -INFINITY ? 0.f : z[i] * exp2f(m[i] - l2)) + 1.f;
-          m[i] = l2;
-        } else {
-          z[i] += exp2f(l2 - m[i]);
-        }
+        const float mn = fmaxf(m[i], l2);
+        z[i] = z[i] * exp2f(m[i] - mn) + exp2f(l2 - mn);
+        m[i] = mn;
       }
+    }
+  };
+  // The prefetch is unconditional (past the last block it reloads that
+  // block) so that every path has the same loads in flight and the waits
+  // before the MFMAs cover only the block they consume.
+  vz_bf16x8 b0[NK], b1[NK];
+  if (nblk > 0) {
+    load_blk(b0, 0);
+    for (int blk = 0;; blk += 2) {
+      load_blk(b1, min(blk + 1, nblk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute_blk(b0, blk);
+      if (blk + 1 >= nblk) break;
+      load_blk(b0, min(blk + 2, nblk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute_blk(b1, blk + 1);
+      if (blk + 2 >= nblk) break;
     }
   }
   // Lanes of one half share their heads: fold over the 32 columns.
@@ -360,43 +379,56 @@ __global__ __launch_bounds__(VZ_SEL_THREADS) void vz_evict_kernel(
 // ---------------------------------------------------------------------------
 // Gather kept rows of K, V and entries of A
 // ---------------------------------------------------------------------------
+// One workgroup per (cache, run of 64 output rows for 256-byte rows), the
+// runs of a cache consecutive in dispatch order so that neighbouring
+// workgroups stream neighbouring rows; the output is written with
+// non-temporal stores (it is not read again here).
 template <int ROWB>
 __global__ __launch_bounds__(VZ_THREADS) void vz_gather_kernel(
-    VzDesc V, const char* __restrict__ k, const char* __restrict__ v,
+    VzDesc V, int blocks_per_cache, const char* __restrict__ k, const char* __restrict__ v,
     const float* __restrict__ a_t, const int32_t* __restrict__ idx, char* __restrict__ k_out,
     char* __restrict__ v_out, float* __restrict__ a_out) {
   constexpr int CH = ROWB / 16;
   constexpr int RPP = VZ_THREADS / CH;          // rows per pass
   constexpr int PASSES = 4;
-  const int u = blockIdx.x;
+  const int u = blockIdx.x / blocks_per_cache;
+  const int t0 = (blockIdx.x - u * blocks_per_cache) * RPP * PASSES;
   const int seq = u / V.upseq;
   const int n = V.len[seq];
   const int nl = min(n, V.budget[seq]);
+  if (t0 >= nl) return;
   const int esz = V.dtype == 0 ? 2 : 4;
   const int ch = threadIdx.x % CH;
   const int32_t* ix = idx + (size_t)u * V.cap;
-  for (int t0 = blockIdx.y * RPP * PASSES; t0 < nl; t0 += gridDim.y * RPP * PASSES) {
-    uint4 kv[PASSES], vv[PASSES];
-    int src[PASSES];
+  uint4 kv[PASSES], vv[PASSES];
+  int src[PASSES];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int t = t0 + p * RPP + threadIdx.x / CH;
-      src[p] = 0;
-      if (t >= nl) continue;
-      int s = ix[t];
-      if ((unsigned)s >= (unsigned)n) s = 0;
-      src[p] = s;
-      kv[p] = *reinterpret_cast<const uint4*>(k + (u * V.ks[0] + s * V.ks[1]) * esz + ch * 16);
-      vv[p] = *reinterpret_cast<const uint4*>(v + (u * V.vs[0] + s * V.vs[1]) * esz + ch * 16);
-    }
+  for (int p = 0; p < PASSES; ++p) {
+    const int t = t0 + p * RPP + threadIdx.x / CH;
+    src[p] = 0;
+    if (t >= nl) continue;
+    int s = ix[t];
+    if ((unsigned)s >= (unsigned)n) s = 0;
+    src[p] = s;
+    kv[p] = *reinterpret_cast<const uint4*>(k + (u * V.ks[0] + s * V.ks[1]) * esz + ch * 16);
+    vv[p] = *reinterpret_cast<const uint4*>(v + (u * V.vs[0] + s * V.vs[1]) * esz + ch * 16);
+  }
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int t = t0 + p * RPP + threadIdx.x / CH;
-      if (t >= nl) continue;
-      *reinterpret_cast<uint4*>(k_out + (u * V.ks[0] + (int64_t)t * V.ks[1]) * esz + ch * 16) = kv[p];
-      *reinterpret_cast<uint4*>(v_out + (u * V.vs[0] + (int64_t)t * V.vs[1]) * esz + ch * 16) = vv[p];
-      if (ch == 0) a_out[(size_t)u * V.cap + t] = a_t[(size_t)u * V.cap + src[p]];
-    }
+  for (int p = 0; p < PASSES; ++p) {
+    const int t = t0 + p * RPP + threadIdx.x / CH;
+    if (t >= nl) continue;
+    uint4* ko = reinterpret_cast<uint4*>(k_out + (u * V.ks[0] + (int64_t)t * V.ks[1]) * esz + ch * 16);
+    uint4* vo = reinterpret_cast<uint4*>(v_out + (u * V.vs[0] + (int64_t)t * V.vs[1]) * esz + ch * 16);
+    __builtin_nontemporal_store(kv[p].x, &ko->x);
+    __builtin_nontemporal_store(kv[p].y, &ko->y);
+    __builtin_nontemporal_store(kv[p].z, &ko->z);
+    __builtin_nontemporal_store(kv[p].w, &ko->w);
+    __builtin_nontemporal_store(vv[p].x, &vo->x);
+    __builtin_nontemporal_store(vv[p].y, &vo->y);
+    __builtin_nontemporal_store(vv[p].z, &vo->z);
+    __builtin_nontemporal_store(vv[p].w, &vo->w);
+    if (ch == 0)
+      __builtin_nontemporal_store(a_t[(size_t)u * V.cap + src[p]], &a_out[(size_t)u * V.cap + t]);
   }
 }
 
@@ -535,16 +567,16 @@ static hipError_t vz_launch_gather(const VzDesc& V, const void* k, const void* v
   int maxnl = 1;
   for (int i = 0; i < V.n_seq; ++i) maxnl = std::max(maxnl, std::min(V.len[i], V.budget[i]));
   const int rows_per_block = (VZ_THREADS / (rowb / 16)) * 4;
-  const int gy = std::min(1024, (maxnl + rows_per_block - 1) / rows_per_block);
-  const dim3 grid(V.n_units, gy);
+  const int bpc = (maxnl + rows_per_block - 1) / rows_per_block;
+  const dim3 grid((unsigned)((int64_t)V.n_units * bpc));
   const char* kc = (const char*)k;
   const char* vc = (const char*)v;
   char* ko = (char*)k_out;
   char* vo = (char*)v_out;
   switch (rowb) {
-    case 128: hipLaunchKernelGGL((vz_gather_kernel<128>), grid, dim3(VZ_THREADS), 0, st, V, kc, vc, a_t, idx, ko, vo, a_out); break;
-    case 256: hipLaunchKernelGGL((vz_gather_kernel<256>), grid, dim3(VZ_THREADS), 0, st, V, kc, vc, a_t, idx, ko, vo, a_out); break;
-    default: hipLaunchKernelGGL((vz_gather_kernel<512>), grid, dim3(VZ_THREADS), 0, st, V, kc, vc, a_t, idx, ko, vo, a_out); break;
+    case 128: hipLaunchKernelGGL((vz_gather_kernel<128>), grid, dim3(VZ_THREADS), 0, st, V, bpc, kc, vc, a_t, idx, ko, vo, a_out); break;
+    case 256: hipLaunchKernelGGL((vz_gather_kernel<256>), grid, dim3(VZ_THREADS), 0, st, V, bpc, kc, vc, a_t, idx, ko, vo, a_out); break;
+    default: hipLaunchKernelGGL((vz_gather_kernel<512>), grid, dim3(VZ_THREADS), 0, st, V, bpc, kc, vc, a_t, idx, ko, vo, a_out); break;
   }
   return hipGetLastError();
 }

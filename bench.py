@@ -112,6 +112,130 @@ def cpu_baseline(cfg, hdr, prob_units, budgets, max_units=8):
                        f"scores+smoothing+selection in fp64, {dt:.1f} s wall")
 
 
+def decode_bytes(cfg):
+    """Algorithmic bytes of one decode step: per cache, K read once for the
+    logits, the new token's queries, A_prev read, kept K and V rows read and
+    written, A_out and the kept positions written."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    d, G = cfg.head_dim, cfg.gqa
+    per_seq = cfg.n_layers * cfg.n_kv_heads
+    tot = dict(logits=0, gather=0, total=0)
+    for n, B in zip(cfg.lens, cfg.budgets):
+        nl = min(n, B)
+        lg = n * d * e + G * d * e + 4 * (n - 1)
+        ga = 4 * nl * d * e + 8 * nl
+        tot["logits"] += per_seq * lg
+        tot["gather"] += per_seq * ga
+        tot["total"] += per_seq * (lg + ga)
+    return tot
+
+
+def bench_decode(args):
+    """One decode step of decayed eviction (kvc_vz_step) over every cache of
+    the decode workload, inputs resident in HBM; per-kernel event timing and
+    a CPU-oracle sample."""
+    import torch
+    from audio_kv_cache_amd import api, synth
+    cfg = synth.DECODE_CONFIGS[args.decode_config]
+    log(f"[bench] decode: generating {cfg.name}")
+    prob = synth.decode_problem(cfg)
+
+    def dev(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q, k, v = dev(prob.q), dev(prob.k), dev(prob.v)
+    a_prev = torch.from_numpy(prob.a_prev).cuda()
+    spec = api.VzSpec(n_layers=cfg.n_layers, n_kv_heads=cfg.n_kv_heads, gqa=cfg.gqa,
+                      head_dim=cfg.head_dim, lens=cfg.lens, budgets=cfg.budgets,
+                      capacity=cfg.capacity, dtype=cfg.dtype)
+    prm = api.VzParams(cfg.gamma, cfg.n_sink, cfg.recent_frac)
+    _, wsb = api.kvc_vz_plan(spec, prm)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    ko, vo = torch.empty_like(k), torch.empty_like(v)
+    ao = torch.empty_like(a_prev)
+    at = torch.empty_like(a_prev)
+    idx = torch.empty(a_prev.shape, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / args.steps
+
+    step_ms = timed(lambda: api.kvc_vz_step(spec, prm, q, k, v, a_prev, ko, vo, ao, idx, ws,
+                                            stream))
+    stages = {
+        "accumulate": timed(lambda: api.kvc_vz_accumulate(spec, prm, q, k, a_prev, at, ws,
+                                                          stream)),
+        "evict": timed(lambda: api.kvc_vz_evict(spec, prm, at, idx, stream)),
+        "gather": timed(lambda: api.kvc_vz_gather(spec, prm, k, v, at, idx, ko, vo, ao,
+                                                  stream)),
+    }
+    ab = decode_bytes(cfg)
+    units = prob.n_units
+    rows = sum(int(n) for n in cfg.lens) * cfg.n_layers * cfg.n_kv_heads
+    gbs = ab["total"] / (step_ms * 1e-3) / 1e9
+    g_gbs = ab["gather"] / (stages["gather"] * 1e-3) / 1e9
+    a_gbs = ab["logits"] / (stages["accumulate"] * 1e-3) / 1e9
+    log(f"[bench] decode {step_ms * 1e3:.1f} us/step, path {gbs:.0f} GB/s; stages " +
+        ", ".join(f"{n2} {t * 1e3:.1f} us" for n2, t in stages.items()))
+    out = {
+        "workload": f"{cfg.name}: {units} caches ({cfg.n_seq} seq x {cfg.n_layers} layers x "
+                    f"{cfg.n_kv_heads} KV heads), n={list(cfg.lens)} rows, budget "
+                    f"{list(cfg.budgets)}, GQA {cfg.gqa}, head_dim {cfg.head_dim}, {cfg.dtype}, "
+                    f"gamma {cfg.gamma}, T {cfg.n_sink}, recent {cfg.recent_frac}",
+        "us_per_step": round(step_ms * 1e3, 2),
+        "cache_rows_per_s": rows / (step_ms * 1e-3),
+        "algorithmic_bytes_per_step": ab["total"],
+        "path_hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "stage_us": {n2: round(t * 1e3, 2) for n2, t in stages.items()},
+        "roofline": {"gather": {"bound": "hbm", "kernel": "vz_gather_kernel<256>",
+                                "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
+                                "traffic": committed_traffic("voxzip.hip", "vz_gather_kernel",
+                                                             cfg.name)},
+                     "accumulate": {"bound": "hbm",
+                                    "kernel": "vz_logits_bf16_kernel + vz_accum_kernel",
+                                    "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4)}},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import voxzip as VZ
+        from oracle import oracle as O
+        import concurrent.futures as cf
+        sample = list(range(min(64, units)))
+        cores = min(len(sample), O.threads())
+
+        def run(u):
+            n = int(cfg.lens[prob.seq_of(u)])
+            B = int(cfg.budgets[prob.seq_of(u)])
+            VZ.step(O.widen(prob.q[u], cfg.dtype), O.widen(prob.k[u, :n], cfg.dtype),
+                    prob.v[u, :n], prob.a_prev[u, :n - 1].astype(np.float64), B, cfg.gamma,
+                    cfg.n_sink, cfg.recent_frac)
+
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(cores) as ex:
+            list(ex.map(run, sample))
+        dt = time.perf_counter() - t0
+        srows = sum(int(cfg.lens[prob.seq_of(u)]) for u in sample)
+        out["cpu_baseline"] = dict(value=srows / dt, unit="cache rows/s", cores=cores,
+                                   kind="oracle",
+                                   sample=f"{len(sample)} caches of the same workload, one "
+                                          f"decode step each in fp64, {dt:.2f} s wall")
+    del prob
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +244,9 @@ def main():
     ap.add_argument("--config", default="omni30b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-step (decayed eviction) measurement")
+    ap.add_argument("--decode-config", default="vz_omni30b")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -257,6 +384,8 @@ def main():
         others["gather"] = hbm("gather", "kvc_gather_kernel<256>", ab["gather"], stages["gather"],
                                "gather.hip")
 
+    decode = None if args.no_decode else bench_decode(args)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample of units")
@@ -280,6 +409,7 @@ def main():
         "stage_ms": {k2: round(v2, 4) for k2, v2 in stages.items()},
         "roofline": roof,
         "roofline_other_kernels": others,
+        "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
