@@ -428,6 +428,315 @@ __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_pool_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16, query-stationary form of both passes
+// ---------------------------------------------------------------------------
+// Each wave keeps two 32-query blocks of the unit in registers (A/B operand
+// fragments, and in the pooling pass the LSE of every output row it holds)
+// and the workgroup streams the tile's keys through LDS in chunks of 64 rows,
+// double-buffered: the next chunk's global loads are in flight while the
+// current one is consumed, one barrier per chunk.  Per MFMA this reads a
+// quarter of the LDS bytes of the key-stationary form above (which re-reads
+// every query block and its LSE values from LDS for each 32 keys), and no LSE
+// value is read from LDS at all.  A K row sits in LDS with a 16-byte pad so
+// that the 32 rows read by one fragment load fall in distinct bank groups.
+template <int D>
+struct QsCfg {
+  static constexpr int CHUNK = 64;                   // keys per LDS chunk
+  static constexpr int ROWB = D * 2;                 // bytes per bf16 K row
+  static constexpr int RS = ROWB + 16;               // padded LDS row stride
+  static constexpr int NK = D / 16;                  // MFMA k-steps
+  static constexpr int PIECES = CHUNK * ROWB / 16;   // 16-byte pieces per chunk
+};
+
+// Waves of a query-stationary workgroup: two query blocks each.
+template <int NBC>
+struct QsWaves {
+  static constexpr int NW = (NBC + 1) / 2;
+  static constexpr int NT = 64 * NW;
+  static constexpr int MINB = 8 / NW;                // two waves per SIMD
+};
+
+// Loads of one chunk (rows key0 .. key0+63 of the unit) into registers:
+// thread t takes pieces t, t + NT, ... (consecutive threads, consecutive
+// 16-byte pieces of a row).  Past the last piece a thread reloads it, so
+// every register is written on every path and the array is never demoted
+// to scratch memory.
+typedef unsigned int qs_u32x4 __attribute__((ext_vector_type(4)));
+
+template <int D, int NT>
+__device__ inline void qs_kload(qs_u32x4 (&r)[(QsCfg<D>::PIECES + NT - 1) / NT], const uint16_t* ku,
+                                int64_t kstride, int key0) {
+  constexpr int PPR = QsCfg<D>::ROWB / 16, PER = (QsCfg<D>::PIECES + NT - 1) / NT;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int p = min((int)threadIdx.x + j * NT, QsCfg<D>::PIECES - 1);
+    const int row = p / PPR, pc = p - row * PPR;
+    r[j] = reinterpret_cast<const qs_u32x4*>(ku + (int64_t)(key0 + row) * kstride)[pc];
+  }
+}
+
+template <int D, int NT>
+__device__ inline void qs_kstore(const qs_u32x4 (&r)[(QsCfg<D>::PIECES + NT - 1) / NT], char* buf) {
+  constexpr int PPR = QsCfg<D>::ROWB / 16, PER = (QsCfg<D>::PIECES + NT - 1) / NT;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int p = (int)threadIdx.x + j * NT;
+    if (QsCfg<D>::PIECES % NT == 0 || p < QsCfg<D>::PIECES) {
+      const int row = p / PPR, pc = p - row * PPR;
+      *reinterpret_cast<qs_u32x4*>(buf + row * QsCfg<D>::RS + pc * 16) = r[j];
+    }
+  }
+}
+
+// Fragment of 32 K rows (block kb of the chunk in LDS) for the lane: row
+// kb*32 + lane%32, the lane half's permuted head-dimension range.
+template <int D>
+__device__ inline void qs_kfrag(bf16x8 (&f)[QsCfg<D>::NK], const char* buf, int kb, int lane) {
+  const char* p = buf + (kb * 32 + (lane & 31)) * QsCfg<D>::RS + (lane >> 5) * D;
+#pragma unroll
+  for (int kk = 0; kk < QsCfg<D>::NK; ++kk) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(p + kk * 16);
+    __builtin_memcpy(&f[kk], &raw, 16);
+  }
+}
+
+// The lane's fragments of query block qb (row qb*32 + lane%32, same
+// permutation); zero past the unit's G*W queries.
+template <int D>
+__device__ inline void qs_qfrag(bf16x8 (&f)[QsCfg<D>::NK], const uint16_t* qg, int qb, int gw,
+                                int lane) {
+  const int row = qb * 32 + (lane & 31);
+  const uint16_t* p = qg + (size_t)(row < gw ? row : 0) * D + (lane >> 5) * (D / 2);
+#pragma unroll
+  for (int kk = 0; kk < QsCfg<D>::NK; ++kk) {
+    uint4 raw = row < gw ? reinterpret_cast<const uint4*>(p)[kk] : make_uint4(0, 0, 0, 0);
+    __builtin_memcpy(&f[kk], &raw, 16);
+  }
+}
+
+// Interleave the 8 MFMAs of one block with the VALU work of the previous
+// block: 1 MFMA, then `n` VALU instructions, eight times.  A wave issues in
+// order, so without this the exponentials of a block wait behind the next
+// block's whole dependent MFMA chain.
+#define QS_INTERLEAVE(n)                                   \
+  do {                                                     \
+    _Pragma("unroll") for (int _i = 0; _i < 8; ++_i) {     \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   \
+      __builtin_amdgcn_sched_group_barrier(0x002, n, 0);   \
+    }                                                      \
+  } while (0)
+
+template <int D, int NBC>
+__global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_score_pool_qs_kernel(
+    KvcDesc Dsc, int tile0, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const float* __restrict__ lse2, float* __restrict__ s) {
+  using C = QsCfg<D>;
+  constexpr int NW = QsWaves<NBC>::NW, NT = QsWaves<NBC>::NT, NK = C::NK;
+  __shared__ __attribute__((aligned(16))) char sK[2][C::CHUNK * C::RS];
+  __shared__ float sRed[NW][KVC_TILE_KEYS];
+  const int tile = tile0 + xcd_local_tile((int)blockIdx.x, (int)gridDim.x);
+  const TileInfo ti = tile_info(Dsc, tile);
+  const int gw = NBC * 32;
+  const float c = kLog2e / sqrtf((float)D);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool two = 2 * wave + 1 < NBC;
+  const uint16_t* qg = q + ((size_t)((int64_t)ti.seq * Dsc.n_layers + ti.l) * Dsc.n_heads * Dsc.gqa +
+                            (size_t)ti.h * Dsc.gqa) * Dsc.nwin * D;
+  const uint16_t* ku = k + ti.l * Dsc.ks[0] + ti.h * Dsc.ks[1] + Dsc.tok0[ti.seq] * Dsc.ks[2];
+
+  // A operand (rows = queries) and minus the LSE of each output row the lane
+  // holds: element i of the 32x32 block is row (i/4)*8 + (lane/32)*4 + i%4.
+  // A wave with a single query block repeats it as its second block and
+  // gives that copy -inf, so its terms are exactly zero.
+  bf16x8 qf0[NK], qf1[NK];
+  qs_qfrag<D>(qf0, qg, 2 * wave, gw, lane);
+  qs_qfrag<D>(qf1, qg, two ? 2 * wave + 1 : 2 * wave, gw, lane);
+  float nl0[16], nl1[16];
+  {
+    const float* lu = lse2 + (size_t)ti.u * gw;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+      nl0[i] = -lu[(2 * wave) * 32 + row];
+      nl1[i] = two ? -lu[(2 * wave + 1) * 32 + row] : -INFINITY;
+    }
+  }
+  auto mma = [&](floatx16& acc, const bf16x8 (&qf)[NK], const bf16x8 (&kf)[NK]) {
+    acc = floatx16{};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[kk], kf[kk], acc, 0, 0, 0);
+  };
+  // Pairwise sum of the 16 terms: a serial chain of adds would leave the
+  // VALU waiting on each add's latency.
+  auto pool = [&](const floatx16& acc, const float (&nl)[16]) {
+    float e[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c, nl[i]));
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) e[i] = e[i] + e[i + w];
+    return e[0];
+  };
+  // Both lane halves hold the same sum after the exchange and both write it
+  // (same value, same address): no lane mask, no branch in the loop body.
+  auto flush = [&](float sum, int key) {       // key = tile-relative first key of the block
+    sum += __shfl_xor(sum, 32);
+    sRed[wave][key + (lane & 31)] = sum;
+  };
+
+  // The loop body is branch-free so that the scheduling groups hold: the
+  // last chunk reloads and restages itself into the idle buffer.
+  const int nch = ti.keys / C::CHUNK;
+  qs_u32x4 kr[(C::PIECES + NT - 1) / NT];
+  qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0);
+  qs_kstore<D, NT>(kr, sK[0]);
+  __syncthreads();
+  floatx16 X, Y;          // X: query block 0, Y: query block 1 of the current key block
+  bf16x8 kf0[NK], kf1[NK];
+  float s0 = 0.f;         // pooled sum of the current key block (block 0 part)
+  qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0 + min(1, nch - 1) * C::CHUNK);
+  qs_kfrag<D>(kf0, sK[0], 0, lane);
+  mma(X, qf0, kf0);
+  for (int ch = 0;;) {
+    const char* buf = sK[ch & 1];
+    // [B] keys 0-31 x block 1, beside keys 0-31 x block 0
+    qs_kfrag<D>(kf1, buf, 1, lane);
+    mma(Y, qf1, kf0);
+    s0 = pool(X, nl0);
+    QS_INTERLEAVE(6);
+    // [C] keys 32-63 x block 0, beside keys 0-31 x block 1
+    mma(X, qf0, kf1);
+    flush(s0 + pool(Y, nl1), ch * C::CHUNK);
+    QS_INTERLEAVE(6);
+    // [D] keys 32-63 x block 1, beside keys 32-63 x block 0
+    mma(Y, qf1, kf1);
+    s0 = pool(X, nl0);
+    QS_INTERLEAVE(6);
+    qs_kstore<D, NT>(kr, sK[(ch + 1) & 1]);
+    __syncthreads();
+    if (++ch == nch) break;
+    qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0 + min(ch + 1, nch - 1) * C::CHUNK);
+    // [A] keys 0-31 of the new chunk x block 0, beside the last block of
+    // the previous chunk
+    qs_kfrag<D>(kf0, sK[ch & 1], 0, lane);
+    const floatx16 Yp = Y;
+    mma(X, qf0, kf0);
+    flush(s0 + pool(Yp, nl1), (ch - 1) * C::CHUNK + 32);
+    QS_INTERLEAVE(6);
+  }
+  flush(s0 + pool(Y, nl1), (nch - 1) * C::CHUNK + 32);
+  __syncthreads();
+  // Sum the waves' partial pools for every key of the tile.
+  float* srow = s + Dsc.srow_base[ti.seq] + (int64_t)(ti.u - ti.seq * Dsc.upseq) * ti.L;
+  const float inv_gw = 1.0f / (float)gw;
+  for (int j = threadIdx.x; j < ti.keys; j += NT) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += sRed[w][j];
+    srow[ti.key0 + j] = v * inv_gw;
+  }
+}
+
+template <int D, int NBC>
+__global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_score_stats_qs_kernel(
+    KvcDesc Dsc, int tile0, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    float2* __restrict__ partials) {
+  using C = QsCfg<D>;
+  constexpr int NT = QsWaves<NBC>::NT, NK = C::NK;
+  __shared__ __attribute__((aligned(16))) char sK[2][C::CHUNK * C::RS];
+  const int tile = tile0 + xcd_local_tile((int)blockIdx.x, (int)gridDim.x);
+  const TileInfo ti = tile_info(Dsc, tile);
+  const int gw = NBC * 32;
+  const float c = kLog2e / sqrtf((float)D);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool two = 2 * wave + 1 < NBC;
+  const uint16_t* qg = q + ((size_t)((int64_t)ti.seq * Dsc.n_layers + ti.l) * Dsc.n_heads * Dsc.gqa +
+                            (size_t)ti.h * Dsc.gqa) * Dsc.nwin * D;
+  const uint16_t* ku = k + ti.l * Dsc.ks[0] + ti.h * Dsc.ks[1] + Dsc.tok0[ti.seq] * Dsc.ks[2];
+
+  // B operand (columns = queries): the wave's two query blocks (a wave with
+  // one block repeats it and discards the copy's statistics).
+  bf16x8 qf0[NK], qf1[NK];
+  qs_qfrag<D>(qf0, qg, 2 * wave, gw, lane);
+  qs_qfrag<D>(qf1, qg, two ? 2 * wave + 1 : 2 * wave, gw, lane);
+  float m0 = -INFINITY, z0 = 0.f, m1 = -INFINITY, z1 = 0.f;
+  auto mma = [&](floatx16& acc, const bf16x8 (&kf)[NK], const bf16x8 (&qf)[NK]) {
+    acc = floatx16{};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], acc, 0, 0, 0);
+  };
+  // Online (max, sum of exp2) over the lane's 16 keys of one block, with
+  // pairwise max and sum trees (no serial dependency chains).
+  auto stat = [&](const floatx16& acc, float& m, float& z) {
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = fmaxf(acc[i], acc[i + 8]);
+#pragma unroll
+    for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
+    const float mn = fmaxf(m, t[0]);
+    const float nmc = -mn * c;
+    float e[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c, nmc));
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) e[i] = e[i] + e[i + w];
+    z = z * __builtin_amdgcn_exp2f((m - mn) * c) + e[0];   // m = -inf: exp2(-inf) = 0
+    m = mn;
+  };
+
+  const int nch = ti.keys / C::CHUNK;
+  qs_u32x4 kr[(C::PIECES + NT - 1) / NT];
+  qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0);
+  qs_kstore<D, NT>(kr, sK[0]);
+  __syncthreads();
+  floatx16 X, Y;
+  bf16x8 kf0[NK], kf1[NK];
+  qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0 + min(1, nch - 1) * C::CHUNK);
+  qs_kfrag<D>(kf0, sK[0], 0, lane);
+  mma(X, kf0, qf0);
+  for (int ch = 0;;) {
+    const char* buf = sK[ch & 1];
+    qs_kfrag<D>(kf1, buf, 1, lane);
+    mma(Y, kf0, qf1);
+    stat(X, m0, z0);
+    QS_INTERLEAVE(7);
+    mma(X, kf1, qf0);
+    stat(Y, m1, z1);
+    QS_INTERLEAVE(7);
+    mma(Y, kf1, qf1);
+    stat(X, m0, z0);
+    QS_INTERLEAVE(7);
+    qs_kstore<D, NT>(kr, sK[(ch + 1) & 1]);
+    __syncthreads();
+    if (++ch == nch) break;
+    qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0 + min(ch + 1, nch - 1) * C::CHUNK);
+    qs_kfrag<D>(kf0, sK[ch & 1], 0, lane);
+    const floatx16 Yp = Y;
+    mma(X, kf0, qf0);
+    stat(Yp, m1, z1);
+    QS_INTERLEAVE(7);
+  }
+  stat(Y, m1, z1);
+  // The other lane half holds the other 16 keys of each 32-key block.
+  {
+    float m2 = __shfl_xor(m0, 32), z2 = __shfl_xor(z0, 32);
+    merge_stat(m0, z0, m2, z2, c);
+    m2 = __shfl_xor(m1, 32);
+    z2 = __shfl_xor(z1, 32);
+    merge_stat(m1, z1, m2, z2, c);
+  }
+  if (lane < 32) {
+    partials[(size_t)tile * gw + (2 * wave) * 32 + lane] = make_float2(m0, z0);
+    if (two) partials[(size_t)tile * gw + (2 * wave + 1) * 32 + lane] = make_float2(m1, z1);
+  }
+}
+
 size_t kvc_scores_workspace(const KvcDesc& D) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   return up(sizeof(float) * (size_t)D.n_units * D.gw) +
@@ -454,18 +763,38 @@ static void launch_pair(const KvcDesc& D, int u0, int u1, const void* q, const v
                        D, t0, (const elem_t*)q, (const elem_t*)k, (const float*)lse2, s);
 }
 
+// Query-stationary bf16 passes; units [u0, u1) in one sequence.
+template <int Dm, int NBC>
+static void launch_qs(const KvcDesc& D, int u0, int u1, const void* q, const void* k, float* s,
+                      float2* partials, float* lse2, hipStream_t st, int which) {
+  const int seq = u0 / D.upseq;
+  const int tpu = kvc_tiles_per_unit(D.L[seq]);
+  const int t0 = D.tile_base[seq] + (u0 - seq * D.upseq) * tpu;
+  const int nt = (u1 - u0) * tpu;
+  constexpr int NT = QsWaves<NBC>::NT;
+  if (which & 1) {
+    hipLaunchKernelGGL((kvc_score_stats_qs_kernel<Dm, NBC>), dim3(nt), dim3(NT), 0, st, D, t0,
+                       (const uint16_t*)q, (const uint16_t*)k, partials);
+    hipLaunchKernelGGL(kvc_score_lse_kernel, dim3(u1 - u0), dim3(KVC_MAX_GW), 0, st, D, u0,
+                       kLog2e / sqrtf((float)Dm), (const float2*)partials, lse2);
+  }
+  if (which & 2)
+    hipLaunchKernelGGL((kvc_score_pool_qs_kernel<Dm, NBC>), dim3(nt), dim3(NT), 0, st, D, t0,
+                       (const uint16_t*)q, (const uint16_t*)k, (const float*)lse2, s);
+}
+
 template <int Dm>
 static void launch_bf16(const KvcDesc& D, int u0, int u1, const void* q, const void* k, float* s,
                         float2* partials, float* lse2, hipStream_t st, int which) {
   switch (D.gw / 32) {
-    case 1: launch_pair<TBf16, Dm, 1>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    case 2: launch_pair<TBf16, Dm, 2>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    case 3: launch_pair<TBf16, Dm, 3>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    case 4: launch_pair<TBf16, Dm, 4>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    case 5: launch_pair<TBf16, Dm, 5>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    case 6: launch_pair<TBf16, Dm, 6>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    case 7: launch_pair<TBf16, Dm, 7>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    default: launch_pair<TBf16, Dm, 8>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 1: launch_qs<Dm, 1>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 2: launch_qs<Dm, 2>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 3: launch_qs<Dm, 3>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 4: launch_qs<Dm, 4>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 5: launch_qs<Dm, 5>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 6: launch_qs<Dm, 6>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 7: launch_qs<Dm, 7>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    default: launch_qs<Dm, 8>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
   }
 }
 
