@@ -11,17 +11,21 @@
 //   stats  per query (max, sum of exp) of each 1024-key tile, folded per
 //          unit into LSE (log2 units) by a small kernel after it
 //   pool   recompute the logits, p = exp2(l*c - LSE2), sum over the G*W
-//          queries inside the lane, write s.
-// Q of the unit sits in LDS (rows padded by 16 bytes against bank
-// conflicts); each wave streams its own K rows straight into MFMA operand
-// registers.  Inside a lane's 128-byte half row the head dimension is read in
-// a permuted order (lane group g owns d in [g*d/G, (g+1)*d/G)); the same
-// permutation is applied to Q and K, so the contraction is unchanged and
-// every lane reads contiguous memory.
+//          queries, write s.
+// Inside a lane's half row the head dimension is read in a permuted order
+// (lane group g owns d in [g*d/G, (g+1)*d/G)); the same permutation is
+// applied to Q and K, so the contraction is unchanged and every lane reads
+// contiguous memory.
 //
-// bf16 inputs: v_mfma_f32_32x32x16_bf16 (fp32 accumulate).  fp32 inputs:
-// widened to fp64 and contracted with v_mfma_f64_16x16x4f64, which keeps the
-// logits exact to ~1e-15 so the 1e-5 fp32 tolerance is met with margin.
+// bf16 inputs (v_mfma_f32_32x32x16_bf16, fp32 accumulate): query-stationary
+// kernels -- each wave holds two 32-query blocks (and, pooling, their LSE)
+// in registers while the workgroup streams the tile's keys through
+// double-buffered LDS chunks; the MFMAs of one block are interleaved with
+// the exponentials of the previous one.  fp32 inputs: key-stationary
+// kernels (Q in LDS, each wave streams its own K rows into operand
+// registers), widened to fp64 and contracted with v_mfma_f64_16x16x4f64,
+// which keeps the logits exact to ~1e-15 so the 1e-5 fp32 tolerance is met
+// with margin.
 #include "kvc_internal.h"
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -32,30 +36,6 @@ typedef double doublex4 __attribute__((__vector_size__(4 * sizeof(double))));
 #define SCORE_WAVES 4
 
 static constexpr float kLog2e = 1.4426950408889634f;
-
-struct TBf16 {
-  using elem_t = uint16_t;
-  using frag_t = bf16x8;
-  using acc_t = floatx16;
-  static constexpr int M = 32, KS = 16, E = 8, NOUT = 16, G = 2;
-  static constexpr int MINB = 2;  // workgroups per CU the registers are sized for
-  __device__ static acc_t zero() { return acc_t{}; }
-  __device__ static acc_t mma(frag_t a, frag_t b, acc_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  // Output element i of a lane sits at row out_row(i, lane), column lane % M.
-  __device__ static int out_row(int i, int lane) { return (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3); }
-  __device__ static float val(const acc_t& a, int i) { return a[i]; }
-  // NK fragments covering the lane's D/G contiguous elements at p.
-  template <int NK>
-  __device__ static void load(frag_t (&f)[NK], const elem_t* p) {
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const uint4 raw = reinterpret_cast<const uint4*>(p)[kk];
-      __builtin_memcpy(&f[kk], &raw, 16);
-    }
-  }
-};
 
 struct TF64 {
   using elem_t = float;
@@ -86,8 +66,6 @@ struct TF64 {
 // Per-instance tiling: RB key row blocks per wave step in the stats pass,
 // CB key column blocks per wave step in the pooling pass.
 template <class T, int D> struct Tiling;
-template <> struct Tiling<TBf16, 64> { static constexpr int RB = 2, CB = 1; };
-template <> struct Tiling<TBf16, 128> { static constexpr int RB = 2, CB = 1; };
 template <> struct Tiling<TF64, 64> { static constexpr int RB = 1, CB = 1; };
 template <> struct Tiling<TF64, 128> { static constexpr int RB = 1, CB = 1; };
 
