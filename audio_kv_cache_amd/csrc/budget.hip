@@ -1,4 +1,6 @@
-// budget.hip -- head-aware token budget (step 3), one workgroup per sequence.
+// budget.hip -- head-aware token budget (step 3), one workgroup per budget
+// pool: a sequence's n_layers x n_kv_heads heads, or the n_kv_heads heads of
+// one of its layers.
 //
 // AudioKV article, section 3.1 (layered cache allocation): every head keeps
 // a local window w plus a uniform base share r, and the remaining budget
@@ -32,19 +34,27 @@ __global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
   __shared__ int s_nA, s_capped;
   __shared__ int64_t s_wsum[BUDGET_THREADS / 64];
 
-  const int seq = blockIdx.x;
-  const int n = D.upseq;
+  // Pool `pool` of sequence `seq`: heads pool*n .. pool*n + n - 1 of the
+  // sequence (flattened (layer, head) order, as S is laid out).  Every pool
+  // keeps n*min(kbar, L) rows in total, so its first row is known up front.
+  const int npools = D.upseq / D.pool_size;
+  const int seq = blockIdx.x / npools;
+  const int pool = blockIdx.x - seq * npools;
+  const int n = D.pool_size;
   const int L = D.L[seq];
   const int tid = threadIdx.x;
-  const int64_t u0 = (int64_t)seq * n;
+  const int64_t u0 = (int64_t)seq * D.upseq + (int64_t)pool * n;
+  S += (int64_t)pool * n;
+  const bool last = seq == D.n_seq - 1 && pool == npools - 1;
 
   const int64_t kbar = (int64_t)floor(D.retention[seq] * (double)L);
+  const int64_t row0 = D.row_base[seq] + (int64_t)pool * n * (kbar < L ? kbar : (int64_t)L);
   if (kbar >= L) {
     for (int u = tid; u < n; u += BUDGET_THREADS) {
       budgets[u0 + u] = L;
-      offsets[u0 + u] = D.row_base[seq] + (int64_t)u * L;
+      offsets[u0 + u] = row0 + (int64_t)u * L;
     }
-    if (seq == D.n_seq - 1 && tid == 0) offsets[u0 + n] = D.row_base[seq] + (int64_t)n * L;
+    if (last && tid == 0) offsets[u0 + n] = row0 + (int64_t)n * L;
     return;
   }
   const int64_t r = (int64_t)floor(D.base_ratio * (double)kbar);
@@ -156,19 +166,19 @@ __global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
   __syncthreads();
   int64_t before = 0;
   for (int w = 0; w < (tid >> 6); ++w) before += s_wsum[w];
-  int64_t run = D.row_base[seq] + before + incl - part;
+  int64_t run = row0 + before + incl - part;
   for (int u = lo; u < hi; ++u) {
     const int64_t bu = fixed + extra[u];
     budgets[u0 + u] = (int32_t)bu;
     offsets[u0 + u] = run;
     run += bu;
   }
-  if (seq == D.n_seq - 1 && hi == n && lo < hi) offsets[u0 + n] = run;
+  if (last && hi == n && lo < hi) offsets[u0 + n] = run;
 }
 
 hipError_t kvc_launch_budget(const KvcDesc& D, const float* S, int32_t* budgets,
                              int64_t* offsets, hipStream_t st) {
-  hipLaunchKernelGGL(kvc_budget_kernel, dim3(D.n_seq), dim3(BUDGET_THREADS), 0, st, D, S,
-                     budgets, offsets);
+  hipLaunchKernelGGL(kvc_budget_kernel, dim3(D.n_seq * (D.upseq / D.pool_size)),
+                     dim3(BUDGET_THREADS), 0, st, D, S, budgets, offsets);
   return hipGetLastError();
 }

@@ -56,6 +56,8 @@ static kvc_status make_desc(const kvc_problem* p, const kvc_params* prm, KvcDesc
   if (!(prm->rho > 0.0 && prm->rho <= 1.0)) return KVC_ERR_INVALID_ARG;
   if (!(prm->base_ratio >= 0.0 && prm->base_ratio <= 1.0)) return KVC_ERR_INVALID_ARG;
   if (prm->window < 0) return KVC_ERR_INVALID_ARG;
+  if (prm->budget_pool != KVC_POOL_SEQUENCE && prm->budget_pool != KVC_POOL_LAYER)
+    return KVC_ERR_INVALID_ARG;
   const int esz = p->dtype == KVC_BF16 ? 2 : 4;
   for (int a = 0; a < 3; ++a)
     if (p->k_stride[a] < 0 || p->v_stride[a] < 0) return KVC_ERR_INVALID_ARG;
@@ -84,6 +86,7 @@ static kvc_status make_desc(const kvc_problem* p, const kvc_params* prm, KvcDesc
   D->nwin = p->n_window_q;
   D->gw = (int)gw;
   D->upseq = (int)upseq;
+  D->pool_size = prm->budget_pool == KVC_POOL_LAYER ? p->n_kv_heads : (int)upseq;
   D->window = prm->window;
   D->dtype = p->dtype == KVC_BF16 ? 0 : 1;
   D->alpha = (float)prm->alpha;

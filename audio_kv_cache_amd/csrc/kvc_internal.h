@@ -21,6 +21,7 @@
 struct KvcDesc {
   int32_t n_seq, n_layers, n_heads, gqa, d, nwin, gw, upseq;  // upseq = n_layers*n_heads
   int32_t window, dtype;                                      // dtype: 0 bf16, 1 f32
+  int32_t pool_size;                    // heads per budget pool (upseq or n_heads)
   float alpha, rho;
   double base_ratio;
   int64_t ks[3], vs[3];                 // element strides: layer, head, token

@@ -57,6 +57,7 @@ class Config:
     retention: tuple = ()    # fixed per-sequence retention, or () for U(0.2,0.6)
     length_choices: tuple = ()
     sink_beta: float = SINK_BETA
+    budget_pool: int = 0     # 0: one pool per sequence, 1: one pool per layer
 
 
 CONFIGS = {

@@ -278,7 +278,7 @@ def main():
     del prob
     spec = api.Spec.for_tensors(k, v, gqa=cfg.gqa, seq_lens=hdr.lengths,
                                 retention=hdr.retention, n_window=cfg.n_window)
-    prm = api.Params(cfg.alpha, cfg.rho, cfg.window, cfg.base_ratio)
+    prm = api.Params(cfg.alpha, cfg.rho, cfg.window, cfg.base_ratio, cfg.budget_pool)
     out = api.allocate(spec, prm, k.device)
     stream = torch.cuda.current_stream()
 

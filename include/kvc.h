@@ -14,7 +14,8 @@
  *               F = rfft(s), E(k) = sum_{i<=k} |F_i|^2,
  *               k* = min{k : E(k) >= rho E(L/2)}, low-pass keeps bins 0..k*,
  *               s_hat = (1 - alpha) s + alpha irfft(F masked)
- *   3. budget   b_u = w + r + share of B_score proportional to S_u
+ *   3. budget   b_u = w + r + share of B_score proportional to S_u within
+ *               the unit's budget pool (the sequence, or its layer)
  *               (article section 3.1; defaults from the section 5.1 config)
  *   4. select   the b_u - w largest s_hat among positions [0, L-w), equal
  *               values resolved toward the lower position, plus the window
@@ -64,7 +65,16 @@ typedef struct {
   double rho;        /* SSS energy cutoff ratio, 0 < rho <= 1          [0.7] */
   int32_t window;    /* w, most recent positions always kept, >= 0      [32] */
   double base_ratio; /* r = floor(base_ratio * kbar), 0 <= . <= 1      [0.5] */
+  int32_t budget_pool; /* which heads share one budget pool (a kvc_pool)  [0] */
 } kvc_params;
+
+/* Budget pool of step 3.  AudioKV's section 3.1 indexes the audio score by
+ * layer and head without saying whether the score-proportional share is
+ * split across the whole model or within each layer:
+ *   KVC_POOL_SEQUENCE  one pool per sequence: all n_layers*n_kv_heads heads
+ *   KVC_POOL_LAYER     one pool per (sequence, layer): its n_kv_heads heads
+ * Either way every pool of n heads keeps n*min(kbar, L) rows in total. */
+typedef enum { KVC_POOL_SEQUENCE = 0, KVC_POOL_LAYER = 1 } kvc_pool;
 
 /* Problem shape.  Supported: 1 <= n_seq <= 64; head_dim in {64, 128};
  * gqa_group * n_window_q a multiple of 32 and at most 256; every sequence

@@ -154,13 +154,23 @@ def unit_compress(qu, ku, dtype: str, b: int, alpha: float, rho: float, window: 
     return dict(s=s, s_hat=s_hat, kstar=ks, energy=E, kept=kept)
 
 
-def problem_budgets(prob):
-    """Budgets for every unit in (seq, layer, head) order, plus offsets."""
+def problem_budgets(prob, budget_pool=None):
+    """Budgets for every unit in (seq, layer, head) order, plus offsets.
+
+    budget_pool 0 (default of the config): one pool per sequence over all its
+    (layer, KV head) heads; 1: the same budget rule applied to each layer's
+    KV heads on their own."""
     cfg, hdr = prob.cfg, prob.hdr
+    pool = cfg.budget_pool if budget_pool is None else budget_pool
+    S = np.asarray(hdr.head_scores).reshape(cfg.n_layers, cfg.n_kv_heads)
     out = []
     for i in range(cfg.n_seq):
-        out.append(budget(hdr.head_scores, int(hdr.lengths[i]), float(hdr.retention[i]),
-                          cfg.base_ratio, cfg.window))
+        L, r = int(hdr.lengths[i]), float(hdr.retention[i])
+        if pool == 1:
+            for l in range(cfg.n_layers):
+                out.append(budget(S[l], L, r, cfg.base_ratio, cfg.window))
+        else:
+            out.append(budget(S, L, r, cfg.base_ratio, cfg.window))
     b = np.concatenate(out).astype(np.int32)
     off = np.concatenate([[0], np.cumsum(b, dtype=np.int64)]).astype(np.int64)
     return b, off

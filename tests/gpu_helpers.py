@@ -56,7 +56,8 @@ class Dev:
         self.S = torch.from_numpy(np.ascontiguousarray(hdr.head_scores)).cuda()
         self.spec = api.Spec.for_tensors(self.k, self.v, gqa=cfg.gqa, seq_lens=hdr.lengths,
                                          retention=hdr.retention, n_window=cfg.n_window)
-        self.params = api.Params(cfg.alpha, cfg.rho, cfg.window, cfg.base_ratio)
+        self.params = api.Params(cfg.alpha, cfg.rho, cfg.window, cfg.base_ratio,
+                                 cfg.budget_pool)
         self.rows, self.ws_bytes = api.kvc_plan(self.spec, self.params)
 
     def units(self):
@@ -126,7 +127,8 @@ class Dev:
         o = api.compress(self.q, self.k, self.v, self.S, gqa=self.cfg.gqa,
                          seq_lens=self.hdr.lengths, retention=self.hdr.retention,
                          alpha=self.cfg.alpha, rho=self.cfg.rho, window=self.cfg.window,
-                         base_ratio=self.cfg.base_ratio, out=out)
+                         base_ratio=self.cfg.base_ratio, budget_pool=self.cfg.budget_pool,
+                         out=out)
         torch.cuda.synchronize()
         return o
 

@@ -46,6 +46,13 @@ def spec(**kw):
     return api.Spec(**base)
 
 
+def test_plan_total_rows_same_for_both_budget_pools():
+    sp = spec(seq_lens=[8192, 1024], retention=[0.6, 1.0])
+    a = api.kvc_plan(sp, api.Params(budget_pool=C.KVC_POOL_SEQUENCE))
+    b = api.kvc_plan(sp, api.Params(budget_pool=C.KVC_POOL_LAYER))
+    assert a == b
+
+
 def test_plan_total_rows_closed_form():
     for lens, ret in [([32768], 0.4), ([8192], 0.6), ([1024], 0.6), ([65536], 0.2),
                       ([4096, 32768, 8192], [0.2, 0.55, 1.0])]:
@@ -85,6 +92,7 @@ def test_invalid_problems_rejected_before_launch():
     assert status(spec(), api.Params(rho=0.0)) == C.KVC_ERR_INVALID_ARG
     assert status(spec(), api.Params(base_ratio=-0.1)) == C.KVC_ERR_INVALID_ARG
     assert status(spec(), api.Params(window=-1)) == C.KVC_ERR_INVALID_ARG
+    assert status(spec(), api.Params(budget_pool=2)) == C.KVC_ERR_INVALID_ARG
     assert status(spec(), q=None) == C.KVC_ERR_INVALID_ARG
     assert status(spec(), ko=ctypes.c_void_p((1 << 20) + 8)) == C.KVC_ERR_INVALID_ARG
     assert status(spec(), ws=ctypes.c_void_p((1 << 20) + 64)) == C.KVC_ERR_INVALID_ARG

@@ -74,6 +74,26 @@ def test_budget_bitexact_configs(name):
     assert int(off[-1]) == api.kvc_plan(spec, prm)[0]
 
 
+@pytest.mark.parametrize("name", ["tiny", "qwen7b", "omni30b", "ragged", "long64k"])
+def test_budget_bitexact_layer_pool(name):
+    say(f"[budget] layer pool {name}")
+    cfg = dataclasses.replace(synth.CONFIGS[name], budget_pool=1)
+    hdr = synth.header(cfg)
+    spec = api.Spec(n_layers=cfg.n_layers, n_kv_heads=cfg.n_kv_heads, gqa=cfg.gqa,
+                    head_dim=cfg.head_dim, seq_lens=hdr.lengths, retention=hdr.retention,
+                    dtype=cfg.dtype, n_window=cfg.n_window)
+    prm = api.Params(cfg.alpha, cfg.rho, cfg.window, cfg.base_ratio, budget_pool=1)
+    S = torch.from_numpy(hdr.head_scores).cuda()
+    b = torch.empty(spec.n_units, dtype=torch.int32, device="cuda")
+    off = torch.empty(spec.n_units + 1, dtype=torch.int64, device="cuda")
+    api.kvc_budget(spec, prm, S, b, off)
+    torch.cuda.synchronize()
+    want, want_off = O.problem_budgets(synth.Problem(hdr, None, None, None), budget_pool=1)
+    assert np.array_equal(b.cpu().numpy(), want)
+    assert np.array_equal(off.cpu().numpy(), want_off)
+    assert int(off[-1]) == api.kvc_plan(spec, prm)[0]
+
+
 def _budget_gpu(S, L, ret, base, w):
     S = np.asarray(S, np.float32).reshape(1, -1)
     spec = api.Spec(n_layers=1, n_kv_heads=S.shape[1], gqa=1, head_dim=64, seq_lens=[L],
@@ -322,6 +342,12 @@ def test_compress_omni30b_sampled():
     say("[e2e] omni30b")
     D = dev("omni30b")
     _check_e2e(D, [(0, 0, 0), (0, 31, 2)])
+
+
+def test_compress_qwen7b_layer_pool_sampled():
+    say("[e2e] qwen7b, one budget pool per layer")
+    D = dev("qwen7b", budget_pool=1)
+    _check_e2e(D, [(0, 0, 0), (0, 13, 2), (0, 27, 3)])
 
 
 def test_compress_long64k_sampled():

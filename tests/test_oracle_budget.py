@@ -151,3 +151,50 @@ def test_uniform_scores_differ_by_at_most_one_lower_index_first():
 def test_single_head_gets_exactly_kbar():
     for L, ret in [(1024, 0.6), (32768, 0.4), (65536, 0.2)]:
         assert O.budget([0.7], L, ret).tolist() == [math.floor(ret * L)]
+
+
+# ---------------------------------------------------------------------------
+# One budget pool per layer (the alternative reading of AudioKV section 3.1:
+# the score-proportional share split among a layer's heads only)
+# ---------------------------------------------------------------------------
+class _Prob:
+    def __init__(self, S, lengths, retention, base_ratio=0.5, window=4, pool=1):
+        NL, H = np.asarray(S).shape
+        self.cfg = type("C", (), dict(n_layers=NL, n_kv_heads=H, n_seq=len(lengths),
+                                      base_ratio=base_ratio, window=window, budget_pool=pool))()
+        self.hdr = type("H", (), dict(head_scores=np.asarray(S, np.float32),
+                                      lengths=np.asarray(lengths), retention=np.asarray(retention)))()
+
+
+def test_layer_pool_hand_case():
+    # L = 100, retention 0.5 -> kbar 50; w = 4, base_ratio 0.5 -> r = 25,
+    # fixed = 29, cap = 71.  Layer 0, S = (1, 3): R = 2*50 - 2*29 = 42,
+    # quotas 10.5 and 31.5, floors 10 + 31 = 41, one left over, equal
+    # remainders -> the lower head: (11, 31) -> budgets (40, 60).  Layer 1,
+    # S = (0, 0): uniform 21 each -> (50, 50).  One pool over all four heads
+    # instead: R = 84 split 21 / 63 / 0 / 0 -> (50, 92, 29, 29).
+    S = [[1.0, 3.0], [0.0, 0.0]]
+    b_layer, off = O.problem_budgets(_Prob(S, [100], [0.5], pool=1))
+    assert b_layer.tolist() == [40, 60, 50, 50]
+    assert off.tolist() == [0, 40, 100, 150, 200]
+    b_seq, _ = O.problem_budgets(_Prob(S, [100], [0.5], pool=0))
+    assert b_seq.tolist() == [50, 92, 29, 29]
+
+
+def test_layer_pool_sums_per_layer_and_single_layer_equals_sequence_pool():
+    r = np.random.default_rng(5)
+    for _ in range(50):
+        NL, H = int(r.integers(1, 6)), int(r.integers(1, 9))
+        L = int(r.choice([64, 256, 1024]))
+        ret = float(r.uniform(0.2, 1.0))
+        S = r.uniform(0, 1, (NL, H)).astype(np.float32)
+        S[r.random((NL, H)) < 0.3] = 0.0
+        kbar = math.floor(ret * L)
+        if kbar < L and 4 + math.floor(0.5 * kbar) > kbar:
+            continue
+        b, _ = O.problem_budgets(_Prob(S, [L], [ret], pool=1))
+        per = b.reshape(NL, H).sum(axis=1)
+        assert (per == H * min(kbar, L)).all()
+        if NL == 1:
+            b0, _ = O.problem_budgets(_Prob(S, [L], [ret], pool=0))
+            assert np.array_equal(b, b0)
