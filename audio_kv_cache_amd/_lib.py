@@ -24,9 +24,9 @@ KVC_ERR_HIP = 5
 KVC_BF16 = 0
 KVC_F32 = 1
 
-EXPORTS = ("kvc_plan", "kvc_compress", "kvc_scores", "kvc_score_stats", "kvc_score_pool",
-           "kvc_smooth", "kvc_budget", "kvc_select", "kvc_gather", "kvc_status_str",
-           "kvc_last_hip_error")
+EXPORTS = ("kvc_plan", "kvc_compress", "kvc_compress_layers", "kvc_scores", "kvc_score_stats",
+           "kvc_score_pool", "kvc_smooth", "kvc_budget", "kvc_select", "kvc_gather",
+           "kvc_status_str", "kvc_last_hip_error")
 # include/kvc_voxzip.h
 VZ_EXPORTS = ("kvc_vz_plan", "kvc_vz_step", "kvc_vz_accumulate", "kvc_vz_evict",
               "kvc_vz_gather")
@@ -95,6 +95,9 @@ def lib():
             L.kvc_plan.argtypes = [prob, prm, _P(ctypes.c_int64), _P(ctypes.c_size_t)]
             L.kvc_compress.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, ctypes.c_size_t, _vp]
+            L.kvc_compress_layers.argtypes = [prob, prm, ctypes.c_int32, ctypes.c_int32, _vp,
+                                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              ctypes.c_size_t, _vp]
             L.kvc_scores.argtypes = [prob, prm, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
             L.kvc_score_stats.argtypes = [prob, prm, _vp, _vp, _vp, ctypes.c_size_t, _vp]
             L.kvc_score_pool.argtypes = [prob, prm, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -102,7 +105,7 @@ def lib():
             L.kvc_budget.argtypes = [prob, prm, _vp, _vp, _vp, _vp]
             L.kvc_select.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp]
             L.kvc_gather.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
-            for name in EXPORTS[:9]:
+            for name in EXPORTS[:10]:
                 getattr(L, name).restype = ctypes.c_int
             vp, vq = _P(kvc_vz_problem), _P(kvc_vz_params)
             L.kvc_vz_plan.argtypes = [vp, vq, _P(ctypes.c_int64), _P(ctypes.c_size_t)]

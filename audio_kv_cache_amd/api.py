@@ -121,6 +121,19 @@ def kvc_compress(spec, params, q, k, v, head_scores, k_out, v_out, idx_out, seg_
                                  _stream(stream)), "kvc_compress")
 
 
+def kvc_compress_layers(spec, params, layer_begin, layer_end, q, k, v, head_scores, k_out,
+                        v_out, idx_out, seg_offsets, budgets, workspace, stream=None):
+    """q, k, v hold layers [layer_begin, layer_end) only (k, v with spec's
+    strides); outputs are the whole problem's."""
+    C.check(C.lib().kvc_compress_layers(ctypes.byref(spec.c()), ctypes.byref(params.c()),
+                                        int(layer_begin), int(layer_end), _ptr(q), _ptr(k),
+                                        _ptr(v), _ptr(head_scores), _ptr(k_out), _ptr(v_out),
+                                        _ptr(idx_out), _ptr(seg_offsets), _ptr(budgets),
+                                        _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream)), "kvc_compress_layers")
+
+
 def kvc_scores(spec, params, q, k, s_out, workspace, stream=None):
     C.check(C.lib().kvc_scores(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(q),
                                _ptr(k), _ptr(s_out), _ptr(workspace),

@@ -48,9 +48,8 @@ __global__ __launch_bounds__(GATHER_THREADS) void kvc_gather_kernel(
       const int l = within / D.n_heads, h = within - l * D.n_heads;
       int pos = idx[t];
       if ((unsigned)pos >= (unsigned)D.L[seq]) pos = 0;  // never read outside the row
-      const int64_t tok = D.tok0[seq] + pos;
-      const char* ks = k + (l * D.ks[0] + h * D.ks[1] + tok * D.ks[2]) * esz;
-      const char* vs = v + (l * D.vs[0] + h * D.vs[1] + tok * D.vs[2]) * esz;
+      const char* ks = k + (kvc_kv_offset(D.ks, D, seq, l, h) + (int64_t)pos * D.ks[2]) * esz;
+      const char* vs = v + (kvc_kv_offset(D.vs, D, seq, l, h) + (int64_t)pos * D.vs[2]) * esz;
       kv[p] = *reinterpret_cast<const uint4*>(ks + chunk * 16);
       vv[p] = *reinterpret_cast<const uint4*>(vs + chunk * 16);
     }

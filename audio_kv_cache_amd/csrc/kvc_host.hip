@@ -87,6 +87,8 @@ static kvc_status make_desc(const kvc_problem* p, const kvc_params* prm, KvcDesc
   D->gw = (int)gw;
   D->upseq = (int)upseq;
   D->pool_size = prm->budget_pool == KVC_POOL_LAYER ? p->n_kv_heads : (int)upseq;
+  D->layer0 = 0;
+  D->q_layers = p->n_layers;
   D->window = prm->window;
   D->dtype = p->dtype == KVC_BF16 ? 0 : 1;
   D->alpha = (float)prm->alpha;
@@ -163,14 +165,17 @@ static Carve carve(const KvcDesc& D, void* ws) {
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-extern "C" kvc_status kvc_compress(const kvc_problem* prob, const kvc_params* params,
-                                   const void* q_window, const void* k, const void* v,
-                                   const float* head_scores, void* k_out, void* v_out,
-                                   int32_t* idx_out, int64_t* seg_offsets, int32_t* budgets,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+static kvc_status compress_range(const kvc_problem* prob, const kvc_params* params, int lb,
+                                 int le, const void* q_window, const void* k, const void* v,
+                                 const float* head_scores, void* k_out, void* v_out,
+                                 int32_t* idx_out, int64_t* seg_offsets, int32_t* budgets,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   KvcDesc D;
   kvc_status st = make_desc(prob, params, &D);
   if (st != KVC_OK) return st;
+  if (lb < 0 || le > D.n_layers || lb >= le) return KVC_ERR_INVALID_ARG;
+  D.layer0 = lb;
+  D.q_layers = le - lb;
   if (!q_window || !k || !v || !head_scores || !k_out || !v_out || !idx_out || !seg_offsets ||
       !budgets || !workspace)
     return KVC_ERR_INVALID_ARG;
@@ -181,25 +186,59 @@ extern "C" kvc_status kvc_compress(const kvc_problem* prob, const kvc_params* pa
   if (workspace_bytes < need) return KVC_ERR_WORKSPACE;
   const Carve c = carve(D, workspace);
   hipStream_t s = (hipStream_t)stream;
-  // One launch per step and sequence over all of the sequence's units (more,
-  // smaller launches cost more in launch and queue latency than they save).
+  // Budgets and offsets of every unit (they depend only on S, L and the
+  // retention), then one launch per step and sequence over the units of
+  // layers [lb, le) (more, smaller launches cost more in launch and queue
+  // latency than they save).
   hipError_t e = kvc_launch_budget(D, head_scores, budgets, seg_offsets, s);
   if (e != hipSuccess) return hip_status(e);
+  const bool whole = lb == 0 && le == D.n_layers;
   for (int seq = 0; seq < D.n_seq; ++seq) {
-    const int u0 = seq * D.upseq, u1 = u0 + D.upseq;
+    const int u0 = (seq * D.n_layers + lb) * D.n_heads, u1 = (seq * D.n_layers + le) * D.n_heads;
     if ((e = kvc_launch_scores(D, u0, u1, q_window, k, c.srows, c.partials, c.lse2, s)) !=
         hipSuccess)
       return hip_status(e);
   }
   for (int seq = 0; seq < D.n_seq; ++seq) {
-    const int u0 = seq * D.upseq, u1 = u0 + D.upseq;
+    const int u0 = (seq * D.n_layers + lb) * D.n_heads, u1 = (seq * D.n_layers + le) * D.n_heads;
     if ((e = kvc_launch_sss_select(D, u0, u1, 1 | 2, c.srows, nullptr, nullptr, budgets,
                                    seg_offsets, idx_out, s)) != hipSuccess)
       return hip_status(e);
   }
-  e = kvc_launch_gather(D, 0, D.n_units, k, v, idx_out, seg_offsets, k_out, v_out,
-                        D.row_base[D.n_seq], s);
+  if (whole) {
+    e = kvc_launch_gather(D, 0, D.n_units, k, v, idx_out, seg_offsets, k_out, v_out,
+                          D.row_base[D.n_seq], s);
+  } else {
+    for (int seq = 0; seq < D.n_seq && e == hipSuccess; ++seq) {
+      const int u0 = (seq * D.n_layers + lb) * D.n_heads;
+      const int u1 = (seq * D.n_layers + le) * D.n_heads;
+      // grid sizing only: the layers' share of the sequence's rows
+      const int64_t est = (D.row_base[seq + 1] - D.row_base[seq]) * (le - lb) / D.n_layers;
+      e = kvc_launch_gather(D, u0, u1, k, v, idx_out, seg_offsets, k_out, v_out, est, s);
+    }
+  }
   return hip_status(e);
+}
+
+extern "C" kvc_status kvc_compress(const kvc_problem* prob, const kvc_params* params,
+                                   const void* q_window, const void* k, const void* v,
+                                   const float* head_scores, void* k_out, void* v_out,
+                                   int32_t* idx_out, int64_t* seg_offsets, int32_t* budgets,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  const int nl = prob ? prob->n_layers : 0;
+  return compress_range(prob, params, 0, nl, q_window, k, v, head_scores, k_out, v_out, idx_out,
+                        seg_offsets, budgets, workspace, workspace_bytes, stream);
+}
+
+extern "C" kvc_status kvc_compress_layers(const kvc_problem* prob, const kvc_params* params,
+                                          int32_t layer_begin, int32_t layer_end,
+                                          const void* q_window, const void* k, const void* v,
+                                          const float* head_scores, void* k_out, void* v_out,
+                                          int32_t* idx_out, int64_t* seg_offsets,
+                                          int32_t* budgets, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  return compress_range(prob, params, layer_begin, layer_end, q_window, k, v, head_scores, k_out,
+                        v_out, idx_out, seg_offsets, budgets, workspace, workspace_bytes, stream);
 }
 
 static kvc_status scores_common(const kvc_problem* prob, const kvc_params* params,

@@ -22,6 +22,7 @@ struct KvcDesc {
   int32_t n_seq, n_layers, n_heads, gqa, d, nwin, gw, upseq;  // upseq = n_layers*n_heads
   int32_t window, dtype;                                      // dtype: 0 bf16, 1 f32
   int32_t pool_size;                    // heads per budget pool (upseq or n_heads)
+  int32_t layer0, q_layers;             // q/k/v hold layers layer0 .. layer0+q_layers-1
   float alpha, rho;
   double base_ratio;
   int64_t ks[3], vs[3];                 // element strides: layer, head, token
@@ -35,6 +36,17 @@ struct KvcDesc {
   int32_t n_units;
   int32_t total_tiles;
 };
+
+// Element offsets of unit (seq, l, h)'s window queries in q_window and of
+// its first K (or V) row: the q/k/v pointers hold layers layer0 onward.
+__host__ __device__ inline int64_t kvc_q_offset(const KvcDesc& D, int seq, int l, int h) {
+  return (((int64_t)seq * D.q_layers + (l - D.layer0)) * D.n_heads * D.gqa + (int64_t)h * D.gqa) *
+         D.nwin * D.d;
+}
+__host__ __device__ inline int64_t kvc_kv_offset(const int64_t (&st)[3], const KvcDesc& D, int seq,
+                                                 int l, int h) {
+  return (int64_t)(l - D.layer0) * st[0] + (int64_t)h * st[1] + D.tok0[seq] * st[2];
+}
 
 // Unit u -> (sequence, unit within sequence).
 __host__ __device__ inline int kvc_tiles_per_unit(int L) {

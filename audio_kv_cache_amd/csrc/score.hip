@@ -150,9 +150,8 @@ __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_stats_kernel
   const int ncb = NBC > 0 ? NBC : gw / M;
   const float c = kLog2e / sqrtf((float)D);
   const elem_t* qg =
-      q + ((size_t)((int64_t)ti.seq * Dsc.n_layers + ti.l) * Dsc.n_heads * Dsc.gqa +
-           (size_t)ti.h * Dsc.gqa) * Dsc.nwin * D;
-  const elem_t* ku = k + ti.l * Dsc.ks[0] + ti.h * Dsc.ks[1] + Dsc.tok0[ti.seq] * Dsc.ks[2];
+      q + kvc_q_offset(Dsc, ti.seq, ti.l, ti.h);
+  const elem_t* ku = k + kvc_kv_offset(Dsc.ks, Dsc, ti.seq, ti.l, ti.h);
   stage_q<T, D, QS>(sQ, qg, gw);
   __syncthreads();
 
@@ -310,9 +309,8 @@ __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_pool_kernel(
   const float c = kLog2e / sqrtf((float)D);
   const float inv_gw = 1.0f / (float)gw;
   const elem_t* qg =
-      q + ((size_t)((int64_t)ti.seq * Dsc.n_layers + ti.l) * Dsc.n_heads * Dsc.gqa +
-           (size_t)ti.h * Dsc.gqa) * Dsc.nwin * D;
-  const elem_t* ku = k + ti.l * Dsc.ks[0] + ti.h * Dsc.ks[1] + Dsc.tok0[ti.seq] * Dsc.ks[2];
+      q + kvc_q_offset(Dsc, ti.seq, ti.l, ti.h);
+  const elem_t* ku = k + kvc_kv_offset(Dsc.ks, Dsc, ti.seq, ti.l, ti.h);
   stage_q<T, D, QS>(sQ, qg, gw);
   if (threadIdx.x < gw) sL[threadIdx.x] = lse2[(size_t)ti.u * gw + threadIdx.x];
   __syncthreads();
@@ -519,9 +517,8 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
   const float c = kLog2e / sqrtf((float)D);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool two = 2 * wave + 1 < NBC;
-  const uint16_t* qg = q + ((size_t)((int64_t)ti.seq * Dsc.n_layers + ti.l) * Dsc.n_heads * Dsc.gqa +
-                            (size_t)ti.h * Dsc.gqa) * Dsc.nwin * D;
-  const uint16_t* ku = k + ti.l * Dsc.ks[0] + ti.h * Dsc.ks[1] + Dsc.tok0[ti.seq] * Dsc.ks[2];
+  const uint16_t* qg = q + kvc_q_offset(Dsc, ti.seq, ti.l, ti.h);
+  const uint16_t* ku = k + kvc_kv_offset(Dsc.ks, Dsc, ti.seq, ti.l, ti.h);
 
   // A operand (rows = queries) and minus the LSE of each output row the lane
   // holds: element i of the 32x32 block is row (i/4)*8 + (lane/32)*4 + i%4.
@@ -630,9 +627,8 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
   const float c = kLog2e / sqrtf((float)D);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool two = 2 * wave + 1 < NBC;
-  const uint16_t* qg = q + ((size_t)((int64_t)ti.seq * Dsc.n_layers + ti.l) * Dsc.n_heads * Dsc.gqa +
-                            (size_t)ti.h * Dsc.gqa) * Dsc.nwin * D;
-  const uint16_t* ku = k + ti.l * Dsc.ks[0] + ti.h * Dsc.ks[1] + Dsc.tok0[ti.seq] * Dsc.ks[2];
+  const uint16_t* qg = q + kvc_q_offset(Dsc, ti.seq, ti.l, ti.h);
+  const uint16_t* ku = k + kvc_kv_offset(Dsc.ks, Dsc, ti.seq, ti.l, ti.h);
 
   // B operand (columns = queries): the wave's two query blocks (a wave with
   // one block repeats it and discards the copy's statistics).

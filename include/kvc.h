@@ -120,6 +120,29 @@ kvc_status kvc_compress(const kvc_problem *prob, const kvc_params *params,
                         int32_t *budgets, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/* Streaming prefill: steps 1-5 for the units of layers [layer_begin,
+ * layer_end) only, so a caller can compress each layer (or group of layers)
+ * as soon as its K/V exist.  Budgets and offsets depend only on the head
+ * scores, the lengths and the retention, so they are computed for every unit
+ * on every call (identically); the rows of the range's units land at their
+ * final places in the whole-problem outputs, which the other layers' calls
+ * fill in turn.  Arguments as for kvc_compress, except:
+ *   q_window  device [n_seq][layer_end-layer_begin][n_kv_heads*gqa_group]
+ *             [n_window_q][head_dim]: the range's window queries only
+ *   k, v      device, element (l, h, t, c) of layer l in the range at
+ *             (l - layer_begin)*stride[0] + h*stride[1] + t*stride[2] + c:
+ *             pointers to the range's first layer, prob's strides
+ *   k_out, v_out, idx_out, seg_offsets, budgets, workspace: sized for the
+ *             whole problem (kvc_plan); rows of other layers are untouched.
+ * 0 <= layer_begin < layer_end <= n_layers, else KVC_ERR_INVALID_ARG. */
+kvc_status kvc_compress_layers(const kvc_problem *prob, const kvc_params *params,
+                               int32_t layer_begin, int32_t layer_end,
+                               const void *q_window, const void *k, const void *v,
+                               const float *head_scores, void *k_out, void *v_out,
+                               int32_t *idx_out, int64_t *seg_offsets,
+                               int32_t *budgets, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* Stage entry points, same conventions; they run the kernels kvc_compress
  * runs, one step at a time.
  *

@@ -162,3 +162,14 @@ def test_vz_invalid_problems_rejected_before_launch():
     assert vz_status(vz_spec(), api.VzParams(n_sink=-1)) == C.KVC_ERR_INVALID_ARG
     assert vz_status(vz_spec(), ws_bytes=16) == C.KVC_ERR_WORKSPACE
     assert vz_status(vz_spec(k_stride=(8200 * 128, 100))) == C.KVC_ERR_INVALID_ARG  # row < d
+
+
+def test_compress_layers_rejects_bad_ranges():
+    L = C.lib()
+    sp = spec()
+    fake = ctypes.c_void_p(1 << 20)
+    for lb, le in [(-1, 2), (3, 3), (5, 2), (0, 49)]:
+        st = L.kvc_compress_layers(ctypes.byref(sp.c()), ctypes.byref(api.Params().c()), lb, le,
+                                   fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                   1 << 40, None)
+        assert st == C.KVC_ERR_INVALID_ARG, (lb, le)

@@ -373,3 +373,36 @@ def test_compress_deterministic():
     b = D.compress()
     for key in ("idx", "k_out", "v_out", "budgets", "offsets"):
         assert torch.equal(a[key], b[key]), key
+
+
+# ---------------------------------------------------------------------------
+# Streaming prefill: layer-range calls reproduce the whole-model call
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,ranges", [("qwen7b", [(0, 1), (1, 3), (3, 4)]),
+                                         ("ragged", [(0, 2), (2, 3)])])
+def test_compress_layers_equals_whole_call(name, ranges):
+    say(f"[e2e] layer ranges {name} {ranges}")
+    NL = ranges[-1][1]
+    cfg = dataclasses.replace(synth.CONFIGS[name], n_layers=NL)
+    if name == "ragged":
+        cfg = dataclasses.replace(cfg, n_seq=3)
+    D = Dev(synth.problem(cfg))
+    whole = D.compress()
+    out = api.allocate(D.spec, D.params, "cuda")
+    for t in ("k_out", "v_out"):
+        out[t].zero_()
+    out["idx"].fill_(-1)
+    for lb, le in ranges:
+        # each range's inputs in buffers of their own, as a streaming caller has them
+        q = D.q[:, lb:le].contiguous()
+        k = D.k[lb:le].contiguous()
+        v = D.v[lb:le].contiguous()
+        api.kvc_compress_layers(D.spec, D.params, lb, le, q, k, v, D.S, out["k_out"],
+                                out["v_out"], out["idx"], out["offsets"], out["budgets"],
+                                out["workspace"])
+    torch.cuda.synchronize()
+    for key in ("budgets", "offsets", "idx"):
+        assert torch.equal(out[key], whole[key]), key
+    for key in ("k_out", "v_out"):
+        assert torch.equal(out[key].view(torch.int16) if D.dtype == "bf16" else out[key],
+                           whole[key].view(torch.int16) if D.dtype == "bf16" else whole[key]), key
