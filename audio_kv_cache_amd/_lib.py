@@ -34,12 +34,14 @@ VZ_EXPORTS = ("kvc_vz_plan", "kvc_vz_step", "kvc_vz_accumulate", "kvc_vz_evict",
 
 KVC_POOL_SEQUENCE = 0
 KVC_POOL_LAYER = 1
+KVC_SCORE_MEAN = 0
+KVC_SCORE_MAX = 1
 
 
 class kvc_params(ctypes.Structure):
     _fields_ = [("alpha", ctypes.c_double), ("rho", ctypes.c_double),
                 ("window", ctypes.c_int32), ("base_ratio", ctypes.c_double),
-                ("budget_pool", ctypes.c_int32)]
+                ("budget_pool", ctypes.c_int32), ("score_pool", ctypes.c_int32)]
 
 
 class kvc_problem(ctypes.Structure):

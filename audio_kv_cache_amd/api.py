@@ -27,10 +27,11 @@ class Params:
     window: int = 32
     base_ratio: float = 0.5
     budget_pool: int = C.KVC_POOL_SEQUENCE   # or C.KVC_POOL_LAYER
+    score_pool: int = C.KVC_SCORE_MEAN       # or C.KVC_SCORE_MAX
 
     def c(self) -> C.kvc_params:
         return C.kvc_params(float(self.alpha), float(self.rho), int(self.window),
-                            float(self.base_ratio), int(self.budget_pool))
+                            float(self.base_ratio), int(self.budget_pool), int(self.score_pool))
 
 
 class Spec:
@@ -201,13 +202,13 @@ def allocate(spec: Spec, params: Params, device):
 
 
 def compress(q, k, v, head_scores, *, gqa, seq_lens, retention, alpha=0.5, rho=0.7,
-             window=32, base_ratio=0.5, budget_pool=C.KVC_POOL_SEQUENCE, out=None,
-             stream=None):
+             window=32, base_ratio=0.5, budget_pool=C.KVC_POOL_SEQUENCE,
+             score_pool=C.KVC_SCORE_MEAN, out=None, stream=None):
     """Whole path; returns dict(k_out, v_out, idx, offsets, budgets, workspace)."""
     _require_gpu(q, k, v, head_scores)
     spec = Spec.for_tensors(k, v, gqa=gqa, seq_lens=seq_lens, retention=retention,
                             n_window=q.shape[-2])
-    params = Params(alpha, rho, window, base_ratio, budget_pool)
+    params = Params(alpha, rho, window, base_ratio, budget_pool, score_pool)
     o = out if out is not None else allocate(spec, params, k.device)
     kvc_compress(spec, params, q, k, v, head_scores, o["k_out"], o["v_out"], o["idx"],
                  o["offsets"], o["budgets"], o["workspace"], stream)

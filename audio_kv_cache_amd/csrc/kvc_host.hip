@@ -58,6 +58,8 @@ static kvc_status make_desc(const kvc_problem* p, const kvc_params* prm, KvcDesc
   if (prm->window < 0) return KVC_ERR_INVALID_ARG;
   if (prm->budget_pool != KVC_POOL_SEQUENCE && prm->budget_pool != KVC_POOL_LAYER)
     return KVC_ERR_INVALID_ARG;
+  if (prm->score_pool != KVC_SCORE_MEAN && prm->score_pool != KVC_SCORE_MAX)
+    return KVC_ERR_INVALID_ARG;
   const int esz = p->dtype == KVC_BF16 ? 2 : 4;
   for (int a = 0; a < 3; ++a)
     if (p->k_stride[a] < 0 || p->v_stride[a] < 0) return KVC_ERR_INVALID_ARG;
@@ -73,6 +75,7 @@ static kvc_status make_desc(const kvc_problem* p, const kvc_params* prm, KvcDesc
   if (p->head_dim != 64 && p->head_dim != 128) return KVC_ERR_UNSUPPORTED;
   const int64_t gw = (int64_t)p->gqa_group * p->n_window_q;
   if (gw % 32 != 0 || gw > KVC_MAX_GW) return KVC_ERR_UNSUPPORTED;
+  if (prm->score_pool == KVC_SCORE_MAX && p->n_window_q % 32 != 0) return KVC_ERR_UNSUPPORTED;
   const int64_t upseq = (int64_t)p->n_layers * p->n_kv_heads;
   if (upseq > KVC_MAX_UNITS_PER_SEQ) return KVC_ERR_UNSUPPORTED;
   if (upseq * p->n_seq > (int64_t)1 << 30) return KVC_ERR_UNSUPPORTED;
@@ -87,6 +90,7 @@ static kvc_status make_desc(const kvc_problem* p, const kvc_params* prm, KvcDesc
   D->gw = (int)gw;
   D->upseq = (int)upseq;
   D->pool_size = prm->budget_pool == KVC_POOL_LAYER ? p->n_kv_heads : (int)upseq;
+  D->score_max = prm->score_pool == KVC_SCORE_MAX;
   D->layer0 = 0;
   D->q_layers = p->n_layers;
   D->window = prm->window;

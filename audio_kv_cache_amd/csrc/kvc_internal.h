@@ -23,6 +23,7 @@ struct KvcDesc {
   int32_t window, dtype;                                      // dtype: 0 bf16, 1 f32
   int32_t pool_size;                    // heads per budget pool (upseq or n_heads)
   int32_t layer0, q_layers;             // q/k/v hold layers layer0 .. layer0+q_layers-1
+  int32_t score_max;                    // 1: max over query heads of head means
   float alpha, rho;
   double base_ratio;
   int64_t ks[3], vs[3];                 // element strides: layer, head, token

@@ -374,6 +374,12 @@ __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_pool_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
+      // Max pooling over query heads: each head's W rows are whole blocks
+      // (W a multiple of 32); at a head's last block its sum is completed
+      // over the lanes holding the key and folded into the running maximum.
+      float hmax[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) hmax[cb] = 0.f;
 #pragma unroll
       for (int rb = 0; rb < MAXRB; ++rb) {
         if (rb < nrb) {
@@ -381,7 +387,24 @@ __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_pool_kernel(
           mma_blk(X, b, rb, qoff);
           pool_blk(X, acc_s, rb, ln);
           if constexpr (!PIPE) __builtin_amdgcn_sched_barrier(0);
+          if (Dsc.score_max && ((rb + 1) * M) % Dsc.nwin == 0) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+              float v = acc_s[cb];
+#pragma unroll
+              for (int o = M; o < 64; o <<= 1) v += __shfl_xor(v, o);
+              hmax[cb] = fmaxf(hmax[cb], v);
+              acc_s[cb] = 0.f;
+            }
+          }
         }
+      }
+      if (Dsc.score_max) {
+        const float inv_w = 1.0f / (float)Dsc.nwin;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          if (lgrp == 0) srow[kb + cb * M + lrow] = hmax[cb] * inv_w;
+        return;
       }
     }
 #pragma unroll
@@ -503,14 +526,19 @@ __device__ inline void qs_qfrag(bf16x8 (&f)[QsCfg<D>::NK], const uint16_t* qg, i
     }                                                      \
   } while (0)
 
-template <int D, int NBC>
+// MAXP: max pooling over query heads (W a multiple of 32, so every 32-query
+// block belongs to one head): the per-block sums are kept apart in LDS and
+// combined per head, then maximised, at the end of the tile.  Otherwise the
+// wave's two blocks are summed in-lane and the waves summed at the end.
+template <int D, int NBC, bool MAXP>
 __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_score_pool_qs_kernel(
     KvcDesc Dsc, int tile0, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const float* __restrict__ lse2, float* __restrict__ s) {
   using C = QsCfg<D>;
   constexpr int NW = QsWaves<NBC>::NW, NT = QsWaves<NBC>::NT, NK = C::NK;
+  constexpr int NROWS = MAXP ? 2 * NW : NW;
   __shared__ __attribute__((aligned(16))) char sK[2][C::CHUNK * C::RS];
-  __shared__ float sRed[NW][KVC_TILE_KEYS];
+  __shared__ float sRed[NROWS][KVC_TILE_KEYS];
   const int tile = tile0 + xcd_local_tile((int)blockIdx.x, (int)gridDim.x);
   const TileInfo ti = tile_info(Dsc, tile);
   const int gw = NBC * 32;
@@ -556,9 +584,18 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
   };
   // Both lane halves hold the same sum after the exchange and both write it
   // (same value, same address): no lane mask, no branch in the loop body.
-  auto flush = [&](float sum, int key) {       // key = tile-relative first key of the block
+  auto flush1 = [&](float sum, int row, int key) {
     sum += __shfl_xor(sum, 32);
-    sRed[wave][key + (lane & 31)] = sum;
+    sRed[row][key + (lane & 31)] = sum;
+  };
+  // sums of the wave's blocks 0 and 1 for the 32 keys from `key` (tile-relative)
+  auto flush = [&](float s_b0, float s_b1, int key) {
+    if constexpr (MAXP) {
+      flush1(s_b0, 2 * wave, key);
+      flush1(s_b1, 2 * wave + 1, key);
+    } else {
+      flush1(s_b0 + s_b1, wave, key);
+    }
   };
 
   // The loop body is branch-free so that the scheduling groups hold: the
@@ -583,7 +620,7 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
     QS_INTERLEAVE(6);
     // [C] keys 32-63 x block 0, beside keys 0-31 x block 1
     mma(X, qf0, kf1);
-    flush(s0 + pool(Y, nl1), ch * C::CHUNK);
+    flush(s0, pool(Y, nl1), ch * C::CHUNK);
     QS_INTERLEAVE(6);
     // [D] keys 32-63 x block 1, beside keys 32-63 x block 0
     mma(Y, qf1, kf1);
@@ -598,19 +635,33 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
     qs_kfrag<D>(kf0, sK[ch & 1], 0, lane);
     const floatx16 Yp = Y;
     mma(X, qf0, kf0);
-    flush(s0 + pool(Yp, nl1), (ch - 1) * C::CHUNK + 32);
+    flush(s0, pool(Yp, nl1), (ch - 1) * C::CHUNK + 32);
     QS_INTERLEAVE(6);
   }
-  flush(s0 + pool(Y, nl1), (nch - 1) * C::CHUNK + 32);
+  flush(s0, pool(Y, nl1), (nch - 1) * C::CHUNK + 32);
   __syncthreads();
   // Sum the waves' partial pools for every key of the tile.
   float* srow = s + Dsc.srow_base[ti.seq] + (int64_t)(ti.u - ti.seq * Dsc.upseq) * ti.L;
-  const float inv_gw = 1.0f / (float)gw;
-  for (int j = threadIdx.x; j < ti.keys; j += NT) {
-    float v = 0.f;
+  if constexpr (MAXP) {
+    const int bph = Dsc.nwin / 32;             // blocks per head
+    const float inv_w = 1.0f / (float)Dsc.nwin;
+    for (int j = threadIdx.x; j < ti.keys; j += NT) {
+      float best = 0.f;
+      for (int b0 = 0; b0 < NBC; b0 += bph) {
+        float v = 0.f;
+        for (int b = b0; b < b0 + bph; ++b) v += sRed[b][j];
+        best = fmaxf(best, v);
+      }
+      srow[ti.key0 + j] = best * inv_w;
+    }
+  } else {
+    const float inv_gw = 1.0f / (float)gw;
+    for (int j = threadIdx.x; j < ti.keys; j += NT) {
+      float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) v += sRed[w][j];
-    srow[ti.key0 + j] = v * inv_gw;
+      for (int w = 0; w < NW; ++w) v += sRed[w][j];
+      srow[ti.key0 + j] = v * inv_gw;
+    }
   }
 }
 
@@ -752,9 +803,12 @@ static void launch_qs(const KvcDesc& D, int u0, int u1, const void* q, const voi
     hipLaunchKernelGGL(kvc_score_lse_kernel, dim3(u1 - u0), dim3(KVC_MAX_GW), 0, st, D, u0,
                        kLog2e / sqrtf((float)Dm), (const float2*)partials, lse2);
   }
-  if (which & 2)
-    hipLaunchKernelGGL((kvc_score_pool_qs_kernel<Dm, NBC>), dim3(nt), dim3(NT), 0, st, D, t0,
-                       (const uint16_t*)q, (const uint16_t*)k, (const float*)lse2, s);
+  if ((which & 2) && D.score_max)
+    hipLaunchKernelGGL((kvc_score_pool_qs_kernel<Dm, NBC, true>), dim3(nt), dim3(NT), 0, st, D,
+                       t0, (const uint16_t*)q, (const uint16_t*)k, (const float*)lse2, s);
+  else if (which & 2)
+    hipLaunchKernelGGL((kvc_score_pool_qs_kernel<Dm, NBC, false>), dim3(nt), dim3(NT), 0, st, D,
+                       t0, (const uint16_t*)q, (const uint16_t*)k, (const float*)lse2, s);
 }
 
 template <int Dm>

@@ -58,6 +58,7 @@ class Config:
     length_choices: tuple = ()
     sink_beta: float = SINK_BETA
     budget_pool: int = 0     # 0: one pool per sequence, 1: one pool per layer
+    score_pool: int = 0      # 0: mean over the group's queries, 1: max over heads
 
 
 CONFIGS = {

@@ -7,7 +7,8 @@
  * Models"), run per unit u = (sequence, layer, KV head):
  *
  *   1. scores   s[j] = mean over the unit's G*W observation-window queries of
- *               softmax_j(q . k_j / sqrt(d)) over the L audio keys
+ *               softmax_j(q . k_j / sqrt(d)) over the L audio keys (or the
+ *               max over query heads of the head means, kvc_score)
  *               (article section 1.2; softmax(qK^T/sqrt(d)) as in the VoxZip
  *               digest's decayed-eviction equation)
  *   2. smooth   Spectral Score Smoothing (article section 2.2):
@@ -66,7 +67,18 @@ typedef struct {
   int32_t window;    /* w, most recent positions always kept, >= 0      [32] */
   double base_ratio; /* r = floor(base_ratio * kbar), 0 <= . <= 1      [0.5] */
   int32_t budget_pool; /* which heads share one budget pool (a kvc_pool)  [0] */
+  int32_t score_pool;  /* pooling of step 1 over query heads (kvc_score) [0] */
 } kvc_params;
+
+/* Pooling of step 1 over the KV head's G query heads.  AudioKV's article
+ * (section 1.2) does not say how the group's attention rows are combined:
+ *   KVC_SCORE_MEAN  s = mean over all G*W window queries (per head mean,
+ *                   then mean over heads)
+ *   KVC_SCORE_MAX   s = max over the G heads of each head's mean over its
+ *                   W window queries (a strongly attending head is not
+ *                   averaged away, as in C3's max over a group's query
+ *                   heads); needs n_window_q a multiple of 32. */
+typedef enum { KVC_SCORE_MEAN = 0, KVC_SCORE_MAX = 1 } kvc_score;
 
 /* Budget pool of step 3.  AudioKV's section 3.1 indexes the audio score by
  * layer and head without saying whether the score-proportional share is

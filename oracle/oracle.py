@@ -87,6 +87,16 @@ def scores(q, k) -> np.ndarray:
     return s
 
 
+def scores_maxpool(q, k, W: int) -> np.ndarray:
+    """Max over query heads of each head's mean softmax row: q [G*W, d]
+    holds the heads' W window queries head after head; each head's row is
+    the mean-pooled score of its own W queries (kvo_scores on them)."""
+    q = np.asarray(q, dtype=np.float64)
+    G = q.shape[0] // W
+    assert G * W == q.shape[0]
+    return np.max(np.stack([scores(q[g * W:(g + 1) * W], k) for g in range(G)]), axis=0)
+
+
 def dft(s) -> np.ndarray:
     s = np.ascontiguousarray(s, dtype=np.float64)
     L = s.shape[0]
@@ -140,15 +150,17 @@ def gather(x, kept) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Whole-problem driver
 # --------------------------------------------------------------------------
-def unit_compress(qu, ku, dtype: str, b: int, alpha: float, rho: float, window: int):
+def unit_compress(qu, ku, dtype: str, b: int, alpha: float, rho: float, window: int,
+                  score_pool: int = 0):
     """One (sequence, layer, KV head) unit: scores -> SSS -> top-k.
 
     qu: [G, W, d] stored window queries of the KV head's group; ku: [L, d].
+    score_pool 1 takes the max over the G heads of the head means.
     Returns dict(s, s_hat, kstar, energy, kept).
     """
     q = widen(qu, dtype).reshape(-1, np.asarray(qu).shape[-1])
     k = widen(ku, dtype)
-    s = scores(q, k)
+    s = scores_maxpool(q, k, np.asarray(qu).shape[1]) if score_pool == 1 else scores(q, k)
     s_hat, ks, E, _ = sss(s, alpha, rho)
     kept = select(s_hat, window, b)
     return dict(s=s, s_hat=s_hat, kstar=ks, energy=E, kept=kept)
@@ -213,7 +225,8 @@ def compress(prob, units=None, n_threads=None):
         i, l, h = key
         qu, ku, vu = unit_inputs(prob, i, l, h)
         u = unit_index(cfg, i, l, h)
-        r = unit_compress(qu, ku, cfg.dtype, int(b[u]), cfg.alpha, cfg.rho, cfg.window)
+        r = unit_compress(qu, ku, cfg.dtype, int(b[u]), cfg.alpha, cfg.rho, cfg.window,
+                          cfg.score_pool)
         r["k_out"] = gather(ku, r["kept"])
         r["v_out"] = gather(vu, r["kept"])
         r["idx"] = r["kept"]

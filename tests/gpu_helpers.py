@@ -57,7 +57,7 @@ class Dev:
         self.spec = api.Spec.for_tensors(self.k, self.v, gqa=cfg.gqa, seq_lens=hdr.lengths,
                                          retention=hdr.retention, n_window=cfg.n_window)
         self.params = api.Params(cfg.alpha, cfg.rho, cfg.window, cfg.base_ratio,
-                                 cfg.budget_pool)
+                                 cfg.budget_pool, cfg.score_pool)
         self.rows, self.ws_bytes = api.kvc_plan(self.spec, self.params)
 
     def units(self):
@@ -128,7 +128,7 @@ class Dev:
                          seq_lens=self.hdr.lengths, retention=self.hdr.retention,
                          alpha=self.cfg.alpha, rho=self.cfg.rho, window=self.cfg.window,
                          base_ratio=self.cfg.base_ratio, budget_pool=self.cfg.budget_pool,
-                         out=out)
+                         score_pool=self.cfg.score_pool, out=out)
         torch.cuda.synchronize()
         return o
 

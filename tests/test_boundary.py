@@ -93,6 +93,8 @@ def test_invalid_problems_rejected_before_launch():
     assert status(spec(), api.Params(base_ratio=-0.1)) == C.KVC_ERR_INVALID_ARG
     assert status(spec(), api.Params(window=-1)) == C.KVC_ERR_INVALID_ARG
     assert status(spec(), api.Params(budget_pool=2)) == C.KVC_ERR_INVALID_ARG
+    assert status(spec(), api.Params(score_pool=2)) == C.KVC_ERR_INVALID_ARG
+    assert status(spec(gqa=16, n_window=16), api.Params(score_pool=1)) == C.KVC_ERR_UNSUPPORTED
     assert status(spec(), q=None) == C.KVC_ERR_INVALID_ARG
     assert status(spec(), ko=ctypes.c_void_p((1 << 20) + 8)) == C.KVC_ERR_INVALID_ARG
     assert status(spec(), ws=ctypes.c_void_p((1 << 20) + 64)) == C.KVC_ERR_INVALID_ARG

@@ -234,7 +234,10 @@ def _check_scores(D, units):
     for (i, l, h) in units:
         qu, ku, _ = O.unit_inputs(D.prob, i, l, h)
         q = O.widen(qu, D.dtype).reshape(-1, D.cfg.head_dim)
-        ref = O.scores(q, O.widen(ku, D.dtype))
+        if D.cfg.score_pool == 1:
+            ref = O.scores_maxpool(q, O.widen(ku, D.dtype), D.cfg.n_window)
+        else:
+            ref = O.scores(q, O.widen(ku, D.dtype))
         err = rel_err(D.row(s, i, l, h), ref)
         worst = max(worst, err)
         assert err <= TOL[D.dtype], ((i, l, h), err)
@@ -277,6 +280,17 @@ def test_scores_two_pass_entry_points(dtype):
         assert rel_err(D.row(s2, i, l, h), ref) <= TOL[D.dtype]
 
 
+@pytest.mark.parametrize("dtype,d,gqa,W", [("bf16", 128, 8, 32), ("bf16", 64, 7, 32),
+                                           ("bf16", 128, 1, 32), ("bf16", 128, 2, 64),
+                                           ("f32", 64, 2, 32), ("f32", 128, 2, 64)])
+def test_scores_maxpool(dtype, d, gqa, W):
+    say(f"[scores] max over heads {dtype} d={d} G={gqa} W={W}")
+    cfg = small(dtype=dtype, head_dim=d, gqa=gqa, n_window=W, n_seq=2, lengths=(2048, 128),
+                retention=(0.5, 0.9), base_ratio=0.0, score_pool=1)
+    D = Dev(synth.problem(cfg))
+    _check_scores(D, D.units())
+
+
 def test_scores_no_sink_variant():
     say("[scores] qwen7b-shaped, no sink")
     cfg = dataclasses.replace(synth.CONFIGS["qwen7b"], n_layers=2, sink_beta=0.0)
@@ -300,7 +314,8 @@ def _check_e2e(D, units):
     for (i, l, h) in units:
         u = D.uindex(i, l, h)
         qu, ku, vu = O.unit_inputs(D.prob, i, l, h)
-        r = O.unit_compress(qu, ku, D.dtype, int(b[u]), D.cfg.alpha, D.cfg.rho, D.cfg.window)
+        r = O.unit_compress(qu, ku, D.dtype, int(b[u]), D.cfg.alpha, D.cfg.rho, D.cfg.window,
+                            D.cfg.score_pool)
         got = idx[off[u]:off[u + 1]]
         ndiff += check_kept_sets(got, r["kept"], r["s_hat"], int(b[u]), D.cfg.window, D.dtype)
         kon = ko[off[u]:off[u + 1]]
@@ -347,6 +362,12 @@ def test_compress_omni30b_sampled():
 def test_compress_qwen7b_layer_pool_sampled():
     say("[e2e] qwen7b, one budget pool per layer")
     D = dev("qwen7b", budget_pool=1)
+    _check_e2e(D, [(0, 0, 0), (0, 13, 2), (0, 27, 3)])
+
+
+def test_compress_qwen7b_maxpool_sampled():
+    say("[e2e] qwen7b, max over query heads")
+    D = dev("qwen7b", score_pool=1)
     _check_e2e(D, [(0, 0, 0), (0, 13, 2), (0, 27, 3)])
 
 

@@ -83,3 +83,38 @@ def test_large_logits_do_not_overflow():
     assert np.all(np.isfinite(s))
     assert s[3] == pytest.approx(1.0, abs=1e-300)
     assert s.sum() == pytest.approx(1.0)
+
+
+# ---------------------------------------------------------------------------
+# Max pooling over query heads (the alternative reading of how a GQA group's
+# attention rows are combined; C3 takes a max over a group's query heads)
+# ---------------------------------------------------------------------------
+def test_maxpool_two_heads_logistic_closed_form():
+    # Head 0's queries are all x e_0, head 1's all y e_0; two keys e_0 and 0.
+    # Each head's mean row is its single softmax row: (expit(x/sqrt d),
+    # expit(-x/sqrt d)); the max over heads takes each key's larger one.
+    from scipy.special import expit
+    d, W = 16, 3
+    for x, y in [(2.0, -1.0), (0.5, 7.0), (-3.0, -3.0)]:
+        q = np.zeros((2 * W, d))
+        q[:W, 0] = x
+        q[W:, 0] = y
+        k = np.zeros((2, d)); k[0, 0] = 1.0
+        s = O.scores_maxpool(q, k, W)
+        a = expit(np.array([x, y]) / math.sqrt(d))
+        assert s[0] == pytest.approx(a.max(), rel=1e-13)
+        assert s[1] == pytest.approx((1 - a).max(), rel=1e-13)
+
+
+def test_maxpool_one_head_is_the_mean_and_dominates_the_mean():
+    r = np.random.default_rng(8)
+    q, k = r.standard_normal((32, 16)), r.standard_normal((50, 16))
+    assert np.array_equal(O.scores_maxpool(q, k, 32), O.scores(q, k))
+    q = r.standard_normal((4 * 8, 16))
+    smax, smean = O.scores_maxpool(q, k, 8), O.scores(q, k)
+    assert (smax >= smean - 1e-15).all()
+    # heads in any order, queries within a head in any order
+    perm = np.concatenate([np.arange(8) + 8 * h for h in (2, 0, 3, 1)])
+    assert np.allclose(O.scores_maxpool(q[perm], k, 8), smax, atol=1e-15)
+    perm = np.concatenate([r.permutation(8) + 8 * h for h in range(4)])
+    assert np.allclose(O.scores_maxpool(q[perm], k, 8), smax, atol=1e-15)
