@@ -26,6 +26,8 @@
 // registers), widened to fp64 and contracted with v_mfma_f64_16x16x4f64,
 // which keeps the logits exact to ~1e-15 so the 1e-5 fp32 tolerance is met
 // with margin.
+#include <type_traits>
+
 #include "kvc_internal.h"
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -665,6 +667,15 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
   }
 }
 
+// Statistics pass.  Fast path: each lane takes its reference maximum per
+// query block from the tile's first 32 keys (one extra MFMA block) and sums
+// exp2(l*c - m*c) over the whole tile with that fixed reference: no running
+// maximum, no rescaling, the same VALU work per key as the pooling pass.
+// Terms below the reference by more than the fp32 range underflow, which
+// loses nothing next to the reference term itself (>= 1).  A sum can only go
+// wrong by overflowing, when a later key's logit exceeds the reference by
+// more than about 127 / c; the workgroup then recomputes the tile with the
+// exact online maximum.
 template <int D, int NBC>
 __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_score_stats_qs_kernel(
     KvcDesc Dsc, int tile0, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -672,6 +683,7 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
   using C = QsCfg<D>;
   constexpr int NT = QsWaves<NBC>::NT, NK = C::NK;
   __shared__ __attribute__((aligned(16))) char sK[2][C::CHUNK * C::RS];
+  __shared__ int sRedo;
   const int tile = tile0 + xcd_local_tile((int)blockIdx.x, (int)gridDim.x);
   const TileInfo ti = tile_info(Dsc, tile);
   const int gw = NBC * 32;
@@ -686,15 +698,12 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
   bf16x8 qf0[NK], qf1[NK];
   qs_qfrag<D>(qf0, qg, 2 * wave, gw, lane);
   qs_qfrag<D>(qf1, qg, two ? 2 * wave + 1 : 2 * wave, gw, lane);
-  float m0 = -INFINITY, z0 = 0.f, m1 = -INFINITY, z1 = 0.f;
   auto mma = [&](floatx16& acc, const bf16x8 (&kf)[NK], const bf16x8 (&qf)[NK]) {
     acc = floatx16{};
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], acc, 0, 0, 0);
   };
-  // Online (max, sum of exp2) over the lane's 16 keys of one block, with
-  // pairwise max and sum trees (no serial dependency chains).
-  auto stat = [&](const floatx16& acc, float& m, float& z) {
+  auto bmax = [&](const floatx16& acc) {
     float t[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) t[i] = fmaxf(acc[i], acc[i + 8]);
@@ -702,8 +711,9 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
     for (int w = 4; w >= 1; w >>= 1)
 #pragma unroll
       for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
-    const float mn = fmaxf(m, t[0]);
-    const float nmc = -mn * c;
+    return t[0];
+  };
+  auto esum = [&](const floatx16& acc, float nmc) {
     float e[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c, nmc));
@@ -711,43 +721,83 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
     for (int w = 8; w >= 1; w >>= 1)
 #pragma unroll
       for (int i = 0; i < w; ++i) e[i] = e[i] + e[i + w];
-    z = z * __builtin_amdgcn_exp2f((m - mn) * c) + e[0];   // m = -inf: exp2(-inf) = 0
-    m = mn;
+    return e[0];
   };
 
   const int nch = ti.keys / C::CHUNK;
-  qs_u32x4 kr[(C::PIECES + NT - 1) / NT];
-  qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0);
-  qs_kstore<D, NT>(kr, sK[0]);
-  __syncthreads();
-  floatx16 X, Y;
-  bf16x8 kf0[NK], kf1[NK];
-  qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0 + min(1, nch - 1) * C::CHUNK);
-  qs_kfrag<D>(kf0, sK[0], 0, lane);
-  mma(X, kf0, qf0);
-  for (int ch = 0;;) {
-    const char* buf = sK[ch & 1];
-    qs_kfrag<D>(kf1, buf, 1, lane);
-    mma(Y, kf0, qf1);
-    stat(X, m0, z0);
-    QS_INTERLEAVE(7);
-    mma(X, kf1, qf0);
-    stat(Y, m1, z1);
-    QS_INTERLEAVE(7);
-    mma(Y, kf1, qf1);
-    stat(X, m0, z0);
-    QS_INTERLEAVE(7);
-    qs_kstore<D, NT>(kr, sK[(ch + 1) & 1]);
+  float m0, z0, m1, z1;
+  // One pass over the tile through the LDS pipeline.  EXACT: online maximum
+  // (rescaling z when it grows); otherwise the fixed references m0, m1.
+  auto run = [&](auto exact_tag) {
+    constexpr bool EXACT = decltype(exact_tag)::value;
+    float n0 = -m0 * c, n1 = -m1 * c;
+    auto stat = [&](const floatx16& acc, float& m, float& z, float& nmc) {
+      if constexpr (EXACT) {
+        const float mn = fmaxf(m, bmax(acc));
+        const float nn = -mn * c;
+        z = z * __builtin_amdgcn_exp2f((m - mn) * c) + esum(acc, nn);  // m = -inf: adds to 0
+        m = mn;
+        nmc = nn;
+      } else {
+        z += esum(acc, nmc);
+      }
+    };
+    qs_u32x4 kr[(C::PIECES + NT - 1) / NT];
+    qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0);
+    qs_kstore<D, NT>(kr, sK[0]);
     __syncthreads();
-    if (++ch == nch) break;
-    qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0 + min(ch + 1, nch - 1) * C::CHUNK);
-    qs_kfrag<D>(kf0, sK[ch & 1], 0, lane);
-    const floatx16 Yp = Y;
+    floatx16 X, Y;
+    bf16x8 kf0[NK], kf1[NK];
+    qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0 + min(1, nch - 1) * C::CHUNK);
+    qs_kfrag<D>(kf0, sK[0], 0, lane);
+    if constexpr (!EXACT) {
+      // references from the tile's first 32 keys
+      floatx16 R;
+      mma(R, kf0, qf0);
+      m0 = bmax(R);
+      mma(R, kf0, qf1);
+      m1 = bmax(R);
+      n0 = -m0 * c;
+      n1 = -m1 * c;
+    }
     mma(X, kf0, qf0);
-    stat(Yp, m1, z1);
-    QS_INTERLEAVE(7);
+    for (int ch = 0;;) {
+      const char* buf = sK[ch & 1];
+      qs_kfrag<D>(kf1, buf, 1, lane);
+      mma(Y, kf0, qf1);
+      stat(X, m0, z0, n0);
+      QS_INTERLEAVE(7);
+      mma(X, kf1, qf0);
+      stat(Y, m1, z1, n1);
+      QS_INTERLEAVE(7);
+      mma(Y, kf1, qf1);
+      stat(X, m0, z0, n0);
+      QS_INTERLEAVE(7);
+      qs_kstore<D, NT>(kr, sK[(ch + 1) & 1]);
+      __syncthreads();
+      if (++ch == nch) break;
+      qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0 + min(ch + 1, nch - 1) * C::CHUNK);
+      qs_kfrag<D>(kf0, sK[ch & 1], 0, lane);
+      const floatx16 Yp = Y;
+      mma(X, kf0, qf0);
+      stat(Yp, m1, z1, n1);
+      QS_INTERLEAVE(7);
+    }
+    stat(Y, m1, z1, n1);
+  };
+
+  z0 = z1 = 0.f;
+  if (threadIdx.x == 0) sRedo = 0;
+  run(std::integral_constant<bool, false>{});
+  // An overflowed sum in any wave sends the whole workgroup (its barriers
+  // must match) through the exact pass.
+  if (!(z0 < INFINITY) || !(z1 < INFINITY)) sRedo = 1;
+  __syncthreads();
+  if (sRedo) {
+    m0 = m1 = -INFINITY;
+    z0 = z1 = 0.f;
+    run(std::integral_constant<bool, true>{});
   }
-  stat(Y, m1, z1);
   // The other lane half holds the other 16 keys of each 32-key block.
   {
     float m2 = __shfl_xor(m0, 32), z2 = __shfl_xor(z0, 32);

@@ -368,7 +368,8 @@ def main():
 
         t_hbm = ab["pool"] / (HBM_PEAK_GBS * 1e9)
         t_mfma = ab["score_flops"] / (MFMA_PEAK_TFLOPS[cfg.dtype] * 1e12)
-        pool_kernel = f"kvc_score_pool_kernel<{cfg.dtype}, d={cfg.head_dim}, GW={cfg.gqa * cfg.n_window}>"
+        pool_kernel = (f"kvc_score_pool_qs_kernel<d={cfg.head_dim}, blocks={cfg.gqa * cfg.n_window // 32}>"
+                       if cfg.dtype == "bf16" else "kvc_score_pool_kernel<TF64>")
         if t_hbm >= t_mfma:
             roof = hbm("score_pool", pool_kernel, ab["pool"], stages["score_pool"], "score.hip")
         else:
@@ -376,10 +377,11 @@ def main():
             roof = {"bound": "mfma", "kernel": pool_kernel, "achieved": round(tf, 2),
                     "peak": MFMA_PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s",
                     "frac": round(tf / MFMA_PEAK_TFLOPS[cfg.dtype], 4),
-                    "traffic": committed_traffic("score.hip", "kvc_score_pool_kernel", cfg.name)}
+                    "traffic": committed_traffic("score.hip", pool_kernel.split("<")[0], cfg.name)}
         roof["mfma_frac"] = round(ab["score_flops"] / (stages["score_pool"] * 1e-3) / 1e12
                                   / MFMA_PEAK_TFLOPS[cfg.dtype], 4)
-        others["score_stats"] = hbm("score_stats", "kvc_score_stats_kernel", ab["stats"],
+        others["score_stats"] = hbm("score_stats", "kvc_score_stats_qs_kernel" if cfg.dtype == "bf16"
+                                    else "kvc_score_stats_kernel", ab["stats"],
                                     stages["score_stats"], "score.hip")
         others["gather"] = hbm("gather", "kvc_gather_kernel<256>", ab["gather"], stages["gather"],
                                "gather.hip")

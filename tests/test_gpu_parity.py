@@ -291,6 +291,30 @@ def test_scores_maxpool(dtype, d, gqa, W):
     _check_scores(D, D.units())
 
 
+@pytest.mark.parametrize("case", ["late_spike", "early_spike"])
+def test_scores_reference_overflow_and_underflow(case):
+    # The bf16 statistics pass sums exp2 against a reference taken from each
+    # tile's first 32 keys.  late_spike: a key far past them whose logit
+    # exceeds the reference by far more than the fp32 exponent range (the
+    # pass must fall back to the exact online maximum); early_spike: the
+    # first keys dominate and every later term underflows against them.
+    say(f"[scores] reference {case}")
+    cfg = small(dtype="bf16", head_dim=128, gqa=8, n_seq=1, lengths=(2048,), retention=(0.5,),
+                base_ratio=0.0, n_layers=1, n_kv_heads=1)
+    prob = synth.problem(cfg)
+    qm = synth.bf16_bits_to_f32(prob.q[0, 0].reshape(-1, 128)).mean(axis=0)
+    k = synth.bf16_bits_to_f32(prob.k[0, 0]).copy()
+    if case == "late_spike":
+        k[:64] = 0.0
+        k[1500] = 8.0 * qm / np.linalg.norm(qm) * 40.0
+    else:
+        k[:32] = 8.0 * qm / np.linalg.norm(qm) * 40.0
+        k[32:] *= 0.05
+    prob.k[0, 0] = synth.f32_to_bf16_bits(k)
+    D = Dev(prob)
+    _check_scores(D, D.units())
+
+
 def test_scores_no_sink_variant():
     say("[scores] qwen7b-shaped, no sink")
     cfg = dataclasses.replace(synth.CONFIGS["qwen7b"], n_layers=2, sink_beta=0.0)
