@@ -1,0 +1,345 @@
+"""Pins of the C3 retrieval oracle (oracle/c3.py): closed forms, invariants,
+library routines, independent exact arithmetic and brute force.
+
+C3 digest page: content clustering (recursive bisecting k-means per layer
+and KV head, 8 iterations, seed 0, initial granularity 16, node sizes down
+to 4), shared competition (max over a group's query heads of the cosine
+with a node centroid; whole nodes fill the budget), adaptive resolution
+(EMA equation, R paired split/merge exchanges, inheritance rules)."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from audio_kv_cache_amd import synth
+from oracle import c3 as C3
+
+M64 = (1 << 64) - 1
+
+
+def bf16(x):
+    return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(np.asarray(x, np.float32))).astype(np.float64)
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# SplitMix64 and the initial pair
+# ---------------------------------------------------------------------------
+def inv_splitmix64(y):
+    """Inverse of SplitMix64's output function, built from the inverses of
+    its steps (xor-shift inverse, multiplicative inverse mod 2^64)."""
+    def unxorshift(z, k):
+        x = z
+        for _ in range(64 // k + 1):
+            x = z ^ (x >> k)
+        return x & M64
+    z = unxorshift(y, 31)
+    z = (z * pow(0x94D049BB133111EB, -1, 1 << 64)) & M64
+    z = unxorshift(z, 27)
+    z = (z * pow(0xBF58476D1CE4E5B9, -1, 1 << 64)) & M64
+    z = unxorshift(z, 30)
+    return (z - 0x9E3779B97F4A7C15) & M64
+
+
+def test_splitmix64_is_a_bijection_with_the_published_constants():
+    r = rng(0)
+    for x in [0, 1, M64] + [int(v) for v in r.integers(0, 2**63, 200)]:
+        assert inv_splitmix64(C3.splitmix64(x)) == x
+    assert len({C3.splitmix64(x) for x in range(5000)}) == 5000
+
+
+def test_splitmix64_first_outputs_of_the_zero_seeded_stream():
+    # The generator's stream from state 0 is x_i = i * gamma; its first
+    # output for seed 0 is the widely quoted 0xE220A8397B1DCDAF.
+    assert C3.splitmix64(0) == 0xE220A8397B1DCDAF
+
+
+def test_init_pair_distinct_and_in_range():
+    for size in (5, 6, 17, 1000, 1 << 17):
+        for start in range(0, 40, 3):
+            a0, a1 = C3.init_pair(0, 3, 2, start, size)
+            assert 0 <= a0 < size and 0 <= a1 < size and a0 != a1
+
+
+# ---------------------------------------------------------------------------
+# decision helpers
+# ---------------------------------------------------------------------------
+def test_quantize_moves_only_tiny_keys():
+    k = bf16(np.array([1.0, -3.5, 2.0 ** -17, 2.0 ** -20 * 1.5, -(2.0 ** -26), 4064.0]))
+    q = C3.quantize(k)
+    assert q[0] == 1.0 and q[1] == -3.5 and q[2] == 2.0 ** -17 and q[5] == 4064.0
+    assert q[3] == 2.0 ** -20 * 1.5                 # still a grid point
+    assert q[4] == 0.0                               # below half a grid step
+
+
+def test_round16_keeps_16_significant_bits():
+    x = np.array([1.0 + 2.0 ** -15, 1.0 + 2.0 ** -16, 1.0 + 3 * 2.0 ** -16, 1.0 + 2.0 ** -17 + 2.0 ** -23],
+                 dtype=np.float32)
+    r = C3.round16(x)
+    assert r[0] == np.float32(1.0 + 2.0 ** -15)     # representable
+    assert r[1] == np.float32(1.0)                   # tie to even
+    assert r[2] == np.float32(1.0 + 2.0 ** -14)     # tie to even (up)
+    assert r[3] == np.float32(1.0)                   # below half
+    mant = r.view(np.uint32) & 0xFF
+    assert (mant == 0).all()
+
+
+def test_to_bf16_rounding():
+    x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20, -2.5])
+    assert C3.to_bf16(x).tolist() == [1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7, -2.5]
+
+
+def test_assignment_is_the_nearest_centroid_rule():
+    # Against exact distances (fractions) away from the fp32 rounding band.
+    r = rng(1)
+    d = 16
+    mu0, mu1 = r.standard_normal(d), r.standard_normal(d)
+    X = bf16(r.standard_normal((400, d)) * 1.5)
+    w, b = C3.bisector(mu0[None], mu1[None])
+    to1 = C3.assign(X.astype(np.float32), np.repeat(w, 400, 0), np.repeat(b, 400, 0))
+    d0 = ((X - mu0) ** 2).sum(1)
+    d1 = ((X - mu1) ** 2).sum(1)
+    clear = np.abs(d0 - d1) > 1e-3 * (d0 + d1)
+    assert clear.sum() > 350
+    assert np.array_equal(to1[clear], (d1 < d0)[clear])
+
+
+def test_key_on_the_bisector_joins_cluster_0():
+    mu0 = np.array([[-1.0, 0.0, 0.0, 0.0]])
+    mu1 = np.array([[1.0, 0.0, 0.0, 0.0]])
+    w, b = C3.bisector(mu0, mu1)
+    X = np.array([[0.0, 5.0, -2.0, 1.0], [2.0 ** -10, 0, 0, 0], [-(2.0 ** -10), 0, 0, 0]], np.float32)
+    assert C3.assign(X, np.repeat(w, 3, 0), np.repeat(b, 3, 0)).tolist() == [False, True, False]
+
+
+# ---------------------------------------------------------------------------
+# tree
+# ---------------------------------------------------------------------------
+def members(t, x):
+    return t.perm[t.start[x]:t.start[x] + t.size[x]]
+
+
+def test_tree_invariants_and_exact_centroids():
+    r = rng(2)
+    K = bf16(r.standard_normal((700, 16)))
+    t = C3.build_tree(K, cache=5)
+    n = K.shape[0]
+    assert sorted(t.perm.tolist()) == list(range(n))
+    assert t.start[0] == 0 and t.size[0] == n and t.depth[0] == 0 and t.parent[0] == -1
+    for x in range(t.n_nodes):
+        mem = members(t, x)
+        if t.left[x] < 0:                            # a leaf keeps position order
+            assert (np.diff(mem) > 0).all()
+        # exact mean via rational arithmetic, then fp32 and bf16 rounding
+        for c in range(0, 16, 5):
+            exact = sum(Fraction(float(v)) for v in K[mem, c]) / len(mem)
+            want = C3.to_bf16(np.array([float(exact)]))[0]
+            assert t.centroid[x, c] == want
+        l = t.left[x]
+        if l >= 0:
+            assert t.parent[l] == x and t.parent[l + 1] == x
+            assert t.start[l] == t.start[x] and t.start[l + 1] == t.start[x] + t.size[l]
+            assert t.size[l] + t.size[l + 1] == t.size[x] and t.size[l] > 0 and t.size[l + 1] > 0
+            assert t.depth[l] == t.depth[x] + 1
+        else:
+            assert t.size[x] <= C3.LEAF or t.depth[x] == C3.MAX_DEPTH or t.size[x] > 0
+    # breadth-first numbering: depth, then start, increase with the id
+    key = t.depth * (n + 1) + t.start
+    assert (np.diff(key) > 0).all()
+    # every node above the leaves that has more than LEAF keys was tried;
+    # with continuous random keys no split is abandoned
+    assert ((t.left >= 0) | (t.size <= C3.LEAF)).all()
+
+
+def test_one_dimensional_groups_split_the_same_from_any_start():
+    # keys 0,1,2 and 10,11 on one axis: 2-means from any two distinct
+    # members ends at {0,1,2} | {10,11} within a few iterations.
+    K = np.zeros((5, 8))
+    K[:, 0] = [10, 0, 11, 2, 1]
+    for cache in range(12):
+        t = C3.build_tree(K, cache=cache)
+        l = t.left[0]
+        got = {frozenset(members(t, l).tolist()), frozenset(members(t, l + 1).tolist())}
+        assert got == {frozenset({1, 3, 4}), frozenset({0, 2})}
+        cents = sorted([t.centroid[l, 0], t.centroid[l + 1, 0]])
+        assert cents == [1.0, 10.5]
+
+
+def test_tight_groups_are_never_cut():
+    # 8 tight groups of 6 keys at +-20 e0 +-5 e1 +-1 e2: whichever local
+    # optimum 2-means reaches from its initial pair, no split cuts through a
+    # group (the spread inside a group is far below the gaps), so every node
+    # down to depth 3 is a union of whole groups and depth 3 holds one group
+    # per node.
+    r = rng(3)
+    signs = np.array([[a, b, c] for a in (-1, 1) for b in (-1, 1) for c in (-1, 1)], float)
+    pts, lab = [], []
+    for gi, s in enumerate(signs):
+        for _ in range(6):
+            v = np.zeros(8)
+            v[:3] = s * [20, 5, 1]
+            v += r.standard_normal(8) * 0.01
+            pts.append(v)
+            lab.append(gi)
+    order = r.permutation(len(pts))
+    K = bf16(np.array(pts)[order])
+    lab = np.array(lab)[order]
+    for cache in range(4):
+        t = C3.build_tree(K, cache=cache)
+        for x in np.nonzero(t.depth <= 3)[0]:
+            g = lab[members(t, x)]
+            assert all((g == v).sum() == 6 for v in set(g.tolist()))
+        d3 = np.nonzero(t.depth == 3)[0]
+        assert len(d3) == 8 and all(len(set(lab[members(t, x)].tolist())) == 1 for x in d3)
+
+
+def test_identical_keys_never_split_and_small_caches():
+    K = np.tile(bf16(np.arange(8.0)), (50, 1))
+    t = C3.build_tree(K)
+    assert t.n_nodes == 1 and t.left[0] == -1
+    t = C3.build_tree(bf16(rng(4).standard_normal((4, 8))))
+    assert t.n_nodes == 1
+    t = C3.build_tree(np.zeros((0, 8)))
+    assert t.n_nodes == 0
+    t = C3.build_tree(bf16(rng(4).standard_normal((5, 8))))
+    assert t.n_nodes == 3 and sorted(t.size.tolist()) == sorted([5] + t.size[1:].tolist())
+
+
+def test_key_range_is_checked():
+    with pytest.raises(ValueError):
+        C3.build_tree(np.full((6, 4), 4096.0))
+    with pytest.raises(ValueError):
+        C3.build_tree(np.array([[np.nan, 0, 0, 0]] * 6))
+
+
+# ---------------------------------------------------------------------------
+# frontier and step
+# ---------------------------------------------------------------------------
+def test_frontier_depth_is_rounded_log2():
+    assert [C3.frontier_depth(n) for n in (0, 1, 11, 12, 16, 22, 23, 32, 45, 46, 32768)] == \
+           [0, 0, 0, 0, 0, 0, 1, 1, 1, 2, 11]
+
+
+def partition_of(t, F, n):
+    cover = np.concatenate([members(t, x) for x in F]) if len(F) else np.zeros(0, np.int64)
+    return sorted(cover.tolist()) == list(range(n))
+
+
+def test_initial_frontier_tiles_the_member_order():
+    r = rng(5)
+    n = 4096
+    t = C3.build_tree(bf16(r.standard_normal((n, 16))))
+    F = C3.initial_frontier(t, n)
+    assert partition_of(t, F, n)
+    st = t.start[F]
+    assert st[0] == 0 and (st[1:] == st[:-1] + t.size[F][:-1]).all()
+    # depth 8 = log2(4096 / 16); shallower entries are leaves (unbalanced
+    # splits reach size <= 4 early)
+    assert len(F) <= 256 and (t.depth[F] <= 8).all()
+    assert ((t.depth[F] == 8) | (t.left[F] < 0)).all()
+    assert (t.depth == 8).sum() + ((t.left < 0) & (t.depth < 8)).sum() == len(F)
+
+
+def test_scores_are_max_cosine_and_zero_norm_safe():
+    r = rng(6)
+    t = C3.build_tree(bf16(r.standard_normal((300, 32))))
+    F = C3.initial_frontier(t, 300)
+    q = bf16(r.standard_normal((4, 32)))
+    sig = C3.node_scores(t, F, q)
+    for i, x in enumerate(F):
+        c = t.centroid[x].astype(np.float64)
+        cos = [float(np.dot(qq, c) / (np.linalg.norm(qq) * np.linalg.norm(c))) for qq in q]
+        assert sig[i] == pytest.approx(max(cos), rel=1e-12)
+    q[0] = 0
+    assert np.isfinite(C3.node_scores(t, F, q)).all()
+
+
+def brute_retrieve(t, F, sig, B):
+    # positions ranked by (sigma of their node desc, node start, position)
+    # positions ranked by (sigma of their node desc, node start, place in
+    # the node's member list)
+    rows = []
+    for i, x in enumerate(F):
+        for j, p in enumerate(members(t, x)):
+            rows.append((-sig[i], t.start[x], j, p))
+    rows.sort()
+    return sorted(r[3] for r in rows[:B])
+
+
+def test_retrieve_against_brute_force_ranking():
+    r = rng(7)
+    t = C3.build_tree(bf16(r.standard_normal((200, 8))))
+    F = C3.initial_frontier(t, 200)
+    sig = C3.node_scores(t, F, r.standard_normal((2, 8)))
+    for B in (1, 7, 16, 50, 199):
+        kept = C3.retrieve(t, F, sig, 200, B)
+        assert kept.tolist() == brute_retrieve(t, F, sig, B)
+    assert C3.retrieve(t, F, sig, 200, 200).tolist() == list(range(200))
+    # equal scores: the earlier node (by start) goes first
+    flat = np.zeros(len(F))
+    assert C3.retrieve(t, F, flat, 200, 30).tolist() == brute_retrieve(t, F, flat, 30)
+
+
+def test_update_ema_split_merge_rules():
+    r = rng(8)
+    n = 1024
+    t = C3.build_tree(bf16(r.standard_normal((n, 16))))
+    F = C3.initial_frontier(t, n)
+    e = np.zeros(len(F))
+    A0 = len(F)
+    for _ in range(8):
+        sig = C3.node_scores(t, F, r.standard_normal((3, 16)))
+        F2, e2 = C3.update_frontier(t, F, e, sig, 0.5, 2)
+        ema = 0.5 * e + 0.5 * sig
+        assert len(F2) == A0 and partition_of(t, F2, n)
+        assert (np.diff(t.start[F2]) > 0).all()
+        old = {int(x): ema[i] for i, x in enumerate(F)}
+        new = {int(x): e2[i] for i, x in enumerate(F2)}
+        stay = set(old) & set(new)
+        assert all(new[x] == old[x] for x in stay)
+        born = set(new) - set(old)
+        gone = set(old) - set(new)
+        split = [x for x in gone if t.left[x] in born]
+        merged = [x for x in born if t.left[x] in gone]
+        assert len(split) == len(merged) <= 2
+        for x in split:
+            l = t.left[x]
+            assert new[l] == new[l + 1] == old[x]
+            # highest EMA among the nodes that could split
+            assert old[x] >= max(v for y, v in old.items() if t.left[y] >= 0 and y not in split) \
+                or len(split) == 2
+        for p in merged:
+            l = t.left[p]
+            assert new[p] == max(old[l], old[l + 1])
+        F, e = F2, e2
+
+
+def test_update_hand_case():
+    # Root with two children, each with two children: frontier = the four
+    # grandchildren.  R = 1: the grandchild with the highest EMA among those
+    # with children splits; the sibling pair with the lowest max merges.
+    K = np.zeros((40, 4))
+    K[:, 0] = np.repeat([-30, -10, 10, 30], 10) + np.tile(np.arange(10) * 0.25, 4)
+    t = C3.build_tree(bf16(K))
+    F = np.nonzero(t.depth == 2)[0]
+    F = F[np.argsort(t.start[F])]
+    assert len(F) == 4 and (t.left[F] >= 0).all()
+    sig = np.array([0.1, 0.2, 0.9, 0.3])
+    F2, e2 = C3.update_frontier(t, F, np.zeros(4), sig, 0.5, 1)
+    # entry 2 (e = 0.45) splits; pairs: (0,1) max 0.1, (2,3) excluded (2 splits)
+    assert F2.tolist() == [t.parent[F[0]], t.left[F[2]], t.left[F[2]] + 1, F[3]]
+    assert e2.tolist() == [0.1, 0.45, 0.45, 0.15]
+
+
+def test_step_bypass_when_the_cache_fits():
+    r = rng(9)
+    t = C3.build_tree(bf16(r.standard_normal((64, 8))))
+    F = C3.initial_frontier(t, 64)
+    e = np.zeros(len(F))
+    out = C3.step(t, F, e, r.standard_normal((2, 8)), 64, 64)
+    assert out["kept"].tolist() == list(range(64))
+    assert np.array_equal(out["F"], F) and np.array_equal(out["e"], e)
