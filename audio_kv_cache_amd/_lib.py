@@ -30,6 +30,9 @@ EXPORTS = ("kvc_plan", "kvc_compress", "kvc_compress_layers", "kvc_scores", "kvc
 # include/kvc_voxzip.h
 VZ_EXPORTS = ("kvc_vz_plan", "kvc_vz_step", "kvc_vz_accumulate", "kvc_vz_evict",
               "kvc_vz_gather")
+# include/kvc_c3.h
+C3_EXPORTS = ("kvc_c3_plan", "kvc_c3_build", "kvc_c3_step", "kvc_c3_score", "kvc_c3_select",
+              "kvc_c3_update", "kvc_c3_gather")
 
 
 KVC_POOL_SEQUENCE = 0
@@ -67,6 +70,30 @@ class kvc_vz_problem(ctypes.Structure):
                 ("len", ctypes.POINTER(ctypes.c_int64)),
                 ("budget", ctypes.POINTER(ctypes.c_int64)),
                 ("k_stride", ctypes.c_int64 * 2), ("v_stride", ctypes.c_int64 * 2)]
+
+
+class kvc_c3_params(ctypes.Structure):
+    _fields_ = [("lam", ctypes.c_double), ("r_swaps", ctypes.c_int32),
+                ("seed", ctypes.c_uint64)]
+
+
+class kvc_c3_problem(ctypes.Structure):
+    _fields_ = [("n_seq", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("gqa_group", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int64),
+                ("len", ctypes.POINTER(ctypes.c_int64)),
+                ("budget", ctypes.POINTER(ctypes.c_int64)),
+                ("k_stride", ctypes.c_int64 * 2), ("v_stride", ctypes.c_int64 * 2),
+                ("out_stride", ctypes.c_int64 * 2)]
+
+
+class kvc_c3_layout(ctypes.Structure):
+    _fields_ = [("node_cap", ctypes.c_int64), ("kept_cap", ctypes.c_int64),
+                ("index_bytes", ctypes.c_size_t), ("state_bytes", ctypes.c_size_t),
+                ("build_workspace_bytes", ctypes.c_size_t),
+                ("step_workspace_bytes", ctypes.c_size_t)] + \
+        [(f, ctypes.c_size_t) for f in ("start", "size", "left", "parent", "depth", "perm",
+                                          "n_nodes", "centroid", "count", "frontier", "ema")]
 
 
 class KvcError(RuntimeError):
@@ -118,6 +145,17 @@ def lib():
             L.kvc_vz_evict.argtypes = [vp, vq, _vp, _vp, _vp]
             L.kvc_vz_gather.argtypes = [vp, vq, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
             for name in VZ_EXPORTS:
+                getattr(L, name).restype = ctypes.c_int
+            cp, cq = _P(kvc_c3_problem), _P(kvc_c3_params)
+            L.kvc_c3_plan.argtypes = [cp, cq, _P(kvc_c3_layout)]
+            L.kvc_c3_build.argtypes = [cp, cq, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+            L.kvc_c3_step.argtypes = [cp, cq, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      ctypes.c_size_t, _vp]
+            L.kvc_c3_score.argtypes = [cp, cq, _vp, _vp, _vp, _vp, _vp]
+            L.kvc_c3_select.argtypes = [cp, cq, _vp, _vp, _vp, _vp, _vp]
+            L.kvc_c3_update.argtypes = [cp, cq, _vp, _vp, _vp, _vp, _vp]
+            L.kvc_c3_gather.argtypes = [cp, cq, _vp, _vp, _vp, _vp, _vp, _vp]
+            for name in C3_EXPORTS:
                 getattr(L, name).restype = ctypes.c_int
             L.kvc_status_str.argtypes = [ctypes.c_int]
             L.kvc_status_str.restype = ctypes.c_char_p

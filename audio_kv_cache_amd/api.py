@@ -307,3 +307,153 @@ def kvc_vz_gather(spec, params, k, v, a, idx, k_out, v_out, a_out, stream=None):
     C.check(C.lib().kvc_vz_gather(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(k),
                                   _ptr(v), _ptr(a), _ptr(idx), _ptr(k_out), _ptr(v_out),
                                   _ptr(a_out), _stream(stream)), "kvc_vz_gather")
+
+
+# ---------------------------------------------------------------------------
+# Query-guided retrieval (include/kvc_c3.h)
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class C3Params:
+    lam: float = 0.5
+    r_swaps: int = 2
+    seed: int = 0
+
+    def c(self) -> C.kvc_c3_params:
+        return C.kvc_c3_params(float(self.lam), int(self.r_swaps), int(self.seed))
+
+
+class C3Spec:
+    """Host-side kvc_c3_problem: bf16 key/value caches [units][capacity][head_dim]
+    (or any strides with head_dim contiguous), per-sequence audio lengths n and
+    budgets B, output rows [units][out_rows][head_dim]."""
+
+    def __init__(self, *, n_layers, n_kv_heads, gqa, head_dim, lens, budgets, capacity,
+                 k_stride=None, v_stride=None, out_stride=None):
+        self.n_layers, self.n_kv_heads, self.gqa = int(n_layers), int(n_kv_heads), int(gqa)
+        self.head_dim, self.capacity = int(head_dim), int(capacity)
+        self._len = np.ascontiguousarray(np.asarray(lens, dtype=np.int64).reshape(-1))
+        self.n_seq = int(self._len.shape[0])
+        self._budget = np.ascontiguousarray(np.broadcast_to(
+            np.asarray(budgets, dtype=np.int64), (self.n_seq,)).copy())
+        dense = (self.capacity * self.head_dim, self.head_dim)
+        self.k_stride = tuple(int(x) for x in (k_stride or dense))
+        self.v_stride = tuple(int(x) for x in (v_stride or dense))
+        self.out_rows = int(max(1, np.minimum(self._len, self._budget).max()))
+        self.out_stride = tuple(int(x) for x in (out_stride or
+                                                  (self.out_rows * self.head_dim, self.head_dim)))
+
+    @property
+    def n_units(self) -> int:
+        return self.n_seq * self.n_layers * self.n_kv_heads
+
+    @property
+    def lens(self) -> np.ndarray:
+        return self._len
+
+    @property
+    def budgets(self) -> np.ndarray:
+        return self._budget
+
+    def c(self) -> C.kvc_c3_problem:
+        p = C.kvc_c3_problem()
+        p.n_seq, p.n_layers, p.n_kv_heads = self.n_seq, self.n_layers, self.n_kv_heads
+        p.gqa_group, p.head_dim, p.capacity = self.gqa, self.head_dim, self.capacity
+        p.len = self._len.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        p.budget = self._budget.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        for a in range(2):
+            p.k_stride[a] = self.k_stride[a]
+            p.v_stride[a] = self.v_stride[a]
+            p.out_stride[a] = self.out_stride[a]
+        return p
+
+
+def kvc_c3_plan(spec: C3Spec, params: C3Params) -> C.kvc_c3_layout:
+    lay = C.kvc_c3_layout()
+    C.check(C.lib().kvc_c3_plan(ctypes.byref(spec.c()), ctypes.byref(params.c()),
+                                ctypes.byref(lay)), "kvc_c3_plan")
+    return lay
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def kvc_c3_build(spec, params, k, index, state, workspace, stream=None):
+    C.check(C.lib().kvc_c3_build(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(k),
+                                 _ptr(index), _ptr(state), _ptr(workspace), _nbytes(workspace),
+                                 _stream(stream)), "kvc_c3_build")
+
+
+def kvc_c3_step(spec, params, index, state_in, state_out, q, k, v, k_out, v_out, idx_out,
+                workspace, stream=None):
+    C.check(C.lib().kvc_c3_step(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(index),
+                                _ptr(state_in), _ptr(state_out), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(k_out), _ptr(v_out), _ptr(idx_out), _ptr(workspace),
+                                _nbytes(workspace), _stream(stream)), "kvc_c3_step")
+
+
+def kvc_c3_score(spec, params, index, state, q, sigma, stream=None):
+    C.check(C.lib().kvc_c3_score(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(index),
+                                 _ptr(state), _ptr(q), _ptr(sigma), _stream(stream)),
+            "kvc_c3_score")
+
+
+def kvc_c3_select(spec, params, index, state, sigma, idx_out, stream=None):
+    C.check(C.lib().kvc_c3_select(ctypes.byref(spec.c()), ctypes.byref(params.c()),
+                                  _ptr(index), _ptr(state), _ptr(sigma), _ptr(idx_out),
+                                  _stream(stream)), "kvc_c3_select")
+
+
+def kvc_c3_update(spec, params, index, state_in, sigma, state_out, stream=None):
+    C.check(C.lib().kvc_c3_update(ctypes.byref(spec.c()), ctypes.byref(params.c()),
+                                  _ptr(index), _ptr(state_in), _ptr(sigma), _ptr(state_out),
+                                  _stream(stream)), "kvc_c3_update")
+
+
+def kvc_c3_gather(spec, params, k, v, idx, k_out, v_out, stream=None):
+    C.check(C.lib().kvc_c3_gather(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(k),
+                                  _ptr(v), _ptr(idx), _ptr(k_out), _ptr(v_out),
+                                  _stream(stream)), "kvc_c3_gather")
+
+
+class C3Views:
+    """torch views of an index and a state buffer (uint8 device tensors) by
+    the layout's offsets."""
+
+    def __init__(self, spec: C3Spec, lay, index, state):
+        U, NC, CAP, D = spec.n_units, int(lay.node_cap), spec.capacity, spec.head_dim
+
+        def view(buf, off, count, dtype, shape):
+            esz = torch.empty((), dtype=dtype).element_size()
+            return buf[off:off + count * esz].view(dtype).view(*shape)
+        self.start = view(index, lay.start, U * NC, torch.int32, (U, NC))
+        self.size = view(index, lay.size, U * NC, torch.int32, (U, NC))
+        self.left = view(index, lay.left, U * NC, torch.int32, (U, NC))
+        self.parent = view(index, lay.parent, U * NC, torch.int32, (U, NC))
+        self.depth = view(index, lay.depth, U * NC, torch.int32, (U, NC))
+        self.perm = view(index, lay.perm, U * CAP, torch.int32, (U, CAP))
+        self.n_nodes = view(index, lay.n_nodes, U, torch.int32, (U,))
+        self.centroid = view(index, lay.centroid, U * NC * D, torch.int16, (U, NC, D))
+        self.count = view(state, lay.count, U, torch.int32, (U,))
+        self.frontier = view(state, lay.frontier, U * CAP, torch.int32, (U, CAP))
+        self.ema = view(state, lay.ema, U * CAP, torch.float64, (U, CAP))
+
+
+def c3_allocate(spec: C3Spec, params: C3Params, device):
+    """Index, two states, workspaces and outputs for a C3 problem."""
+    lay = kvc_c3_plan(spec, params)
+    U, R, D = spec.n_units, spec.out_rows, spec.head_dim
+
+    def buf(n):
+        return torch.empty((max(int(n), 256),), dtype=torch.uint8, device=device)
+    return dict(
+        layout=lay,
+        index=buf(lay.index_bytes),
+        state=[buf(lay.state_bytes), buf(lay.state_bytes)],
+        build_ws=buf(lay.build_workspace_bytes),
+        step_ws=buf(lay.step_workspace_bytes),
+        k_out=torch.empty((U, R, D), dtype=torch.bfloat16, device=device),
+        v_out=torch.empty((U, R, D), dtype=torch.bfloat16, device=device),
+        idx=torch.empty((U, int(lay.kept_cap)), dtype=torch.int32, device=device),
+        sigma=torch.empty((U, spec.capacity), dtype=torch.float32, device=device),
+    )

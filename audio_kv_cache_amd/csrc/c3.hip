@@ -1,0 +1,1485 @@
+// c3.hip -- C3 query-guided retrieval of audio KV (kvc_c3.h).
+//
+// C3 digest page ("C3: Speech-Guided KV Retrieval for Long-Context
+// SpeechLLM Inference"): at prefill every (layer, KV head) cache gets a
+// binary tree of key clusters from recursive bisecting 2-means (8 Lloyd
+// iterations per split, seed 0); a decode step scores the active frontier of
+// the tree by the best cosine over the group's query heads, fills the budget
+// with the members of the best nodes, and moves resolution with an EMA of
+// the scores and paired split/merge exchanges.
+//
+// Build, level synchronous over every cache at once (one tree depth per
+// round; the host waits once per depth for two counts):
+//   local   nodes of 5..96 keys, each owned by the 128-position chunk that
+//           holds its first member: the workgroup stages the members' keys
+//           in LDS once and runs all 8 Lloyd iterations there -- a thread
+//           per key for the fp32 hyperplane test, a wave per node for the
+//           exact fp64 member sums (64 lanes over the columns, keys in
+//           order) -- then partitions the node's perm range in place.
+//   span    nodes over 96 keys: per iteration one launch over 128-key
+//           blocks of every such node (hyperplane test, exact block sums
+//           added with fp64 atomics, exact in any order) and one launch per
+//           node for the new means; then a stable partition per node.
+//   ids     one workgroup per cache: breadth-first ids of the new children
+//           (a scan over the depth's nodes), their records and centroids,
+//           and the next depth's local heads and span list.
+// Every sum that feeds a split is exact (keys on the 2^-24 grid, |k| < 4096,
+// n <= 2^17: partial sums stay multiples of 2^-24 below 2^29), so the
+// reduction order on the GPU cannot change a decision; the fp32 hyperplane
+// test uses a fixed column order and exact products.
+//
+// Step: score (workgroups over the frontier entries, thread per entry),
+// select + update (one 1024-lane workgroup per cache: weighted radix select
+// of the best nodes, a position bitmap in LDS listed ascending, then the EMA
+// and R masked max/min reductions for the exchanges), gather.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/kvc_c3.h"
+#include "kvc_internal.h"
+
+// Separate roundings wherever the code writes a product and a sum; the one
+// fused multiply-add used (the hyperplane test) is written out and exact.
+#pragma clang fp contract(off)
+
+#define C3_MAX_SEQ 64
+#define C3_MAX_CAP 131072
+#define C3_MAX_G 32
+#define C3_LEAF 4
+#define C3_ITERS 8
+#define C3_MAXD 24
+#define C3_CH 128                          // positions per local chunk
+#define C3_MLOC 96                         // largest node split in one workgroup
+#define C3_ROWS (C3_CH + C3_MLOC - 1)      // keys a local workgroup can hold
+#define C3_HEADS (C3_CH / (C3_LEAF + 1) + 1)
+#define C3_T 256
+#define C3_BIG 1024
+#define C3_SW 8                            // score workgroups per cache
+
+struct C3Desc {
+  int32_t n_seq, upseq, gqa, d, n_units, R;
+  int32_t cap, ncap, nchunk, kept_cap;
+  double lam;
+  uint64_t seed;
+  int64_t ks[2], vs[2], os[2];
+  int32_t len[C3_MAX_SEQ], budget[C3_MAX_SEQ];
+};
+
+struct C3Index {
+  int32_t *start, *size, *left, *parent, *depth, *perm, *nn;
+  uint16_t* cent;
+};
+
+struct C3State {
+  int32_t* count;
+  int32_t* fr;
+  double* e;
+};
+
+struct C3Work {
+  uint16_t* cres;    // [U][cap][d]: child centroids, at each child's start
+  int32_t* res_n0;   // [U][cap]: split result at each node's start (n0, or -1)
+  uint8_t* flags;    // [U][cap]: cluster of each position (span nodes)
+  int32_t* head;     // [U][cap]: local node starting here at this depth, or -1
+  int32_t* ptmp;     // [U][cap]
+  int32_t* lvl;      // [U][C3_MAXD + 2]: first id of each depth
+  double* rsum;      // [U][d]
+  int2* snode;       // [2][smax]: (cache, node) of each span slot
+  float* sw;         // [smax][d]
+  float* sb;         // [smax]
+  double* s0;        // [smax][d]
+  double* s1;        // [smax][d]
+  int32_t* sn1;      // [smax]
+  int32_t* salive;   // [smax]
+  int32_t* cnt;      // [C3_MAXD + 1][4]: candidates, span nodes, largest span node
+  int32_t* err;      // [1]
+  int32_t smax;
+};
+
+// ---------------------------------------------------------------------------
+// Arithmetic of the split decisions
+// ---------------------------------------------------------------------------
+__device__ inline float c3_bf(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ inline uint16_t c3_to_bf16(double x) {
+  const uint32_t b = __float_as_uint((float)x);
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+// Snap a bf16 key to the grid 2^-24 (only |k| < 2^-17 moves) and flag keys
+// outside the supported range (|k| >= 4096, inf, nan).
+__device__ inline uint32_t c3_snap(uint32_t h, int& bad) {
+  const uint32_t e = (h >> 7) & 0xFFu;
+  if (e >= 127u + 12u) {
+    bad = 1;
+    return h;
+  }
+  if (e >= 110u) return h;
+  const float y = rintf(__uint_as_float(h << 16) * 0x1p24f) * 0x1p-24f;
+  return __float_as_uint(y) >> 16;
+}
+
+__device__ inline uint4 c3_snap8(uint4 v, int& bad) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = c3_snap(w[i] & 0xFFFFu, bad) | (c3_snap(w[i] >> 16, bad) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ inline float c3_round16(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return __uint_as_float((b + 0x7Fu + ((b >> 8) & 1u)) & 0xFFFFFF00u);
+}
+
+// Hyperplane between two fp64 means for the CPL columns of this lane (lane l
+// owns columns CPL*l ..); returns b on every lane.  b is the pairwise sum of
+// the products: adjacent columns first, then adjacent pairs, and so on,
+// which is the lane order of an xor butterfly.
+template <int CPL>
+__device__ inline float c3_bisect(const double* mu0, const double* mu1, float* w) {
+  float p[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    float wf = c3_round16((float)(mu1[i] - mu0[i]));
+    if (fabsf(wf) < 0x1p-100f) wf = 0.0f;
+    const float mf = (float)(0.5 * (mu0[i] + mu1[i]));
+    w[i] = wf;
+    p[i] = wf * mf;
+  }
+  float s = p[0];
+  if constexpr (CPL == 2) s = p[0] + p[1];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) s = s + __shfl_xor(s, o);
+  return s;
+}
+
+// The CPL column values of this lane in a key row staged in LDS.
+template <int CPL>
+__device__ inline void c3_row_vals(const unsigned char* row, int lane, double* v) {
+  if constexpr (CPL == 2) {
+    const uint32_t h = *reinterpret_cast<const uint32_t*>(row + lane * 4);
+    v[0] = (double)c3_bf(h & 0xFFFFu);
+    v[CPL - 1] = (double)c3_bf(h >> 16);
+  } else {
+    const uint32_t h = *reinterpret_cast<const uint16_t*>(row + lane * 2);
+    v[0] = (double)c3_bf(h);
+  }
+}
+
+// s(k) = sum_c k_c w_c in fp32, column order; every product is exact.
+template <int D>
+__device__ inline float c3_plane(const unsigned char* row, const float* w) {
+  const uint4* kr = reinterpret_cast<const uint4*>(row);
+  const float4* wr = reinterpret_cast<const float4*>(w);
+  float s = 0.0f;
+#pragma unroll
+  for (int c8 = 0; c8 < D / 8; ++c8) {
+    const uint4 kk = kr[c8];
+    const float4 w0 = wr[2 * c8], w1 = wr[2 * c8 + 1];
+    s = fmaf(c3_bf(kk.x & 0xFFFFu), w0.x, s);
+    s = fmaf(c3_bf(kk.x >> 16), w0.y, s);
+    s = fmaf(c3_bf(kk.y & 0xFFFFu), w0.z, s);
+    s = fmaf(c3_bf(kk.y >> 16), w0.w, s);
+    s = fmaf(c3_bf(kk.z & 0xFFFFu), w1.x, s);
+    s = fmaf(c3_bf(kk.z >> 16), w1.y, s);
+    s = fmaf(c3_bf(kk.w & 0xFFFFu), w1.z, s);
+    s = fmaf(c3_bf(kk.w >> 16), w1.w, s);
+  }
+  return s;
+}
+
+__device__ inline uint64_t c3_mix(uint64_t x) {
+  uint64_t z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Two distinct members (indices into the node's range) for the initial means.
+__device__ inline void c3_init_pair(uint64_t seed, int u, int dep, int start, int size, int* a0,
+                                    int* a1) {
+  const uint64_t h0 = c3_mix(seed ^ ((uint64_t)u << 40) ^ ((uint64_t)dep << 32) ^ (uint64_t)start);
+  const uint64_t h1 = c3_mix(h0);
+  const uint64_t x0 = h0 % (uint64_t)size;
+  *a0 = (int)x0;
+  *a1 = (int)((x0 + 1 + h1 % (uint64_t)(size - 1)) % (uint64_t)size);
+}
+
+__device__ inline int c3_n(const C3Desc& P, int u) { return P.len[u / P.upseq]; }
+__device__ inline int c3_b(const C3Desc& P, int u) { return P.budget[u / P.upseq]; }
+
+// Exclusive prefix sum of v over the workgroup in thread order, and the
+// total.  `scratch` holds one value per wave.  Two barriers.
+template <int NT>
+__device__ inline int c3_block_scan(int v, int* scratch, int* total) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int c = scratch[w];
+    off += w < wave ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + incl - v;
+}
+
+// ---------------------------------------------------------------------------
+// Build: roots
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(C3_T) void c3_init_kernel(C3Desc P, C3Index X, C3Work W) {
+  const int u = blockIdx.x, n = c3_n(P, u);
+  const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
+  for (int p = threadIdx.x; p < n; p += C3_T) {
+    X.perm[ub + p] = p;
+    W.head[ub + p] = -1;
+  }
+  for (int c = threadIdx.x; c < P.d; c += C3_T) W.rsum[(size_t)u * P.d + c] = 0.0;
+  if (threadIdx.x == 0) {
+    X.nn[u] = n > 0 ? 1 : 0;
+    int32_t* lv = W.lvl + (size_t)u * (C3_MAXD + 2);
+    lv[0] = 0;
+    lv[1] = n > 0 ? 1 : 0;
+    if (n > 0) {
+      X.start[nb] = 0;
+      X.size[nb] = n;
+      X.left[nb] = -1;
+      X.parent[nb] = -1;
+      X.depth[nb] = 0;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && n > C3_LEAF) {
+    if (n <= C3_MLOC) {
+      W.head[ub] = 0;
+    } else {
+      const int s = atomicAdd(&W.cnt[1], 1);
+      W.snode[s] = make_int2(u, 0);
+    }
+  }
+}
+
+// Exact fp64 column sums of every cache's keys (the root's mean).
+template <int D>
+__global__ __launch_bounds__(C3_T) void c3_root_sum_kernel(C3Desc P, C3Work W,
+                                                           const uint16_t* __restrict__ k) {
+  constexpr int CPL = D / 64;
+  const int u = blockIdx.x / P.nchunk, chn = blockIdx.x - u * P.nchunk;
+  const int n = c3_n(P, u), base = chn * C3_CH;
+  if (base >= n) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rows = min(C3_CH, n - base);
+  double acc[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) acc[i] = 0.0;
+  int bad = 0;
+  for (int r = wave; r < rows; r += C3_T / 64) {
+    const uint16_t* row = k + u * P.ks[0] + (int64_t)(base + r) * P.ks[1];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) acc[i] += (double)c3_bf(c3_snap(row[lane * CPL + i], bad));
+  }
+  __shared__ double red[C3_T / 64][D];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) red[wave][lane * CPL + i] = acc[i];
+  if (bad) atomicOr(W.err, 1);
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += C3_T) {
+    double s = 0.0;
+    for (int w = 0; w < C3_T / 64; ++w) s += red[w][c];
+    atomicAdd(&W.rsum[(size_t)u * D + c], s);
+  }
+}
+
+__global__ __launch_bounds__(C3_T) void c3_root_fin_kernel(C3Desc P, C3Index X, C3Work W) {
+  const int u = blockIdx.x, n = c3_n(P, u);
+  if (n == 0) return;
+  for (int c = threadIdx.x; c < P.d; c += C3_T)
+    X.cent[(size_t)u * P.ncap * P.d + c] = c3_to_bf16(W.rsum[(size_t)u * P.d + c] / (double)n);
+}
+
+// ---------------------------------------------------------------------------
+// Build: nodes of 5..96 keys, all 8 iterations in one workgroup
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Index X, C3Work W,
+                                                        const uint16_t* __restrict__ k) {
+  constexpr int RB = 2 * D + 16;          // padded LDS row: conflict-free row-per-lane reads
+  constexpr int CPL = D / 64;
+  constexpr int PPR = D / 8;              // 16-byte pieces per key row
+  __shared__ __align__(16) unsigned char sK[C3_ROWS * RB];
+  __shared__ __align__(16) float sW[C3_HEADS][D + 4];
+  __shared__ float sB[C3_HEADS];
+  __shared__ int sStart[C3_HEADS], sSize[C3_HEADS], sNode[C3_HEADS], sA0[C3_HEADS],
+      sA1[C3_HEADS], sDead[C3_HEADS], sN0[C3_HEADS];
+  __shared__ int sIsHead[C3_CH];
+  __shared__ int sPerm[C3_ROWS];
+  __shared__ signed char sRowNode[C3_ROWS];
+  __shared__ unsigned char sFlag[C3_ROWS];
+  __shared__ int sNh;
+
+  const int u = blockIdx.x / P.nchunk, chn = blockIdx.x - u * P.nchunk;
+  const int n = c3_n(P, u), base = chn * C3_CH;
+  if (base >= n) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
+
+  if (tid < C3_CH) sIsHead[tid] = (base + tid < n) ? W.head[ub + base + tid] : -1;
+  __syncthreads();
+  if (tid == 0) {
+    int nh = 0;
+    for (int t = 0; t < C3_CH; ++t) {
+      const int x = sIsHead[t];
+      if (x < 0) continue;
+      sNode[nh] = x;
+      sStart[nh] = base + t;
+      sSize[nh] = X.size[nb + x];
+      ++nh;
+    }
+    sNh = nh;
+  }
+  __syncthreads();
+  const int nh = sNh;
+  if (nh == 0) return;
+  const int row0 = sStart[0];
+  const int rows = sStart[nh - 1] + sSize[nh - 1] - row0;
+  if (tid < nh) {
+    int a0, a1;
+    c3_init_pair(P.seed, u, dep, sStart[tid], sSize[tid], &a0, &a1);
+    sA0[tid] = a0;
+    sA1[tid] = a1;
+    sDead[tid] = 0;
+  }
+  for (int r = tid; r < rows; r += C3_T) {
+    int j = -1;
+    for (int h = 0; h < nh; ++h)
+      if (r >= sStart[h] - row0 && r < sStart[h] - row0 + sSize[h]) j = h;
+    sRowNode[r] = (signed char)j;
+    sPerm[r] = j >= 0 ? X.perm[ub + row0 + r] : 0;
+  }
+  __syncthreads();
+  int bad = 0;
+  for (int i = tid; i < rows * PPR; i += C3_T) {
+    const int r = i / PPR, pc = i - r * PPR;
+    if (sRowNode[r] < 0) continue;
+    const uint16_t* src = k + u * P.ks[0] + (int64_t)sPerm[r] * P.ks[1] + pc * 8;
+    *reinterpret_cast<uint4*>(sK + r * RB + pc * 16) =
+        c3_snap8(*reinterpret_cast<const uint4*>(src), bad);
+  }
+  if (bad) atomicOr(W.err, 1);
+  __syncthreads();
+
+  // Initial hyperplanes from the two chosen members.
+  for (int j = wave; j < nh; j += C3_T / 64) {
+    const int r0 = sStart[j] - row0;
+    double m0[CPL], m1[CPL];
+    float w[CPL];
+    c3_row_vals<CPL>(sK + (r0 + sA0[j]) * RB, lane, m0);
+    c3_row_vals<CPL>(sK + (r0 + sA1[j]) * RB, lane, m1);
+    const float b = c3_bisect<CPL>(m0, m1, w);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) sW[j][lane * CPL + i] = w[i];
+    if (lane == 0) sB[j] = b;
+  }
+  __syncthreads();
+
+  for (int it = 0; it < C3_ITERS; ++it) {
+    for (int r = tid; r < rows; r += C3_T) {
+      const int j = sRowNode[r];
+      if (j >= 0 && !sDead[j]) sFlag[r] = c3_plane<D>(sK + r * RB, &sW[j][0]) > sB[j] ? 1 : 0;
+    }
+    __syncthreads();
+    for (int j = wave; j < nh; j += C3_T / 64) {
+      if (sDead[j]) continue;
+      const int r0 = sStart[j] - row0, m = sSize[j];
+      double a0[CPL], a1[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) a0[i] = a1[i] = 0.0;
+      int n1 = 0;
+      for (int r = r0; r < r0 + m; ++r) {
+        double v[CPL];
+        c3_row_vals<CPL>(sK + r * RB, lane, v);
+        if (__builtin_amdgcn_readfirstlane(sFlag[r])) {
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) a1[i] += v[i];
+          ++n1;
+        } else {
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) a0[i] += v[i];
+        }
+      }
+      if (n1 == 0 || n1 == m) {
+        if (lane == 0) {
+          sDead[j] = 1;
+          W.res_n0[ub + sStart[j]] = -1;
+        }
+        continue;
+      }
+      double mu0[CPL], mu1[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        mu0[i] = a0[i] / (double)(m - n1);
+        mu1[i] = a1[i] / (double)n1;
+      }
+      if (it + 1 < C3_ITERS) {
+        float w[CPL];
+        const float b = c3_bisect<CPL>(mu0, mu1, w);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) sW[j][lane * CPL + i] = w[i];
+        if (lane == 0) sB[j] = b;
+      } else {
+        const int n0 = m - n1;
+        uint16_t* c0 = W.cres + (ub + sStart[j]) * D;
+        uint16_t* c1 = W.cres + (ub + sStart[j] + n0) * D;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          c0[lane * CPL + i] = c3_to_bf16(mu0[i]);
+          c1[lane * CPL + i] = c3_to_bf16(mu1[i]);
+        }
+        if (lane == 0) {
+          sN0[j] = n0;
+          W.res_n0[ub + sStart[j]] = n0;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // Stable partition of each split node's range, in place (this workgroup
+  // alone reads and writes the positions of the nodes it owns).
+  for (int r = tid; r < rows; r += C3_T) {
+    const int j = sRowNode[r];
+    if (j < 0 || sDead[j]) continue;
+    const int f = sFlag[r];
+    const int r0 = sStart[j] - row0;
+    int rank = 0;
+    for (int q = r0; q < r; ++q) rank += sFlag[q] == f;
+    const int np = sStart[j] + (f ? sN0[j] + rank : rank);
+    X.perm[ub + np] = sPerm[r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Build: nodes over 96 keys, one launch per iteration
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void c3_span_init_kernel(C3Desc P, int dep, int par, C3Index X,
+                                                          C3Work W, const uint16_t* __restrict__ k) {
+  constexpr int CPL = D / 64;
+  const int s = blockIdx.x, lane = threadIdx.x;
+  const int2 un = W.snode[par * W.smax + s];
+  const int u = un.x, x = un.y;
+  const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
+  const int st = X.start[nb + x], m = X.size[nb + x];
+  int a0, a1;
+  c3_init_pair(P.seed, u, dep, st, m, &a0, &a1);
+  const uint16_t* r0 = k + u * P.ks[0] + (int64_t)X.perm[ub + st + a0] * P.ks[1];
+  const uint16_t* r1 = k + u * P.ks[0] + (int64_t)X.perm[ub + st + a1] * P.ks[1];
+  double m0[CPL], m1[CPL];
+  float w[CPL];
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    m0[i] = (double)c3_bf(c3_snap(r0[lane * CPL + i], bad));
+    m1[i] = (double)c3_bf(c3_snap(r1[lane * CPL + i], bad));
+  }
+  const float b = c3_bisect<CPL>(m0, m1, w);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    W.sw[(size_t)s * D + lane * CPL + i] = w[i];
+    W.s0[(size_t)s * D + lane * CPL + i] = 0.0;
+    W.s1[(size_t)s * D + lane * CPL + i] = 0.0;
+  }
+  if (lane == 0) {
+    W.sb[s] = b;
+    W.sn1[s] = 0;
+    W.salive[s] = 1;
+  }
+}
+
+// One 128-key block of one span node: hyperplane test, block sums, atomics.
+template <int D>
+__global__ __launch_bounds__(C3_T) void c3_span_iter_kernel(C3Desc P, int par, C3Index X,
+                                                            C3Work W, const uint16_t* __restrict__ k) {
+  constexpr int RB = 2 * D + 16, CPL = D / 64, PPR = D / 8;
+  __shared__ __align__(16) unsigned char sK[C3_CH * RB];
+  __shared__ __align__(16) float sWv[D + 4];
+  __shared__ unsigned char sFlag[C3_CH];
+  __shared__ double red0[C3_T / 64][D], red1[C3_T / 64][D];
+  __shared__ int sN1[C3_T / 64];
+  const int s = blockIdx.x;
+  if (!W.salive[s]) return;
+  const int2 un = W.snode[par * W.smax + s];
+  const int u = un.x, x = un.y;
+  const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
+  const int st = X.start[nb + x], m = X.size[nb + x];
+  const int p0 = st + blockIdx.y * C3_CH;
+  if (p0 >= st + m) return;
+  const int rows = min(C3_CH, st + m - p0);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int c = tid; c < D; c += C3_T) sWv[c] = W.sw[(size_t)s * D + c];
+  const float b = W.sb[s];
+  int bad = 0;
+  for (int i = tid; i < rows * PPR; i += C3_T) {
+    const int r = i / PPR, pc = i - r * PPR;
+    const uint16_t* src = k + u * P.ks[0] + (int64_t)X.perm[ub + p0 + r] * P.ks[1] + pc * 8;
+    *reinterpret_cast<uint4*>(sK + r * RB + pc * 16) =
+        c3_snap8(*reinterpret_cast<const uint4*>(src), bad);
+  }
+  if (bad) atomicOr(W.err, 1);
+  __syncthreads();
+  if (tid < rows) {
+    const unsigned char f = c3_plane<D>(sK + tid * RB, sWv) > b ? 1 : 0;
+    sFlag[tid] = f;
+    W.flags[ub + p0 + tid] = f;
+  }
+  __syncthreads();
+  double a0[CPL], a1[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) a0[i] = a1[i] = 0.0;
+  int n1 = 0;
+  const int per = (rows + C3_T / 64 - 1) / (C3_T / 64);
+  const int rb = wave * per, re = min(rows, rb + per);
+  for (int r = rb; r < re; ++r) {
+    double v[CPL];
+    c3_row_vals<CPL>(sK + r * RB, lane, v);
+    if (__builtin_amdgcn_readfirstlane(sFlag[r])) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) a1[i] += v[i];
+      ++n1;
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) a0[i] += v[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    red0[wave][lane * CPL + i] = a0[i];
+    red1[wave][lane * CPL + i] = a1[i];
+  }
+  if (lane == 0) sN1[wave] = n1;
+  __syncthreads();
+  for (int c = tid; c < D; c += C3_T) {
+    double t0 = 0.0, t1 = 0.0;
+    for (int w = 0; w < C3_T / 64; ++w) {
+      t0 += red0[w][c];
+      t1 += red1[w][c];
+    }
+    atomicAdd(&W.s0[(size_t)s * D + c], t0);
+    atomicAdd(&W.s1[(size_t)s * D + c], t1);
+  }
+  if (tid == 0) {
+    int t = 0;
+    for (int w = 0; w < C3_T / 64; ++w) t += sN1[w];
+    atomicAdd(&W.sn1[s], t);
+  }
+}
+
+// New means of a span node; the last iteration records the split.
+template <int D>
+__global__ __launch_bounds__(64) void c3_span_fin_kernel(C3Desc P, int par, int last, C3Index X,
+                                                         C3Work W) {
+  constexpr int CPL = D / 64;
+  const int s = blockIdx.x, lane = threadIdx.x;
+  if (!W.salive[s]) return;
+  const int2 un = W.snode[par * W.smax + s];
+  const int u = un.x, x = un.y;
+  const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
+  const int st = X.start[nb + x], m = X.size[nb + x];
+  const int n1 = W.sn1[s];
+  if (n1 == 0 || n1 == m) {
+    if (lane == 0) {
+      W.salive[s] = 0;
+      W.res_n0[ub + st] = -1;
+    }
+    return;
+  }
+  double mu0[CPL], mu1[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const size_t o = (size_t)s * D + lane * CPL + i;
+    mu0[i] = W.s0[o] / (double)(m - n1);
+    mu1[i] = W.s1[o] / (double)n1;
+    W.s0[o] = 0.0;
+    W.s1[o] = 0.0;
+  }
+  if (!last) {
+    float w[CPL];
+    const float b = c3_bisect<CPL>(mu0, mu1, w);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) W.sw[(size_t)s * D + lane * CPL + i] = w[i];
+    if (lane == 0) {
+      W.sb[s] = b;
+      W.sn1[s] = 0;
+    }
+  } else {
+    const int n0 = m - n1;
+    uint16_t* c0 = W.cres + (ub + st) * D;
+    uint16_t* c1 = W.cres + (ub + st + n0) * D;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      c0[lane * CPL + i] = c3_to_bf16(mu0[i]);
+      c1[lane * CPL + i] = c3_to_bf16(mu1[i]);
+    }
+    if (lane == 0) W.res_n0[ub + st] = n0;
+  }
+}
+
+// Stable partition of a split span node's perm range (through ptmp).
+__global__ __launch_bounds__(C3_BIG) void c3_span_part_kernel(C3Desc P, int par, C3Index X,
+                                                              C3Work W) {
+  __shared__ int scan[C3_BIG / 64];
+  const int s = blockIdx.x;
+  if (!W.salive[s]) return;
+  const int2 un = W.snode[par * W.smax + s];
+  const int u = un.x, x = un.y;
+  const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
+  const int st = X.start[nb + x], m = X.size[nb + x];
+  const int n0 = W.res_n0[ub + st];
+  int zeros = 0;
+  for (int b0 = 0; b0 < m; b0 += C3_BIG) {
+    const int i = b0 + threadIdx.x;
+    const bool in = i < m;
+    const int f = in ? W.flags[ub + st + i] : 0;
+    int tot;
+    const int zb = c3_block_scan<C3_BIG>(in && !f, scan, &tot) + zeros;
+    if (in) W.ptmp[ub + st + (f ? n0 + (i - zb) : zb)] = X.perm[ub + st + i];
+    zeros += tot;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < m; i += C3_BIG) X.perm[ub + st + i] = W.ptmp[ub + st + i];
+}
+
+// ---------------------------------------------------------------------------
+// Build: children ids and records, next depth's work lists
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(C3_BIG) void c3_ids_kernel(C3Desc P, int dep, C3Index X, C3Work W) {
+  __shared__ int scan[C3_BIG / 64];
+  const int u = blockIdx.x;
+  const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
+  int32_t* lv = W.lvl + (size_t)u * (C3_MAXD + 2);
+  const int lo = lv[dep], hi = lv[dep + 1];
+  int made = 0, cand = 0, big = 0;
+  int32_t* cnt = W.cnt + (dep + 1) * 4;
+  const int par = (dep + 1) & 1;
+  for (int b0 = lo; b0 < hi; b0 += C3_BIG) {
+    const int x = b0 + threadIdx.x;
+    const bool in = x < hi;
+    int st = 0, m = 0, n0 = -1;
+    if (in) {
+      st = X.start[nb + x];
+      m = X.size[nb + x];
+      if (m > C3_LEAF) n0 = W.res_n0[ub + st];
+      W.head[ub + st] = -1;
+    }
+    const bool ok = n0 > 0;
+    int tot;
+    const int rank = c3_block_scan<C3_BIG>(ok, scan, &tot);
+    if (ok) {
+      const int l = hi + 2 * (made + rank);
+      X.left[nb + x] = l;
+      const int cs[2] = {st, st + n0}, cm[2] = {n0, m - n0};
+#pragma unroll
+      for (int side = 0; side < 2; ++side) {
+        const size_t y = nb + l + side;
+        X.start[y] = cs[side];
+        X.size[y] = cm[side];
+        X.left[y] = -1;
+        X.parent[y] = x;
+        X.depth[y] = dep + 1;
+        const uint4* src = reinterpret_cast<const uint4*>(W.cres + (ub + cs[side]) * D);
+        uint4* dst = reinterpret_cast<uint4*>(X.cent + y * D);
+        for (int i = 0; i < D / 8; ++i) dst[i] = src[i];
+        if (cm[side] > C3_LEAF) {
+          ++cand;
+          if (cm[side] <= C3_MLOC) {
+            W.head[ub + cs[side]] = l + side;
+          } else {
+            big = max(big, cm[side]);
+            const int slot = atomicAdd(&cnt[1], 1);
+            W.snode[par * W.smax + slot] = make_int2(u, l + side);
+          }
+        }
+      }
+    }
+    made += tot;
+  }
+  if (cand) atomicAdd(&cnt[0], cand);
+  if (big) atomicMax(&cnt[2], big);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    lv[dep + 2] = hi + 2 * made;
+    X.nn[u] = hi + 2 * made;
+  }
+}
+
+// Initial frontier: nodes at depth round(log2(n/16)) and leaves above it,
+// listed by start; e = 0.
+__global__ __launch_bounds__(C3_BIG) void c3_frontier_kernel(C3Desc P, C3Index X, C3State S,
+                                                             C3Work W) {
+  __shared__ int scan[C3_BIG / 64];
+  const int u = blockIdx.x, n = c3_n(P, u);
+  const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
+  int d0 = 0;
+  while ((int64_t)n * n >= (int64_t(1) << (2 * d0 + 9))) ++d0;
+  for (int p = threadIdx.x; p < n; p += C3_BIG) W.ptmp[ub + p] = -1;
+  __syncthreads();
+  const int nn = X.nn[u];
+  for (int x = threadIdx.x; x < nn; x += C3_BIG) {
+    const int dp = X.depth[nb + x];
+    if (dp == d0 || (dp < d0 && X.left[nb + x] < 0)) W.ptmp[ub + X.start[nb + x]] = x;
+  }
+  __syncthreads();
+  int a = 0;
+  for (int b0 = 0; b0 < n; b0 += C3_BIG) {
+    const int p = b0 + threadIdx.x;
+    const int x = p < n ? W.ptmp[ub + p] : -1;
+    int tot;
+    const int r = c3_block_scan<C3_BIG>(x >= 0, scan, &tot) + a;
+    if (x >= 0) {
+      S.fr[ub + r] = x;
+      S.e[ub + r] = 0.0;
+    }
+    a += tot;
+  }
+  if (threadIdx.x == 0) S.count[u] = a;
+}
+
+// ---------------------------------------------------------------------------
+// Step: scores
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(C3_T) void c3_score_kernel(C3Desc P, C3Index X, C3State S,
+                                                        const uint16_t* __restrict__ q,
+                                                        float* __restrict__ sigma) {
+  __shared__ __align__(16) float sQ[C3_MAX_G][D];
+  __shared__ float sQn[C3_MAX_G];
+  const int u = blockIdx.x / C3_SW, part = blockIdx.x - u * C3_SW;
+  if (c3_n(P, u) <= c3_b(P, u)) return;
+  const int G = P.gqa, A = S.count[u];
+  const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
+  for (int i = threadIdx.x; i < G * D; i += C3_T) sQ[i / D][i % D] = c3_bf(q[(size_t)u * G * D + i]);
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float s = 0.0f;
+    for (int c = 0; c < D; ++c) s = fmaf(sQ[threadIdx.x][c], sQ[threadIdx.x][c], s);
+    sQn[threadIdx.x] = sqrtf(s);
+  }
+  __syncthreads();
+  for (int i = part * C3_T + threadIdx.x; i < A; i += C3_SW * C3_T) {
+    const int x = S.fr[ub + i];
+    const uint4* row = reinterpret_cast<const uint4*>(X.cent + (nb + x) * D);
+    float c[D];
+#pragma unroll
+    for (int p = 0; p < D / 8; ++p) {
+      const uint4 v = row[p];
+      c[8 * p + 0] = c3_bf(v.x & 0xFFFFu);
+      c[8 * p + 1] = c3_bf(v.x >> 16);
+      c[8 * p + 2] = c3_bf(v.y & 0xFFFFu);
+      c[8 * p + 3] = c3_bf(v.y >> 16);
+      c[8 * p + 4] = c3_bf(v.z & 0xFFFFu);
+      c[8 * p + 5] = c3_bf(v.z >> 16);
+      c[8 * p + 6] = c3_bf(v.w & 0xFFFFu);
+      c[8 * p + 7] = c3_bf(v.w >> 16);
+    }
+    float cn = 0.0f;
+#pragma unroll
+    for (int j = 0; j < D; ++j) cn = fmaf(c[j], c[j], cn);
+    cn = sqrtf(cn);
+    float best = -INFINITY;
+    for (int g = 0; g < G; ++g) {
+      const float4* qg = reinterpret_cast<const float4*>(&sQ[g][0]);
+      float dot = 0.0f;
+#pragma unroll
+      for (int j = 0; j < D / 4; ++j) {
+        const float4 qq = qg[j];
+        dot = fmaf(qq.x, c[4 * j], dot);
+        dot = fmaf(qq.y, c[4 * j + 1], dot);
+        dot = fmaf(qq.z, c[4 * j + 2], dot);
+        dot = fmaf(qq.w, c[4 * j + 3], dot);
+      }
+      const float den = sQn[g] * cn;
+      best = fmaxf(best, den > 0.0f ? dot / den : 0.0f);
+    }
+    sigma[ub + i] = best;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Step: selection and frontier update (one workgroup per cache)
+// ---------------------------------------------------------------------------
+// Ascending key of a score for a descending order: larger sigma first
+// (-0.0 taken as +0.0).
+__device__ inline uint32_t c3_desc_key(float x) {
+  const uint32_t b = __float_as_uint(x + 0.0f);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ~ord;
+}
+
+__device__ inline double c3_ema(const C3Desc& P, double e, float s) {
+  const double a = P.lam * e;
+  const double c = (1.0 - P.lam) * (double)s;
+  return a + c;
+}
+
+__global__ __launch_bounds__(C3_BIG) void c3_select_update_kernel(
+    C3Desc P, C3Index X, C3State Sin, const float* __restrict__ sigma, int32_t* __restrict__ idx,
+    C3State Sout, int do_sel, int do_upd) {
+  __shared__ uint32_t hist[C3_BIG / 64][256];
+  __shared__ uint32_t bm[C3_MAX_CAP / 32];
+  __shared__ int scan[C3_BIG / 64];
+  __shared__ uint32_t s_digit, s_below;
+  __shared__ double rv[C3_BIG / 64];
+  __shared__ int ri[C3_BIG / 64];
+  __shared__ int sSplit[8], sMerge[8];
+  __shared__ int sNs, sNm;
+  const int u = blockIdx.x, n = c3_n(P, u), B = c3_b(P, u);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
+  const int A = Sin.count[u];
+  const int32_t* F = Sin.fr + ub;
+  const double* E = Sin.e + ub;
+  const float* sg = sigma + ub;
+  const int32_t* NS = X.start + nb;
+  const int32_t* NZ = X.size + nb;
+  const int32_t* NL = X.left + nb;
+  const int32_t* NP = X.parent + nb;
+  if (n <= B) {
+    if (do_sel)
+      for (int t = tid; t < n; t += C3_BIG) idx[(size_t)u * P.kept_cap + t] = t;
+    if (do_upd) {
+      for (int i = tid; i < A; i += C3_BIG) {
+        Sout.fr[ub + i] = F[i];
+        Sout.e[ub + i] = E[i];
+      }
+      if (tid == 0) Sout.count[u] = A;
+    }
+    return;
+  }
+
+  if (do_sel) {
+    // Weighted radix select: the smallest key T with weight(key <= T) >= B.
+    uint32_t prefix = 0, pmask = 0, need = (uint32_t)B;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int b = lane; b < 256; b += 64) hist[wave][b] = 0;
+      __syncthreads();
+      for (int i = tid; i < A; i += C3_BIG) {
+        const uint32_t key = c3_desc_key(sg[i]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], (uint32_t)NZ[F[i]]);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t c4[4], own = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t s = 0;
+          for (int w = 0; w < C3_BIG / 64; ++w) s += hist[w][4 * lane + e];
+          c4[e] = s;
+          own += s;
+        }
+        uint32_t incl = own;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(incl, o);
+          if (lane >= o) incl += y;
+        }
+        const uint32_t excl = incl - own;
+        if (excl < need && need <= incl) {
+          uint32_t run = excl;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (run < need && need <= run + c4[e]) {
+              s_digit = (uint32_t)(4 * lane + e);
+              s_below = run;
+            }
+            run += c4[e];
+          }
+        }
+      }
+      __syncthreads();
+      prefix |= s_digit << shift;
+      pmask |= 255u << shift;
+      need -= s_below;
+      __syncthreads();
+    }
+    // Keys below T are taken whole; entries equal to T (ties) in entry order
+    // until `need` keys.  Their members go into a position bitmap.
+    const int nw = (n + 31) >> 5;
+    for (int w = tid; w < nw; w += C3_BIG) bm[w] = 0;
+    __syncthreads();
+    int tie_before = 0;
+    for (int b0 = 0; b0 < A; b0 += C3_BIG) {
+      const int i = b0 + tid;
+      const bool in = i < A;
+      const uint32_t key = in ? c3_desc_key(sg[i]) : 0xFFFFFFFFu;
+      const int x = in ? F[i] : 0;
+      const int m = in ? NZ[x] : 0;
+      const bool eq = in && key == prefix;
+      int tot;
+      const int before = c3_block_scan<C3_BIG>(eq ? m : 0, scan, &tot) + tie_before;
+      int take = 0;
+      if (in && key < prefix) take = m;
+      if (eq) take = min(m, max(0, (int)need - before));
+      if (take > 0) {
+        const int st = NS[x];
+        for (int j = 0; j < take; ++j) {
+          const int pos = X.perm[ub + st + j];
+          atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+        }
+      }
+      tie_before += tot;
+    }
+    __syncthreads();
+    int kept = 0;
+    for (int b0 = 0; b0 < nw; b0 += C3_BIG) {
+      const int w = b0 + tid;
+      const uint32_t bits = w < nw ? bm[w] : 0u;
+      int tot;
+      int r = c3_block_scan<C3_BIG>(__popc(bits), scan, &tot) + kept;
+      uint32_t v = bits;
+      while (v) {
+        const int bit = __ffs(v) - 1;
+        idx[(size_t)u * P.kept_cap + r++] = w * 32 + bit;
+        v &= v - 1;
+      }
+      kept += tot;
+    }
+  }
+
+  if (do_upd) {
+    // R masked max reductions: split candidates (nodes with children),
+    // highest e, earliest entry on ties.
+    const int R = P.R;
+    if (tid == 0) {
+      sNs = 0;
+      sNm = 0;
+    }
+    __syncthreads();
+    for (int round = 0; round < R; ++round) {
+      double bv = -INFINITY;
+      int bi = -1;
+      const int ns = sNs;
+      for (int i = tid; i < A; i += C3_BIG) {
+        if (NL[F[i]] < 0) continue;
+        bool chosen = false;
+        for (int t = 0; t < ns; ++t) chosen |= sSplit[t] == i;
+        if (chosen) continue;
+        const double e = c3_ema(P, E[i], sg[i]);
+        if (bi < 0 || e > bv || (e == bv && i < bi)) {
+          bv = e;
+          bi = i;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const double ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if (lane == 0) {
+        rv[wave] = bv;
+        ri[wave] = bi;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        double v = -INFINITY;
+        int b = -1;
+        for (int w = 0; w < C3_BIG / 64; ++w)
+          if (ri[w] >= 0 && (b < 0 || rv[w] > v || (rv[w] == v && ri[w] < b))) {
+            v = rv[w];
+            b = ri[w];
+          }
+        if (b >= 0) sSplit[sNs++] = b;
+      }
+      __syncthreads();
+    }
+    // R masked min reductions over sibling pairs (i, i + 1), neither a split
+    // candidate: lowest max(e_i, e_i+1), earliest pair on ties.
+    const int ns = sNs;
+    for (int round = 0; round < R; ++round) {
+      double bv = INFINITY;
+      int bi = -1;
+      const int nm = sNm;
+      for (int i = tid; i + 1 < A; i += C3_BIG) {
+        const int x = F[i];
+        const int p = NP[x];
+        if (p < 0 || NL[p] != x || F[i + 1] != x + 1) continue;
+        bool skip = false;
+        for (int t = 0; t < ns; ++t) skip |= sSplit[t] == i || sSplit[t] == i + 1;
+        for (int t = 0; t < nm; ++t) skip |= sMerge[t] == i;
+        if (skip) continue;
+        const double pr = fmax(c3_ema(P, E[i], sg[i]), c3_ema(P, E[i + 1], sg[i + 1]));
+        if (bi < 0 || pr < bv || (pr == bv && i < bi)) {
+          bv = pr;
+          bi = i;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const double ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (oi >= 0 && (bi < 0 || ov < bv || (ov == bv && oi < bi))) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if (lane == 0) {
+        rv[wave] = bv;
+        ri[wave] = bi;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        double v = INFINITY;
+        int b = -1;
+        for (int w = 0; w < C3_BIG / 64; ++w)
+          if (ri[w] >= 0 && (b < 0 || rv[w] < v || (rv[w] == v && ri[w] < b))) {
+            v = rv[w];
+            b = ri[w];
+          }
+        if (b >= 0) sMerge[sNm++] = b;
+      }
+      __syncthreads();
+    }
+    const int kx = min(sNs, sNm);
+    // Rewrite the frontier: a split entry emits its two children, a merged
+    // pair its parent, every other entry itself.
+    int outp = 0;
+    for (int b0 = 0; b0 < A; b0 += C3_BIG) {
+      const int i = b0 + tid;
+      int cnt = 0;
+      bool sp = false, mg = false;
+      if (i < A) {
+        for (int t = 0; t < kx; ++t) {
+          sp |= sSplit[t] == i;
+          mg |= sMerge[t] == i;
+        }
+        bool second = false;
+        for (int t = 0; t < kx; ++t) second |= sMerge[t] == i - 1;
+        cnt = sp ? 2 : (second ? 0 : 1);
+      }
+      int tot;
+      const int o = c3_block_scan<C3_BIG>(cnt, scan, &tot) + outp;
+      if (cnt > 0) {
+        const int x = F[i];
+        const double e = c3_ema(P, E[i], sg[i]);
+        if (sp) {
+          const int l = NL[x];
+          Sout.fr[ub + o] = l;
+          Sout.fr[ub + o + 1] = l + 1;
+          Sout.e[ub + o] = e;
+          Sout.e[ub + o + 1] = e;
+        } else if (mg) {
+          Sout.fr[ub + o] = NP[x];
+          Sout.e[ub + o] = fmax(e, c3_ema(P, E[i + 1], sg[i + 1]));
+        } else {
+          Sout.fr[ub + o] = x;
+          Sout.e[ub + o] = e;
+        }
+      }
+      outp += tot;
+    }
+    if (tid == 0) Sout.count[u] = outp;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Step: gather of the kept rows
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(C3_T) void c3_gather_kernel(C3Desc P, int bpc,
+                                                         const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v,
+                                                         const int32_t* __restrict__ idx,
+                                                         uint16_t* __restrict__ ko,
+                                                         uint16_t* __restrict__ vo) {
+  constexpr int PPR = D / 8;
+  constexpr int RPP = C3_T / PPR;
+  constexpr int PASSES = 4;
+  const int u = blockIdx.x / bpc;
+  const int t0 = (blockIdx.x - u * bpc) * RPP * PASSES;
+  const int n = c3_n(P, u);
+  const int nl = min(n, c3_b(P, u));
+  if (t0 >= nl) return;
+  const int pc = threadIdx.x % PPR;
+  uint4 kv[PASSES], vv[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int t = t0 + p * RPP + threadIdx.x / PPR;
+    if (t >= nl) continue;
+    int s = idx[(size_t)u * P.kept_cap + t];
+    if ((unsigned)s >= (unsigned)n) s = 0;
+    kv[p] = *reinterpret_cast<const uint4*>(k + u * P.ks[0] + (int64_t)s * P.ks[1] + pc * 8);
+    vv[p] = *reinterpret_cast<const uint4*>(v + u * P.vs[0] + (int64_t)s * P.vs[1] + pc * 8);
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int t = t0 + p * RPP + threadIdx.x / PPR;
+    if (t >= nl) continue;
+    uint4* kd = reinterpret_cast<uint4*>(ko + u * P.os[0] + (int64_t)t * P.os[1] + pc * 8);
+    uint4* vd = reinterpret_cast<uint4*>(vo + u * P.os[0] + (int64_t)t * P.os[1] + pc * 8);
+    __builtin_nontemporal_store(kv[p].x, &kd->x);
+    __builtin_nontemporal_store(kv[p].y, &kd->y);
+    __builtin_nontemporal_store(kv[p].z, &kd->z);
+    __builtin_nontemporal_store(kv[p].w, &kd->w);
+    __builtin_nontemporal_store(vv[p].x, &vd->x);
+    __builtin_nontemporal_store(vv[p].y, &vd->y);
+    __builtin_nontemporal_store(vv[p].z, &vd->z);
+    __builtin_nontemporal_store(vv[p].w, &vd->w);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+static kvc_status c3_hip(hipError_t e) {
+  if (e == hipSuccess) return KVC_OK;
+  kvc_note_hip_error((int)e);
+  return KVC_ERR_HIP;
+}
+
+static size_t c3_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+static kvc_status c3_desc(const kvc_c3_problem* p, const kvc_c3_params* prm, C3Desc* V) {
+  if (!p || !prm || !V || !p->len || !p->budget) return KVC_ERR_INVALID_ARG;
+  if (p->n_seq < 1 || p->n_layers < 1 || p->n_kv_heads < 1 || p->gqa_group < 1 ||
+      p->head_dim < 1 || p->capacity < 1)
+    return KVC_ERR_INVALID_ARG;
+  if (!(prm->lambda >= 0.0 && prm->lambda <= 1.0) || prm->r_swaps < 0 || prm->r_swaps > 8)
+    return KVC_ERR_INVALID_ARG;
+  for (int a = 0; a < 2; ++a) {
+    if (p->k_stride[a] < 0 || p->v_stride[a] < 0 || p->out_stride[a] < 0) return KVC_ERR_INVALID_ARG;
+    if (p->k_stride[a] % 8 || p->v_stride[a] % 8 || p->out_stride[a] % 8) return KVC_ERR_INVALID_ARG;
+  }
+  if (p->k_stride[1] < p->head_dim || p->v_stride[1] < p->head_dim || p->out_stride[1] < p->head_dim)
+    return KVC_ERR_INVALID_ARG;
+  if (p->k_stride[0] < p->k_stride[1] * p->capacity || p->v_stride[0] < p->v_stride[1] * p->capacity)
+    return KVC_ERR_INVALID_ARG;
+  if (p->n_seq > C3_MAX_SEQ || p->capacity > C3_MAX_CAP) return KVC_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return KVC_ERR_UNSUPPORTED;
+  if (p->gqa_group > C3_MAX_G) return KVC_ERR_UNSUPPORTED;
+  const int64_t upseq = (int64_t)p->n_layers * p->n_kv_heads;
+  if (upseq > KVC_MAX_UNITS_PER_SEQ) return KVC_ERR_UNSUPPORTED;
+  memset(V, 0, sizeof(*V));
+  int64_t kept = 1;
+  for (int i = 0; i < p->n_seq; ++i) {
+    const int64_t n = p->len[i], B = p->budget[i];
+    if (n < 0 || n > p->capacity || B < 1) return KVC_ERR_INVALID_ARG;
+    V->len[i] = (int32_t)n;
+    V->budget[i] = (int32_t)std::min<int64_t>(B, INT32_MAX);
+    kept = std::max(kept, std::min(n, B));
+  }
+  if (p->out_stride[0] < p->out_stride[1] * kept) return KVC_ERR_INVALID_ARG;
+  V->n_seq = p->n_seq;
+  V->upseq = (int32_t)upseq;
+  V->gqa = p->gqa_group;
+  V->d = p->head_dim;
+  V->n_units = (int32_t)(upseq * p->n_seq);
+  V->R = prm->r_swaps;
+  V->cap = (int32_t)p->capacity;
+  V->ncap = (int32_t)(2 * p->capacity);
+  V->nchunk = (int32_t)((p->capacity + C3_CH - 1) / C3_CH);
+  V->kept_cap = (int32_t)kept;
+  V->lam = prm->lambda;
+  V->seed = prm->seed;
+  for (int a = 0; a < 2; ++a) {
+    V->ks[a] = p->k_stride[a];
+    V->vs[a] = p->v_stride[a];
+    V->os[a] = p->out_stride[a];
+  }
+  return KVC_OK;
+}
+
+static int64_t c3_smax(const C3Desc& V) {
+  return (int64_t)V.n_units * (V.cap / (C3_MLOC + 1) + 1);
+}
+
+static void c3_layout(const C3Desc& V, kvc_c3_layout* L) {
+  memset(L, 0, sizeof(*L));
+  const size_t U = (size_t)V.n_units, NC = (size_t)V.ncap, CAP = (size_t)V.cap, D = (size_t)V.d;
+  L->node_cap = (int64_t)NC;
+  L->kept_cap = V.kept_cap;
+  size_t o = 0;
+  L->start = o;    o += c3_up(4 * U * NC);
+  L->size = o;     o += c3_up(4 * U * NC);
+  L->left = o;     o += c3_up(4 * U * NC);
+  L->parent = o;   o += c3_up(4 * U * NC);
+  L->depth = o;    o += c3_up(4 * U * NC);
+  L->perm = o;     o += c3_up(4 * U * CAP);
+  L->n_nodes = o;  o += c3_up(4 * U);
+  L->centroid = o; o += c3_up(2 * U * NC * D);
+  L->index_bytes = o;
+  o = 0;
+  L->count = o;    o += c3_up(4 * U);
+  L->frontier = o; o += c3_up(4 * U * CAP);
+  L->ema = o;      o += c3_up(8 * U * CAP);
+  L->state_bytes = o;
+  const size_t S = (size_t)c3_smax(V);
+  L->build_workspace_bytes = c3_up(2 * U * CAP * D) + c3_up(4 * U * CAP) + c3_up(U * CAP) +
+                             c3_up(4 * U * CAP) + c3_up(4 * U * CAP) +
+                             c3_up(4 * U * (C3_MAXD + 2)) + c3_up(8 * U * D) + c3_up(8 * 2 * S) +
+                             c3_up(4 * S * D) + c3_up(4 * S) + 2 * c3_up(8 * S * D) + c3_up(4 * S) +
+                             c3_up(4 * S) + c3_up(16 * (C3_MAXD + 1)) + c3_up(4);
+  L->step_workspace_bytes = c3_up(4 * U * CAP);
+}
+
+static C3Index c3_index(const kvc_c3_layout& L, const void* base) {
+  char* b = (char*)base;
+  C3Index X;
+  X.start = (int32_t*)(b + L.start);
+  X.size = (int32_t*)(b + L.size);
+  X.left = (int32_t*)(b + L.left);
+  X.parent = (int32_t*)(b + L.parent);
+  X.depth = (int32_t*)(b + L.depth);
+  X.perm = (int32_t*)(b + L.perm);
+  X.nn = (int32_t*)(b + L.n_nodes);
+  X.cent = (uint16_t*)(b + L.centroid);
+  return X;
+}
+
+static C3State c3_state(const kvc_c3_layout& L, const void* base) {
+  char* b = (char*)base;
+  C3State S;
+  S.count = (int32_t*)(b + L.count);
+  S.fr = (int32_t*)(b + L.frontier);
+  S.e = (double*)(b + L.ema);
+  return S;
+}
+
+static C3Work c3_work(const C3Desc& V, void* ws) {
+  const size_t U = (size_t)V.n_units, CAP = (size_t)V.cap, D = (size_t)V.d;
+  const size_t S = (size_t)c3_smax(V);
+  char* p = (char*)ws;
+  C3Work W;
+  W.cres = (uint16_t*)p;   p += c3_up(2 * U * CAP * D);
+  W.res_n0 = (int32_t*)p;  p += c3_up(4 * U * CAP);
+  W.flags = (uint8_t*)p;   p += c3_up(U * CAP);
+  W.head = (int32_t*)p;    p += c3_up(4 * U * CAP);
+  W.ptmp = (int32_t*)p;    p += c3_up(4 * U * CAP);
+  W.lvl = (int32_t*)p;     p += c3_up(4 * U * (C3_MAXD + 2));
+  W.rsum = (double*)p;     p += c3_up(8 * U * D);
+  W.snode = (int2*)p;      p += c3_up(8 * 2 * S);
+  W.sw = (float*)p;        p += c3_up(4 * S * D);
+  W.sb = (float*)p;        p += c3_up(4 * S);
+  W.s0 = (double*)p;       p += c3_up(8 * S * D);
+  W.s1 = (double*)p;       p += c3_up(8 * S * D);
+  W.sn1 = (int32_t*)p;     p += c3_up(4 * S);
+  W.salive = (int32_t*)p;  p += c3_up(4 * S);
+  W.cnt = (int32_t*)p;     p += c3_up(16 * (C3_MAXD + 1));
+  W.err = (int32_t*)p;
+  W.smax = (int32_t)S;
+  return W;
+}
+
+static bool c3_a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool c3_a256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
+
+extern "C" kvc_status kvc_c3_plan(const kvc_c3_problem* prob, const kvc_c3_params* params,
+                                  kvc_c3_layout* layout) {
+  C3Desc V;
+  const kvc_status st = c3_desc(prob, params, &V);
+  if (st != KVC_OK) return st;
+  if (!layout) return KVC_ERR_INVALID_ARG;
+  c3_layout(V, layout);
+  return KVC_OK;
+}
+
+#define C3_LAUNCH(D_, kern, grid, block, ...)                                       \
+  do {                                                                              \
+    if ((D_) == 128)                                                                \
+      hipLaunchKernelGGL((kern<128>), (grid), (block), 0, st, __VA_ARGS__);          \
+    else                                                                            \
+      hipLaunchKernelGGL((kern<64>), (grid), (block), 0, st, __VA_ARGS__);           \
+  } while (0)
+
+extern "C" kvc_status kvc_c3_build(const kvc_c3_problem* prob, const kvc_c3_params* params,
+                                   const void* k, void* index, void* state, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  C3Desc V;
+  kvc_status rs = c3_desc(prob, params, &V);
+  if (rs != KVC_OK) return rs;
+  if (!k || !index || !state || !workspace) return KVC_ERR_INVALID_ARG;
+  if (!c3_a16(k) || !c3_a256(index) || !c3_a256(state) || !c3_a256(workspace))
+    return KVC_ERR_INVALID_ARG;
+  kvc_c3_layout L;
+  c3_layout(V, &L);
+  if (workspace_bytes < L.build_workspace_bytes) return KVC_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const C3Index X = c3_index(L, index);
+  const C3State S = c3_state(L, state);
+  const C3Work W = c3_work(V, workspace);
+  const uint16_t* kk = (const uint16_t*)k;
+  hipError_t e = hipMemsetAsync(W.cnt, 0, c3_up(16 * (C3_MAXD + 1)) + c3_up(4), st);
+  if (e != hipSuccess) return c3_hip(e);
+  const unsigned U = (unsigned)V.n_units;
+  hipLaunchKernelGGL(c3_init_kernel, dim3(U), dim3(C3_T), 0, st, V, X, W);
+  C3_LAUNCH(V.d, c3_root_sum_kernel, dim3(U * V.nchunk), dim3(C3_T), V, W, kk);
+  hipLaunchKernelGGL(c3_root_fin_kernel, dim3(U), dim3(C3_T), 0, st, V, X, W);
+  if ((e = hipGetLastError()) != hipSuccess) return c3_hip(e);
+  // Depth 0 work, known on the host.
+  int cand = 0, span = 0, big = 0;
+  for (int u = 0; u < V.n_units; ++u) {
+    const int n = V.len[u / V.upseq];
+    if (n > C3_LEAF) ++cand;
+    if (n > C3_MLOC) {
+      ++span;
+      big = std::max(big, n);
+    }
+  }
+  for (int dep = 0; dep < C3_MAXD && cand > 0; ++dep) {
+    const int par = dep & 1;
+    if (cand > span)
+      C3_LAUNCH(V.d, c3_local_kernel, dim3(U * V.nchunk), dim3(C3_T), V, dep, X, W, kk);
+    if (span > 0) {
+      const dim3 g1((unsigned)span), g2((unsigned)span, (unsigned)((big + C3_CH - 1) / C3_CH));
+      C3_LAUNCH(V.d, c3_span_init_kernel, g1, dim3(64), V, dep, par, X, W, kk);
+      for (int it = 0; it < C3_ITERS; ++it) {
+        C3_LAUNCH(V.d, c3_span_iter_kernel, g2, dim3(C3_T), V, par, X, W, kk);
+        C3_LAUNCH(V.d, c3_span_fin_kernel, g1, dim3(64), V, par, it + 1 == C3_ITERS ? 1 : 0, X, W);
+      }
+      hipLaunchKernelGGL(c3_span_part_kernel, g1, dim3(C3_BIG), 0, st, V, par, X, W);
+    }
+    C3_LAUNCH(V.d, c3_ids_kernel, dim3(U), dim3(C3_BIG), V, dep, X, W);
+    if ((e = hipGetLastError()) != hipSuccess) return c3_hip(e);
+    int32_t h[4];
+    e = hipMemcpyAsync(h, W.cnt + (dep + 1) * 4, sizeof(h), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return c3_hip(e);
+    cand = h[0];
+    span = h[1];
+    big = h[2];
+    if (span > W.smax) return KVC_ERR_UNSUPPORTED;  // cannot happen: span nodes are disjoint
+  }
+  hipLaunchKernelGGL(c3_frontier_kernel, dim3(U), dim3(C3_BIG), 0, st, V, X, S, W);
+  if ((e = hipGetLastError()) != hipSuccess) return c3_hip(e);
+  int32_t bad = 0;
+  e = hipMemcpyAsync(&bad, W.err, sizeof(bad), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return c3_hip(e);
+  return bad ? KVC_ERR_INVALID_ARG : KVC_OK;
+}
+
+static hipError_t c3_launch_score(const C3Desc& V, const C3Index& X, const C3State& S,
+                                  const void* q, float* sigma, hipStream_t st) {
+  C3_LAUNCH(V.d, c3_score_kernel, dim3((unsigned)V.n_units * C3_SW), dim3(C3_T), V, X, S,
+            (const uint16_t*)q, sigma);
+  return hipGetLastError();
+}
+
+static hipError_t c3_launch_su(const C3Desc& V, const C3Index& X, const C3State& Sin,
+                               const float* sigma, int32_t* idx, const C3State& Sout, int sel,
+                               int upd, hipStream_t st) {
+  hipLaunchKernelGGL(c3_select_update_kernel, dim3((unsigned)V.n_units), dim3(C3_BIG), 0, st, V,
+                     X, Sin, sigma, idx, Sout, sel, upd);
+  return hipGetLastError();
+}
+
+static hipError_t c3_launch_gather(const C3Desc& V, const void* k, const void* v,
+                                   const int32_t* idx, void* ko, void* vo, hipStream_t st) {
+  const int rpb = (C3_T / (V.d / 8)) * 4;
+  const int bpc = (V.kept_cap + rpb - 1) / rpb;
+  C3_LAUNCH(V.d, c3_gather_kernel, dim3((unsigned)((int64_t)V.n_units * bpc)), dim3(C3_T), V, bpc,
+            (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)ko, (uint16_t*)vo);
+  return hipGetLastError();
+}
+
+static kvc_status c3_common(const kvc_c3_problem* prob, const kvc_c3_params* params, C3Desc* V,
+                            kvc_c3_layout* L) {
+  const kvc_status rs = c3_desc(prob, params, V);
+  if (rs != KVC_OK) return rs;
+  c3_layout(*V, L);
+  return KVC_OK;
+}
+
+extern "C" kvc_status kvc_c3_score(const kvc_c3_problem* prob, const kvc_c3_params* params,
+                                   const void* index, const void* state, const void* q,
+                                   float* sigma, void* stream) {
+  C3Desc V;
+  kvc_c3_layout L;
+  kvc_status rs = c3_common(prob, params, &V, &L);
+  if (rs != KVC_OK) return rs;
+  if (!index || !state || !q || !sigma || !c3_a256(index) || !c3_a256(state) || !c3_a16(q))
+    return KVC_ERR_INVALID_ARG;
+  return c3_hip(c3_launch_score(V, c3_index(L, index), c3_state(L, state), q, sigma,
+                                (hipStream_t)stream));
+}
+
+extern "C" kvc_status kvc_c3_select(const kvc_c3_problem* prob, const kvc_c3_params* params,
+                                    const void* index, const void* state, const float* sigma,
+                                    int32_t* idx_out, void* stream) {
+  C3Desc V;
+  kvc_c3_layout L;
+  kvc_status rs = c3_common(prob, params, &V, &L);
+  if (rs != KVC_OK) return rs;
+  if (!index || !state || !sigma || !idx_out || !c3_a256(index) || !c3_a256(state))
+    return KVC_ERR_INVALID_ARG;
+  const C3State S = c3_state(L, state);
+  return c3_hip(c3_launch_su(V, c3_index(L, index), S, sigma, idx_out, S, 1, 0,
+                             (hipStream_t)stream));
+}
+
+extern "C" kvc_status kvc_c3_update(const kvc_c3_problem* prob, const kvc_c3_params* params,
+                                    const void* index, const void* state_in, const float* sigma,
+                                    void* state_out, void* stream) {
+  C3Desc V;
+  kvc_c3_layout L;
+  kvc_status rs = c3_common(prob, params, &V, &L);
+  if (rs != KVC_OK) return rs;
+  if (!index || !state_in || !sigma || !state_out || state_in == state_out || !c3_a256(index) ||
+      !c3_a256(state_in) || !c3_a256(state_out))
+    return KVC_ERR_INVALID_ARG;
+  return c3_hip(c3_launch_su(V, c3_index(L, index), c3_state(L, state_in), sigma, nullptr,
+                             c3_state(L, state_out), 0, 1, (hipStream_t)stream));
+}
+
+extern "C" kvc_status kvc_c3_gather(const kvc_c3_problem* prob, const kvc_c3_params* params,
+                                    const void* k, const void* v, const int32_t* idx, void* k_out,
+                                    void* v_out, void* stream) {
+  C3Desc V;
+  kvc_c3_layout L;
+  kvc_status rs = c3_common(prob, params, &V, &L);
+  if (rs != KVC_OK) return rs;
+  if (!k || !v || !idx || !k_out || !v_out || !c3_a16(k) || !c3_a16(v) || !c3_a16(k_out) ||
+      !c3_a16(v_out))
+    return KVC_ERR_INVALID_ARG;
+  return c3_hip(c3_launch_gather(V, k, v, idx, k_out, v_out, (hipStream_t)stream));
+}
+
+extern "C" kvc_status kvc_c3_step(const kvc_c3_problem* prob, const kvc_c3_params* params,
+                                  const void* index, const void* state_in, void* state_out,
+                                  const void* q, const void* k, const void* v, void* k_out,
+                                  void* v_out, int32_t* idx_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  C3Desc V;
+  kvc_c3_layout L;
+  kvc_status rs = c3_common(prob, params, &V, &L);
+  if (rs != KVC_OK) return rs;
+  if (!index || !state_in || !state_out || state_in == state_out || !q || !k || !v || !k_out ||
+      !v_out || !idx_out || !workspace)
+    return KVC_ERR_INVALID_ARG;
+  if (!c3_a256(index) || !c3_a256(state_in) || !c3_a256(state_out) || !c3_a256(workspace) ||
+      !c3_a16(q) || !c3_a16(k) || !c3_a16(v) || !c3_a16(k_out) || !c3_a16(v_out))
+    return KVC_ERR_INVALID_ARG;
+  if (workspace_bytes < L.step_workspace_bytes) return KVC_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const C3Index X = c3_index(L, index);
+  const C3State Si = c3_state(L, state_in), So = c3_state(L, state_out);
+  float* sigma = (float*)workspace;
+  hipError_t e = c3_launch_score(V, X, Si, q, sigma, st);
+  if (e == hipSuccess) e = c3_launch_su(V, X, Si, sigma, idx_out, So, 1, 1, st);
+  if (e == hipSuccess) e = c3_launch_gather(V, k, v, idx_out, k_out, v_out, st);
+  return c3_hip(e);
+}

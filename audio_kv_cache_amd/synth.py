@@ -326,3 +326,83 @@ def decode_problem(cfg: DecodeConfig) -> DecodeProblem:
     with _cf.ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(fill, range(U)))
     return DecodeProblem(cfg, q, k, v, a)
+
+
+# ---------------------------------------------------------------------------
+# Query-guided retrieval (C3): audio key/value caches and decode queries
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class C3Config:
+    name: str
+    index: int
+    n_seq: int
+    n_layers: int
+    n_kv_heads: int
+    gqa: int
+    head_dim: int
+    lens: tuple              # audio keys n per cache, per sequence
+    budgets: tuple           # B per sequence
+    capacity: int
+
+
+C3_CONFIGS = {
+    # parity-sized
+    "c3_tiny": C3Config("c3_tiny", 20, 1, 2, 2, 4, 64, lens=(300,), budgets=(40,), capacity=320),
+    # d = 128; nodes over 96 keys take the multi-workgroup path; the middle
+    # sequence fits its budget (retrieval bypassed)
+    "c3_mixed": C3Config("c3_mixed", 21, 3, 1, 2, 8, 128, lens=(1000, 37, 2500),
+                         budgets=(100, 64, 200), capacity=2560),
+    # empty cache, a root that cannot split, the smallest splittable root,
+    # a 97-key root (the smallest multi-workgroup node), a budget of 1
+    "c3_edge": C3Config("c3_edge", 22, 5, 1, 1, 2, 64, lens=(0, 4, 5, 97, 150),
+                        budgets=(1, 1, 2, 10, 1), capacity=160),
+    # Qwen3-Omni-30B-A3B shape (48 layers, 4 KV heads, 8 query heads per KV
+    # head, head_dim 128) at a 32K-token audio context and a 512-key budget
+    "c3_omni30b": C3Config("c3_omni30b", 23, 1, 48, 4, 8, 128, lens=(32768,), budgets=(512,),
+                           capacity=32768),
+}
+
+
+def c3_cache(cfg: C3Config, u: int):
+    """One cache's audio keys and values (bf16 bits [n, d]): noise plus a slow
+    drift along the audio (as for the prefill inputs) and a sink on row 0."""
+    n_units = cfg.n_seq * cfg.n_layers * cfg.n_kv_heads
+    rng = np.random.default_rng(np.random.SeedSequence(3000 + cfg.index).spawn(n_units)[u])
+    seq = u // (cfg.n_layers * cfg.n_kv_heads)
+    n, d = int(cfg.lens[seq]), cfg.head_dim
+    periods = rng.uniform(50.0, 400.0, size=N_SINUSOIDS)
+    phases = rng.uniform(0.0, 2.0 * math.pi, size=(N_SINUSOIDS, d))
+    sink = rng.standard_normal(d)
+    sink /= np.linalg.norm(sink)
+    kn = rng.standard_normal((n, d), dtype=np.float32)
+    vv = rng.standard_normal((n, d), dtype=np.float32)
+    t = np.arange(n, dtype=np.float64)
+    w = 2.0 * math.pi / periods
+    A = np.concatenate([np.sin(np.outer(t, w)), np.cos(np.outer(t, w))], axis=1)
+    B = DRIFT_AMP * np.concatenate([np.cos(phases), np.sin(phases)], axis=0)
+    k = kn + (A @ B).astype(np.float32)
+    if n:
+        k[0] += np.float32(SINK_BETA * math.sqrt(d)) * sink.astype(np.float32)
+    return f32_to_bf16_bits(k), f32_to_bf16_bits(vv)
+
+
+def c3_problem(cfg: C3Config):
+    """k, v bf16 bits [units, capacity, d] (rows past n are zero)."""
+    U = cfg.n_seq * cfg.n_layers * cfg.n_kv_heads
+    k = np.zeros((U, cfg.capacity, cfg.head_dim), dtype=np.uint16)
+    v = np.zeros((U, cfg.capacity, cfg.head_dim), dtype=np.uint16)
+
+    def fill(u):
+        ku, vu = c3_cache(cfg, u)
+        k[u, :ku.shape[0]], v[u, :vu.shape[0]] = ku, vu
+
+    with _cf.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, range(U)))
+    return k, v
+
+
+def c3_queries(cfg: C3Config, step: int) -> np.ndarray:
+    """Decode-step queries, bf16 bits [units, G, d]."""
+    U = cfg.n_seq * cfg.n_layers * cfg.n_kv_heads
+    rng = np.random.default_rng(np.random.SeedSequence([4000 + cfg.index, step]))
+    return f32_to_bf16_bits(rng.standard_normal((U, cfg.gqa, cfg.head_dim), dtype=np.float32))

@@ -24,12 +24,13 @@ reproduce exactly (readings, each listed in the design doc):
   * a node with more than LEAF = 4 keys splits by 8 Lloyd iterations of
     2-means; depth is capped at MAX_DEPTH = 24;
   * assignment: w = mu1 - mu0 rounded to fp32 and then to 16 significant
-    bits (|w| < 2^-100 -> 0), m = (mu0 + mu1) / 2 rounded to fp32,
-    b = sum_c w_c m_c and s(k) = sum_c k_c w_c in fp32, both summed in
-    column order; the key joins cluster 1 iff s(k) > b (the nearest-centroid
-    test written as the side of the bisecting hyperplane; a key on it joins
-    cluster 0).  Every k_c w_c is exact in fp32, so a fused multiply-add
-    gives the same s(k);
+    bits (|w| < 2^-100 -> 0), m = (mu0 + mu1) / 2 rounded to fp32;
+    s(k) = sum_c k_c w_c in fp32 summed in column order, b = the pairwise
+    fp32 sum of the rounded products w_c m_c (adjacent columns, then
+    adjacent pairs, and so on); the key joins cluster 1 iff s(k) > b (the
+    nearest-centroid test written as the side of the bisecting hyperplane;
+    a key on it joins cluster 0).  Every k_c w_c is exact in fp32, so a
+    fused multiply-add gives the same s(k);
   * a split that leaves a cluster empty at any iteration is abandoned (the
     node stays a leaf); new means are exact sums over the count (fp64);
   * "seed 0": the initial centroids are two distinct member keys chosen by
@@ -124,10 +125,10 @@ def bisector(mu0, mu1):
     w = round16((mu1 - mu0).astype(np.float32))
     w = np.where(np.abs(w) < W_FLUSH, np.float32(0), w).astype(np.float32)
     m = (0.5 * (mu0 + mu1)).astype(np.float32)
-    b = np.zeros(w.shape[:-1], dtype=np.float32)
-    for c in range(w.shape[-1]):
-        b = b + w[..., c] * m[..., c]
-    return w, b
+    p = w * m                                        # fp32, each rounded
+    while p.shape[-1] > 1:                           # pairwise: (0+1), (2+3), ...
+        p = p[..., 0::2] + p[..., 1::2]
+    return w, p[..., 0]
 
 
 def assign(X32, W, b) -> np.ndarray:

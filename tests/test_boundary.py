@@ -18,16 +18,17 @@ INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 def declared_symbols(name):
     text = open(os.path.join(INCLUDE, name)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kvc_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     L = C.lib()
     headers = sorted(f for f in os.listdir(INCLUDE) if f.endswith(".h"))
-    assert headers == ["kvc.h", "kvc_voxzip.h"]
+    assert headers == ["kvc.h", "kvc_c3.h", "kvc_voxzip.h"]
     assert set(declared_symbols("kvc.h")) == set(C.EXPORTS)
     assert set(declared_symbols("kvc_voxzip.h")) == set(C.VZ_EXPORTS)
-    for n in C.EXPORTS + C.VZ_EXPORTS:
+    assert set(declared_symbols("kvc_c3.h")) == set(C.C3_EXPORTS)
+    for n in C.EXPORTS + C.VZ_EXPORTS + C.C3_EXPORTS:
         assert hasattr(L, n), n
 
 
@@ -175,3 +176,66 @@ def test_compress_layers_rejects_bad_ranges():
                                    fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
                                    1 << 40, None)
         assert st == C.KVC_ERR_INVALID_ARG, (lb, le)
+
+
+# ---------------------------------------------------------------------------
+# include/kvc_c3.h
+# ---------------------------------------------------------------------------
+def c3_spec(**kw):
+    base = dict(n_layers=48, n_kv_heads=4, gqa=8, head_dim=128, lens=[32768], budgets=[512],
+                capacity=32768)
+    base.update(kw)
+    return api.C3Spec(**base)
+
+
+def test_c3_plan_layout():
+    sp = c3_spec(lens=[32768, 300, 0], budgets=[512, 512, 512])
+    lay = api.kvc_c3_plan(sp, api.C3Params())
+    U, NC, CAP, D = sp.n_units, 2 * 32768, 32768, 128
+    assert lay.node_cap == NC and lay.kept_cap == 512
+    spans = sorted([(lay.start, 4 * U * NC), (lay.size, 4 * U * NC), (lay.left, 4 * U * NC),
+                    (lay.parent, 4 * U * NC), (lay.depth, 4 * U * NC), (lay.perm, 4 * U * CAP),
+                    (lay.n_nodes, 4 * U), (lay.centroid, 2 * U * NC * D)])
+    for (o, n), (o2, _) in zip(spans, spans[1:] + [(lay.index_bytes, 0)]):
+        assert o % 256 == 0 and o + n <= o2
+    st = sorted([(lay.count, 4 * U), (lay.frontier, 4 * U * CAP), (lay.ema, 8 * U * CAP)])
+    for (o, n), (o2, _) in zip(st, st[1:] + [(lay.state_bytes, 0)]):
+        assert o % 256 == 0 and o + n <= o2
+    assert lay.step_workspace_bytes >= 4 * U * CAP
+    # child centroids per position (bf16) dominate the build workspace
+    assert lay.build_workspace_bytes >= 2 * U * CAP * D
+    # every cache fits its budget: one kept row per cache at least
+    assert api.kvc_c3_plan(c3_spec(lens=[0]), api.C3Params()).kept_cap == 1
+
+
+def c3_status(sp, prm=None, ws_bytes=1 << 40):
+    L = C.lib()
+    prm = prm or api.C3Params()
+    fake = ctypes.c_void_p(1 << 20)
+    other = ctypes.c_void_p(1 << 21)
+    return L.kvc_c3_step(ctypes.byref(sp.c()), ctypes.byref(prm.c()), fake, fake, other, fake,
+                         fake, fake, fake, fake, fake, fake, ws_bytes, None)
+
+
+def test_c3_invalid_problems_rejected_before_launch():
+    assert c3_status(c3_spec(lens=[32769])) == C.KVC_ERR_INVALID_ARG          # n > capacity
+    assert c3_status(c3_spec(lens=[-1])) == C.KVC_ERR_INVALID_ARG
+    assert c3_status(c3_spec(budgets=[0])) == C.KVC_ERR_INVALID_ARG
+    assert c3_status(c3_spec(head_dim=96)) == C.KVC_ERR_UNSUPPORTED
+    assert c3_status(c3_spec(gqa=33)) == C.KVC_ERR_UNSUPPORTED
+    assert c3_status(c3_spec(capacity=140000, lens=[1000])) == C.KVC_ERR_UNSUPPORTED
+    assert c3_status(c3_spec(lens=[1000] * 65, budgets=[10])) == C.KVC_ERR_UNSUPPORTED
+    assert c3_status(c3_spec(), api.C3Params(lam=1.5)) == C.KVC_ERR_INVALID_ARG
+    assert c3_status(c3_spec(), api.C3Params(r_swaps=9)) == C.KVC_ERR_INVALID_ARG
+    assert c3_status(c3_spec(), ws_bytes=16) == C.KVC_ERR_WORKSPACE
+    assert c3_status(c3_spec(k_stride=(32768 * 128, 100))) == C.KVC_ERR_INVALID_ARG
+    assert c3_status(c3_spec(out_stride=(100 * 128, 128))) == C.KVC_ERR_INVALID_ARG  # < B rows
+    # state_in == state_out
+    L = C.lib()
+    sp = c3_spec()
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.kvc_c3_step(ctypes.byref(sp.c()), ctypes.byref(api.C3Params().c()), fake, fake,
+                         fake, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None) \
+        == C.KVC_ERR_INVALID_ARG
+    assert L.kvc_c3_build(ctypes.byref(sp.c()), ctypes.byref(api.C3Params().c()), fake, fake,
+                          fake, fake, 16, None) == C.KVC_ERR_WORKSPACE
