@@ -33,6 +33,9 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 # MI355X dense matrix peaks, TFLOP/s: bf16 MFMA; fp32 inputs run on the fp64
 # MFMA (78.6 TFLOP/s dense fp64)
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 78.6}
+# VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one wave64
+# instruction per SIMD per 4 cycles (T lane-ops/s).
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 ROOT = pathlib.Path(__file__).resolve().parent
 
 
@@ -236,6 +239,155 @@ def bench_decode(args):
     return out
 
 
+def c3_bytes(cfg, A_total, kept_total):
+    """Algorithmic HBM bytes of one C3 decode step: every frontier entry's
+    centroid (bf16), id and score once; every kept K and V row read and
+    written once, with its position."""
+    d = cfg.head_dim
+    score = A_total * (2 * d + 4 + 4)
+    select = A_total * (4 + 4 + 8 + 4) + kept_total * 4
+    gather = kept_total * (2 * 2 * 2 * d + 4)
+    return {"score": score, "select_update": select, "gather": gather,
+            "total": score + select + gather}
+
+
+def bench_c3(args):
+    """C3 retrieval: the prefill tree build over every cache and the decode
+    step (scores, budget fill, frontier update, gather), inputs resident in
+    HBM; per-kernel event timing and a CPU-oracle sample."""
+    import torch
+    from audio_kv_cache_amd import api, synth
+    cfg = synth.C3_CONFIGS[args.c3_config]
+    log(f"[bench] c3: generating {cfg.name}")
+    k_np, v_np = synth.c3_problem(cfg)
+    k = torch.from_numpy(k_np.view(np.int16)).cuda().view(torch.bfloat16)
+    v = torch.from_numpy(v_np.view(np.int16)).cuda().view(torch.bfloat16)
+    spec = api.C3Spec(n_layers=cfg.n_layers, n_kv_heads=cfg.n_kv_heads, gqa=cfg.gqa,
+                      head_dim=cfg.head_dim, lens=cfg.lens, budgets=cfg.budgets,
+                      capacity=cfg.capacity)
+    prm = api.C3Params()
+    o = api.c3_allocate(spec, prm, "cuda")
+    stream = torch.cuda.current_stream()
+    U = spec.n_units
+    log("[bench] c3: building")
+    api.kvc_c3_build(spec, prm, k, o["index"], o["state"][0], o["build_ws"], stream)
+    builds = []
+    for _ in range(args.c3_builds):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        api.kvc_c3_build(spec, prm, k, o["index"], o["state"][0], o["build_ws"], stream)
+        torch.cuda.synchronize()
+        builds.append(time.perf_counter() - t0)
+    build_ms = 1e3 * sorted(builds)[len(builds) // 2]
+    V = api.C3Views(spec, o["layout"], o["index"], o["state"][0])
+    left = V.left.cpu().numpy()
+    size = V.size.cpu().numpy()
+    nn = V.n_nodes.cpu().numpy()
+    split_keys = sum(int(size[u, :nn[u]][left[u, :nn[u]] >= 0].sum()) for u in range(U))
+    A_total = int(V.count.sum().item())
+    kept_total = sum(min(int(cfg.lens[u // (cfg.n_layers * cfg.n_kv_heads)]),
+                         int(cfg.budgets[u // (cfg.n_layers * cfg.n_kv_heads)])) for u in range(U))
+    keys = sum(int(n) for n in cfg.lens) * cfg.n_layers * cfg.n_kv_heads
+    # Build: 8 Lloyd iterations over the keys of every node that splits; per
+    # key and iteration d multiply-adds for the hyperplane test and d adds
+    # for the member sums.
+    build_ops = split_keys * 8 * 2 * cfg.head_dim
+    build_tops = build_ops / (build_ms * 1e-3) / 1e12
+    log(f"[bench] c3 build {build_ms:.2f} ms ({keys / (build_ms * 1e-3):.4g} keys/s, "
+        f"{build_tops:.2f} T lane-ops/s), {int(nn.sum())} nodes, frontier {A_total}")
+
+    qs = [torch.from_numpy(synth.c3_queries(cfg, s).view(np.int16)).cuda().view(torch.bfloat16)
+          for s in range(4)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cur = [0]
+
+    def step(i):
+        si, so = o["state"][cur[0]], o["state"][1 - cur[0]]
+        api.kvc_c3_step(spec, prm, o["index"], si, so, qs[i % 4], k, v, o["k_out"], o["v_out"],
+                        o["idx"], o["step_ws"], stream)
+        cur[0] = 1 - cur[0]
+
+    def timed(fn, n):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(n):
+            fn(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n
+
+    step_ms = timed(step, args.steps)
+    si = o["state"][cur[0]]
+    so = o["state"][1 - cur[0]]
+    stages = {
+        "score": timed(lambda i: api.kvc_c3_score(spec, prm, o["index"], si, qs[0], o["sigma"],
+                                                  stream), args.steps),
+        "select": timed(lambda i: api.kvc_c3_select(spec, prm, o["index"], si, o["sigma"],
+                                                    o["idx"], stream), args.steps),
+        "update": timed(lambda i: api.kvc_c3_update(spec, prm, o["index"], si, o["sigma"], so,
+                                                    stream), args.steps),
+        "gather": timed(lambda i: api.kvc_c3_gather(spec, prm, k, v, o["idx"], o["k_out"],
+                                                    o["v_out"], stream), args.steps),
+    }
+    ab = c3_bytes(cfg, A_total, kept_total)
+    gbs = {n2: ab[n3] / (stages[n2] * 1e-3) / 1e9 for n2, n3 in
+           (("score", "score"), ("gather", "gather"))}
+    log(f"[bench] c3 step {step_ms * 1e3:.1f} us; stages " +
+        ", ".join(f"{n2} {t * 1e3:.1f} us" for n2, t in stages.items()))
+
+    def hbm(kernel, g, src):
+        return {"bound": "hbm", "kernel": kernel, "achieved": round(g, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(g / HBM_PEAK_GBS, 4),
+                "traffic": committed_traffic(src, kernel.split("<")[0], cfg.name)}
+
+    out = {
+        "workload": f"{cfg.name}: {U} caches ({cfg.n_seq} seq x {cfg.n_layers} layers x "
+                    f"{cfg.n_kv_heads} KV heads), n={list(cfg.lens)} audio keys, budget "
+                    f"{list(cfg.budgets)}, GQA {cfg.gqa}, head_dim {cfg.head_dim}, bf16, "
+                    f"lambda {prm.lam}, R {prm.r_swaps}",
+        "build_ms": round(build_ms, 3),
+        "build_keys_per_s": keys / (build_ms * 1e-3),
+        "build_roofline": {"bound": "alu", "kernels": "c3_local_kernel + c3_span_* (whole build)",
+                           "achieved": round(build_tops, 3), "peak": VALU_PEAK_TOPS,
+                           "unit": "T lane-ops/s", "frac": round(build_tops / VALU_PEAK_TOPS, 4),
+                           "ops": build_ops},
+        "nodes": int(nn.sum()), "frontier_entries": A_total,
+        "us_per_step": round(step_ms * 1e3, 2),
+        "steps_per_s": 1e3 / step_ms,
+        "algorithmic_bytes_per_step": ab["total"],
+        "stage_us": {n2: round(t * 1e3, 2) for n2, t in stages.items()},
+        "roofline": {"score": hbm("c3_score_kernel<128>", gbs["score"], "c3.hip"),
+                     "gather": hbm("c3_gather_kernel<128>", gbs["gather"], "c3.hip")},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import c3 as C3
+        u = 0
+        n = int(cfg.lens[0])
+        Kf = synth.bf16_bits_to_f32(k_np[u, :n]).astype(np.float64)
+        t0 = time.perf_counter()
+        tree = C3.build_tree(Kf, cache=u)
+        tb = time.perf_counter() - t0
+        F = C3.initial_frontier(tree, n)
+        e = np.zeros(len(F))
+        q0 = synth.bf16_bits_to_f32(synth.c3_queries(cfg, 0)[u]).astype(np.float64)
+        t0 = time.perf_counter()
+        nst = 5
+        for _ in range(nst):
+            r = C3.step(tree, F, e, q0, n, int(cfg.budgets[0]))
+            F, e = r["F"], r["e"]
+        ts = (time.perf_counter() - t0) / nst
+        out["cpu_baseline"] = dict(value=n / tb,
+                                   unit="keys/s (tree build)", cores=1, kind="oracle",
+                                   sample=f"cache 0 of the same workload: tree build of {n} keys "
+                                          f"{tb:.2f} s; one decode step {ts * 1e3:.2f} ms "
+                                          f"(about {U * ts:.2f} s for all {U} caches)",
+                                   step_caches_per_s=1.0 / ts)
+    del k_np, v_np
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +399,12 @@ def main():
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step (decayed eviction) measurement")
     ap.add_argument("--decode-config", default="vz_omni30b")
+    ap.add_argument("--no-c3", action="store_true",
+                    help="skip the query-guided retrieval (C3) measurement")
+    ap.add_argument("--c3-config", default="c3_omni30b")
+    ap.add_argument("--c3-builds", type=int, default=3)
+    ap.add_argument("--c3-only", action="store_true",
+                    help="measure only the C3 leg and print its object")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -258,6 +416,10 @@ def main():
 
     import torch
     from audio_kv_cache_amd import api, synth
+
+    if args.c3_only:
+        print(json.dumps(bench_c3(args)), flush=True)
+        return
 
     cfg = synth.CONFIGS[args.config]
     log(f"[bench] generating {cfg.name} inputs")
@@ -387,6 +549,7 @@ def main():
                                "gather.hip")
 
     decode = None if args.no_decode else bench_decode(args)
+    retrieval = None if args.no_c3 else bench_c3(args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -412,6 +575,7 @@ def main():
         "roofline": roof,
         "roofline_other_kernels": others,
         "decode": decode,
+        "retrieval": retrieval,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
