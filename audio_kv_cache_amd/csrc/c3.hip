@@ -86,6 +86,7 @@ struct C3Work {
   int32_t* ptmp;     // [U][cap]
   int32_t* lvl;      // [U][C3_MAXD + 2]: first id of each depth
   double* rsum;      // [U][d]
+  int32_t* tiny;     // [U]: 1 if a nonzero key value of the cache lies below 2^-17
   int2* snode;       // [2][smax]: (cache, node) of each span slot
   float* sw;         // [smax][d]
   float* sb;         // [smax]
@@ -93,7 +94,10 @@ struct C3Work {
   double* s1;        // [smax][d]
   int32_t* sn1;      // [smax]
   int32_t* salive;   // [smax]
-  int32_t* cnt;      // [C3_MAXD + 1][4]: candidates, span nodes, largest span node
+  int32_t* cnt;      // [C3_MAXD + 1][4]: candidates, span nodes, largest span
+                     // node, chunks holding local nodes
+  int32_t* cflag;    // [U * nchunk]: chunk already listed for the next depth
+  int32_t* clist;    // [2][U * nchunk]: chunks holding local nodes, per depth parity
   int32_t* err;      // [1]
   int32_t smax;
 };
@@ -126,6 +130,25 @@ __device__ inline uint4 c3_snap8(uint4 v, int& bad) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = c3_snap(w[i] & 0xFFFFu, bad) | (c3_snap(w[i] >> 16, bad) << 16);
   return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+typedef unsigned short c3_u16x2 __attribute__((ext_vector_type(2)));
+
+// c3_snap8 for keys already range-checked: the 8 values only change when
+// one of them is a nonzero below 2^-17 (|bits| - 1 < 0x36FF), which a packed
+// 16-bit test finds for all 8 at once.
+__device__ inline uint4 c3_snap8_fast(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  c3_u16x2 lo = {0xFFFFu, 0xFFFFu};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c3_u16x2 a = __builtin_bit_cast(c3_u16x2, w[i] & 0x7FFF7FFFu);
+    a = a - (c3_u16x2){1u, 1u};
+    lo = __builtin_elementwise_min(lo, a);
+  }
+  if (lo.x >= 0x36FFu && lo.y >= 0x36FFu) return v;
+  int ignored = 0;
+  return c3_snap8(v, ignored);
 }
 
 __device__ inline float c3_round16(float x) {
@@ -190,6 +213,32 @@ __device__ inline float c3_plane(const unsigned char* row, const float* w) {
   return s;
 }
 
+// Stage key rows into LDS (padded rows of RB bytes), snapped to the grid:
+// row r < rows with valid[r] >= 0 comes from key src[r] of cache u.  Every
+// load of a thread is issued before its first LDS store.  (The key range
+// was checked when the root sums were taken.)
+template <int D, int MAXR>
+__device__ inline void c3_stage(const C3Desc& P, int u, const uint16_t* __restrict__ k,
+                                const int* src, const signed char* valid, int rows,
+                                unsigned char* sK, bool tiny) {
+  constexpr int RB = 2 * D + 16, PPR = D / 8, PER = (MAXR * PPR + C3_T - 1) / C3_T;
+  uint4 buf[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int i = threadIdx.x + p * C3_T;
+    const int r = i / PPR, pc = i - r * PPR;
+    if (r < rows && (valid == nullptr || valid[r] >= 0))
+      buf[p] = *reinterpret_cast<const uint4*>(k + u * P.ks[0] + (int64_t)src[r] * P.ks[1] + pc * 8);
+  }
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int i = threadIdx.x + p * C3_T;
+    const int r = i / PPR, pc = i - r * PPR;
+    if (r < rows && (valid == nullptr || valid[r] >= 0))
+      *reinterpret_cast<uint4*>(sK + r * RB + pc * 16) = tiny ? c3_snap8_fast(buf[p]) : buf[p];
+  }
+}
+
 __device__ inline uint64_t c3_mix(uint64_t x) {
   uint64_t z = x + 0x9E3779B97F4A7C15ull;
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -235,6 +284,16 @@ __device__ inline int c3_block_scan(int v, int* scratch, int* total) {
   return off + incl - v;
 }
 
+// List chunk g (cache u's chunk of position p) for the local kernel of the
+// next depth, once.
+__device__ inline void c3_list_chunk(const C3Desc& P, const C3Work& W, int u, int p, int dep1) {
+  const int g = u * P.nchunk + p / C3_CH;
+  if (atomicExch(&W.cflag[g], 1) == 0) {
+    const int i = atomicAdd(&W.cnt[dep1 * 4 + 3], 1);
+    W.clist[(dep1 & 1) * P.n_units * P.nchunk + i] = g;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Build: roots
 // ---------------------------------------------------------------------------
@@ -245,8 +304,10 @@ __global__ __launch_bounds__(C3_T) void c3_init_kernel(C3Desc P, C3Index X, C3Wo
     X.perm[ub + p] = p;
     W.head[ub + p] = -1;
   }
+  for (int c = threadIdx.x; c < P.nchunk; c += C3_T) W.cflag[(size_t)u * P.nchunk + c] = 0;
   for (int c = threadIdx.x; c < P.d; c += C3_T) W.rsum[(size_t)u * P.d + c] = 0.0;
   if (threadIdx.x == 0) {
+    W.tiny[u] = 0;
     X.nn[u] = n > 0 ? 1 : 0;
     int32_t* lv = W.lvl + (size_t)u * (C3_MAXD + 2);
     lv[0] = 0;
@@ -263,6 +324,7 @@ __global__ __launch_bounds__(C3_T) void c3_init_kernel(C3Desc P, C3Index X, C3Wo
   if (threadIdx.x == 0 && n > C3_LEAF) {
     if (n <= C3_MLOC) {
       W.head[ub] = 0;
+      c3_list_chunk(P, W, u, 0, 0);
     } else {
       const int s = atomicAdd(&W.cnt[1], 1);
       W.snode[s] = make_int2(u, 0);
@@ -270,34 +332,50 @@ __global__ __launch_bounds__(C3_T) void c3_init_kernel(C3Desc P, C3Index X, C3Wo
   }
 }
 
-// Exact fp64 column sums of every cache's keys (the root's mean).
+// Exact fp64 column sums of every cache's keys (the root's mean).  Thread t
+// owns 16-byte piece t % (D/8) of rows t / (D/8) + k * RG of its chunk.
 template <int D>
 __global__ __launch_bounds__(C3_T) void c3_root_sum_kernel(C3Desc P, C3Work W,
                                                            const uint16_t* __restrict__ k) {
-  constexpr int CPL = D / 64;
+  constexpr int PPR = D / 8, RG = C3_T / PPR, PER = C3_CH / RG;
   const int u = blockIdx.x / P.nchunk, chn = blockIdx.x - u * P.nchunk;
   const int n = c3_n(P, u), base = chn * C3_CH;
   if (base >= n) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rows = min(C3_CH, n - base);
-  double acc[CPL];
+  const int pc = threadIdx.x % PPR, rg = threadIdx.x / PPR;
+  uint4 buf[PER];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) acc[i] = 0.0;
-  int bad = 0;
-  for (int r = wave; r < rows; r += C3_T / 64) {
-    const uint16_t* row = k + u * P.ks[0] + (int64_t)(base + r) * P.ks[1];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) acc[i] += (double)c3_bf(c3_snap(row[lane * CPL + i], bad));
+  for (int p = 0; p < PER; ++p) {
+    const int r = rg + p * RG;
+    if (r < rows)
+      buf[p] = *reinterpret_cast<const uint4*>(k + u * P.ks[0] + (int64_t)(base + r) * P.ks[1] + pc * 8);
   }
-  __shared__ double red[C3_T / 64][D];
+  double acc[8];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) red[wave][lane * CPL + i] = acc[i];
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0;
+  int bad = 0, tiny = 0;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    if (rg + p * RG >= rows) continue;
+    const uint4 v = c3_snap8(buf[p], bad);
+    tiny |= (v.x != buf[p].x) | (v.y != buf[p].y) | (v.z != buf[p].z) | (v.w != buf[p].w);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += (double)c3_bf(w[j] & 0xFFFFu);
+      acc[2 * j + 1] += (double)c3_bf(w[j] >> 16);
+    }
+  }
+  __shared__ double red[RG][D];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[rg][pc * 8 + j] = acc[j];
   if (bad) atomicOr(W.err, 1);
+  if (tiny) atomicOr(&W.tiny[u], 1);
   __syncthreads();
   for (int c = threadIdx.x; c < D; c += C3_T) {
-    double s = 0.0;
-    for (int w = 0; w < C3_T / 64; ++w) s += red[w][c];
-    atomicAdd(&W.rsum[(size_t)u * D + c], s);
+    double t = 0.0;
+    for (int g = 0; g < RG; ++g) t += red[g][c];
+    atomicAdd(&W.rsum[(size_t)u * D + c], t);
   }
 }
 
@@ -305,49 +383,141 @@ __global__ __launch_bounds__(C3_T) void c3_root_fin_kernel(C3Desc P, C3Index X, 
   const int u = blockIdx.x, n = c3_n(P, u);
   if (n == 0) return;
   for (int c = threadIdx.x; c < P.d; c += C3_T)
-    X.cent[(size_t)u * P.ncap * P.d + c] = c3_to_bf16(W.rsum[(size_t)u * P.d + c] / (double)n);
+    X.cent[(size_t)u * P.ncap * P.d + c] = c3_to_bf16(W.rsum[(size_t)u * P.d + c] * (1.0 / (double)n));
 }
 
 // ---------------------------------------------------------------------------
 // Build: nodes of 5..96 keys, all 8 iterations in one workgroup
 // ---------------------------------------------------------------------------
+// Bits [r0, r0 + m) (m <= 96) of a 256-bit row mask held in 4 words: the
+// first 64 in lo, the rest in hi.
+__device__ inline void c3_take_bits(const uint64_t* wd, int r0, int m, uint64_t& lo,
+                                    uint64_t& hi) {
+  auto at = [&](int pos) -> uint64_t {
+    const int w = pos >> 6, sh = pos & 63;
+    const uint64_t a = w < 4 ? wd[w] : 0ull;
+    const uint64_t b = w + 1 < 4 ? wd[w + 1] : 0ull;
+    return sh ? (a >> sh) | (b << (64 - sh)) : a;
+  };
+  lo = at(r0);
+  hi = at(r0 + 64);
+  if (m < 64) {
+    lo &= (1ull << m) - 1ull;
+    hi = 0ull;
+  } else {
+    hi &= (1ull << (m - 64)) - 1ull;
+  }
+}
+
+// a[0..7] += (or -=) the 8 columns at piece gl of every row r0 + bit of
+// (lo, hi); four rows' loads in flight at a time.  The values are on the
+// 2^-24 grid, so the sums are exact in any order.
+template <int RB, bool SUB>
+__device__ inline void c3_acc_rows(const unsigned char* sK, int r0, uint64_t lo, uint64_t hi,
+                                   int gl, double (&a)[8]) {
+  while (lo | hi) {
+    int rr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (lo) {
+        rr[q] = r0 + __builtin_ctzll(lo);
+        lo &= lo - 1ull;
+      } else if (hi) {
+        rr[q] = r0 + 64 + __builtin_ctzll(hi);
+        hi &= hi - 1ull;
+      } else {
+        rr[q] = -1;
+      }
+    }
+    uint4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (rr[q] >= 0) v[q] = *reinterpret_cast<const uint4*>(sK + rr[q] * RB + gl * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (rr[q] < 0) continue;
+      const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double x0 = (double)c3_bf(w[i] & 0xFFFFu), x1 = (double)c3_bf(w[i] >> 16);
+        if (SUB) {
+          a[2 * i] -= x0;
+          a[2 * i + 1] -= x1;
+        } else {
+          a[2 * i] += x0;
+          a[2 * i + 1] += x1;
+        }
+      }
+    }
+  }
+}
+
+// Hyperplane between two fp64 means for the 8 columns of piece gl (columns
+// 8 gl .. 8 gl + 7); the lanes of one node are LPN consecutive lanes.  b is
+// the pairwise sum of the products (adjacent columns, then adjacent pairs,
+// ...): the first three levels inside the lane, the rest across lanes.
+template <int LPN>
+__device__ inline float c3_bisect8(const double (&mu0)[8], const double (&mu1)[8], float (&w)[8]) {
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float wf = c3_round16((float)(mu1[i] - mu0[i]));
+    if (fabsf(wf) < 0x1p-100f) wf = 0.0f;
+    const float mf = (float)(0.5 * (mu0[i] + mu1[i]));
+    w[i] = wf;
+    p[i] = wf * mf;
+  }
+  float s = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+#pragma unroll
+  for (int o = 1; o < LPN; o <<= 1) s = s + __shfl_xor(s, o);
+  return s;
+}
+
 template <int D>
 __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Index X, C3Work W,
                                                         const uint16_t* __restrict__ k) {
   constexpr int RB = 2 * D + 16;          // padded LDS row: conflict-free row-per-lane reads
-  constexpr int CPL = D / 64;
-  constexpr int PPR = D / 8;              // 16-byte pieces per key row
+  constexpr int LPN = D / 8;              // lanes per node in the member-sum phase
+  constexpr int GPW = 64 / LPN;           // nodes per wave at a time
+  constexpr int NW = C3_T / 64;
+  constexpr int NPR = GPW * NW;           // nodes per round
+  constexpr int ROUNDS = (C3_HEADS + NPR - 1) / NPR;
   __shared__ __align__(16) unsigned char sK[C3_ROWS * RB];
   __shared__ __align__(16) float sW[C3_HEADS][D + 4];
   __shared__ float sB[C3_HEADS];
   __shared__ int sStart[C3_HEADS], sSize[C3_HEADS], sNode[C3_HEADS], sA0[C3_HEADS],
       sA1[C3_HEADS], sDead[C3_HEADS], sN0[C3_HEADS];
-  __shared__ int sIsHead[C3_CH];
   __shared__ int sPerm[C3_ROWS];
   __shared__ signed char sRowNode[C3_ROWS];
-  __shared__ unsigned char sFlag[C3_ROWS];
+  __shared__ uint64_t sBits[NW], sOld[NW];   // cluster-1 flag of every row, new and previous
   __shared__ int sNh;
 
-  const int u = blockIdx.x / P.nchunk, chn = blockIdx.x - u * P.nchunk;
+  const int g = W.clist[(dep & 1) * P.n_units * P.nchunk + blockIdx.x];
+  const int u = g / P.nchunk, chn = g - u * P.nchunk;
   const int n = c3_n(P, u), base = chn * C3_CH;
-  if (base >= n) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = lane / LPN, gl = lane % LPN;
   const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
+  if (tid == 0) W.cflag[g] = 0;
 
-  if (tid < C3_CH) sIsHead[tid] = (base + tid < n) ? W.head[ub + base + tid] : -1;
-  __syncthreads();
-  if (tid == 0) {
-    int nh = 0;
-    for (int t = 0; t < C3_CH; ++t) {
-      const int x = sIsHead[t];
-      if (x < 0) continue;
-      sNode[nh] = x;
-      sStart[nh] = base + t;
-      sSize[nh] = X.size[nb + x];
-      ++nh;
-    }
-    sNh = nh;
+  // Heads in position order: a ballot per wave of the chunk's positions.
+  static_assert(C3_CH == 128, "two waves cover a chunk");
+  if (tid < NW) sBits[tid] = 0ull;
+  int myhead = -1;
+  if (tid < C3_CH) {
+    myhead = (base + tid < n) ? W.head[ub + base + tid] : -1;
+    const uint64_t hb = __ballot(myhead >= 0);
+    if (lane == 0) sOld[wave] = hb;
   }
+  __syncthreads();
+  if (myhead >= 0) {
+    const uint64_t below = lane ? (sOld[wave] & ((1ull << lane) - 1ull)) : 0ull;
+    const int rank = (wave ? __popcll(sOld[0]) : 0) + __popcll(below);
+    sNode[rank] = myhead;
+    sStart[rank] = base + tid;
+    sSize[rank] = X.size[nb + myhead];
+  }
+  if (tid == 0) sNh = __popcll(sOld[0]) + __popcll(sOld[1]);
   __syncthreads();
   const int nh = sNh;
   if (nh == 0) return;
@@ -368,85 +538,99 @@ __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Ind
     sPerm[r] = j >= 0 ? X.perm[ub + row0 + r] : 0;
   }
   __syncthreads();
-  int bad = 0;
-  for (int i = tid; i < rows * PPR; i += C3_T) {
-    const int r = i / PPR, pc = i - r * PPR;
-    if (sRowNode[r] < 0) continue;
-    const uint16_t* src = k + u * P.ks[0] + (int64_t)sPerm[r] * P.ks[1] + pc * 8;
-    *reinterpret_cast<uint4*>(sK + r * RB + pc * 16) =
-        c3_snap8(*reinterpret_cast<const uint4*>(src), bad);
-  }
-  if (bad) atomicOr(W.err, 1);
+  c3_stage<D, C3_ROWS>(P, u, k, sPerm, sRowNode, rows, sK, W.tiny[u] != 0);
   __syncthreads();
 
-  // Initial hyperplanes from the two chosen members.
-  for (int j = wave; j < nh; j += C3_T / 64) {
-    const int r0 = sStart[j] - row0;
-    double m0[CPL], m1[CPL];
-    float w[CPL];
-    c3_row_vals<CPL>(sK + (r0 + sA0[j]) * RB, lane, m0);
-    c3_row_vals<CPL>(sK + (r0 + sA1[j]) * RB, lane, m1);
-    const float b = c3_bisect<CPL>(m0, m1, w);
+  // Each node is owned by LPN lanes (lane gl: columns 8 gl .. 8 gl + 7),
+  // which keep its total and its cluster-1 sum in registers.
+  double tot[ROUNDS][8], s1[ROUNDS][8];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) sW[j][lane * CPL + i] = w[i];
-    if (lane == 0) sB[j] = b;
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    const int j = rd * NPR + wave * GPW + grp;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tot[rd][i] = s1[rd][i] = 0.0;
+    if (j >= nh) continue;
+    const int r0 = sStart[j] - row0, m = sSize[j];
+    const uint64_t lo = m >= 64 ? ~0ull : (1ull << m) - 1ull;
+    const uint64_t hi = m > 64 ? (1ull << (m - 64)) - 1ull : 0ull;
+    c3_acc_rows<RB, false>(sK, r0, lo, hi, gl, tot[rd]);
+    double m0[8], m1[8];
+    float w[8];
+    const uint4 v0 = *reinterpret_cast<const uint4*>(sK + (r0 + sA0[j]) * RB + gl * 16);
+    const uint4 v1 = *reinterpret_cast<const uint4*>(sK + (r0 + sA1[j]) * RB + gl * 16);
+    const uint32_t h0[4] = {v0.x, v0.y, v0.z, v0.w}, h1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m0[2 * i] = (double)c3_bf(h0[i] & 0xFFFFu);
+      m0[2 * i + 1] = (double)c3_bf(h0[i] >> 16);
+      m1[2 * i] = (double)c3_bf(h1[i] & 0xFFFFu);
+      m1[2 * i + 1] = (double)c3_bf(h1[i] >> 16);
+    }
+    const float b = c3_bisect8<LPN>(m0, m1, w);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sW[j][gl * 8 + i] = w[i];
+    if (gl == 0) sB[j] = b;
   }
   __syncthreads();
 
   for (int it = 0; it < C3_ITERS; ++it) {
-    for (int r = tid; r < rows; r += C3_T) {
-      const int j = sRowNode[r];
-      if (j >= 0 && !sDead[j]) sFlag[r] = c3_plane<D>(sK + r * RB, &sW[j][0]) > sB[j] ? 1 : 0;
+    // Hyperplane test, a thread per row; one ballot word per wave.
+    {
+      const int r = tid;
+      const int j = r < rows ? sRowNode[r] : -1;
+      const bool f = j >= 0 && !sDead[j] && c3_plane<D>(sK + r * RB, &sW[j][0]) > sB[j];
+      const uint64_t word = __ballot(f);
+      if (lane == 0) {
+        sOld[wave] = sBits[wave];
+        sBits[wave] = word;
+      }
     }
     __syncthreads();
-    for (int j = wave; j < nh; j += C3_T / 64) {
-      if (sDead[j]) continue;
+    // New means from the rows whose cluster changed (exact running sums).
+#pragma unroll
+    for (int rd = 0; rd < ROUNDS; ++rd) {
+      const int j = rd * NPR + wave * GPW + grp;
+      if (j >= nh || sDead[j]) continue;
       const int r0 = sStart[j] - row0, m = sSize[j];
-      double a0[CPL], a1[CPL];
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) a0[i] = a1[i] = 0.0;
-      int n1 = 0;
-      for (int r = r0; r < r0 + m; ++r) {
-        double v[CPL];
-        c3_row_vals<CPL>(sK + r * RB, lane, v);
-        if (__builtin_amdgcn_readfirstlane(sFlag[r])) {
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) a1[i] += v[i];
-          ++n1;
-        } else {
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) a0[i] += v[i];
-        }
-      }
+      uint64_t nlo, nhi, olo, ohi;
+      c3_take_bits(sBits, r0, m, nlo, nhi);
+      c3_take_bits(sOld, r0, m, olo, ohi);
+      c3_acc_rows<RB, false>(sK, r0, nlo & ~olo, nhi & ~ohi, gl, s1[rd]);
+      c3_acc_rows<RB, true>(sK, r0, olo & ~nlo, ohi & ~nhi, gl, s1[rd]);
+      const int n1 = __popcll(nlo) + __popcll(nhi);
       if (n1 == 0 || n1 == m) {
-        if (lane == 0) {
+        if (gl == 0) {
           sDead[j] = 1;
           W.res_n0[ub + sStart[j]] = -1;
         }
         continue;
       }
-      double mu0[CPL], mu1[CPL];
+      const double i0 = 1.0 / (double)(m - n1), i1 = 1.0 / (double)n1;
+      double mu0[8], mu1[8];
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        mu0[i] = a0[i] / (double)(m - n1);
-        mu1[i] = a1[i] / (double)n1;
+      for (int i = 0; i < 8; ++i) {
+        mu0[i] = (tot[rd][i] - s1[rd][i]) * i0;
+        mu1[i] = s1[rd][i] * i1;
       }
       if (it + 1 < C3_ITERS) {
-        float w[CPL];
-        const float b = c3_bisect<CPL>(mu0, mu1, w);
+        float w[8];
+        const float b = c3_bisect8<LPN>(mu0, mu1, w);
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) sW[j][lane * CPL + i] = w[i];
-        if (lane == 0) sB[j] = b;
+        for (int i = 0; i < 8; ++i) sW[j][gl * 8 + i] = w[i];
+        if (gl == 0) sB[j] = b;
       } else {
         const int n0 = m - n1;
-        uint16_t* c0 = W.cres + (ub + sStart[j]) * D;
-        uint16_t* c1 = W.cres + (ub + sStart[j] + n0) * D;
+        uint32_t c0[4], c1[4];
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-          c0[lane * CPL + i] = c3_to_bf16(mu0[i]);
-          c1[lane * CPL + i] = c3_to_bf16(mu1[i]);
+        for (int i = 0; i < 4; ++i) {
+          c0[i] = (uint32_t)c3_to_bf16(mu0[2 * i]) | ((uint32_t)c3_to_bf16(mu0[2 * i + 1]) << 16);
+          c1[i] = (uint32_t)c3_to_bf16(mu1[2 * i]) | ((uint32_t)c3_to_bf16(mu1[2 * i + 1]) << 16);
         }
-        if (lane == 0) {
+        *reinterpret_cast<uint4*>(W.cres + (ub + sStart[j]) * D + gl * 8) =
+            make_uint4(c0[0], c0[1], c0[2], c0[3]);
+        *reinterpret_cast<uint4*>(W.cres + (ub + sStart[j] + n0) * D + gl * 8) =
+            make_uint4(c1[0], c1[1], c1[2], c1[3]);
+        if (gl == 0) {
           sN0[j] = n0;
           W.res_n0[ub + sStart[j]] = n0;
         }
@@ -460,10 +644,12 @@ __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Ind
   for (int r = tid; r < rows; r += C3_T) {
     const int j = sRowNode[r];
     if (j < 0 || sDead[j]) continue;
-    const int f = sFlag[r];
     const int r0 = sStart[j] - row0;
-    int rank = 0;
-    for (int q = r0; q < r; ++q) rank += sFlag[q] == f;
+    uint64_t lo, hi;
+    c3_take_bits(sBits, r0, r - r0 + 1, lo, hi);   // bits r0 .. r
+    const int f = (int)((r - r0 < 64 ? lo >> (r - r0) : hi >> (r - r0 - 64)) & 1ull);
+    const int ones = __popcll(lo) + __popcll(hi) - f;   // ones before r
+    const int rank = f ? ones : (r - r0) - ones;
     const int np = sStart[j] + (f ? sN0[j] + rank : rank);
     X.perm[ub + np] = sPerm[r];
   }
@@ -507,85 +693,136 @@ __global__ __launch_bounds__(64) void c3_span_init_kernel(C3Desc P, int dep, int
   }
 }
 
-// One 128-key block of one span node: hyperplane test, block sums, atomics.
+// Column sums of rows base + bit of a uniform 32-bit mask, lanes over the
+// columns (CPL each); four rows' loads in flight at a time.  Exact.
+template <int RB, int CPL, bool SUB>
+__device__ inline void c3_acc_cols(const unsigned char* sK, int base, uint32_t mask, int lane,
+                                   double (&a)[CPL]) {
+  while (mask) {
+    int rr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      rr[q] = mask ? base + __builtin_ctz(mask) : -1;
+      mask &= mask ? mask - 1u : 0u;
+    }
+    double v[4][CPL];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (rr[q] >= 0) c3_row_vals<CPL>(sK + rr[q] * RB, lane, v[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (rr[q] >= 0)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) a[i] = SUB ? a[i] - v[q][i] : a[i] + v[q][i];
+  }
+}
+
+// C3_SPB consecutive 128-key blocks of one span node per workgroup: the
+// next block's keys are loaded into registers while the current one is
+// tested.  Iteration 0 adds every row to the node's total and the rows of
+// cluster 1 to its cluster-1 sum; later iterations add and subtract only the
+// rows that changed cluster (the previous cluster of each position is kept
+// in the flags array).  One set of atomics per workgroup.
+#define C3_SPB 4
 template <int D>
-__global__ __launch_bounds__(C3_T) void c3_span_iter_kernel(C3Desc P, int par, C3Index X,
+__global__ __launch_bounds__(C3_T) void c3_span_iter_kernel(C3Desc P, int par, int it, C3Index X,
                                                             C3Work W, const uint16_t* __restrict__ k) {
-  constexpr int RB = 2 * D + 16, CPL = D / 64, PPR = D / 8;
+  constexpr int RB = 2 * D + 16, CPL = D / 64, PPR = D / 8, NW = C3_T / 64;
+  constexpr int PER = C3_CH * PPR / C3_T;       // 16-byte pieces per thread and block
   __shared__ __align__(16) unsigned char sK[C3_CH * RB];
   __shared__ __align__(16) float sWv[D + 4];
-  __shared__ unsigned char sFlag[C3_CH];
-  __shared__ double red0[C3_T / 64][D], red1[C3_T / 64][D];
-  __shared__ int sN1[C3_T / 64];
+  __shared__ uint64_t sNew[C3_CH / 64], sOld[C3_CH / 64];
+  __shared__ double red0[NW][D], red1[NW][D];
+  __shared__ int sPerm[C3_SPB * C3_CH];
   const int s = blockIdx.x;
   if (!W.salive[s]) return;
   const int2 un = W.snode[par * W.smax + s];
   const int u = un.x, x = un.y;
   const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
   const int st = X.start[nb + x], m = X.size[nb + x];
-  const int p0 = st + blockIdx.y * C3_CH;
-  if (p0 >= st + m) return;
-  const int rows = min(C3_CH, st + m - p0);
+  const int q0 = st + blockIdx.y * (C3_SPB * C3_CH);
+  if (q0 >= st + m) return;
+  const int total = min(C3_SPB * C3_CH, st + m - q0);
+  const int nblk = (total + C3_CH - 1) / C3_CH;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool tiny = W.tiny[u] != 0;
+  for (int i = tid; i < total; i += C3_T) sPerm[i] = X.perm[ub + q0 + i];
   for (int c = tid; c < D; c += C3_T) sWv[c] = W.sw[(size_t)s * D + c];
   const float b = W.sb[s];
-  int bad = 0;
-  for (int i = tid; i < rows * PPR; i += C3_T) {
-    const int r = i / PPR, pc = i - r * PPR;
-    const uint16_t* src = k + u * P.ks[0] + (int64_t)X.perm[ub + p0 + r] * P.ks[1] + pc * 8;
-    *reinterpret_cast<uint4*>(sK + r * RB + pc * 16) =
-        c3_snap8(*reinterpret_cast<const uint4*>(src), bad);
-  }
-  if (bad) atomicOr(W.err, 1);
   __syncthreads();
-  if (tid < rows) {
-    const unsigned char f = c3_plane<D>(sK + tid * RB, sWv) > b ? 1 : 0;
-    sFlag[tid] = f;
-    W.flags[ub + p0 + tid] = f;
-  }
-  __syncthreads();
+  uint4 buf[PER];
+  auto load = [&](int blk) {
+    const int rows = min(C3_CH, total - blk * C3_CH);
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int i = tid + p * C3_T, r = i / PPR, pc = i - r * PPR;
+      if (r < rows)
+        buf[p] = *reinterpret_cast<const uint4*>(k + u * P.ks[0] +
+                                                 (int64_t)sPerm[blk * C3_CH + r] * P.ks[1] + pc * 8);
+    }
+  };
+  load(0);
   double a0[CPL], a1[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) a0[i] = a1[i] = 0.0;
-  int n1 = 0;
-  const int per = (rows + C3_T / 64 - 1) / (C3_T / 64);
-  const int rb = wave * per, re = min(rows, rb + per);
-  for (int r = rb; r < re; ++r) {
-    double v[CPL];
-    c3_row_vals<CPL>(sK + r * RB, lane, v);
-    if (__builtin_amdgcn_readfirstlane(sFlag[r])) {
+  int dn1 = 0;
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int rows = min(C3_CH, total - blk * C3_CH);
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) a1[i] += v[i];
-      ++n1;
-    } else {
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) a0[i] += v[i];
+    for (int p = 0; p < PER; ++p) {
+      const int i = tid + p * C3_T, r = i / PPR, pc = i - r * PPR;
+      if (r < rows)
+        *reinterpret_cast<uint4*>(sK + r * RB + pc * 16) = tiny ? c3_snap8_fast(buf[p]) : buf[p];
     }
+    __syncthreads();
+    if (blk + 1 < nblk) load(blk + 1);
+    if (tid < C3_CH) {
+      const size_t pos = ub + q0 + blk * C3_CH + tid;
+      const bool f = tid < rows && c3_plane<D>(sK + tid * RB, sWv) > b;
+      const bool o = tid < rows && it > 0 && W.flags[pos] != 0;
+      if (tid < rows) W.flags[pos] = f ? 1 : 0;
+      const uint64_t wn = __ballot(f), wo = __ballot(o);
+      if (lane == 0) {
+        sNew[wave] = wn;
+        sOld[wave] = wo;
+      }
+    }
+    __syncthreads();
+    // Wave w handles rows 32w .. 32w + 31, lanes over the columns.
+    const int rb = wave * 32;
+    const int nr = max(0, min(32, rows - rb));
+    const uint32_t live = nr >= 32 ? 0xFFFFFFFFu : (1u << nr) - 1u;
+    const uint32_t nw = (uint32_t)(sNew[rb >> 6] >> (rb & 63)) & live;
+    const uint32_t ow = (uint32_t)(sOld[rb >> 6] >> (rb & 63)) & live;
+    if (it == 0) {
+      c3_acc_cols<RB, CPL, false>(sK, rb, live, lane, a0);
+      c3_acc_cols<RB, CPL, false>(sK, rb, nw, lane, a1);
+    } else {
+      c3_acc_cols<RB, CPL, false>(sK, rb, nw & ~ow, lane, a1);
+      c3_acc_cols<RB, CPL, true>(sK, rb, ow & ~nw, lane, a1);
+    }
+    dn1 += __popc(nw) - __popc(ow);
+    __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     red0[wave][lane * CPL + i] = a0[i];
     red1[wave][lane * CPL + i] = a1[i];
   }
-  if (lane == 0) sN1[wave] = n1;
+  __shared__ int sDn[NW];
+  if (lane == 0) sDn[wave] = dn1;
   __syncthreads();
-  for (int c = tid; c < D; c += C3_T) {
-    double t0 = 0.0, t1 = 0.0;
-    for (int w = 0; w < C3_T / 64; ++w) {
-      t0 += red0[w][c];
-      t1 += red1[w][c];
-    }
-    atomicAdd(&W.s0[(size_t)s * D + c], t0);
-    atomicAdd(&W.s1[(size_t)s * D + c], t1);
+  for (int c = tid; c < (it == 0 ? 2 * D : D); c += C3_T) {
+    const int h = c < D ? 1 : 0, cc = c < D ? c : c - D;
+    double t = 0.0;
+    for (int w = 0; w < NW; ++w) t += h ? red1[w][cc] : red0[w][cc];
+    atomicAdd(h ? &W.s1[(size_t)s * D + cc] : &W.s0[(size_t)s * D + cc], t);
   }
-  if (tid == 0) {
-    int t = 0;
-    for (int w = 0; w < C3_T / 64; ++w) t += sN1[w];
-    atomicAdd(&W.sn1[s], t);
-  }
+  if (tid == 0) atomicAdd(&W.sn1[s], sDn[0] + sDn[1] + sDn[2] + sDn[3]);
 }
 
-// New means of a span node; the last iteration records the split.
+// New means of a span node from its total (s0) and running cluster-1 sum
+// (s1) and count; the last iteration records the split.
 template <int D>
 __global__ __launch_bounds__(64) void c3_span_fin_kernel(C3Desc P, int par, int last, C3Index X,
                                                          C3Work W) {
@@ -604,24 +841,20 @@ __global__ __launch_bounds__(64) void c3_span_fin_kernel(C3Desc P, int par, int 
     }
     return;
   }
+  const double i0 = 1.0 / (double)(m - n1), i1 = 1.0 / (double)n1;
   double mu0[CPL], mu1[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const size_t o = (size_t)s * D + lane * CPL + i;
-    mu0[i] = W.s0[o] / (double)(m - n1);
-    mu1[i] = W.s1[o] / (double)n1;
-    W.s0[o] = 0.0;
-    W.s1[o] = 0.0;
+    mu0[i] = (W.s0[o] - W.s1[o]) * i0;
+    mu1[i] = W.s1[o] * i1;
   }
   if (!last) {
     float w[CPL];
     const float b = c3_bisect<CPL>(mu0, mu1, w);
 #pragma unroll
     for (int i = 0; i < CPL; ++i) W.sw[(size_t)s * D + lane * CPL + i] = w[i];
-    if (lane == 0) {
-      W.sb[s] = b;
-      W.sn1[s] = 0;
-    }
+    if (lane == 0) W.sb[s] = b;
   } else {
     const int n0 = m - n1;
     uint16_t* c0 = W.cres + (ub + st) * D;
@@ -705,6 +938,7 @@ __global__ __launch_bounds__(C3_BIG) void c3_ids_kernel(C3Desc P, int dep, C3Ind
           ++cand;
           if (cm[side] <= C3_MLOC) {
             W.head[ub + cs[side]] = l + side;
+            c3_list_chunk(P, W, u, cs[side], dep + 1);
           } else {
             big = max(big, cm[side]);
             const int slot = atomicAdd(&cnt[1], 1);
@@ -1230,9 +1464,11 @@ static void c3_layout(const C3Desc& V, kvc_c3_layout* L) {
   const size_t S = (size_t)c3_smax(V);
   L->build_workspace_bytes = c3_up(2 * U * CAP * D) + c3_up(4 * U * CAP) + c3_up(U * CAP) +
                              c3_up(4 * U * CAP) + c3_up(4 * U * CAP) +
-                             c3_up(4 * U * (C3_MAXD + 2)) + c3_up(8 * U * D) + c3_up(8 * 2 * S) +
+                             c3_up(4 * U * (C3_MAXD + 2)) + c3_up(8 * U * D) + c3_up(4 * U) +
+                             c3_up(8 * 2 * S) +
                              c3_up(4 * S * D) + c3_up(4 * S) + 2 * c3_up(8 * S * D) + c3_up(4 * S) +
-                             c3_up(4 * S) + c3_up(16 * (C3_MAXD + 1)) + c3_up(4);
+                             c3_up(4 * S) + c3_up(16 * (C3_MAXD + 1)) + c3_up(4) +
+                             c3_up(4 * U * V.nchunk) + c3_up(8 * U * V.nchunk);
   L->step_workspace_bytes = c3_up(4 * U * CAP);
 }
 
@@ -1271,6 +1507,7 @@ static C3Work c3_work(const C3Desc& V, void* ws) {
   W.ptmp = (int32_t*)p;    p += c3_up(4 * U * CAP);
   W.lvl = (int32_t*)p;     p += c3_up(4 * U * (C3_MAXD + 2));
   W.rsum = (double*)p;     p += c3_up(8 * U * D);
+  W.tiny = (int32_t*)p;    p += c3_up(4 * U);
   W.snode = (int2*)p;      p += c3_up(8 * 2 * S);
   W.sw = (float*)p;        p += c3_up(4 * S * D);
   W.sb = (float*)p;        p += c3_up(4 * S);
@@ -1279,7 +1516,9 @@ static C3Work c3_work(const C3Desc& V, void* ws) {
   W.sn1 = (int32_t*)p;     p += c3_up(4 * S);
   W.salive = (int32_t*)p;  p += c3_up(4 * S);
   W.cnt = (int32_t*)p;     p += c3_up(16 * (C3_MAXD + 1));
-  W.err = (int32_t*)p;
+  W.err = (int32_t*)p;     p += c3_up(4);
+  W.cflag = (int32_t*)p;   p += c3_up(4 * U * V.nchunk);
+  W.clist = (int32_t*)p;
   W.smax = (int32_t)S;
   return W;
 }
@@ -1330,10 +1569,11 @@ extern "C" kvc_status kvc_c3_build(const kvc_c3_problem* prob, const kvc_c3_para
   hipLaunchKernelGGL(c3_root_fin_kernel, dim3(U), dim3(C3_T), 0, st, V, X, W);
   if ((e = hipGetLastError()) != hipSuccess) return c3_hip(e);
   // Depth 0 work, known on the host.
-  int cand = 0, span = 0, big = 0;
+  int cand = 0, span = 0, big = 0, chunks = 0;
   for (int u = 0; u < V.n_units; ++u) {
     const int n = V.len[u / V.upseq];
     if (n > C3_LEAF) ++cand;
+    if (n > C3_LEAF && n <= C3_MLOC) ++chunks;
     if (n > C3_MLOC) {
       ++span;
       big = std::max(big, n);
@@ -1341,13 +1581,14 @@ extern "C" kvc_status kvc_c3_build(const kvc_c3_problem* prob, const kvc_c3_para
   }
   for (int dep = 0; dep < C3_MAXD && cand > 0; ++dep) {
     const int par = dep & 1;
-    if (cand > span)
-      C3_LAUNCH(V.d, c3_local_kernel, dim3(U * V.nchunk), dim3(C3_T), V, dep, X, W, kk);
+    if (chunks > 0)
+      C3_LAUNCH(V.d, c3_local_kernel, dim3((unsigned)chunks), dim3(C3_T), V, dep, X, W, kk);
     if (span > 0) {
-      const dim3 g1((unsigned)span), g2((unsigned)span, (unsigned)((big + C3_CH - 1) / C3_CH));
+      const dim3 g1((unsigned)span),
+          g2((unsigned)span, (unsigned)((big + C3_SPB * C3_CH - 1) / (C3_SPB * C3_CH)));
       C3_LAUNCH(V.d, c3_span_init_kernel, g1, dim3(64), V, dep, par, X, W, kk);
       for (int it = 0; it < C3_ITERS; ++it) {
-        C3_LAUNCH(V.d, c3_span_iter_kernel, g2, dim3(C3_T), V, par, X, W, kk);
+        C3_LAUNCH(V.d, c3_span_iter_kernel, g2, dim3(C3_T), V, par, it, X, W, kk);
         C3_LAUNCH(V.d, c3_span_fin_kernel, g1, dim3(64), V, par, it + 1 == C3_ITERS ? 1 : 0, X, W);
       }
       hipLaunchKernelGGL(c3_span_part_kernel, g1, dim3(C3_BIG), 0, st, V, par, X, W);
@@ -1361,6 +1602,7 @@ extern "C" kvc_status kvc_c3_build(const kvc_c3_problem* prob, const kvc_c3_para
     cand = h[0];
     span = h[1];
     big = h[2];
+    chunks = h[3];
     if (span > W.smax) return KVC_ERR_UNSUPPORTED;  // cannot happen: span nodes are disjoint
   }
   hipLaunchKernelGGL(c3_frontier_kernel, dim3(U), dim3(C3_BIG), 0, st, V, X, S, W);

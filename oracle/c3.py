@@ -32,7 +32,8 @@ reproduce exactly (readings, each listed in the design doc):
     a key on it joins cluster 0).  Every k_c w_c is exact in fp32, so a
     fused multiply-add gives the same s(k);
   * a split that leaves a cluster empty at any iteration is abandoned (the
-    node stays a leaf); new means are exact sums over the count (fp64);
+    node stays a leaf); a mean is the exact member sum times the fp64
+    reciprocal of the count (1/n rounded once, then one rounded product);
   * "seed 0": the initial centroids are two distinct member keys chosen by
     the SplitMix64 mixing function (Steele, Lea and Flood, "Fast splittable
     pseudorandom number generators", OOPSLA 2014) of (seed, cache, depth,
@@ -186,8 +187,8 @@ def _level_two_means(Xq, seg, sizes, a0, a1):
             n1 = np.bincount(seg, weights=to1, minlength=len(sizes)).astype(np.int64)
             alive &= (n1 > 0) & (n1 < sizes)
             S1 = np.add.reduceat(Xq * to1[:, None], offs, axis=0)
-            mu1 = np.where(alive[:, None], S1 / n1[:, None], mu1)
-            mu0 = np.where(alive[:, None], (S - S1) / (sizes - n1)[:, None], mu0)
+            mu1 = np.where(alive[:, None], S1 * (1.0 / n1)[:, None], mu1)
+            mu0 = np.where(alive[:, None], (S - S1) * (1.0 / (sizes - n1))[:, None], mu0)
     return alive, to1, mu0, mu1
 
 
@@ -202,7 +203,7 @@ def build_tree(K, cache: int = 0, seed: int = 0) -> Tree:
         z = np.zeros(0, np.int64)
         return Tree(z, z, z, z, z, np.zeros((0, d), np.float32), perm)
     start, size, left, parent, depth = [0], [n], [-1], [-1], [0]
-    means = [Kq.sum(axis=0) / n]
+    means = [Kq.sum(axis=0) * (1.0 / n)]
     lo, hi = 0, 1
     for dep in range(MAX_DEPTH):
         cand = [x for x in range(lo, hi) if size[x] > LEAF]

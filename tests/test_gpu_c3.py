@@ -247,6 +247,24 @@ def test_other_lambda_and_swaps(lam, R):
     run_steps(dev, 3, trees)
 
 
+def test_tiny_and_zero_keys_are_snapped_alike():
+    # Keys below 2^-17 are moved to the 2^-24 grid before any sum; zeros and
+    # subnormal bf16 values as well.
+    cfg = synth.C3_CONFIGS["c3_tiny"]
+    k, v = synth.c3_problem(cfg)
+    r = np.random.default_rng(5)
+    tiny = (r.standard_normal((60, cfg.head_dim)) * 3e-6).astype(np.float32)
+    tiny[::7] = 0.0
+    tiny[3, :5] = np.float32(2.0 ** -130)
+    for u in range(k.shape[0]):
+        k[u, 100:160] = synth.f32_to_bf16_bits(tiny)
+        k[u, 200:210, ::3] = 0
+    dev = C3Dev(cfg, k, v)
+    dev.build()
+    for u in range(dev.U):
+        assert_tree_equal(dev, u, oracle_tree(dev, u))
+
+
 def test_key_out_of_range_is_reported():
     cfg = synth.C3_CONFIGS["c3_tiny"]
     k, v = synth.c3_problem(cfg)
