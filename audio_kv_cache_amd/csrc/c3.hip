@@ -93,7 +93,8 @@ struct C3Work {
   double* s0;        // [smax][d]
   double* s1;        // [smax][d]
   int32_t* sn1;      // [smax]
-  int32_t* salive;   // [smax]
+  int32_t* salive;   // [smax]: 1 iterating, 2 converged (split found), 0 abandoned
+  int32_t* sflip;    // [smax]: rows that changed cluster in the current iteration
   int32_t* cnt;      // [C3_MAXD + 1][4]: candidates, span nodes, largest span
                      // node, chunks holding local nodes
   int32_t* cflag;    // [U * nchunk]: chunk already listed for the next depth
@@ -490,7 +491,9 @@ __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Ind
   __shared__ int sPerm[C3_ROWS];
   __shared__ signed char sRowNode[C3_ROWS];
   __shared__ uint64_t sBits[NW], sOld[NW];   // cluster-1 flag of every row, new and previous
-  __shared__ int sNh;
+  __shared__ double sInv[C3_MLOC + 1];        // 1 / k, correctly rounded
+  __shared__ int sConv[C3_HEADS];             // 1 once the partition stopped changing
+  __shared__ int sNh, sLeft[2];
 
   const int g = W.clist[(dep & 1) * P.n_units * P.nchunk + blockIdx.x];
   const int u = g / P.nchunk, chn = g - u * P.nchunk;
@@ -529,7 +532,9 @@ __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Ind
     sA0[tid] = a0;
     sA1[tid] = a1;
     sDead[tid] = 0;
+    sConv[tid] = 0;
   }
+  if (tid >= 1 && tid <= C3_MLOC) sInv[tid] = 1.0 / (double)tid;
   for (int r = tid; r < rows; r += C3_T) {
     int j = -1;
     for (int h = 0; h < nh; ++h)
@@ -541,63 +546,104 @@ __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Ind
   c3_stage<D, C3_ROWS>(P, u, k, sPerm, sRowNode, rows, sK, W.tiny[u] != 0);
   __syncthreads();
 
-  // Each node is owned by LPN lanes (lane gl: columns 8 gl .. 8 gl + 7),
-  // which keep its total and its cluster-1 sum in registers.
+  // A node is owned by gpn groups of LPN lanes (lane gl: columns
+  // 8 gl .. 8 gl + 7; group part p: the node's rows r0 + p, r0 + p + gpn,
+  // ...), which keep partial totals and cluster-1 sums in registers and
+  // combine them with shuffles (exact).  Few nodes get more groups each.
+  const int gpn = (nh * 4 <= NPR) ? 4 : ((nh * 2 <= NPR) ? 2 : 1);
+  const int part = grp % gpn;
+  const uint64_t pat =
+      gpn == 1 ? ~0ull : ((gpn == 2 ? 0x5555555555555555ull : 0x1111111111111111ull) << part);
+  auto combine = [&](const double (&a)[8], double (&out)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = a[i];
+    if (gpn >= 2)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] += __shfl_xor(out[i], LPN);
+    if (gpn >= 4)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] += __shfl_xor(out[i], 2 * LPN);
+  };
   double tot[ROUNDS][8], s1[ROUNDS][8];
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
-    const int j = rd * NPR + wave * GPW + grp;
+    const int j = (rd * NPR + wave * GPW + grp) / gpn;
+    const bool valid = j < nh;
+    double pt[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tot[rd][i] = s1[rd][i] = 0.0;
-    if (j >= nh) continue;
-    const int r0 = sStart[j] - row0, m = sSize[j];
-    const uint64_t lo = m >= 64 ? ~0ull : (1ull << m) - 1ull;
-    const uint64_t hi = m > 64 ? (1ull << (m - 64)) - 1ull : 0ull;
-    c3_acc_rows<RB, false>(sK, r0, lo, hi, gl, tot[rd]);
-    double m0[8], m1[8];
-    float w[8];
-    const uint4 v0 = *reinterpret_cast<const uint4*>(sK + (r0 + sA0[j]) * RB + gl * 16);
-    const uint4 v1 = *reinterpret_cast<const uint4*>(sK + (r0 + sA1[j]) * RB + gl * 16);
-    const uint32_t h0[4] = {v0.x, v0.y, v0.z, v0.w}, h1[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m0[2 * i] = (double)c3_bf(h0[i] & 0xFFFFu);
-      m0[2 * i + 1] = (double)c3_bf(h0[i] >> 16);
-      m1[2 * i] = (double)c3_bf(h1[i] & 0xFFFFu);
-      m1[2 * i + 1] = (double)c3_bf(h1[i] >> 16);
+    for (int i = 0; i < 8; ++i) pt[i] = s1[rd][i] = 0.0;
+    int r0 = 0, m = 0;
+    if (valid) {
+      r0 = sStart[j] - row0;
+      m = sSize[j];
+      const uint64_t lo = m >= 64 ? ~0ull : (1ull << m) - 1ull;
+      const uint64_t hi = m > 64 ? (1ull << (m - 64)) - 1ull : 0ull;
+      c3_acc_rows<RB, false>(sK, r0, lo & pat, hi & pat, gl, pt);
     }
-    const float b = c3_bisect8<LPN>(m0, m1, w);
+    combine(pt, tot[rd]);
+    if (valid && part == 0) {
+      double m0[8], m1[8];
+      float w[8];
+      const uint4 v0 = *reinterpret_cast<const uint4*>(sK + (r0 + sA0[j]) * RB + gl * 16);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(sK + (r0 + sA1[j]) * RB + gl * 16);
+      const uint32_t h0[4] = {v0.x, v0.y, v0.z, v0.w}, h1[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sW[j][gl * 8 + i] = w[i];
-    if (gl == 0) sB[j] = b;
+      for (int i = 0; i < 4; ++i) {
+        m0[2 * i] = (double)c3_bf(h0[i] & 0xFFFFu);
+        m0[2 * i + 1] = (double)c3_bf(h0[i] >> 16);
+        m1[2 * i] = (double)c3_bf(h1[i] & 0xFFFFu);
+        m1[2 * i + 1] = (double)c3_bf(h1[i] >> 16);
+      }
+      const float b = c3_bisect8<LPN>(m0, m1, w);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sW[j][gl * 8 + i] = w[i];
+      if (gl == 0) sB[j] = b;
+    }
   }
   __syncthreads();
 
+  // Iterations stop early for a node whose partition repeats: its means,
+  // and so every later partition, are then the same (exact arithmetic).
   for (int it = 0; it < C3_ITERS; ++it) {
     // Hyperplane test, a thread per row; one ballot word per wave.
     {
       const int r = tid;
       const int j = r < rows ? sRowNode[r] : -1;
-      const bool f = j >= 0 && !sDead[j] && c3_plane<D>(sK + r * RB, &sW[j][0]) > sB[j];
+      const uint64_t prev = sBits[wave];
+      bool f;
+      if (j >= 0 && sConv[j])
+        f = (prev >> lane) & 1ull;
+      else
+        f = j >= 0 && !sDead[j] && c3_plane<D>(sK + r * RB, &sW[j][0]) > sB[j];
       const uint64_t word = __ballot(f);
       if (lane == 0) {
-        sOld[wave] = sBits[wave];
+        sOld[wave] = prev;
         sBits[wave] = word;
       }
+      if (tid == 0) sLeft[it & 1] = 0;
     }
     __syncthreads();
     // New means from the rows whose cluster changed (exact running sums).
 #pragma unroll
     for (int rd = 0; rd < ROUNDS; ++rd) {
-      const int j = rd * NPR + wave * GPW + grp;
-      if (j >= nh || sDead[j]) continue;
-      const int r0 = sStart[j] - row0, m = sSize[j];
-      uint64_t nlo, nhi, olo, ohi;
-      c3_take_bits(sBits, r0, m, nlo, nhi);
-      c3_take_bits(sOld, r0, m, olo, ohi);
-      c3_acc_rows<RB, false>(sK, r0, nlo & ~olo, nhi & ~ohi, gl, s1[rd]);
-      c3_acc_rows<RB, true>(sK, r0, olo & ~nlo, ohi & ~nhi, gl, s1[rd]);
-      const int n1 = __popcll(nlo) + __popcll(nhi);
+      const int j = (rd * NPR + wave * GPW + grp) / gpn;
+      const bool live = j < nh && !sDead[j] && !sConv[j];
+      int m = 1, n1 = 0;
+      bool same = false;
+      if (live) {
+        const int r0 = sStart[j] - row0;
+        m = sSize[j];
+        uint64_t nlo, nhi, olo, ohi;
+        c3_take_bits(sBits, r0, m, nlo, nhi);
+        c3_take_bits(sOld, r0, m, olo, ohi);
+        c3_acc_rows<RB, false>(sK, r0, nlo & ~olo & pat, nhi & ~ohi & pat, gl, s1[rd]);
+        c3_acc_rows<RB, true>(sK, r0, olo & ~nlo & pat, ohi & ~nhi & pat, gl, s1[rd]);
+        n1 = __popcll(nlo) + __popcll(nhi);
+        same = it > 0 && nlo == olo && nhi == ohi;
+      }
+      double sf[8];
+      combine(s1[rd], sf);
+      if (!live || part != 0) continue;
       if (n1 == 0 || n1 == m) {
         if (gl == 0) {
           sDead[j] = 1;
@@ -605,14 +651,16 @@ __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Ind
         }
         continue;
       }
-      const double i0 = 1.0 / (double)(m - n1), i1 = 1.0 / (double)n1;
+      const double i0 = sInv[m - n1], i1 = sInv[n1];
       double mu0[8], mu1[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        mu0[i] = (tot[rd][i] - s1[rd][i]) * i0;
-        mu1[i] = s1[rd][i] * i1;
+        mu0[i] = (tot[rd][i] - sf[i]) * i0;
+        mu1[i] = sf[i] * i1;
       }
-      if (it + 1 < C3_ITERS) {
+      if (same && gl == 0) sConv[j] = 1;
+      if (!same && gl == 0) sLeft[it & 1] = 1;
+      if (it + 1 < C3_ITERS && !same) {
         float w[8];
         const float b = c3_bisect8<LPN>(mu0, mu1, w);
 #pragma unroll
@@ -637,6 +685,7 @@ __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Ind
       }
     }
     __syncthreads();
+    if (sLeft[it & 1] == 0) break;
   }
 
   // Stable partition of each split node's range, in place (this workgroup
@@ -689,6 +738,7 @@ __global__ __launch_bounds__(64) void c3_span_init_kernel(C3Desc P, int dep, int
   if (lane == 0) {
     W.sb[s] = b;
     W.sn1[s] = 0;
+    W.sflip[s] = 0;
     W.salive[s] = 1;
   }
 }
@@ -735,7 +785,7 @@ __global__ __launch_bounds__(C3_T) void c3_span_iter_kernel(C3Desc P, int par, i
   __shared__ double red0[NW][D], red1[NW][D];
   __shared__ int sPerm[C3_SPB * C3_CH];
   const int s = blockIdx.x;
-  if (!W.salive[s]) return;
+  if (W.salive[s] != 1) return;
   const int2 un = W.snode[par * W.smax + s];
   const int u = un.x, x = un.y;
   const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
@@ -765,7 +815,7 @@ __global__ __launch_bounds__(C3_T) void c3_span_iter_kernel(C3Desc P, int par, i
   double a0[CPL], a1[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) a0[i] = a1[i] = 0.0;
-  int dn1 = 0;
+  int dn1 = 0, flips = 0;
   for (int blk = 0; blk < nblk; ++blk) {
     const int rows = min(C3_CH, total - blk * C3_CH);
 #pragma unroll
@@ -802,6 +852,7 @@ __global__ __launch_bounds__(C3_T) void c3_span_iter_kernel(C3Desc P, int par, i
       c3_acc_cols<RB, CPL, true>(sK, rb, ow & ~nw, lane, a1);
     }
     dn1 += __popc(nw) - __popc(ow);
+    flips += __popc(nw ^ ow);
     __syncthreads();
   }
 #pragma unroll
@@ -809,8 +860,11 @@ __global__ __launch_bounds__(C3_T) void c3_span_iter_kernel(C3Desc P, int par, i
     red0[wave][lane * CPL + i] = a0[i];
     red1[wave][lane * CPL + i] = a1[i];
   }
-  __shared__ int sDn[NW];
-  if (lane == 0) sDn[wave] = dn1;
+  __shared__ int sDn[NW], sFl[NW];
+  if (lane == 0) {
+    sDn[wave] = dn1;
+    sFl[wave] = flips;
+  }
   __syncthreads();
   for (int c = tid; c < (it == 0 ? 2 * D : D); c += C3_T) {
     const int h = c < D ? 1 : 0, cc = c < D ? c : c - D;
@@ -818,17 +872,20 @@ __global__ __launch_bounds__(C3_T) void c3_span_iter_kernel(C3Desc P, int par, i
     for (int w = 0; w < NW; ++w) t += h ? red1[w][cc] : red0[w][cc];
     atomicAdd(h ? &W.s1[(size_t)s * D + cc] : &W.s0[(size_t)s * D + cc], t);
   }
-  if (tid == 0) atomicAdd(&W.sn1[s], sDn[0] + sDn[1] + sDn[2] + sDn[3]);
+  if (tid == 0) {
+    atomicAdd(&W.sn1[s], sDn[0] + sDn[1] + sDn[2] + sDn[3]);
+    if (it > 0) atomicAdd(&W.sflip[s], sFl[0] + sFl[1] + sFl[2] + sFl[3]);
+  }
 }
 
 // New means of a span node from its total (s0) and running cluster-1 sum
 // (s1) and count; the last iteration records the split.
 template <int D>
-__global__ __launch_bounds__(64) void c3_span_fin_kernel(C3Desc P, int par, int last, C3Index X,
-                                                         C3Work W) {
+__global__ __launch_bounds__(64) void c3_span_fin_kernel(C3Desc P, int par, int it, int last,
+                                                         C3Index X, C3Work W) {
   constexpr int CPL = D / 64;
   const int s = blockIdx.x, lane = threadIdx.x;
-  if (!W.salive[s]) return;
+  if (W.salive[s] != 1) return;
   const int2 un = W.snode[par * W.smax + s];
   const int u = un.x, x = un.y;
   const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
@@ -849,7 +906,12 @@ __global__ __launch_bounds__(64) void c3_span_fin_kernel(C3Desc P, int par, int 
     mu0[i] = (W.s0[o] - W.s1[o]) * i0;
     mu1[i] = W.s1[o] * i1;
   }
-  if (!last) {
+  // A partition that repeats the previous one is a fixed point: record the
+  // split now and stop iterating this node.
+  const bool conv = it > 0 && W.sflip[s] == 0;
+  if (lane == 0) W.sflip[s] = 0;
+  if (conv && lane == 0) W.salive[s] = 2;
+  if (!last && !conv) {
     float w[CPL];
     const float b = c3_bisect<CPL>(mu0, mu1, w);
 #pragma unroll
@@ -873,7 +935,7 @@ __global__ __launch_bounds__(C3_BIG) void c3_span_part_kernel(C3Desc P, int par,
                                                               C3Work W) {
   __shared__ int scan[C3_BIG / 64];
   const int s = blockIdx.x;
-  if (!W.salive[s]) return;
+  if (W.salive[s] == 0) return;
   const int2 un = W.snode[par * W.smax + s];
   const int u = un.x, x = un.y;
   const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
@@ -1467,7 +1529,7 @@ static void c3_layout(const C3Desc& V, kvc_c3_layout* L) {
                              c3_up(4 * U * (C3_MAXD + 2)) + c3_up(8 * U * D) + c3_up(4 * U) +
                              c3_up(8 * 2 * S) +
                              c3_up(4 * S * D) + c3_up(4 * S) + 2 * c3_up(8 * S * D) + c3_up(4 * S) +
-                             c3_up(4 * S) + c3_up(16 * (C3_MAXD + 1)) + c3_up(4) +
+                             c3_up(4 * S) + c3_up(4 * S) + c3_up(16 * (C3_MAXD + 1)) + c3_up(4) +
                              c3_up(4 * U * V.nchunk) + c3_up(8 * U * V.nchunk);
   L->step_workspace_bytes = c3_up(4 * U * CAP);
 }
@@ -1515,6 +1577,7 @@ static C3Work c3_work(const C3Desc& V, void* ws) {
   W.s1 = (double*)p;       p += c3_up(8 * S * D);
   W.sn1 = (int32_t*)p;     p += c3_up(4 * S);
   W.salive = (int32_t*)p;  p += c3_up(4 * S);
+  W.sflip = (int32_t*)p;   p += c3_up(4 * S);
   W.cnt = (int32_t*)p;     p += c3_up(16 * (C3_MAXD + 1));
   W.err = (int32_t*)p;     p += c3_up(4);
   W.cflag = (int32_t*)p;   p += c3_up(4 * U * V.nchunk);
@@ -1589,7 +1652,8 @@ extern "C" kvc_status kvc_c3_build(const kvc_c3_problem* prob, const kvc_c3_para
       C3_LAUNCH(V.d, c3_span_init_kernel, g1, dim3(64), V, dep, par, X, W, kk);
       for (int it = 0; it < C3_ITERS; ++it) {
         C3_LAUNCH(V.d, c3_span_iter_kernel, g2, dim3(C3_T), V, par, it, X, W, kk);
-        C3_LAUNCH(V.d, c3_span_fin_kernel, g1, dim3(64), V, par, it + 1 == C3_ITERS ? 1 : 0, X, W);
+        C3_LAUNCH(V.d, c3_span_fin_kernel, g1, dim3(64), V, par, it, it + 1 == C3_ITERS ? 1 : 0, X,
+                  W);
       }
       hipLaunchKernelGGL(c3_span_part_kernel, g1, dim3(C3_BIG), 0, st, V, par, X, W);
     }
