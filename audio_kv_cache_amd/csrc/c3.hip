@@ -779,11 +779,13 @@ __global__ __launch_bounds__(C3_T) void c3_span_iter_kernel(C3Desc P, int par, i
                                                             C3Work W, const uint16_t* __restrict__ k) {
   constexpr int RB = 2 * D + 16, CPL = D / 64, PPR = D / 8, NW = C3_T / 64;
   constexpr int PER = C3_CH * PPR / C3_T;       // 16-byte pieces per thread and block
+  static_assert(2 * NW * D * 8 <= C3_CH * RB, "the block reduction fits in the key tile");
   __shared__ __align__(16) unsigned char sK[C3_CH * RB];
   __shared__ __align__(16) float sWv[D + 4];
   __shared__ uint64_t sNew[C3_CH / 64], sOld[C3_CH / 64];
-  __shared__ double red0[NW][D], red1[NW][D];
   __shared__ int sPerm[C3_SPB * C3_CH];
+  double(*red0)[D] = reinterpret_cast<double(*)[D]>(sK);          // after the last block
+  double(*red1)[D] = reinterpret_cast<double(*)[D]>(sK + NW * D * 8);
   const int s = blockIdx.x;
   if (W.salive[s] != 1) return;
   const int2 un = W.snode[par * W.smax + s];
@@ -801,6 +803,7 @@ __global__ __launch_bounds__(C3_T) void c3_span_iter_kernel(C3Desc P, int par, i
   const float b = W.sb[s];
   __syncthreads();
   uint4 buf[PER];
+  int oldf = 0;
   auto load = [&](int blk) {
     const int rows = min(C3_CH, total - blk * C3_CH);
 #pragma unroll
@@ -810,6 +813,7 @@ __global__ __launch_bounds__(C3_T) void c3_span_iter_kernel(C3Desc P, int par, i
         buf[p] = *reinterpret_cast<const uint4*>(k + u * P.ks[0] +
                                                  (int64_t)sPerm[blk * C3_CH + r] * P.ks[1] + pc * 8);
     }
+    oldf = (it > 0 && tid < rows) ? W.flags[ub + q0 + blk * C3_CH + tid] : 0;
   };
   load(0);
   double a0[CPL], a1[CPL];
@@ -824,12 +828,12 @@ __global__ __launch_bounds__(C3_T) void c3_span_iter_kernel(C3Desc P, int par, i
       if (r < rows)
         *reinterpret_cast<uint4*>(sK + r * RB + pc * 16) = tiny ? c3_snap8_fast(buf[p]) : buf[p];
     }
+    const bool o = oldf != 0;
     __syncthreads();
     if (blk + 1 < nblk) load(blk + 1);
     if (tid < C3_CH) {
       const size_t pos = ub + q0 + blk * C3_CH + tid;
       const bool f = tid < rows && c3_plane<D>(sK + tid * RB, sWv) > b;
-      const bool o = tid < rows && it > 0 && W.flags[pos] != 0;
       if (tid < rows) W.flags[pos] = f ? 1 : 0;
       const uint64_t wn = __ballot(f), wo = __ballot(o);
       if (lane == 0) {
