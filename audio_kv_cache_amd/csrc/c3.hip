@@ -1059,19 +1059,23 @@ __global__ __launch_bounds__(C3_BIG) void c3_frontier_kernel(C3Desc P, C3Index X
 // ---------------------------------------------------------------------------
 // Step: scores
 // ---------------------------------------------------------------------------
-template <int D>
+// A thread per frontier entry: its centroid row is streamed from global
+// memory in 16-byte pieces (8 columns) and folded into the norm and the dot
+// products with every query head of the group (HPT >= G of them).
+template <int D, int HPT>
 __global__ __launch_bounds__(C3_T) void c3_score_kernel(C3Desc P, C3Index X, C3State S,
                                                         const uint16_t* __restrict__ q,
                                                         float* __restrict__ sigma) {
-  __shared__ __align__(16) float sQ[C3_MAX_G][D];
-  __shared__ float sQn[C3_MAX_G];
+  __shared__ __align__(16) float sQ[HPT][D];
+  __shared__ float sQn[HPT];
   const int u = blockIdx.x / C3_SW, part = blockIdx.x - u * C3_SW;
   if (c3_n(P, u) <= c3_b(P, u)) return;
   const int G = P.gqa, A = S.count[u];
   const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
-  for (int i = threadIdx.x; i < G * D; i += C3_T) sQ[i / D][i % D] = c3_bf(q[(size_t)u * G * D + i]);
+  for (int i = threadIdx.x; i < HPT * D; i += C3_T)
+    sQ[i / D][i % D] = i < G * D ? c3_bf(q[(size_t)u * G * D + i]) : 0.0f;
   __syncthreads();
-  if (threadIdx.x < G) {
+  if (threadIdx.x < HPT) {
     float s = 0.0f;
     for (int c = 0; c < D; ++c) s = fmaf(sQ[threadIdx.x][c], sQ[threadIdx.x][c], s);
     sQn[threadIdx.x] = sqrtf(s);
@@ -1080,37 +1084,41 @@ __global__ __launch_bounds__(C3_T) void c3_score_kernel(C3Desc P, C3Index X, C3S
   for (int i = part * C3_T + threadIdx.x; i < A; i += C3_SW * C3_T) {
     const int x = S.fr[ub + i];
     const uint4* row = reinterpret_cast<const uint4*>(X.cent + (nb + x) * D);
-    float c[D];
+    float dot[HPT];
 #pragma unroll
+    for (int g = 0; g < HPT; ++g) dot[g] = 0.0f;
+    float cn = 0.0f;
+#pragma unroll 4
     for (int p = 0; p < D / 8; ++p) {
       const uint4 v = row[p];
-      c[8 * p + 0] = c3_bf(v.x & 0xFFFFu);
-      c[8 * p + 1] = c3_bf(v.x >> 16);
-      c[8 * p + 2] = c3_bf(v.y & 0xFFFFu);
-      c[8 * p + 3] = c3_bf(v.y >> 16);
-      c[8 * p + 4] = c3_bf(v.z & 0xFFFFu);
-      c[8 * p + 5] = c3_bf(v.z >> 16);
-      c[8 * p + 6] = c3_bf(v.w & 0xFFFFu);
-      c[8 * p + 7] = c3_bf(v.w >> 16);
-    }
-    float cn = 0.0f;
+      const float c[8] = {c3_bf(v.x & 0xFFFFu), c3_bf(v.x >> 16), c3_bf(v.y & 0xFFFFu),
+                          c3_bf(v.y >> 16),     c3_bf(v.z & 0xFFFFu), c3_bf(v.z >> 16),
+                          c3_bf(v.w & 0xFFFFu), c3_bf(v.w >> 16)};
 #pragma unroll
-    for (int j = 0; j < D; ++j) cn = fmaf(c[j], c[j], cn);
+      for (int j = 0; j < 8; ++j) cn = fmaf(c[j], c[j], cn);
+#pragma unroll
+      for (int g = 0; g < HPT; ++g) {
+        const float4 q0 = *reinterpret_cast<const float4*>(&sQ[g][8 * p]);
+        const float4 q1 = *reinterpret_cast<const float4*>(&sQ[g][8 * p + 4]);
+        float d = dot[g];
+        d = fmaf(q0.x, c[0], d);
+        d = fmaf(q0.y, c[1], d);
+        d = fmaf(q0.z, c[2], d);
+        d = fmaf(q0.w, c[3], d);
+        d = fmaf(q1.x, c[4], d);
+        d = fmaf(q1.y, c[5], d);
+        d = fmaf(q1.z, c[6], d);
+        d = fmaf(q1.w, c[7], d);
+        dot[g] = d;
+      }
+    }
     cn = sqrtf(cn);
     float best = -INFINITY;
-    for (int g = 0; g < G; ++g) {
-      const float4* qg = reinterpret_cast<const float4*>(&sQ[g][0]);
-      float dot = 0.0f;
 #pragma unroll
-      for (int j = 0; j < D / 4; ++j) {
-        const float4 qq = qg[j];
-        dot = fmaf(qq.x, c[4 * j], dot);
-        dot = fmaf(qq.y, c[4 * j + 1], dot);
-        dot = fmaf(qq.z, c[4 * j + 2], dot);
-        dot = fmaf(qq.w, c[4 * j + 3], dot);
-      }
+    for (int g = 0; g < HPT; ++g) {
+      if (g >= G) break;
       const float den = sQn[g] * cn;
-      best = fmaxf(best, den > 0.0f ? dot / den : 0.0f);
+      best = fmaxf(best, den > 0.0f ? dot[g] / den : 0.0f);
     }
     sigma[ub + i] = best;
   }
@@ -1684,8 +1692,19 @@ extern "C" kvc_status kvc_c3_build(const kvc_c3_problem* prob, const kvc_c3_para
 
 static hipError_t c3_launch_score(const C3Desc& V, const C3Index& X, const C3State& S,
                                   const void* q, float* sigma, hipStream_t st) {
-  C3_LAUNCH(V.d, c3_score_kernel, dim3((unsigned)V.n_units * C3_SW), dim3(C3_T), V, X, S,
-            (const uint16_t*)q, sigma);
+  const dim3 grid((unsigned)V.n_units * C3_SW), block(C3_T);
+  const uint16_t* qq = (const uint16_t*)q;
+  if (V.d == 128) {
+    if (V.gqa <= 8)
+      hipLaunchKernelGGL((c3_score_kernel<128, 8>), grid, block, 0, st, V, X, S, qq, sigma);
+    else
+      hipLaunchKernelGGL((c3_score_kernel<128, 32>), grid, block, 0, st, V, X, S, qq, sigma);
+  } else {
+    if (V.gqa <= 8)
+      hipLaunchKernelGGL((c3_score_kernel<64, 8>), grid, block, 0, st, V, X, S, qq, sigma);
+    else
+      hipLaunchKernelGGL((c3_score_kernel<64, 32>), grid, block, 0, st, V, X, S, qq, sigma);
+  }
   return hipGetLastError();
 }
 

@@ -358,8 +358,8 @@ def bench_c3(args):
         "steps_per_s": 1e3 / step_ms,
         "algorithmic_bytes_per_step": ab["total"],
         "stage_us": {n2: round(t * 1e3, 2) for n2, t in stages.items()},
-        "roofline": {"score": hbm("c3_score_kernel<128>", gbs["score"], "c3.hip"),
-                     "gather": hbm("c3_gather_kernel<128>", gbs["gather"], "c3.hip")},
+        "roofline": {"score": hbm(f"c3_score_kernel<{cfg.head_dim}, 8>", gbs["score"], "c3.hip"),
+                     "gather": hbm(f"c3_gather_kernel<{cfg.head_dim}>", gbs["gather"], "c3.hip")},
     }
     if not args.no_cpu_baseline:
         from oracle import c3 as C3

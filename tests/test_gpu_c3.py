@@ -247,6 +247,18 @@ def test_other_lambda_and_swaps(lam, R):
     run_steps(dev, 3, trees)
 
 
+@pytest.mark.parametrize("gqa,d", [(12, 128), (32, 64), (1, 64)])
+def test_group_sizes(gqa, d):
+    cfg = synth.C3Config(f"c3_g{gqa}_d{d}", 24, 2, 1, 2, gqa, d, lens=(700, 333),
+                         budgets=(64, 40), capacity=704)
+    dev = C3Dev(cfg)
+    dev.build()
+    trees = [oracle_tree(dev, u) for u in range(dev.U)]
+    for u in range(dev.U):
+        assert_tree_equal(dev, u, trees[u])
+    run_steps(dev, 2, trees)
+
+
 def test_tiny_and_zero_keys_are_snapped_alike():
     # Keys below 2^-17 are moved to the 2^-24 grid before any sum; zeros and
     # subnormal bf16 values as well.
