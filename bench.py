@@ -272,7 +272,7 @@ def bench_c3(args):
     log("[bench] c3: building")
     api.kvc_c3_build(spec, prm, k, o["index"], o["state"][0], o["build_ws"], stream)
     builds = []
-    for _ in range(args.c3_builds):
+    for _ in range(max(1, args.c3_builds)):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         api.kvc_c3_build(spec, prm, k, o["index"], o["state"][0], o["build_ws"], stream)
