@@ -130,7 +130,7 @@ def lib():
             L.kvc_scores.argtypes = [prob, prm, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
             L.kvc_score_stats.argtypes = [prob, prm, _vp, _vp, _vp, ctypes.c_size_t, _vp]
             L.kvc_score_pool.argtypes = [prob, prm, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
-            L.kvc_smooth.argtypes = [prob, prm, _vp, _vp, _vp, _vp]
+            L.kvc_smooth.argtypes = [prob, prm, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
             L.kvc_budget.argtypes = [prob, prm, _vp, _vp, _vp, _vp]
             L.kvc_select.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp]
             L.kvc_gather.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp, _vp, _vp]

@@ -156,9 +156,13 @@ def kvc_score_pool(spec, params, q, k, s_out, workspace, stream=None):
             "kvc_score_pool")
 
 
-def kvc_smooth(spec, params, s, s_hat, kstar, stream=None):
+def kvc_smooth(spec, params, s, s_hat, kstar, stream=None, workspace=None):
+    """workspace: needed only when a length is not a power of two."""
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     C.check(C.lib().kvc_smooth(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(s),
-                               _ptr(s_hat), _ptr(kstar), _stream(stream)), "kvc_smooth")
+                               _ptr(s_hat), _ptr(kstar),
+                               None if workspace is None else _ptr(workspace), wsb,
+                               _stream(stream)), "kvc_smooth")
 
 
 def kvc_budget(spec, params, head_scores, budgets, seg_offsets, stream=None):

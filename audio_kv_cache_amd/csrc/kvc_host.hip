@@ -106,7 +106,10 @@ static kvc_status make_desc(const kvc_problem* p, const kvc_params* prm, KvcDesc
   int64_t tiles = 0;
   for (int i = 0; i < p->n_seq; ++i) {
     const int64_t L = p->seq_start[i + 1] - p->seq_start[i];
-    if (!is_pow2(L) || L < KVC_MIN_L || L > KVC_MAX_L) return KVC_ERR_UNSUPPORTED;
+    if (L < KVC_MIN_L || L > KVC_MAX_L) return KVC_ERR_UNSUPPORTED;
+    // Other lengths take Bluestein's algorithm through FFTs of at most 32768
+    // points: up to 32768 for even L, 16384 for odd L.
+    if (!is_pow2(L) && ((L & 1) ? L : L / 2) > 16384) return KVC_ERR_UNSUPPORTED;
     if (L <= prm->window) return KVC_ERR_BUDGET;
     const int64_t kbar = kbar_of(p->retention[i], L);
     if (kbar < L) {
@@ -115,7 +118,7 @@ static kvc_status make_desc(const kvc_problem* p, const kvc_params* prm, KvcDesc
     }
     D->tok0[i] = p->seq_start[i];
     D->L[i] = (int32_t)L;
-    D->log2L[i] = 63 - __builtin_clzll((unsigned long long)L);
+    D->log2L[i] = is_pow2(L) ? 63 - __builtin_clzll((unsigned long long)L) : -1;
     D->retention[i] = p->retention[i];
     D->row_base[i] = rows;
     D->srow_base[i] = srows;
@@ -138,22 +141,32 @@ static size_t score_rows_bytes(const KvcDesc& D) {
   return sizeof(float) * (size_t)D.srow_base[D.n_seq];
 }
 
+// Scratch of the smoothing launches for lengths that are not powers of two
+// (one launch per sequence at a time, so the largest one).
+static size_t sss_scratch_bytes(const KvcDesc& D) {
+  size_t m = 0;
+  for (int i = 0; i < D.n_seq; ++i) m = std::max(m, kvc_sss_scratch_bytes(D.L[i], D.upseq));
+  return (m + 255) & ~size_t(255);
+}
+
 extern "C" kvc_status kvc_plan(const kvc_problem* prob, const kvc_params* params,
                                int64_t* total_rows, size_t* workspace_bytes) {
   KvcDesc D;
   const kvc_status st = make_desc(prob, params, &D);
   if (st != KVC_OK) return st;
   if (total_rows) *total_rows = D.row_base[D.n_seq];
-  if (workspace_bytes) *workspace_bytes = kvc_scores_workspace(D) + up256(score_rows_bytes(D));
+  if (workspace_bytes)
+    *workspace_bytes = kvc_scores_workspace(D) + up256(score_rows_bytes(D)) + sss_scratch_bytes(D);
   return KVC_OK;
 }
 
-// Workspace layout: [lse2 | partials] (kvc_scores_workspace) then the score
-// rows.
+// Workspace layout: [lse2 | partials] (kvc_scores_workspace), the score
+// rows, then the smoothing scratch for lengths that are not powers of two.
 struct Carve {
   float* lse2;
   float2* partials;
   float* srows;
+  void* sss;
 };
 
 static Carve carve(const KvcDesc& D, void* ws) {
@@ -164,6 +177,8 @@ static Carve carve(const KvcDesc& D, void* ws) {
   c.partials = (float2*)p;
   p += up256(sizeof(float2) * (size_t)D.total_tiles * D.gw);
   c.srows = (float*)p;
+  p += up256(score_rows_bytes(D));
+  c.sss = sss_scratch_bytes(D) ? (void*)p : nullptr;
   return c;
 }
 
@@ -186,7 +201,7 @@ static kvc_status compress_range(const kvc_problem* prob, const kvc_params* para
   if (!aligned16(q_window) || !aligned16(k) || !aligned16(v) || !aligned16(k_out) ||
       !aligned16(v_out) || ((uintptr_t)workspace & 255u))
     return KVC_ERR_INVALID_ARG;
-  const size_t need = kvc_scores_workspace(D) + up256(score_rows_bytes(D));
+  const size_t need = kvc_scores_workspace(D) + up256(score_rows_bytes(D)) + sss_scratch_bytes(D);
   if (workspace_bytes < need) return KVC_ERR_WORKSPACE;
   const Carve c = carve(D, workspace);
   hipStream_t s = (hipStream_t)stream;
@@ -206,7 +221,7 @@ static kvc_status compress_range(const kvc_problem* prob, const kvc_params* para
   for (int seq = 0; seq < D.n_seq; ++seq) {
     const int u0 = (seq * D.n_layers + lb) * D.n_heads, u1 = (seq * D.n_layers + le) * D.n_heads;
     if ((e = kvc_launch_sss_select(D, u0, u1, 1 | 2, c.srows, nullptr, nullptr, budgets,
-                                   seg_offsets, idx_out, s)) != hipSuccess)
+                                   seg_offsets, idx_out, c.sss, s)) != hipSuccess)
       return hip_status(e);
   }
   if (whole) {
@@ -285,16 +300,20 @@ extern "C" kvc_status kvc_score_pool(const kvc_problem* prob, const kvc_params* 
 
 extern "C" kvc_status kvc_smooth(const kvc_problem* prob, const kvc_params* params,
                                  const float* s_in, float* s_hat, int32_t* kstar,
-                                 void* stream) {
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   KvcDesc D;
   kvc_status st = make_desc(prob, params, &D);
   if (st != KVC_OK) return st;
   if (!s_in || !s_hat || !kstar) return KVC_ERR_INVALID_ARG;
   if (((uintptr_t)s_in & 7u) || ((uintptr_t)s_hat & 7u)) return KVC_ERR_INVALID_ARG;
+  const size_t need = sss_scratch_bytes(D);
+  if (need && (!workspace || ((uintptr_t)workspace & 255u))) return KVC_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return KVC_ERR_WORKSPACE;
   for (int seq = 0; seq < D.n_seq; ++seq) {
     const hipError_t e =
         kvc_launch_sss_select(D, seq * D.upseq, (seq + 1) * D.upseq, 1 | 4, s_in, s_hat, kstar,
-                              nullptr, nullptr, nullptr, (hipStream_t)stream);
+                              nullptr, nullptr, nullptr, need ? workspace : nullptr,
+                              (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
   }
   return KVC_OK;
@@ -321,7 +340,7 @@ extern "C" kvc_status kvc_select(const kvc_problem* prob, const kvc_params* para
   for (int seq = 0; seq < D.n_seq; ++seq) {
     const hipError_t e =
         kvc_launch_sss_select(D, seq * D.upseq, (seq + 1) * D.upseq, 2, s_hat, nullptr, nullptr,
-                              budgets, seg_offsets, idx_out, (hipStream_t)stream);
+                              budgets, seg_offsets, idx_out, nullptr, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
   }
   return KVC_OK;

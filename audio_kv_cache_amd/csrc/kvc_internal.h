@@ -49,9 +49,14 @@ __host__ __device__ inline int64_t kvc_kv_offset(const int64_t (&st)[3], const K
   return (int64_t)(l - D.layer0) * st[0] + (int64_t)h * st[1] + D.tok0[seq] * st[2];
 }
 
-// Unit u -> (sequence, unit within sequence).
+// Score tiles of one unit's L keys: tiles of KVC_TILE_KEYS keys over the
+// first L64 = L - L % 64 keys (the last one may be shorter, a multiple of 64),
+// then one tail tile of the last L % 64 keys when there are any.
+__host__ __device__ inline int kvc_main_tiles(int L) {
+  return ((L & ~63) + KVC_TILE_KEYS - 1) / KVC_TILE_KEYS;
+}
 __host__ __device__ inline int kvc_tiles_per_unit(int L) {
-  return L > KVC_TILE_KEYS ? L / KVC_TILE_KEYS : 1;
+  return kvc_main_tiles(L) + ((L & 63) ? 1 : 0);
 }
 
 // Kernel launchers (defined next to each kernel).
@@ -65,9 +70,13 @@ hipError_t kvc_launch_scores(const KvcDesc& D, int u0, int u1, const void* q, co
                              int which = 3);
 // mode bit 0: smooth (else read s_hat from s_in); bit 1: select;
 // bit 2: export s_hat and kstar.
+// scratch: kvc_sss_scratch_bytes(L, u1 - u0) bytes, needed only when L is not
+// a power of two (lengths handled through Bluestein's algorithm).
 hipError_t kvc_launch_sss_select(const KvcDesc& D, int u0, int u1, int mode, const float* s_in,
                                  float* s_hat_out, int32_t* kstar_out, const int32_t* budgets,
-                                 const int64_t* offsets, int32_t* idx_out, hipStream_t st);
+                                 const int64_t* offsets, int32_t* idx_out, void* scratch,
+                                 hipStream_t st);
+size_t kvc_sss_scratch_bytes(int L, int units);
 hipError_t kvc_launch_gather(const KvcDesc& D, int u0, int u1, const void* k, const void* v,
                              const int32_t* idx, const int64_t* offsets, void* k_out, void* v_out,
                              int64_t est_rows, hipStream_t st);

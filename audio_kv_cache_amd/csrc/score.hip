@@ -84,6 +84,7 @@ __device__ inline int xcd_local_tile(int b, int n) {
 
 struct TileInfo {
   int seq, u, l, h, t, tpu, L, keys, key0;
+  bool tail;   // the L % 64 keys past the last multiple of 64 (kvc_score_tail_kernel)
 };
 
 __device__ inline TileInfo tile_info(const KvcDesc& Dsc, int tile) {
@@ -99,8 +100,10 @@ __device__ inline TileInfo tile_info(const KvcDesc& Dsc, int tile) {
   ti.u = seq * Dsc.upseq + uin;
   ti.l = uin / Dsc.n_heads;
   ti.h = uin - ti.l * Dsc.n_heads;
-  ti.keys = ti.L < KVC_TILE_KEYS ? ti.L : KVC_TILE_KEYS;
-  ti.key0 = ti.t * ti.keys;
+  const int L64 = ti.L & ~63;
+  ti.tail = ti.t == kvc_main_tiles(ti.L);
+  ti.key0 = ti.tail ? L64 : ti.t * KVC_TILE_KEYS;
+  ti.keys = ti.tail ? ti.L - L64 : min(KVC_TILE_KEYS, L64 - ti.key0);
   return ti;
 }
 
@@ -148,6 +151,7 @@ __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_stats_kernel
 
   const int tile = tile0 + xcd_local_tile((int)blockIdx.x, (int)gridDim.x);
   const TileInfo ti = tile_info(Dsc, tile);
+  if (ti.tail) return;  // kvc_score_tail_kernel
   const int gw = NBC > 0 ? NBC * M : Dsc.gw;
   const int ncb = NBC > 0 ? NBC : gw / M;
   const float c = kLog2e / sqrtf((float)D);
@@ -306,6 +310,7 @@ __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_pool_kernel(
 
   const int tile = tile0 + xcd_local_tile((int)blockIdx.x, (int)gridDim.x);
   const TileInfo ti = tile_info(Dsc, tile);
+  if (ti.tail) return;  // kvc_score_tail_kernel
   const int gw = NBC > 0 ? NBC * M : Dsc.gw;
   const int nrb = NBC > 0 ? NBC : gw / M;
   const float c = kLog2e / sqrtf((float)D);
@@ -543,6 +548,7 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
   __shared__ float sRed[NROWS][KVC_TILE_KEYS];
   const int tile = tile0 + xcd_local_tile((int)blockIdx.x, (int)gridDim.x);
   const TileInfo ti = tile_info(Dsc, tile);
+  if (ti.tail) return;  // kvc_score_tail_kernel
   const int gw = NBC * 32;
   const float c = kLog2e / sqrtf((float)D);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -686,6 +692,7 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
   __shared__ int sRedo;
   const int tile = tile0 + xcd_local_tile((int)blockIdx.x, (int)gridDim.x);
   const TileInfo ti = tile_info(Dsc, tile);
+  if (ti.tail) return;  // kvc_score_tail_kernel
   const int gw = NBC * 32;
   const float c = kLog2e / sqrtf((float)D);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -812,6 +819,86 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
   }
 }
 
+// The L % 64 keys of each unit past its last multiple of 64: in mode 1 the
+// statistics pass's (max, sum) per window query over them (the tail tile's
+// partial, folded with the others), in mode 2 their pooled scores.  Plain
+// fp32 dot products; one workgroup per unit.
+template <class E, int D>
+__global__ __launch_bounds__(256) void kvc_score_tail_kernel(KvcDesc Dsc, int unit0, int mode,
+                                                             const E* __restrict__ q,
+                                                             const E* __restrict__ k,
+                                                             const float* __restrict__ lse2,
+                                                             float2* __restrict__ partials,
+                                                             float* __restrict__ s) {
+  __shared__ float sK[63][D + 1];
+  __shared__ float sPart[4][64];
+  const int u = unit0 + (int)blockIdx.x;
+  const int seq = u / Dsc.upseq, within = u - seq * Dsc.upseq;
+  const int l = within / Dsc.n_heads, h = within - l * Dsc.n_heads;
+  const int L = Dsc.L[seq], L64 = L & ~63, nt = L - L64;
+  const int gw = Dsc.gw;
+  const float c = kLog2e / sqrtf((float)D);
+  auto val = [](E x) -> float {
+    if constexpr (sizeof(E) == 2) return __uint_as_float((uint32_t)x << 16);
+    else return (float)x;
+  };
+  const E* qg = q + kvc_q_offset(Dsc, seq, l, h);
+  const E* ku = k + kvc_kv_offset(Dsc.ks, Dsc, seq, l, h);
+  for (int i = threadIdx.x; i < nt * D; i += 256) {
+    const int j = i / D, cc = i - j * D;
+    sK[j][cc] = val(ku[(int64_t)(L64 + j) * Dsc.ks[2] + cc]);
+  }
+  __syncthreads();
+  if (mode == 1) {
+    const int tile = Dsc.tile_base[seq] + within * kvc_tiles_per_unit(L) + kvc_main_tiles(L);
+    for (int r = threadIdx.x; r < gw; r += 256) {
+      const E* qr = qg + (size_t)r * D;
+      float m = -INFINITY, z = 0.f;
+      for (int j = 0; j < nt; ++j) {
+        float dot = 0.f;
+        for (int cc = 0; cc < D; ++cc) dot = fmaf(val(qr[cc]), sK[j][cc], dot);
+        merge_stat(m, z, dot, 1.0f, c);
+      }
+      partials[(size_t)tile * gw + r] = make_float2(m, z);
+    }
+    return;
+  }
+  // Pooling: thread (key j, part p) sums the probabilities of the heads
+  // g = p, p + 4, ... (each head's W rows), then the parts are folded.
+  const int j = threadIdx.x & 63, part = threadIdx.x >> 6;
+  const int W = Dsc.nwin, G = gw / W;
+  const float* lu = lse2 + (size_t)u * gw;
+  float acc = Dsc.score_max ? 0.f : 0.f;
+  if (j < nt) {
+    for (int g = part; g < G; g += 4) {
+      float v = 0.f;
+      for (int r = g * W; r < (g + 1) * W; ++r) {
+        const E* qr = qg + (size_t)r * D;
+        float dot = 0.f;
+        for (int cc = 0; cc < D; ++cc) dot = fmaf(val(qr[cc]), sK[j][cc], dot);
+        v += __builtin_amdgcn_exp2f(fmaf(dot, c, -lu[r]));
+      }
+      acc = Dsc.score_max ? fmaxf(acc, v) : acc + v;
+    }
+  }
+  sPart[part][j] = acc;
+  __syncthreads();
+  if (part == 0 && j < nt) {
+    float* srow = s + Dsc.srow_base[seq] + (int64_t)within * L;
+    const float a = sPart[0][j], b = sPart[1][j], cc2 = sPart[2][j], d2 = sPart[3][j];
+    srow[L64 + j] = Dsc.score_max ? fmaxf(fmaxf(a, b), fmaxf(cc2, d2)) / (float)W
+                                  : ((a + b) + (cc2 + d2)) / (float)gw;
+  }
+}
+
+template <class E, int Dm>
+static void launch_tail(const KvcDesc& D, int u0, int u1, int mode, const void* q, const void* k,
+                        const float* lse2, float2* partials, float* s, hipStream_t st) {
+  if ((D.L[u0 / D.upseq] & 63) == 0) return;
+  hipLaunchKernelGGL((kvc_score_tail_kernel<E, Dm>), dim3(u1 - u0), dim3(256), 0, st, D, u0, mode,
+                     (const E*)q, (const E*)k, lse2, partials, s);
+}
+
 size_t kvc_scores_workspace(const KvcDesc& D) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   return up(sizeof(float) * (size_t)D.n_units * D.gw) +
@@ -830,12 +917,15 @@ static void launch_pair(const KvcDesc& D, int u0, int u1, const void* q, const v
   if (which & 1) {
     hipLaunchKernelGGL((kvc_score_stats_kernel<T, Dm, NBC>), dim3(nt), dim3(SCORE_THREADS), 0, st,
                        D, t0, (const elem_t*)q, (const elem_t*)k, partials);
+    launch_tail<elem_t, Dm>(D, u0, u1, 1, q, k, lse2, partials, s, st);
     hipLaunchKernelGGL(kvc_score_lse_kernel, dim3(u1 - u0), dim3(KVC_MAX_GW), 0, st, D, u0,
                        kLog2e / sqrtf((float)Dm), (const float2*)partials, lse2);
   }
-  if (which & 2)
+  if (which & 2) {
     hipLaunchKernelGGL((kvc_score_pool_kernel<T, Dm, NBC>), dim3(nt), dim3(SCORE_THREADS), 0, st,
                        D, t0, (const elem_t*)q, (const elem_t*)k, (const float*)lse2, s);
+    launch_tail<elem_t, Dm>(D, u0, u1, 2, q, k, lse2, partials, s, st);
+  }
 }
 
 // Query-stationary bf16 passes; units [u0, u1) in one sequence.
@@ -850,6 +940,7 @@ static void launch_qs(const KvcDesc& D, int u0, int u1, const void* q, const voi
   if (which & 1) {
     hipLaunchKernelGGL((kvc_score_stats_qs_kernel<Dm, NBC>), dim3(nt), dim3(NT), 0, st, D, t0,
                        (const uint16_t*)q, (const uint16_t*)k, partials);
+    launch_tail<uint16_t, Dm>(D, u0, u1, 1, q, k, lse2, partials, s, st);
     hipLaunchKernelGGL(kvc_score_lse_kernel, dim3(u1 - u0), dim3(KVC_MAX_GW), 0, st, D, u0,
                        kLog2e / sqrtf((float)Dm), (const float2*)partials, lse2);
   }
@@ -859,6 +950,7 @@ static void launch_qs(const KvcDesc& D, int u0, int u1, const void* q, const voi
   else if (which & 2)
     hipLaunchKernelGGL((kvc_score_pool_qs_kernel<Dm, NBC, false>), dim3(nt), dim3(NT), 0, st, D,
                        t0, (const uint16_t*)q, (const uint16_t*)k, (const float*)lse2, s);
+  if (which & 2) launch_tail<uint16_t, Dm>(D, u0, u1, 2, q, k, lse2, partials, s, st);
 }
 
 template <int Dm>

@@ -621,12 +621,335 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_select_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Lengths that are not powers of two
+// ---------------------------------------------------------------------------
+// The real transform of length L is a complex one of length Np (L/2 packed
+// values for even L, L real values for odd L), computed with Bluestein's
+// algorithm: X_k = conj(w_k) sum_n (x_n conj(w_n)) w_{k-n}, w_m = e^{i pi
+// m^2 / Np}, the convolution taken with power-of-two FFTs of length
+// M >= 2 Np - 1 (the Stockham passes above).  The spectrum, the energies and
+// the low-pass go through global scratch (2 Np + 2 complex values per unit:
+// the packed spectrum, then the L/2 + 1 real-input bins); the selection is a
+// radix select over the smoothed row.
+
+// e^{i pi m^2 / Np}, the exponent reduced modulo 2 Np in integers first.
+__device__ __forceinline__ float2 kvc_chirp(int m, int Np) {
+  const long long r = ((long long)m * m) % (2LL * Np);
+  return cispi((float)r / (float)Np);
+}
+
+__device__ __forceinline__ float2 conjf2(float2 a) { return make_float2(a.x, -a.y); }
+
+// Forward DFT of length Np of in(n) (n < Np).  On exit slot s of thread t
+// holds X_k, k = t V + s (meaningful for k < Np).  bhat: FFT_M of the chirp
+// filter, natural order.
+template <int M, int V, class IN>
+__device__ __forceinline__ void kvc_bluestein(IN in, int Np, const float2* __restrict__ bhat,
+                                              float* lds, int t, bool act, float (&re)[V],
+                                              float (&im)[V]) {
+  constexpr int T = M / V;
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < V; ++s) {
+      const int n = in_index<V, T, M>(s, t);
+      const float2 a = n < Np ? cmul(in(n), conjf2(kvc_chirp(n, Np))) : make_float2(0.f, 0.f);
+      re[s] = a.x;
+      im[s] = a.y;
+    }
+  }
+  Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
+  fft_stages<M, V, 1>(re, im, lds, t, act, [&](int s) { return in_index<V, T, M>(s, t); }, none);
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < V; ++s) {
+      const float2 p = cmul(make_float2(re[s], im[s]), bhat[in_index<V, T, M>(s, t)]);
+      re[s] = p.x;
+      im[s] = -p.y;  // conj: the inverse FFT as conj(FFT(conj(.))) / M
+    }
+  }
+  fft_stages<M, V, 1>(re, im, lds, t, act, [&](int s) { return t * V + s; }, none);
+  if (act) {
+    const float invM = 1.0f / (float)M;
+#pragma unroll
+    for (int s = 0; s < V; ++s) {
+      const int k = t * V + s;
+      const float2 c = make_float2(re[s] * invM, -im[s] * invM);
+      const float2 x = k < Np ? cmul(conjf2(kvc_chirp(k, Np)), c) : make_float2(0.f, 0.f);
+      re[s] = x.x;
+      im[s] = x.y;
+    }
+  }
+}
+
+// FFT_M of the chirp filter b (b_m = w_m for 0 <= m < Np, b_{M-m} = w_m for
+// 0 < m < Np, zero between), natural order; one workgroup.
+template <int LOGM>
+__global__ __launch_bounds__(SSS_T) void kvc_sss_chirp_kernel(int Np, float2* __restrict__ bhat) {
+  constexpr int M = 1 << LOGM;
+  constexpr int V = kvc_sss_v(M);
+  constexpr int T = M / V;
+  __shared__ __attribute__((aligned(16))) float lds[Xbuf<M>::kFloats];
+  const int t = threadIdx.x;
+  const bool act = t < T;
+  float re[V], im[V];
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < V; ++s) {
+      const int m = in_index<V, T, M>(s, t);
+      const int mm = m < Np ? m : (M - m < Np ? M - m : -1);
+      const float2 b = mm >= 0 ? kvc_chirp(mm, Np) : make_float2(0.f, 0.f);
+      re[s] = b.x;
+      im[s] = b.y;
+    }
+  }
+  Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
+  fft_stages<M, V, 1>(re, im, lds, t, act, [&](int s) { return in_index<V, T, M>(s, t); }, none);
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < V; ++s) bhat[in_index<V, T, M>(s, t)] = make_float2(re[s], im[s]);
+  }
+}
+
+// Top-k selection from a smoothed row in memory: the b - w largest values
+// among positions [0, L - w) (equal values: lower position first) and the
+// window [L - w, L), ascending.  Four 8-bit radix passes over order-preserving
+// keys find the k-th largest key, then one ordered pass writes the kept
+// positions.
+__device__ __forceinline__ void kvc_select_row(const KvcDesc& D, int u, const float* hrow, int L,
+                                               const int32_t* budgets, const int64_t* offsets,
+                                               int32_t* idx_out, SssShared& sh) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_digit, s_above;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = D.window, ncand = L - w;
+  const int b = budgets[u], k = b - w;
+  const int64_t off = offsets[u];
+  int32_t* out = idx_out + off;
+  for (int i = t; i < w; i += SSS_T) out[max(k, 0) + i] = ncand + i;
+  if (k <= 0) return;
+  if (k >= ncand) {
+    for (int p = t; p < ncand; p += SSS_T) out[p] = p;
+    return;
+  }
+  uint32_t prefix = 0, pmask = 0, want = (uint32_t)k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = t; i < 256; i += SSS_T) hist[i] = 0;
+    __syncthreads();
+    for (int p = t; p < ncand; p += SSS_T) {
+      const uint32_t key = order_key(hrow[p]);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (t < 64) {
+      // lane l owns bins 255-4l .. 252-4l (descending); inclusive scan from the top
+      uint32_t c4[4], own = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c4[e] = hist[255 - 4 * lane - e];
+        own += c4[e];
+      }
+      uint32_t incl = own;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      const uint32_t excl = incl - own;
+      if (excl < want && want <= incl) {
+        uint32_t run = excl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (run < want && want <= run + c4[e]) {
+            s_digit = (uint32_t)(255 - 4 * lane - e);
+            s_above = run;
+          }
+          run += c4[e];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= s_digit << shift;
+    pmask |= 255u << shift;
+    want -= s_above;
+    __syncthreads();
+  }
+  // Keys above `prefix` are all kept, plus the first `want` equal ones.
+  int taken = 0, eq_seen = 0;
+  for (int p0 = 0; p0 < ncand; p0 += SSS_T) {
+    const int p = p0 + t;
+    const bool valid = p < ncand;
+    const uint32_t key = valid ? order_key(hrow[p]) : 0u;
+    const bool gt = valid && key > prefix;
+    const bool eq = valid && key == prefix;
+    int eq_tot, take_tot;
+    const int eq_rank = block_scan<int>(eq ? 1 : 0, sh.si, &eq_tot) + eq_seen;
+    const bool take = gt || (eq && eq_rank < (int)want);
+    const int pos = block_scan<int>(take ? 1 : 0, sh.si, &take_tot) + taken;
+    if (take) out[pos] = p;
+    eq_seen += eq_tot;
+    taken += take_tot;
+  }
+}
+
+template <int LOGM>
+__global__ __launch_bounds__(SSS_T) void kvc_sss_general_kernel(
+    KvcDesc D, int mode, int unit0, const float* s_in, float* s_hat_out,
+    int32_t* __restrict__ kstar_out, const int32_t* __restrict__ budgets,
+    const int64_t* __restrict__ offsets, int32_t* __restrict__ idx_out, float2* scratch,
+    const float2* __restrict__ bhat) {
+  constexpr int M = 1 << LOGM;
+  constexpr int V = kvc_sss_v(M);
+  constexpr int T = M / V;
+  __shared__ __attribute__((aligned(16))) float lds[Xbuf<M>::kFloats];
+  __shared__ SssShared sh;
+  const int u = unit0 + (int)blockIdx.x;
+  const int seq = u / D.upseq;
+  const int within = u - seq * D.upseq;
+  const int L = D.L[seq];
+  const int64_t row = D.srow_base[seq] + (int64_t)within * L;
+  const float* srow = s_in + row;
+  // s_hat goes to its own rows, or over the input rows (read first, position
+  // by position, by the same thread) when the caller keeps it internal.
+  float* hrow = (s_hat_out ? s_hat_out : const_cast<float*>(s_in)) + row;
+  const bool even = (L & 1) == 0;
+  const int Np = even ? L / 2 : L;
+  float2* X = scratch + (size_t)(u - unit0) * (2 * Np + 2);
+  float2* Y = X + Np;  // L/2 + 1 <= Np + 1 bins
+  const int t = threadIdx.x;
+  const bool act = t < T;
+  float re[V], im[V];
+  if (mode & 1) {
+    // Spectrum of the row.
+    auto in_row = [&](int n) {
+      return even ? make_float2(srow[2 * n], srow[2 * n + 1]) : make_float2(srow[n], 0.f);
+    };
+    kvc_bluestein<M, V>(in_row, Np, bhat, lds, t, act, re, im);
+    if (act) {
+#pragma unroll
+      for (int s = 0; s < V; ++s)
+        if (t * V + s < Np) X[t * V + s] = make_float2(re[s], im[s]);
+    }
+    if (t == 0) sh.kstar = L / 2;  // the last bin, should rounding leave E short of rho E(L/2)
+    __syncthreads();
+    // Real bins F_0 .. F_{L/2} (unpacked for even L), their energies in fp64.
+    const int nb = L / 2 + 1;
+    const int per = (nb + SSS_T - 1) / SSS_T;
+    const int k0 = min(nb, t * per), k1 = min(nb, k0 + per);
+    double esum = 0.0;
+    for (int kk = k0; kk < k1; ++kk) {
+      float2 F;
+      if (even) {
+        const float2 zk = X[kk % Np], zm = X[(Np - kk % Np) % Np];
+        const float2 A = make_float2(0.5f * (zk.x + zm.x), 0.5f * (zk.y - zm.y));
+        const float2 B = make_float2(0.5f * (zk.y + zm.y), -0.5f * (zk.x - zm.x));
+        const float2 W = cispi(-2.0f * (float)kk / (float)L);
+        const float2 WB = cmul(W, B);
+        F = make_float2(A.x + WB.x, A.y + WB.y);
+      } else {
+        F = X[kk];
+      }
+      Y[kk] = F;
+      esum += (double)F.x * F.x + (double)F.y * F.y;
+    }
+    double total;
+    const double before = block_scan<double>(esum, sh.sd, &total);
+    const double target = (double)D.rho * total;
+    {
+      double e = before;
+      int cand = L;
+      for (int kk = k0; kk < k1; ++kk) {
+        const float2 F = Y[kk];
+        e += (double)F.x * F.x + (double)F.y * F.y;
+        if (e >= target && cand == L) cand = kk;
+      }
+      if (cand < L) atomicMin(&sh.kstar, cand);
+    }
+    __syncthreads();
+    const int kstar = sh.kstar;
+    if ((mode & 4) && t == 0) kstar_out[u] = kstar;
+    // Masked spectrum, back to the complex sequence the inverse transforms.
+    auto Fm = [&](int kk) { return kk <= kstar ? Y[kk] : make_float2(0.f, 0.f); };
+    for (int kk = t; kk < Np; kk += SSS_T) {
+      float2 z;
+      if (even) {
+        const float2 Fk = Fm(kk), Fr = Fm(Np - kk);
+        const float2 A = make_float2(0.5f * (Fk.x + Fr.x), 0.5f * (Fk.y - Fr.y));
+        const float2 Dd = make_float2(0.5f * (Fk.x - Fr.x), 0.5f * (Fk.y + Fr.y));
+        const float2 B = cmul(cispi(2.0f * (float)kk / (float)L), Dd);
+        z = make_float2(A.x - B.y, A.y + B.x);
+      } else {
+        z = kk <= (L - 1) / 2 ? Fm(kk) : conjf2(Fm(L - kk));
+      }
+      X[kk] = conjf2(z);  // the inverse DFT as conj(DFT(conj(.))) / Np
+    }
+    __syncthreads();
+    kvc_bluestein<M, V>([&](int n) { return X[n]; }, Np, bhat, lds, t, act, re, im);
+    // Blend with the raw row: s_hat = (1 - alpha) s + alpha lowpass.
+    const float invNp = 1.0f / (float)Np, a = D.alpha, oma = 1.0f - D.alpha;
+    if (act) {
+#pragma unroll
+      for (int s = 0; s < V; ++s) {
+        const int m = t * V + s;
+        if (m >= Np) continue;
+        const float lre = re[s] * invNp, lim = -im[s] * invNp;
+        if (even) {
+          const float s0 = srow[2 * m], s1 = srow[2 * m + 1];
+          hrow[2 * m] = oma * s0 + a * lre;
+          hrow[2 * m + 1] = oma * s1 + a * lim;
+        } else {
+          hrow[m] = oma * srow[m] + a * lre;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (mode & 2)
+    kvc_select_row(D, u, (mode & 1) ? hrow : srow, L, budgets, offsets, idx_out, sh);
+}
+
+// Scratch for lengths that are not powers of two: the chirp spectrum and
+// 2 Np + 2 complex values per unit of a launch.
+size_t kvc_sss_scratch_bytes(int L, int units) {
+  if ((L & (L - 1)) == 0) return 0;
+  const int Np = (L & 1) ? L : L / 2;
+  int M = 1;
+  while (M < 2 * Np - 1) M <<= 1;
+  return ((sizeof(float2) * (size_t)M + 255) & ~size_t(255)) +
+         sizeof(float2) * (2 * (size_t)Np + 2) * units;
+}
+
 // Units [u0, u1) must lie in one sequence.
 hipError_t kvc_launch_sss_select(const KvcDesc& D, int u0, int u1, int mode, const float* s_in,
                                  float* s_hat_out, int32_t* kstar_out, const int32_t* budgets,
-                                 const int64_t* offsets, int32_t* idx_out, hipStream_t st) {
+                                 const int64_t* offsets, int32_t* idx_out, void* scratch,
+                                 hipStream_t st) {
   if (u1 <= u0) return hipSuccess;
   const int L = D.L[u0 / D.upseq];
+  if ((L & (L - 1)) != 0) {
+    if (!scratch && (mode & 1)) return hipErrorInvalidValue;
+    const int Np = (L & 1) ? L : L / 2;
+    int logm = 0;
+    while ((1 << logm) < 2 * Np - 1) ++logm;
+    float2* bhat = (float2*)scratch;
+    float2* rows = scratch ? (float2*)((char*)scratch +
+                                       ((sizeof(float2) * ((size_t)1 << logm) + 255) & ~size_t(255)))
+                           : nullptr;
+    void (*chirp)(int, float2*) = nullptr;
+    void (*kern)(KvcDesc, int, int, const float*, float*, int32_t*, const int32_t*, const int64_t*,
+                 int32_t*, float2*, const float2*) = nullptr;
+    switch (logm) {
+#define KVC_GEN(LM) case LM: chirp = kvc_sss_chirp_kernel<LM>; kern = kvc_sss_general_kernel<LM>; break;
+      KVC_GEN(7) KVC_GEN(8) KVC_GEN(9) KVC_GEN(10) KVC_GEN(11) KVC_GEN(12) KVC_GEN(13)
+      KVC_GEN(14) KVC_GEN(15)
+#undef KVC_GEN
+      default: return hipErrorInvalidValue;
+    }
+    if (mode & 1) hipLaunchKernelGGL(chirp, dim3(1), dim3(SSS_T), 0, st, Np, bhat);
+    hipLaunchKernelGGL(kern, dim3(u1 - u0), dim3(SSS_T), 0, st, D, mode, u0, s_in, s_hat_out,
+                       kstar_out, budgets, offsets, idx_out, rows, (const float2*)bhat);
+    return hipGetLastError();
+  }
   void (*kern)(KvcDesc, int, int, const float*, float*, int32_t*, const int32_t*, const int64_t*,
                int32_t*) = nullptr;
   switch (L) {

@@ -72,6 +72,12 @@ CONFIGS = {
                      length_choices=(4096, 8192, 16384, 32768)),
     "long64k": Config("long64k", 4, 1, 48, 4, 8, 128, "bf16",
                       lengths=(65536,), retention=(0.2,)),
+    # an audio length that is not a power of two (40 minutes at 12.5 Hz)
+    "omni30b_30000": Config("omni30b_30000", 5, 1, 48, 4, 8, 128, "bf16", alpha=0.6,
+                            lengths=(30000,), retention=(0.4,)),
+    # mixed lengths, none a power of two, odd and even
+    "ragged_npot": Config("ragged_npot", 6, 3, 4, 2, 4, 128, "bf16",
+                          lengths=(3000, 12345, 777), retention=(0.5, 0.3, 0.8)),
 }
 
 

@@ -490,12 +490,12 @@ def main():
         kst = torch.empty(spec.n_units, dtype=torch.int32, device="cuda")
         ws = out["workspace"]
         api.kvc_scores(spec, prm, q, k, s_rows, ws, stream)
-        api.kvc_smooth(spec, prm, s_rows, sh_rows, kst, stream)
+        api.kvc_smooth(spec, prm, s_rows, sh_rows, kst, stream, ws)
         calls = {
             "budget": lambda: api.kvc_budget(spec, prm, S, out["budgets"], out["offsets"], stream),
             "score_stats": lambda: api.kvc_score_stats(spec, prm, q, k, ws, stream),
             "score_pool": lambda: api.kvc_score_pool(spec, prm, q, k, s_rows, ws, stream),
-            "smooth": lambda: api.kvc_smooth(spec, prm, s_rows, sh_rows, kst, stream),
+            "smooth": lambda: api.kvc_smooth(spec, prm, s_rows, sh_rows, kst, stream, ws),
             "select": lambda: api.kvc_select(spec, prm, sh_rows, out["budgets"], out["offsets"],
                                              out["idx"], stream),
             "gather": lambda: api.kvc_gather(spec, prm, k, v, out["idx"], out["offsets"],

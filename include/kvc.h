@@ -90,7 +90,11 @@ typedef enum { KVC_POOL_SEQUENCE = 0, KVC_POOL_LAYER = 1 } kvc_pool;
 
 /* Problem shape.  Supported: 1 <= n_seq <= 64; head_dim in {64, 128};
  * gqa_group * n_window_q a multiple of 32 and at most 256; every sequence
- * length L a power of two with 64 <= L <= 65536 and L > window;
+ * length L with 64 <= L <= 65536 and L > window, and, when L is not a power
+ * of two, L <= 32768 (even) or L <= 16384 (odd): such lengths take the
+ * transform of step 2 through Bluestein's algorithm (the chirp-z form of
+ * the DFT of length L, or of the L/2 packed values for even L, as a
+ * convolution done with power-of-two FFTs of at most 32768 points);
  * n_layers * n_kv_heads <= 4096. */
 typedef struct {
   int32_t n_seq, n_layers, n_kv_heads, gqa_group, head_dim, n_window_q;
@@ -160,7 +164,9 @@ kvc_status kvc_compress_layers(const kvc_problem *prob, const kvc_params *params
  *
  * kvc_scores: step 1 -> s, device float varlen rows (see above).
  * kvc_smooth: step 2 on given rows s -> s_hat (same layout) and kstar
- *             (device int32 [units]).
+ *             (device int32 [units]).  The workspace (256-byte aligned,
+ *             kvc_plan's workspace_bytes suffice) is used only when some
+ *             length is not a power of two; it may be NULL otherwise.
  * kvc_budget: step 3 -> budgets [units], seg_offsets [units+1].
  * kvc_select: step 4 on given rows s_hat with given budgets/offsets ->
  *             idx_out.  s_hat must be finite.
@@ -182,7 +188,7 @@ kvc_status kvc_score_pool(const kvc_problem *prob, const kvc_params *params,
                           void *workspace, size_t workspace_bytes, void *stream);
 kvc_status kvc_smooth(const kvc_problem *prob, const kvc_params *params,
                       const float *s, float *s_hat, int32_t *kstar,
-                      void *stream);
+                      void *workspace, size_t workspace_bytes, void *stream);
 kvc_status kvc_budget(const kvc_problem *prob, const kvc_params *params,
                       const float *head_scores, int32_t *budgets,
                       int64_t *seg_offsets, void *stream);

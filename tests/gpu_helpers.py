@@ -100,7 +100,8 @@ class Dev:
         s = torch.from_numpy(np.ascontiguousarray(s_flat, dtype=np.float32)).cuda()
         sh = torch.empty_like(s)
         ks = torch.empty(self.spec.n_units, dtype=torch.int32, device="cuda")
-        api.kvc_smooth(self.spec, self.params, s, sh, ks)
+        ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        api.kvc_smooth(self.spec, self.params, s, sh, ks, workspace=ws)
         torch.cuda.synchronize()
         return sh.cpu().numpy(), ks.cpu().numpy()
 

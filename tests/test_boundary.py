@@ -80,7 +80,8 @@ def status(sp, prm=None, **ptrs):
 
 
 def test_invalid_problems_rejected_before_launch():
-    assert status(spec(seq_lens=[3000])) == C.KVC_ERR_UNSUPPORTED          # not a power of two
+    assert status(spec(seq_lens=[32770])) == C.KVC_ERR_UNSUPPORTED         # even, not 2^k, > 32768
+    assert status(spec(seq_lens=[16385])) == C.KVC_ERR_UNSUPPORTED         # odd, > 16384
     assert status(spec(seq_lens=[131072])) == C.KVC_ERR_UNSUPPORTED        # too long
     assert status(spec(seq_lens=[32])) == C.KVC_ERR_UNSUPPORTED            # too short
     assert status(spec(head_dim=96)) == C.KVC_ERR_UNSUPPORTED
@@ -103,6 +104,20 @@ def test_invalid_problems_rejected_before_launch():
     assert status(spec(k_stride=(0, 0, 64))) == C.KVC_ERR_INVALID_ARG     # stride < head_dim
     assert status(spec()) == C.KVC_ERR_WORKSPACE                           # 0 bytes given
     assert C.lib().kvc_last_hip_error() == 0
+
+
+def test_lengths_that_are_not_powers_of_two():
+    # Bluestein's algorithm takes the transform for these; the workspace
+    # grows by the chirp spectrum and two complex rows per unit.
+    for L in (3000, 2047, 32768 - 2, 16383, 100):
+        sp = spec(seq_lens=[L], retention=0.9)
+        rows, ws = api.kvc_plan(sp, api.Params())
+        assert rows == 48 * 4 * math.floor(0.9 * L)
+        n_p = L // 2 if L % 2 == 0 else L
+        assert ws >= 4 * 48 * 4 * L + 16 * n_p * 48 * 4
+    sp = spec(seq_lens=[4096], retention=0.9)
+    rows, ws4096 = api.kvc_plan(sp, api.Params())
+    assert ws4096 < 4 * 48 * 4 * 4096 + 16 * 2048 * 48 * 4   # powers of two need no scratch
 
 
 def test_gqa_96_window_queries_is_supported():

@@ -1,0 +1,102 @@
+"""GPU parity for sequence lengths that are not powers of two: the score
+passes' ragged tiles and tail keys, Spectral Score Smoothing through
+Bluestein's algorithm (the DFT of any length as a chirp convolution done
+with power-of-two FFTs) and the selection from a smoothed row, against the
+oracle (whose DFT is the direct sum for any length), through include/kvc.h.
+
+Criteria as for powers of two (tests/gpu_helpers.py): norm-wise tolerance on
+s and s_hat, k* equal or inside the ambiguity band, selection bit-exact on
+identical rows, end-to-end kept sets equal except within tolerance of the
+threshold, budgets and gathered rows bit-exact.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from audio_kv_cache_amd import synth  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+import tests.test_gpu_parity as P  # noqa: E402
+from tests.gpu_helpers import Dev, check_smoothed_row  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("L", [65, 100, 1000, 3001, 12345, 30000, 32766])
+def test_select_any_length(L):
+    P.say(f"[select] L={L}")
+    H = 4
+    cfg = P.small(n_layers=1, n_kv_heads=H, lengths=(L,), retention=(0.5,), base_ratio=0.0)
+    D = Dev(synth.problem(cfg))
+    rng = np.random.default_rng(L)
+    w = cfg.window
+    rows = [rng.integers(-3, 4, L).astype(np.float32)]
+    r = rng.standard_normal(L).astype(np.float32)
+    r[::7] = 0.0
+    r[::11] = -0.0
+    rows.append(r)
+    rows.append(np.round(rng.random(L), 2).astype(np.float32))
+    rows.append((np.sin(np.arange(L) / 37.0) + 1e-3 * rng.random(L)).astype(np.float32))
+    budgets = np.array([w, L, w + 1 + (L - w) // 3, L - 1], np.int32)
+    offsets = np.concatenate([[0], np.cumsum(budgets)]).astype(np.int64)
+    idx = D.select(np.concatenate(rows), budgets, offsets)
+    for h in range(H):
+        want = O.select(rows[h].astype(np.float64), w, int(budgets[h]))
+        assert np.array_equal(idx[offsets[h]:offsets[h + 1]], want), (h, int(budgets[h]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("L", [66, 67, 100, 999, 1000, 3000, 4097, 12345, 16383])
+def test_smooth_any_length(L, dtype):
+    P.say(f"[smooth] L={L} {dtype}")
+    for alpha, rho in [(0.5, 0.7), (1.0, 0.95), (0.3, 0.2)]:
+        cfg = P.small(n_layers=1, n_kv_heads=4, lengths=(L,), dtype=dtype, alpha=alpha, rho=rho,
+                      retention=(0.9,), base_ratio=0.0)
+        D = Dev(synth.problem(cfg))
+        rows = P._sss_rows(L, 4, np.random.default_rng(L))
+        sh, ks = D.smooth(np.concatenate(rows))
+        for h in range(4):
+            check_smoothed_row(rows[h], sh[h * L:(h + 1) * L], int(ks[h]), alpha, rho, dtype)
+        assert int(ks[3]) == 0            # constant row: only the DC bin
+        assert P.rel_err(sh[3 * L:4 * L], rows[3]) <= 1e-5
+
+
+@pytest.mark.parametrize("L", [30000, 32766])
+def test_smooth_long_lengths(L):
+    P.say(f"[smooth] L={L}")
+    cfg = P.small(n_layers=1, n_kv_heads=2, lengths=(L,), dtype="bf16", alpha=0.6, rho=0.7,
+                  retention=(0.9,), base_ratio=0.0)
+    D = Dev(synth.problem(cfg))
+    rows = P._sss_rows(L, 2, np.random.default_rng(L))
+    sh, ks = D.smooth(np.concatenate(rows))
+    for h in range(2):
+        check_smoothed_row(rows[h], sh[h * L:(h + 1) * L], int(ks[h]), 0.6, 0.7, "bf16")
+
+
+@pytest.mark.parametrize("dtype,d,gqa", [("bf16", 128, 8), ("bf16", 64, 2), ("f32", 64, 2),
+                                         ("f32", 128, 1)])
+def test_scores_any_length(dtype, d, gqa):
+    P.say(f"[scores] {dtype} d={d} gqa={gqa}")
+    cfg = P.small(dtype=dtype, head_dim=d, gqa=gqa, n_seq=3, lengths=(100, 1100, 3001),
+                  retention=(0.9, 0.5, 0.5), base_ratio=0.0)
+    D = Dev(synth.problem(cfg))
+    P._check_scores(D, D.units())
+
+
+def test_scores_any_length_maxpool():
+    cfg = P.small(dtype="bf16", head_dim=128, gqa=8, n_seq=2, lengths=(1000, 2047),
+                  retention=(0.5, 0.5), base_ratio=0.0, score_pool=1)
+    D = Dev(synth.problem(cfg))
+    P._check_scores(D, D.units())
+
+
+def test_compress_ragged_npot():
+    P.say("[e2e] ragged_npot")
+    D = P.dev("ragged_npot")
+    P._check_e2e(D, D.units())
+
+
+def test_compress_omni30b_30000_sampled():
+    P.say("[e2e] omni30b_30000")
+    D = P.dev("omni30b_30000")
+    P._check_e2e(D, [(0, 0, 0), (0, 23, 2), (0, 47, 3)])

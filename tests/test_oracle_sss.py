@@ -36,7 +36,7 @@ def test_lowpass_matches_numpy_irfft_for_every_cutoff(L):
         np.testing.assert_allclose(lp, ref, rtol=0, atol=1e-12)
 
 
-@pytest.mark.parametrize("L", [16, 64, 1024])
+@pytest.mark.parametrize("L", [16, 64, 1024, 100, 999, 3001])
 @pytest.mark.parametrize("c,a,f", [(1.0, 0.5, 3), (0.2, 1.0, 5), (0.0, 1.0, 1), (1.0, 1.0, 7)])
 def test_cosine_closed_form(L, c, a, f):
     # s = c + a cos(2 pi f j / L), 0 < f < L/2: F_0 = L c, F_f = a L / 2, rest 0.
