@@ -51,12 +51,15 @@ __host__ __device__ inline int64_t kvc_kv_offset(const int64_t (&st)[3], const K
 
 // Score tiles of one unit's L keys: tiles of KVC_TILE_KEYS keys over the
 // first L64 = L - L % 64 keys (the last one may be shorter, a multiple of 64),
-// then one tail tile of the last L % 64 keys when there are any.
+// then KVC_TAIL_SPLITS tail tiles sharing the last L % 64 keys when there are
+// any (at most KVC_TAIL_KEYS each).
+#define KVC_TAIL_SPLITS 4
+#define KVC_TAIL_KEYS 16
 __host__ __device__ inline int kvc_main_tiles(int L) {
   return ((L & ~63) + KVC_TILE_KEYS - 1) / KVC_TILE_KEYS;
 }
 __host__ __device__ inline int kvc_tiles_per_unit(int L) {
-  return kvc_main_tiles(L) + ((L & 63) ? 1 : 0);
+  return kvc_main_tiles(L) + ((L & 63) ? KVC_TAIL_SPLITS : 0);
 }
 
 // Kernel launchers (defined next to each kernel).

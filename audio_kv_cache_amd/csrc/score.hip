@@ -84,7 +84,7 @@ __device__ inline int xcd_local_tile(int b, int n) {
 
 struct TileInfo {
   int seq, u, l, h, t, tpu, L, keys, key0;
-  bool tail;   // the L % 64 keys past the last multiple of 64 (kvc_score_tail_kernel)
+  bool tail;   // a tile of the L % 64 keys past the last multiple of 64 (kvc_score_tail_kernel)
 };
 
 __device__ inline TileInfo tile_info(const KvcDesc& Dsc, int tile) {
@@ -101,7 +101,7 @@ __device__ inline TileInfo tile_info(const KvcDesc& Dsc, int tile) {
   ti.l = uin / Dsc.n_heads;
   ti.h = uin - ti.l * Dsc.n_heads;
   const int L64 = ti.L & ~63;
-  ti.tail = ti.t == kvc_main_tiles(ti.L);
+  ti.tail = ti.t >= kvc_main_tiles(ti.L);
   ti.key0 = ti.tail ? L64 : ti.t * KVC_TILE_KEYS;
   ti.keys = ti.tail ? ti.L - L64 : min(KVC_TILE_KEYS, L64 - ti.key0);
   return ti;
@@ -819,23 +819,32 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
   }
 }
 
-// The L % 64 keys of each unit past its last multiple of 64: in mode 1 the
-// statistics pass's (max, sum) per window query over them (the tail tile's
-// partial, folded with the others), in mode 2 their pooled scores.  Plain
-// fp32 dot products; one workgroup per unit.
+// The L % 64 keys of each unit past its last multiple of 64, split into
+// KVC_TAIL_SPLITS ranges of at most KVC_TAIL_KEYS keys, one workgroup per
+// (unit, range) and one thread per window query.  Mode 1: the statistics
+// pass's (max, sum) per query over the range (a tile's partial, folded with
+// the others); mode 2: the range's pooled scores.  Plain fp32 dot products,
+// each query row read once and the keys broadcast from LDS.
 template <class E, int D>
-__global__ __launch_bounds__(256) void kvc_score_tail_kernel(KvcDesc Dsc, int unit0, int mode,
-                                                             const E* __restrict__ q,
-                                                             const E* __restrict__ k,
-                                                             const float* __restrict__ lse2,
-                                                             float2* __restrict__ partials,
-                                                             float* __restrict__ s) {
-  __shared__ float sK[63][D + 1];
-  __shared__ float sPart[4][64];
-  const int u = unit0 + (int)blockIdx.x;
+__global__ __launch_bounds__(KVC_MAX_GW) void kvc_score_tail_kernel(KvcDesc Dsc, int unit0,
+                                                                    int mode,
+                                                                    const E* __restrict__ q,
+                                                                    const E* __restrict__ k,
+                                                                    const float* __restrict__ lse2,
+                                                                    float2* __restrict__ partials,
+                                                                    float* __restrict__ s) {
+  constexpr int NK = KVC_TAIL_KEYS;
+  __shared__ __attribute__((aligned(16))) float sK[NK][D];
+  __shared__ float sP[KVC_MAX_GW][NK + 1];
+  __shared__ float sH[KVC_MAX_GW][NK];
+  const int u = unit0 + (int)blockIdx.x / KVC_TAIL_SPLITS;
+  const int split = (int)blockIdx.x % KVC_TAIL_SPLITS;
   const int seq = u / Dsc.upseq, within = u - seq * Dsc.upseq;
   const int l = within / Dsc.n_heads, h = within - l * Dsc.n_heads;
   const int L = Dsc.L[seq], L64 = L & ~63, nt = L - L64;
+  const int per = (nt + KVC_TAIL_SPLITS - 1) / KVC_TAIL_SPLITS;
+  const int j0 = L64 + split * per;
+  const int nk = max(0, min(per, L - j0));
   const int gw = Dsc.gw;
   const float c = kLog2e / sqrtf((float)D);
   auto val = [](E x) -> float {
@@ -844,50 +853,65 @@ __global__ __launch_bounds__(256) void kvc_score_tail_kernel(KvcDesc Dsc, int un
   };
   const E* qg = q + kvc_q_offset(Dsc, seq, l, h);
   const E* ku = k + kvc_kv_offset(Dsc.ks, Dsc, seq, l, h);
-  for (int i = threadIdx.x; i < nt * D; i += 256) {
+  for (int i = threadIdx.x; i < nk * D; i += KVC_MAX_GW) {
     const int j = i / D, cc = i - j * D;
-    sK[j][cc] = val(ku[(int64_t)(L64 + j) * Dsc.ks[2] + cc]);
+    sK[j][cc] = val(ku[(int64_t)(j0 + j) * Dsc.ks[2] + cc]);
   }
   __syncthreads();
-  if (mode == 1) {
-    const int tile = Dsc.tile_base[seq] + within * kvc_tiles_per_unit(L) + kvc_main_tiles(L);
-    for (int r = threadIdx.x; r < gw; r += 256) {
-      const E* qr = qg + (size_t)r * D;
-      float m = -INFINITY, z = 0.f;
-      for (int j = 0; j < nt; ++j) {
-        float dot = 0.f;
-        for (int cc = 0; cc < D; ++cc) dot = fmaf(val(qr[cc]), sK[j][cc], dot);
-        merge_stat(m, z, dot, 1.0f, c);
+  const int r = threadIdx.x;
+  float acc[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) acc[j] = 0.f;
+  if (r < gw) {
+    const E* qr = qg + (size_t)r * D;
+    for (int c0 = 0; c0 < D; c0 += 8) {
+      float qv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = val(qr[c0 + e]);
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        if (j < nk) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[j] = fmaf(qv[e], sK[j][c0 + e], acc[j]);
+        }
       }
+    }
+  }
+  if (mode == 1) {
+    if (r < gw) {
+      float m = -INFINITY, z = 0.f;
+#pragma unroll
+      for (int j = 0; j < NK; ++j)
+        if (j < nk) merge_stat(m, z, acc[j], 1.0f, c);
+      const int tile = Dsc.tile_base[seq] + within * kvc_tiles_per_unit(L) + kvc_main_tiles(L) +
+                       split;
       partials[(size_t)tile * gw + r] = make_float2(m, z);
     }
     return;
   }
-  // Pooling: thread (key j, part p) sums the probabilities of the heads
-  // g = p, p + 4, ... (each head's W rows), then the parts are folded.
-  const int j = threadIdx.x & 63, part = threadIdx.x >> 6;
-  const int W = Dsc.nwin, G = gw / W;
-  const float* lu = lse2 + (size_t)u * gw;
-  float acc = Dsc.score_max ? 0.f : 0.f;
-  if (j < nt) {
-    for (int g = part; g < G; g += 4) {
-      float v = 0.f;
-      for (int r = g * W; r < (g + 1) * W; ++r) {
-        const E* qr = qg + (size_t)r * D;
-        float dot = 0.f;
-        for (int cc = 0; cc < D; ++cc) dot = fmaf(val(qr[cc]), sK[j][cc], dot);
-        v += __builtin_amdgcn_exp2f(fmaf(dot, c, -lu[r]));
-      }
-      acc = Dsc.score_max ? fmaxf(acc, v) : acc + v;
-    }
+  if (nk == 0) return;
+  if (r < gw) {
+    const float lr = lse2[(size_t)u * gw + r];
+#pragma unroll
+    for (int j = 0; j < NK; ++j) sP[r][j] = __builtin_amdgcn_exp2f(fmaf(acc[j], c, -lr));
   }
-  sPart[part][j] = acc;
   __syncthreads();
-  if (part == 0 && j < nt) {
+  // Per (head g, key j): the sum over the head's W window queries; then over
+  // heads, the mean over all G W queries or the largest head mean.
+  const int W = Dsc.nwin, G = gw / W;
+  for (int x = threadIdx.x; x < G * NK; x += KVC_MAX_GW) {
+    const int g = x / NK, j = x - g * NK;
+    float v = 0.f;
+    for (int rr = g * W; rr < (g + 1) * W; ++rr) v += sP[rr][j];
+    sH[g][j] = v;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nk) {
+    const int j = threadIdx.x;
+    float a = 0.f;
+    for (int g = 0; g < G; ++g) a = Dsc.score_max ? fmaxf(a, sH[g][j]) : a + sH[g][j];
     float* srow = s + Dsc.srow_base[seq] + (int64_t)within * L;
-    const float a = sPart[0][j], b = sPart[1][j], cc2 = sPart[2][j], d2 = sPart[3][j];
-    srow[L64 + j] = Dsc.score_max ? fmaxf(fmaxf(a, b), fmaxf(cc2, d2)) / (float)W
-                                  : ((a + b) + (cc2 + d2)) / (float)gw;
+    srow[j0 + j] = Dsc.score_max ? a / (float)W : a / (float)gw;
   }
 }
 
@@ -895,8 +919,9 @@ template <class E, int Dm>
 static void launch_tail(const KvcDesc& D, int u0, int u1, int mode, const void* q, const void* k,
                         const float* lse2, float2* partials, float* s, hipStream_t st) {
   if ((D.L[u0 / D.upseq] & 63) == 0) return;
-  hipLaunchKernelGGL((kvc_score_tail_kernel<E, Dm>), dim3(u1 - u0), dim3(256), 0, st, D, u0, mode,
-                     (const E*)q, (const E*)k, lse2, partials, s);
+  hipLaunchKernelGGL((kvc_score_tail_kernel<E, Dm>), dim3((u1 - u0) * KVC_TAIL_SPLITS),
+                     dim3(KVC_MAX_GW), 0, st, D, u0, mode, (const E*)q, (const E*)k, lse2,
+                     partials, s);
 }
 
 size_t kvc_scores_workspace(const KvcDesc& D) {

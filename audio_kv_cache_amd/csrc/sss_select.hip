@@ -230,24 +230,30 @@ __device__ __forceinline__ void xchg(float (&re)[V], float (&im)[V], float* lds,
     exchange<V>(re, im, lds, act, widx, ridx, x);
 }
 
+// Radix of the pass that follows sub-length Ns: V values per thread, at most
+// RM (a smaller RM trades an extra pass for fewer live registers).
+__host__ __device__ constexpr int fft_radix(int N, int V, int Ns, int RM) {
+  return (N / Ns) < (V < RM ? V : RM) ? (N / Ns) : (V < RM ? V : RM);
+}
+
 // Forward complex FFT of length N = T V, passes from sub-length Ns on.  On
-// entry slot s holds x[in_index<V, T, N>(s)]; on exit slot s holds
-// X[ridx_final(s)] (plus the extra read of `xf`, if any).
-template <int N, int V, int Ns, class RF>
+// entry slot s holds x[in_index<fft_radix(N, V, 1, RM), T, N>(s)]; on exit
+// slot s holds X[ridx_final(s)] (plus the extra read of `xf`, if any).
+template <int N, int V, int Ns, int RM = 32, class RF>
 __device__ __forceinline__ void fft_stages(float (&re)[V], float (&im)[V], float* lds, int t,
                                            bool act, RF ridx_final, Extra& xf) {
   constexpr int T = N / V;
-  constexpr int R = (N / Ns) < V ? (N / Ns) : V;
+  constexpr int R = fft_radix(N, V, Ns, RM);
   constexpr int Nn = Ns * R;
   if (act) fft_pass<V, R, T, Ns>(re, im, t);
   auto wf = [&](int s) { return out_index<R, T, Ns>(s, t); };
   if constexpr (Nn >= N) {
     xchg<N, V>(re, im, lds, act, wf, ridx_final, xf);
   } else {
-    constexpr int R2 = (N / Nn) < V ? (N / Nn) : V;
+    constexpr int R2 = fft_radix(N, V, Nn, RM);
     Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
     xchg<N, V>(re, im, lds, act, wf, [&](int s) { return in_index<R2, T, N>(s, t); }, none);
-    fft_stages<N, V, Nn>(re, im, lds, t, act, ridx_final, xf);
+    fft_stages<N, V, Nn, RM>(re, im, lds, t, act, ridx_final, xf);
   }
 }
 
@@ -469,14 +475,16 @@ __device__ __forceinline__ void smooth_unit(const KvcDesc& D, int mode, int u, c
 }
 
 // ---------------------------------------------------------------------------
-// Selection for one unit from s_hat held as in smooth_unit's output.
+// Selection for one unit of L positions from s_hat held as in smooth_unit's
+// output (thread t: positions 2 V t + 2 s in re[s], 2 V t + 2 s + 1 in
+// im[s]; positions >= L are not part of the row).  stage: kStage ints of
+// LDS, free for the output staging.
 // ---------------------------------------------------------------------------
-template <int N, int V>
-__device__ __forceinline__ void select_unit(const KvcDesc& D, int u, float (&re)[V], float (&im)[V],
-                            const int32_t* budgets, const int64_t* offsets, int32_t* idx_out,
-                            SssShared& sh, int* stage, int t, bool act) {
-  constexpr int kStage = Xbuf<N>::kFloats;  // the FFT exchange buffer, free by now
-  constexpr int L = 2 * N;
+template <int V>
+__device__ __forceinline__ void select_unit(const KvcDesc& D, int u, int L, float (&re)[V],
+                            float (&im)[V], const int32_t* budgets, const int64_t* offsets,
+                            int32_t* idx_out, SssShared& sh, int* stage, int kStage, int t,
+                            bool act) {
   const int w = D.window;
   const int ncand = L - w;
   const int b = budgets[u];
@@ -537,7 +545,7 @@ __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, float (&re)
     for (int s = 0; s < 2 * V; ++s) {
       const int p = p0 + s;
       bool sel;
-      if (p >= ncand) sel = true;
+      if (p >= ncand) sel = p < L;
       else if (take_all) sel = true;
       else if (take_none) sel = false;
       else if (KEY(s) > thr) sel = true;
@@ -616,8 +624,8 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_select_kernel(
   }
   if (mode & 2) {
     __syncthreads();  // the exchange buffer becomes the output staging area
-    select_unit<N, V>(D, u, re, im, budgets, offsets, idx_out, sh, reinterpret_cast<int*>(lds), t,
-                      act);
+    select_unit<V>(D, u, L, re, im, budgets, offsets, idx_out, sh, reinterpret_cast<int*>(lds),
+                   Xbuf<N>::kFloats, t, act);
   }
 }
 
@@ -628,14 +636,34 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_select_kernel(
 // values for even L, L real values for odd L), computed with Bluestein's
 // algorithm: X_k = conj(w_k) sum_n (x_n conj(w_n)) w_{k-n}, w_m = e^{i pi
 // m^2 / Np}, the convolution taken with power-of-two FFTs of length
-// M >= 2 Np - 1 (the Stockham passes above).  The spectrum, the energies and
-// the low-pass go through global scratch (2 Np + 2 complex values per unit:
-// the packed spectrum, then the L/2 + 1 real-input bins); the selection is a
-// radix select over the smoothed row.
+// M >= 2 Np - 1 (the Stockham passes above).  A per-launch prologue computes
+// the table conj(w_n), n < Np, and FFT_M of the chirp filter; each unit's
+// packed spectrum and its L/2 + 1 real bins go through global scratch
+// (2 Np + 2 complex values per unit).  Selection then runs on the smoothed
+// row in registers, as for powers of two.
 
-// e^{i pi m^2 / Np}, the exponent reduced modulo 2 Np in integers first.
+// Scratch regions of one launch, 256-byte aligned: FFT_M of the chirp filter
+// (M values), the chirp table (Np values), then the units' rows.
+struct BluesteinScratch {
+  size_t chirp_off, rows_off, bytes_per_unit;
+};
+__host__ __device__ inline size_t kvc_up256(size_t x) { return (x + 255) & ~size_t(255); }
+__host__ inline BluesteinScratch kvc_bluestein_scratch(int Np, int M) {
+  BluesteinScratch b;
+  b.chirp_off = kvc_up256(sizeof(float2) * (size_t)M);
+  b.rows_off = b.chirp_off + kvc_up256(sizeof(float2) * (size_t)Np);
+  b.bytes_per_unit = sizeof(float2) * (2 * (size_t)Np + 2);
+  return b;
+}
+
+// Largest radix of the Bluestein FFTs: radix-32 passes over 32 values per
+// thread exceed the 128 registers a 1024-thread workgroup leaves each lane.
+__host__ __device__ constexpr int kvc_bluestein_rm(int M) { return M >= 32 * SSS_T ? 16 : 32; }
+
+// e^{i pi m^2 / Np}, the exponent reduced modulo 2 Np in integers first
+// (m < 16384, so m^2 fits 32 bits).
 __device__ __forceinline__ float2 kvc_chirp(int m, int Np) {
-  const long long r = ((long long)m * m) % (2LL * Np);
+  const uint32_t r = ((uint32_t)m * (uint32_t)m) % (uint32_t)(2 * Np);
   return cispi((float)r / (float)Np);
 }
 
@@ -643,60 +671,67 @@ __device__ __forceinline__ float2 conjf2(float2 a) { return make_float2(a.x, -a.
 
 // Forward DFT of length Np of in(n) (n < Np).  On exit slot s of thread t
 // holds X_k, k = t V + s (meaningful for k < Np).  bhat: FFT_M of the chirp
-// filter, natural order.
+// filter, natural order; cw: conj(w_n), n < Np.
 template <int M, int V, class IN>
 __device__ __forceinline__ void kvc_bluestein(IN in, int Np, const float2* __restrict__ bhat,
-                                              float* lds, int t, bool act, float (&re)[V],
-                                              float (&im)[V]) {
+                                              const float2* __restrict__ cw, float* lds, int t,
+                                              bool act, float (&re)[V], float (&im)[V]) {
   constexpr int T = M / V;
+  constexpr int RM = kvc_bluestein_rm(M);
+  constexpr int R0 = fft_radix(M, V, 1, RM);
   if (act) {
 #pragma unroll
     for (int s = 0; s < V; ++s) {
-      const int n = in_index<V, T, M>(s, t);
-      const float2 a = n < Np ? cmul(in(n), conjf2(kvc_chirp(n, Np))) : make_float2(0.f, 0.f);
+      const int n = in_index<R0, T, M>(s, t);
+      const float2 a = n < Np ? cmul(in(n), cw[n]) : make_float2(0.f, 0.f);
       re[s] = a.x;
       im[s] = a.y;
     }
   }
   Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
-  fft_stages<M, V, 1>(re, im, lds, t, act, [&](int s) { return in_index<V, T, M>(s, t); }, none);
+  fft_stages<M, V, 1, RM>(re, im, lds, t, act, [&](int s) { return in_index<R0, T, M>(s, t); }, none);
   if (act) {
 #pragma unroll
     for (int s = 0; s < V; ++s) {
-      const float2 p = cmul(make_float2(re[s], im[s]), bhat[in_index<V, T, M>(s, t)]);
+      const float2 p = cmul(make_float2(re[s], im[s]), bhat[in_index<R0, T, M>(s, t)]);
       re[s] = p.x;
       im[s] = -p.y;  // conj: the inverse FFT as conj(FFT(conj(.))) / M
     }
   }
-  fft_stages<M, V, 1>(re, im, lds, t, act, [&](int s) { return t * V + s; }, none);
+  fft_stages<M, V, 1, RM>(re, im, lds, t, act, [&](int s) { return t * V + s; }, none);
   if (act) {
     const float invM = 1.0f / (float)M;
 #pragma unroll
     for (int s = 0; s < V; ++s) {
       const int k = t * V + s;
       const float2 c = make_float2(re[s] * invM, -im[s] * invM);
-      const float2 x = k < Np ? cmul(conjf2(kvc_chirp(k, Np)), c) : make_float2(0.f, 0.f);
+      const float2 x = k < Np ? cmul(cw[k], c) : make_float2(0.f, 0.f);
       re[s] = x.x;
       im[s] = x.y;
     }
   }
 }
 
-// FFT_M of the chirp filter b (b_m = w_m for 0 <= m < Np, b_{M-m} = w_m for
-// 0 < m < Np, zero between), natural order; one workgroup.
+// The launch prologue: cw[n] = conj(w_n) for n < Np, and FFT_M of the chirp
+// filter b (b_m = w_m for 0 <= m < Np, b_{M-m} = w_m for 0 < m < Np, zero
+// between), natural order; one workgroup.
 template <int LOGM>
-__global__ __launch_bounds__(SSS_T) void kvc_sss_chirp_kernel(int Np, float2* __restrict__ bhat) {
+__global__ __launch_bounds__(SSS_T) void kvc_sss_chirp_kernel(int Np, float2* __restrict__ bhat,
+                                                              float2* __restrict__ cw) {
   constexpr int M = 1 << LOGM;
   constexpr int V = kvc_sss_v(M);
   constexpr int T = M / V;
+  constexpr int RM = kvc_bluestein_rm(M);
+  constexpr int R0 = fft_radix(M, V, 1, RM);
   __shared__ __attribute__((aligned(16))) float lds[Xbuf<M>::kFloats];
   const int t = threadIdx.x;
   const bool act = t < T;
+  for (int n = t; n < Np; n += SSS_T) cw[n] = conjf2(kvc_chirp(n, Np));
   float re[V], im[V];
   if (act) {
 #pragma unroll
     for (int s = 0; s < V; ++s) {
-      const int m = in_index<V, T, M>(s, t);
+      const int m = in_index<R0, T, M>(s, t);
       const int mm = m < Np ? m : (M - m < Np ? M - m : -1);
       const float2 b = mm >= 0 ? kvc_chirp(mm, Np) : make_float2(0.f, 0.f);
       re[s] = b.x;
@@ -704,100 +739,19 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_chirp_kernel(int Np, float2* __
     }
   }
   Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
-  fft_stages<M, V, 1>(re, im, lds, t, act, [&](int s) { return in_index<V, T, M>(s, t); }, none);
+  fft_stages<M, V, 1, RM>(re, im, lds, t, act, [&](int s) { return in_index<R0, T, M>(s, t); }, none);
   if (act) {
 #pragma unroll
-    for (int s = 0; s < V; ++s) bhat[in_index<V, T, M>(s, t)] = make_float2(re[s], im[s]);
-  }
-}
-
-// Top-k selection from a smoothed row in memory: the b - w largest values
-// among positions [0, L - w) (equal values: lower position first) and the
-// window [L - w, L), ascending.  Four 8-bit radix passes over order-preserving
-// keys find the k-th largest key, then one ordered pass writes the kept
-// positions.
-__device__ __forceinline__ void kvc_select_row(const KvcDesc& D, int u, const float* hrow, int L,
-                                               const int32_t* budgets, const int64_t* offsets,
-                                               int32_t* idx_out, SssShared& sh) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_digit, s_above;
-  const int t = threadIdx.x, lane = t & 63;
-  const int w = D.window, ncand = L - w;
-  const int b = budgets[u], k = b - w;
-  const int64_t off = offsets[u];
-  int32_t* out = idx_out + off;
-  for (int i = t; i < w; i += SSS_T) out[max(k, 0) + i] = ncand + i;
-  if (k <= 0) return;
-  if (k >= ncand) {
-    for (int p = t; p < ncand; p += SSS_T) out[p] = p;
-    return;
-  }
-  uint32_t prefix = 0, pmask = 0, want = (uint32_t)k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = t; i < 256; i += SSS_T) hist[i] = 0;
-    __syncthreads();
-    for (int p = t; p < ncand; p += SSS_T) {
-      const uint32_t key = order_key(hrow[p]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (t < 64) {
-      // lane l owns bins 255-4l .. 252-4l (descending); inclusive scan from the top
-      uint32_t c4[4], own = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c4[e] = hist[255 - 4 * lane - e];
-        own += c4[e];
-      }
-      uint32_t incl = own;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-      }
-      const uint32_t excl = incl - own;
-      if (excl < want && want <= incl) {
-        uint32_t run = excl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (run < want && want <= run + c4[e]) {
-            s_digit = (uint32_t)(255 - 4 * lane - e);
-            s_above = run;
-          }
-          run += c4[e];
-        }
-      }
-    }
-    __syncthreads();
-    prefix |= s_digit << shift;
-    pmask |= 255u << shift;
-    want -= s_above;
-    __syncthreads();
-  }
-  // Keys above `prefix` are all kept, plus the first `want` equal ones.
-  int taken = 0, eq_seen = 0;
-  for (int p0 = 0; p0 < ncand; p0 += SSS_T) {
-    const int p = p0 + t;
-    const bool valid = p < ncand;
-    const uint32_t key = valid ? order_key(hrow[p]) : 0u;
-    const bool gt = valid && key > prefix;
-    const bool eq = valid && key == prefix;
-    int eq_tot, take_tot;
-    const int eq_rank = block_scan<int>(eq ? 1 : 0, sh.si, &eq_tot) + eq_seen;
-    const bool take = gt || (eq && eq_rank < (int)want);
-    const int pos = block_scan<int>(take ? 1 : 0, sh.si, &take_tot) + taken;
-    if (take) out[pos] = p;
-    eq_seen += eq_tot;
-    taken += take_tot;
+    for (int s = 0; s < V; ++s) bhat[in_index<R0, T, M>(s, t)] = make_float2(re[s], im[s]);
   }
 }
 
 template <int LOGM>
 __global__ __launch_bounds__(SSS_T) void kvc_sss_general_kernel(
-    KvcDesc D, int mode, int unit0, const float* s_in, float* s_hat_out,
+    KvcDesc D, int mode, int unit0, const float* __restrict__ s_in, float* __restrict__ s_hat_out,
     int32_t* __restrict__ kstar_out, const int32_t* __restrict__ budgets,
-    const int64_t* __restrict__ offsets, int32_t* __restrict__ idx_out, float2* scratch,
-    const float2* __restrict__ bhat) {
+    const int64_t* __restrict__ offsets, int32_t* __restrict__ idx_out, float2* __restrict__ rows,
+    const float2* __restrict__ bhat, const float2* __restrict__ cw) {
   constexpr int M = 1 << LOGM;
   constexpr int V = kvc_sss_v(M);
   constexpr int T = M / V;
@@ -809,22 +763,24 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_general_kernel(
   const int L = D.L[seq];
   const int64_t row = D.srow_base[seq] + (int64_t)within * L;
   const float* srow = s_in + row;
-  // s_hat goes to its own rows, or over the input rows (read first, position
-  // by position, by the same thread) when the caller keeps it internal.
-  float* hrow = (s_hat_out ? s_hat_out : const_cast<float*>(s_in)) + row;
   const bool even = (L & 1) == 0;
   const int Np = even ? L / 2 : L;
-  float2* X = scratch + (size_t)(u - unit0) * (2 * Np + 2);
-  float2* Y = X + Np;  // L/2 + 1 <= Np + 1 bins
   const int t = threadIdx.x;
   const bool act = t < T;
-  float re[V], im[V];
+  // Values for the selection: position 2 VS t + 2 s in kr[s], the next in
+  // ki[s] (T threads cover 2 VS T >= L positions).
+  constexpr int VS = V < 16 ? V : 16;
+  static_assert(2 * VS * T >= M, "selection layout covers the row");
+  float kr[VS], ki[VS];
   if (mode & 1) {
+    float re[V], im[V];
+    float2* X = rows + (size_t)(u - unit0) * (2 * Np + 2);
+    float2* Y = X + Np;  // L/2 + 1 <= Np + 1 bins
     // Spectrum of the row.
     auto in_row = [&](int n) {
       return even ? make_float2(srow[2 * n], srow[2 * n + 1]) : make_float2(srow[n], 0.f);
     };
-    kvc_bluestein<M, V>(in_row, Np, bhat, lds, t, act, re, im);
+    kvc_bluestein<M, V>(in_row, Np, bhat, cw, lds, t, act, re, im);
     if (act) {
 #pragma unroll
       for (int s = 0; s < V; ++s)
@@ -884,39 +840,73 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_general_kernel(
       X[kk] = conjf2(z);  // the inverse DFT as conj(DFT(conj(.))) / Np
     }
     __syncthreads();
-    kvc_bluestein<M, V>([&](int n) { return X[n]; }, Np, bhat, lds, t, act, re, im);
-    // Blend with the raw row: s_hat = (1 - alpha) s + alpha lowpass.
+    kvc_bluestein<M, V>([&](int n) { return X[n]; }, Np, bhat, cw, lds, t, act, re, im);
+    // Blend with the raw row: s_hat = (1 - alpha) s + alpha lowpass, into
+    // LDS by position for the selection.
     const float invNp = 1.0f / (float)Np, a = D.alpha, oma = 1.0f - D.alpha;
+    float* hrow = (mode & 4) ? s_hat_out + row : nullptr;
     if (act) {
 #pragma unroll
       for (int s = 0; s < V; ++s) {
         const int m = t * V + s;
-        if (m >= Np) continue;
         const float lre = re[s] * invNp, lim = -im[s] * invNp;
         if (even) {
-          const float s0 = srow[2 * m], s1 = srow[2 * m + 1];
-          hrow[2 * m] = oma * s0 + a * lre;
-          hrow[2 * m + 1] = oma * s1 + a * lim;
-        } else {
-          hrow[m] = oma * srow[m] + a * lre;
+          if (m < Np) {
+            // (rows of a sequence after one of odd length may start at an odd
+            // float offset: scalar accesses)
+            const float h0 = oma * srow[2 * m] + a * lre, h1 = oma * srow[2 * m + 1] + a * lim;
+            lds[2 * m] = h0;
+            lds[2 * m + 1] = h1;
+            if (hrow) {
+              hrow[2 * m] = h0;
+              hrow[2 * m + 1] = h1;
+            }
+          }
+        } else if (m < L) {
+          const float h = oma * srow[m] + a * lre;
+          lds[m] = h;
+          if (hrow) hrow[m] = h;
         }
       }
     }
+    if (!(mode & 2)) return;
     __syncthreads();
+    if (act) {
+#pragma unroll
+      for (int s = 0; s < VS; ++s) {
+        const int p = 2 * VS * t + 2 * s;
+        kr[s] = p < L ? lds[p] : 0.f;
+        ki[s] = p + 1 < L ? lds[p + 1] : 0.f;
+      }
+    }
+  } else if (act) {
+#pragma unroll
+    for (int s = 0; s < VS; ++s) {
+      const int p = 2 * VS * t + 2 * s;
+      kr[s] = p < L ? srow[p] : 0.f;
+      ki[s] = p + 1 < L ? srow[p + 1] : 0.f;
+    }
   }
-  if (mode & 2)
-    kvc_select_row(D, u, (mode & 1) ? hrow : srow, L, budgets, offsets, idx_out, sh);
+  if (mode & 2) {
+    __syncthreads();  // the exchange buffer becomes the output staging area
+    select_unit<VS>(D, u, L, kr, ki, budgets, offsets, idx_out, sh, reinterpret_cast<int*>(lds),
+                    Xbuf<M>::kFloats, t, act);
+  }
 }
 
-// Scratch for lengths that are not powers of two: the chirp spectrum and
-// 2 Np + 2 complex values per unit of a launch.
+static int kvc_bluestein_logm(int L) {
+  const int Np = (L & 1) ? L : L / 2;
+  int logm = 0;
+  while ((1 << logm) < 2 * Np - 1) ++logm;
+  return logm;
+}
+
+// Scratch for lengths that are not powers of two (see BluesteinScratch).
 size_t kvc_sss_scratch_bytes(int L, int units) {
   if ((L & (L - 1)) == 0) return 0;
   const int Np = (L & 1) ? L : L / 2;
-  int M = 1;
-  while (M < 2 * Np - 1) M <<= 1;
-  return ((sizeof(float2) * (size_t)M + 255) & ~size_t(255)) +
-         sizeof(float2) * (2 * (size_t)Np + 2) * units;
+  const BluesteinScratch b = kvc_bluestein_scratch(Np, 1 << kvc_bluestein_logm(L));
+  return b.rows_off + b.bytes_per_unit * (size_t)units;
 }
 
 // Units [u0, u1) must lie in one sequence.
@@ -929,15 +919,15 @@ hipError_t kvc_launch_sss_select(const KvcDesc& D, int u0, int u1, int mode, con
   if ((L & (L - 1)) != 0) {
     if (!scratch && (mode & 1)) return hipErrorInvalidValue;
     const int Np = (L & 1) ? L : L / 2;
-    int logm = 0;
-    while ((1 << logm) < 2 * Np - 1) ++logm;
-    float2* bhat = (float2*)scratch;
-    float2* rows = scratch ? (float2*)((char*)scratch +
-                                       ((sizeof(float2) * ((size_t)1 << logm) + 255) & ~size_t(255)))
-                           : nullptr;
-    void (*chirp)(int, float2*) = nullptr;
+    const int logm = kvc_bluestein_logm(L);
+    const BluesteinScratch b = kvc_bluestein_scratch(Np, 1 << logm);
+    char* base = (char*)scratch;
+    float2* bhat = scratch ? (float2*)base : nullptr;
+    float2* cw = scratch ? (float2*)(base + b.chirp_off) : nullptr;
+    float2* rows = scratch ? (float2*)(base + b.rows_off) : nullptr;
+    void (*chirp)(int, float2*, float2*) = nullptr;
     void (*kern)(KvcDesc, int, int, const float*, float*, int32_t*, const int32_t*, const int64_t*,
-                 int32_t*, float2*, const float2*) = nullptr;
+                 int32_t*, float2*, const float2*, const float2*) = nullptr;
     switch (logm) {
 #define KVC_GEN(LM) case LM: chirp = kvc_sss_chirp_kernel<LM>; kern = kvc_sss_general_kernel<LM>; break;
       KVC_GEN(7) KVC_GEN(8) KVC_GEN(9) KVC_GEN(10) KVC_GEN(11) KVC_GEN(12) KVC_GEN(13)
@@ -945,9 +935,10 @@ hipError_t kvc_launch_sss_select(const KvcDesc& D, int u0, int u1, int mode, con
 #undef KVC_GEN
       default: return hipErrorInvalidValue;
     }
-    if (mode & 1) hipLaunchKernelGGL(chirp, dim3(1), dim3(SSS_T), 0, st, Np, bhat);
+    if (mode & 1) hipLaunchKernelGGL(chirp, dim3(1), dim3(SSS_T), 0, st, Np, bhat, cw);
     hipLaunchKernelGGL(kern, dim3(u1 - u0), dim3(SSS_T), 0, st, D, mode, u0, s_in, s_hat_out,
-                       kstar_out, budgets, offsets, idx_out, rows, (const float2*)bhat);
+                       kstar_out, budgets, offsets, idx_out, rows, (const float2*)bhat,
+                       (const float2*)cw);
     return hipGetLastError();
   }
   void (*kern)(KvcDesc, int, int, const float*, float*, int32_t*, const int32_t*, const int64_t*,
