@@ -33,6 +33,12 @@ VZ_EXPORTS = ("kvc_vz_plan", "kvc_vz_step", "kvc_vz_accumulate", "kvc_vz_evict",
 # include/kvc_c3.h
 C3_EXPORTS = ("kvc_c3_plan", "kvc_c3_build", "kvc_c3_step", "kvc_c3_score", "kvc_c3_select",
               "kvc_c3_update", "kvc_c3_gather")
+# include/kvc_wnw.h
+WNW_EXPORTS = ("kvc_wnw_plan", "kvc_wnw_init", "kvc_wnw_step", "kvc_wnw_chunk_scores",
+               "kvc_wnw_update", "kvc_wnw_recall", "kvc_wnw_fixed_select")
+KVC_WNW_FIXED = 0
+KVC_WNW_ANCHOR = 1
+KVC_WNW_TIDAL = 2
 
 
 KVC_POOL_SEQUENCE = 0
@@ -96,6 +102,30 @@ class kvc_c3_layout(ctypes.Structure):
                                           "n_nodes", "centroid", "count", "frontier", "ema")]
 
 
+class kvc_wnw_params(ctypes.Structure):
+    _fields_ = [("chunk_len", ctypes.c_int32), ("chunk_stride", ctypes.c_int32),
+                ("top_chunks", ctypes.c_int32), ("release_after", ctypes.c_int32)]
+
+
+class kvc_wnw_problem(ctypes.Structure):
+    _fields_ = [("n_seq", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("gqa_group", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int64),
+                ("len", ctypes.POINTER(ctypes.c_int64)),
+                ("role", ctypes.POINTER(ctypes.c_uint8)),
+                ("k_stride", ctypes.c_int64 * 2), ("host_stride", ctypes.c_int64 * 2),
+                ("slot_stride", ctypes.c_int64 * 2)]
+
+
+class kvc_wnw_layout(ctypes.Structure):
+    _fields_ = [("n_anchor", ctypes.c_int32), ("n_tidal", ctypes.c_int32),
+                ("block_cap", ctypes.c_int32), ("chunk_cap", ctypes.c_int32),
+                ("slot_cap", ctypes.c_int32),
+                ("state_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)] + \
+        [(f, ctypes.c_size_t) for f in ("idle", "slot_of_block", "block_of_slot", "selected",
+                                          "n_recalled", "recalled_block", "recalled_slot")]
+
+
 class KvcError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -156,6 +186,18 @@ def lib():
             L.kvc_c3_update.argtypes = [cp, cq, _vp, _vp, _vp, _vp, _vp]
             L.kvc_c3_gather.argtypes = [cp, cq, _vp, _vp, _vp, _vp, _vp, _vp]
             for name in C3_EXPORTS:
+                getattr(L, name).restype = ctypes.c_int
+            wp, wq = _P(kvc_wnw_problem), _P(kvc_wnw_params)
+            L.kvc_wnw_plan.argtypes = [wp, wq, _P(kvc_wnw_layout)]
+            L.kvc_wnw_init.argtypes = [wp, wq, _vp, _vp]
+            L.kvc_wnw_step.argtypes = [wp, wq, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       ctypes.c_size_t, _vp]
+            L.kvc_wnw_chunk_scores.argtypes = [wp, wq, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+            L.kvc_wnw_update.argtypes = [wp, wq, _vp, _vp, _vp, _vp]
+            L.kvc_wnw_recall.argtypes = [wp, wq, _vp, _vp, _vp, _vp, _vp, _vp]
+            L.kvc_wnw_fixed_select.argtypes = [prob, prm, ctypes.c_int32, _vp, _vp, _vp, _vp,
+                                               _vp]
+            for name in WNW_EXPORTS:
                 getattr(L, name).restype = ctypes.c_int
             L.kvc_status_str.argtypes = [ctypes.c_int]
             L.kvc_status_str.restype = ctypes.c_char_p

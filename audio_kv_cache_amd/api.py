@@ -461,3 +461,155 @@ def c3_allocate(spec: C3Spec, params: C3Params, device):
         idx=torch.empty((U, int(lay.kept_cap)), dtype=torch.int32, device=device),
         sigma=torch.empty((U, spec.capacity), dtype=torch.float32, device=device),
     )
+
+
+# ---------------------------------------------------------------------------
+# WnW chunk recall (include/kvc_wnw.h)
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class WnwParams:
+    chunk_len: int = 50       # 4 s at 12.5 audio tokens per second
+    chunk_stride: int = 25    # 2 s
+    top_chunks: int = 3
+    release_after: int = 3
+
+    def c(self) -> C.kvc_wnw_params:
+        return C.kvc_wnw_params(int(self.chunk_len), int(self.chunk_stride),
+                                int(self.top_chunks), int(self.release_after))
+
+    @property
+    def slot_cap(self) -> int:
+        return self.top_chunks * self.release_after * (self.chunk_len // self.chunk_stride)
+
+
+class WnwSpec:
+    """Host-side kvc_wnw_problem: per-sequence audio lengths, a role per KV
+    head (0 fixed, 1 anchor, 2 tidal), the anchors' device keys, the tidal
+    heads' page-locked host copies and device slot buffers (dense
+    [units][rows][head_dim] strides by default)."""
+
+    def __init__(self, *, n_layers, n_kv_heads, gqa, head_dim, lens, roles, capacity,
+                 slot_rows, k_stride=None, host_stride=None, slot_stride=None):
+        self.n_layers, self.n_kv_heads, self.gqa = int(n_layers), int(n_kv_heads), int(gqa)
+        self.head_dim, self.capacity = int(head_dim), int(capacity)
+        self._len = np.ascontiguousarray(np.asarray(lens, dtype=np.int64).reshape(-1))
+        self.n_seq = int(self._len.shape[0])
+        self._role = np.ascontiguousarray(np.asarray(roles, dtype=np.uint8).reshape(-1))
+        assert self._role.shape[0] == self.n_layers * self.n_kv_heads
+        dense = (self.capacity * self.head_dim, self.head_dim)
+        self.k_stride = tuple(int(x) for x in (k_stride or dense))
+        self.host_stride = tuple(int(x) for x in (host_stride or dense))
+        self.slot_rows = int(slot_rows)
+        self.slot_stride = tuple(int(x) for x in (slot_stride or
+                                                   (self.slot_rows * self.head_dim, self.head_dim)))
+
+    @property
+    def n_units(self) -> int:
+        return self.n_seq * self.n_layers * self.n_kv_heads
+
+    @property
+    def lens(self) -> np.ndarray:
+        return self._len
+
+    @property
+    def roles(self) -> np.ndarray:
+        return self._role
+
+    def c(self) -> C.kvc_wnw_problem:
+        p = C.kvc_wnw_problem()
+        p.n_seq, p.n_layers, p.n_kv_heads = self.n_seq, self.n_layers, self.n_kv_heads
+        p.gqa_group, p.head_dim, p.capacity = self.gqa, self.head_dim, self.capacity
+        p.len = self._len.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        p.role = self._role.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+        for a in range(2):
+            p.k_stride[a] = self.k_stride[a]
+            p.host_stride[a] = self.host_stride[a]
+            p.slot_stride[a] = self.slot_stride[a]
+        return p
+
+
+def kvc_wnw_plan(spec: WnwSpec, params: WnwParams) -> C.kvc_wnw_layout:
+    lay = C.kvc_wnw_layout()
+    C.check(C.lib().kvc_wnw_plan(ctypes.byref(spec.c()), ctypes.byref(params.c()),
+                                 ctypes.byref(lay)), "kvc_wnw_plan")
+    return lay
+
+
+def kvc_wnw_init(spec, params, state, stream=None):
+    C.check(C.lib().kvc_wnw_init(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(state),
+                                 _stream(stream)), "kvc_wnw_init")
+
+
+def _hptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def kvc_wnw_step(spec, params, q, k, state_in, state_out, host_k, host_v, slot_k, slot_v,
+                 sigma, workspace, stream=None):
+    C.check(C.lib().kvc_wnw_step(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(q),
+                                 _ptr(k), _ptr(state_in), _ptr(state_out), _hptr(host_k),
+                                 _hptr(host_v), _hptr(slot_k), _hptr(slot_v), _hptr(sigma),
+                                 _ptr(workspace), _nbytes(workspace), _stream(stream)),
+            "kvc_wnw_step")
+
+
+def kvc_wnw_chunk_scores(spec, params, q, k, sigma, workspace, stream=None):
+    C.check(C.lib().kvc_wnw_chunk_scores(ctypes.byref(spec.c()), ctypes.byref(params.c()),
+                                         _ptr(q), _ptr(k), _ptr(sigma), _ptr(workspace),
+                                         _nbytes(workspace), _stream(stream)),
+            "kvc_wnw_chunk_scores")
+
+
+def kvc_wnw_update(spec, params, sigma, state_in, state_out, stream=None):
+    C.check(C.lib().kvc_wnw_update(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(sigma),
+                                   _ptr(state_in), _ptr(state_out), _stream(stream)),
+            "kvc_wnw_update")
+
+
+def kvc_wnw_recall(spec, params, state, host_k, host_v, slot_k, slot_v, stream=None):
+    C.check(C.lib().kvc_wnw_recall(ctypes.byref(spec.c()), ctypes.byref(params.c()), _ptr(state),
+                                   _hptr(host_k), _hptr(host_v), _hptr(slot_k), _hptr(slot_v),
+                                   _stream(stream)), "kvc_wnw_recall")
+
+
+def kvc_wnw_fixed_select(spec: Spec, params: Params, seg_len, s_hat, budgets, seg_offsets,
+                         idx_out, stream=None):
+    C.check(C.lib().kvc_wnw_fixed_select(ctypes.byref(spec.c()), ctypes.byref(params.c()),
+                                         int(seg_len), _ptr(s_hat), _ptr(budgets),
+                                         _ptr(seg_offsets), _ptr(idx_out), _stream(stream)),
+            "kvc_wnw_fixed_select")
+
+
+class WnwViews:
+    """torch views of a WnW state buffer (uint8 device tensor) by the
+    layout's offsets."""
+
+    def __init__(self, spec: WnwSpec, params: WnwParams, lay, state):
+        N = spec.n_seq
+
+        def view(off, cols):
+            return state[off:off + 4 * N * cols].view(torch.int32).view(N, cols)
+        self.idle = view(lay.idle, int(lay.chunk_cap))
+        self.slot_of_block = view(lay.slot_of_block, int(lay.block_cap))
+        self.block_of_slot = view(lay.block_of_slot, int(lay.slot_cap))
+        self.selected = view(lay.selected, int(params.top_chunks))
+        self.n_recalled = view(lay.n_recalled, 1).view(N)
+        self.recalled_block = view(lay.recalled_block, int(lay.slot_cap))
+        self.recalled_slot = view(lay.recalled_slot, int(lay.slot_cap))
+
+
+def wnw_allocate(spec: WnwSpec, params: WnwParams, device):
+    """Two states, a workspace, chunk scores and slot buffers for a WnW problem."""
+    lay = kvc_wnw_plan(spec, params)
+
+    def buf(n):
+        return torch.empty((max(int(n), 256),), dtype=torch.uint8, device=device)
+    U, D = spec.n_units, spec.head_dim
+    return dict(
+        layout=lay,
+        state=[buf(lay.state_bytes), buf(lay.state_bytes)],
+        ws=buf(lay.workspace_bytes),
+        sigma=torch.zeros((spec.n_seq, int(lay.chunk_cap)), dtype=torch.float32, device=device),
+        slot_k=torch.zeros((U, spec.slot_rows, D), dtype=torch.bfloat16, device=device),
+        slot_v=torch.zeros((U, spec.slot_rows, D), dtype=torch.bfloat16, device=device),
+    )

@@ -8,6 +8,7 @@
 
 #include "../../include/kvc.h"
 #include "kvc_internal.h"
+#include "kvc_wnw.h"
 
 static thread_local int g_last_hip_error = 0;
 
@@ -344,6 +345,20 @@ extern "C" kvc_status kvc_select(const kvc_problem* prob, const kvc_params* para
     if (e != hipSuccess) return hip_status(e);
   }
   return KVC_OK;
+}
+
+extern "C" kvc_status kvc_wnw_fixed_select(const kvc_problem* prob, const kvc_params* params,
+                                           int32_t seg_len, const float* s_hat,
+                                           const int32_t* budgets, const int64_t* seg_offsets,
+                                           int32_t* idx_out, void* stream) {
+  KvcDesc D;
+  kvc_status st = make_desc(prob, params, &D);
+  if (st != KVC_OK) return st;
+  if (!s_hat || !budgets || !seg_offsets || !idx_out) return KVC_ERR_INVALID_ARG;
+  if (seg_len < 1 || seg_len > 64) return KVC_ERR_INVALID_ARG;
+  if ((uintptr_t)s_hat & 3u) return KVC_ERR_INVALID_ARG;
+  return hip_status(kvc_launch_wnw_fixed_select(D, seg_len, s_hat, budgets, seg_offsets, idx_out,
+                                                (hipStream_t)stream));
 }
 
 extern "C" kvc_status kvc_gather(const kvc_problem* prob, const kvc_params* params,

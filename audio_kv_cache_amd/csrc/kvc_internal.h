@@ -84,6 +84,11 @@ hipError_t kvc_launch_gather(const KvcDesc& D, int u0, int u1, const void* k, co
                              const int32_t* idx, const int64_t* offsets, void* k_out, void* v_out,
                              int64_t est_rows, hipStream_t st);
 
+// Segment-wise selection of fixed heads (wnw.hip): every unit, as kvc_select.
+hipError_t kvc_launch_wnw_fixed_select(const KvcDesc& D, int seg, const float* s_hat,
+                                       const int32_t* budgets, const int64_t* offsets,
+                                       int32_t* idx_out, hipStream_t st);
+
 // Record a HIP error for kvc_last_hip_error() (calling thread).
 void kvc_note_hip_error(int e);
 

@@ -1,0 +1,741 @@
+// wnw.hip -- decode-time chunk recall (WnW digest page, "WnW: Waxing-and-
+// Waning KV Cache for Long-Form Speech LLMs": anchor, tidal and fixed KV
+// heads; 4 s chunks with a 2 s stride, the top 3 chunks per step, release
+// after 3 unselected steps) and the segment-wise selection of fixed heads.
+//
+// One decode step, all sequences at once:
+//   wnw_logits_kernel      anchor logits q_g . k_j / sqrt(d) (log2 units) for
+//                          every anchor's G query heads, and per-wave
+//                          (max, sum exp) partials; one thread per key.
+//   wnw_lse_kernel         the partials folded into each head's LSE.
+//   wnw_block_mass_kernel  per block: the anchors' attention mass (mean over
+//                          heads of exp2(l - LSE)), anchors and positions in
+//                          order; one thread per block.
+//   wnw_sigma_kernel       chunk scores: the sums of m consecutive blocks.
+//   wnw_update_kernel      one 1024-thread workgroup per sequence: top-K by
+//                          packed (score, index) maxima, idle counts,
+//                          residency, slot release and assignment with
+//                          block scans, the recall list.
+//   wnw_recall_kernel      one workgroup per (tidal head, sequence): 16-byte
+//                          copies of the recalled blocks' K and V rows from
+//                          page-locked host memory (read over PCIe by the
+//                          kernel itself, so no host round trip is needed to
+//                          learn which blocks to fetch) into the slots.
+// Decisions (top-K ties, slot order) are made in integers on one workgroup,
+// so they are reproducible; the scores are fp32 sums in a fixed order.
+#include <algorithm>
+#include <cstring>
+
+#include "kvc_internal.h"
+#include "kvc_wnw.h"
+
+#define WNW_MAX_SEQ 64
+#define WNW_MAX_ANCHOR 64
+#define WNW_MAX_UNITS 4096
+#define WNW_MAX_CAP 131072
+#define WNW_MAX_G 32
+#define WNW_MAX_M 8
+#define WNW_MAX_K 8
+#define WNW_MAX_H 8
+#define WNW_MAX_CHUNKS 65536
+#define WNW_TILE 256
+#define WNW_UT 1024
+#define WNW_MAX_SLOTS (WNW_MAX_K * WNW_MAX_H * WNW_MAX_M)
+
+static constexpr float kWnwLog2e = 1.4426950408889634f;
+
+struct WnwDesc {
+  int32_t n_seq, upseq, gqa, d;
+  int32_t S, m, K, H, slot_cap, block_cap, chunk_cap;
+  int32_t n_anchor, n_tidal, max_len, max_parts;
+  int32_t len[WNW_MAX_SEQ];
+  int16_t anchor_unit[WNW_MAX_ANCHOR];     // unit within a sequence: l * n_heads + h
+  uint32_t tidal_mask[WNW_MAX_UNITS / 32];
+  int64_t ks[2], hs[2], ss[2];
+};
+
+struct WnwState {
+  int32_t *idle, *slot_of_block, *block_of_slot, *selected, *n_recalled, *recalled_block,
+      *recalled_slot;
+};
+
+struct WnwWork {
+  float* logits;   // [n_seq * n_anchor][G][max_len]
+  float2* parts;   // [n_seq * n_anchor][G][max_parts]
+  float* lse2;     // [n_seq * n_anchor][G]
+  float* beta;     // [n_seq][block_cap]
+  float* sigma;    // [n_seq][chunk_cap]
+};
+
+__device__ __forceinline__ float wnw_bf16(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ void wnw_merge(float& m, float& z, float m2, float z2) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) return;
+  const float a = (m == -INFINITY) ? 0.f : z * __builtin_amdgcn_exp2f(m - mm);
+  const float b = (m2 == -INFINITY) ? 0.f : z2 * __builtin_amdgcn_exp2f(m2 - mm);
+  m = mm;
+  z = a + b;
+}
+
+// ---------------------------------------------------------------------------
+// Steps 1-2: anchor attention, block masses, chunk scores
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(WNW_TILE) void wnw_logits_kernel(WnwDesc W, const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k,
+                                                              WnwWork X) {
+  __shared__ __attribute__((aligned(16))) float sq[WNW_MAX_G][D];
+  const int sa = blockIdx.y, seq = sa / W.n_anchor, a = sa - seq * W.n_anchor;
+  const int n = W.len[seq], tile = blockIdx.x;
+  if (tile * WNW_TILE >= n) return;
+  const int G = W.gqa;
+  const uint16_t* qs = q + (size_t)sa * G * D;
+  for (int i = threadIdx.x; i < G * D; i += WNW_TILE) sq[i / D][i % D] = wnw_bf16(qs[i]);
+  __syncthreads();
+  const int j = tile * WNW_TILE + (int)threadIdx.x;
+  const bool valid = j < n;
+  const int64_t unit = (int64_t)seq * W.upseq + W.anchor_unit[a];
+  uint4 kr[D / 8];
+  if (valid) {
+    const uint4* row = reinterpret_cast<const uint4*>(k + unit * W.ks[0] + (int64_t)j * W.ks[1]);
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) kr[i] = row[i];
+  }
+  const float c = kWnwLog2e / sqrtf((float)D);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int part = tile * (WNW_TILE / 64) + wave;
+  for (int g = 0; g < G; ++g) {
+    float dot = 0.f;
+    if (valid) {
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        const float4 q0 = *reinterpret_cast<const float4*>(&sq[g][8 * i]);
+        const float4 q1 = *reinterpret_cast<const float4*>(&sq[g][8 * i + 4]);
+        const uint32_t w0 = kr[i].x, w1 = kr[i].y, w2 = kr[i].z, w3 = kr[i].w;
+        dot = fmaf(wnw_bf16(w0 & 0xffffu), q0.x, dot);
+        dot = fmaf(wnw_bf16(w0 >> 16), q0.y, dot);
+        dot = fmaf(wnw_bf16(w1 & 0xffffu), q0.z, dot);
+        dot = fmaf(wnw_bf16(w1 >> 16), q0.w, dot);
+        dot = fmaf(wnw_bf16(w2 & 0xffffu), q1.x, dot);
+        dot = fmaf(wnw_bf16(w2 >> 16), q1.y, dot);
+        dot = fmaf(wnw_bf16(w3 & 0xffffu), q1.z, dot);
+        dot = fmaf(wnw_bf16(w3 >> 16), q1.w, dot);
+      }
+    }
+    const float l2 = dot * c;
+    const size_t row = (size_t)sa * G + g;
+    if (valid) X.logits[row * W.max_len + j] = l2;
+    // this wave's (max, sum exp2) over its valid keys
+    float mx = valid ? l2 : -INFINITY;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float z = valid ? __builtin_amdgcn_exp2f(l2 - mx) : 0.f;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+    if (lane == 0) X.parts[row * W.max_parts + part] = make_float2(mx, z);
+  }
+}
+
+__global__ __launch_bounds__(256) void wnw_lse_kernel(WnwDesc W, WnwWork X) {
+  __shared__ float2 sred[4];
+  const int sa = blockIdx.x, seq = sa / W.n_anchor;
+  const int nparts = (W.len[seq] + 63) / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int g = 0; g < W.gqa; ++g) {
+    const float2* p = X.parts + ((size_t)sa * W.gqa + g) * W.max_parts;
+    float m = -INFINITY, z = 0.f;
+    for (int i = threadIdx.x; i < nparts; i += 256) wnw_merge(m, z, p[i].x, p[i].y);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float m2 = __shfl_xor(m, o), z2 = __shfl_xor(z, o);
+      wnw_merge(m, z, m2, z2);
+    }
+    if (lane == 0) sred[wave] = make_float2(m, z);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float mm = sred[0].x, zz = sred[0].y;
+      for (int w = 1; w < 4; ++w) wnw_merge(mm, zz, sred[w].x, sred[w].y);
+      X.lse2[(size_t)sa * W.gqa + g] = mm + __builtin_amdgcn_logf(zz);
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void wnw_block_mass_kernel(WnwDesc W, WnwWork X) {
+  const int seq = blockIdx.y, b = blockIdx.x * 256 + (int)threadIdx.x;
+  const int n = W.len[seq], B = (n + W.S - 1) / W.S;
+  if (b >= W.block_cap) return;
+  float beta = 0.f;
+  if (b < B) {
+    const int lo = b * W.S, hi = min(n, lo + W.S);
+    const float invG = 1.0f / (float)W.gqa;
+    for (int a = 0; a < W.n_anchor; ++a) {
+      const int sa = seq * W.n_anchor + a;
+      float pa = 0.f;
+      for (int j = lo; j < hi; ++j) {
+        float pj = 0.f;
+        for (int g = 0; g < W.gqa; ++g) {
+          const size_t row = (size_t)sa * W.gqa + g;
+          pj += __builtin_amdgcn_exp2f(X.logits[row * W.max_len + j] - X.lse2[row]);
+        }
+        pa += pj;
+      }
+      beta += pa * invG;
+    }
+  }
+  X.beta[(size_t)seq * W.block_cap + b] = beta;
+}
+
+__global__ __launch_bounds__(256) void wnw_sigma_kernel(WnwDesc W, const float* __restrict__ beta,
+                                                        float* __restrict__ sigma) {
+  const int seq = blockIdx.y, c = blockIdx.x * 256 + (int)threadIdx.x;
+  if (c >= W.chunk_cap) return;
+  const int n = W.len[seq], B = (n + W.S - 1) / W.S, C = max(1, B - W.m + 1);
+  float s = 0.f;
+  if (c < C) {
+    const float* bs = beta + (size_t)seq * W.block_cap;
+    for (int b = c; b < min(c + W.m, B); ++b) s += bs[b];
+  }
+  sigma[(size_t)seq * W.chunk_cap + c] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Steps 3-4: selection, residency, slots (one workgroup per sequence)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wnw_order_key(float f) {
+  if (f == 0.0f) f = 0.0f;
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Exclusive scan over the workgroup's WNW_UT threads; *total gets the sum.
+__device__ __forceinline__ int wnw_scan(int v, int* sw, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) sw[w] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < WNW_UT / 64; ++i) {
+    const int x = sw[i];
+    if (i < w) before += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(WNW_UT) void wnw_update_kernel(WnwDesc W, const float* __restrict__ sigma,
+                                                            WnwState in, WnwState out) {
+  __shared__ unsigned long long sbest[WNW_UT / 64];
+  __shared__ int ssel[WNW_MAX_K];
+  __shared__ int sfree[WNW_MAX_SLOTS];
+  __shared__ int sw[WNW_UT / 64];
+  const int seq = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n = W.len[seq], B = (n + W.S - 1) / W.S, C = max(1, B - W.m + 1);
+  const float* sg = sigma + (size_t)seq * W.chunk_cap;
+  const size_t oc = (size_t)seq * W.chunk_cap, ob = (size_t)seq * W.block_cap,
+               os = (size_t)seq * W.slot_cap;
+  // Top-K: the largest (score, -index) key, K times.
+  const int nsel = min(W.K, C);
+  for (int r = 0; r < nsel; ++r) {
+    unsigned long long best = 0;
+    for (int c = t; c < C; c += WNW_UT) {
+      bool taken = false;
+      for (int i = 0; i < r; ++i) taken |= (ssel[i] == c);
+      if (taken) continue;
+      const unsigned long long key =
+          ((unsigned long long)wnw_order_key(sg[c]) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)c);
+      best = key > best ? key : best;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long y = __shfl_xor(best, o);
+      best = y > best ? y : best;
+    }
+    if (lane == 0) sbest[wave] = best;
+    __syncthreads();
+    if (t == 0) {
+      unsigned long long bb = 0;
+      for (int i = 0; i < WNW_UT / 64; ++i) bb = sbest[i] > bb ? sbest[i] : bb;
+      ssel[r] = (int)(0xffffffffu - (uint32_t)(bb & 0xffffffffull));
+    }
+    __syncthreads();
+  }
+  if (t < W.K) out.selected[(size_t)seq * W.K + t] = t < nsel ? ssel[t] : -1;
+  // Idle counts.
+  for (int c = t; c < W.chunk_cap; c += WNW_UT) {
+    int z = -1;
+    if (c < C) {
+      bool s = false;
+      for (int i = 0; i < nsel; ++i) s |= (ssel[i] == c);
+      const int z0 = in.idle[oc + c];
+      z = s ? 0 : (z0 >= 0 ? (z0 + 1 >= W.H ? -1 : z0 + 1) : -1);
+    }
+    out.idle[oc + c] = z;
+  }
+  __syncthreads();
+  auto resident = [&](int b) {
+    bool r = false;
+    for (int c = max(0, b - W.m + 1); c <= min(b, C - 1); ++c) r |= out.idle[oc + c] >= 0;
+    return r;
+  };
+  // Kept slots stay, the others are free.
+  bool fr = false;
+  if (t < W.slot_cap) {
+    const int blk = in.block_of_slot[os + t];
+    const bool keep = blk >= 0 && blk < B && resident(blk);
+    out.block_of_slot[os + t] = keep ? blk : -1;
+    fr = !keep;
+  }
+  int nfree;
+  const int fr_rank = wnw_scan(fr ? 1 : 0, sw, &nfree);
+  if (fr) sfree[fr_rank] = t;
+  __syncthreads();
+  // Blocks: kept slot, none, or the next free slot (ascending blocks).
+  int base = 0;
+  for (int b0 = 0; b0 < W.block_cap; b0 += WNW_UT) {
+    const int b = b0 + t;
+    bool isnew = false;
+    int slot = -1;
+    if (b < B && resident(b)) {
+      slot = in.slot_of_block[ob + b];
+      isnew = slot < 0;
+    }
+    int tot;
+    const int r = wnw_scan(isnew ? 1 : 0, sw, &tot) + base;
+    if (isnew) {
+      slot = r < nfree ? sfree[r] : -1;
+      if (slot >= 0) {
+        out.block_of_slot[os + slot] = b;
+        out.recalled_block[os + r] = b;
+        out.recalled_slot[os + r] = slot;
+      }
+    }
+    if (b < W.block_cap) out.slot_of_block[ob + b] = slot;
+    base += tot;
+  }
+  const int nrec = min(base, nfree);
+  for (int r = nrec + t; r < W.slot_cap; r += WNW_UT) {
+    out.recalled_block[os + r] = -1;
+    out.recalled_slot[os + r] = -1;
+  }
+  if (t == 0) out.n_recalled[seq] = nrec;
+}
+
+// ---------------------------------------------------------------------------
+// Step 5: recall copies, host -> slots
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void wnw_recall_kernel(WnwDesc W, WnwState st,
+                                                         const uint16_t* __restrict__ hk,
+                                                         const uint16_t* __restrict__ hv,
+                                                         uint16_t* __restrict__ sk,
+                                                         uint16_t* __restrict__ sv) {
+  __shared__ int sunit;
+  const int tid = blockIdx.x, seq = blockIdx.y;
+  if (threadIdx.x == 0) {
+    // the tid-th tidal unit of the role table
+    int seen = 0, u = -1;
+    for (int w = 0; w < (W.upseq + 31) / 32 && u < 0; ++w) {
+      const uint32_t m = W.tidal_mask[w];
+      const int pc = __popc(m);
+      if (seen + pc > tid) {
+        uint32_t mm = m;
+        for (int i = 0; i < tid - seen; ++i) mm &= mm - 1;
+        u = w * 32 + __ffs(mm) - 1;
+      }
+      seen += pc;
+    }
+    sunit = u;
+  }
+  __syncthreads();
+  const int uw = sunit;
+  if (uw < 0) return;
+  const int64_t unit = (int64_t)seq * W.upseq + uw;
+  const int n = W.len[seq], B = (n + W.S - 1) / W.S;
+  // (a state from elsewhere is range-checked entry by entry)
+  const int nrec = min(max(st.n_recalled[seq], 0), W.slot_cap);
+  constexpr int PR = D / 8;  // 16-byte pieces per row
+  const size_t os = (size_t)seq * W.slot_cap;
+  for (int r = 0; r < nrec; ++r) {
+    const int b = st.recalled_block[os + r], s = st.recalled_slot[os + r];
+    if (b < 0 || b >= B || s < 0 || s >= W.slot_cap) continue;
+    const int rows = min(W.S, n - b * W.S);
+    const uint16_t* hkb = hk + unit * W.hs[0] + (int64_t)b * W.S * W.hs[1];
+    const uint16_t* hvb = hv + unit * W.hs[0] + (int64_t)b * W.S * W.hs[1];
+    uint16_t* skb = sk + unit * W.ss[0] + (int64_t)s * W.S * W.ss[1];
+    uint16_t* svb = sv + unit * W.ss[0] + (int64_t)s * W.S * W.ss[1];
+    for (int i = threadIdx.x; i < rows * PR; i += 256) {
+      const int row = i / PR, p = i - row * PR;
+      const uint4 kx = reinterpret_cast<const uint4*>(hkb + (int64_t)row * W.hs[1])[p];
+      const uint4 vx = reinterpret_cast<const uint4*>(hvb + (int64_t)row * W.hs[1])[p];
+      reinterpret_cast<uint4*>(skb + (int64_t)row * W.ss[1])[p] = kx;
+      reinterpret_cast<uint4*>(svb + (int64_t)row * W.ss[1])[p] = vx;
+    }
+  }
+}
+
+__global__ void wnw_fill_kernel(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Fixed heads: segment-wise selection at prefill (one workgroup per unit,
+// one wave per segment of at most 64 positions)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void wnw_fixed_select_kernel(KvcDesc D, int seg,
+                                                               const float* __restrict__ s_hat,
+                                                               const int32_t* __restrict__ budgets,
+                                                               const int64_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ idx_out) {
+  const int u = blockIdx.x;
+  const int seq = u / D.upseq, within = u - seq * D.upseq;
+  const int L = D.L[seq], w = D.window, ncand = L - w;
+  // (budgets hold w <= b <= L, as for kvc_select; clamped all the same)
+  const int k = min(max(budgets[u] - w, 0), max(ncand, 0));
+  int32_t* out = idx_out + offsets[u];
+  for (int i = threadIdx.x; i < w; i += 256) out[max(k, 0) + i] = ncand + i;
+  if (k <= 0 || ncand <= 0) return;
+  const float* row = s_hat + D.srow_base[seq] + (int64_t)within * L;
+  // Quotas: every full segment has the same floor and remainder, the short
+  // last one (if any) its own; the R leftovers go by remainder, then index.
+  const int64_t nfull = ncand / seg, last = ncand - nfull * seg;
+  const int64_t qf = (int64_t)k * seg / ncand, rf = (int64_t)k * seg % ncand;
+  const int64_t ql = last ? (int64_t)k * last / ncand : 0, rl = last ? (int64_t)k * last % ncand : 0;
+  const int64_t R = k - nfull * qf - ql;
+  const bool last_first = last && rl > rf;
+  const int64_t rfull =  // full segments with +1
+      std::max<int64_t>(0, std::min<int64_t>(nfull, last_first ? R - 1 : R));
+  const int64_t qlast = ql + ((last_first && R >= 1) || (!last_first && R > nfull) ? 1 : 0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t J = nfull + (last ? 1 : 0);
+  for (int64_t j = wave; j < J; j += 4) {
+    const int lo = (int)(j * seg), len = (int)std::min<int64_t>(seg, ncand - j * seg);
+    const int64_t quota = (j < nfull) ? qf + (j < rfull ? 1 : 0) : qlast;
+    const int64_t before = (j < nfull) ? j * qf + std::min<int64_t>(j, rfull) : nfull * qf + rfull;
+    const bool valid = lane < len;
+    const uint32_t key = valid ? wnw_order_key(row[lo + lane]) : 0u;
+    int rank = 0;
+    for (int o = 0; o < len; ++o) {
+      const uint32_t ko = __shfl(key, o);
+      rank += (ko > key) || (ko == key && o < lane);
+    }
+    const bool take = valid && rank < quota;
+    const unsigned long long mask = __ballot(take);
+    const int pos = __popcll(mask & ((1ull << lane) - 1ull));
+    if (take) out[before + pos] = lo + lane;
+  }
+}
+
+hipError_t kvc_launch_wnw_fixed_select(const KvcDesc& D, int seg, const float* s_hat,
+                                       const int32_t* budgets, const int64_t* offsets,
+                                       int32_t* idx_out, hipStream_t st) {
+  hipLaunchKernelGGL(wnw_fixed_select_kernel, dim3(D.n_units), dim3(256), 0, st, D, seg, s_hat,
+                     budgets, offsets, idx_out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+static size_t wnw_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+static kvc_status wnw_hip(hipError_t e) {
+  if (e == hipSuccess) return KVC_OK;
+  kvc_note_hip_error((int)e);
+  return KVC_ERR_HIP;
+}
+
+static kvc_status wnw_desc(const kvc_wnw_problem* p, const kvc_wnw_params* prm, WnwDesc* W) {
+  if (!p || !prm || !W || !p->len || !p->role) return KVC_ERR_INVALID_ARG;
+  if (p->n_seq < 1 || p->n_layers < 1 || p->n_kv_heads < 1 || p->gqa_group < 1 ||
+      p->head_dim < 1 || p->capacity < 1)
+    return KVC_ERR_INVALID_ARG;
+  const int S = prm->chunk_stride, Wc = prm->chunk_len;
+  if (S < 1 || Wc < S || Wc % S != 0 || prm->top_chunks < 1 || prm->release_after < 1)
+    return KVC_ERR_INVALID_ARG;
+  if (Wc / S > WNW_MAX_M || prm->top_chunks > WNW_MAX_K || prm->release_after > WNW_MAX_H)
+    return KVC_ERR_UNSUPPORTED;
+  if (p->n_seq > WNW_MAX_SEQ || p->capacity > WNW_MAX_CAP) return KVC_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return KVC_ERR_UNSUPPORTED;
+  if (p->gqa_group > WNW_MAX_G) return KVC_ERR_UNSUPPORTED;
+  const int64_t upseq = (int64_t)p->n_layers * p->n_kv_heads;
+  if (upseq > WNW_MAX_UNITS) return KVC_ERR_UNSUPPORTED;
+  memset(W, 0, sizeof(*W));
+  int na = 0, nt = 0;
+  for (int64_t u = 0; u < upseq; ++u) {
+    const uint8_t r = p->role[u];
+    if (r > KVC_WNW_TIDAL) return KVC_ERR_INVALID_ARG;
+    if (r == KVC_WNW_ANCHOR) {
+      if (na == WNW_MAX_ANCHOR) return KVC_ERR_UNSUPPORTED;
+      W->anchor_unit[na++] = (int16_t)u;
+    } else if (r == KVC_WNW_TIDAL) {
+      W->tidal_mask[u / 32] |= 1u << (u % 32);
+      ++nt;
+    }
+  }
+  if (na < 1) return KVC_ERR_INVALID_ARG;
+  for (int a = 0; a < 2; ++a)
+    if (p->k_stride[a] < 0 || p->host_stride[a] < 0 || p->slot_stride[a] < 0 ||
+        p->k_stride[a] % 8 || p->host_stride[a] % 8 || p->slot_stride[a] % 8)
+      return KVC_ERR_INVALID_ARG;
+  const int m = Wc / S;
+  const int64_t slot_cap = (int64_t)prm->top_chunks * prm->release_after * m;
+  if (p->k_stride[1] < p->head_dim || p->k_stride[0] < p->k_stride[1] * p->capacity)
+    return KVC_ERR_INVALID_ARG;
+  if (nt > 0) {
+    if (p->host_stride[1] < p->head_dim || p->host_stride[0] < p->host_stride[1] * p->capacity)
+      return KVC_ERR_INVALID_ARG;
+    if (p->slot_stride[1] < p->head_dim || p->slot_stride[0] < p->slot_stride[1] * slot_cap * S)
+      return KVC_ERR_INVALID_ARG;
+  }
+  int max_len = 1, bcap = 1, ccap = 1;
+  for (int i = 0; i < p->n_seq; ++i) {
+    const int64_t n = p->len[i];
+    if (n < 1 || n > p->capacity) return KVC_ERR_INVALID_ARG;
+    const int64_t B = (n + S - 1) / S, C = std::max<int64_t>(1, B - m + 1);
+    if (C > WNW_MAX_CHUNKS) return KVC_ERR_UNSUPPORTED;
+    W->len[i] = (int32_t)n;
+    max_len = std::max<int>(max_len, (int)n);
+    bcap = std::max<int>(bcap, (int)B);
+    ccap = std::max<int>(ccap, (int)C);
+  }
+  W->n_seq = p->n_seq;
+  W->upseq = (int32_t)upseq;
+  W->gqa = p->gqa_group;
+  W->d = p->head_dim;
+  W->S = S;
+  W->m = m;
+  W->K = prm->top_chunks;
+  W->H = prm->release_after;
+  W->slot_cap = (int32_t)slot_cap;
+  W->block_cap = bcap;
+  W->chunk_cap = ccap;
+  W->n_anchor = na;
+  W->n_tidal = nt;
+  W->max_len = max_len;
+  W->max_parts = ((max_len + WNW_TILE - 1) / WNW_TILE) * (WNW_TILE / 64);
+  for (int a = 0; a < 2; ++a) {
+    W->ks[a] = p->k_stride[a];
+    W->hs[a] = p->host_stride[a];
+    W->ss[a] = p->slot_stride[a];
+  }
+  return KVC_OK;
+}
+
+static void wnw_layout(const WnwDesc& W, kvc_wnw_layout* L) {
+  memset(L, 0, sizeof(*L));
+  const size_t N = (size_t)W.n_seq;
+  L->n_anchor = W.n_anchor;
+  L->n_tidal = W.n_tidal;
+  L->block_cap = W.block_cap;
+  L->chunk_cap = W.chunk_cap;
+  L->slot_cap = W.slot_cap;
+  size_t o = 0;
+  L->idle = o;           o += wnw_up(4 * N * W.chunk_cap);
+  L->slot_of_block = o;  o += wnw_up(4 * N * W.block_cap);
+  L->block_of_slot = o;  o += wnw_up(4 * N * W.slot_cap);
+  L->selected = o;       o += wnw_up(4 * N * W.K);
+  L->n_recalled = o;     o += wnw_up(4 * N);
+  L->recalled_block = o; o += wnw_up(4 * N * W.slot_cap);
+  L->recalled_slot = o;  o += wnw_up(4 * N * W.slot_cap);
+  L->state_bytes = o;
+  const size_t SA = N * W.n_anchor * W.gqa;
+  L->workspace_bytes = wnw_up(4 * SA * W.max_len) + wnw_up(8 * SA * W.max_parts) +
+                       wnw_up(4 * SA) + wnw_up(4 * N * W.block_cap) + wnw_up(4 * N * W.chunk_cap);
+}
+
+static WnwState wnw_state(const kvc_wnw_layout& L, const void* p) {
+  char* b = (char*)p;
+  WnwState s;
+  s.idle = (int32_t*)(b + L.idle);
+  s.slot_of_block = (int32_t*)(b + L.slot_of_block);
+  s.block_of_slot = (int32_t*)(b + L.block_of_slot);
+  s.selected = (int32_t*)(b + L.selected);
+  s.n_recalled = (int32_t*)(b + L.n_recalled);
+  s.recalled_block = (int32_t*)(b + L.recalled_block);
+  s.recalled_slot = (int32_t*)(b + L.recalled_slot);
+  return s;
+}
+
+static WnwWork wnw_work(const WnwDesc& W, void* p) {
+  char* b = (char*)p;
+  const size_t N = (size_t)W.n_seq, SA = N * W.n_anchor * W.gqa;
+  WnwWork X;
+  X.logits = (float*)b;  b += wnw_up(4 * SA * W.max_len);
+  X.parts = (float2*)b;  b += wnw_up(8 * SA * W.max_parts);
+  X.lse2 = (float*)b;    b += wnw_up(4 * SA);
+  X.beta = (float*)b;    b += wnw_up(4 * N * W.block_cap);
+  X.sigma = (float*)b;
+  return X;
+}
+
+static bool wnw_a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool wnw_a256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
+
+// Page-locked host memory the device can read; its device-side address.
+static bool wnw_host_ptr(const void* p, const void** dev) {
+  if (!p || !wnw_a16(p)) return false;
+  hipPointerAttribute_t a;
+  memset(&a, 0, sizeof(a));
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (a.type != hipMemoryTypeHost || !a.devicePointer) return false;
+  *dev = a.devicePointer;
+  return wnw_a16(*dev);
+}
+
+extern "C" kvc_status kvc_wnw_plan(const kvc_wnw_problem* prob, const kvc_wnw_params* params,
+                                   kvc_wnw_layout* layout) {
+  WnwDesc W;
+  const kvc_status st = wnw_desc(prob, params, &W);
+  if (st != KVC_OK) return st;
+  if (!layout) return KVC_ERR_INVALID_ARG;
+  wnw_layout(W, layout);
+  return KVC_OK;
+}
+
+extern "C" kvc_status kvc_wnw_init(const kvc_wnw_problem* prob, const kvc_wnw_params* params,
+                                   void* state, void* stream) {
+  WnwDesc W;
+  kvc_status rs = wnw_desc(prob, params, &W);
+  if (rs != KVC_OK) return rs;
+  if (!state || !wnw_a256(state)) return KVC_ERR_INVALID_ARG;
+  kvc_wnw_layout L;
+  wnw_layout(W, &L);
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t words = (int64_t)(L.state_bytes / 4);
+  hipLaunchKernelGGL(wnw_fill_kernel, dim3(256), dim3(256), 0, st, (int32_t*)state, words, -1);
+  hipLaunchKernelGGL(wnw_fill_kernel, dim3(1), dim3(64), 0, st,
+                     (int32_t*)((char*)state + L.n_recalled), (int64_t)W.n_seq, 0);
+  return wnw_hip(hipGetLastError());
+}
+
+static hipError_t wnw_launch_scores(const WnwDesc& W, const void* q, const void* k, float* sigma,
+                                    const WnwWork& X, hipStream_t st) {
+  const dim3 g1((unsigned)((W.max_len + WNW_TILE - 1) / WNW_TILE), (unsigned)(W.n_seq * W.n_anchor));
+  if (W.d == 128)
+    hipLaunchKernelGGL(wnw_logits_kernel<128>, g1, dim3(WNW_TILE), 0, st, W, (const uint16_t*)q,
+                       (const uint16_t*)k, X);
+  else
+    hipLaunchKernelGGL(wnw_logits_kernel<64>, g1, dim3(WNW_TILE), 0, st, W, (const uint16_t*)q,
+                       (const uint16_t*)k, X);
+  hipLaunchKernelGGL(wnw_lse_kernel, dim3((unsigned)(W.n_seq * W.n_anchor)), dim3(256), 0, st, W, X);
+  hipLaunchKernelGGL(wnw_block_mass_kernel, dim3((unsigned)((W.block_cap + 255) / 256), (unsigned)W.n_seq),
+                     dim3(256), 0, st, W, X);
+  hipLaunchKernelGGL(wnw_sigma_kernel, dim3((unsigned)((W.chunk_cap + 255) / 256), (unsigned)W.n_seq),
+                     dim3(256), 0, st, W, (const float*)X.beta, sigma);
+  return hipGetLastError();
+}
+
+static hipError_t wnw_launch_recall(const WnwDesc& W, const WnwState& s, const void* hk,
+                                    const void* hv, void* sk, void* sv, hipStream_t st) {
+  if (W.n_tidal == 0) return hipSuccess;
+  const dim3 g((unsigned)W.n_tidal, (unsigned)W.n_seq);
+  if (W.d == 128)
+    hipLaunchKernelGGL(wnw_recall_kernel<128>, g, dim3(256), 0, st, W, s, (const uint16_t*)hk,
+                       (const uint16_t*)hv, (uint16_t*)sk, (uint16_t*)sv);
+  else
+    hipLaunchKernelGGL(wnw_recall_kernel<64>, g, dim3(256), 0, st, W, s, (const uint16_t*)hk,
+                       (const uint16_t*)hv, (uint16_t*)sk, (uint16_t*)sv);
+  return hipGetLastError();
+}
+
+// Checks the host copies and slots of a call that recalls; their device
+// addresses in *dk, *dv.
+static kvc_status wnw_check_recall(const WnwDesc& W, const void* hk, const void* hv,
+                                   const void* sk, const void* sv, const void** dk,
+                                   const void** dv) {
+  *dk = *dv = nullptr;
+  if (W.n_tidal == 0) return KVC_OK;
+  if (!sk || !sv || !wnw_a16(sk) || !wnw_a16(sv)) return KVC_ERR_INVALID_ARG;
+  if (!wnw_host_ptr(hk, dk) || !wnw_host_ptr(hv, dv)) return KVC_ERR_INVALID_ARG;
+  return KVC_OK;
+}
+
+extern "C" kvc_status kvc_wnw_chunk_scores(const kvc_wnw_problem* prob, const kvc_wnw_params* params,
+                                           const void* q, const void* k, float* sigma,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  WnwDesc W;
+  kvc_status rs = wnw_desc(prob, params, &W);
+  if (rs != KVC_OK) return rs;
+  if (!q || !k || !sigma || !workspace || !wnw_a16(q) || !wnw_a16(k) || !wnw_a256(workspace))
+    return KVC_ERR_INVALID_ARG;
+  kvc_wnw_layout L;
+  wnw_layout(W, &L);
+  if (workspace_bytes < L.workspace_bytes) return KVC_ERR_WORKSPACE;
+  return wnw_hip(wnw_launch_scores(W, q, k, sigma, wnw_work(W, workspace), (hipStream_t)stream));
+}
+
+extern "C" kvc_status kvc_wnw_update(const kvc_wnw_problem* prob, const kvc_wnw_params* params,
+                                     const float* sigma, const void* state_in, void* state_out,
+                                     void* stream) {
+  WnwDesc W;
+  kvc_status rs = wnw_desc(prob, params, &W);
+  if (rs != KVC_OK) return rs;
+  if (!sigma || !state_in || !state_out || state_in == state_out || !wnw_a256(state_in) ||
+      !wnw_a256(state_out))
+    return KVC_ERR_INVALID_ARG;
+  kvc_wnw_layout L;
+  wnw_layout(W, &L);
+  hipLaunchKernelGGL(wnw_update_kernel, dim3((unsigned)W.n_seq), dim3(WNW_UT), 0,
+                     (hipStream_t)stream, W, sigma, wnw_state(L, state_in), wnw_state(L, state_out));
+  return wnw_hip(hipGetLastError());
+}
+
+extern "C" kvc_status kvc_wnw_recall(const kvc_wnw_problem* prob, const kvc_wnw_params* params,
+                                     const void* state, const void* host_k, const void* host_v,
+                                     void* slot_k, void* slot_v, void* stream) {
+  WnwDesc W;
+  kvc_status rs = wnw_desc(prob, params, &W);
+  if (rs != KVC_OK) return rs;
+  if (!state || !wnw_a256(state)) return KVC_ERR_INVALID_ARG;
+  const void *dk, *dv;
+  if ((rs = wnw_check_recall(W, host_k, host_v, slot_k, slot_v, &dk, &dv)) != KVC_OK) return rs;
+  kvc_wnw_layout L;
+  wnw_layout(W, &L);
+  return wnw_hip(wnw_launch_recall(W, wnw_state(L, state), dk, dv, slot_k, slot_v,
+                                   (hipStream_t)stream));
+}
+
+extern "C" kvc_status kvc_wnw_step(const kvc_wnw_problem* prob, const kvc_wnw_params* params,
+                                   const void* q, const void* k, const void* state_in,
+                                   void* state_out, const void* host_k, const void* host_v,
+                                   void* slot_k, void* slot_v, float* sigma, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  WnwDesc W;
+  kvc_status rs = wnw_desc(prob, params, &W);
+  if (rs != KVC_OK) return rs;
+  if (!q || !k || !state_in || !state_out || state_in == state_out || !workspace)
+    return KVC_ERR_INVALID_ARG;
+  if (!wnw_a16(q) || !wnw_a16(k) || !wnw_a256(state_in) || !wnw_a256(state_out) ||
+      !wnw_a256(workspace))
+    return KVC_ERR_INVALID_ARG;
+  const void *dk, *dv;
+  if ((rs = wnw_check_recall(W, host_k, host_v, slot_k, slot_v, &dk, &dv)) != KVC_OK) return rs;
+  kvc_wnw_layout L;
+  wnw_layout(W, &L);
+  if (workspace_bytes < L.workspace_bytes) return KVC_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const WnwWork X = wnw_work(W, workspace);
+  float* sg = sigma ? sigma : X.sigma;
+  hipError_t e = wnw_launch_scores(W, q, k, sg, X, st);
+  if (e != hipSuccess) return wnw_hip(e);
+  const WnwState so = wnw_state(L, state_out);
+  hipLaunchKernelGGL(wnw_update_kernel, dim3((unsigned)W.n_seq), dim3(WNW_UT), 0, st, W,
+                     (const float*)sg, wnw_state(L, state_in), so);
+  if ((e = hipGetLastError()) != hipSuccess) return wnw_hip(e);
+  return wnw_hip(wnw_launch_recall(W, so, dk, dv, slot_k, slot_v, st));
+}

@@ -412,3 +412,127 @@ def c3_queries(cfg: C3Config, step: int) -> np.ndarray:
     U = cfg.n_seq * cfg.n_layers * cfg.n_kv_heads
     rng = np.random.default_rng(np.random.SeedSequence([4000 + cfg.index, step]))
     return f32_to_bf16_bits(rng.standard_normal((U, cfg.gqa, cfg.head_dim), dtype=np.float32))
+
+
+# ---------------------------------------------------------------------------
+# Decode-time chunk recall (WnW): audio caches, head roles, anchor queries
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class WnwConfig:
+    name: str
+    index: int
+    n_seq: int
+    n_layers: int
+    n_kv_heads: int
+    gqa: int
+    head_dim: int
+    lens: tuple              # audio tokens n per sequence
+    capacity: int
+    anchors: tuple           # units l * n_kv_heads + h with the anchor role
+    fixed: tuple = ()        # units with the fixed role; every other unit is tidal
+
+
+WNW_FOCUS = 2.0     # query gain on the attended keys' mean (see wnw_queries)
+WNW_SPAN = 4        # attended keys per anchor query
+WNW_DRIFT = 4       # positions the attended span moves per step (about 0.3 s)
+WNW_JUMP = 16       # every WNW_JUMP steps the span jumps to a new place
+
+WNW_CONFIGS = {
+    # parity-sized: a short last block (317 = 12 * 25 + 17)
+    "wnw_tiny": WnwConfig("wnw_tiny", 30, 1, 2, 2, 2, 64, lens=(317,), capacity=320,
+                          anchors=(0,), fixed=(2,)),
+    # d = 128, three sequences (one of a single chunk), two anchors
+    "wnw_mixed": WnwConfig("wnw_mixed", 31, 3, 3, 2, 4, 128, lens=(1000, 51, 2503),
+                           capacity=2560, anchors=(0, 3), fixed=(5,)),
+    # one token, under one block, exactly one chunk, a chunk and a half
+    "wnw_edge": WnwConfig("wnw_edge", 32, 4, 1, 3, 1, 64, lens=(1, 24, 50, 76), capacity=80,
+                          anchors=(1,)),
+    # Voxtral-Mini-3B shape (30 layers, 8 KV heads, 4 query heads per KV
+    # head, head_dim 128): 5 anchor heads in the middle layers and 235 tidal
+    # heads, at a 32K-token audio context (about 44 minutes at 12.5 tokens/s)
+    "wnw_voxtral3b": WnwConfig("wnw_voxtral3b", 33, 1, 30, 8, 4, 128, lens=(32768,),
+                               capacity=32768, anchors=(100, 109, 118, 127, 136)),
+}
+
+
+def wnw_roles(cfg: WnwConfig) -> np.ndarray:
+    r = np.full(cfg.n_layers * cfg.n_kv_heads, 2, np.uint8)
+    r[list(cfg.fixed)] = 0
+    r[list(cfg.anchors)] = 1
+    return r
+
+
+def wnw_cache(cfg: WnwConfig, u: int):
+    """One unit's audio keys and values (bf16 bits [n, d]): noise plus a slow
+    drift along the audio and a sink on row 0, as for C3."""
+    n_units = cfg.n_seq * cfg.n_layers * cfg.n_kv_heads
+    rng = np.random.default_rng(np.random.SeedSequence(5000 + cfg.index).spawn(n_units)[u])
+    seq = u // (cfg.n_layers * cfg.n_kv_heads)
+    n, d = int(cfg.lens[seq]), cfg.head_dim
+    periods = rng.uniform(50.0, 400.0, size=N_SINUSOIDS)
+    phases = rng.uniform(0.0, 2.0 * math.pi, size=(N_SINUSOIDS, d))
+    sink = rng.standard_normal(d)
+    sink /= np.linalg.norm(sink)
+    kn = rng.standard_normal((n, d), dtype=np.float32)
+    vv = rng.standard_normal((n, d), dtype=np.float32)
+    t = np.arange(n, dtype=np.float64)
+    w = 2.0 * math.pi / periods
+    A = np.concatenate([np.sin(np.outer(t, w)), np.cos(np.outer(t, w))], axis=1)
+    B = DRIFT_AMP * np.concatenate([np.cos(phases), np.sin(phases)], axis=0)
+    k = kn + (A @ B).astype(np.float32)
+    k[0] += np.float32(SINK_BETA * math.sqrt(d)) * sink.astype(np.float32)
+    return f32_to_bf16_bits(k), f32_to_bf16_bits(vv)
+
+
+def wnw_anchor_keys(cfg: WnwConfig) -> np.ndarray:
+    """Anchor units' keys, bf16 bits [n_seq, n_anchor, capacity, d] (rows past n zero)."""
+    upseq = cfg.n_layers * cfg.n_kv_heads
+    out = np.zeros((cfg.n_seq, len(cfg.anchors), cfg.capacity, cfg.head_dim), np.uint16)
+    for i in range(cfg.n_seq):
+        for a, un in enumerate(sorted(cfg.anchors)):
+            k, _ = wnw_cache(cfg, i * upseq + un)
+            out[i, a, :k.shape[0]] = k
+    return out
+
+
+def wnw_queries(cfg: WnwConfig, step: int, k_anchor_bits: np.ndarray) -> np.ndarray:
+    """Anchor queries of one decode step, bf16 bits [n_seq, n_anchor, G, d]:
+    FOCUS times the mean of WNW_SPAN consecutive keys of the anchor (a span
+    that moves WNW_DRIFT positions per step and jumps every WNW_JUMP steps)
+    plus unit noise, so each anchor attends mostly to one moving stretch."""
+    nA, G, d = len(cfg.anchors), cfg.gqa, cfg.head_dim
+    out = np.zeros((cfg.n_seq, nA, G, d), np.float32)
+    for i in range(cfg.n_seq):
+        n = int(cfg.lens[i])
+        hop = np.random.default_rng(np.random.SeedSequence([5200 + cfg.index, i, step // WNW_JUMP]))
+        start = int(hop.integers(0, n))
+        c = (start + WNW_DRIFT * (step % WNW_JUMP)) % n
+        rng = np.random.default_rng(np.random.SeedSequence([5100 + cfg.index, i, step]))
+        for a in range(nA):
+            k = bf16_bits_to_f32(k_anchor_bits[i, a, :n])
+            lo = min(c, max(0, n - WNW_SPAN))
+            mu = k[lo:lo + WNW_SPAN].mean(axis=0)
+            out[i, a] = WNW_FOCUS * mu[None, :] + rng.standard_normal((G, d), dtype=np.float32)
+    return f32_to_bf16_bits(out)
+
+
+def wnw_host_copies(cfg: WnwConfig, fast: bool = False):
+    """K and V of every unit, bf16 bits [units, capacity, d] (the tidal heads'
+    host copies are read from it).  fast: uniform random bits in place of
+    the cache model (for timing, where only the bytes matter)."""
+    U = cfg.n_seq * cfg.n_layers * cfg.n_kv_heads
+    shape = (U, cfg.capacity, cfg.head_dim)
+    if fast:
+        rng = np.random.default_rng(np.random.SeedSequence(5300 + cfg.index))
+        return rng.integers(0, 1 << 16, size=shape, dtype=np.uint16), \
+            rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    k = np.zeros(shape, np.uint16)
+    v = np.zeros(shape, np.uint16)
+
+    def fill(u):
+        ku, vu = wnw_cache(cfg, u)
+        k[u, :ku.shape[0]], v[u, :vu.shape[0]] = ku, vu
+
+    with _cf.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, range(U)))
+    return k, v

@@ -24,11 +24,12 @@ def declared_symbols(name):
 def test_library_exports_every_declared_symbol():
     L = C.lib()
     headers = sorted(f for f in os.listdir(INCLUDE) if f.endswith(".h"))
-    assert headers == ["kvc.h", "kvc_c3.h", "kvc_voxzip.h"]
+    assert headers == ["kvc.h", "kvc_c3.h", "kvc_voxzip.h", "kvc_wnw.h"]
     assert set(declared_symbols("kvc.h")) == set(C.EXPORTS)
     assert set(declared_symbols("kvc_voxzip.h")) == set(C.VZ_EXPORTS)
     assert set(declared_symbols("kvc_c3.h")) == set(C.C3_EXPORTS)
-    for n in C.EXPORTS + C.VZ_EXPORTS + C.C3_EXPORTS:
+    assert set(declared_symbols("kvc_wnw.h")) == set(C.WNW_EXPORTS)
+    for n in C.EXPORTS + C.VZ_EXPORTS + C.C3_EXPORTS + C.WNW_EXPORTS:
         assert hasattr(L, n), n
 
 
@@ -254,3 +255,86 @@ def test_c3_invalid_problems_rejected_before_launch():
         == C.KVC_ERR_INVALID_ARG
     assert L.kvc_c3_build(ctypes.byref(sp.c()), ctypes.byref(api.C3Params().c()), fake, fake,
                           fake, fake, 16, None) == C.KVC_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------------------
+# include/kvc_wnw.h
+# ---------------------------------------------------------------------------
+def wnw_spec(**kw):
+    prm = api.WnwParams()
+    roles = np.full(30 * 8, C.KVC_WNW_TIDAL, np.uint8)
+    roles[[12, 45, 77, 101, 160]] = C.KVC_WNW_ANCHOR
+    base = dict(n_layers=30, n_kv_heads=8, gqa=4, head_dim=128, lens=[32768], roles=roles,
+                capacity=32768, slot_rows=prm.slot_cap * prm.chunk_stride)
+    base.update(kw)
+    return api.WnwSpec(**base)
+
+
+def test_wnw_plan_layout():
+    prm = api.WnwParams()
+    sp = wnw_spec(lens=[32768, 1000, 51])
+    lay = api.kvc_wnw_plan(sp, prm)
+    assert (lay.n_anchor, lay.n_tidal) == (5, 235)
+    assert lay.block_cap == 32768 // 25 + 1 and lay.chunk_cap == lay.block_cap - 1
+    assert lay.slot_cap == 3 * 3 * 2
+    N = 3
+    spans = sorted([(lay.idle, 4 * N * lay.chunk_cap), (lay.slot_of_block, 4 * N * lay.block_cap),
+                    (lay.block_of_slot, 4 * N * lay.slot_cap), (lay.selected, 4 * N * 3),
+                    (lay.n_recalled, 4 * N), (lay.recalled_block, 4 * N * lay.slot_cap),
+                    (lay.recalled_slot, 4 * N * lay.slot_cap)])
+    for (o, n), (o2, _) in zip(spans, spans[1:] + [(lay.state_bytes, 0)]):
+        assert o % 256 == 0 and o + n <= o2
+    # logits of every anchor head dominate the workspace
+    assert lay.workspace_bytes >= 4 * N * 5 * 4 * 32768
+
+
+def wnw_status(sp, prm=None, ws_bytes=1 << 40, same_state=False):
+    L = C.lib()
+    prm = prm or api.WnwParams()
+    fake = ctypes.c_void_p(1 << 20)
+    other = ctypes.c_void_p(1 << 21)
+    # (every call here must fail validation: nothing may launch on fake pointers)
+    if same_state:
+        return L.kvc_wnw_update(ctypes.byref(sp.c()), ctypes.byref(prm.c()), fake, fake, fake,
+                                None)
+    st = L.kvc_wnw_chunk_scores(ctypes.byref(sp.c()), ctypes.byref(prm.c()), fake, fake, fake,
+                                fake, ws_bytes, None)
+    if st != C.KVC_ERR_WORKSPACE:   # an invalid problem: the update rejects it too
+        assert L.kvc_wnw_update(ctypes.byref(sp.c()), ctypes.byref(prm.c()), fake, fake, other,
+                                None) == st
+    return st
+
+
+def test_wnw_invalid_problems_rejected_before_launch():
+    P = api.WnwParams
+    roles = wnw_spec().roles
+    assert wnw_status(wnw_spec(lens=[0])) == C.KVC_ERR_INVALID_ARG
+    assert wnw_status(wnw_spec(lens=[32769])) == C.KVC_ERR_INVALID_ARG
+    assert wnw_status(wnw_spec(roles=np.where(roles == 1, 0, roles))) == C.KVC_ERR_INVALID_ARG
+    assert wnw_status(wnw_spec(roles=np.full(240, 3, np.uint8))) == C.KVC_ERR_INVALID_ARG
+    assert wnw_status(wnw_spec(roles=np.ones(240, np.uint8))) == C.KVC_ERR_UNSUPPORTED  # 240 anchors
+    assert wnw_status(wnw_spec(), P(chunk_len=60)) == C.KVC_ERR_INVALID_ARG   # not a multiple
+    assert wnw_status(wnw_spec(), P(chunk_len=10)) == C.KVC_ERR_INVALID_ARG   # shorter than S
+    assert wnw_status(wnw_spec(), P(chunk_len=225)) == C.KVC_ERR_UNSUPPORTED  # m = 9
+    assert wnw_status(wnw_spec(), P(top_chunks=0)) == C.KVC_ERR_INVALID_ARG
+    assert wnw_status(wnw_spec(), P(top_chunks=9)) == C.KVC_ERR_UNSUPPORTED
+    assert wnw_status(wnw_spec(), P(release_after=9)) == C.KVC_ERR_UNSUPPORTED
+    assert wnw_status(wnw_spec(head_dim=96)) == C.KVC_ERR_UNSUPPORTED
+    assert wnw_status(wnw_spec(gqa=33)) == C.KVC_ERR_UNSUPPORTED
+    assert wnw_status(wnw_spec(capacity=140000, lens=[1000])) == C.KVC_ERR_UNSUPPORTED
+    assert wnw_status(wnw_spec(lens=[1000] * 65)) == C.KVC_ERR_UNSUPPORTED
+    assert wnw_status(wnw_spec(k_stride=(32768 * 128, 100))) == C.KVC_ERR_INVALID_ARG
+    assert wnw_status(wnw_spec(host_stride=(1000 * 128, 128))) == C.KVC_ERR_INVALID_ARG
+    assert wnw_status(wnw_spec(slot_rows=100)) == C.KVC_ERR_INVALID_ARG       # < 18 blocks
+    assert wnw_status(wnw_spec(), ws_bytes=16) == C.KVC_ERR_WORKSPACE
+    assert wnw_status(wnw_spec(), same_state=True) == C.KVC_ERR_INVALID_ARG
+
+
+def test_wnw_fixed_select_rejects_segment_lengths():
+    L = C.lib()
+    sp = api.Spec(n_layers=2, n_kv_heads=2, gqa=2, head_dim=64, seq_lens=[256], retention=[0.5],
+                  dtype="bf16")
+    fake = ctypes.c_void_p(1 << 20)
+    for seg in (0, 65):
+        assert L.kvc_wnw_fixed_select(ctypes.byref(sp.c()), ctypes.byref(api.Params().c()), seg,
+                                      fake, fake, fake, fake, None) == C.KVC_ERR_INVALID_ARG
