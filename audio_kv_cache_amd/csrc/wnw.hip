@@ -8,9 +8,10 @@
 //                          every anchor's G query heads, and per-wave
 //                          (max, sum exp) partials; one thread per key.
 //   wnw_lse_kernel         the partials folded into each head's LSE.
-//   wnw_block_mass_kernel  per block: the anchors' attention mass (mean over
-//                          heads of exp2(l - LSE)), anchors and positions in
-//                          order; one thread per block.
+//   wnw_position_mass_kernel  per position: the anchors' attention mass
+//                          (sum over anchors of the mean over heads of
+//                          exp2(l - LSE)); one thread per position.
+//   wnw_block_mass_kernel  per block: its positions' masses summed in order.
 //   wnw_sigma_kernel       chunk scores: the sums of m consecutive blocks.
 //   wnw_update_kernel      one 1024-thread workgroup per sequence: top-K by
 //                          packed (score, index) maxima, idle counts,
@@ -63,6 +64,7 @@ struct WnwWork {
   float* logits;   // [n_seq * n_anchor][G][max_len]
   float2* parts;   // [n_seq * n_anchor][G][max_parts]
   float* lse2;     // [n_seq * n_anchor][G]
+  float* pmass;    // [n_seq][max_len]
   float* beta;     // [n_seq][block_cap]
   float* sigma;    // [n_seq][chunk_cap]
 };
@@ -162,27 +164,33 @@ __global__ __launch_bounds__(256) void wnw_lse_kernel(WnwDesc W, WnwWork X) {
   }
 }
 
+// Attention mass per position: sum over anchors of the mean over their heads
+// of exp2(l - LSE); one thread per position (coalesced logit reads).
+__global__ __launch_bounds__(256) void wnw_position_mass_kernel(WnwDesc W, WnwWork X) {
+  const int seq = blockIdx.y, j = blockIdx.x * 256 + (int)threadIdx.x;
+  const int n = W.len[seq];
+  if (j >= n) return;
+  const float invG = 1.0f / (float)W.gqa;
+  float p = 0.f;
+  for (int a = 0; a < W.n_anchor; ++a) {
+    const size_t row0 = (size_t)(seq * W.n_anchor + a) * W.gqa;
+    float pa = 0.f;
+    for (int g = 0; g < W.gqa; ++g)
+      pa += __builtin_amdgcn_exp2f(X.logits[(row0 + g) * W.max_len + j] - X.lse2[row0 + g]);
+    p += pa * invG;
+  }
+  X.pmass[(size_t)seq * W.max_len + j] = p;
+}
+
+// Block masses: the sums of S consecutive position masses, in order.
 __global__ __launch_bounds__(256) void wnw_block_mass_kernel(WnwDesc W, WnwWork X) {
   const int seq = blockIdx.y, b = blockIdx.x * 256 + (int)threadIdx.x;
   const int n = W.len[seq], B = (n + W.S - 1) / W.S;
   if (b >= W.block_cap) return;
   float beta = 0.f;
   if (b < B) {
-    const int lo = b * W.S, hi = min(n, lo + W.S);
-    const float invG = 1.0f / (float)W.gqa;
-    for (int a = 0; a < W.n_anchor; ++a) {
-      const int sa = seq * W.n_anchor + a;
-      float pa = 0.f;
-      for (int j = lo; j < hi; ++j) {
-        float pj = 0.f;
-        for (int g = 0; g < W.gqa; ++g) {
-          const size_t row = (size_t)sa * W.gqa + g;
-          pj += __builtin_amdgcn_exp2f(X.logits[row * W.max_len + j] - X.lse2[row]);
-        }
-        pa += pj;
-      }
-      beta += pa * invG;
-    }
+    const float* pm = X.pmass + (size_t)seq * W.max_len;
+    for (int j = b * W.S; j < min(n, (b + 1) * W.S); ++j) beta += pm[j];
   }
   X.beta[(size_t)seq * W.block_cap + b] = beta;
 }
@@ -552,7 +560,8 @@ static void wnw_layout(const WnwDesc& W, kvc_wnw_layout* L) {
   L->state_bytes = o;
   const size_t SA = N * W.n_anchor * W.gqa;
   L->workspace_bytes = wnw_up(4 * SA * W.max_len) + wnw_up(8 * SA * W.max_parts) +
-                       wnw_up(4 * SA) + wnw_up(4 * N * W.block_cap) + wnw_up(4 * N * W.chunk_cap);
+                       wnw_up(4 * SA) + wnw_up(4 * N * W.max_len) + wnw_up(4 * N * W.block_cap) +
+                       wnw_up(4 * N * W.chunk_cap);
 }
 
 static WnwState wnw_state(const kvc_wnw_layout& L, const void* p) {
@@ -575,6 +584,7 @@ static WnwWork wnw_work(const WnwDesc& W, void* p) {
   X.logits = (float*)b;  b += wnw_up(4 * SA * W.max_len);
   X.parts = (float2*)b;  b += wnw_up(8 * SA * W.max_parts);
   X.lse2 = (float*)b;    b += wnw_up(4 * SA);
+  X.pmass = (float*)b;   b += wnw_up(4 * N * W.max_len);
   X.beta = (float*)b;    b += wnw_up(4 * N * W.block_cap);
   X.sigma = (float*)b;
   return X;
@@ -633,8 +643,12 @@ static hipError_t wnw_launch_scores(const WnwDesc& W, const void* q, const void*
     hipLaunchKernelGGL(wnw_logits_kernel<64>, g1, dim3(WNW_TILE), 0, st, W, (const uint16_t*)q,
                        (const uint16_t*)k, X);
   hipLaunchKernelGGL(wnw_lse_kernel, dim3((unsigned)(W.n_seq * W.n_anchor)), dim3(256), 0, st, W, X);
-  hipLaunchKernelGGL(wnw_block_mass_kernel, dim3((unsigned)((W.block_cap + 255) / 256), (unsigned)W.n_seq),
-                     dim3(256), 0, st, W, X);
+  hipLaunchKernelGGL(wnw_position_mass_kernel,
+                     dim3((unsigned)((W.max_len + 255) / 256), (unsigned)W.n_seq), dim3(256), 0, st,
+                     W, X);
+  hipLaunchKernelGGL(wnw_block_mass_kernel,
+                     dim3((unsigned)((W.block_cap + 255) / 256), (unsigned)W.n_seq), dim3(256), 0,
+                     st, W, X);
   hipLaunchKernelGGL(wnw_sigma_kernel, dim3((unsigned)((W.chunk_cap + 255) / 256), (unsigned)W.n_seq),
                      dim3(256), 0, st, W, (const float*)X.beta, sigma);
   return hipGetLastError();

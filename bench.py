@@ -16,6 +16,10 @@ reach.  Algorithmic bytes per (sequence, layer, KV head) unit:
   + G W d e          window queries read
 (e = element size, b = the unit's budget); V is never read for the scores and
 the score rows are workspace.
+
+The same line carries three decode-time legs under "decode", "retrieval"
+and "recall" (decayed eviction, query-guided retrieval, chunk recall), each
+timed on its own workload; --no-decode, --no-c3 and --no-wnw skip them.
 """
 from __future__ import annotations
 
@@ -388,6 +392,175 @@ def bench_c3(args):
     return out
 
 
+PCIE_PEAK_GBS = 64.0        # PCIe 5.0 x16, one direction (the MI355X host link)
+
+
+def bench_wnw(args):
+    """WnW chunk recall: one decode step (anchor chunk scores, top-3 with
+    release hysteresis, slot update, recall of newly resident blocks of every
+    tidal head from page-locked host memory), inputs resident (anchor keys
+    in HBM, tidal copies in host memory); per-stage event timing, the bytes
+    recalled per step, a cold step (everything recalled), CPU-oracle sample."""
+    import torch
+    from audio_kv_cache_amd import api, synth
+    cfg = synth.WNW_CONFIGS[args.wnw_config]
+    prm = api.WnwParams()
+    S = prm.chunk_stride
+    log(f"[bench] wnw: generating {cfg.name}")
+    roles = synth.wnw_roles(cfg)
+    spec = api.WnwSpec(n_layers=cfg.n_layers, n_kv_heads=cfg.n_kv_heads, gqa=cfg.gqa,
+                       head_dim=cfg.head_dim, lens=cfg.lens, roles=roles, capacity=cfg.capacity,
+                       slot_rows=prm.slot_cap * S)
+    ka = synth.wnw_anchor_keys(cfg)
+    U, upseq, d = spec.n_units, cfg.n_layers * cfg.n_kv_heads, cfg.head_dim
+    k = torch.zeros((U, cfg.capacity, d), dtype=torch.int16, device="cuda")
+    for i in range(cfg.n_seq):
+        for a, un in enumerate(sorted(cfg.anchors)):
+            k[i * upseq + un] = torch.from_numpy(ka[i, a].view(np.int16)).cuda()
+    kh_np, vh_np = synth.wnw_host_copies(cfg, fast=True)
+    hk = torch.empty(kh_np.shape, dtype=torch.int16, pin_memory=True)
+    hv = torch.empty(vh_np.shape, dtype=torch.int16, pin_memory=True)
+    hk.copy_(torch.from_numpy(kh_np.view(np.int16)))
+    hv.copy_(torch.from_numpy(vh_np.view(np.int16)))
+    del kh_np, vh_np
+    o = api.wnw_allocate(spec, prm, "cuda")
+    lay = o["layout"]
+    stream = torch.cuda.current_stream()
+    n_steps = args.warmup + args.steps
+    qs = [torch.from_numpy(synth.wnw_queries(cfg, t, ka).view(np.int16)).cuda()
+          for t in range(n_steps)]
+    cur = [0]
+
+    def reset():
+        for st in o["state"]:
+            api.kvc_wnw_init(spec, prm, st, stream)
+        cur[0] = 0
+
+    def step(t):
+        si, so = o["state"][cur[0]], o["state"][1 - cur[0]]
+        api.kvc_wnw_step(spec, prm, qs[t], k, si, so, hk, hv, o["slot_k"], o["slot_v"],
+                         o["sigma"], o["ws"], stream)
+        cur[0] = 1 - cur[0]
+
+    # Pass 1, untimed: the blocks recalled by each step.
+    reset()
+    rec_blocks = []
+    for t in range(n_steps):
+        step(t)
+        torch.cuda.synchronize()
+        V = api.WnwViews(spec, prm, lay, o["state"][cur[0]])
+        nrec = V.n_recalled.cpu().numpy()
+        rb = V.recalled_block.cpu().numpy()
+        rows = 0
+        for i, n in enumerate(cfg.lens):
+            for r in range(int(nrec[i])):
+                rows += min(S, int(n) - int(rb[i, r]) * S)
+        rec_blocks.append((int(nrec.sum()), rows))
+    row_bytes = 2 * d * 2 * int(lay.n_tidal)          # K and V rows of every tidal head
+    timed_rows = sum(r for _, r in rec_blocks[args.warmup:])
+    bytes_per_step = timed_rows * row_bytes / args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Pass 2, timed: the same steps from the same state.
+    reset()
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for t in range(args.warmup, n_steps):
+        step(t)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(n):
+            fn(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n
+
+    si, so = o["state"][cur[0]], o["state"][1 - cur[0]]
+    stages = {
+        "chunk_scores": timed(lambda i: api.kvc_wnw_chunk_scores(spec, prm, qs[-1], k, o["sigma"],
+                                                                 o["ws"], stream), args.steps),
+        "update": timed(lambda i: api.kvc_wnw_update(spec, prm, o["sigma"], si, so, stream),
+                        args.steps),
+    }
+    # Cold step: from the empty state, every selected block is recalled.
+    cold = []
+    for _ in range(max(3, args.steps // 4)):
+        reset()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        step(0)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(ev0.elapsed_time(ev1))
+    V = api.WnwViews(spec, prm, lay, o["state"][cur[0]])
+    cold_rows = 0
+    for i, n in enumerate(cfg.lens):
+        rb = V.recalled_block[i].cpu().numpy()
+        for r in range(int(V.n_recalled[i].item())):
+            cold_rows += min(S, int(n) - int(rb[r]) * S)
+    cold_ms = sorted(cold)[len(cold) // 2]
+    # the recall alone on the cold step's list
+    so_cold = o["state"][cur[0]]
+    recall_ms = timed(lambda i: api.kvc_wnw_recall(spec, prm, so_cold, hk, hv, o["slot_k"],
+                                                   o["slot_v"], stream), args.steps)
+    cold_bytes = cold_rows * row_bytes
+    recall_gbs = cold_bytes / (recall_ms * 1e-3) / 1e9
+    anchor_bytes = sum(int(n) for n in cfg.lens) * int(lay.n_anchor) * d * 2
+    score_gbs = anchor_bytes / (stages["chunk_scores"] * 1e-3) / 1e9
+    log(f"[bench] wnw step {step_ms * 1e3:.1f} us, {bytes_per_step / 1e6:.3f} MB recalled per "
+        f"step; chunk scores {stages['chunk_scores'] * 1e3:.1f} us, update "
+        f"{stages['update'] * 1e3:.1f} us; cold step {cold_ms * 1e3:.1f} us recalling "
+        f"{cold_bytes / 1e6:.2f} MB ({recall_gbs:.1f} GB/s in the recall kernel)")
+    out = {
+        "workload": f"{cfg.name}: {cfg.n_seq} seq x n={list(cfg.lens)} audio tokens, "
+                    f"{cfg.n_layers} layers x {cfg.n_kv_heads} KV heads ({lay.n_anchor} anchor, "
+                    f"{lay.n_tidal} tidal), GQA {cfg.gqa}, head_dim {d}, bf16; chunks "
+                    f"{prm.chunk_len}/{prm.chunk_stride} tokens, top {prm.top_chunks}, release "
+                    f"after {prm.release_after}",
+        "us_per_step": round(step_ms * 1e3, 2),
+        "steps_per_s": 1e3 / step_ms,
+        "recalled_bytes_per_step": bytes_per_step,
+        "recalled_blocks": [b for b, _ in rec_blocks[args.warmup:]],
+        "stage_us": {n2: round(t * 1e3, 2) for n2, t in stages.items()},
+        "cold_step_us": round(cold_ms * 1e3, 2),
+        "cold_recall_bytes": cold_bytes,
+        "roofline": {
+            "recall": {"bound": "pcie", "kernel": f"wnw_recall_kernel<{d}>",
+                       "achieved": round(recall_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(recall_gbs / PCIE_PEAK_GBS, 4),
+                       "note": "cold-step recall list, host to device over PCIe"},
+            "chunk_scores": {"bound": "hbm", "kernel": "wnw_logits_kernel + lse/mass/sigma",
+                             "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
+                             "traffic": None},
+        },
+    }
+    if not args.no_cpu_baseline:
+        from oracle import wnw as Wo
+        n = int(cfg.lens[0])
+        ks = [synth.bf16_bits_to_f32(ka[0, a, :n]).astype(np.float64)
+              for a in range(len(cfg.anchors))]
+        st = Wo.Residency(n, S, prm.chunk_len, prm.top_chunks, prm.release_after)
+        t0 = time.perf_counter()
+        nst = 5
+        for t in range(nst):
+            qa = synth.bf16_bits_to_f32(synth.wnw_queries(cfg, t, ka)[0]).astype(np.float64)
+            _, _, st, _ = Wo.step(st, list(qa), ks)
+        ts = (time.perf_counter() - t0) / nst
+        out["cpu_baseline"] = dict(value=1.0 / ts, unit="steps/s (scores + update, no copies)",
+                                   cores=1, kind="oracle",
+                                   sample=f"{nst} decode steps of sequence 0 of the same workload, "
+                                          f"{ts * 1e3:.1f} ms per step")
+    del hk, hv, k
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,6 +578,11 @@ def main():
     ap.add_argument("--c3-builds", type=int, default=3)
     ap.add_argument("--c3-only", action="store_true",
                     help="measure only the C3 leg and print its object")
+    ap.add_argument("--no-wnw", action="store_true",
+                    help="skip the chunk-recall (WnW) measurement")
+    ap.add_argument("--wnw-config", default="wnw_voxtral3b")
+    ap.add_argument("--wnw-only", action="store_true",
+                    help="measure only the WnW leg and print its object")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -419,6 +597,9 @@ def main():
 
     if args.c3_only:
         print(json.dumps(bench_c3(args)), flush=True)
+        return
+    if args.wnw_only:
+        print(json.dumps(bench_wnw(args)), flush=True)
         return
 
     cfg = synth.CONFIGS[args.config]
@@ -550,6 +731,7 @@ def main():
 
     decode = None if args.no_decode else bench_decode(args)
     retrieval = None if args.no_c3 else bench_c3(args)
+    recall = None if args.no_wnw else bench_wnw(args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -576,6 +758,7 @@ def main():
         "roofline_other_kernels": others,
         "decode": decode,
         "retrieval": retrieval,
+        "recall": recall,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
