@@ -305,10 +305,10 @@ def bench_c3(args):
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     cur = [0]
 
-    def step(i):
+    def step(i, st=stream):
         si, so = o["state"][cur[0]], o["state"][1 - cur[0]]
         api.kvc_c3_step(spec, prm, o["index"], si, so, qs[i % 4], k, v, o["k_out"], o["v_out"],
-                        o["idx"], o["step_ws"], stream)
+                        o["idx"], o["step_ws"], st)
         cur[0] = 1 - cur[0]
 
     def timed(fn, n):
@@ -323,6 +323,8 @@ def bench_c3(args):
         return ev0.elapsed_time(ev1) / n
 
     step_ms = timed(step, args.steps)
+    # the same steps replayed from one captured graph
+    graph_step_ms = graph_ms(lambda: [step(i, None) for i in range(args.steps)], args.steps)
     si = o["state"][cur[0]]
     so = o["state"][1 - cur[0]]
     stages = {
@@ -338,7 +340,7 @@ def bench_c3(args):
     ab = c3_bytes(cfg, A_total, kept_total)
     gbs = {n2: ab[n3] / (stages[n2] * 1e-3) / 1e9 for n2, n3 in
            (("score", "score"), ("gather", "gather"))}
-    log(f"[bench] c3 step {step_ms * 1e3:.1f} us; stages " +
+    log(f"[bench] c3 step {step_ms * 1e3:.1f} us ({graph_step_ms * 1e3:.1f} us from a graph); stages " +
         ", ".join(f"{n2} {t * 1e3:.1f} us" for n2, t in stages.items()))
 
     def hbm(kernel, g, src):
@@ -359,6 +361,7 @@ def bench_c3(args):
                            "ops": build_ops},
         "nodes": int(nn.sum()), "frontier_entries": A_total,
         "us_per_step": round(step_ms * 1e3, 2),
+        "us_per_step_graph": round(graph_step_ms * 1e3, 2),
         "steps_per_s": 1e3 / step_ms,
         "algorithmic_bytes_per_step": ab["total"],
         "stage_us": {n2: round(t * 1e3, 2) for n2, t in stages.items()},
@@ -393,6 +396,24 @@ def bench_c3(args):
 
 
 PCIE_PEAK_GBS = 64.0        # PCIe 5.0 x16, one direction (the MI355X host link)
+
+
+def graph_ms(issue, n):
+    """Capture issue() (n steps launched on the current stream) into one HIP
+    graph, replay it once, and return the event time per step."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        issue()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / n
 
 
 def bench_wnw(args):
@@ -436,10 +457,10 @@ def bench_wnw(args):
             api.kvc_wnw_init(spec, prm, st, stream)
         cur[0] = 0
 
-    def step(t):
+    def step(t, st=stream):
         si, so = o["state"][cur[0]], o["state"][1 - cur[0]]
         api.kvc_wnw_step(spec, prm, qs[t], k, si, so, hk, hv, o["slot_k"], o["slot_v"],
-                         o["sigma"], o["ws"], stream)
+                         o["sigma"], o["ws"], st)
         cur[0] = 1 - cur[0]
 
     # Pass 1, untimed: the blocks recalled by each step.
@@ -471,6 +492,12 @@ def bench_wnw(args):
     ev1.record(stream)
     torch.cuda.synchronize()
     step_ms = ev0.elapsed_time(ev1) / args.steps
+    # Pass 3: the same timed steps from the same state, replayed from one graph.
+    reset()
+    for t in range(args.warmup):
+        step(t)
+    graph_step_ms = graph_ms(lambda: [step(t, None) for t in range(args.warmup, n_steps)],
+                             args.steps)
 
     def timed(fn, n):
         torch.cuda.synchronize()
@@ -513,7 +540,8 @@ def bench_wnw(args):
     recall_gbs = cold_bytes / (recall_ms * 1e-3) / 1e9
     anchor_bytes = sum(int(n) for n in cfg.lens) * int(lay.n_anchor) * d * 2
     score_gbs = anchor_bytes / (stages["chunk_scores"] * 1e-3) / 1e9
-    log(f"[bench] wnw step {step_ms * 1e3:.1f} us, {bytes_per_step / 1e6:.3f} MB recalled per "
+    log(f"[bench] wnw step {step_ms * 1e3:.1f} us ({graph_step_ms * 1e3:.1f} us from a graph), "
+        f"{bytes_per_step / 1e6:.3f} MB recalled per "
         f"step; chunk scores {stages['chunk_scores'] * 1e3:.1f} us, update "
         f"{stages['update'] * 1e3:.1f} us; cold step {cold_ms * 1e3:.1f} us recalling "
         f"{cold_bytes / 1e6:.2f} MB ({recall_gbs:.1f} GB/s in the recall kernel)")
@@ -524,6 +552,7 @@ def bench_wnw(args):
                     f"{prm.chunk_len}/{prm.chunk_stride} tokens, top {prm.top_chunks}, release "
                     f"after {prm.release_after}",
         "us_per_step": round(step_ms * 1e3, 2),
+        "us_per_step_graph": round(graph_step_ms * 1e3, 2),
         "steps_per_s": 1e3 / step_ms,
         "recalled_bytes_per_step": bytes_per_step,
         "recalled_blocks": [b for b, _ in rec_blocks[args.warmup:]],
@@ -625,9 +654,9 @@ def main():
     out = api.allocate(spec, prm, k.device)
     stream = torch.cuda.current_stream()
 
-    def step():
+    def step(st=stream):
         api.kvc_compress(spec, prm, q, k, v, S, out["k_out"], out["v_out"], out["idx"],
-                         out["offsets"], out["budgets"], out["workspace"], stream)
+                         out["offsets"], out["budgets"], out["workspace"], st)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -643,6 +672,9 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    # the same K steps replayed from one captured graph (no host launches)
+    ms_graph = graph_ms(lambda: [step(None) for _ in range(args.steps)], args.steps)
+    log(f"[bench] from a graph: {ms_graph:.3f} ms/step")
     budgets = out["budgets"].cpu().numpy()
     ab = algorithmic_bytes(cfg, hdr, budgets)
     tokheads = sum(int(L) for L in hdr.lengths) * cfg.n_layers * cfg.n_kv_heads
@@ -742,7 +774,7 @@ def main():
     line = {
         "metric": "compressed tokens·heads/s and % of HBM peak, L=32K audio tokens, 1 GPU",
         "value": value, "unit": "tokens·heads/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_graph": round(ms_graph, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.n_seq} seq x L={int(hdr.lengths[0]) if cfg.n_seq == 1 else 'ragged'}"
                                f", {cfg.n_layers} layers x {cfg.n_kv_heads} KV heads, GQA {cfg.gqa}, "
