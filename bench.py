@@ -675,6 +675,16 @@ def main():
     # the same K steps replayed from one captured graph (no host launches)
     ms_graph = graph_ms(lambda: [step(None) for _ in range(args.steps)], args.steps)
     log(f"[bench] from a graph: {ms_graph:.3f} ms/step")
+    # per-step spread: K more steps, each between its own pair of events
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    pct = {f"p{p}": round(float(np.percentile(per_step, p)), 4) for p in (10, 50, 90)}
     budgets = out["budgets"].cpu().numpy()
     ab = algorithmic_bytes(cfg, hdr, budgets)
     tokheads = sum(int(L) for L in hdr.lengths) * cfg.n_layers * cfg.n_kv_heads
@@ -774,7 +784,8 @@ def main():
     line = {
         "metric": "compressed tokens·heads/s and % of HBM peak, L=32K audio tokens, 1 GPU",
         "value": value, "unit": "tokens·heads/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_graph": round(ms_graph, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_graph": round(ms_graph, 4),
+        "ms_per_step_percentiles": pct, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.n_seq} seq x L={int(hdr.lengths[0]) if cfg.n_seq == 1 else 'ragged'}"
                                f", {cfg.n_layers} layers x {cfg.n_kv_heads} KV heads, GQA {cfg.gqa}, "
