@@ -15,9 +15,14 @@
 //    j mod Ns + m Ns, natural order after the last pass; Govindaraju et al.,
 //    SC 2008).  Every thread keeps V = 8, 16 or 32 values in registers and
 //    runs radix-V butterflies on them; passes exchange data through one
-//    LDS buffer of N floats (real and imaginary parts in turn), padded by one
-//    float per 32 so strided passes do not collide on banks.  N = 32768 (L =
-//    65536) thus fits in 132 KiB of LDS without a multi-pass global variant.
+//    LDS buffer (N complex values, or for N = 32768 (L = 65536) N floats
+//    with the real and imaginary parts in turn, 128 KiB), so every length
+//    fits one workgroup without a multi-pass global variant.  The buffer is
+//    not padded: the first pass's strided writes conflict on LDS banks
+//    (counters: about 3 conflict cycles per LDS instruction over the
+//    kernel at L = 32768), but one pad slot per 16 pairs, as tried, made
+//    the addresses nonlinear in the slot index and raised the register
+//    spills at L = 32768 from 10 to 55 VGPRs per lane.
 //  * E(k) is summed in fp64 from the fp32 spectrum; k* is the first bin
 //    whose prefix reaches rho E(N), found with a block scan.
 //
