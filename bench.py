@@ -693,6 +693,21 @@ def main():
     log(f"[bench] {ms:.3f} ms/step, {value:.4g} tokens·heads/s, path {path_gbs:.0f} GB/s "
         f"({100 * path_gbs / HBM_PEAK_GBS:.1f} % of HBM peak)")
 
+    # A measured ceiling beside the spec peak: a plain 2 GiB device copy
+    # (1 GiB read + 1 GiB written), timed with events.
+    csrc = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(5):
+        cdst.copy_(csrc)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * csrc.numel() * 4 * 5 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del csrc, cdst
+    log(f"[bench] device copy ceiling {copy_gbs:.0f} GB/s")
+
     if args.calib_copy:
         # A plain copy of known size: what HBM counters read for it scales
         # the counters of the path's kernels to bytes.
@@ -749,7 +764,8 @@ def main():
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                     "traffic": committed_traffic(src, kernel.split("<")[0], cfg.name),
                     "algorithmic_bytes": nbytes // launches, "avg_launch_us":
-                        round(ms * 1e3 / launches, 1)}
+                        round(ms * 1e3 / launches, 1),
+                    "frac_of_copy": round(gbs / copy_gbs, 4)}
 
         t_hbm = ab["pool"] / (HBM_PEAK_GBS * 1e9)
         t_mfma = ab["score_flops"] / (MFMA_PEAK_TFLOPS[cfg.dtype] * 1e12)
@@ -795,7 +811,9 @@ def main():
                    "tokens_heads_per_step": tokheads,
                    "algorithmic_bytes_per_step": ab["total"]},
         "path_hbm": {"achieved": round(path_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(path_gbs / HBM_PEAK_GBS, 4)},
+                     "frac": round(path_gbs / HBM_PEAK_GBS, 4),
+                     "copy_ceiling": round(copy_gbs, 1),
+                     "frac_of_copy": round(path_gbs / copy_gbs, 4)},
         "stage_ms": {k2: round(v2, 4) for k2, v2 in stages.items()},
         "roofline": roof,
         "roofline_other_kernels": others,

@@ -100,3 +100,19 @@ def test_compress_omni30b_30000_sampled():
     P.say("[e2e] omni30b_30000")
     D = P.dev("omni30b_30000")
     P._check_e2e(D, [(0, 0, 0), (0, 23, 2), (0, 47, 3)])
+
+
+def test_compress_ragged_npot_layer_pool():
+    P.say("[e2e] ragged_npot, one budget pool per layer")
+    D = P.dev("ragged_npot", budget_pool=1)
+    P._check_e2e(D, D.units())
+
+
+def test_compress_ragged_npot_maxpool():
+    P.say("[e2e] ragged_npot, max over query heads")
+    D = P.dev("ragged_npot", score_pool=1)
+    P._check_e2e(D, D.units())
+
+
+def test_compress_layers_npot_equals_whole_call():
+    P.test_compress_layers_equals_whole_call("ragged_npot", [(0, 1), (1, 3), (3, 4)])
