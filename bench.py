@@ -779,11 +779,22 @@ def main():
                     "peak": MFMA_PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s",
                     "frac": round(tf / MFMA_PEAK_TFLOPS[cfg.dtype], 4),
                     "traffic": committed_traffic("score.hip", pool_kernel.split("<")[0], cfg.name)}
+        # Beside HBM and MFMA, the per-element VALU work of both passes: an FMA,
+        # an exponential (two FMA issue slots) and an add per logit, against
+        # the VALU issue rate (lane-ops/s).
+        logits = ab["score_flops"] // (2 * cfg.head_dim)
+
+        def valu_frac(ms):
+            return round(4 * logits / (ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4)
         roof["mfma_frac"] = round(ab["score_flops"] / (stages["score_pool"] * 1e-3) / 1e12
                                   / MFMA_PEAK_TFLOPS[cfg.dtype], 4)
+        roof["valu_frac"] = valu_frac(stages["score_pool"])
         others["score_stats"] = hbm("score_stats", "kvc_score_stats_qs_kernel" if cfg.dtype == "bf16"
                                     else "kvc_score_stats_kernel", ab["stats"],
                                     stages["score_stats"], "score.hip")
+        others["score_stats"]["mfma_frac"] = round(
+            ab["score_flops"] / (stages["score_stats"] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[cfg.dtype], 4)
+        others["score_stats"]["valu_frac"] = valu_frac(stages["score_stats"])
         others["gather"] = hbm("gather", "kvc_gather_kernel<256>", ab["gather"], stages["gather"],
                                "gather.hip")
 
