@@ -16,7 +16,7 @@ retrieval bypassed when the audio fits the budget).
 
 The tree is a set of integer decisions taken by floating point, so every
 decision is defined here in the precision and operation order a GPU can
-reproduce exactly (readings, each listed in the design doc):
+reproduce exactly (readings of the page):
   * one index per (sequence, layer, KV head) cache of n audio keys (bf16);
     keys must be finite with |k| < 4096 and n <= 2^17;
   * the keys are first snapped to the grid 2^-24 (only |k| < 2^-17 moves),

@@ -21,8 +21,8 @@
  *               block), with the cap at L and largest-remainder rounding
  *   kvo_select  per-head top-k of the smoothed row plus the local window
  *
- * Conventions (the readings taken where the pages are silent are listed in
- * the design doc of the repository): all floating point is IEEE fp64, sums run
+ * Conventions (readings taken where the pages are silent): all floating
+ * point is IEEE fp64, sums run
  * in ascending index order, and the file is compiled with
  * -ffp-contract=off so that no multiply-add is fused.
  *

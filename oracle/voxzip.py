@@ -17,7 +17,7 @@ concatenation rule), with the hyper-parameters of its details list:
     tokens of highest A(t); the new cache is the concatenation
     K[:T], K[I_hist], K[-M:] (V alike).
 
-Readings taken where the page is open (each is listed in the design doc):
+Readings taken where the page is open:
   * one cache per (sequence, layer, KV head); the G query heads of the KV
     head's group each give one softmax row over the cache, and A adds their
     mean (the plain GQA reading; a sum would select identically);

@@ -21,7 +21,7 @@ its reproduction notes:
     segment (instead of one top-k over the whole audio), so that no stretch
     of a long recording is left without cache.
 
-Readings taken where the page is open (each is listed in the design doc):
+Readings taken where the page is open:
   * chunk geometry in tokens: stride S (2 s) and length W = m S (4 s, m = 2);
     block b = positions [b S, min((b + 1) S, n)), B = ceil(n / S) blocks;
     chunk c = blocks c .. c + m - 1 (clipped), C = max(1, B - m + 1) chunks,
