@@ -15,7 +15,8 @@ CSRC = PKG / "csrc"
 BUILD = PKG / "_build"
 LIB = PKG / "libkvc.so"
 SOURCES = ["kvc_host.hip", "budget.hip", "score.hip", "sss_select.hip", "gather.hip",
-           "voxzip.hip", "c3.hip", "wnw.hip"]
+           "voxzip.hip", "c3.hip", "wnw.hip",
+           "check.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

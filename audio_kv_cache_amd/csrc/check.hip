@@ -1,0 +1,82 @@
+// check.hip -- optional input checks of the prefill entry points (enabled by
+// the environment variable KVC_CHECK_INPUTS=1): every window query, key and
+// value element of the units in a call must be finite, every head score
+// finite and >= 0.  One thread per 16-byte piece; a violation sets a flag.
+#include "kvc_internal.h"
+
+template <class E>
+__device__ __forceinline__ bool kvc_piece_bad(uint4 x) {
+  if constexpr (sizeof(E) == 2) {
+    // bf16: exponent bits all ones -> Inf or NaN
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      bad |= ((w[i] & 0x7F80u) == 0x7F80u) | (((w[i] >> 16) & 0x7F80u) == 0x7F80u);
+    return bad;
+  } else {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bad |= (w[i] & 0x7F800000u) == 0x7F800000u;
+    return bad;
+  }
+}
+
+// grid: (row blocks of 256, units of the range); block 256.
+template <class E>
+__global__ __launch_bounds__(256) void kvc_check_kernel(KvcDesc D, int u0, const E* __restrict__ q,
+                                                        const E* __restrict__ k,
+                                                        const E* __restrict__ v,
+                                                        const float* __restrict__ S,
+                                                        int32_t* __restrict__ flag) {
+  const int u = u0 + (int)blockIdx.y;
+  const int seq = u / D.upseq, within = u - seq * D.upseq;
+  const int l = within / D.n_heads, h = within - l * D.n_heads;
+  const int L = D.L[seq];
+  const int pieces = D.d * (int)sizeof(E) / 16;  // per row
+  bool bad = false;
+  const int r0 = blockIdx.x * 256;
+  if (r0 < L) {
+    const E* kb = k + kvc_kv_offset(D.ks, D, seq, l, h);
+    const E* vb = v + kvc_kv_offset(D.vs, D, seq, l, h);
+    const int rows = min(256, L - r0);
+    for (int i = threadIdx.x; i < rows * pieces; i += 256) {
+      const int r = r0 + i / pieces, p = i % pieces;
+      bad |= kvc_piece_bad<E>(reinterpret_cast<const uint4*>(kb + (int64_t)r * D.ks[2])[p]);
+      bad |= kvc_piece_bad<E>(reinterpret_cast<const uint4*>(vb + (int64_t)r * D.vs[2])[p]);
+    }
+  }
+  if (blockIdx.x == 0) {
+    const uint4* qb = reinterpret_cast<const uint4*>(q + kvc_q_offset(D, seq, l, h));
+    const int n = D.gqa * D.nwin * pieces;
+    for (int i = threadIdx.x; i < n; i += 256) bad |= kvc_piece_bad<E>(qb[i]);
+    if (threadIdx.x == 0) {
+      const float s = S[l * D.n_heads + h];
+      bad |= !(s >= 0.0f) || s == INFINITY;
+    }
+  }
+  if (bad) atomicOr(flag, 1);
+}
+
+__global__ void kvc_check_clear_kernel(int32_t* flag) { flag[threadIdx.x] = 0; }  // one thread
+
+hipError_t kvc_launch_check(const KvcDesc& D, int u0, int u1, const void* q, const void* k,
+                            const void* v, const float* S, int32_t* flag, hipStream_t st) {
+  if (u1 <= u0) return hipSuccess;
+  int lmax = 1;
+  for (int i = 0; i < D.n_seq; ++i) lmax = max(lmax, (int)D.L[i]);
+  const dim3 grid((unsigned)((lmax + 255) / 256), (unsigned)(u1 - u0));
+  if (D.dtype == 0)
+    hipLaunchKernelGGL(kvc_check_kernel<uint16_t>, grid, dim3(256), 0, st, D, u0,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, S, flag);
+  else
+    hipLaunchKernelGGL(kvc_check_kernel<float>, grid, dim3(256), 0, st, D, u0, (const float*)q,
+                       (const float*)k, (const float*)v, S, flag);
+  return hipGetLastError();
+}
+
+hipError_t kvc_launch_check_clear(int32_t* flag, hipStream_t st) {
+  hipLaunchKernelGGL(kvc_check_clear_kernel, dim3(1), dim3(1), 0, st, flag);
+  return hipGetLastError();
+}

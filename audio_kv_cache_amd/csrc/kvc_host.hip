@@ -2,6 +2,7 @@
 // carving and kernel launches.  No allocation, no synchronisation: every
 // entry point enqueues on the caller's stream and returns.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -185,6 +186,15 @@ static Carve carve(const KvcDesc& D, void* ws) {
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// KVC_CHECK_INPUTS=1 in the environment: kvc_compress and kvc_compress_layers
+// first check that every input element they read is finite (and the head
+// scores >= 0), wait for the result, and return KVC_ERR_INVALID_ARG without
+// compressing otherwise.  Read on every call.
+static bool check_inputs() {
+  const char* e = getenv("KVC_CHECK_INPUTS");
+  return e && e[0] == '1';
+}
+
 static kvc_status compress_range(const kvc_problem* prob, const kvc_params* params, int lb,
                                  int le, const void* q_window, const void* k, const void* v,
                                  const float* head_scores, void* k_out, void* v_out,
@@ -206,6 +216,21 @@ static kvc_status compress_range(const kvc_problem* prob, const kvc_params* para
   if (workspace_bytes < need) return KVC_ERR_WORKSPACE;
   const Carve c = carve(D, workspace);
   hipStream_t s = (hipStream_t)stream;
+  if (check_inputs()) {
+    // Optional checks: the flag lives in the score rows, which the scores
+    // overwrite afterwards; this path waits for the check's result.
+    int32_t* flag = (int32_t*)c.srows;
+    hipError_t e = kvc_launch_check_clear(flag, s);
+    for (int seq = 0; seq < D.n_seq && e == hipSuccess; ++seq) {
+      const int u0 = (seq * D.n_layers + lb) * D.n_heads, u1 = (seq * D.n_layers + le) * D.n_heads;
+      e = kvc_launch_check(D, u0, u1, q_window, k, v, head_scores, flag, s);
+    }
+    int32_t bad = 0;
+    if (e == hipSuccess) e = hipMemcpyAsync(&bad, flag, sizeof(bad), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e);
+    if (bad) return KVC_ERR_INVALID_ARG;
+  }
   // Budgets and offsets of every unit (they depend only on S, L and the
   // retention), then one launch per step and sequence over the units of
   // layers [lb, le) (more, smaller launches cost more in launch and queue

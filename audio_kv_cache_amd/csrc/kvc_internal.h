@@ -89,6 +89,12 @@ hipError_t kvc_launch_wnw_fixed_select(const KvcDesc& D, int seg, const float* s
                                        const int32_t* budgets, const int64_t* offsets,
                                        int32_t* idx_out, hipStream_t st);
 
+// Optional input checks (check.hip): units [u0, u1) of one call; a bad
+// element sets *flag (cleared first by kvc_launch_check_clear).
+hipError_t kvc_launch_check(const KvcDesc& D, int u0, int u1, const void* q, const void* k,
+                            const void* v, const float* S, int32_t* flag, hipStream_t st);
+hipError_t kvc_launch_check_clear(int32_t* flag, hipStream_t st);
+
 // Record a HIP error for kvc_last_hip_error() (calling thread).
 void kvc_note_hip_error(int e);
 

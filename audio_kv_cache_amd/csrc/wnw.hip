@@ -7,7 +7,8 @@
 //   wnw_logits_kernel      anchor logits q_g . k_j / sqrt(d) (log2 units) for
 //                          every anchor's G query heads, and per-wave
 //                          (max, sum exp) partials; one thread per key.
-//   wnw_lse_kernel         the partials folded into each head's LSE.
+//   wnw_lse_kernel         the partials folded into each head's LSE (one
+//                          workgroup per head).
 //   wnw_position_mass_kernel  per position: the anchors' attention mass
 //                          (sum over anchors of the mean over heads of
 //                          exp2(l - LSE)); one thread per position.
@@ -139,28 +140,27 @@ __global__ __launch_bounds__(WNW_TILE) void wnw_logits_kernel(WnwDesc W, const u
   }
 }
 
+// One workgroup per (sequence, anchor, query head) row.
 __global__ __launch_bounds__(256) void wnw_lse_kernel(WnwDesc W, WnwWork X) {
   __shared__ float2 sred[4];
-  const int sa = blockIdx.x, seq = sa / W.n_anchor;
+  const size_t row = blockIdx.x;
+  const int seq = (int)(row / ((size_t)W.n_anchor * W.gqa));
   const int nparts = (W.len[seq] + 63) / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int g = 0; g < W.gqa; ++g) {
-    const float2* p = X.parts + ((size_t)sa * W.gqa + g) * W.max_parts;
-    float m = -INFINITY, z = 0.f;
-    for (int i = threadIdx.x; i < nparts; i += 256) wnw_merge(m, z, p[i].x, p[i].y);
+  const float2* p = X.parts + row * W.max_parts;
+  float m = -INFINITY, z = 0.f;
+  for (int i = threadIdx.x; i < nparts; i += 256) wnw_merge(m, z, p[i].x, p[i].y);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float m2 = __shfl_xor(m, o), z2 = __shfl_xor(z, o);
-      wnw_merge(m, z, m2, z2);
-    }
-    if (lane == 0) sred[wave] = make_float2(m, z);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float mm = sred[0].x, zz = sred[0].y;
-      for (int w = 1; w < 4; ++w) wnw_merge(mm, zz, sred[w].x, sred[w].y);
-      X.lse2[(size_t)sa * W.gqa + g] = mm + __builtin_amdgcn_logf(zz);
-    }
-    __syncthreads();
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o), z2 = __shfl_xor(z, o);
+    wnw_merge(m, z, m2, z2);
+  }
+  if (lane == 0) sred[wave] = make_float2(m, z);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = sred[0].x, zz = sred[0].y;
+    for (int w = 1; w < 4; ++w) wnw_merge(mm, zz, sred[w].x, sred[w].y);
+    X.lse2[row] = mm + __builtin_amdgcn_logf(zz);
   }
 }
 
@@ -642,7 +642,8 @@ static hipError_t wnw_launch_scores(const WnwDesc& W, const void* q, const void*
   else
     hipLaunchKernelGGL(wnw_logits_kernel<64>, g1, dim3(WNW_TILE), 0, st, W, (const uint16_t*)q,
                        (const uint16_t*)k, X);
-  hipLaunchKernelGGL(wnw_lse_kernel, dim3((unsigned)(W.n_seq * W.n_anchor)), dim3(256), 0, st, W, X);
+  hipLaunchKernelGGL(wnw_lse_kernel, dim3((unsigned)(W.n_seq * W.n_anchor * W.gqa)), dim3(256), 0,
+                     st, W, X);
   hipLaunchKernelGGL(wnw_position_mass_kernel,
                      dim3((unsigned)((W.max_len + 255) / 256), (unsigned)W.n_seq), dim3(256), 0, st,
                      W, X);

@@ -24,6 +24,7 @@ timed on its own workload; --no-decode, --no-c3 and --no-wnw skip them.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -141,6 +142,7 @@ def bench_decode(args):
     """One decode step of decayed eviction (kvc_vz_step) over every cache of
     the decode workload, inputs resident in HBM; per-kernel event timing and
     a CPU-oracle sample."""
+    gc.collect()
     import torch
     from audio_kv_cache_amd import api, synth
     cfg = synth.DECODE_CONFIGS[args.decode_config]
@@ -259,6 +261,7 @@ def bench_c3(args):
     """C3 retrieval: the prefill tree build over every cache and the decode
     step (scores, budget fill, frontier update, gather), inputs resident in
     HBM; per-kernel event timing and a CPU-oracle sample."""
+    gc.collect()
     import torch
     from audio_kv_cache_amd import api, synth
     cfg = synth.C3_CONFIGS[args.c3_config]
@@ -422,6 +425,7 @@ def bench_wnw(args):
     tidal head from page-locked host memory), inputs resident (anchor keys
     in HBM, tidal copies in host memory); per-stage event timing, the bytes
     recalled per step, a cold step (everything recalled), CPU-oracle sample."""
+    gc.collect()
     import torch
     from audio_kv_cache_amd import api, synth
     cfg = synth.WNW_CONFIGS[args.wnw_config]
@@ -615,6 +619,10 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    # The collector stays off while launches are timed: a full collection
+    # pausing the host for tens of ms inside a timed loop leaves the GPU idle
+    # and shows up as kernel time.  Each leg collects once before it starts.
+    gc.disable()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by (sequence, layer, KV head) unit with no exchange; "

@@ -37,7 +37,13 @@
  *   - Inputs are read-only, outputs fully overwritten, workspace contents
  *     are undefined on return.  Calls on different streams with disjoint
  *     outputs and workspaces may run concurrently.  Stateless, thread-safe.
- *   - Non-finite inputs are undefined behaviour.
+ *   - Non-finite inputs are undefined behaviour, unless the environment
+ *     sets KVC_CHECK_INPUTS=1: then kvc_compress and kvc_compress_layers
+ *     first check every query, key and value element of the call's units
+ *     (finite) and every head score (finite, >= 0), wait on `stream` for
+ *     the result and return KVC_ERR_INVALID_ARG without compressing on a
+ *     violation (a checking mode: it reads all of K and V once more and
+ *     synchronises).
  */
 #ifndef KVC_H
 #define KVC_H
