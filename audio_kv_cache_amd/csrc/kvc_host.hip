@@ -75,6 +75,8 @@ static kvc_status make_desc(const kvc_problem* p, const kvc_params* prm, KvcDesc
 
   if (p->n_seq > KVC_MAX_SEQ) return KVC_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return KVC_ERR_UNSUPPORTED;
+  // the score kernels address a 64-row key chunk with 32-bit byte offsets
+  if (p->k_stride[2] >= (int64_t(1) << 24)) return KVC_ERR_UNSUPPORTED;
   const int64_t gw = (int64_t)p->gqa_group * p->n_window_q;
   if (gw % 32 != 0 || gw > KVC_MAX_GW) return KVC_ERR_UNSUPPORTED;
   if (prm->score_pool == KVC_SCORE_MAX && p->n_window_q % 32 != 0) return KVC_ERR_UNSUPPORTED;

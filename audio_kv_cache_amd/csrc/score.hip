@@ -467,20 +467,31 @@ struct QsWaves {
 // thread t takes pieces t, t + NT, ... (consecutive threads, consecutive
 // 16-byte pieces of a row).  Past the last piece a thread reloads it, so
 // every register is written on every path and the array is never demoted
-// to scratch memory.
+// to scratch memory.  The pieces' byte offsets within a chunk are computed
+// once per tile (32-bit; the host bounds the token stride), and each chunk
+// only moves the uniform base pointer, so the loads need no 64-bit vector
+// address arithmetic.
 typedef unsigned int qs_u32x4 __attribute__((ext_vector_type(4)));
 
 template <int D, int NT>
-__device__ inline void qs_kload(qs_u32x4 (&r)[(QsCfg<D>::PIECES + NT - 1) / NT], const uint16_t* ku,
-                                int64_t kstride, int key0) {
-  constexpr int PPR = QsCfg<D>::ROWB / 16, PER = (QsCfg<D>::PIECES + NT - 1) / NT;
+struct QsLoader {
+  static constexpr int PPR = QsCfg<D>::ROWB / 16;
+  static constexpr int PER = (QsCfg<D>::PIECES + NT - 1) / NT;
+  uint32_t off[PER];
+  __device__ explicit QsLoader(int64_t kstride) {
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int p = min((int)threadIdx.x + j * NT, QsCfg<D>::PIECES - 1);
-    const int row = p / PPR, pc = p - row * PPR;
-    r[j] = reinterpret_cast<const qs_u32x4*>(ku + (int64_t)(key0 + row) * kstride)[pc];
+    for (int j = 0; j < PER; ++j) {
+      const int p = min((int)threadIdx.x + j * NT, QsCfg<D>::PIECES - 1);
+      const int row = p / PPR, pc = p - row * PPR;
+      off[j] = (uint32_t)(row * kstride * 2 + pc * 16);
+    }
   }
-}
+  __device__ void load(qs_u32x4 (&r)[PER], const uint16_t* ku, int64_t kstride, int key0) const {
+    const char* base = reinterpret_cast<const char*>(ku + (int64_t)key0 * kstride);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) r[j] = *reinterpret_cast<const qs_u32x4*>(base + off[j]);
+  }
+};
 
 template <int D, int NT>
 __device__ inline void qs_kstore(const qs_u32x4 (&r)[(QsCfg<D>::PIECES + NT - 1) / NT], char* buf) {
@@ -609,14 +620,15 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
   // The loop body is branch-free so that the scheduling groups hold: the
   // last chunk reloads and restages itself into the idle buffer.
   const int nch = ti.keys / C::CHUNK;
+  const QsLoader<D, NT> kl(Dsc.ks[2]);
   qs_u32x4 kr[(C::PIECES + NT - 1) / NT];
-  qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0);
+  kl.load(kr, ku, Dsc.ks[2], ti.key0);
   qs_kstore<D, NT>(kr, sK[0]);
   __syncthreads();
   floatx16 X, Y;          // X: query block 0, Y: query block 1 of the current key block
   bf16x8 kf0[NK], kf1[NK];
   float s0 = 0.f;         // pooled sum of the current key block (block 0 part)
-  qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0 + min(1, nch - 1) * C::CHUNK);
+  kl.load(kr, ku, Dsc.ks[2], ti.key0 + min(1, nch - 1) * C::CHUNK);
   qs_kfrag<D>(kf0, sK[0], 0, lane);
   mma(X, qf0, kf0);
   for (int ch = 0;;) {
@@ -637,7 +649,7 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
     qs_kstore<D, NT>(kr, sK[(ch + 1) & 1]);
     __syncthreads();
     if (++ch == nch) break;
-    qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0 + min(ch + 1, nch - 1) * C::CHUNK);
+    kl.load(kr, ku, Dsc.ks[2], ti.key0 + min(ch + 1, nch - 1) * C::CHUNK);
     // [A] keys 0-31 of the new chunk x block 0, beside the last block of
     // the previous chunk
     qs_kfrag<D>(kf0, sK[ch & 1], 0, lane);
@@ -731,6 +743,7 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
     return e[0];
   };
 
+  const QsLoader<D, NT> kl(Dsc.ks[2]);
   const int nch = ti.keys / C::CHUNK;
   float m0, z0, m1, z1;
   // One pass over the tile through the LDS pipeline.  EXACT: online maximum
@@ -750,12 +763,12 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
       }
     };
     qs_u32x4 kr[(C::PIECES + NT - 1) / NT];
-    qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0);
+    kl.load(kr, ku, Dsc.ks[2], ti.key0);
     qs_kstore<D, NT>(kr, sK[0]);
     __syncthreads();
     floatx16 X, Y;
     bf16x8 kf0[NK], kf1[NK];
-    qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0 + min(1, nch - 1) * C::CHUNK);
+    kl.load(kr, ku, Dsc.ks[2], ti.key0 + min(1, nch - 1) * C::CHUNK);
     qs_kfrag<D>(kf0, sK[0], 0, lane);
     if constexpr (!EXACT) {
       // references from the tile's first 32 keys
@@ -783,7 +796,7 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
       qs_kstore<D, NT>(kr, sK[(ch + 1) & 1]);
       __syncthreads();
       if (++ch == nch) break;
-      qs_kload<D, NT>(kr, ku, Dsc.ks[2], ti.key0 + min(ch + 1, nch - 1) * C::CHUNK);
+      kl.load(kr, ku, Dsc.ks[2], ti.key0 + min(ch + 1, nch - 1) * C::CHUNK);
       qs_kfrag<D>(kf0, sK[ch & 1], 0, lane);
       const floatx16 Yp = Y;
       mma(X, kf0, qf0);

@@ -398,22 +398,28 @@ __global__ void wnw_fill_kernel(int32_t* p, int64_t n, int32_t v) {
 }
 
 // ---------------------------------------------------------------------------
-// Fixed heads: segment-wise selection at prefill (one workgroup per unit,
-// one wave per segment of at most 64 positions)
+// Fixed heads: segment-wise selection at prefill.  Grid (unit, group of
+// WNW_SEGS segments); one wave per segment of at most 64 positions.  Each
+// segment's quota and its first output slot are closed forms, so the
+// segments need no exchange.
 // ---------------------------------------------------------------------------
+#define WNW_SEGS 16
+
 __global__ __launch_bounds__(256) void wnw_fixed_select_kernel(KvcDesc D, int seg,
                                                                const float* __restrict__ s_hat,
                                                                const int32_t* __restrict__ budgets,
                                                                const int64_t* __restrict__ offsets,
                                                                int32_t* __restrict__ idx_out) {
+  __shared__ __attribute__((aligned(16))) uint32_t skey[4][64];
   const int u = blockIdx.x;
   const int seq = u / D.upseq, within = u - seq * D.upseq;
   const int L = D.L[seq], w = D.window, ncand = L - w;
   // (budgets hold w <= b <= L, as for kvc_select; clamped all the same)
   const int k = min(max(budgets[u] - w, 0), max(ncand, 0));
   int32_t* out = idx_out + offsets[u];
-  for (int i = threadIdx.x; i < w; i += 256) out[max(k, 0) + i] = ncand + i;
-  if (k <= 0 || ncand <= 0) return;
+  if (blockIdx.y == 0)
+    for (int i = threadIdx.x; i < w; i += 256) out[k + i] = ncand + i;
+  if (k <= 0) return;
   const float* row = s_hat + D.srow_base[seq] + (int64_t)within * L;
   // Quotas: every full segment has the same floor and remainder, the short
   // last one (if any) its own; the R leftovers go by remainder, then index.
@@ -427,17 +433,24 @@ __global__ __launch_bounds__(256) void wnw_fixed_select_kernel(KvcDesc D, int se
   const int64_t qlast = ql + ((last_first && R >= 1) || (!last_first && R > nfull) ? 1 : 0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t J = nfull + (last ? 1 : 0);
-  for (int64_t j = wave; j < J; j += 4) {
+  const int64_t j1 = std::min<int64_t>(J, (int64_t)(blockIdx.y + 1) * WNW_SEGS);
+  for (int64_t j = (int64_t)blockIdx.y * WNW_SEGS + wave; j < j1; j += 4) {
     const int lo = (int)(j * seg), len = (int)std::min<int64_t>(seg, ncand - j * seg);
     const int64_t quota = (j < nfull) ? qf + (j < rfull ? 1 : 0) : qlast;
     const int64_t before = (j < nfull) ? j * qf + std::min<int64_t>(j, rfull) : nfull * qf + rfull;
     const bool valid = lane < len;
     const uint32_t key = valid ? wnw_order_key(row[lo + lane]) : 0u;
+    skey[wave][lane] = key;   // the wave's own row: no barrier needed
+    __builtin_amdgcn_wave_barrier();
     int rank = 0;
-    for (int o = 0; o < len; ++o) {
-      const uint32_t ko = __shfl(key, o);
-      rank += (ko > key) || (ko == key && o < lane);
+    for (int o = 0; o < len; o += 4) {
+      const uint4 kq = *reinterpret_cast<const uint4*>(&skey[wave][o]);   // same for every lane
+      const uint32_t ko[4] = {kq.x, kq.y, kq.z, kq.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        rank += (o + e < len) && ((ko[e] > key) || (ko[e] == key && o + e < lane));
     }
+    __builtin_amdgcn_wave_barrier();
     const bool take = valid && rank < quota;
     const unsigned long long mask = __ballot(take);
     const int pos = __popcll(mask & ((1ull << lane) - 1ull));
@@ -448,8 +461,11 @@ __global__ __launch_bounds__(256) void wnw_fixed_select_kernel(KvcDesc D, int se
 hipError_t kvc_launch_wnw_fixed_select(const KvcDesc& D, int seg, const float* s_hat,
                                        const int32_t* budgets, const int64_t* offsets,
                                        int32_t* idx_out, hipStream_t st) {
-  hipLaunchKernelGGL(wnw_fixed_select_kernel, dim3(D.n_units), dim3(256), 0, st, D, seg, s_hat,
-                     budgets, offsets, idx_out);
+  int jmax = 1;
+  for (int i = 0; i < D.n_seq; ++i) jmax = max(jmax, (D.L[i] - D.window + seg - 1) / seg);
+  const dim3 grid((unsigned)D.n_units, (unsigned)((jmax + WNW_SEGS - 1) / WNW_SEGS));
+  hipLaunchKernelGGL(wnw_fixed_select_kernel, grid, dim3(256), 0, st, D, seg, s_hat, budgets,
+                     offsets, idx_out);
   return hipGetLastError();
 }
 

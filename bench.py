@@ -744,6 +744,9 @@ def main():
             "smooth": lambda: api.kvc_smooth(spec, prm, s_rows, sh_rows, kst, stream, ws),
             "select": lambda: api.kvc_select(spec, prm, sh_rows, out["budgets"], out["offsets"],
                                              out["idx"], stream),
+            # the fixed heads' segment-wise variant (WnW), 50-position segments
+            "select_segments": lambda: api.kvc_wnw_fixed_select(
+                spec, prm, 50, sh_rows, out["budgets"], out["offsets"], out["idx"], stream),
             "gather": lambda: api.kvc_gather(spec, prm, k, v, out["idx"], out["offsets"],
                                              out["k_out"], out["v_out"], stream),
         }

@@ -101,7 +101,7 @@ typedef enum { KVC_POOL_SEQUENCE = 0, KVC_POOL_LAYER = 1 } kvc_pool;
  * transform of step 2 through Bluestein's algorithm (the chirp-z form of
  * the DFT of length L, or of the L/2 packed values for even L, as a
  * convolution done with power-of-two FFTs of at most 32768 points);
- * n_layers * n_kv_heads <= 4096. */
+ * n_layers * n_kv_heads <= 4096; k_stride[2] < 2^24. */
 typedef struct {
   int32_t n_seq, n_layers, n_kv_heads, gqa_group, head_dim, n_window_q;
   kvc_dtype dtype;            /* element type of q, k, v, k_out, v_out     */
