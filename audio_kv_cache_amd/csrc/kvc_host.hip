@@ -240,11 +240,18 @@ static kvc_status compress_range(const kvc_problem* prob, const kvc_params* para
   hipError_t e = kvc_launch_budget(D, head_scores, budgets, seg_offsets, s);
   if (e != hipSuccess) return hip_status(e);
   const bool whole = lb == 0 && le == D.n_layers;
-  for (int seq = 0; seq < D.n_seq; ++seq) {
-    const int u0 = (seq * D.n_layers + lb) * D.n_heads, u1 = (seq * D.n_layers + le) * D.n_heads;
-    if ((e = kvc_launch_scores(D, u0, u1, q_window, k, c.srows, c.partials, c.lse2, s)) !=
+  if (whole) {
+    // one launch per pass over every sequence's tiles
+    if ((e = kvc_launch_scores(D, 0, D.n_units, q_window, k, c.srows, c.partials, c.lse2, s)) !=
         hipSuccess)
       return hip_status(e);
+  } else {
+    for (int seq = 0; seq < D.n_seq; ++seq) {
+      const int u0 = (seq * D.n_layers + lb) * D.n_heads, u1 = (seq * D.n_layers + le) * D.n_heads;
+      if ((e = kvc_launch_scores(D, u0, u1, q_window, k, c.srows, c.partials, c.lse2, s)) !=
+          hipSuccess)
+        return hip_status(e);
+    }
   }
   for (int seq = 0; seq < D.n_seq; ++seq) {
     const int u0 = (seq * D.n_layers + lb) * D.n_heads, u1 = (seq * D.n_layers + le) * D.n_heads;
@@ -300,12 +307,8 @@ static kvc_status scores_common(const kvc_problem* prob, const kvc_params* param
     return KVC_ERR_INVALID_ARG;
   if (workspace_bytes < kvc_scores_workspace(D)) return KVC_ERR_WORKSPACE;
   const Carve c = carve(D, workspace);
-  for (int seq = 0; seq < D.n_seq; ++seq) {
-    const hipError_t e = kvc_launch_scores(D, seq * D.upseq, (seq + 1) * D.upseq, q_window, k,
-                                           s_out, c.partials, c.lse2, (hipStream_t)stream, which);
-    if (e != hipSuccess) return hip_status(e);
-  }
-  return KVC_OK;
+  return hip_status(kvc_launch_scores(D, 0, D.n_units, q_window, k, s_out, c.partials, c.lse2,
+                                      (hipStream_t)stream, which));
 }
 
 extern "C" kvc_status kvc_scores(const kvc_problem* prob, const kvc_params* params,

@@ -65,8 +65,9 @@ __host__ __device__ inline int kvc_tiles_per_unit(int L) {
 // Kernel launchers (defined next to each kernel).
 hipError_t kvc_launch_budget(const KvcDesc& D, const float* S, int32_t* budgets,
                              int64_t* offsets, hipStream_t st);
-// Range launches: units [u0, u1) (natural (seq, layer, head) order) must lie
-// within one sequence for the score and smoothing/selection launches.
+// Range launches: units [u0, u1) (natural (seq, layer, head) order); the
+// score launches take any range, the smoothing/selection launches a range
+// within one sequence.
 // which: 1 = statistics pass (+ LSE fold), 2 = pooling pass, 3 = both.
 hipError_t kvc_launch_scores(const KvcDesc& D, int u0, int u1, const void* q, const void* k,
                              float* s, float2* partials, float* lse2, hipStream_t st,

@@ -855,6 +855,7 @@ __global__ __launch_bounds__(KVC_MAX_GW) void kvc_score_tail_kernel(KvcDesc Dsc,
   const int seq = u / Dsc.upseq, within = u - seq * Dsc.upseq;
   const int l = within / Dsc.n_heads, h = within - l * Dsc.n_heads;
   const int L = Dsc.L[seq], L64 = L & ~63, nt = L - L64;
+  if (nt == 0) return;   // (a launch over several sequences: this one has no tail tiles)
   const int per = (nt + KVC_TAIL_SPLITS - 1) / KVC_TAIL_SPLITS;
   const int j0 = L64 + split * per;
   const int nk = max(0, min(per, L - j0));
@@ -928,10 +929,20 @@ __global__ __launch_bounds__(KVC_MAX_GW) void kvc_score_tail_kernel(KvcDesc Dsc,
   }
 }
 
+// First score tile of unit u (u = n_units: the total).  Units [u0, u1) may
+// span sequences: the tiles of consecutive units are consecutive.
+static int tile_of_unit(const KvcDesc& D, int u) {
+  const int seq = u / D.upseq;
+  if (seq >= D.n_seq) return D.tile_base[D.n_seq];
+  return D.tile_base[seq] + (u - seq * D.upseq) * kvc_tiles_per_unit(D.L[seq]);
+}
+
 template <class E, int Dm>
 static void launch_tail(const KvcDesc& D, int u0, int u1, int mode, const void* q, const void* k,
                         const float* lse2, float2* partials, float* s, hipStream_t st) {
-  if ((D.L[u0 / D.upseq] & 63) == 0) return;
+  bool any = false;  // any unit of the range with tail keys
+  for (int seq = u0 / D.upseq; seq <= (u1 - 1) / D.upseq; ++seq) any |= (D.L[seq] & 63) != 0;
+  if (!any) return;
   hipLaunchKernelGGL((kvc_score_tail_kernel<E, Dm>), dim3((u1 - u0) * KVC_TAIL_SPLITS),
                      dim3(KVC_MAX_GW), 0, st, D, u0, mode, (const E*)q, (const E*)k, lse2,
                      partials, s);
@@ -948,10 +959,8 @@ template <class T, int Dm, int NBC>
 static void launch_pair(const KvcDesc& D, int u0, int u1, const void* q, const void* k, float* s,
                         float2* partials, float* lse2, hipStream_t st, int which) {
   using elem_t = typename T::elem_t;
-  const int seq = u0 / D.upseq;
-  const int tpu = kvc_tiles_per_unit(D.L[seq]);
-  const int t0 = D.tile_base[seq] + (u0 - seq * D.upseq) * tpu;
-  const int nt = (u1 - u0) * tpu;
+  const int t0 = tile_of_unit(D, u0);
+  const int nt = tile_of_unit(D, u1) - t0;
   if (which & 1) {
     hipLaunchKernelGGL((kvc_score_stats_kernel<T, Dm, NBC>), dim3(nt), dim3(SCORE_THREADS), 0, st,
                        D, t0, (const elem_t*)q, (const elem_t*)k, partials);
@@ -970,10 +979,8 @@ static void launch_pair(const KvcDesc& D, int u0, int u1, const void* q, const v
 template <int Dm, int NBC>
 static void launch_qs(const KvcDesc& D, int u0, int u1, const void* q, const void* k, float* s,
                       float2* partials, float* lse2, hipStream_t st, int which) {
-  const int seq = u0 / D.upseq;
-  const int tpu = kvc_tiles_per_unit(D.L[seq]);
-  const int t0 = D.tile_base[seq] + (u0 - seq * D.upseq) * tpu;
-  const int nt = (u1 - u0) * tpu;
+  const int t0 = tile_of_unit(D, u0);
+  const int nt = tile_of_unit(D, u1) - t0;
   constexpr int NT = QsWaves<NBC>::NT;
   if (which & 1) {
     hipLaunchKernelGGL((kvc_score_stats_qs_kernel<Dm, NBC>), dim3(nt), dim3(NT), 0, st, D, t0,
