@@ -147,9 +147,34 @@ static size_t score_rows_bytes(const KvcDesc& D) {
 
 // Scratch of the smoothing launches for lengths that are not powers of two
 // (one launch per sequence at a time, so the largest one).
+// Sequences grouped by length (in order of first appearance), units
+// [lo, hi) of each: one smoothing/selection launch per group.
+template <class F>
+static hipError_t for_each_length_group(const KvcDesc& D, int lo, int hi, F f) {
+  bool done[KVC_MAX_SEQ] = {};
+  for (int i = 0; i < D.n_seq; ++i) {
+    if (done[i]) continue;
+    KvcSeqGroup g;
+    g.n = 0;
+    g.lo = lo;
+    g.hi = hi;
+    for (int j = i; j < D.n_seq; ++j)
+      if (!done[j] && D.L[j] == D.L[i]) {
+        g.seq[g.n++] = (uint8_t)j;
+        done[j] = true;
+      }
+    const hipError_t e = f(g);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 static size_t sss_scratch_bytes(const KvcDesc& D) {
   size_t m = 0;
-  for (int i = 0; i < D.n_seq; ++i) m = std::max(m, kvc_sss_scratch_bytes(D.L[i], D.upseq));
+  for_each_length_group(D, 0, D.upseq, [&](const KvcSeqGroup& g) {
+    m = std::max(m, kvc_sss_scratch_bytes(D.L[g.seq[0]], g.n * D.upseq));
+    return hipSuccess;
+  });
   return (m + 255) & ~size_t(255);
 }
 
@@ -253,12 +278,11 @@ static kvc_status compress_range(const kvc_problem* prob, const kvc_params* para
         return hip_status(e);
     }
   }
-  for (int seq = 0; seq < D.n_seq; ++seq) {
-    const int u0 = (seq * D.n_layers + lb) * D.n_heads, u1 = (seq * D.n_layers + le) * D.n_heads;
-    if ((e = kvc_launch_sss_select(D, u0, u1, 1 | 2, c.srows, nullptr, nullptr, budgets,
-                                   seg_offsets, idx_out, c.sss, s)) != hipSuccess)
-      return hip_status(e);
-  }
+  e = for_each_length_group(D, lb * D.n_heads, le * D.n_heads, [&](const KvcSeqGroup& g) {
+    return kvc_launch_sss_select(D, g, 1 | 2, c.srows, nullptr, nullptr, budgets, seg_offsets,
+                                 idx_out, c.sss, s);
+  });
+  if (e != hipSuccess) return hip_status(e);
   if (whole) {
     e = kvc_launch_gather(D, 0, D.n_units, k, v, idx_out, seg_offsets, k_out, v_out,
                           D.row_base[D.n_seq], s);
@@ -340,14 +364,10 @@ extern "C" kvc_status kvc_smooth(const kvc_problem* prob, const kvc_params* para
   const size_t need = sss_scratch_bytes(D);
   if (need && (!workspace || ((uintptr_t)workspace & 255u))) return KVC_ERR_INVALID_ARG;
   if (workspace_bytes < need) return KVC_ERR_WORKSPACE;
-  for (int seq = 0; seq < D.n_seq; ++seq) {
-    const hipError_t e =
-        kvc_launch_sss_select(D, seq * D.upseq, (seq + 1) * D.upseq, 1 | 4, s_in, s_hat, kstar,
-                              nullptr, nullptr, nullptr, need ? workspace : nullptr,
-                              (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e);
-  }
-  return KVC_OK;
+  return hip_status(for_each_length_group(D, 0, D.upseq, [&](const KvcSeqGroup& g) {
+    return kvc_launch_sss_select(D, g, 1 | 4, s_in, s_hat, kstar, nullptr, nullptr, nullptr,
+                                 need ? workspace : nullptr, (hipStream_t)stream);
+  }));
 }
 
 extern "C" kvc_status kvc_budget(const kvc_problem* prob, const kvc_params* params,
@@ -368,13 +388,10 @@ extern "C" kvc_status kvc_select(const kvc_problem* prob, const kvc_params* para
   if (st != KVC_OK) return st;
   if (!s_hat || !budgets || !seg_offsets || !idx_out) return KVC_ERR_INVALID_ARG;
   if ((uintptr_t)s_hat & 7u) return KVC_ERR_INVALID_ARG;
-  for (int seq = 0; seq < D.n_seq; ++seq) {
-    const hipError_t e =
-        kvc_launch_sss_select(D, seq * D.upseq, (seq + 1) * D.upseq, 2, s_hat, nullptr, nullptr,
-                              budgets, seg_offsets, idx_out, nullptr, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e);
-  }
-  return KVC_OK;
+  return hip_status(for_each_length_group(D, 0, D.upseq, [&](const KvcSeqGroup& g) {
+    return kvc_launch_sss_select(D, g, 2, s_hat, nullptr, nullptr, budgets, seg_offsets, idx_out,
+                                 nullptr, (hipStream_t)stream);
+  }));
 }
 
 extern "C" kvc_status kvc_wnw_fixed_select(const kvc_problem* prob, const kvc_params* params,

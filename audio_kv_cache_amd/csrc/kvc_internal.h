@@ -72,14 +72,26 @@ hipError_t kvc_launch_budget(const KvcDesc& D, const float* S, int32_t* budgets,
 hipError_t kvc_launch_scores(const KvcDesc& D, int u0, int u1, const void* q, const void* k,
                              float* s, float2* partials, float* lse2, hipStream_t st,
                              int which = 3);
+// Smoothing/selection launch over several sequences of one length: units
+// seq[k] * upseq + lo .. seq[k] * upseq + hi - 1 for k < n (workgroup
+// b -> k = b / (hi - lo), unit lo + b % (hi - lo) of sequence seq[k]).
+struct KvcSeqGroup {
+  int32_t n, lo, hi;
+  uint8_t seq[KVC_MAX_SEQ];
+};
+__host__ __device__ inline int kvc_group_unit(const KvcSeqGroup& g, int upseq, int b) {
+  const int per = g.hi - g.lo;
+  const int k = b / per;
+  return (int)g.seq[k] * upseq + g.lo + (b - k * per);
+}
 // mode bit 0: smooth (else read s_hat from s_in); bit 1: select;
 // bit 2: export s_hat and kstar.
 // scratch: kvc_sss_scratch_bytes(L, u1 - u0) bytes, needed only when L is not
 // a power of two (lengths handled through Bluestein's algorithm).
-hipError_t kvc_launch_sss_select(const KvcDesc& D, int u0, int u1, int mode, const float* s_in,
-                                 float* s_hat_out, int32_t* kstar_out, const int32_t* budgets,
-                                 const int64_t* offsets, int32_t* idx_out, void* scratch,
-                                 hipStream_t st);
+hipError_t kvc_launch_sss_select(const KvcDesc& D, const KvcSeqGroup& g, int mode,
+                                 const float* s_in, float* s_hat_out, int32_t* kstar_out,
+                                 const int32_t* budgets, const int64_t* offsets, int32_t* idx_out,
+                                 void* scratch, hipStream_t st);
 size_t kvc_sss_scratch_bytes(int L, int units);
 hipError_t kvc_launch_gather(const KvcDesc& D, int u0, int u1, const void* k, const void* v,
                              const int32_t* idx, const int64_t* offsets, void* k_out, void* v_out,

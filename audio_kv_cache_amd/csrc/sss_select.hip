@@ -598,7 +598,7 @@ __host__ __device__ constexpr int kvc_sss_v(int N) {
 
 template <int LOG2N>
 __global__ __launch_bounds__(SSS_T) void kvc_sss_select_kernel(
-    KvcDesc D, int mode, int unit0, const float* __restrict__ s_in, float* __restrict__ s_hat_out,
+    KvcDesc D, int mode, KvcSeqGroup G, const float* __restrict__ s_in, float* __restrict__ s_hat_out,
     int32_t* __restrict__ kstar_out, const int32_t* __restrict__ budgets,
     const int64_t* __restrict__ offsets, int32_t* __restrict__ idx_out) {
   constexpr int N = 1 << LOG2N;
@@ -607,8 +607,8 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_select_kernel(
   constexpr int T = N / V;
   __shared__ __attribute__((aligned(16))) float lds[Xbuf<N>::kFloats];
   __shared__ SssShared sh;
-  // This launch covers units unit0 .. unit0 + gridDim.x - 1 of one sequence.
-  const int u = unit0 + (int)blockIdx.x;
+  // This launch covers the group's units, all of one length.
+  const int u = kvc_group_unit(G, D.upseq, (int)blockIdx.x);
   const int seq = u / D.upseq;
   const int within = u - seq * D.upseq;
   const int64_t row = D.srow_base[seq] + (int64_t)within * L;
@@ -753,7 +753,7 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_chirp_kernel(int Np, float2* __
 
 template <int LOGM>
 __global__ __launch_bounds__(SSS_T) void kvc_sss_general_kernel(
-    KvcDesc D, int mode, int unit0, const float* __restrict__ s_in, float* __restrict__ s_hat_out,
+    KvcDesc D, int mode, KvcSeqGroup G, const float* __restrict__ s_in, float* __restrict__ s_hat_out,
     int32_t* __restrict__ kstar_out, const int32_t* __restrict__ budgets,
     const int64_t* __restrict__ offsets, int32_t* __restrict__ idx_out, float2* __restrict__ rows,
     const float2* __restrict__ bhat, const float2* __restrict__ cw) {
@@ -762,7 +762,7 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_general_kernel(
   constexpr int T = M / V;
   __shared__ __attribute__((aligned(16))) float lds[Xbuf<M>::kFloats];
   __shared__ SssShared sh;
-  const int u = unit0 + (int)blockIdx.x;
+  const int u = kvc_group_unit(G, D.upseq, (int)blockIdx.x);
   const int seq = u / D.upseq;
   const int within = u - seq * D.upseq;
   const int L = D.L[seq];
@@ -779,7 +779,7 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_general_kernel(
   float kr[VS], ki[VS];
   if (mode & 1) {
     float re[V], im[V];
-    float2* X = rows + (size_t)(u - unit0) * (2 * Np + 2);
+    float2* X = rows + (size_t)blockIdx.x * (2 * Np + 2);
     float2* Y = X + Np;  // L/2 + 1 <= Np + 1 bins
     // Spectrum of the row.
     auto in_row = [&](int n) {
@@ -915,12 +915,13 @@ size_t kvc_sss_scratch_bytes(int L, int units) {
 }
 
 // Units [u0, u1) must lie in one sequence.
-hipError_t kvc_launch_sss_select(const KvcDesc& D, int u0, int u1, int mode, const float* s_in,
-                                 float* s_hat_out, int32_t* kstar_out, const int32_t* budgets,
-                                 const int64_t* offsets, int32_t* idx_out, void* scratch,
-                                 hipStream_t st) {
-  if (u1 <= u0) return hipSuccess;
-  const int L = D.L[u0 / D.upseq];
+hipError_t kvc_launch_sss_select(const KvcDesc& D, const KvcSeqGroup& g, int mode,
+                                 const float* s_in, float* s_hat_out, int32_t* kstar_out,
+                                 const int32_t* budgets, const int64_t* offsets, int32_t* idx_out,
+                                 void* scratch, hipStream_t st) {
+  const int nwg = g.n * (g.hi - g.lo);
+  if (nwg <= 0) return hipSuccess;
+  const int L = D.L[g.seq[0]];
   if ((L & (L - 1)) != 0) {
     if (!scratch && (mode & 1)) return hipErrorInvalidValue;
     const int Np = (L & 1) ? L : L / 2;
@@ -931,8 +932,8 @@ hipError_t kvc_launch_sss_select(const KvcDesc& D, int u0, int u1, int mode, con
     float2* cw = scratch ? (float2*)(base + b.chirp_off) : nullptr;
     float2* rows = scratch ? (float2*)(base + b.rows_off) : nullptr;
     void (*chirp)(int, float2*, float2*) = nullptr;
-    void (*kern)(KvcDesc, int, int, const float*, float*, int32_t*, const int32_t*, const int64_t*,
-                 int32_t*, float2*, const float2*, const float2*) = nullptr;
+    void (*kern)(KvcDesc, int, KvcSeqGroup, const float*, float*, int32_t*, const int32_t*,
+                 const int64_t*, int32_t*, float2*, const float2*, const float2*) = nullptr;
     switch (logm) {
 #define KVC_GEN(LM) case LM: chirp = kvc_sss_chirp_kernel<LM>; kern = kvc_sss_general_kernel<LM>; break;
       KVC_GEN(7) KVC_GEN(8) KVC_GEN(9) KVC_GEN(10) KVC_GEN(11) KVC_GEN(12) KVC_GEN(13)
@@ -941,13 +942,13 @@ hipError_t kvc_launch_sss_select(const KvcDesc& D, int u0, int u1, int mode, con
       default: return hipErrorInvalidValue;
     }
     if (mode & 1) hipLaunchKernelGGL(chirp, dim3(1), dim3(SSS_T), 0, st, Np, bhat, cw);
-    hipLaunchKernelGGL(kern, dim3(u1 - u0), dim3(SSS_T), 0, st, D, mode, u0, s_in, s_hat_out,
+    hipLaunchKernelGGL(kern, dim3(nwg), dim3(SSS_T), 0, st, D, mode, g, s_in, s_hat_out,
                        kstar_out, budgets, offsets, idx_out, rows, (const float2*)bhat,
                        (const float2*)cw);
     return hipGetLastError();
   }
-  void (*kern)(KvcDesc, int, int, const float*, float*, int32_t*, const int32_t*, const int64_t*,
-               int32_t*) = nullptr;
+  void (*kern)(KvcDesc, int, KvcSeqGroup, const float*, float*, int32_t*, const int32_t*,
+               const int64_t*, int32_t*) = nullptr;
   switch (L) {
     case 64: kern = kvc_sss_select_kernel<5>; break;
     case 128: kern = kvc_sss_select_kernel<6>; break;
@@ -962,7 +963,7 @@ hipError_t kvc_launch_sss_select(const KvcDesc& D, int u0, int u1, int mode, con
     case 65536: kern = kvc_sss_select_kernel<15>; break;
     default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(kern, dim3(u1 - u0), dim3(SSS_T), 0, st, D, mode, u0, s_in, s_hat_out,
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(SSS_T), 0, st, D, mode, g, s_in, s_hat_out,
                      kstar_out, budgets, offsets, idx_out);
   return hipGetLastError();
 }
