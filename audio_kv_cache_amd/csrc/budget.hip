@@ -78,12 +78,15 @@ __global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
       int nA = 0;
       for (int u0 = 0; u0 < n; u0 += 16) {
         // 16 independent LDS loads first, then the adds in u order.
+        // (loads at a clamped index, then a select: no branch per element,
+        // so the 32 LDS loads are all in flight before the first add)
         double x[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int u = u0 + j;
-          const bool a = u < n && active[u] != 0;
-          x[j] = a ? (double)sS[u] : 0.0;
+          const int u = min(u0 + j, n - 1);
+          const float sv = sS[u];
+          const bool a = (u0 + j < n) & (active[u] != 0);
+          x[j] = a ? (double)sv : 0.0;
           nA += a;
         }
 #pragma unroll
