@@ -5,15 +5,19 @@
 //
 // One decode step, all sequences at once:
 //   wnw_logits_kernel      anchor logits q_g . k_j / sqrt(d) (log2 units) for
-//                          every anchor's G query heads, and per-wave
-//                          (max, sum exp) partials; one thread per key.
+//                          every anchor's G query heads on the matrix cores
+//                          (16x16x32 bf16 MFMA: the query heads as rows, 16
+//                          keys as columns), and one (max, sum exp)
+//                          partial per workgroup of 256 keys and query head.
 //   wnw_lse_kernel         the partials folded into each head's LSE (one
 //                          workgroup per head).
-//   wnw_position_mass_kernel  per position: the anchors' attention mass
+//   wnw_mass_kernel        per run of blocks: the positions' attention mass
 //                          (sum over anchors of the mean over heads of
-//                          exp2(l - LSE)); one thread per position.
-//   wnw_block_mass_kernel  per block: its positions' masses summed in order.
-//   wnw_sigma_kernel       chunk scores: the sums of m consecutive blocks.
+//                          exp2(l - LSE), i.e. the sum over all anchor heads
+//                          divided by G) staged in LDS, the blocks' masses
+//                          summed in position order, and the chunk scores
+//                          (sums of m consecutive blocks; m - 1 blocks past
+//                          the run are recomputed by the workgroup).
 //   wnw_update_kernel      one 1024-thread workgroup per sequence: top-K by
 //                          packed (score, index) maxima, idle counts,
 //                          residency, slot release and assignment with
@@ -51,7 +55,7 @@ struct WnwDesc {
   int32_t S, m, K, H, slot_cap, block_cap, chunk_cap;
   int32_t n_anchor, n_tidal, max_len, max_parts;
   int32_t len[WNW_MAX_SEQ];
-  int16_t anchor_unit[WNW_MAX_ANCHOR];     // unit within a sequence: l * n_heads + h
+  int32_t anchor_unit[WNW_MAX_ANCHOR];     // unit within a sequence: l * n_heads + h
   uint32_t tidal_mask[WNW_MAX_UNITS / 32];
   int64_t ks[2], hs[2], ss[2];
 };
@@ -63,10 +67,8 @@ struct WnwState {
 
 struct WnwWork {
   float* logits;   // [n_seq * n_anchor][G][max_len]
-  float2* parts;   // [n_seq * n_anchor][G][max_parts]
+  float2* parts;   // [n_seq * n_anchor][G][max_parts], one per 256-key tile
   float* lse2;     // [n_seq * n_anchor][G]
-  float* pmass;    // [n_seq][max_len]
-  float* beta;     // [n_seq][block_cap]
   float* sigma;    // [n_seq][chunk_cap]
 };
 
@@ -84,59 +86,113 @@ __device__ __forceinline__ void wnw_merge(float& m, float& z, float m2, float z2
 // ---------------------------------------------------------------------------
 // Steps 1-2: anchor attention, block masses, chunk scores
 // ---------------------------------------------------------------------------
+typedef __bf16 wnw_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float wnw_f4 __attribute__((ext_vector_type(4)));
+
+// One workgroup per (sequence, anchor) and 256 keys; wave w takes keys
+// 64 w .. 64 w + 63 of the tile in four groups of 16.  A group's logits are
+// one v_mfma_f32_16x16x32_bf16 chain per 16 query heads: A = the query heads
+// (rows; zero past G), B = the 16 keys (columns).  Lane l supplies row or
+// column l % 16 and, at k-step ks, head dims ks*32 + (l/16)*8 .. +7 of both
+// operands, so every dim is contracted once and a lane reads 16-byte runs of
+// its key row (64 contiguous bytes per key and k-step across the lane
+// group).  Output lane l holds key l % 16 for query heads (l/16)*4 .. +3 of
+// the block.  Keys past the sequence read its last row and are masked.
 template <int D>
 __global__ __launch_bounds__(WNW_TILE) void wnw_logits_kernel(WnwDesc W, const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               WnwWork X) {
-  __shared__ __attribute__((aligned(16))) float sq[WNW_MAX_G][D];
+  constexpr int KS = D / 32;
+  constexpr int NWV = WNW_TILE / 64;
+  __shared__ float2 sred[WNW_MAX_G][NWV];
   const int sa = blockIdx.y, seq = sa / W.n_anchor, a = sa - seq * W.n_anchor;
   const int n = W.len[seq], tile = blockIdx.x;
   if (tile * WNW_TILE >= n) return;
   const int G = W.gqa;
-  const uint16_t* qs = q + (size_t)sa * G * D;
-  for (int i = threadIdx.x; i < G * D; i += WNW_TILE) sq[i / D][i % D] = wnw_bf16(qs[i]);
-  __syncthreads();
-  const int j = tile * WNW_TILE + (int)threadIdx.x;
-  const bool valid = j < n;
-  const int64_t unit = (int64_t)seq * W.upseq + W.anchor_unit[a];
-  uint4 kr[D / 8];
-  if (valid) {
-    const uint4* row = reinterpret_cast<const uint4*>(k + unit * W.ks[0] + (int64_t)j * W.ks[1]);
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) kr[i] = row[i];
-  }
-  const float c = kWnwLog2e / sqrtf((float)D);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int part = tile * (WNW_TILE / 64) + wave;
-  for (int g = 0; g < G; ++g) {
-    float dot = 0.f;
-    if (valid) {
+  const int col = lane & 15, grp = lane >> 4;
+  const uint16_t* qs = q + (size_t)sa * G * D;
+  wnw_bf16x8 qa[2][KS];
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        const float4 q0 = *reinterpret_cast<const float4*>(&sq[g][8 * i]);
-        const float4 q1 = *reinterpret_cast<const float4*>(&sq[g][8 * i + 4]);
-        const uint32_t w0 = kr[i].x, w1 = kr[i].y, w2 = kr[i].z, w3 = kr[i].w;
-        dot = fmaf(wnw_bf16(w0 & 0xffffu), q0.x, dot);
-        dot = fmaf(wnw_bf16(w0 >> 16), q0.y, dot);
-        dot = fmaf(wnw_bf16(w1 & 0xffffu), q0.z, dot);
-        dot = fmaf(wnw_bf16(w1 >> 16), q0.w, dot);
-        dot = fmaf(wnw_bf16(w2 & 0xffffu), q1.x, dot);
-        dot = fmaf(wnw_bf16(w2 >> 16), q1.y, dot);
-        dot = fmaf(wnw_bf16(w3 & 0xffffu), q1.z, dot);
-        dot = fmaf(wnw_bf16(w3 >> 16), q1.w, dot);
-      }
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = qb * 16 + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      // rows past G: the last head's bits masked to zero (no branch)
+      uint4 raw = *reinterpret_cast<const uint4*>(qs + (size_t)min(row, G - 1) * D + ks * 32 + grp * 8);
+      const uint32_t keep = row < G ? 0xFFFFFFFFu : 0u;
+      raw.x &= keep;
+      raw.y &= keep;
+      raw.z &= keep;
+      raw.w &= keep;
+      __builtin_memcpy(&qa[qb][ks], &raw, 16);
     }
-    const float l2 = dot * c;
-    const size_t row = (size_t)sa * G + g;
-    if (valid) X.logits[row * W.max_len + j] = l2;
-    // this wave's (max, sum exp2) over its valid keys
-    float mx = valid ? l2 : -INFINITY;
+  }
+  const bool two = G > 16;
+  const int64_t unit = (int64_t)seq * W.upseq + W.anchor_unit[a];
+  const uint16_t* ku = k + unit * W.ks[0];
+  const float c = kWnwLog2e / sqrtf((float)D);
+  const int j0 = tile * WNW_TILE + wave * 64;
+  // All 4 x KS fragment loads of the wave are issued before the first MFMA.
+  uint4 kraw[4][KS];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    float z = valid ? __builtin_amdgcn_exp2f(l2 - mx) : 0.f;
+  for (int kg = 0; kg < 4; ++kg) {
+    const int j = min(j0 + kg * 16 + col, n - 1);
+    const uint16_t* kr = ku + (int64_t)j * W.ks[1] + grp * 8;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
-    if (lane == 0) X.parts[row * W.max_parts + part] = make_float2(mx, z);
+    for (int ks = 0; ks < KS; ++ks) kraw[kg][ks] = *reinterpret_cast<const uint4*>(kr + ks * 32);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  wnw_f4 acc[2][4];
+#pragma unroll
+  for (int kg = 0; kg < 4; ++kg) {
+    wnw_bf16x8 kb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) __builtin_memcpy(&kb[ks], &kraw[kg][ks], 16);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      wnw_f4 t = {0.f, 0.f, 0.f, 0.f};
+      if (qb == 0 || two)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[qb][ks], kb[ks], t, 0, 0, 0);
+      acc[qb][kg] = t;
+    }
+  }
+  // Logits out, and this wave's (max, sum exp2) per query head over its 64
+  // keys: the lane's four keys, then the 16 lanes of its group.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = qb * 16 + grp * 4 + i;   // uniform per lane group
+      float l2[4], mx = -INFINITY;
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg) {
+        const int j = j0 + kg * 16 + col;
+        l2[kg] = acc[qb][kg][i] * c;
+        if (j < n) {
+          mx = fmaxf(mx, l2[kg]);
+          if (g < G) X.logits[((size_t)sa * G + g) * W.max_len + j] = l2[kg];
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      float z = 0.f;
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg)
+        if (j0 + kg * 16 + col < n) z += __builtin_amdgcn_exp2f(l2[kg] - mx);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o);
+      if (col == 0 && g < G) sred[g][wave] = make_float2(mx, z);
+    }
+  }
+  __syncthreads();
+  // The tile's partial per query head (waves with no key past n give (-inf, 0)).
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float m = -INFINITY, z = 0.f;
+    for (int w = 0; w < NWV; ++w) wnw_merge(m, z, sred[g][w].x, sred[g][w].y);
+    X.parts[((size_t)sa * G + g) * W.max_parts + tile] = make_float2(m, z);
   }
 }
 
@@ -145,7 +201,7 @@ __global__ __launch_bounds__(256) void wnw_lse_kernel(WnwDesc W, WnwWork X) {
   __shared__ float2 sred[4];
   const size_t row = blockIdx.x;
   const int seq = (int)(row / ((size_t)W.n_anchor * W.gqa));
-  const int nparts = (W.len[seq] + 63) / 64;
+  const int nparts = (W.len[seq] + WNW_TILE - 1) / WNW_TILE;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float2* p = X.parts + row * W.max_parts;
   float m = -INFINITY, z = 0.f;
@@ -164,48 +220,77 @@ __global__ __launch_bounds__(256) void wnw_lse_kernel(WnwDesc W, WnwWork X) {
   }
 }
 
-// Attention mass per position: sum over anchors of the mean over their heads
-// of exp2(l - LSE); one thread per position (coalesced logit reads).
-__global__ __launch_bounds__(256) void wnw_position_mass_kernel(WnwDesc W, WnwWork X) {
-  const int seq = blockIdx.y, j = blockIdx.x * 256 + (int)threadIdx.x;
-  const int n = W.len[seq];
-  if (j >= n) return;
-  const float invG = 1.0f / (float)W.gqa;
-  float p = 0.f;
-  for (int a = 0; a < W.n_anchor; ++a) {
-    const size_t row0 = (size_t)(seq * W.n_anchor + a) * W.gqa;
-    float pa = 0.f;
-    for (int g = 0; g < W.gqa; ++g)
-      pa += __builtin_amdgcn_exp2f(X.logits[(row0 + g) * W.max_len + j] - X.lse2[row0 + g]);
-    p += pa * invG;
+// Chunk scores of chunks b0 .. b0 + nb - 1 of one sequence (nb = the blocks
+// per workgroup; the grid covers chunk_cap, zeros past the sequence's C).
+// Positions are taken WNW_MT at a time: a thread per position computes its
+// mass into LDS, then a thread per block adds the block's positions of the
+// tile in order to the block's running mass.  Every sum has a fixed order.
+#define WNW_MT 256
+__global__ __launch_bounds__(WNW_MT) void wnw_mass_kernel(WnwDesc W, WnwWork X, float* __restrict__ sigma,
+                                                          int nb) {
+  __shared__ float slse[WNW_MAX_ANCHOR * WNW_MAX_G];
+  __shared__ float spm[WNW_MT];
+  __shared__ float sbeta[WNW_MT + WNW_MAX_M];
+  const int seq = blockIdx.y, tid = threadIdx.x;
+  const int n = W.len[seq], S = W.S, m = W.m;
+  const int B = (n + S - 1) / S, C = max(1, B - m + 1);
+  const int b0 = blockIdx.x * nb;
+  const int cend = min(W.chunk_cap, b0 + nb);
+  float* sg = sigma + (size_t)seq * W.chunk_cap;
+  if (b0 >= C) {
+    for (int c = b0 + tid; c < cend; c += WNW_MT) sg[c] = 0.f;
+    return;
   }
-  X.pmass[(size_t)seq * W.max_len + j] = p;
+  const int G = W.gqa, ra = W.n_anchor * G;
+  const size_t row0 = (size_t)seq * ra;
+  for (int i = tid; i < ra; i += WNW_MT) slse[i] = X.lse2[row0 + i];
+  const int nbw = min(B, b0 + nb + m - 1) - b0;   // blocks whose mass is needed
+  for (int j = tid; j < nbw; j += WNW_MT) sbeta[j] = 0.f;
+  __syncthreads();
+  const float invG = 1.0f / (float)G;
+  const int p_lo = b0 * S, p_hi = min(n, (b0 + nbw) * S);
+  for (int t0 = p_lo; t0 < p_hi; t0 += WNW_MT) {
+    const int p = t0 + tid;
+    // The rows' terms summed in row order, then divided by G (every anchor
+    // has G heads); eight rows' loads in flight at a time.
+    float pm = 0.f;
+    if (p < p_hi) {
+      const float* lp = X.logits + row0 * W.max_len + p;
+      int r = 0;
+      for (; r + 8 <= ra; r += 8) {
+        float l[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) l[i] = lp[(size_t)(r + i) * W.max_len];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pm += __builtin_amdgcn_exp2f(l[i] - slse[r + i]);
+      }
+      for (; r < ra; ++r) pm += __builtin_amdgcn_exp2f(lp[(size_t)r * W.max_len] - slse[r]);
+      pm *= invG;
+    }
+    spm[tid] = pm;
+    __syncthreads();
+    const int t1 = min(p_hi, t0 + WNW_MT);
+    const int jb0 = (t0 - p_lo) / S, jb1 = (t1 - 1 - p_lo) / S;
+    for (int jb = jb0 + tid; jb <= jb1; jb += WNW_MT) {
+      const int lo = max(t0, p_lo + jb * S), hi = min(t1, p_lo + (jb + 1) * S);
+      float sb = 0.f;
+      for (int x = lo; x < hi; ++x) sb += spm[x - t0];
+      sbeta[jb] += sb;
+    }
+    __syncthreads();
+  }
+  for (int c = b0 + tid; c < cend; c += WNW_MT) {
+    float sc = 0.f;
+    if (c < C)
+      for (int b = c; b < min(c + m, B); ++b) sc += sbeta[b - b0];
+    sg[c] = sc;
+  }
 }
 
-// Block masses: the sums of S consecutive position masses, in order.
-__global__ __launch_bounds__(256) void wnw_block_mass_kernel(WnwDesc W, WnwWork X) {
-  const int seq = blockIdx.y, b = blockIdx.x * 256 + (int)threadIdx.x;
-  const int n = W.len[seq], B = (n + W.S - 1) / W.S;
-  if (b >= W.block_cap) return;
-  float beta = 0.f;
-  if (b < B) {
-    const float* pm = X.pmass + (size_t)seq * W.max_len;
-    for (int j = b * W.S; j < min(n, (b + 1) * W.S); ++j) beta += pm[j];
-  }
-  X.beta[(size_t)seq * W.block_cap + b] = beta;
-}
-
-__global__ __launch_bounds__(256) void wnw_sigma_kernel(WnwDesc W, const float* __restrict__ beta,
-                                                        float* __restrict__ sigma) {
-  const int seq = blockIdx.y, c = blockIdx.x * 256 + (int)threadIdx.x;
-  if (c >= W.chunk_cap) return;
-  const int n = W.len[seq], B = (n + W.S - 1) / W.S, C = max(1, B - W.m + 1);
-  float s = 0.f;
-  if (c < C) {
-    const float* bs = beta + (size_t)seq * W.block_cap;
-    for (int b = c; b < min(c + W.m, B); ++b) s += bs[b];
-  }
-  sigma[(size_t)seq * W.chunk_cap + c] = s;
+// Blocks per mass workgroup: as many as fit one tile of positions with the
+// m - 1 blocks recomputed past them, at least one.
+static int wnw_mass_blocks(const WnwDesc& W) {
+  return std::max(1, (WNW_MT - (W.m - 1) * W.S) / W.S);
 }
 
 // ---------------------------------------------------------------------------
@@ -502,7 +587,7 @@ static kvc_status wnw_desc(const kvc_wnw_problem* p, const kvc_wnw_params* prm, 
     if (r > KVC_WNW_TIDAL) return KVC_ERR_INVALID_ARG;
     if (r == KVC_WNW_ANCHOR) {
       if (na == WNW_MAX_ANCHOR) return KVC_ERR_UNSUPPORTED;
-      W->anchor_unit[na++] = (int16_t)u;
+      W->anchor_unit[na++] = (int32_t)u;
     } else if (r == KVC_WNW_TIDAL) {
       W->tidal_mask[u / 32] |= 1u << (u % 32);
       ++nt;
@@ -548,7 +633,7 @@ static kvc_status wnw_desc(const kvc_wnw_problem* p, const kvc_wnw_params* prm, 
   W->n_anchor = na;
   W->n_tidal = nt;
   W->max_len = max_len;
-  W->max_parts = ((max_len + WNW_TILE - 1) / WNW_TILE) * (WNW_TILE / 64);
+  W->max_parts = (max_len + WNW_TILE - 1) / WNW_TILE;
   for (int a = 0; a < 2; ++a) {
     W->ks[a] = p->k_stride[a];
     W->hs[a] = p->host_stride[a];
@@ -576,8 +661,7 @@ static void wnw_layout(const WnwDesc& W, kvc_wnw_layout* L) {
   L->state_bytes = o;
   const size_t SA = N * W.n_anchor * W.gqa;
   L->workspace_bytes = wnw_up(4 * SA * W.max_len) + wnw_up(8 * SA * W.max_parts) +
-                       wnw_up(4 * SA) + wnw_up(4 * N * W.max_len) + wnw_up(4 * N * W.block_cap) +
-                       wnw_up(4 * N * W.chunk_cap);
+                       wnw_up(4 * SA) + wnw_up(4 * N * W.chunk_cap);
 }
 
 static WnwState wnw_state(const kvc_wnw_layout& L, const void* p) {
@@ -600,8 +684,6 @@ static WnwWork wnw_work(const WnwDesc& W, void* p) {
   X.logits = (float*)b;  b += wnw_up(4 * SA * W.max_len);
   X.parts = (float2*)b;  b += wnw_up(8 * SA * W.max_parts);
   X.lse2 = (float*)b;    b += wnw_up(4 * SA);
-  X.pmass = (float*)b;   b += wnw_up(4 * N * W.max_len);
-  X.beta = (float*)b;    b += wnw_up(4 * N * W.block_cap);
   X.sigma = (float*)b;
   return X;
 }
@@ -660,14 +742,9 @@ static hipError_t wnw_launch_scores(const WnwDesc& W, const void* q, const void*
                        (const uint16_t*)k, X);
   hipLaunchKernelGGL(wnw_lse_kernel, dim3((unsigned)(W.n_seq * W.n_anchor * W.gqa)), dim3(256), 0,
                      st, W, X);
-  hipLaunchKernelGGL(wnw_position_mass_kernel,
-                     dim3((unsigned)((W.max_len + 255) / 256), (unsigned)W.n_seq), dim3(256), 0, st,
-                     W, X);
-  hipLaunchKernelGGL(wnw_block_mass_kernel,
-                     dim3((unsigned)((W.block_cap + 255) / 256), (unsigned)W.n_seq), dim3(256), 0,
-                     st, W, X);
-  hipLaunchKernelGGL(wnw_sigma_kernel, dim3((unsigned)((W.chunk_cap + 255) / 256), (unsigned)W.n_seq),
-                     dim3(256), 0, st, W, (const float*)X.beta, sigma);
+  const int nb = wnw_mass_blocks(W);
+  hipLaunchKernelGGL(wnw_mass_kernel, dim3((unsigned)((W.chunk_cap + nb - 1) / nb), (unsigned)W.n_seq),
+                     dim3(WNW_MT), 0, st, W, X, sigma, nb);
   return hipGetLastError();
 }
 

@@ -568,7 +568,7 @@ def bench_wnw(args):
                        "achieved": round(recall_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                        "frac": round(recall_gbs / PCIE_PEAK_GBS, 4),
                        "note": "cold-step recall list, host to device over PCIe"},
-            "chunk_scores": {"bound": "hbm", "kernel": "wnw_logits_kernel + lse/mass/sigma",
+            "chunk_scores": {"bound": "hbm", "kernel": "wnw_logits_kernel + wnw_lse_kernel + wnw_mass_kernel",
                              "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
                              "traffic": None},
