@@ -7,14 +7,17 @@
 // rows of largest A, concatenated in order.
 //
 // Four kernels per step, every cache u = (sequence, layer, KV head):
-//   logits  one workgroup per (cache, 1024-row chunk): the G x 1024 logits
+//   logits  one workgroup per (cache, 256-row part): the G x 256 logits
 //           (log2 units, c = log2(e)/sqrt(d) folded in) into workspace, and
-//           per query head the chunk's (max, sum of exp2).  bf16 on
-//           v_mfma_f32_32x32x16_bf16 with the G query heads as A rows (the
-//           block is padded to 32 rows) and 32 cache rows as B columns;
-//           fp32 inputs on fp64 VALU dot products.
-//   accum   same grid: fold the chunk statistics into each head's LSE and
-//           write A = gamma * [A_prev, 0] + mean_g exp2(l_g - LSE_g).
+//           per query head the part's (max, sum of exp2).  bf16 on
+//           v_mfma_f32_16x16x32_bf16 with the G query heads as A rows (16
+//           per block, zero past G) and 16 cache rows as B columns, every
+//           fragment load of a wave in flight before its first MFMA; fp32
+//           inputs on fp64 VALU dot products.
+//   accum   one workgroup per (cache, 1024-row chunk): fold the parts'
+//           statistics into each head's LSE (a wave per head, lanes over
+//           the parts) and write A = gamma * [A_prev, 0] +
+//           mean_g exp2(l_g - LSE_g).
 //   evict   one 1024-lane workgroup per cache: radix select of the N largest
 //           A among the middle rows (four 8-bit digit passes over
 //           order-preserving u32 keys), then an ordered compaction that
@@ -33,10 +36,9 @@
 #include "../../include/kvc_voxzip.h"
 #include "kvc_internal.h"
 
-typedef __bf16 vz_bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef float vz_floatx16 __attribute__((__vector_size__(16 * sizeof(float))));
 
 #define VZ_CHUNK 1024
+#define VZ_PART 256                       // rows per logits workgroup and partial
 #define VZ_THREADS 256
 #define VZ_SEL_THREADS 1024
 #define VZ_MAX_SEQ 64
@@ -48,6 +50,7 @@ static constexpr float kVzLog2e = 1.4426950408889634f;
 struct VzDesc {
   int32_t n_seq, upseq, gqa, d, dtype, n_sink;
   int32_t n_units, nch;             // nch = chunks per cache at capacity
+  int32_t npart;                    // VZ_PART-row parts per cache at capacity
   float gamma;
   int64_t cap;
   int64_t ks[2], vs[2];             // element strides: cache, row
@@ -58,7 +61,7 @@ struct VzDesc {
 };
 
 // ---------------------------------------------------------------------------
-// Logits and chunk statistics
+// Logits and part statistics
 // ---------------------------------------------------------------------------
 // Fold (m2, z2) into (m, z): z = sum of exp2(l - m) over the values seen.
 __device__ inline void vz_merge(float& m, float& z, float m2, float z2) {
@@ -70,112 +73,110 @@ __device__ inline void vz_merge(float& m, float& z, float m2, float z2) {
   z = a + b;
 }
 
-// Output element i of lane l of the 32x32 MFMA block sits at row
-// (i/4)*8 + (l/32)*4 + i%4 and column l%32.  With the G query heads as rows,
-// only elements i < NI can hold a head (NI = 4 for G <= 8, 8 for G <= 16).
-template <int D, int NI>
+typedef __bf16 vz_bf16x8v __attribute__((ext_vector_type(8)));
+typedef float vz_f4 __attribute__((ext_vector_type(4)));
+
+// Wave w takes rows row0 + 64 w .. +63 of the part in four groups of 16.  A
+// group's logits are one v_mfma_f32_16x16x32_bf16 chain per 16 query heads:
+// lane l supplies head (A) or row (B) l % 16 and, at k-step ks, head dims
+// ks*32 + (l/16)*8 .. +7 of both operands (so a row is read as 64-byte
+// runs); output lane l holds row l % 16 for heads (l/16)*4 .. +3 of the
+// block.  Rows past n read row n - 1 and are masked.
+template <int D>
 __global__ __launch_bounds__(VZ_THREADS) void vz_logits_bf16_kernel(
     VzDesc V, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     float* __restrict__ lg, float2* __restrict__ part) {
-  constexpr int NK = D / 16;           // k-steps of 16; a lane covers 8 per step
-  const int u = blockIdx.x, chunk = blockIdx.y;
+  constexpr int KS = D / 32;
+  constexpr int NWV = VZ_THREADS / 64;
+  __shared__ float2 sst[VZ_MAX_G][NWV];
+  const int u = blockIdx.x, pi = blockIdx.y;
   const int seq = u / V.upseq;
   const int n = V.len[seq];
-  const int row0 = chunk * VZ_CHUNK;
+  const int row0 = pi * VZ_PART;
   if (row0 >= n) return;
   const int G = V.gqa;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col = lane & 31, half = lane >> 5;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
   const float c = kVzLog2e / sqrtf((float)D);
-
-  // A operand: query head `col` (zero rows past G), the lane's half of the
-  // head dimension in 8-element steps.  K uses the same permutation, so the
-  // contraction over d is complete.
-  vz_bf16x8 a[NK];
-  {
-    const uint16_t* qp = q + ((size_t)u * G + (col < G ? col : 0)) * D + half * (D / 2);
+  const uint16_t* qs = q + (size_t)u * G * D;
+  vz_bf16x8v qa[2][KS];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      uint4 raw = col < G ? reinterpret_cast<const uint4*>(qp)[kk] : make_uint4(0, 0, 0, 0);
-      __builtin_memcpy(&a[kk], &raw, 16);
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = qb * 16 + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      // heads past G: the last head's bits masked to zero (no branch)
+      uint4 raw = *reinterpret_cast<const uint4*>(qs + (size_t)min(row, G - 1) * D + ks * 32 + grp * 8);
+      const uint32_t keep = row < G ? 0xFFFFFFFFu : 0u;
+      raw.x &= keep;
+      raw.y &= keep;
+      raw.z &= keep;
+      raw.w &= keep;
+      __builtin_memcpy(&qa[qb][ks], &raw, 16);
     }
   }
-  float m[NI], z[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    m[i] = -INFINITY;
-    z[i] = 0.f;
-  }
+  const bool two = G > 16;
   const uint16_t* kc = k + (int64_t)u * V.ks[0];
   float* lgu = lg + (size_t)u * G * V.cap;
-  // The wave's (up to) 256 rows of the chunk, 32 per MFMA block; the next
-  // block's rows load while this block computes.
-  const int wrow0 = row0 + wave * 256;
-  const int nblk = wrow0 >= n ? 0 : min(8, (n - wrow0 + 31) / 32);
-  auto load_blk = [&](vz_bf16x8 (&b)[NK], int blk) {
-    const int r0 = wrow0 + blk * 32;
-    const int r = r0 + col;
-    const uint16_t* kp = kc + (int64_t)(r < n ? r : r0) * V.ks[1] + half * (D / 2);
+  const int j0 = row0 + wave * 64;
+  uint4 kraw[4][KS];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const uint4 raw = reinterpret_cast<const uint4*>(kp)[kk];
-      __builtin_memcpy(&b[kk], &raw, 16);
+  for (int kg = 0; kg < 4; ++kg) {
+    const int j = min(j0 + kg * 16 + col, n - 1);
+    const uint16_t* kr = kc + (int64_t)j * V.ks[1] + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kraw[kg][ks] = *reinterpret_cast<const uint4*>(kr + ks * 32);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  vz_f4 acc[2][4];
+#pragma unroll
+  for (int kg = 0; kg < 4; ++kg) {
+    vz_bf16x8v kb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) __builtin_memcpy(&kb[ks], &kraw[kg][ks], 16);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      vz_f4 t = {0.f, 0.f, 0.f, 0.f};
+      if (qb == 0 || two)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[qb][ks], kb[ks], t, 0, 0, 0);
+      acc[qb][kg] = t;
     }
-  };
-  auto compute_blk = [&](const vz_bf16x8 (&b)[NK], int blk) {
-    const int r = wrow0 + blk * 32 + col;
-    vz_floatx16 acc = {};
+  }
+  // Logits out; the wave's (max, sum exp2) per head over its 64 rows: the
+  // lane's four rows, then the 16 lanes of its group.
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], b[kk], acc, 0, 0, 0);
+  for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int g = (i >> 2) * 8 + half * 4 + (i & 3);
-      if (g < G && r < n) {
-        const float l2 = acc[i] * c;
-        lgu[(size_t)g * V.cap + r] = l2;
-        const float mn = fmaxf(m[i], l2);
-        z[i] = z[i] * exp2f(m[i] - mn) + exp2f(l2 - mn);
-        m[i] = mn;
+    for (int i = 0; i < 4; ++i) {
+      const int g = qb * 16 + grp * 4 + i;
+      float l2[4], mx = -INFINITY;
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg) {
+        const int j = j0 + kg * 16 + col;
+        l2[kg] = acc[qb][kg][i] * c;
+        if (j < n) {
+          mx = fmaxf(mx, l2[kg]);
+          if (g < G) lgu[(size_t)g * V.cap + j] = l2[kg];
+        }
       }
-    }
-  };
-  // The prefetch is unconditional (past the last block it reloads that
-  // block) so that every path has the same loads in flight and the waits
-  // before the MFMAs cover only the block they consume.
-  vz_bf16x8 b0[NK], b1[NK];
-  if (nblk > 0) {
-    load_blk(b0, 0);
-    for (int blk = 0;; blk += 2) {
-      load_blk(b1, min(blk + 1, nblk - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      compute_blk(b0, blk);
-      if (blk + 1 >= nblk) break;
-      load_blk(b0, min(blk + 2, nblk - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      compute_blk(b1, blk + 1);
-      if (blk + 2 >= nblk) break;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      float z = 0.f;
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg)
+        if (j0 + kg * 16 + col < n) z += exp2f(l2[kg] - mx);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o);
+      if (col == 0 && g < G) sst[g][wave] = make_float2(mx, z);
     }
   }
-  // Lanes of one half share their heads: fold over the 32 columns.
-  __shared__ float2 sst[4][VZ_MAX_G];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-      const float m2 = __shfl_xor(m[i], o);
-      const float z2 = __shfl_xor(z[i], o);
-      vz_merge(m[i], z[i], m2, z2);
-    }
-    const int g = (i >> 2) * 8 + half * 4 + (i & 3);
-    if (col == 0 && g < G) sst[wave][g] = make_float2(m[i], z[i]);
-  }
-  // A wave with no rows in the chunk leaves (-inf, 0), which folds as empty.
+  // A wave with no rows in the part leaves (-inf, 0), which folds as empty.
   __syncthreads();
   if ((int)threadIdx.x < G) {
     float mm = -INFINITY, zz = 0.f;
-    for (int w = 0; w < 4; ++w) vz_merge(mm, zz, sst[w][threadIdx.x].x, sst[w][threadIdx.x].y);
-    part[((size_t)u * V.nch + chunk) * G + threadIdx.x] = make_float2(mm, zz);
+    for (int w = 0; w < NWV; ++w) vz_merge(mm, zz, sst[threadIdx.x][w].x, sst[threadIdx.x][w].y);
+    part[((size_t)u * V.npart + pi) * G + threadIdx.x] = make_float2(mm, zz);
   }
 }
 
@@ -184,10 +185,10 @@ template <int D>
 __global__ __launch_bounds__(VZ_THREADS) void vz_logits_f32_kernel(
     VzDesc V, const float* __restrict__ q, const float* __restrict__ k,
     float* __restrict__ lg, float2* __restrict__ part) {
-  const int u = blockIdx.x, chunk = blockIdx.y;
+  const int u = blockIdx.x, pi = blockIdx.y;
   const int seq = u / V.upseq;
   const int n = V.len[seq];
-  const int row0 = chunk * VZ_CHUNK;
+  const int row0 = pi * VZ_PART;
   if (row0 >= n) return;
   const int G = V.gqa;
   __shared__ float sq[VZ_MAX_G * D];
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_logits_f32_kernel(
   __shared__ float2 sst[4][VZ_MAX_G];
   for (int g = 0; g < G; ++g) {
     float m = -INFINITY, z = 0.f;
-    for (int r = row0 + threadIdx.x; r < n && r < row0 + VZ_CHUNK; r += VZ_THREADS) {
+    for (int r = row0 + threadIdx.x; r < n && r < row0 + VZ_PART; r += VZ_THREADS) {
       const float* kp = kc + (int64_t)r * V.ks[1];
       double dot = 0.0;
 #pragma unroll 8
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_logits_f32_kernel(
   if ((int)threadIdx.x < G) {
     float mm = -INFINITY, zz = 0.f;
     for (int w = 0; w < 4; ++w) vz_merge(mm, zz, sst[w][threadIdx.x].x, sst[w][threadIdx.x].y);
-    part[((size_t)u * V.nch + chunk) * G + threadIdx.x] = make_float2(mm, zz);
+    part[((size_t)u * V.npart + pi) * G + threadIdx.x] = make_float2(mm, zz);
   }
 }
 
@@ -237,14 +238,23 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_accum_kernel(
   if (row0 >= n) return;
   const int G = V.gqa;
   __shared__ float lse[VZ_MAX_G];
-  if ((int)threadIdx.x < G) {
-    const int nch = (n + VZ_CHUNK - 1) / VZ_CHUNK;
-    float m = -INFINITY, z = 0.f;
-    for (int ch = 0; ch < nch; ++ch) {
-      const float2 p = part[((size_t)u * V.nch + ch) * G + threadIdx.x];
-      vz_merge(m, z, p.x, p.y);
+  // Each head's LSE: a wave per head, lanes over the parts.
+  {
+    const int np = (n + VZ_PART - 1) / VZ_PART;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int g = wave; g < G; g += VZ_THREADS / 64) {
+      float m = -INFINITY, z = 0.f;
+      for (int p = lane; p < np; p += 64) {
+        const float2 pp = part[((size_t)u * V.npart + p) * G + g];
+        vz_merge(m, z, pp.x, pp.y);
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(m, o), z2 = __shfl_xor(z, o);
+        vz_merge(m, z, m2, z2);
+      }
+      if (lane == 0) lse[g] = m + log2f(z);
     }
-    lse[threadIdx.x] = m + log2f(z);
   }
   __syncthreads();
   const float inv_g = 1.0f / (float)G;
@@ -253,8 +263,17 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_accum_kernel(
   float* at = a_t + (size_t)u * V.cap;
   const int rend = min(n, row0 + VZ_CHUNK);
   for (int r = row0 + threadIdx.x; r < rend; r += VZ_THREADS) {
+    // the heads' terms in head order, eight heads' loads in flight at a time
     float s = 0.f;
-    for (int g = 0; g < G; ++g) s += exp2f(lgu[(size_t)g * V.cap + r] - lse[g]);
+    int g = 0;
+    for (; g + 8 <= G; g += 8) {
+      float l[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) l[i] = lgu[(size_t)(g + i) * V.cap + r];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += exp2f(l[i] - lse[g + i]);
+    }
+    for (; g < G; ++g) s += exp2f(lgu[(size_t)g * V.cap + r] - lse[g]);
     const float prev = r < n - 1 ? V.gamma * ap[r] : 0.f;
     at[r] = prev + s * inv_g;
   }
@@ -486,6 +505,7 @@ static kvc_status vz_desc(const kvc_vz_problem* p, const kvc_vz_params* prm, VzD
   V->n_units = (int32_t)(upseq * p->n_seq);
   V->cap = p->capacity;
   V->nch = (int32_t)((p->capacity + VZ_CHUNK - 1) / VZ_CHUNK);
+  V->npart = (int32_t)((p->capacity + VZ_PART - 1) / VZ_PART);
   V->gamma = (float)prm->gamma;
   for (int a = 0; a < 2; ++a) {
     V->ks[a] = p->k_stride[a];
@@ -502,7 +522,7 @@ struct VzCarve {
 
 static size_t vz_ws_logits(const VzDesc& V) {
   return vz_up(sizeof(float) * (size_t)V.n_units * V.gqa * V.cap) +
-         vz_up(sizeof(float2) * (size_t)V.n_units * V.nch * V.gqa);
+         vz_up(sizeof(float2) * (size_t)V.n_units * V.npart * V.gqa);
 }
 
 static VzCarve vz_carve(const VzDesc& V, void* ws) {
@@ -511,7 +531,7 @@ static VzCarve vz_carve(const VzDesc& V, void* ws) {
   c.lg = (float*)p;
   p += vz_up(sizeof(float) * (size_t)V.n_units * V.gqa * V.cap);
   c.part = (float2*)p;
-  p += vz_up(sizeof(float2) * (size_t)V.n_units * V.nch * V.gqa);
+  p += vz_up(sizeof(float2) * (size_t)V.n_units * V.npart * V.gqa);
   c.a_t = (float*)p;
   return c;
 }
@@ -521,32 +541,21 @@ static bool vz_a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static hipError_t vz_launch_accumulate(const VzDesc& V, const void* q, const void* k,
                                        const float* a_prev, float* a_t, const VzCarve& c,
                                        hipStream_t st) {
-  const dim3 grid(V.n_units, V.nch);
+  const dim3 pgrid(V.n_units, V.npart), grid(V.n_units, V.nch);
   if (V.dtype == 0) {
     const uint16_t* qq = (const uint16_t*)q;
     const uint16_t* kk = (const uint16_t*)k;
-    if (V.d == 128) {
-      if (V.gqa <= 8)
-        hipLaunchKernelGGL((vz_logits_bf16_kernel<128, 4>), grid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
-      else if (V.gqa <= 16)
-        hipLaunchKernelGGL((vz_logits_bf16_kernel<128, 8>), grid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
-      else
-        hipLaunchKernelGGL((vz_logits_bf16_kernel<128, 16>), grid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
-    } else {
-      if (V.gqa <= 8)
-        hipLaunchKernelGGL((vz_logits_bf16_kernel<64, 4>), grid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
-      else if (V.gqa <= 16)
-        hipLaunchKernelGGL((vz_logits_bf16_kernel<64, 8>), grid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
-      else
-        hipLaunchKernelGGL((vz_logits_bf16_kernel<64, 16>), grid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
-    }
+    if (V.d == 128)
+      hipLaunchKernelGGL((vz_logits_bf16_kernel<128>), pgrid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
+    else
+      hipLaunchKernelGGL((vz_logits_bf16_kernel<64>), pgrid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
   } else {
     const float* qq = (const float*)q;
     const float* kk = (const float*)k;
     if (V.d == 128)
-      hipLaunchKernelGGL((vz_logits_f32_kernel<128>), grid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
+      hipLaunchKernelGGL((vz_logits_f32_kernel<128>), pgrid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
     else
-      hipLaunchKernelGGL((vz_logits_f32_kernel<64>), grid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
+      hipLaunchKernelGGL((vz_logits_f32_kernel<64>), pgrid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
