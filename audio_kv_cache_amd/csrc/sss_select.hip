@@ -31,7 +31,10 @@
 // 32-bit keys (-0 folded into +0); a bitwise search for the largest key T
 // with count(key >= T) >= k finds the k-th largest value, positions equal to
 // T are taken from the lowest position upward, and a block scan writes the
-// kept positions in ascending order.
+// kept positions in ascending order.  Each thread transposes its keys into
+// 32-bit planes once (bit s of plane b = bit b of its key s), so a round of
+// the search costs a popcount per 32 keys instead of 32 compares, and the
+// search leaves the masks of the keys above and equal to T.
 #include "kvc_internal.h"
 
 #define SSS_T KVC_SSS_THREADS
@@ -479,6 +482,28 @@ __device__ __forceinline__ void smooth_unit(const KvcDesc& D, int mode, int u, c
   }
 }
 
+// One level of a 32 x 32 bit-matrix transpose (row k = A[k], column j = bit
+// j): rows k and k + J (bit J of k clear) exchange the high J-bit half of
+// each 2J-bit group of row k with the low half of row k + J.
+template <int J, uint32_t M>
+__device__ __forceinline__ void transpose_level(uint32_t (&A)[32]) {
+#pragma unroll
+  for (int k = 0; k < 32; ++k)
+    if (!(k & J)) {
+      const uint32_t x = ((A[k] >> J) ^ A[k + J]) & M;
+      A[k + J] ^= x;
+      A[k] ^= x << J;
+    }
+}
+// Afterwards bit s of A[b] is bit b of the original A[s].
+__device__ __forceinline__ void transpose32(uint32_t (&A)[32]) {
+  transpose_level<16, 0x0000FFFFu>(A);
+  transpose_level<8, 0x00FF00FFu>(A);
+  transpose_level<4, 0x0F0F0F0Fu>(A);
+  transpose_level<2, 0x33333333u>(A);
+  transpose_level<1, 0x55555555u>(A);
+}
+
 // ---------------------------------------------------------------------------
 // Selection for one unit of L positions from s_hat held as in smooth_unit's
 // output (thread t: positions 2 V t + 2 s in re[s], 2 V t + 2 s + 1 in
@@ -495,26 +520,46 @@ __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, int L, floa
   const int b = budgets[u];
   const int k = b - w;
   const int64_t off = offsets[u];
-  // Order-preserving keys, stored in place of the values: position
-  // p0 + 2s is re[s], p0 + 2s + 1 is im[s].
-#pragma unroll
-  for (int s = 0; s < V; ++s) {
-    re[s] = __uint_as_float(order_key(re[s]));
-    im[s] = __uint_as_float(order_key(im[s]));
-  }
-#define KEY(s) __float_as_uint(((s) & 1) ? im[(s) >> 1] : re[(s) >> 1])
+  // Order-preserving keys of the thread's slots s (position p0 + s; slot
+  // s is re[s/2] for even s, im[s/2] for odd s), transposed into planes per
+  // group of 32 slots.  Slots past the row or the candidates never enter
+  // the masks.
+  constexpr int NG = (2 * V + 31) / 32;
   const int p0 = 2 * V * t;  // first position held by this thread
+  uint32_t P[NG][32];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int sl = 32 * g + j;
+      P[g][j] = sl < 2 * V ? order_key((sl & 1) ? im[sl >> 1] : re[sl >> 1]) : 0u;
+    }
+    transpose32(P[g]);
+  }
+  const int nval = act ? min(2 * V, max(0, ncand - p0)) : 0;
+  uint32_t match[NG], above[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int nv = min(32, max(0, nval - 32 * g));
+    match[g] = nv >= 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u);
+    above[g] = 0u;
+  }
 
   // Largest T with #{key >= T} >= k, bit by bit from the top; one barrier
-  // per bit (the reduction slots alternate between bits).
-  uint32_t thr = 0;
+  // per bit (the reduction slots alternate between bits).  Per bit, the
+  // keys still equal to T's prefix with that bit set are `hit`: they stay
+  // equal if T takes the bit, else they are above T from then on.
   if (k > 0 && k < ncand) {
-    const int nval = act ? min(2 * V, max(0, ncand - p0)) : 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = thr | (1u << bit);
-      int cnt = 0;
+    int acnt = 0;
 #pragma unroll
-      for (int s = 0; s < 2 * V; ++s) cnt += (s < nval) & (KEY(s) >= c);
+    for (int bit = 31; bit >= 0; --bit) {
+      uint32_t hit[NG];
+      int cnt = acnt;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        hit[g] = match[g] & P[g][bit];
+        cnt += __popc(hit[g]);
+      }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
       if ((threadIdx.x & 63) == 0) sh.s3[bit & 1][0][threadIdx.x >> 6] = cnt;
@@ -522,18 +567,25 @@ __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, int L, floa
       int tot = 0;
 #pragma unroll
       for (int i = 0; i < SSS_WAVES; ++i) tot += sh.s3[bit & 1][0][i];
-      if (tot >= k) thr = c;
+      if (tot >= k) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) match[g] = hit[g];
+      } else {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          above[g] |= hit[g];
+          acnt += __popc(hit[g]);
+          match[g] &= ~P[g][bit];
+        }
+      }
     }
   }
-  // Counts above and at the threshold.
+  // Counts above and at the threshold (the masks hold candidates only).
   int ngt = 0, neq = 0;
-  if (act) {
 #pragma unroll
-    for (int s = 0; s < 2 * V; ++s) {
-      const bool cd = p0 + s < ncand;
-      ngt += cd && KEY(s) > thr;
-      neq += cd && KEY(s) == thr;
-    }
+  for (int g = 0; g < NG; ++g) {
+    ngt += __popc(above[g]);
+    neq += __popc(match[g]);
   }
   int gt_total, eq_total;
   const int eq_before = block_scan<int>(neq, sh.si, &eq_total);
@@ -549,12 +601,14 @@ __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, int L, floa
 #pragma unroll
     for (int s = 0; s < 2 * V; ++s) {
       const int p = p0 + s;
+      const bool gt = (above[s >> 5] >> (s & 31)) & 1u;
+      const bool eq = (match[s >> 5] >> (s & 31)) & 1u;
       bool sel;
       if (p >= ncand) sel = p < L;
       else if (take_all) sel = true;
       else if (take_none) sel = false;
-      else if (KEY(s) > thr) sel = true;
-      else if (KEY(s) == thr) sel = (er++ < need);
+      else if (gt) sel = true;
+      else if (eq) sel = (er++ < need);
       else sel = false;
       if (sel) {
         if (s < 32) selmask_lo |= 1u << s;
@@ -587,7 +641,6 @@ __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, int L, floa
       if (sel && base + o < b) idx_out[off + base + (o++)] = p0 + s;
     }
   }
-#undef KEY
 }
 
 // Values per thread for a half-length N: at most 1024 threads, at least 8
