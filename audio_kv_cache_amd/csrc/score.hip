@@ -281,9 +281,19 @@ __global__ __launch_bounds__(KVC_MAX_GW) void kvc_score_lse_kernel(KvcDesc Dsc, 
   const int tile0 = Dsc.tile_base[seq] + (u - seq * Dsc.upseq) * tpu;
   const int gw = Dsc.gw;
   if ((int)threadIdx.x >= gw) return;
+  // Tiles merged in order; eight tiles' loads in flight at a time.
+  const float2* pp = partials + (size_t)tile0 * gw + threadIdx.x;
   float mm = -INFINITY, zz = 0.f;
-  for (int t = 0; t < tpu; ++t) {
-    const float2 p = partials[(size_t)(tile0 + t) * gw + threadIdx.x];
+  int t = 0;
+  for (; t + 8 <= tpu; t += 8) {
+    float2 p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = pp[(size_t)(t + i) * gw];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) merge_stat(mm, zz, p[i].x, p[i].y, c);
+  }
+  for (; t < tpu; ++t) {
+    const float2 p = pp[(size_t)t * gw];
     merge_stat(mm, zz, p.x, p.y, c);
   }
   lse2[(size_t)u * gw + threadIdx.x] = mm * c + __builtin_amdgcn_logf(zz);
