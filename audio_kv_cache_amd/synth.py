@@ -452,6 +452,12 @@ WNW_CONFIGS = {
     # heads, at a 32K-token audio context (about 44 minutes at 12.5 tokens/s)
     "wnw_voxtral3b": WnwConfig("wnw_voxtral3b", 33, 1, 30, 8, 4, 128, lens=(32768,),
                                capacity=32768, anchors=(100, 109, 118, 127, 136)),
+    # more than 16 query heads per KV head: a partial second block of 16
+    # heads (d = 64), and two full blocks (d = 128, two sequences)
+    "wnw_g20": WnwConfig("wnw_g20", 34, 1, 2, 2, 20, 64, lens=(613,), capacity=640,
+                         anchors=(0, 3)),
+    "wnw_g32": WnwConfig("wnw_g32", 35, 2, 1, 3, 32, 128, lens=(400, 1207), capacity=1216,
+                         anchors=(1,)),
 }
 
 

@@ -185,7 +185,7 @@ def test_vz_accumulate_tiny_all():
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("gqa", [1, 7, 8, 12, 32])
+@pytest.mark.parametrize("gqa", [1, 7, 8, 12, 20, 32])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_vz_accumulate_shapes(dtype, gqa, d):
     say(f"[vz] accumulate {dtype} G={gqa} d={d}")

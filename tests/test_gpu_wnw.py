@@ -149,7 +149,7 @@ class WnwDev:
         return True
 
 
-@pytest.mark.parametrize("name", ["wnw_tiny", "wnw_mixed", "wnw_edge"])
+@pytest.mark.parametrize("name", ["wnw_tiny", "wnw_mixed", "wnw_edge", "wnw_g20", "wnw_g32"])
 def test_steps_match_oracle(name):
     say(f"[wnw] {name}")
     D = WnwDev(synth.WNW_CONFIGS[name], api.WnwParams())
