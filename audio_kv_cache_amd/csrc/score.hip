@@ -877,9 +877,15 @@ __global__ __launch_bounds__(KVC_MAX_GW) void kvc_score_tail_kernel(KvcDesc Dsc,
   };
   const E* qg = q + kvc_q_offset(Dsc, seq, l, h);
   const E* ku = k + kvc_kv_offset(Dsc.ks, Dsc, seq, l, h);
-  for (int i = threadIdx.x; i < nk * D; i += KVC_MAX_GW) {
-    const int j = i / D, cc = i - j * D;
-    sK[j][cc] = val(ku[(int64_t)(j0 + j) * Dsc.ks[2] + cc]);
+  // The range's key rows into LDS as fp32, a 16-byte piece per thread.
+  constexpr int EP = 16 / (int)sizeof(E), PPR = D / EP;   // elements per piece, pieces per row
+  for (int i = threadIdx.x; i < nk * PPR; i += KVC_MAX_GW) {
+    const int j = i / PPR, pc = i - j * PPR;
+    const uint4 raw = *reinterpret_cast<const uint4*>(ku + (int64_t)(j0 + j) * Dsc.ks[2] + pc * EP);
+    E ev[EP];
+    __builtin_memcpy(ev, &raw, 16);
+#pragma unroll
+    for (int e = 0; e < EP; ++e) sK[j][pc * EP + e] = val(ev[e]);
   }
   __syncthreads();
   const int r = threadIdx.x;
@@ -887,16 +893,29 @@ __global__ __launch_bounds__(KVC_MAX_GW) void kvc_score_tail_kernel(KvcDesc Dsc,
 #pragma unroll
   for (int j = 0; j < NK; ++j) acc[j] = 0.f;
   if (r < gw) {
-    const E* qr = qg + (size_t)r * D;
-    for (int c0 = 0; c0 < D; c0 += 8) {
-      float qv[8];
+    // The query row in pieces of 64 elements, each piece's 16-byte loads
+    // issued together (the row is 16-byte aligned), then the dot products
+    // over the piece in element order.
+    constexpr int CH = 64, PL = CH * (int)sizeof(E) / 16;
+    const uint4* qr = reinterpret_cast<const uint4*>(qg + (size_t)r * D);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qv[e] = val(qr[c0 + e]);
+    for (int c0 = 0; c0 < D; c0 += CH) {
+      uint4 raw[PL];
 #pragma unroll
-      for (int j = 0; j < NK; ++j) {
-        if (j < nk) {
+      for (int i = 0; i < PL; ++i) raw[i] = qr[c0 * (int)sizeof(E) / 16 + i];
+      E qe[CH];
+      __builtin_memcpy(qe, raw, sizeof(qe));
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[j] = fmaf(qv[e], sK[j][c0 + e], acc[j]);
+      for (int e0 = 0; e0 < CH; e0 += 8) {
+        float qv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[e] = val(qe[e0 + e]);
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+          if (j < nk) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[j] = fmaf(qv[e], sK[j][c0 + e0 + e], acc[j]);
+          }
         }
       }
     }
