@@ -1177,12 +1177,28 @@ __global__ __launch_bounds__(C3_BIG) void c3_select_update_kernel(
   }
 
   if (do_sel) {
+    // Key, node and weight of the thread's entries tid and tid + C3_BIG,
+    // read once (entries past 2 C3_BIG are read again in every pass).
+    uint32_t ck[2], cw[2];
+    int cx[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = tid + j * C3_BIG;
+      cx[j] = i < A ? F[i] : 0;
+      ck[j] = i < A ? c3_desc_key(sg[i]) : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) cw[j] = tid + j * C3_BIG < A ? (uint32_t)NZ[cx[j]] : 0u;
     // Weighted radix select: the smallest key T with weight(key <= T) >= B.
     uint32_t prefix = 0, pmask = 0, need = (uint32_t)B;
     for (int shift = 24; shift >= 0; shift -= 8) {
       for (int b = lane; b < 256; b += 64) hist[wave][b] = 0;
       __syncthreads();
-      for (int i = tid; i < A; i += C3_BIG) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (tid + j * C3_BIG < A && (ck[j] & pmask) == prefix)
+          atomicAdd(&hist[wave][(ck[j] >> shift) & 255u], cw[j]);
+      for (int i = tid + 2 * C3_BIG; i < A; i += C3_BIG) {
         const uint32_t key = c3_desc_key(sg[i]);
         if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], (uint32_t)NZ[F[i]]);
       }
@@ -1230,9 +1246,10 @@ __global__ __launch_bounds__(C3_BIG) void c3_select_update_kernel(
     for (int b0 = 0; b0 < A; b0 += C3_BIG) {
       const int i = b0 + tid;
       const bool in = i < A;
-      const uint32_t key = in ? c3_desc_key(sg[i]) : 0xFFFFFFFFu;
-      const int x = in ? F[i] : 0;
-      const int m = in ? NZ[x] : 0;
+      const int jc = b0 / C3_BIG;   // uniform
+      const uint32_t key = !in ? 0xFFFFFFFFu : jc < 2 ? ck[jc & 1] : c3_desc_key(sg[i]);
+      const int x = !in ? 0 : jc < 2 ? cx[jc & 1] : F[i];
+      const int m = !in ? 0 : jc < 2 ? (int)cw[jc & 1] : NZ[x];
       const bool eq = in && key == prefix;
       int tot;
       const int before = c3_block_scan<C3_BIG>(eq ? m : 0, scan, &tot) + tie_before;
@@ -1273,22 +1290,47 @@ __global__ __launch_bounds__(C3_BIG) void c3_select_update_kernel(
       sNs = 0;
       sNm = 0;
     }
+    // Entries tid and tid + C3_BIG, read once for all rounds: EMA, whether
+    // the node has children, and whether (i, i + 1) is a sibling pair and
+    // its larger EMA (entries past 2 C3_BIG are read again in every round).
+    double cema[2], cpr[2];
+    bool ckid[2], cpair[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = tid + j * C3_BIG;
+      ckid[j] = cpair[j] = false;
+      cema[j] = cpr[j] = 0.0;
+      if (i < A) {
+        const int x = F[i];
+        cema[j] = c3_ema(P, E[i], sg[i]);
+        ckid[j] = NL[x] >= 0;
+        if (i + 1 < A) {
+          const int pp = NP[x];
+          cpair[j] = pp >= 0 && NL[pp] == x && F[i + 1] == x + 1;
+          if (cpair[j]) cpr[j] = fmax(cema[j], c3_ema(P, E[i + 1], sg[i + 1]));
+        }
+      }
+    }
     __syncthreads();
     for (int round = 0; round < R; ++round) {
       double bv = -INFINITY;
       int bi = -1;
       const int ns = sNs;
-      for (int i = tid; i < A; i += C3_BIG) {
-        if (NL[F[i]] < 0) continue;
+      auto consider = [&](int i, bool kid, double e) {
+        if (!kid) return;
         bool chosen = false;
         for (int t = 0; t < ns; ++t) chosen |= sSplit[t] == i;
-        if (chosen) continue;
-        const double e = c3_ema(P, E[i], sg[i]);
+        if (chosen) return;
         if (bi < 0 || e > bv || (e == bv && i < bi)) {
           bv = e;
           bi = i;
         }
-      }
+      };
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (tid + j * C3_BIG < A) consider(tid + j * C3_BIG, ckid[j], cema[j]);
+      for (int i = tid + 2 * C3_BIG; i < A; i += C3_BIG)
+        consider(i, NL[F[i]] >= 0, c3_ema(P, E[i], sg[i]));
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
         const double ov = __shfl_xor(bv, o);
@@ -1322,19 +1364,25 @@ __global__ __launch_bounds__(C3_BIG) void c3_select_update_kernel(
       double bv = INFINITY;
       int bi = -1;
       const int nm = sNm;
-      for (int i = tid; i + 1 < A; i += C3_BIG) {
-        const int x = F[i];
-        const int p = NP[x];
-        if (p < 0 || NL[p] != x || F[i + 1] != x + 1) continue;
+      auto consider = [&](int i, bool pair, double pr) {
+        if (!pair) return;
         bool skip = false;
         for (int t = 0; t < ns; ++t) skip |= sSplit[t] == i || sSplit[t] == i + 1;
         for (int t = 0; t < nm; ++t) skip |= sMerge[t] == i;
-        if (skip) continue;
-        const double pr = fmax(c3_ema(P, E[i], sg[i]), c3_ema(P, E[i + 1], sg[i + 1]));
+        if (skip) return;
         if (bi < 0 || pr < bv || (pr == bv && i < bi)) {
           bv = pr;
           bi = i;
         }
+      };
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (tid + j * C3_BIG + 1 < A) consider(tid + j * C3_BIG, cpair[j], cpr[j]);
+      for (int i = tid + 2 * C3_BIG; i + 1 < A; i += C3_BIG) {
+        const int x = F[i];
+        const int p = NP[x];
+        const bool pair = p >= 0 && NL[p] == x && F[i + 1] == x + 1;
+        consider(i, pair, pair ? fmax(c3_ema(P, E[i], sg[i]), c3_ema(P, E[i + 1], sg[i + 1])) : 0.0);
       }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
