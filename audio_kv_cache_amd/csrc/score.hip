@@ -877,9 +877,10 @@ __global__ __launch_bounds__(KVC_MAX_GW) void kvc_score_tail_kernel(KvcDesc Dsc,
   };
   const E* qg = q + kvc_q_offset(Dsc, seq, l, h);
   const E* ku = k + kvc_kv_offset(Dsc.ks, Dsc, seq, l, h);
-  // The range's key rows into LDS as fp32, a 16-byte piece per thread.
+  // fp32 inputs: the range's key rows into LDS, a 16-byte piece per thread
+  // (the bf16 path reads them as MFMA operands instead).
   constexpr int EP = 16 / (int)sizeof(E), PPR = D / EP;   // elements per piece, pieces per row
-  for (int i = threadIdx.x; i < nk * PPR; i += KVC_MAX_GW) {
+  for (int i = threadIdx.x; sizeof(E) != 2 && i < nk * PPR; i += KVC_MAX_GW) {
     const int j = i / PPR, pc = i - j * PPR;
     const uint4 raw = *reinterpret_cast<const uint4*>(ku + (int64_t)(j0 + j) * Dsc.ks[2] + pc * EP);
     E ev[EP];
@@ -892,7 +893,51 @@ __global__ __launch_bounds__(KVC_MAX_GW) void kvc_score_tail_kernel(KvcDesc Dsc,
   float acc[NK];
 #pragma unroll
   for (int j = 0; j < NK; ++j) acc[j] = 0.f;
-  if (r < gw) {
+  if constexpr (sizeof(E) == 2) {
+    // bf16: the range's logits on v_mfma_f32_16x16x32_bf16, the window
+    // queries as rows (16 per tile; wave w takes tiles w, w + 4, ...) and
+    // the range's keys as the 16 columns, into LDS; then each thread reads
+    // its query's row.  Lane l supplies row/column l % 16 and, at k-step
+    // ks, head dims ks*32 + (l/16)*8 .. +7 of both operands.  Keys past the
+    // range read its first key (their columns are never read back).
+    typedef __bf16 tb_bf16x8 __attribute__((ext_vector_type(8)));
+    typedef float tb_f4 __attribute__((ext_vector_type(4)));
+    constexpr int KS = D / 32;
+    __shared__ float sL[KVC_MAX_GW][NK + 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
+    if (nk > 0) {
+      tb_bf16x8 kb[KS];
+      const E* kr = ku + (int64_t)(j0 + (col < nk ? col : 0)) * Dsc.ks[2] + grp * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(kr + ks * 32);
+        __builtin_memcpy(&kb[ks], &raw, 16);
+      }
+      for (int qt = wave; qt * 16 < gw; qt += KVC_MAX_GW / 64) {
+        const int qr = min(qt * 16 + col, gw - 1);
+        const E* qp = qg + (size_t)qr * D + grp * 8;
+        tb_f4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(qp + ks * 32);
+          tb_bf16x8 qa;
+          __builtin_memcpy(&qa, &raw, 16);
+          t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb[ks], t, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = qt * 16 + grp * 4 + i;
+          if (q < gw) sL[q][col] = t[i];
+        }
+      }
+    }
+    __syncthreads();
+    if (r < gw) {
+#pragma unroll
+      for (int j = 0; j < NK; ++j)
+        if (j < nk) acc[j] = sL[r][j];
+    }
+  } else if (r < gw) {
     // The query row in pieces of 64 elements, each piece's 16-byte loads
     // issued together (the row is 16-byte aligned), then the dot products
     // over the piece in element order.
