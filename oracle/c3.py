@@ -24,16 +24,16 @@ reproduce exactly (readings of the page):
   * a node with more than LEAF = 4 keys splits by 8 Lloyd iterations of
     2-means; depth is capped at MAX_DEPTH = 24;
   * assignment: w = mu1 - mu0 rounded to fp32 and then to 16 significant
-    bits (|w| < 2^-100 -> 0), m = (mu0 + mu1) / 2 rounded to fp32;
-    s(k) = sum_c k_c w_c in fp32 summed in column order, b = the pairwise
-    fp32 sum of the rounded products w_c m_c (adjacent columns, then
-    adjacent pairs, and so on); the key joins cluster 1 iff s(k) > b (the
-    nearest-centroid test written as the side of the bisecting hyperplane;
-    a key on it joins cluster 0).  Every k_c w_c is exact in fp32, so a
-    fused multiply-add gives the same s(k);
+    bits (|w| < 2^-100 -> 0), m = (mu0 + mu1) / 2 rounded to fp32,
+    b = sum_c w_c m_c and s(k) = sum_c k_c w_c in fp32, both summed in
+    column order (each product rounded to fp32, then added to the running
+    sum); the key joins cluster 1 iff s(k) > b (the nearest-centroid test
+    written as the side of the bisecting hyperplane; a key on it joins
+    cluster 0).  Every k_c w_c is exact in fp32, so a fused multiply-add
+    gives the same s(k);
   * a split that leaves a cluster empty at any iteration is abandoned (the
-    node stays a leaf); a mean is the exact member sum times the fp64
-    reciprocal of the count (1/n rounded once, then one rounded product);
+    node stays a leaf); a mean is the exact member sum divided by the
+    count, correctly rounded in fp64 (the plain definition of the mean);
   * "seed 0": the initial centroids are two distinct member keys chosen by
     the SplitMix64 mixing function (Steele, Lea and Flood, "Fast splittable
     pseudorandom number generators", OOPSLA 2014) of (seed, cache, depth,
@@ -126,10 +126,10 @@ def bisector(mu0, mu1):
     w = round16((mu1 - mu0).astype(np.float32))
     w = np.where(np.abs(w) < W_FLUSH, np.float32(0), w).astype(np.float32)
     m = (0.5 * (mu0 + mu1)).astype(np.float32)
-    p = w * m                                        # fp32, each rounded
-    while p.shape[-1] > 1:                           # pairwise: (0+1), (2+3), ...
-        p = p[..., 0::2] + p[..., 1::2]
-    return w, p[..., 0]
+    b = np.zeros(w.shape[:-1], dtype=np.float32)
+    for c in range(w.shape[-1]):                     # column order, fp32
+        b = b + w[..., c] * m[..., c]
+    return w, b
 
 
 def assign(X32, W, b) -> np.ndarray:
@@ -187,8 +187,8 @@ def _level_two_means(Xq, seg, sizes, a0, a1):
             n1 = np.bincount(seg, weights=to1, minlength=len(sizes)).astype(np.int64)
             alive &= (n1 > 0) & (n1 < sizes)
             S1 = np.add.reduceat(Xq * to1[:, None], offs, axis=0)
-            mu1 = np.where(alive[:, None], S1 * (1.0 / n1)[:, None], mu1)
-            mu0 = np.where(alive[:, None], (S - S1) * (1.0 / (sizes - n1))[:, None], mu0)
+            mu1 = np.where(alive[:, None], S1 / n1[:, None], mu1)
+            mu0 = np.where(alive[:, None], (S - S1) / (sizes - n1)[:, None], mu0)
     return alive, to1, mu0, mu1
 
 
@@ -203,7 +203,7 @@ def build_tree(K, cache: int = 0, seed: int = 0) -> Tree:
         z = np.zeros(0, np.int64)
         return Tree(z, z, z, z, z, np.zeros((0, d), np.float32), perm)
     start, size, left, parent, depth = [0], [n], [-1], [-1], [0]
-    means = [Kq.sum(axis=0) * (1.0 / n)]
+    means = [Kq.sum(axis=0) / n]
     lo, hi = 0, 1
     for dep in range(MAX_DEPTH):
         cand = [x for x in range(lo, hi) if size[x] > LEAF]

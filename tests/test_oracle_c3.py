@@ -116,6 +116,55 @@ def test_key_on_the_bisector_joins_cluster_0():
     assert C3.assign(X, np.repeat(w, 3, 0), np.repeat(b, 3, 0)).tolist() == [False, True, False]
 
 
+def test_bisector_offset_is_the_column_order_fp32_sum():
+    # w_0 m_0 = 1 and w_c m_c = 2^-25 for the other 127 columns.  Added to
+    # the running fp32 sum in column order, every 2^-25 is half an ulp of 1
+    # and rounds away (ties to even), so b = 1 exactly; any other order that
+    # first adds small terms together would end above 1.  The exact sum
+    # (rationals) is 1 + 127 * 2^-25, within the fp32 bound of both.
+    d = 128
+    m = np.full(d, 2.0 ** -12)
+    w = np.full(d, 2.0 ** -13)
+    m[0], w[0] = 1.0, 1.0
+    mu0, mu1 = (m - w / 2)[None], (m + w / 2)[None]
+    wq, b = C3.bisector(mu0, mu1)
+    assert np.array_equal(wq[0], w.astype(np.float32))
+    assert float(b[0]) == 1.0
+    exact = Fraction(1) + 127 * Fraction(1, 2 ** 25)
+    assert abs(Fraction(float(b[0])) - exact) <= d * Fraction(1, 2 ** 24) * exact
+    # random means: within the recursive-summation error bound of the exact
+    # sum of the rounded w_c and m_c (a dropped or misindexed term is far
+    # outside it)
+    r = rng(11)
+    for _ in range(20):
+        mu0, mu1 = r.standard_normal((1, d)), r.standard_normal((1, d))
+        wq, b = C3.bisector(mu0, mu1)
+        mf = (0.5 * (mu0 + mu1)).astype(np.float32)[0]
+        terms = [Fraction(float(wq[0, c])) * Fraction(float(mf[c])) for c in range(d)]
+        bound = (d + 1) * Fraction(1, 2 ** 24) * sum(abs(t) for t in terms)
+        assert abs(Fraction(float(b[0])) - sum(terms)) <= bound
+
+
+def test_lloyd_means_are_correctly_rounded_exact_means():
+    # After the iterations, each live node's two means are the exact means
+    # (rationals) of its two clusters' members, rounded once to fp64.
+    r = rng(12)
+    sizes = np.array([37, 61, 9], dtype=np.int64)
+    X = C3.quantize(bf16(r.standard_normal((int(sizes.sum()), 8)) * 3.0))
+    seg = np.repeat(np.arange(3), sizes)
+    alive, to1, mu0, mu1 = C3._level_two_means(X, seg, sizes, np.array([0, 5, 2]),
+                                               np.array([3, 1, 7]))
+    assert alive.all()
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+    for i in range(3):
+        rows = np.arange(offs[i], offs[i] + sizes[i])
+        for mu, sel in ((mu0[i], ~to1[rows]), (mu1[i], to1[rows])):
+            mem = X[rows[sel]]
+            for c in range(8):
+                exact = sum(Fraction(float(v)) for v in mem[:, c]) / len(mem)
+                assert mu[c] == float(exact)
+
+
 # ---------------------------------------------------------------------------
 # tree
 # ---------------------------------------------------------------------------
