@@ -158,9 +158,9 @@ __device__ inline float c3_round16(float x) {
 }
 
 // Hyperplane between two fp64 means for the CPL columns of this lane (lane l
-// owns columns CPL*l ..); returns b on every lane.  b is the pairwise sum of
-// the products: adjacent columns first, then adjacent pairs, and so on,
-// which is the lane order of an xor butterfly.
+// owns columns CPL*l ..); returns b on every lane.  b is the fp32 sum of the
+// rounded products in column order: each lane reads every lane's products
+// in turn and adds them one at a time (all 64 lanes active).
 template <int CPL>
 __device__ inline float c3_bisect(const double* mu0, const double* mu1, float* w) {
   float p[CPL];
@@ -172,10 +172,10 @@ __device__ inline float c3_bisect(const double* mu0, const double* mu1, float* w
     w[i] = wf;
     p[i] = wf * mf;
   }
-  float s = p[0];
-  if constexpr (CPL == 2) s = p[0] + p[1];
+  float s = 0.0f;
+  for (int l = 0; l < 64; ++l)
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) s = s + __shfl_xor(s, o);
+    for (int i = 0; i < CPL; ++i) s = s + __shfl(p[i], l);
   return s;
 }
 
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(C3_T) void c3_root_fin_kernel(C3Desc P, C3Index X, 
   const int u = blockIdx.x, n = c3_n(P, u);
   if (n == 0) return;
   for (int c = threadIdx.x; c < P.d; c += C3_T)
-    X.cent[(size_t)u * P.ncap * P.d + c] = c3_to_bf16(W.rsum[(size_t)u * P.d + c] * (1.0 / (double)n));
+    X.cent[(size_t)u * P.ncap * P.d + c] = c3_to_bf16(W.rsum[(size_t)u * P.d + c] / (double)n);
 }
 
 // ---------------------------------------------------------------------------
@@ -454,9 +454,9 @@ __device__ inline void c3_acc_rows(const unsigned char* sK, int r0, uint64_t lo,
 }
 
 // Hyperplane between two fp64 means for the 8 columns of piece gl (columns
-// 8 gl .. 8 gl + 7); the lanes of one node are LPN consecutive lanes.  b is
-// the pairwise sum of the products (adjacent columns, then adjacent pairs,
-// ...): the first three levels inside the lane, the rest across lanes.
+// 8 gl .. 8 gl + 7); the lanes of one node are LPN consecutive lanes, all
+// active together.  b is the fp32 sum of the rounded products in column
+// order: the node's lanes in turn, each lane's 8 columns in order.
 template <int LPN>
 __device__ inline float c3_bisect8(const double (&mu0)[8], const double (&mu1)[8], float (&w)[8]) {
   float p[8];
@@ -468,9 +468,12 @@ __device__ inline float c3_bisect8(const double (&mu0)[8], const double (&mu1)[8
     w[i] = wf;
     p[i] = wf * mf;
   }
-  float s = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  const int first = (int)(threadIdx.x & 63) & ~(LPN - 1);
+  float s = 0.0f;
 #pragma unroll
-  for (int o = 1; o < LPN; o <<= 1) s = s + __shfl_xor(s, o);
+  for (int j = 0; j < LPN; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = s + __shfl(p[i], first + j);
   return s;
 }
 
@@ -491,7 +494,6 @@ __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Ind
   __shared__ int sPerm[C3_ROWS];
   __shared__ signed char sRowNode[C3_ROWS];
   __shared__ uint64_t sBits[NW], sOld[NW];   // cluster-1 flag of every row, new and previous
-  __shared__ double sInv[C3_MLOC + 1];        // 1 / k, correctly rounded
   __shared__ int sConv[C3_HEADS];             // 1 once the partition stopped changing
   __shared__ int sNh, sLeft[2];
 
@@ -534,7 +536,6 @@ __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Ind
     sDead[tid] = 0;
     sConv[tid] = 0;
   }
-  if (tid >= 1 && tid <= C3_MLOC) sInv[tid] = 1.0 / (double)tid;
   for (int r = tid; r < rows; r += C3_T) {
     int j = -1;
     for (int h = 0; h < nh; ++h)
@@ -651,12 +652,13 @@ __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Ind
         }
         continue;
       }
-      const double i0 = sInv[m - n1], i1 = sInv[n1];
+      // exact member sums divided by the counts, correctly rounded
+      const double n0d = (double)(m - n1), n1d = (double)n1;
       double mu0[8], mu1[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        mu0[i] = (tot[rd][i] - sf[i]) * i0;
-        mu1[i] = sf[i] * i1;
+        mu0[i] = (tot[rd][i] - sf[i]) / n0d;
+        mu1[i] = sf[i] / n1d;
       }
       if (same && gl == 0) sConv[j] = 1;
       if (!same && gl == 0) sLeft[it & 1] = 1;
@@ -902,13 +904,14 @@ __global__ __launch_bounds__(64) void c3_span_fin_kernel(C3Desc P, int par, int 
     }
     return;
   }
-  const double i0 = 1.0 / (double)(m - n1), i1 = 1.0 / (double)n1;
+  // exact member sums divided by the counts, correctly rounded
+  const double n0d = (double)(m - n1), n1d = (double)n1;
   double mu0[CPL], mu1[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const size_t o = (size_t)s * D + lane * CPL + i;
-    mu0[i] = (W.s0[o] - W.s1[o]) * i0;
-    mu1[i] = W.s1[o] * i1;
+    mu0[i] = (W.s0[o] - W.s1[o]) / n0d;
+    mu1[i] = W.s1[o] / n1d;
   }
   // A partition that repeats the previous one is a fixed point: record the
   // split now and stop iterating this node.

@@ -29,11 +29,12 @@
  *
  * Every split decision is defined so that it is reproducible bit for bit:
  * keys snapped to the grid 2^-24 (only |k| < 2^-17 moves), exact fp64
- * member sums, IEEE division for means; assignment by s(k) > b with
- * w = mu1 - mu0 rounded to fp32 then to 16 significant bits (|w| < 2^-100
- * -> 0), s(k) = sum_c k_c w_c in fp32 in column order (exact products, so
- * fused multiply-add changes nothing), b = pairwise (adjacent pairs, then
- * pairs of pairs) fp32 sum of w_c * fp32((mu0_c + mu1_c) / 2); a key with
+ * member sums, each mean = sum / count correctly rounded in fp64;
+ * assignment by s(k) > b with w = mu1 - mu0 rounded to fp32 then to 16
+ * significant bits (|w| < 2^-100 -> 0), s(k) = sum_c k_c w_c in fp32 in
+ * column order (exact products, so fused multiply-add changes nothing),
+ * b = fp32 sum in column order of the rounded products
+ * w_c * fp32((mu0_c + mu1_c) / 2); a key with
  * s(k) = b joins cluster 0 (the left child).  Members keep their relative
  * order.  Stored centroids are the exact means rounded to fp32 then bf16.
  * Nodes are numbered breadth first (children in parent order, left first).
