@@ -86,6 +86,8 @@ class Spec:
     def for_tensors(k, v, *, gqa, seq_lens, retention, n_window=32):
         """Spec for k/v tensors shaped [n_layers, n_kv_heads, T, head_dim]."""
         NL, H, T, d = k.shape
+        if k.dtype not in _DTYPES:
+            raise ValueError(f"k must be bfloat16 or float32, not {k.dtype}")
         dtype = "bf16" if k.dtype == torch.bfloat16 else "f32"
         return Spec(n_layers=NL, n_kv_heads=H, gqa=gqa, head_dim=d, seq_lens=seq_lens,
                     retention=retention, dtype=dtype, n_window=n_window,
@@ -205,15 +207,66 @@ def allocate(spec: Spec, params: Params, device):
     )
 
 
+_DTYPES = (torch.bfloat16, torch.float32)
+
+
+def check_compress_args(q, k, v, head_scores, *, gqa, seq_lens) -> None:
+    """Reject, before anything reaches the library, tensors whose dtype,
+    shape or memory layout the pointers handed to the kernels would not
+    match (the C ABI sees only pointers and strides).  Raises ValueError."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("head_scores", head_scores)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch.Tensor")
+    if k.dtype not in _DTYPES:
+        raise ValueError(f"k must be bfloat16 or float32, not {k.dtype}")
+    if q.dtype != k.dtype or v.dtype != k.dtype:
+        raise ValueError(f"q, k and v must share one dtype (got {q.dtype}, {k.dtype}, {v.dtype})")
+    if k.dim() != 4 or v.dim() != 4 or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must both be [n_layers, n_kv_heads, T, head_dim]")
+    if k.stride(-1) != 1 or v.stride(-1) != 1:
+        raise ValueError("k and v need head_dim contiguous (stride(-1) == 1)")
+    NL, H, T, d = (int(x) for x in k.shape)
+    lens = np.asarray(seq_lens, dtype=np.int64).reshape(-1)
+    if lens.size == 0 or (lens < 0).any() or int(lens.sum()) > T:
+        raise ValueError(f"seq_lens must be >= 0 with sum(seq_lens) <= T = {T}")
+    if q.dim() < 2 or int(q.shape[-1]) != d:
+        raise ValueError("q's last dimension must be head_dim")
+    nwin = int(q.shape[-2])
+    want = lens.size * NL * H * int(gqa) * nwin * d
+    if not q.is_contiguous() or q.numel() != want:
+        raise ValueError(f"q must be contiguous with n_seq*n_layers*n_kv_heads*gqa*n_window*"
+                         f"head_dim = {want} elements")
+    if head_scores.dtype != torch.float32 or not head_scores.is_contiguous() \
+            or head_scores.numel() != NL * H:
+        raise ValueError(f"head_scores must be contiguous float32 [{NL}, {H}]")
+    devs = {t.device for t in (q, k, v, head_scores)}
+    if len(devs) != 1:
+        raise ValueError("q, k, v and head_scores must be on one device")
+
+
 def compress(q, k, v, head_scores, *, gqa, seq_lens, retention, alpha=0.5, rho=0.7,
              window=32, base_ratio=0.5, budget_pool=C.KVC_POOL_SEQUENCE,
              score_pool=C.KVC_SCORE_MEAN, out=None, stream=None):
     """Whole path; returns dict(k_out, v_out, idx, offsets, budgets, workspace)."""
+    check_compress_args(q, k, v, head_scores, gqa=gqa, seq_lens=seq_lens)
     _require_gpu(q, k, v, head_scores)
     spec = Spec.for_tensors(k, v, gqa=gqa, seq_lens=seq_lens, retention=retention,
                             n_window=q.shape[-2])
     params = Params(alpha, rho, window, base_ratio, budget_pool, score_pool)
-    o = out if out is not None else allocate(spec, params, k.device)
+    if out is None:
+        o = allocate(spec, params, k.device)
+    else:
+        o = out
+        rows, ws = kvc_plan(spec, params)
+        need = dict(k_out=(k.dtype, rows * spec.head_dim), v_out=(k.dtype, rows * spec.head_dim),
+                    idx=(torch.int32, rows), offsets=(torch.int64, spec.n_units + 1),
+                    budgets=(torch.int32, spec.n_units), workspace=(torch.uint8, ws))
+        for name, (dt, n) in need.items():
+            t = o.get(name)
+            if not isinstance(t, torch.Tensor) or t.dtype != dt or not t.is_contiguous() \
+                    or t.numel() < n or t.device != k.device:
+                raise ValueError(f"out[{name!r}] must be a contiguous {dt} tensor of at least "
+                                 f"{n} elements on {k.device}")
     kvc_compress(spec, params, q, k, v, head_scores, o["k_out"], o["v_out"], o["idx"],
                  o["offsets"], o["budgets"], o["workspace"], stream)
     return o

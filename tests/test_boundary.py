@@ -338,3 +338,76 @@ def test_wnw_fixed_select_rejects_segment_lengths():
     for seg in (0, 65):
         assert L.kvc_wnw_fixed_select(ctypes.byref(sp.c()), ctypes.byref(api.Params().c()), seg,
                                       fake, fake, fake, fake, None) == C.KVC_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# The torch wrapper's own checks: every rejection happens before any pointer
+# reaches the library (CPU tensors, so no GPU is touched either way).
+# ---------------------------------------------------------------------------
+def _wrapper_inputs(NL=2, H=2, G=2, W=32, d=64, T=256, dt=None):
+    import torch
+    dt = dt or torch.bfloat16
+    q = torch.zeros((1, NL, H * G, W, d), dtype=dt)
+    k = torch.zeros((NL, H, T, d), dtype=dt)
+    v = torch.zeros((NL, H, T, d), dtype=dt)
+    S = torch.zeros((NL, H), dtype=torch.float32)
+    return q, k, v, S
+
+
+@pytest.mark.parametrize("case", [
+    "f16", "mixed", "q_dtype", "kv_shape", "k_stride", "v_stride", "too_long", "q_count",
+    "q_strided", "q_last_dim", "s_dtype", "s_shape", "s_strided"])
+def test_compress_wrapper_rejects_mismatched_tensors(case):
+    import torch
+    q, k, v, S = _wrapper_inputs()
+    lens = [256]
+    msg = None
+    if case == "f16":
+        q, k, v = q.half(), k.half(), v.half()
+        msg = "bfloat16 or float32"
+    elif case == "mixed":
+        v = v.float()
+        msg = "share one dtype"
+    elif case == "q_dtype":
+        q = q.float()
+        msg = "share one dtype"
+    elif case == "kv_shape":
+        v = v[:, :, :128]
+        msg = "n_layers, n_kv_heads, T, head_dim"
+    elif case == "k_stride":
+        k = torch.zeros((2, 2, 64, 256), dtype=torch.bfloat16).transpose(2, 3)
+        msg = "head_dim contiguous"
+    elif case == "v_stride":
+        v = torch.zeros((2, 2, 64, 256), dtype=torch.bfloat16).transpose(2, 3)
+        msg = "head_dim contiguous"
+    elif case == "too_long":
+        lens = [200, 100]
+        msg = "sum(seq_lens)"
+    elif case == "q_count":
+        q = q[:, :1]
+        msg = "elements"
+    elif case == "q_strided":
+        q = torch.zeros((1, 2, 4, 64, 32), dtype=torch.bfloat16).transpose(3, 4)
+        msg = "contiguous"
+    elif case == "q_last_dim":
+        q = torch.zeros((1, 2, 4, 64, 32), dtype=torch.bfloat16)
+        msg = "head_dim"
+    elif case == "s_dtype":
+        S = S.double()
+        msg = "head_scores"
+    elif case == "s_shape":
+        S = torch.zeros((2, 3), dtype=torch.float32)
+        msg = "head_scores"
+    elif case == "s_strided":
+        S = torch.zeros((2, 4), dtype=torch.float32)[:, ::2]
+        msg = "head_scores"
+    with pytest.raises(ValueError, match=re.escape(msg)):
+        api.compress(q, k, v, S, gqa=2, seq_lens=lens, retention=0.6)
+
+
+def test_compress_wrapper_accepts_consistent_cpu_tensors_up_to_the_device_check():
+    # Well-formed tensors pass every layout check and then fail only because
+    # they are not in GPU memory.
+    q, k, v, S = _wrapper_inputs()
+    with pytest.raises(ValueError, match="GPU memory"):
+        api.compress(q, k, v, S, gqa=2, seq_lens=[256], retention=0.6)
