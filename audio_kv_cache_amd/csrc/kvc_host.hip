@@ -222,6 +222,20 @@ static bool check_inputs() {
   return e && e[0] == '1';
 }
 
+// Run an optional check that leaves a flag in device memory the call is
+// about to overwrite anyway (an output of the entry point), wait for it and
+// report KVC_ERR_INVALID_ARG if it was set.
+template <class F>
+static kvc_status run_check(int32_t* flag, hipStream_t s, F launch) {
+  hipError_t e = kvc_launch_check_clear(flag, s);
+  if (e == hipSuccess) e = launch();
+  int32_t bad = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&bad, flag, sizeof(bad), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e);
+  return bad ? KVC_ERR_INVALID_ARG : KVC_OK;
+}
+
 static kvc_status compress_range(const kvc_problem* prob, const kvc_params* params, int lb,
                                  int le, const void* q_window, const void* k, const void* v,
                                  const float* head_scores, void* k_out, void* v_out,
@@ -388,6 +402,13 @@ extern "C" kvc_status kvc_select(const kvc_problem* prob, const kvc_params* para
   if (st != KVC_OK) return st;
   if (!s_hat || !budgets || !seg_offsets || !idx_out) return KVC_ERR_INVALID_ARG;
   if ((uintptr_t)s_hat & 7u) return KVC_ERR_INVALID_ARG;
+  if (check_inputs() && D.row_base[D.n_seq] > 0) {
+    // the flag lives in idx_out, which the selection overwrites
+    st = run_check(idx_out, (hipStream_t)stream, [&] {
+      return kvc_launch_check_select(D, s_hat, budgets, seg_offsets, idx_out, (hipStream_t)stream);
+    });
+    if (st != KVC_OK) return st;
+  }
   return hip_status(for_each_length_group(D, 0, D.upseq, [&](const KvcSeqGroup& g) {
     return kvc_launch_sss_select(D, g, 2, s_hat, nullptr, nullptr, budgets, seg_offsets, idx_out,
                                  nullptr, (hipStream_t)stream);
@@ -418,6 +439,13 @@ extern "C" kvc_status kvc_gather(const kvc_problem* prob, const kvc_params* para
   if (!k || !v || !idx || !seg_offsets || !k_out || !v_out) return KVC_ERR_INVALID_ARG;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out))
     return KVC_ERR_INVALID_ARG;
+  if (check_inputs() && D.row_base[D.n_seq] > 0) {
+    // the flag lives in k_out, which the gather overwrites
+    st = run_check((int32_t*)k_out, (hipStream_t)stream, [&] {
+      return kvc_launch_check_gather(D, idx, seg_offsets, (int32_t*)k_out, (hipStream_t)stream);
+    });
+    if (st != KVC_OK) return st;
+  }
   return hip_status(kvc_launch_gather(D, 0, D.n_units, k, v, idx, seg_offsets, k_out, v_out,
                                       D.row_base[D.n_seq], (hipStream_t)stream));
 }

@@ -107,6 +107,11 @@ hipError_t kvc_launch_wnw_fixed_select(const KvcDesc& D, int seg, const float* s
 hipError_t kvc_launch_check(const KvcDesc& D, int u0, int u1, const void* q, const void* k,
                             const void* v, const float* S, int32_t* flag, hipStream_t st);
 hipError_t kvc_launch_check_clear(int32_t* flag, hipStream_t st);
+// Optional checks of the stage entry points' caller-made inputs.
+hipError_t kvc_launch_check_gather(const KvcDesc& D, const int32_t* idx, const int64_t* off,
+                                   int32_t* flag, hipStream_t st);
+hipError_t kvc_launch_check_select(const KvcDesc& D, const float* s_hat, const int32_t* budgets,
+                                   const int64_t* off, int32_t* flag, hipStream_t st);
 
 // Record a HIP error for kvc_last_hip_error() (calling thread).
 void kvc_note_hip_error(int e);

@@ -175,8 +175,19 @@ kvc_status kvc_compress_layers(const kvc_problem *prob, const kvc_params *params
  *             length is not a power of two; it may be NULL otherwise.
  * kvc_budget: step 3 -> budgets [units], seg_offsets [units+1].
  * kvc_select: step 4 on given rows s_hat with given budgets/offsets ->
- *             idx_out.  s_hat must be finite.
- * kvc_gather: step 5 for given idx/offsets -> k_out, v_out. */
+ *             idx_out.  s_hat must be finite; seg_offsets must be the
+ *             exclusive prefix sum of budgets (seg_offsets[0] = 0) with
+ *             min(window, L) <= budgets[u] <= L.
+ * kvc_gather: step 5 for given idx/offsets -> k_out, v_out.  Every
+ *             position must lie in [0, L) of its unit's sequence and every
+ *             offset in [0, total_rows].  Out-of-range positions are read
+ *             as position 0 (the kernel never reads outside the row), so
+ *             the call returns KVC_OK with wrong rows; bad offsets are
+ *             undefined behaviour.
+ * With KVC_CHECK_INPUTS=1 in the environment, kvc_select and kvc_gather
+ * first check these conditions on the device (positions, offsets, budgets,
+ * finite s_hat), wait on `stream` for the result and return
+ * KVC_ERR_INVALID_ARG, launching nothing else, on a violation. */
 kvc_status kvc_scores(const kvc_problem *prob, const kvc_params *params,
                       const void *q_window, const void *k, float *s,
                       void *workspace, size_t workspace_bytes, void *stream);

@@ -43,3 +43,60 @@ def test_input_checks(monkeypatch, dtype):
         with pytest.raises(C.KvcError) as e:
             _run(D, q_, k_, v_, S_)
         assert e.value.status == C.KVC_ERR_INVALID_ARG, name
+
+
+def _stage_inputs(D):
+    """Budgets, offsets, smoothed rows and kept positions of a small problem
+    from the library's own stage entry points."""
+    spec, prm = D.spec, D.params
+    rows, ws = api.kvc_plan(spec, prm)
+    dev = D.k.device
+    b = torch.empty(spec.n_units, dtype=torch.int32, device=dev)
+    off = torch.empty(spec.n_units + 1, dtype=torch.int64, device=dev)
+    api.kvc_budget(spec, prm, D.S, b, off)
+    work = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+    s = torch.empty(spec.score_rows(), dtype=torch.float32, device=dev)
+    api.kvc_scores(spec, prm, D.q, D.k, s, work)
+    idx = torch.empty(rows, dtype=torch.int32, device=dev)
+    api.kvc_select(spec, prm, s, b, off, idx)
+    return rows, b, off, s, idx
+
+
+def test_stage_checks_reject_bad_positions_offsets_and_budgets(monkeypatch):
+    cfg = P.small(dtype="bf16", n_seq=2, lengths=(256, 1000), retention=(0.5, 0.4))
+    D = Dev(synth.problem(cfg))
+    spec, prm = D.spec, D.params
+    monkeypatch.delenv("KVC_CHECK_INPUTS", raising=False)
+    rows, b, off, s, idx = _stage_inputs(D)
+    d = spec.head_dim
+    ko = torch.empty((rows, d), dtype=D.k.dtype, device=D.k.device)
+    vo = torch.empty_like(ko)
+    api.kvc_gather(spec, prm, D.k, D.v, idx, off, ko, vo)
+    ref_k = ko.clone()
+    monkeypatch.setenv("KVC_CHECK_INPUTS", "1")
+    # valid inputs: same result with the checks on
+    ko.zero_()
+    api.kvc_gather(spec, prm, D.k, D.v, idx, off, ko, vo)
+    assert torch.equal(ko, ref_k)
+    idx2 = torch.empty_like(idx)
+    api.kvc_select(spec, prm, s, b, off, idx2)
+    assert torch.equal(idx2, idx)
+
+    def rejects(fn):
+        with pytest.raises(C.KvcError) as e:
+            fn()
+        assert e.value.status == C.KVC_ERR_INVALID_ARG
+
+    L1 = int(D.hdr.lengths[1])
+    for bad_pos in (-1, L1, 1 << 30):
+        bi = idx.clone()
+        bi[-1] = bad_pos                  # last unit belongs to the sequence of length 1000
+        rejects(lambda: api.kvc_gather(spec, prm, D.k, D.v, bi, off, ko, vo))
+    bo = off.clone(); bo[3] = bo[4] + 1   # a negative segment
+    rejects(lambda: api.kvc_gather(spec, prm, D.k, D.v, idx, bo, ko, vo))
+    bo = off.clone(); bo[-1] = rows + 64  # past the output rows
+    rejects(lambda: api.kvc_gather(spec, prm, D.k, D.v, idx, bo, ko, vo))
+    bb = b.clone(); bb[0] += 1            # budgets no longer match the segments
+    rejects(lambda: api.kvc_select(spec, prm, s, bb, off, idx2))
+    bs = s.clone(); bs[7] = float("nan")
+    rejects(lambda: api.kvc_select(spec, prm, bs, b, off, idx2))
