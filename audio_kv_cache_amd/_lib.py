@@ -26,7 +26,9 @@ KVC_F32 = 1
 
 EXPORTS = ("kvc_plan", "kvc_compress", "kvc_compress_layers", "kvc_scores", "kvc_score_stats",
            "kvc_score_pool", "kvc_smooth", "kvc_budget", "kvc_select", "kvc_gather",
-           "kvc_status_str", "kvc_last_hip_error")
+           "kvc_compress_noalloc", "kvc_status_str", "kvc_last_hip_error")
+# workspace limit of kvc_compress_noalloc (KVC_NOALLOC_MAX_WORKSPACE)
+KVC_NOALLOC_MAX_WORKSPACE = 64 << 20
 # include/kvc_voxzip.h
 VZ_EXPORTS = ("kvc_vz_plan", "kvc_vz_step", "kvc_vz_accumulate", "kvc_vz_evict",
               "kvc_vz_gather")
@@ -164,7 +166,9 @@ def lib():
             L.kvc_budget.argtypes = [prob, prm, _vp, _vp, _vp, _vp]
             L.kvc_select.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp]
             L.kvc_gather.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
-            for name in EXPORTS[:10]:
+            L.kvc_compress_noalloc.argtypes = [prob, prm, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                               _vp, _vp, _vp]
+            for name in EXPORTS[:11]:
                 getattr(L, name).restype = ctypes.c_int
             vp, vq = _P(kvc_vz_problem), _P(kvc_vz_params)
             L.kvc_vz_plan.argtypes = [vp, vq, _P(ctypes.c_int64), _P(ctypes.c_size_t)]

@@ -124,6 +124,16 @@ def kvc_compress(spec, params, q, k, v, head_scores, k_out, v_out, idx_out, seg_
                                  _stream(stream)), "kvc_compress")
 
 
+def kvc_compress_noalloc(spec, params, q, k, v, head_scores, k_out, v_out, idx_out,
+                         seg_offsets, budgets, stream=None):
+    """kvc_compress with the library's static per-device workspace."""
+    C.check(C.lib().kvc_compress_noalloc(ctypes.byref(spec.c()), ctypes.byref(params.c()),
+                                         _ptr(q), _ptr(k), _ptr(v), _ptr(head_scores),
+                                         _ptr(k_out), _ptr(v_out), _ptr(idx_out),
+                                         _ptr(seg_offsets), _ptr(budgets), _stream(stream)),
+            "kvc_compress_noalloc")
+
+
 def kvc_compress_layers(spec, params, layer_begin, layer_end, q, k, v, head_scores, k_out,
                         v_out, idx_out, seg_offsets, budgets, workspace, stream=None):
     """q, k, v hold layers [layer_begin, layer_end) only (k, v with spec's

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "../../include/kvc.h"
 #include "kvc_internal.h"
@@ -331,6 +332,61 @@ extern "C" kvc_status kvc_compress_layers(const kvc_problem* prob, const kvc_par
                                           size_t workspace_bytes, void* stream) {
   return compress_range(prob, params, layer_begin, layer_end, q_window, k, v, head_scores, k_out,
                         v_out, idx_out, seg_offsets, budgets, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// kvc_compress_noalloc: kvc_compress with its workspace in a file-scope
+// device array instead of a caller's buffer.  Each GPU the library runs on
+// holds its own copy of the array (KVC_NOALLOC_MAX_WORKSPACE bytes) from the
+// first call on that device until the process ends; every call on a device
+// shares that device's copy, so calls that overlap on one device race.  The
+// workspace needs no clearing: every step writes what it later reads.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[KVC_NOALLOC_MAX_WORKSPACE];
+
+#define KVC_MAX_DEVICES 64
+static std::atomic<void*> g_scratch_ptr[KVC_MAX_DEVICES];
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (with that device current).  In host code the array's name is
+// only a stand-in for the symbol: kernels get this address instead.
+static hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= KVC_MAX_DEVICES) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+extern "C" kvc_status kvc_compress_noalloc(const kvc_problem* prob, const kvc_params* params,
+                                           const void* q_window, const void* k, const void* v,
+                                           const float* head_scores, void* k_out, void* v_out,
+                                           int32_t* idx_out, int64_t* seg_offsets,
+                                           int32_t* budgets, void* stream) {
+  // Everything that can be rejected on the host is rejected before the
+  // device is touched.
+  KvcDesc D;
+  const kvc_status st = make_desc(prob, params, &D);
+  if (st != KVC_OK) return st;
+  const size_t need = kvc_scores_workspace(D) + up256(score_rows_bytes(D)) + sss_scratch_bytes(D);
+  if (need > (size_t)KVC_NOALLOC_MAX_WORKSPACE) return KVC_ERR_WORKSPACE;
+  if (!q_window || !k || !v || !head_scores || !k_out || !v_out || !idx_out || !seg_offsets ||
+      !budgets)
+    return KVC_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  const hipError_t e = scratch_ptr(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return compress_range(prob, params, 0, prob->n_layers, q_window, k, v, head_scores, k_out,
+                        v_out, idx_out, seg_offsets, budgets, ws,
+                        (size_t)KVC_NOALLOC_MAX_WORKSPACE, stream);
 }
 
 static kvc_status scores_common(const kvc_problem* prob, const kvc_params* params,

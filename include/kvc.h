@@ -165,6 +165,24 @@ kvc_status kvc_compress_layers(const kvc_problem *prob, const kvc_params *params
                                int32_t *budgets, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* kvc_compress for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and arguments without a workspace.  The library
+ * keeps the workspace in a static device array of KVC_NOALLOC_MAX_WORKSPACE
+ * bytes, one copy per GPU, held from the first call on a device (the
+ * current device) until the process ends; the call itself allocates and
+ * frees nothing.  A problem whose kvc_plan workspace_bytes exceeds the
+ * limit returns KVC_ERR_WORKSPACE before touching the device (48 layers x
+ * 4 KV heads at L = 32768 need about 36 MiB).  All calls on one device
+ * share its array: calls that overlap in time on one device (different
+ * streams, or threads) race and must be serialised by the caller. */
+#define KVC_NOALLOC_MAX_WORKSPACE (64u << 20)
+kvc_status kvc_compress_noalloc(const kvc_problem *prob, const kvc_params *params,
+                                const void *q_window, const void *k, const void *v,
+                                const float *head_scores, void *k_out, void *v_out,
+                                int32_t *idx_out, int64_t *seg_offsets,
+                                int32_t *budgets, void *stream);
+
 /* Stage entry points, same conventions; they run the kernels kvc_compress
  * runs, one step at a time.
  *

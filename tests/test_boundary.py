@@ -411,3 +411,21 @@ def test_compress_wrapper_accepts_consistent_cpu_tensors_up_to_the_device_check(
     q, k, v, S = _wrapper_inputs()
     with pytest.raises(ValueError, match="GPU memory"):
         api.compress(q, k, v, S, gqa=2, seq_lens=[256], retention=0.6)
+
+
+def test_noalloc_entry_point_rejects_before_touching_the_device():
+    # A problem whose workspace exceeds the static array, and null pointers,
+    # are refused on the host (dummy pointers are never dereferenced).
+    L = C.lib()
+    big = spec(seq_lens=[65536], retention=0.2)          # about 72 MiB of workspace
+    prm = api.Params()
+    assert api.kvc_plan(big, prm)[1] > C.KVC_NOALLOC_MAX_WORKSPACE
+    fake = ctypes.c_void_p(1 << 20)
+    args = [fake] * 9
+    assert L.kvc_compress_noalloc(ctypes.byref(big.c()), ctypes.byref(prm.c()), *args,
+                                  None) == C.KVC_ERR_WORKSPACE
+    ok = spec(seq_lens=[8192], retention=0.6, n_layers=28, gqa=7)
+    assert api.kvc_plan(ok, prm)[1] <= C.KVC_NOALLOC_MAX_WORKSPACE
+    nulls = [fake] * 8 + [None]
+    assert L.kvc_compress_noalloc(ctypes.byref(ok.c()), ctypes.byref(prm.c()), *nulls,
+                                  None) == C.KVC_ERR_INVALID_ARG
