@@ -111,10 +111,8 @@ static kvc_status make_desc(const kvc_problem* p, const kvc_params* prm, KvcDesc
   int64_t tiles = 0;
   for (int i = 0; i < p->n_seq; ++i) {
     const int64_t L = p->seq_start[i + 1] - p->seq_start[i];
+    // (lengths that are not powers of two take Bluestein's algorithm)
     if (L < KVC_MIN_L || L > KVC_MAX_L) return KVC_ERR_UNSUPPORTED;
-    // Other lengths take Bluestein's algorithm through FFTs of at most 32768
-    // points: up to 32768 for even L, 16384 for odd L.
-    if (!is_pow2(L) && ((L & 1) ? L : L / 2) > 16384) return KVC_ERR_UNSUPPORTED;
     if (L <= prm->window) return KVC_ERR_BUDGET;
     const int64_t kbar = kbar_of(p->retention[i], L);
     if (kbar < L) {

@@ -719,7 +719,7 @@ __host__ inline BluesteinScratch kvc_bluestein_scratch(int Np, int M) {
 __host__ __device__ constexpr int kvc_bluestein_rm(int M) { return M >= 32 * SSS_T ? 16 : 32; }
 
 // e^{i pi m^2 / Np}, the exponent reduced modulo 2 Np in integers first
-// (m < 16384, so m^2 fits 32 bits).
+// (m < 65536, so m^2 fits 32 bits unsigned).
 __device__ __forceinline__ float2 kvc_chirp(int m, int Np) {
   const uint32_t r = ((uint32_t)m * (uint32_t)m) % (uint32_t)(2 * Np);
   return cispi((float)r / (float)Np);
@@ -952,6 +952,317 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_general_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Bluestein sizes M >= 32768: the transforms split across workgroups
+// ---------------------------------------------------------------------------
+// One workgroup cannot hold an M-point transform for M > 32768 (its values
+// in registers and one part in LDS), and at M = 32768 the single-workgroup
+// kernel above runs out of registers.  These lengths (even L > 16384, odd
+// L > 8192, up to 65536) split each M-point FFT into S = M / H transforms of
+// H = 32768 points, by one radix-S step of decimation in frequency for the
+// forward FFT of the premultiplied sequence a and one of decimation in time
+// for the second FFT (W_n = e^{-2 pi i / n}):
+//   FFT_M(a)_{S k + r} = FFT_H(y_r)_k,  y_r[j] = W_M^{j r} sum_q a_{j+qH} W_S^{q r}
+//   FFT_M(P)_m = sum_r W_M^{r m} FFT_H(P_{S k + r})_{m mod H}
+// so the product with FFT_M of the chirp filter is formed in the decimated
+// order in which the first FFT leaves it, which is the order the second one
+// takes.  Kernels per smoothing launch: split (elementwise), sub-FFT with
+// the product, sub-FFT, spectrum (one workgroup per unit: combine, real
+// bins, fp64 energies, k*, mask, back to the inverse's split), sub-FFT with
+// the product, sub-FFT, finish (combine, blend, selection).  Sub-FFTs are
+// one 1024-thread workgroup each (Stockham passes, 32 values per thread),
+// in place in global scratch.
+#define KVC_BIG_LOGH 15
+#define KVC_BIG_H (1 << KVC_BIG_LOGH)
+
+// Scratch of a long-length launch, in float2 units: FFT_M of the chirp
+// filter in decimated order (sub-transform r's bins at r H ..), the chirp
+// table conj(w_n) (n < Np), then per unit: the M sub-sequence values, the
+// Np-bin spectrum (also the smoothed row's staging area) and the L/2 + 1
+// real bins.
+struct BigScratch {
+  size_t cw_off, rows_off, ustride;
+};
+__host__ __device__ inline BigScratch kvc_big_scratch(int Np, int M) {
+  auto up32 = [](size_t x) { return (x + 31) & ~size_t(31); };
+  BigScratch b;
+  b.cw_off = up32((size_t)M);
+  b.rows_off = b.cw_off + up32((size_t)Np);
+  b.ustride = up32((size_t)M + 2 * (size_t)Np + 2);
+  return b;
+}
+
+// e^{-2 pi i f} for f = x / M given as an integer x (any sign), exact
+// revolutions after reduction modulo M (M a power of two).
+__device__ __forceinline__ float2 kvc_twiddle(int x, int M) {
+  const float f = (float)(x & (M - 1)) / (float)M;
+  return make_float2(__builtin_amdgcn_cosf(f), -__builtin_amdgcn_sinf(f));
+}
+
+// v * W_S^e for S in {1, 2, 4}: multiples of a quarter turn, exact.
+__device__ __forceinline__ float2 kvc_quarter(float2 v, int e, int S) {
+  const int qt = (e * (4 / S)) & 3;  // quarter turns clockwise
+  return qt == 0 ? v : qt == 1 ? make_float2(v.y, -v.x) : qt == 2 ? make_float2(-v.x, -v.y)
+                                                                    : make_float2(-v.y, v.x);
+}
+
+// Value n of the premultiplied sequence of the first forward transform:
+// a_n = in(n) conj(w_n), in(n) = (s_2n, s_2n+1) for even L, (s_n, 0) for odd.
+__device__ __forceinline__ float2 kvc_big_in(const float* srow, bool even, int n, float2 c) {
+  const float2 x = even ? make_float2(srow[2 * n], srow[2 * n + 1]) : make_float2(srow[n], 0.f);
+  return cmul(x, c);
+}
+
+// The radix-S split y_r[j] (r < S) of a length-M sequence given by `val`
+// (val(n) for n < M), written to Y[r H + j].
+template <int S, class F>
+__device__ __forceinline__ void kvc_big_split(float2* __restrict__ Y, int j, int M, F val) {
+  float2 a[S];
+#pragma unroll
+  for (int q = 0; q < S; ++q) a[q] = val(j + q * KVC_BIG_H);
+#pragma unroll
+  for (int r = 0; r < S; ++r) {
+    float2 y = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+      const float2 v = kvc_quarter(a[q], q * r, S);
+      y = make_float2(y.x + v.x, y.y + v.y);
+    }
+    Y[(size_t)r * KVC_BIG_H + j] = r == 0 ? y : cmul(y, kvc_twiddle(j * r, M));
+  }
+}
+
+// sum_r W_M^{r m} E_r[m mod H]: bin m of the M-point FFT from the
+// sub-transforms' outputs.
+template <int S>
+__device__ __forceinline__ float2 kvc_big_combine(const float2* __restrict__ Y, int m, int M) {
+  const int k = m & (KVC_BIG_H - 1);
+  float2 q = Y[k];
+#pragma unroll
+  for (int r = 1; r < S; ++r) {
+    const float2 v = cmul(Y[(size_t)r * KVC_BIG_H + k], kvc_twiddle(r * m, M));
+    q = make_float2(q.x + v.x, q.y + v.y);
+  }
+  return q;
+}
+
+// Split of the chirp filter (b_m = w_m for m < Np, b_{M-m} = w_m for
+// 0 < m < Np, zero between) into the bhat region, and the table
+// cw[n] = conj(w_n); or, per unit, of the first premultiplied sequence.
+// grid (H / 256, units or 1), 256 threads.
+template <int S>
+__global__ __launch_bounds__(256) void kvc_big_split_kernel(KvcDesc D, KvcSeqGroup G, int chirp,
+                                                            int Np, const float* __restrict__ s_in,
+                                                            float2* __restrict__ base) {
+  constexpr int M = S * KVC_BIG_H;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  const BigScratch bs = kvc_big_scratch(Np, M);
+  float2* cw = base + bs.cw_off;
+  if (chirp) {
+    for (int n = j; n < Np; n += KVC_BIG_H) cw[n] = conjf2(kvc_chirp(n, Np));
+    kvc_big_split<S>(base, j, M, [&](int m) {
+      const int mm = m < Np ? m : (M - m < Np ? M - m : -1);
+      return mm >= 0 ? kvc_chirp(mm, Np) : make_float2(0.f, 0.f);
+    });
+    return;
+  }
+  const int u = kvc_group_unit(G, D.upseq, (int)blockIdx.y);
+  const int seq = u / D.upseq, within = u - seq * D.upseq;
+  const int L = D.L[seq];
+  const float* srow = s_in + D.srow_base[seq] + (int64_t)within * L;
+  const bool even = (L & 1) == 0;
+  float2* Y = base + bs.rows_off + (size_t)blockIdx.y * bs.ustride;
+  kvc_big_split<S>(Y, j, M, [&](int n) {
+    return n < Np ? kvc_big_in(srow, even, n, conjf2(kvc_chirp(n, Np))) : make_float2(0.f, 0.f);
+  });
+}
+
+// One H-point FFT in place: sub-sequence (blockIdx.x % S) of slot
+// (blockIdx.x / S), i.e. first + slot * ustride + r * H.  POST: multiply bin
+// k by bhat[r H + k] and conjugate (the product of the convolution, ready
+// for the second FFT).
+template <int S, bool POST>
+__global__ __launch_bounds__(SSS_T) void kvc_big_fft_kernel(float2* __restrict__ first,
+                                                            size_t ustride,
+                                                            const float2* __restrict__ bhat) {
+  constexpr int N = KVC_BIG_H, V = 32, T = N / V, RM = 16;
+  constexpr int R0 = fft_radix(N, V, 1, RM);
+  static_assert(T == SSS_T, "one value slot set per thread");
+  __shared__ __attribute__((aligned(16))) float lds[Xbuf<N>::kFloats];
+  const int r = (int)blockIdx.x % S;
+  float2* y = first + (size_t)(blockIdx.x / S) * ustride + (size_t)r * N;
+  const int t = threadIdx.x;
+  float re[V], im[V];
+#pragma unroll
+  for (int s = 0; s < V; ++s) {
+    const float2 v = y[in_index<R0, T, N>(s, t)];
+    re[s] = v.x;
+    im[s] = v.y;
+  }
+  Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
+  fft_stages<N, V, 1, RM>(re, im, lds, t, true, [&](int s) { return t * V + s; }, none);
+  // (every value of y was read before the first exchange's barrier)
+  float4* o = reinterpret_cast<float4*>(y + t * V);
+#pragma unroll
+  for (int s = 0; s < V; s += 2) {
+    float2 a = make_float2(re[s], im[s]), b = make_float2(re[s + 1], im[s + 1]);
+    if constexpr (POST) {
+      a = conjf2(cmul(a, bhat[(size_t)r * N + t * V + s]));
+      b = conjf2(cmul(b, bhat[(size_t)r * N + t * V + s + 1]));
+    }
+    o[s / 2] = make_float4(a.x, a.y, b.x, b.y);
+  }
+}
+
+// Per unit, after the first convolution: the spectrum X_k (k < Np), the real
+// bins F_0 .. F_{L/2} with their fp64 energies, k*, the masked spectrum
+// merged back to the complex sequence, conjugated and premultiplied for the
+// inverse transform, and its split.  One 1024-thread workgroup per unit.
+template <int S>
+__global__ __launch_bounds__(SSS_T) void kvc_big_spectrum_kernel(KvcDesc D, int mode,
+                                                                 KvcSeqGroup G, int Np,
+                                                                 float2* __restrict__ base,
+                                                                 int32_t* __restrict__ kstar_out) {
+  constexpr int M = S * KVC_BIG_H;
+  __shared__ SssShared sh;
+  const int u = kvc_group_unit(G, D.upseq, (int)blockIdx.x);
+  const int seq = u / D.upseq;
+  const int L = D.L[seq];
+  const bool even = (L & 1) == 0;
+  const int t = threadIdx.x;
+  const BigScratch bs = kvc_big_scratch(Np, M);
+  const float2* cw = base + bs.cw_off;
+  float2* Y = base + bs.rows_off + (size_t)blockIdx.x * bs.ustride;
+  float2* X = Y + M;
+  float2* Fb = X + Np;
+  const float invM = 1.0f / (float)M;
+  for (int k = t; k < Np; k += SSS_T) {
+    const float2 q = kvc_big_combine<S>(Y, k, M);
+    X[k] = cmul(cw[k], make_float2(q.x * invM, -q.y * invM));
+  }
+  if (t == 0) sh.kstar = L / 2;  // the last bin, should rounding leave E short of rho E(L/2)
+  __syncthreads();
+  // Real bins (unpacked for even L) and their energies in fp64, in
+  // contiguous chunks per thread so that a block scan gives the prefixes.
+  const int nb = L / 2 + 1;
+  const int per = (nb + SSS_T - 1) / SSS_T;
+  const int k0 = min(nb, t * per), k1 = min(nb, k0 + per);
+  double esum = 0.0;
+  for (int kk = k0; kk < k1; ++kk) {
+    float2 F;
+    if (even) {
+      const float2 zk = X[kk % Np], zm = X[(Np - kk % Np) % Np];
+      const float2 A = make_float2(0.5f * (zk.x + zm.x), 0.5f * (zk.y - zm.y));
+      const float2 B = make_float2(0.5f * (zk.y + zm.y), -0.5f * (zk.x - zm.x));
+      const float2 WB = cmul(cispi(-2.0f * (float)kk / (float)L), B);
+      F = make_float2(A.x + WB.x, A.y + WB.y);
+    } else {
+      F = X[kk];
+    }
+    Fb[kk] = F;
+    esum += (double)F.x * F.x + (double)F.y * F.y;
+  }
+  double total;
+  const double before = block_scan<double>(esum, sh.sd, &total);
+  const double target = (double)D.rho * total;
+  {
+    double e = before;
+    int cand = L;
+    for (int kk = k0; kk < k1; ++kk) {
+      const float2 F = Fb[kk];
+      e += (double)F.x * F.x + (double)F.y * F.y;
+      if (e >= target && cand == L) cand = kk;
+    }
+    if (cand < L) atomicMin(&sh.kstar, cand);
+  }
+  __syncthreads();
+  const int kstar = sh.kstar;
+  if ((mode & 4) && t == 0) kstar_out[u] = kstar;
+  // Masked spectrum merged back to the complex sequence z the inverse
+  // transforms (as conj(DFT(conj z)) / Np), premultiplied by conj(w_n).
+  auto Fm = [&](int kk) { return kk <= kstar ? Fb[kk] : make_float2(0.f, 0.f); };
+  const float2* cwr = cw;
+  for (int j = t; j < KVC_BIG_H; j += SSS_T) {
+    kvc_big_split<S>(Y, j, M, [&](int n) {
+      if (n >= Np) return make_float2(0.f, 0.f);
+      float2 z;
+      if (even) {
+        const float2 Fk = Fm(n), Fr = Fm(Np - n);
+        const float2 A = make_float2(0.5f * (Fk.x + Fr.x), 0.5f * (Fk.y - Fr.y));
+        const float2 Dd = make_float2(0.5f * (Fk.x - Fr.x), 0.5f * (Fk.y + Fr.y));
+        const float2 B = cmul(cispi(2.0f * (float)n / (float)L), Dd);
+        z = make_float2(A.x - B.y, A.y + B.x);
+      } else {
+        z = n <= (L - 1) / 2 ? Fm(n) : conjf2(Fm(L - n));
+      }
+      return cmul(conjf2(z), cwr[n]);
+    });
+  }
+}
+
+// Per unit, after the second convolution: the low-pass row
+// lp = conj(conj(w_m) conj(sum_r ...) / M) / Np, the blend with the raw row,
+// and the selection on it.  mode without bit 0: selection on s_in as given.
+template <int S, int VS>
+__global__ __launch_bounds__(SSS_T) void kvc_big_finish_kernel(
+    KvcDesc D, int mode, KvcSeqGroup G, int Np, const float* __restrict__ s_in,
+    float* __restrict__ s_hat_out, const int32_t* __restrict__ budgets,
+    const int64_t* __restrict__ offsets, int32_t* __restrict__ idx_out,
+    float2* __restrict__ base) {
+  constexpr int M = S * KVC_BIG_H;
+  constexpr int kStage = 32768;
+  static_assert(2 * VS * SSS_T >= 32768, "selection layout covers the row");
+  __shared__ int stage[kStage];
+  __shared__ SssShared sh;
+  const int u = kvc_group_unit(G, D.upseq, (int)blockIdx.x);
+  const int seq = u / D.upseq, within = u - seq * D.upseq;
+  const int L = D.L[seq];
+  const int64_t row = D.srow_base[seq] + (int64_t)within * L;
+  const float* srow = s_in + row;
+  const bool even = (L & 1) == 0;
+  const int t = threadIdx.x;
+  float kr[VS], ki[VS];
+  const float* src = srow;
+  if (mode & 1) {
+    const BigScratch bs = kvc_big_scratch(Np, M);
+    const float2* cw = base + bs.cw_off;
+    const float2* Y = base + bs.rows_off + (size_t)blockIdx.x * bs.ustride;
+    float* hs = reinterpret_cast<float*>(base + bs.rows_off + (size_t)blockIdx.x * bs.ustride + M);
+    float* hrow = (mode & 4) ? s_hat_out + row : nullptr;
+    const float invM = 1.0f / (float)M, invNp = 1.0f / (float)Np;
+    const float a = D.alpha, oma = 1.0f - D.alpha;
+    for (int m = t; m < Np; m += SSS_T) {
+      const float2 q = kvc_big_combine<S>(Y, m, M);
+      const float2 x = cmul(cw[m], make_float2(q.x * invM, -q.y * invM));
+      const float lre = x.x * invNp, lim = -x.y * invNp;
+      if (even) {
+        const float h0 = oma * srow[2 * m] + a * lre, h1 = oma * srow[2 * m + 1] + a * lim;
+        hs[2 * m] = h0;
+        hs[2 * m + 1] = h1;
+        if (hrow) {
+          hrow[2 * m] = h0;
+          hrow[2 * m + 1] = h1;
+        }
+      } else {
+        const float h = oma * srow[m] + a * lre;
+        hs[m] = h;
+        if (hrow) hrow[m] = h;
+      }
+    }
+    if (!(mode & 2)) return;
+    __syncthreads();
+    src = hs;
+  }
+#pragma unroll
+  for (int s = 0; s < VS; ++s) {
+    const int p = 2 * VS * t + 2 * s;
+    kr[s] = p < L ? src[p] : 0.f;
+    ki[s] = p + 1 < L ? src[p + 1] : 0.f;
+  }
+  __syncthreads();
+  select_unit<VS>(D, u, L, kr, ki, budgets, offsets, idx_out, sh, stage, kStage, t, true);
+}
+
 static int kvc_bluestein_logm(int L) {
   const int Np = (L & 1) ? L : L / 2;
   int logm = 0;
@@ -959,12 +1270,54 @@ static int kvc_bluestein_logm(int L) {
   return logm;
 }
 
-// Scratch for lengths that are not powers of two (see BluesteinScratch).
+// Scratch for lengths that are not powers of two (BluesteinScratch, or
+// BigScratch from M = 32768 on).
 size_t kvc_sss_scratch_bytes(int L, int units) {
   if ((L & (L - 1)) == 0) return 0;
   const int Np = (L & 1) ? L : L / 2;
-  const BluesteinScratch b = kvc_bluestein_scratch(Np, 1 << kvc_bluestein_logm(L));
+  const int logm = kvc_bluestein_logm(L);
+  if (logm >= KVC_BIG_LOGH) {
+    const BigScratch b = kvc_big_scratch(Np, 1 << logm);
+    return sizeof(float2) * (b.rows_off + b.ustride * (size_t)units);
+  }
+  const BluesteinScratch b = kvc_bluestein_scratch(Np, 1 << logm);
   return b.rows_off + b.bytes_per_unit * (size_t)units;
+}
+
+template <int S>
+static hipError_t launch_big(const KvcDesc& D, const KvcSeqGroup& g, int nwg, int mode, int Np,
+                             const float* s_in, float* s_hat_out, int32_t* kstar_out,
+                             const int32_t* budgets, const int64_t* offsets, int32_t* idx_out,
+                             float2* base, hipStream_t st) {
+  constexpr int M = S * KVC_BIG_H;
+  if (nwg > 65535) return hipErrorInvalidConfiguration;  // (grid y of the split)
+  const BigScratch b = kvc_big_scratch(Np, M);
+  float2* rows = base + b.rows_off;
+  if (mode & 1) {
+    const dim3 sg(KVC_BIG_H / 256, 1);
+    hipLaunchKernelGGL(kvc_big_split_kernel<S>, sg, dim3(256), 0, st, D, g, 1, Np, s_in, base);
+    hipLaunchKernelGGL((kvc_big_fft_kernel<S, false>), dim3(S), dim3(SSS_T), 0, st, base,
+                       (size_t)0, (const float2*)nullptr);
+    hipLaunchKernelGGL(kvc_big_split_kernel<S>, dim3(KVC_BIG_H / 256, nwg), dim3(256), 0, st, D,
+                       g, 0, Np, s_in, base);
+    hipLaunchKernelGGL((kvc_big_fft_kernel<S, true>), dim3(nwg * S), dim3(SSS_T), 0, st, rows,
+                       b.ustride, (const float2*)base);
+    hipLaunchKernelGGL((kvc_big_fft_kernel<S, false>), dim3(nwg * S), dim3(SSS_T), 0, st, rows,
+                       b.ustride, (const float2*)nullptr);
+    hipLaunchKernelGGL(kvc_big_spectrum_kernel<S>, dim3(nwg), dim3(SSS_T), 0, st, D, mode, g, Np,
+                       base, kstar_out);
+    hipLaunchKernelGGL((kvc_big_fft_kernel<S, true>), dim3(nwg * S), dim3(SSS_T), 0, st, rows,
+                       b.ustride, (const float2*)base);
+    hipLaunchKernelGGL((kvc_big_fft_kernel<S, false>), dim3(nwg * S), dim3(SSS_T), 0, st, rows,
+                       b.ustride, (const float2*)nullptr);
+  }
+  if (D.L[g.seq[0]] > 32768)
+    hipLaunchKernelGGL((kvc_big_finish_kernel<S, 32>), dim3(nwg), dim3(SSS_T), 0, st, D, mode, g,
+                       Np, s_in, s_hat_out, budgets, offsets, idx_out, base);
+  else
+    hipLaunchKernelGGL((kvc_big_finish_kernel<S, 16>), dim3(nwg), dim3(SSS_T), 0, st, D, mode, g,
+                       Np, s_in, s_hat_out, budgets, offsets, idx_out, base);
+  return hipGetLastError();
 }
 
 // Units [u0, u1) must lie in one sequence.
@@ -979,6 +1332,21 @@ hipError_t kvc_launch_sss_select(const KvcDesc& D, const KvcSeqGroup& g, int mod
     if (!scratch && (mode & 1)) return hipErrorInvalidValue;
     const int Np = (L & 1) ? L : L / 2;
     const int logm = kvc_bluestein_logm(L);
+    if (logm >= KVC_BIG_LOGH) {
+      float2* base = (float2*)scratch;
+      switch (logm) {
+        case KVC_BIG_LOGH:
+          return launch_big<1>(D, g, nwg, mode, Np, s_in, s_hat_out, kstar_out, budgets, offsets,
+                               idx_out, base, st);
+        case KVC_BIG_LOGH + 1:
+          return launch_big<2>(D, g, nwg, mode, Np, s_in, s_hat_out, kstar_out, budgets, offsets,
+                               idx_out, base, st);
+        case KVC_BIG_LOGH + 2:
+          return launch_big<4>(D, g, nwg, mode, Np, s_in, s_hat_out, kstar_out, budgets, offsets,
+                               idx_out, base, st);
+        default: return hipErrorInvalidValue;
+      }
+    }
     const BluesteinScratch b = kvc_bluestein_scratch(Np, 1 << logm);
     char* base = (char*)scratch;
     float2* bhat = scratch ? (float2*)base : nullptr;
@@ -990,7 +1358,7 @@ hipError_t kvc_launch_sss_select(const KvcDesc& D, const KvcSeqGroup& g, int mod
     switch (logm) {
 #define KVC_GEN(LM) case LM: chirp = kvc_sss_chirp_kernel<LM>; kern = kvc_sss_general_kernel<LM>; break;
       KVC_GEN(7) KVC_GEN(8) KVC_GEN(9) KVC_GEN(10) KVC_GEN(11) KVC_GEN(12) KVC_GEN(13)
-      KVC_GEN(14) KVC_GEN(15)
+      KVC_GEN(14)
 #undef KVC_GEN
       default: return hipErrorInvalidValue;
     }

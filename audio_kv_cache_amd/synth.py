@@ -78,6 +78,9 @@ CONFIGS = {
     # mixed lengths, none a power of two, odd and even
     "ragged_npot": Config("ragged_npot", 6, 3, 4, 2, 4, 128, "bf16",
                           lengths=(3000, 12345, 777), retention=(0.5, 0.3, 0.8)),
+    # long-form audio of an odd length between 32K and 64K tokens
+    "long_npot": Config("long_npot", 7, 1, 48, 4, 8, 128, "bf16",
+                        lengths=(49999,), retention=(0.2,)),
 }
 
 

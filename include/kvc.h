@@ -96,12 +96,12 @@ typedef enum { KVC_POOL_SEQUENCE = 0, KVC_POOL_LAYER = 1 } kvc_pool;
 
 /* Problem shape.  Supported: 1 <= n_seq <= 64; head_dim in {64, 128};
  * gqa_group * n_window_q a multiple of 32 and at most 256; every sequence
- * length L with 64 <= L <= 65536 and L > window, and, when L is not a power
- * of two, L <= 32768 (even) or L <= 16384 (odd): such lengths take the
- * transform of step 2 through Bluestein's algorithm (the chirp-z form of
- * the DFT of length L, or of the L/2 packed values for even L, as a
- * convolution done with power-of-two FFTs of at most 32768 points);
- * n_layers * n_kv_heads <= 4096; k_stride[2] < 2^24. */
+ * length L with 64 <= L <= 65536 and L > window.  Lengths that are not
+ * powers of two take the transform of step 2 through Bluestein's algorithm
+ * (the chirp-z form of the DFT of length L, or of the L/2 packed values for
+ * even L, as a convolution done with power-of-two FFTs: in one workgroup
+ * up to 16384 points, beyond that split into transforms of 32768 points
+ * across workgroups); n_layers * n_kv_heads <= 4096; k_stride[2] < 2^24. */
 typedef struct {
   int32_t n_seq, n_layers, n_kv_heads, gqa_group, head_dim, n_window_q;
   kvc_dtype dtype;            /* element type of q, k, v, k_out, v_out     */

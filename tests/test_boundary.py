@@ -81,8 +81,7 @@ def status(sp, prm=None, **ptrs):
 
 
 def test_invalid_problems_rejected_before_launch():
-    assert status(spec(seq_lens=[32770])) == C.KVC_ERR_UNSUPPORTED         # even, not 2^k, > 32768
-    assert status(spec(seq_lens=[16385])) == C.KVC_ERR_UNSUPPORTED         # odd, > 16384
+    assert status(spec(seq_lens=[65537])) == C.KVC_ERR_UNSUPPORTED         # too long
     assert status(spec(seq_lens=[131072])) == C.KVC_ERR_UNSUPPORTED        # too long
     assert status(spec(seq_lens=[32])) == C.KVC_ERR_UNSUPPORTED            # too short
     assert status(spec(head_dim=96)) == C.KVC_ERR_UNSUPPORTED
@@ -109,13 +108,18 @@ def test_invalid_problems_rejected_before_launch():
 
 def test_lengths_that_are_not_powers_of_two():
     # Bluestein's algorithm takes the transform for these; the workspace
-    # grows by the chirp spectrum and two complex rows per unit.
-    for L in (3000, 2047, 32768 - 2, 16383, 100):
+    # grows by the chirp spectrum and two complex rows per unit, and from a
+    # Bluestein size M of 32768 on (even L > 16384, odd L > 8192) by the M
+    # values of the split transforms per unit.
+    for L in (3000, 2047, 32768 - 2, 16383, 100, 16385, 32767, 32770, 49999, 65534, 65535):
         sp = spec(seq_lens=[L], retention=0.9)
         rows, ws = api.kvc_plan(sp, api.Params())
         assert rows == 48 * 4 * math.floor(0.9 * L)
         n_p = L // 2 if L % 2 == 0 else L
         assert ws >= 4 * 48 * 4 * L + 16 * n_p * 48 * 4
+        M = 1 << (2 * n_p - 2).bit_length()
+        if M >= 32768:
+            assert ws >= 4 * 48 * 4 * L + 8 * (M + 2 * n_p) * 48 * 4
     sp = spec(seq_lens=[4096], retention=0.9)
     rows, ws4096 = api.kvc_plan(sp, api.Params())
     assert ws4096 < 4 * 48 * 4 * 4096 + 16 * 2048 * 48 * 4   # powers of two need no scratch

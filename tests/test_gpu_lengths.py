@@ -9,6 +9,8 @@ s and s_hat, k* equal or inside the ambiguity band, selection bit-exact on
 identical rows, end-to-end kept sets equal except within tolerance of the
 threshold, budgets and gathered rows bit-exact.
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 
@@ -22,7 +24,7 @@ from tests.gpu_helpers import Dev, check_smoothed_row  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("L", [65, 100, 1000, 3001, 12345, 30000, 32766])
+@pytest.mark.parametrize("L", [65, 100, 1000, 3001, 12345, 30000, 32766, 40000, 49999, 65535])
 def test_select_any_length(L):
     P.say(f"[select] L={L}")
     H = 4
@@ -61,16 +63,23 @@ def test_smooth_any_length(L, dtype):
         assert P.rel_err(sh[3 * L:4 * L], rows[3]) <= 1e-5
 
 
-@pytest.mark.parametrize("L", [30000, 32766])
+# Bluestein sizes M = 32768 (one sub-transform), 65536 (two) and 131072 (four).
+@pytest.mark.parametrize("L", [16385, 20000, 30000, 32766, 32767, 40000, 49999, 65534, 65535])
 def test_smooth_long_lengths(L):
     P.say(f"[smooth] L={L}")
-    cfg = P.small(n_layers=1, n_kv_heads=2, lengths=(L,), dtype="bf16", alpha=0.6, rho=0.7,
+    cfg = P.small(n_layers=1, n_kv_heads=4, lengths=(L,), dtype="bf16", alpha=0.6, rho=0.7,
                   retention=(0.9,), base_ratio=0.0)
     D = Dev(synth.problem(cfg))
-    rows = P._sss_rows(L, 2, np.random.default_rng(L))
+    rows = P._sss_rows(L, 4, np.random.default_rng(L))
     sh, ks = D.smooth(np.concatenate(rows))
-    for h in range(2):
-        check_smoothed_row(rows[h], sh[h * L:(h + 1) * L], int(ks[h]), 0.6, 0.7, "bf16")
+    # (the oracle's direct DFT takes seconds per row at these lengths; rows
+    # in parallel, ctypes releases the interpreter lock)
+    with ThreadPoolExecutor(4) as ex:
+        errs = list(ex.map(lambda h: check_smoothed_row(rows[h], sh[h * L:(h + 1) * L],
+                                                        int(ks[h]), 0.6, 0.7, "bf16"), range(4)))
+    P.say(f"    k* {ks.tolist()}, s_hat errors {[f'{e[0]:.1e}' for e in errs]}")
+    assert int(ks[3]) == 0            # constant row: only the DC bin
+    assert P.rel_err(sh[3 * L:4 * L], rows[3]) <= 1e-5
 
 
 @pytest.mark.parametrize("dtype,d,gqa", [("bf16", 128, 8), ("bf16", 64, 2), ("f32", 64, 2),
@@ -100,6 +109,22 @@ def test_compress_omni30b_30000_sampled():
     P.say("[e2e] omni30b_30000")
     D = P.dev("omni30b_30000")
     P._check_e2e(D, [(0, 0, 0), (0, 23, 2), (0, 47, 3)])
+
+
+def test_compress_long_npot_sampled():
+    # 48 layers x 4 KV heads at an odd length of 49999 keys (Bluestein size
+    # 131072: four sub-transforms): s and s_hat element by element on sampled
+    # units in the launch configuration of the whole call, then end to end.
+    P.say("[e2e] long_npot")
+    D = P.dev("long_npot")
+    units = [(0, 0, 0), (0, 47, 3)]
+    s = P._check_scores(D, units)
+    sh, ks = D.smooth(s)
+    for (i, l, h) in units:
+        u = D.uindex(i, l, h)
+        check_smoothed_row(D.row(s, i, l, h), D.row(sh, i, l, h), int(ks[u]), D.cfg.alpha,
+                           D.cfg.rho, D.dtype)
+    P._check_e2e(D, units)
 
 
 def test_compress_ragged_npot_layer_pool():
