@@ -170,7 +170,7 @@ static hipError_t for_each_length_group(const KvcDesc& D, int lo, int hi, F f) {
 
 static size_t sss_scratch_bytes(const KvcDesc& D) {
   size_t m = 0;
-  for_each_length_group(D, 0, D.upseq, [&](const KvcSeqGroup& g) {
+  (void)for_each_length_group(D, 0, D.upseq, [&](const KvcSeqGroup& g) {
     m = std::max(m, kvc_sss_scratch_bytes(D.L[g.seq[0]], g.n * D.upseq));
     return hipSuccess;
   });

@@ -95,29 +95,60 @@ def committed_traffic(kernel_file: str, kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, hdr, prob_units, budgets, max_units=8):
-    """The fp64 oracle, as it stands, on a bounded sample of units."""
+    """The fp64 oracle, as it stands, on a bounded sample of units: the
+    first max_units units of sequence 0 (layer 0's KV heads, then layer 1's)
+    on a thread pool of min(max_units, usable cores) threads, and the first
+    unit alone on one thread.  BLAS inside the oracle is held to one thread
+    so the pool size is the number of cores used."""
     from oracle import oracle as O
     from audio_kv_cache_amd import synth
-    cores = min(max_units, O.threads())
-    units = prob_units[:max_units]
+    import concurrent.futures as cf
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    affinity = O.threads()
+    units = [x for x in prob_units if x[0] == 0][:max_units]
+    cores = min(len(units), affinity)
     # regenerate only the sampled units (each is seeded on its own)
     inputs = [synth.unit(cfg, hdr, i, l, h) for (i, l, h) in units]
-    import concurrent.futures as cf
 
     def run(j):
         (i, l, h), (qu, ku, _) = units[j], inputs[j]
         u = (i * cfg.n_layers + l) * cfg.n_kv_heads + h
         O.unit_compress(qu, ku, cfg.dtype, int(budgets[u]), cfg.alpha, cfg.rho, cfg.window)
 
-    t0 = time.perf_counter()
-    with cf.ThreadPoolExecutor(cores) as ex:
-        list(ex.map(run, range(len(units))))
-    dt = time.perf_counter() - t0
-    toks = sum(int(hdr.lengths[i]) for (i, l, h) in units)
+    limit = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        t0 = time.perf_counter()
+        run(0)
+        dt1 = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(cores) as ex:
+            list(ex.map(run, range(len(units))))
+        dt = time.perf_counter() - t0
+    finally:
+        if limit is not None:
+            limit.unregister()
+    L0 = int(hdr.lengths[0])
+    toks = L0 * len(units)
+    layers = sorted({l for (_, l, _) in units})
     return dict(value=toks / dt, unit="tokens·heads/s", cores=cores, kind="oracle",
-                sample=f"{len(units)} units (seq, layer, KV head) of the same workload, "
-                       f"scores+smoothing+selection in fp64, {dt:.1f} s wall")
+                sample=f"subset: {len(units)} units (sequence 0, layers {layers[0]}-{layers[-1]}, "
+                       f"all KV heads) of the same workload, scores+smoothing+selection in fp64, "
+                       f"{dt:.1f} s wall on {cores} threads; one unit on one thread {dt1:.1f} s",
+                one_thread_value=L0 / dt1, affinity_cores=affinity, cpu_model=cpu_model())
 
 
 def decode_bytes(cfg):
@@ -817,7 +848,9 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample of units")
         cpu = cpu_baseline(cfg, hdr, units, budgets)
-        log(f"[bench] oracle {cpu['value']:.4g} tokens·heads/s on {cpu['cores']} threads")
+        log(f"[bench] oracle {cpu['value']:.4g} tokens·heads/s on {cpu['cores']} threads "
+            f"({cpu['one_thread_value']:.4g} on one; {cpu['affinity_cores']} usable cores, "
+            f"{cpu['cpu_model']})")
 
     line = {
         "metric": "compressed tokens·heads/s and % of HBM peak, L=32K audio tokens, 1 GPU",
