@@ -31,7 +31,7 @@ EXPORTS = ("kvc_plan", "kvc_compress", "kvc_compress_layers", "kvc_scores", "kvc
 KVC_NOALLOC_MAX_WORKSPACE = 64 << 20
 # include/kvc_voxzip.h
 VZ_EXPORTS = ("kvc_vz_plan", "kvc_vz_step", "kvc_vz_accumulate", "kvc_vz_evict",
-              "kvc_vz_gather")
+              "kvc_vz_gather", "kvc_vz_step_inplace")
 # include/kvc_c3.h
 C3_EXPORTS = ("kvc_c3_plan", "kvc_c3_build", "kvc_c3_step", "kvc_c3_score", "kvc_c3_select",
               "kvc_c3_update", "kvc_c3_gather")
@@ -178,6 +178,8 @@ def lib():
                                             _vp]
             L.kvc_vz_evict.argtypes = [vp, vq, _vp, _vp, _vp]
             L.kvc_vz_gather.argtypes = [vp, vq, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+            L.kvc_vz_step_inplace.argtypes = [vp, vq, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              ctypes.c_size_t, _vp]
             for name in VZ_EXPORTS:
                 getattr(L, name).restype = ctypes.c_int
             cp, cq = _P(kvc_c3_problem), _P(kvc_c3_params)

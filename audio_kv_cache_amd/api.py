@@ -358,6 +358,15 @@ def kvc_vz_step(spec, params, q, k, v, a_prev, k_out, v_out, a_out, idx_out, wor
             "kvc_vz_step")
 
 
+def kvc_vz_step_inplace(spec, params, q, k, a, pos, free_slot, workspace, stream=None):
+    """Decode step with the cache kept in its slots (a, pos updated in place)."""
+    C.check(C.lib().kvc_vz_step_inplace(ctypes.byref(spec.c()), ctypes.byref(params.c()),
+                                        _ptr(q), _ptr(k), _ptr(a), _ptr(pos), _ptr(free_slot),
+                                        _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream)), "kvc_vz_step_inplace")
+
+
 def kvc_vz_accumulate(spec, params, q, k, a_prev, a, workspace, stream=None):
     C.check(C.lib().kvc_vz_accumulate(ctypes.byref(spec.c()), ctypes.byref(params.c()),
                                       _ptr(q), _ptr(k), _ptr(a_prev), _ptr(a), _ptr(workspace),

@@ -228,9 +228,13 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_logits_f32_kernel(
 // ---------------------------------------------------------------------------
 // A = gamma * [A_prev, 0] + mean over heads of exp2(l - LSE)
 // ---------------------------------------------------------------------------
+// INPLACE: a_prev and a_t are one buffer indexed by cache slot, and every
+// slot's previous value is decayed (the step that freed a slot for the new
+// token zeroed it); otherwise row n-1 is the new token, which has none.
+template <bool INPLACE>
 __global__ __launch_bounds__(VZ_THREADS) void vz_accum_kernel(
     VzDesc V, const float* __restrict__ lg, const float2* __restrict__ part,
-    const float* __restrict__ a_prev, float* __restrict__ a_t) {
+    const float* a_prev, float* a_t) {
   const int u = blockIdx.x, chunk = blockIdx.y;
   const int seq = u / V.upseq;
   const int n = V.len[seq];
@@ -274,7 +278,7 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_accum_kernel(
       for (int i = 0; i < 8; ++i) s += exp2f(l[i] - lse[g + i]);
     }
     for (; g < G; ++g) s += exp2f(lgu[(size_t)g * V.cap + r] - lse[g]);
-    const float prev = r < n - 1 ? V.gamma * ap[r] : 0.f;
+    const float prev = (INPLACE || r < n - 1) ? V.gamma * ap[r] : 0.f;
     at[r] = prev + s * inv_g;
   }
 }
@@ -392,6 +396,99 @@ __global__ __launch_bounds__(VZ_SEL_THREADS) void vz_evict_kernel(
     if (take) ix[T + pos] = j;
     eq_seen += eq_tot;
     taken += take_tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Eviction in place (kvc_vz_step_inplace): at most one row leaves a cache per
+// step, so the kept rows stay in their slots and only the leaving row's slot
+// changes hands.  Slot s of cache u holds the row whose place in the
+// page's concatenated order is pos[s] (older rows lower); with one row in
+// and one out per step, the T sinks are the T lowest places and the M
+// recent rows the M highest, and the middle row to drop is the one of
+// smallest A, the latest place among equal values (the complement of the
+// N kept).  The freed slot gets A = 0 and the next place, ready for the
+// next token's row.  One 256-thread workgroup per cache.
+// ---------------------------------------------------------------------------
+__device__ inline void vz_min_pair(unsigned long long& k, int& s, unsigned long long k2, int s2) {
+  if (k2 < k) {
+    k = k2;
+    s = s2;
+  }
+}
+
+__global__ __launch_bounds__(VZ_THREADS) void vz_slot_evict_kernel(VzDesc V, float* a,
+                                                                   int32_t* pos,
+                                                                   int32_t* free_slot) {
+  __shared__ int s_min[VZ_THREADS / 64], s_max[VZ_THREADS / 64];
+  __shared__ unsigned long long s_key[VZ_THREADS / 64];
+  __shared__ int s_slot[VZ_THREADS / 64];
+  const int u = blockIdx.x, seq = u / V.upseq;
+  const int n = V.len[seq], B = V.budget[seq];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  float* au = a + (size_t)u * V.cap;
+  int32_t* pu = pos + (size_t)u * V.cap;
+  // lowest and highest place
+  int pmin = INT32_MAX, pmax = INT32_MIN;
+  for (int s = tid; s < n; s += VZ_THREADS) {
+    const int p = pu[s];
+    pmin = min(pmin, p);
+    pmax = max(pmax, p);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    pmin = min(pmin, __shfl_xor(pmin, o));
+    pmax = max(pmax, __shfl_xor(pmax, o));
+  }
+  if (lane == 0) {
+    s_min[wave] = pmin;
+    s_max[wave] = pmax;
+  }
+  __syncthreads();
+  pmin = s_min[0];
+  pmax = s_max[0];
+  for (int w = 1; w < VZ_THREADS / 64; ++w) {
+    pmin = min(pmin, s_min[w]);
+    pmax = max(pmax, s_max[w]);
+  }
+  int out = -1;
+  if (n > B) {
+    // middle places: not among the T lowest nor the M highest
+    const int T = V.n_sink, M = V.recent[seq];
+    unsigned long long best = ~0ull;
+    int bslot = -1;
+    for (int s = tid; s < n; s += VZ_THREADS) {
+      const int p = pu[s];
+      if (p - pmin < T || p > pmax - M) continue;
+      // smallest A first; among equal A the latest place (largest p)
+      const unsigned long long key =
+          ((unsigned long long)vz_key(au[s]) << 32) | (unsigned long long)(~(uint32_t)p);
+      vz_min_pair(best, bslot, key, s);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long k2 = __shfl_xor(best, o);
+      const int s2 = __shfl_xor(bslot, o);
+      vz_min_pair(best, bslot, k2, s2);
+    }
+    if (lane == 0) {
+      s_key[wave] = best;
+      s_slot[wave] = bslot;
+    }
+    __syncthreads();
+    best = s_key[0];
+    bslot = s_slot[0];
+    for (int w = 1; w < VZ_THREADS / 64; ++w) vz_min_pair(best, bslot, s_key[w], s_slot[w]);
+    out = bslot;
+  } else if (n < V.cap) {
+    out = n;                                  // the cache still grows: next slot
+  }
+  if (tid == 0) {
+    if (out >= 0) {
+      au[out] = 0.0f;
+      pu[out] = pmax + 1;
+    }
+    free_slot[u] = out;
   }
 }
 
@@ -559,8 +656,12 @@ static hipError_t vz_launch_accumulate(const VzDesc& V, const void* q, const voi
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(vz_accum_kernel, grid, dim3(VZ_THREADS), 0, st, V, (const float*)c.lg,
-                     (const float2*)c.part, a_prev, a_t);
+  if (a_prev == a_t)
+    hipLaunchKernelGGL(vz_accum_kernel<true>, grid, dim3(VZ_THREADS), 0, st, V,
+                       (const float*)c.lg, (const float2*)c.part, a_prev, a_t);
+  else
+    hipLaunchKernelGGL(vz_accum_kernel<false>, grid, dim3(VZ_THREADS), 0, st, V,
+                       (const float*)c.lg, (const float2*)c.part, a_prev, a_t);
   return hipGetLastError();
 }
 
@@ -662,5 +763,31 @@ extern "C" kvc_status kvc_vz_step(const kvc_vz_problem* prob, const kvc_vz_param
   hipError_t e = vz_launch_accumulate(V, q, k, a_prev, c.a_t, c, s);
   if (e == hipSuccess) e = vz_launch_evict(V, c.a_t, idx_out, s);
   if (e == hipSuccess) e = vz_launch_gather(V, k, v, c.a_t, idx_out, k_out, v_out, a_out, s);
+  return vz_hip(e);
+}
+
+extern "C" kvc_status kvc_vz_step_inplace(const kvc_vz_problem* prob,
+                                          const kvc_vz_params* params, const void* q,
+                                          const void* k, float* a, int32_t* pos,
+                                          int32_t* free_slot, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  VzDesc V;
+  const kvc_status st = vz_desc(prob, params, &V);
+  if (st != KVC_OK) return st;
+  if (!q || !k || !a || !pos || !free_slot || !workspace) return KVC_ERR_INVALID_ARG;
+  if (!vz_a16(q) || !vz_a16(k) || ((uintptr_t)workspace & 255u) || ((uintptr_t)a & 3u) ||
+      ((uintptr_t)pos & 3u) || ((uintptr_t)free_slot & 3u))
+    return KVC_ERR_INVALID_ARG;
+  for (int i = 0; i < V.n_seq; ++i)
+    if (V.len[i] > V.budget[i] + 1) return KVC_ERR_UNSUPPORTED;  // one row out per step
+  if (workspace_bytes < vz_ws_logits(V)) return KVC_ERR_WORKSPACE;
+  const VzCarve c = vz_carve(V, workspace);
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = vz_launch_accumulate(V, q, k, a, a, c, s);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(vz_slot_evict_kernel, dim3(V.n_units), dim3(VZ_THREADS), 0, s, V, a, pos,
+                       free_slot);
+    e = hipGetLastError();
+  }
   return vz_hip(e);
 }

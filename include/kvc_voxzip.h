@@ -103,6 +103,35 @@ kvc_status kvc_vz_gather(const kvc_vz_problem *prob, const kvc_vz_params *params
                          const int32_t *idx, void *k_out, void *v_out,
                          float *a_out, void *stream);
 
+/* The decode step with the cache kept in place, for token-by-token decoding
+ * where at most one row leaves a cache per step (n <= B + 1 for every
+ * sequence, else KVC_ERR_UNSUPPORTED).  Instead of compacting the kept rows
+ * into new buffers, every cache keeps its rows in slots 0..n-1 of k (and
+ * of the caller's v, which the step never reads) and records in pos[s] the
+ * place of slot s's row in the page's concatenated order (older rows lower;
+ * a compact cache has pos[s] = s).  Per cache:
+ *   1. accumulate  as kvc_vz_step, over the n slots: a[s] = gamma a[s] +
+ *                  mean_g p_g[s] (the new token's slot holds a = 0)
+ *   2. evict       if n > B: among the slots whose place is neither among
+ *                  the T lowest nor the M highest, the one of smallest a
+ *                  (equal values: the highest place) leaves -- the
+ *                  complement of the N kept middle rows of kvc_vz_step
+ *   3. free_slot[u] = the slot for the next token's row: the one that left,
+ *                  else n while the cache grows (n < capacity), else -1;
+ *                  its a is set to 0 and its pos to the next place.
+ * Reading the slots in pos order gives kvc_vz_step's k_out, v_out, a_out.
+ * The caller writes the next token's key and value into slot free_slot[u]
+ * and calls again with n = min(n, B) + 1.  Per step only K is read (for
+ * the logits), a and pos updated; no row moves.
+ *   a          device float [units][capacity], in/out
+ *   pos        device int32 [units][capacity], in/out
+ *   free_slot  device int32 [units], out
+ *   workspace  device, 256-byte aligned, >= kvc_vz_plan's workspace_bytes */
+kvc_status kvc_vz_step_inplace(const kvc_vz_problem *prob, const kvc_vz_params *params,
+                               const void *q, const void *k, float *a, int32_t *pos,
+                               int32_t *free_slot, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

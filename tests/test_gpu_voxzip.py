@@ -352,3 +352,126 @@ def test_vz_invalid_arguments():
         api.kvc_vz_accumulate(D.spec, D.params, D.q, D.k, D.a_prev,
                               torch.empty(D.shape, device="cuda"),
                               torch.empty(16, dtype=torch.uint8, device="cuda"))
+
+
+# ---------------------------------------------------------------------------
+# The decode step with the cache kept in place (kvc_vz_step_inplace)
+# ---------------------------------------------------------------------------
+def inplace_state(D):
+    """a and pos of a compact cache for the in-place step: a = A_prev with
+    the new token's slot (n - 1) at 0, pos[s] = s; NaN/-1 past n."""
+    U, cap = D.shape
+    a = np.full(D.shape, np.nan, dtype=np.float32)
+    pos = np.full(D.shape, -1, dtype=np.int32)
+    for u in range(U):
+        n = D.n(u)
+        a[u, :n - 1] = D.prob.a_prev[u, :n - 1]
+        a[u, n - 1] = 0.0
+        pos[u, :n] = np.arange(n)
+    return a, pos
+
+
+def run_inplace(D, a_np, pos_np):
+    a = torch.from_numpy(a_np.copy()).cuda()
+    pos = torch.from_numpy(pos_np.copy()).cuda()
+    free = torch.full((D.prob.n_units,), -7, dtype=torch.int32, device="cuda")
+    api.kvc_vz_step_inplace(D.spec, D.params, D.q, D.k, a, pos, free, D.ws())
+    torch.cuda.synchronize()
+    return a.cpu().numpy(), pos.cpu().numpy(), free.cpu().numpy()
+
+
+def check_inplace_against_step(D, units):
+    # Same logits and accumulation kernels, so A is bit-identical to the
+    # compacting step's; the slot that leaves is the one position missing
+    # from its kept list, and the kept slots hold exactly its A values.
+    a0, pos0 = inplace_state(D)
+    a, pos, free = run_inplace(D, a0, pos0)
+    out = D.step()
+    for u in units:
+        n, B = D.n(u), D.B(u)
+        idx = out["idx"][u, :min(n, B)]
+        if n > B:
+            gone = np.setdiff1d(np.arange(n), idx)
+            assert gone.tolist() == [int(free[u])], (u, gone[:4], free[u])
+            e = int(free[u])
+            assert a[u, e] == 0.0 and pos[u, e] == n
+        else:
+            assert int(free[u]) == (n if n < D.cfg.capacity else -1)
+        assert np.array_equal(a[u, idx], out["a_out"][u, :len(idx)]), u
+        assert np.array_equal(pos[u, idx], idx)
+
+
+def test_vz_inplace_matches_compacting_step_full_size():
+    say("[vz] in place, vz_omni30b")
+    D = make("vz_omni30b")
+    check_inplace_against_step(D, range(D.prob.n_units))
+
+
+def test_vz_inplace_mixed_states():
+    # caches that evict one row, grow, sit exactly at the budget, and with
+    # T + M = B (no middle row kept: the only middle candidate leaves)
+    say("[vz] in place, mixed states")
+    D = small(n_seq=4, lens=(501, 300, 500, 26), budgets=(500, 400, 500, 25), capacity=504,
+              n_sink=5, recent_frac=0.8)
+    check_inplace_against_step(D, range(D.prob.n_units))
+
+
+def test_vz_inplace_decode_loop_tracks_the_oracle():
+    # 24 chained steps from a compact cache of 140 rows with budget 150: ten
+    # steps of growth, then one row out per step.  After every step the
+    # slots read in pos order must be the oracle's concatenated cache; the
+    # next token is written into the freed slot.  fp32 inputs keep the kept
+    # sets identical.
+    say("[vz] in place, 24 chained steps, fp32")
+    r = np.random.default_rng(21)
+    G, d, B, cap = 4, 64, 150, 160
+    n = 141
+    k = np.full((1, cap, d), np.nan, dtype=np.float32)
+    v = np.full((1, cap, d), np.nan, dtype=np.float32)
+    k[0, :n] = r.standard_normal((n, d))
+    v[0, :n] = r.standard_normal((n, d))
+    a = np.full((1, cap), np.nan, dtype=np.float32)
+    a[0, :n - 1] = r.random(n - 1) * 1e-3
+    a[0, n - 1] = 0.0
+    pos = np.full((1, cap), -1, dtype=np.int32)
+    pos[0, :n] = np.arange(n)
+    ref_k, ref_v, ref_a = k[0, :n].astype(np.float64), v[0, :n].copy(), a[0, :n - 1].astype(np.float64)
+    kt, at, pt = (torch.from_numpy(x).cuda() for x in (k, a, pos))
+    free = torch.zeros(1, dtype=torch.int32, device="cuda")
+    prm = api.VzParams()
+    for t in range(24):
+        q = r.standard_normal((1, G, d)).astype(np.float32)
+        spec = api.VzSpec(n_layers=1, n_kv_heads=1, gqa=G, head_dim=d, lens=[n], budgets=[B],
+                          capacity=cap, dtype="f32")
+        _, wsb = api.kvc_vz_plan(spec, prm)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        api.kvc_vz_step_inplace(spec, prm, torch.from_numpy(q).cuda(), kt, at, pt, free, ws)
+        torch.cuda.synchronize()
+        ref = VZ.step(q[0].astype(np.float64), ref_k, ref_v, ref_a, B)
+        e = int(free.cpu()[0])
+        an, pn, kn = at.cpu().numpy()[0], pt.cpu().numpy()[0], kt.cpu().numpy()[0]
+        live = [s for s in range(n) if not (n > B and s == e)]
+        order = sorted(live, key=lambda s: pn[s])
+        assert [pn[s] for s in order] == sorted(pn[live].tolist())
+        assert np.array_equal(kn[order], ref["k_out"].astype(np.float32)), t
+        assert rel_err(an[order], ref["a_out"]) <= TOL["f32"], t
+        m = len(order)
+        assert m == min(n, B)
+        # next token into the freed slot (the step already zeroed its A and
+        # gave it the next place)
+        assert an[e] == 0.0 and pn[e] == max(pn[live]) + 1
+        newk = r.standard_normal(d).astype(np.float32)
+        newv = r.standard_normal(d).astype(np.float32)
+        kt[0, e] = torch.from_numpy(newk).cuda()
+        ref_k = np.vstack([ref["k_out"], newk.astype(np.float64)])
+        ref_v = np.vstack([ref["v_out"], newv])
+        ref_a = ref["a_out"]
+        n = m + 1
+
+
+def test_vz_inplace_rejects_more_than_one_row_out():
+    D = small(lens=(502,), budgets=(500,), capacity=504)
+    a0, pos0 = inplace_state(D)
+    with pytest.raises(Exception) as e:
+        run_inplace(D, a0, pos0)
+    assert "status 2" in str(e.value) or getattr(e.value, "status", None) == 2
