@@ -318,13 +318,15 @@ __device__ __forceinline__ void smooth_unit(const KvcDesc& D, int mode, int u, c
                             float* lds, SssShared& sh, int t, bool act) {
   constexpr int T = N / V;
   constexpr int L = 2 * N;
+  constexpr int RM = 32;
+  constexpr int R0 = fft_radix(N, V, 1, RM);
   const int hv = V / 2;
-  // z_m = s_{2m} + i s_{2m+1}, in the order of the first radix-V pass.
+  // z_m = s_{2m} + i s_{2m+1}, in the order of the first pass.
   if (act) {
     const float2* z = reinterpret_cast<const float2*>(srow);
 #pragma unroll
     for (int s = 0; s < V; ++s) {
-      const float2 v = z[in_index<V, T, N>(s, t)];
+      const float2 v = z[in_index<R0, T, N>(s, t)];
       re[s] = v.x;
       im[s] = v.y;
     }
@@ -339,7 +341,7 @@ __device__ __forceinline__ void smooth_unit(const KvcDesc& D, int mode, int u, c
     return s < hv ? k : ((N - k) & (N - 1));
   };
   Extra xf{-1, (t == 0) ? N / 2 : -1, 0.f, 0.f, 0.f, 0.f};
-  fft_stages<N, V, 1>(re, im, lds, t, act, pair_idx, xf);
+  fft_stages<N, V, 1, RM>(re, im, lds, t, act, pair_idx, xf);
 
   // Real spectrum: F_k = A_k + e^{-2 pi i k/L} B_k with
   // A_k = (Z_k + conj Z_{N-k})/2, B_k = (Z_k - conj Z_{N-k})/(2i); the mirror
@@ -378,11 +380,32 @@ __device__ __forceinline__ void smooth_unit(const KvcDesc& D, int mode, int u, c
       pmid = (double)fmid.x * fmid.x + (double)fmid.y * fmid.y;
     }
   }
+  // The spectrum values wait in LDS (free between the forward FFT's last
+  // exchange and the inverse's first) while the block scans run, so that
+  // the registers they occupy are not spilled to scratch across the scans:
+  // all 2V floats of a thread when the buffer holds them (N <= 16384), else
+  // the mirror bins' V floats.  Slot j of thread t at j*T + t (consecutive
+  // threads, consecutive words).
+  constexpr int PARK = 2 * V * T <= Xbuf<N>::kFloats ? 2 * V : V;
+  static_assert(PARK * T <= Xbuf<N>::kFloats, "parked values fit the exchange buffer");
+  auto park_slot = [&](int j) -> float& {
+    // PARK == 2V: re[0..V) then im[0..V); PARK == V: re, im of slots hv..V
+    if constexpr (PARK == 2 * V) return j < V ? re[j] : im[j - V];
+    else return j < hv ? re[hv + j] : im[j];
+  };
+  if (act) {
+#pragma unroll
+    for (int j = 0; j < PARK; ++j) lds[j * T + t] = park_slot(j);
+  }
   // Natural bin order: lower chunks (t ascending), bin N/2, upper chunks
   // (t descending).  Prefix energies from two block scans.
   double lo_tot, hi_tot;
   const double lo_before = block_scan<double>(lo_sum, sh.sd, &lo_tot);
   const double hi_incl = block_scan<double>(hi_sum, sh.sd, &hi_tot) + hi_sum;
+  if (act) {
+#pragma unroll
+    for (int j = 0; j < PARK; ++j) park_slot(j) = lds[j * T + t];
+  }
   if (t == 0) sh.sd[0] = pmid;
   __syncthreads();
   const double pm = sh.sd[0];
@@ -453,14 +476,14 @@ __device__ __forceinline__ void smooth_unit(const KvcDesc& D, int mode, int u, c
   }
   // To the inverse's first-pass order.  Slot V/2 of thread 0 (k = 0) maps to
   // index 0 again and carries the same value as slot 0.
-  xchg<N, V>(re, im, lds, act, pair_idx, [&](int s) { return in_index<V, T, N>(s, t); }, xi);
+  xchg<N, V>(re, im, lds, act, pair_idx, [&](int s) { return in_index<R0, T, N>(s, t); }, xi);
 
   // Inverse FFT as conj(FFT(conj(x))) / N, ending in natural chunks
   // (slot s holds index tV + s).
 #pragma unroll
   for (int s = 0; s < V; ++s) im[s] = -im[s];
   Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
-  fft_stages<N, V, 1>(re, im, lds, t, act, [&](int s) { return t * V + s; }, none);
+  fft_stages<N, V, 1, RM>(re, im, lds, t, act, [&](int s) { return t * V + s; }, none);
 
   // Blend with the raw row: s_hat = (1 - alpha) s + alpha lowpass.
   const float invN = 1.0f / (float)N;
