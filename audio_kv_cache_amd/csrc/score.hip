@@ -82,6 +82,16 @@ __device__ inline int xcd_local_tile(int b, int n) {
   return x * per + (x < rem ? x : rem) + b / kXcds;
 }
 
+// The same ranges, each walked from its last tile to its first: a pass that
+// follows one in xcd_local_tile order starts on the tiles whose keys the
+// other read last (still in the XCD's L2 and the memory-side cache).
+__device__ inline int xcd_local_tile_rev(int b, int n) {
+  constexpr int kXcds = 8;
+  const int x = b % kXcds, per = n / kXcds, rem = n % kXcds;
+  const int cnt = per + (x < rem ? 1 : 0);
+  return x * per + (x < rem ? x : rem) + (cnt - 1 - b / kXcds);
+}
+
 struct TileInfo {
   int seq, u, l, h, t, tpu, L, keys, key0;
   bool tail;   // a tile of the L % 64 keys past the last multiple of 64 (kvc_score_tail_kernel)
@@ -318,7 +328,7 @@ __global__ __launch_bounds__(SCORE_THREADS, T::MINB) void kvc_score_pool_kernel(
   __shared__ __attribute__((aligned(16))) elem_t sQ[MAXRB * M * QS];
   __shared__ float sL[MAXRB * M];
 
-  const int tile = tile0 + xcd_local_tile((int)blockIdx.x, (int)gridDim.x);
+  const int tile = tile0 + xcd_local_tile_rev((int)blockIdx.x, (int)gridDim.x);
   const TileInfo ti = tile_info(Dsc, tile);
   if (ti.tail) return;  // kvc_score_tail_kernel
   const int gw = NBC > 0 ? NBC * M : Dsc.gw;
@@ -567,7 +577,7 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
   constexpr int NROWS = MAXP ? 2 * NW : NW;
   __shared__ __attribute__((aligned(16))) char sK[2][C::CHUNK * C::RS];
   __shared__ float sRed[NROWS][KVC_TILE_KEYS];
-  const int tile = tile0 + xcd_local_tile((int)blockIdx.x, (int)gridDim.x);
+  const int tile = tile0 + xcd_local_tile_rev((int)blockIdx.x, (int)gridDim.x);
   const TileInfo ti = tile_info(Dsc, tile);
   if (ti.tail) return;  // kvc_score_tail_kernel
   const int gw = NBC * 32;
