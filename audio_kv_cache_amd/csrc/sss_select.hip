@@ -989,12 +989,15 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_general_kernel(
 //   FFT_M(P)_m = sum_r W_M^{r m} FFT_H(P_{S k + r})_{m mod H}
 // so the product with FFT_M of the chirp filter is formed in the decimated
 // order in which the first FFT leaves it, which is the order the second one
-// takes.  Kernels per smoothing launch: split (elementwise), sub-FFT with
-// the product, sub-FFT, spectrum (one workgroup per unit: combine, real
-// bins, fp64 energies, k*, mask, back to the inverse's split), sub-FFT with
-// the product, sub-FFT, finish (combine, blend, selection).  Sub-FFTs are
-// one 1024-thread workgroup each (Stockham passes, 32 values per thread),
-// in place in global scratch.
+// takes.  Kernels per smoothing launch: the chirp filter's split and
+// sub-FFTs (once), then per unit the first convolution (one workgroup per
+// sub-sequence: the split from the score row, FFT, product, FFT), the
+// spectrum (one workgroup per unit: combine, real bins, fp64 energies, k*,
+// mask, back to the inverse's split), the second convolution, and the
+// finish (combine, blend, selection).  A sub-sequence's two FFTs run in the
+// same 1024-thread workgroup (Stockham passes, 32 values per thread), the
+// first leaving its output in the order the second starts from, so only
+// the convolution results go through global scratch.
 #define KVC_BIG_LOGH 15
 #define KVC_BIG_H (1 << KVC_BIG_LOGH)
 
@@ -1071,49 +1074,30 @@ __device__ __forceinline__ float2 kvc_big_combine(const float2* __restrict__ Y, 
 
 // Split of the chirp filter (b_m = w_m for m < Np, b_{M-m} = w_m for
 // 0 < m < Np, zero between) into the bhat region, and the table
-// cw[n] = conj(w_n); or, per unit, of the first premultiplied sequence.
-// grid (H / 256, units or 1), 256 threads.
+// cw[n] = conj(w_n).  grid H / 256, 256 threads.
 template <int S>
-__global__ __launch_bounds__(256) void kvc_big_split_kernel(KvcDesc D, KvcSeqGroup G, int chirp,
-                                                            int Np, const float* __restrict__ s_in,
-                                                            float2* __restrict__ base) {
+__global__ __launch_bounds__(256) void kvc_big_chirp_split_kernel(int Np,
+                                                                  float2* __restrict__ base) {
   constexpr int M = S * KVC_BIG_H;
   const int j = blockIdx.x * 256 + threadIdx.x;
   const BigScratch bs = kvc_big_scratch(Np, M);
   float2* cw = base + bs.cw_off;
-  if (chirp) {
-    for (int n = j; n < Np; n += KVC_BIG_H) cw[n] = conjf2(kvc_chirp(n, Np));
-    kvc_big_split<S>(base, j, M, [&](int m) {
-      const int mm = m < Np ? m : (M - m < Np ? M - m : -1);
-      return mm >= 0 ? kvc_chirp(mm, Np) : make_float2(0.f, 0.f);
-    });
-    return;
-  }
-  const int u = kvc_group_unit(G, D.upseq, (int)blockIdx.y);
-  const int seq = u / D.upseq, within = u - seq * D.upseq;
-  const int L = D.L[seq];
-  const float* srow = s_in + D.srow_base[seq] + (int64_t)within * L;
-  const bool even = (L & 1) == 0;
-  float2* Y = base + bs.rows_off + (size_t)blockIdx.y * bs.ustride;
-  kvc_big_split<S>(Y, j, M, [&](int n) {
-    return n < Np ? kvc_big_in(srow, even, n, conjf2(kvc_chirp(n, Np))) : make_float2(0.f, 0.f);
+  for (int n = j; n < Np; n += KVC_BIG_H) cw[n] = conjf2(kvc_chirp(n, Np));
+  kvc_big_split<S>(base, j, M, [&](int m) {
+    const int mm = m < Np ? m : (M - m < Np ? M - m : -1);
+    return mm >= 0 ? kvc_chirp(mm, Np) : make_float2(0.f, 0.f);
   });
 }
 
-// One H-point FFT in place: sub-sequence (blockIdx.x % S) of slot
-// (blockIdx.x / S), i.e. first + slot * ustride + r * H.  POST: multiply bin
-// k by bhat[r H + k] and conjugate (the product of the convolution, ready
-// for the second FFT).
-template <int S, bool POST>
-__global__ __launch_bounds__(SSS_T) void kvc_big_fft_kernel(float2* __restrict__ first,
-                                                            size_t ustride,
-                                                            const float2* __restrict__ bhat) {
+// The chirp filter's H-point sub-FFTs in place: sub-sequence blockIdx.x of
+// the bhat region, natural order (sub-transform r then holds bins S k + r).
+template <int S>
+__global__ __launch_bounds__(SSS_T) void kvc_big_chirp_fft_kernel(float2* __restrict__ base) {
   constexpr int N = KVC_BIG_H, V = 32, T = N / V, RM = 16;
   constexpr int R0 = fft_radix(N, V, 1, RM);
   static_assert(T == SSS_T, "one value slot set per thread");
   __shared__ __attribute__((aligned(16))) float lds[Xbuf<N>::kFloats];
-  const int r = (int)blockIdx.x % S;
-  float2* y = first + (size_t)(blockIdx.x / S) * ustride + (size_t)r * N;
+  float2* y = base + (size_t)blockIdx.x * N;
   const int t = threadIdx.x;
   float re[V], im[V];
 #pragma unroll
@@ -1127,14 +1111,81 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_fft_kernel(float2* __restrict__
   // (every value of y was read before the first exchange's barrier)
   float4* o = reinterpret_cast<float4*>(y + t * V);
 #pragma unroll
-  for (int s = 0; s < V; s += 2) {
-    float2 a = make_float2(re[s], im[s]), b = make_float2(re[s + 1], im[s + 1]);
-    if constexpr (POST) {
-      a = conjf2(cmul(a, bhat[(size_t)r * N + t * V + s]));
-      b = conjf2(cmul(b, bhat[(size_t)r * N + t * V + s + 1]));
+  for (int s = 0; s < V; s += 2) o[s / 2] = make_float4(re[s], im[s], re[s + 1], im[s + 1]);
+}
+
+// One sub-sequence's share of a whole convolution in one workgroup: its
+// H-point FFT (left in the first pass's input order, which is where the
+// second FFT starts), the product with the chirp filter's spectrum and the
+// conjugation, the second H-point FFT (the decimation-in-time sub-transform
+// of the same sub-sequence), stored in place in natural order.  FROM_ROW:
+// the input is split on the fly from the unit's score row (the first
+// transform); else read from the unit's split values (the second).
+template <int S, bool FROM_ROW>
+__global__ __launch_bounds__(SSS_T) void kvc_big_conv_kernel(KvcDesc D, KvcSeqGroup G, int Np,
+                                                             const float* __restrict__ s_in,
+                                                             float2* __restrict__ base) {
+  constexpr int N = KVC_BIG_H, V = 32, T = N / V, RM = 16, M = S * N;
+  constexpr int R0 = fft_radix(N, V, 1, RM);
+  static_assert(T == SSS_T, "one value slot set per thread");
+  __shared__ __attribute__((aligned(16))) float lds[Xbuf<N>::kFloats];
+  const BigScratch bs = kvc_big_scratch(Np, M);
+  const float2* bhat = base;
+  const float2* cw = base + bs.cw_off;
+  const int slot = (int)blockIdx.x / S, r = (int)blockIdx.x % S;
+  float2* y = base + bs.rows_off + (size_t)slot * bs.ustride + (size_t)r * N;
+  const int t = threadIdx.x;
+  float re[V], im[V];
+  if constexpr (FROM_ROW) {
+    const int u = kvc_group_unit(G, D.upseq, slot);
+    const int seq = u / D.upseq, within = u - seq * D.upseq;
+    const int L = D.L[seq];
+    const float* srow = s_in + D.srow_base[seq] + (int64_t)within * L;
+    const bool even = (L & 1) == 0;
+#pragma unroll
+    for (int s = 0; s < V; ++s) {
+      const int j = in_index<R0, T, N>(s, t);
+      float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int q = 0; q < S; ++q) {
+        const int n = j + q * N;
+        if (n < Np) {
+          const float2 v = kvc_quarter(kvc_big_in(srow, even, n, cw[n]), q * r, S);
+          acc = make_float2(acc.x + v.x, acc.y + v.y);
+        }
+      }
+      if (r) acc = cmul(acc, kvc_twiddle(j * r, M));
+      re[s] = acc.x;
+      im[s] = acc.y;
     }
-    o[s / 2] = make_float4(a.x, a.y, b.x, b.y);
+  } else {
+#pragma unroll
+    for (int s = 0; s < V; ++s) {
+      const float2 v = y[in_index<R0, T, N>(s, t)];
+      re[s] = v.x;
+      im[s] = v.y;
+    }
   }
+  Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
+  fft_stages<N, V, 1, RM>(re, im, lds, t, true, [&](int s) { return in_index<R0, T, N>(s, t); },
+                          none);
+  {
+    // (an opaque copy of the thread index: the compiler would otherwise keep
+    // the first FFT's output indices live into the second)
+    int tt = t;
+    asm volatile("" : "+v"(tt));
+    const float2* bh = bhat + (size_t)r * N;
+#pragma unroll
+    for (int s = 0; s < V; ++s) {
+      const float2 p = cmul(make_float2(re[s], im[s]), bh[in_index<R0, T, N>(s, tt)]);
+      re[s] = p.x;
+      im[s] = -p.y;
+    }
+  }
+  fft_stages<N, V, 1, RM>(re, im, lds, t, true, [&](int s) { return t * V + s; }, none);
+  float4* o = reinterpret_cast<float4*>(y + t * V);
+#pragma unroll
+  for (int s = 0; s < V; s += 2) o[s / 2] = make_float4(re[s], im[s], re[s + 1], im[s + 1]);
 }
 
 // Per unit, after the first convolution: the spectrum X_k (k < Np), the real
@@ -1314,25 +1365,16 @@ static hipError_t launch_big(const KvcDesc& D, const KvcSeqGroup& g, int nwg, in
                              float2* base, hipStream_t st) {
   constexpr int M = S * KVC_BIG_H;
   if (nwg > 65535) return hipErrorInvalidConfiguration;  // (grid y of the split)
-  const BigScratch b = kvc_big_scratch(Np, M);
-  float2* rows = base + b.rows_off;
   if (mode & 1) {
-    const dim3 sg(KVC_BIG_H / 256, 1);
-    hipLaunchKernelGGL(kvc_big_split_kernel<S>, sg, dim3(256), 0, st, D, g, 1, Np, s_in, base);
-    hipLaunchKernelGGL((kvc_big_fft_kernel<S, false>), dim3(S), dim3(SSS_T), 0, st, base,
-                       (size_t)0, (const float2*)nullptr);
-    hipLaunchKernelGGL(kvc_big_split_kernel<S>, dim3(KVC_BIG_H / 256, nwg), dim3(256), 0, st, D,
-                       g, 0, Np, s_in, base);
-    hipLaunchKernelGGL((kvc_big_fft_kernel<S, true>), dim3(nwg * S), dim3(SSS_T), 0, st, rows,
-                       b.ustride, (const float2*)base);
-    hipLaunchKernelGGL((kvc_big_fft_kernel<S, false>), dim3(nwg * S), dim3(SSS_T), 0, st, rows,
-                       b.ustride, (const float2*)nullptr);
+    hipLaunchKernelGGL(kvc_big_chirp_split_kernel<S>, dim3(KVC_BIG_H / 256), dim3(256), 0, st,
+                       Np, base);
+    hipLaunchKernelGGL(kvc_big_chirp_fft_kernel<S>, dim3(S), dim3(SSS_T), 0, st, base);
+    hipLaunchKernelGGL((kvc_big_conv_kernel<S, true>), dim3(nwg * S), dim3(SSS_T), 0, st, D, g,
+                       Np, s_in, base);
     hipLaunchKernelGGL(kvc_big_spectrum_kernel<S>, dim3(nwg), dim3(SSS_T), 0, st, D, mode, g, Np,
                        base, kstar_out);
-    hipLaunchKernelGGL((kvc_big_fft_kernel<S, true>), dim3(nwg * S), dim3(SSS_T), 0, st, rows,
-                       b.ustride, (const float2*)base);
-    hipLaunchKernelGGL((kvc_big_fft_kernel<S, false>), dim3(nwg * S), dim3(SSS_T), 0, st, rows,
-                       b.ustride, (const float2*)nullptr);
+    hipLaunchKernelGGL((kvc_big_conv_kernel<S, false>), dim3(nwg * S), dim3(SSS_T), 0, st, D, g,
+                       Np, s_in, base);
   }
   if (D.L[g.seq[0]] > 32768)
     hipLaunchKernelGGL((kvc_big_finish_kernel<S, 32>), dim3(nwg), dim3(SSS_T), 0, st, D, mode, g,
