@@ -29,9 +29,7 @@ __global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
   __shared__ float sS[KVC_MAX_UNITS_PER_SEQ];
   __shared__ int32_t extra[KVC_MAX_UNITS_PER_SEQ];
   __shared__ uint8_t active[KVC_MAX_UNITS_PER_SEQ];
-  __shared__ double s_sum;
   __shared__ int64_t s_R;
-  __shared__ int s_nA, s_capped;
   __shared__ int64_t s_wsum[BUDGET_THREADS / 64];
 
   // Pool `pool` of sequence `seq`: heads pool*n .. pool*n + n - 1 of the
@@ -66,60 +64,91 @@ __global__ __launch_bounds__(BUDGET_THREADS) void kvc_budget_kernel(
     extra[u] = 0;
     sS[u] = S[u];
   }
-  if (tid == 0) s_R = (int64_t)n * kbar - (int64_t)n * fixed;
   __syncthreads();
 
-  // Water-filling rounds.
-  for (;;) {
-    if (tid == 0) {
-      // Sequential in u (the order fixes the rounding); branch-free so the
-      // LDS loads pipeline: adding +0.0 for an inactive head changes nothing.
-      double acc = 0.0;
+  // Water-filling rounds, in wave 0 alone (lanes over the heads), so a
+  // round costs no workgroup barrier.  Each round's sum of the active
+  // scores is the sequential fp64 sum in ascending head order.  When every
+  // partial sum of the scores is exact in fp64 -- all are multiples of the
+  // finest grid 2^emin among them, and n * max(S) < 2^(emin + 53) -- that
+  // sequential sum equals the exact sum, which the lanes then form in any
+  // order (every subset sum is exact too); otherwise lane 0 adds the
+  // scores one by one in head order.
+  if (tid < 64) {
+    const int lane = tid;
+    float smax = 0.0f;
+    int emin = INT32_MAX;
+    for (int u = lane; u < n; u += 64) {
+      const float v = sS[u];
+      smax = fmaxf(smax, v);
+      if (v > 0.0f) {
+        const int be = (int)((__float_as_uint(v) >> 23) & 0xFFu);
+        emin = min(emin, be == 0 ? -149 : be - 150);   // ulp exponent of v
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      smax = fmaxf(smax, __shfl_xor(smax, o));
+      emin = min(emin, __shfl_xor(emin, o));
+    }
+    const bool exact = emin == INT32_MAX || (double)n * (double)smax < ldexp(1.0, emin + 53);
+    int64_t R = (int64_t)n * kbar - (int64_t)n * fixed;
+    for (;;) {
+      double sumA = 0.0;
       int nA = 0;
-      for (int u0 = 0; u0 < n; u0 += 16) {
-        // 16 independent LDS loads first, then the adds in u order.
-        // (loads at a clamped index, then a select: no branch per element,
-        // so the 32 LDS loads are all in flight before the first add)
-        double x[16];
+      if (exact) {
+        for (int u = lane; u < n; u += 64)
+          if (active[u]) {
+            sumA += (double)sS[u];
+            ++nA;
+          }
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int u = min(u0 + j, n - 1);
-          const float sv = sS[u];
-          const bool a = (u0 + j < n) & (active[u] != 0);
-          x[j] = a ? (double)sv : 0.0;
-          nA += a;
+        for (int o = 32; o > 0; o >>= 1) {
+          sumA += __shfl_xor(sumA, o);
+          nA += __shfl_xor(nA, o);
         }
+      } else {
+        if (lane == 0) {
+          // 16 loads in flight, then the adds in head order (a clamped
+          // index and a select instead of a branch per element)
+          for (int u0 = 0; u0 < n; u0 += 16) {
+            double x[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc += x[j];
+            for (int j = 0; j < 16; ++j) {
+              const int u = min(u0 + j, n - 1);
+              const float sv = sS[u];
+              const bool a = (u0 + j < n) & (active[u] != 0);
+              x[j] = a ? (double)sv : 0.0;
+              nA += a;
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) sumA += x[j];
+          }
+        }
+        sumA = __shfl(sumA, 0);
+        nA = __shfl(nA, 0);
       }
-      s_sum = acc;
-      s_nA = nA;
-      s_capped = 0;
-    }
-    __syncthreads();
-    const double sumA = s_sum;
-    const int nA = s_nA;
-    const double Rd = (double)s_R;
-    int my_capped = 0;
-    for (int u = tid; u < n; u += BUDGET_THREADS) {
-      if (!active[u]) continue;
-      const double qu = sumA > 0.0 ? (Rd * (double)sS[u]) / sumA : Rd / (double)nA;
-      q[u] = qu;
-      if (qu >= (double)cap) ++my_capped;
-    }
-    if (my_capped) atomicAdd(&s_capped, my_capped);
-    __syncthreads();
-    const int capped = s_capped;
-    if (capped == 0 || nA == 0) break;
-    for (int u = tid; u < n; u += BUDGET_THREADS)
-      if (active[u] && q[u] >= (double)cap) {
-        active[u] = 0;
-        extra[u] = (int32_t)cap;
+      const double Rd = (double)R;
+      int capped = 0;
+      for (int u = lane; u < n; u += 64) {
+        if (!active[u]) continue;
+        const double qu = sumA > 0.0 ? (Rd * (double)sS[u]) / sumA : Rd / (double)nA;
+        q[u] = qu;
+        capped += qu >= (double)cap;
       }
-    __syncthreads();
-    if (tid == 0) s_R -= cap * (int64_t)capped;
-    __syncthreads();
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) capped += __shfl_xor(capped, o);
+      if (capped == 0 || nA == 0) break;
+      for (int u = lane; u < n; u += 64)
+        if (active[u] && q[u] >= (double)cap) {
+          active[u] = 0;
+          extra[u] = (int32_t)cap;
+        }
+      R -= cap * (int64_t)capped;
+    }
+    if (lane == 0) s_R = R;
   }
+  __syncthreads();
 
   // Largest remainder over the heads still active.
   int64_t my_floor = 0;

@@ -128,6 +128,17 @@ def test_budget_bitexact_hand_cases_and_random():
         if O.budget_rc(S, L, ret, base, 32) != 0:
             continue
         assert np.array_equal(_budget_gpu(S, L, ret, base, 32), O.budget(S, L, ret, base, 32))
+    # Scores spread over about 80 binades: partial sums are no longer exact
+    # in fp64, so the kernel's rounds take the sequential sum in head order.
+    for it in range(12):
+        n = int(rng.integers(2, 400))
+        S = (rng.uniform(0.5, 1.0, n) * np.exp2(-rng.integers(0, 80, n))).astype(np.float32)
+        S[rng.random(n) < 0.1] = 0.0
+        L = int(rng.choice([1024, 8192, 32768]))
+        ret = float(rng.uniform(0.3, 0.9))
+        if O.budget_rc(S, L, ret, 0.5, 32) != 0:
+            continue
+        assert np.array_equal(_budget_gpu(S, L, ret, 0.5, 32), O.budget(S, L, ret, 0.5, 32)), it
 
 
 # ---------------------------------------------------------------------------
