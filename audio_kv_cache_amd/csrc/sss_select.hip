@@ -1188,6 +1188,12 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_conv_kernel(KvcDesc D, KvcSeqGr
   for (int s = 0; s < V; s += 2) o[s / 2] = make_float4(re[s], im[s], re[s + 1], im[s + 1]);
 }
 
+// Loads in these per-unit kernels go out in batches (a batch's loads, then
+// its arithmetic and stores): their loops read and write one scratch area,
+// so the compiler would otherwise wait on every load.  KB: batch size.
+template <int S>
+__host__ __device__ constexpr int kvc_big_batch() { return S >= 4 ? 4 : 8; }
+
 // Per unit, after the first convolution: the spectrum X_k (k < Np), the real
 // bins F_0 .. F_{L/2} with their fp64 energies, k*, the masked spectrum
 // merged back to the complex sequence, conjugated and premultiplied for the
@@ -1197,7 +1203,7 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_spectrum_kernel(KvcDesc D, int 
                                                                  KvcSeqGroup G, int Np,
                                                                  float2* __restrict__ base,
                                                                  int32_t* __restrict__ kstar_out) {
-  constexpr int M = S * KVC_BIG_H;
+  constexpr int M = S * KVC_BIG_H, H = KVC_BIG_H, KB = kvc_big_batch<S>();
   __shared__ SssShared sh;
   const int u = kvc_group_unit(G, D.upseq, (int)blockIdx.x);
   const int seq = u / D.upseq;
@@ -1210,9 +1216,28 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_spectrum_kernel(KvcDesc D, int 
   float2* X = Y + M;
   float2* Fb = X + Np;
   const float invM = 1.0f / (float)M;
-  for (int k = t; k < Np; k += SSS_T) {
-    const float2 q = kvc_big_combine<S>(Y, k, M);
-    X[k] = cmul(cw[k], make_float2(q.x * invM, -q.y * invM));
+  // X_k = conj(w_k) conj(sum_r W_M^{rk} E_r[k mod H]) / M
+  for (int k0 = t; k0 < Np; k0 += KB * SSS_T) {
+    float2 e[KB][S], c[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int k = min(k0 + i * SSS_T, Np - 1);   // (clamped: every load in bounds)
+#pragma unroll
+      for (int r = 0; r < S; ++r) e[i][r] = Y[(size_t)r * H + (k & (H - 1))];
+      c[i] = cw[k];
+    }
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int k = k0 + i * SSS_T;
+      if (k >= Np) continue;
+      float2 q = e[i][0];
+#pragma unroll
+      for (int r = 1; r < S; ++r) {
+        const float2 v = cmul(e[i][r], kvc_twiddle(r * k, M));
+        q = make_float2(q.x + v.x, q.y + v.y);
+      }
+      X[k] = cmul(c[i], make_float2(q.x * invM, -q.y * invM));
+    }
   }
   if (t == 0) sh.kstar = L / 2;  // the last bin, should rounding leave E short of rho E(L/2)
   __syncthreads();
@@ -1222,19 +1247,34 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_spectrum_kernel(KvcDesc D, int 
   const int per = (nb + SSS_T - 1) / SSS_T;
   const int k0 = min(nb, t * per), k1 = min(nb, k0 + per);
   double esum = 0.0;
-  for (int kk = k0; kk < k1; ++kk) {
-    float2 F;
-    if (even) {
-      const float2 zk = X[kk % Np], zm = X[(Np - kk % Np) % Np];
-      const float2 A = make_float2(0.5f * (zk.x + zm.x), 0.5f * (zk.y - zm.y));
-      const float2 B = make_float2(0.5f * (zk.y + zm.y), -0.5f * (zk.x - zm.x));
-      const float2 WB = cmul(cispi(-2.0f * (float)kk / (float)L), B);
-      F = make_float2(A.x + WB.x, A.y + WB.y);
-    } else {
-      F = X[kk];
+  for (int kb = k0; kb < k1; kb += 8) {
+    float2 zk[8], zm[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kk = min(kb + i, k1 - 1);
+      if (even) {
+        zk[i] = X[kk % Np];
+        zm[i] = X[(Np - kk % Np) % Np];
+      } else {
+        zk[i] = X[kk];
+      }
     }
-    Fb[kk] = F;
-    esum += (double)F.x * F.x + (double)F.y * F.y;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kk = kb + i;
+      if (kk >= k1) continue;
+      float2 F;
+      if (even) {
+        const float2 A = make_float2(0.5f * (zk[i].x + zm[i].x), 0.5f * (zk[i].y - zm[i].y));
+        const float2 B = make_float2(0.5f * (zk[i].y + zm[i].y), -0.5f * (zk[i].x - zm[i].x));
+        const float2 WB = cmul(cispi(-2.0f * (float)kk / (float)L), B);
+        F = make_float2(A.x + WB.x, A.y + WB.y);
+      } else {
+        F = zk[i];
+      }
+      Fb[kk] = F;
+      esum += (double)F.x * F.x + (double)F.y * F.y;
+    }
   }
   double total;
   const double before = block_scan<double>(esum, sh.sd, &total);
@@ -1242,10 +1282,16 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_spectrum_kernel(KvcDesc D, int 
   {
     double e = before;
     int cand = L;
-    for (int kk = k0; kk < k1; ++kk) {
-      const float2 F = Fb[kk];
-      e += (double)F.x * F.x + (double)F.y * F.y;
-      if (e >= target && cand == L) cand = kk;
+    for (int kb = k0; kb < k1; kb += 8) {
+      float2 F[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) F[i] = Fb[min(kb + i, k1 - 1)];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (kb + i >= k1) continue;
+        e += (double)F[i].x * F[i].x + (double)F[i].y * F[i].y;
+        if (e >= target && cand == L) cand = kb + i;
+      }
     }
     if (cand < L) atomicMin(&sh.kstar, cand);
   }
@@ -1253,24 +1299,53 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_spectrum_kernel(KvcDesc D, int 
   const int kstar = sh.kstar;
   if ((mode & 4) && t == 0) kstar_out[u] = kstar;
   // Masked spectrum merged back to the complex sequence z the inverse
-  // transforms (as conj(DFT(conj z)) / Np), premultiplied by conj(w_n).
-  auto Fm = [&](int kk) { return kk <= kstar ? Fb[kk] : make_float2(0.f, 0.f); };
-  const float2* cwr = cw;
-  for (int j = t; j < KVC_BIG_H; j += SSS_T) {
-    kvc_big_split<S>(Y, j, M, [&](int n) {
-      if (n >= Np) return make_float2(0.f, 0.f);
+  // transforms (as conj(DFT(conj z)) / Np), premultiplied by conj(w_n):
+  // a_n into X (free now), then split into Y.
+  auto Fm = [&](int kk, float2 v) { return kk <= kstar ? v : make_float2(0.f, 0.f); };
+  for (int n0 = t; n0 < Np; n0 += 8 * SSS_T) {
+    float2 f1[8], f2[8], c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = min(n0 + i * SSS_T, Np - 1);
+      // even: bins n and Np - n; odd: bin n or L - n
+      const int i1 = even ? n : (n <= (L - 1) / 2 ? n : L - n);
+      const int i2 = even ? Np - n : i1;
+      f1[i] = Fb[min(i1, kstar)];   // (masked below; the index kept in bounds)
+      f2[i] = Fb[min(i2, kstar)];
+      c[i] = cw[n];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = n0 + i * SSS_T;
+      if (n >= Np) continue;
       float2 z;
       if (even) {
-        const float2 Fk = Fm(n), Fr = Fm(Np - n);
+        const float2 Fk = Fm(n, f1[i]), Fr = Fm(Np - n, f2[i]);
         const float2 A = make_float2(0.5f * (Fk.x + Fr.x), 0.5f * (Fk.y - Fr.y));
         const float2 Dd = make_float2(0.5f * (Fk.x - Fr.x), 0.5f * (Fk.y + Fr.y));
         const float2 B = cmul(cispi(2.0f * (float)n / (float)L), Dd);
         z = make_float2(A.x - B.y, A.y + B.x);
       } else {
-        z = n <= (L - 1) / 2 ? Fm(n) : conjf2(Fm(L - n));
+        z = n <= (L - 1) / 2 ? Fm(n, f1[i]) : conjf2(Fm(L - n, f1[i]));
       }
-      return cmul(conjf2(z), cwr[n]);
-    });
+      X[n] = cmul(conjf2(z), c[i]);
+    }
+  }
+  __syncthreads();
+  for (int j0 = t; j0 < H; j0 += KB * SSS_T) {
+    float2 a[KB][S];
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+#pragma unroll
+      for (int q = 0; q < S; ++q) {
+        const int n = j0 + i * SSS_T + q * H;
+        a[i][q] = n < Np ? X[n] : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int j = j0 + i * SSS_T;
+      if (j < H) kvc_big_split<S>(Y, j, M, [&](int n) { return a[i][(n - j) / H]; });
+    }
   }
 }
 
@@ -1283,7 +1358,7 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_finish_kernel(
     float* __restrict__ s_hat_out, const int32_t* __restrict__ budgets,
     const int64_t* __restrict__ offsets, int32_t* __restrict__ idx_out,
     float2* __restrict__ base) {
-  constexpr int M = S * KVC_BIG_H;
+  constexpr int M = S * KVC_BIG_H, H = KVC_BIG_H, KB = kvc_big_batch<S>();
   constexpr int kStage = 32768;
   static_assert(2 * VS * SSS_T >= 32768, "selection layout covers the row");
   __shared__ int stage[kStage];
@@ -1305,22 +1380,41 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_finish_kernel(
     float* hrow = (mode & 4) ? s_hat_out + row : nullptr;
     const float invM = 1.0f / (float)M, invNp = 1.0f / (float)Np;
     const float a = D.alpha, oma = 1.0f - D.alpha;
-    for (int m = t; m < Np; m += SSS_T) {
-      const float2 q = kvc_big_combine<S>(Y, m, M);
-      const float2 x = cmul(cw[m], make_float2(q.x * invM, -q.y * invM));
-      const float lre = x.x * invNp, lim = -x.y * invNp;
-      if (even) {
-        const float h0 = oma * srow[2 * m] + a * lre, h1 = oma * srow[2 * m + 1] + a * lim;
-        hs[2 * m] = h0;
-        hs[2 * m + 1] = h1;
-        if (hrow) {
-          hrow[2 * m] = h0;
-          hrow[2 * m + 1] = h1;
+    for (int m0 = t; m0 < Np; m0 += KB * SSS_T) {
+      float2 e[KB][S], c[KB], sv[KB];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const int m = min(m0 + i * SSS_T, Np - 1);
+#pragma unroll
+        for (int r = 0; r < S; ++r) e[i][r] = Y[(size_t)r * H + (m & (H - 1))];
+        c[i] = cw[m];
+        sv[i] = even ? make_float2(srow[2 * m], srow[2 * m + 1]) : make_float2(srow[m], 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const int m = m0 + i * SSS_T;
+        if (m >= Np) continue;
+        float2 q = e[i][0];
+#pragma unroll
+        for (int r = 1; r < S; ++r) {
+          const float2 v = cmul(e[i][r], kvc_twiddle(r * m, M));
+          q = make_float2(q.x + v.x, q.y + v.y);
         }
-      } else {
-        const float h = oma * srow[m] + a * lre;
-        hs[m] = h;
-        if (hrow) hrow[m] = h;
+        const float2 x = cmul(c[i], make_float2(q.x * invM, -q.y * invM));
+        const float lre = x.x * invNp, lim = -x.y * invNp;
+        if (even) {
+          const float h0 = oma * sv[i].x + a * lre, h1 = oma * sv[i].y + a * lim;
+          hs[2 * m] = h0;
+          hs[2 * m + 1] = h1;
+          if (hrow) {
+            hrow[2 * m] = h0;
+            hrow[2 * m + 1] = h1;
+          }
+        } else {
+          const float h = oma * sv[i].x + a * lre;
+          hs[m] = h;
+          if (hrow) hrow[m] = h;
+        }
       }
     }
     if (!(mode & 2)) return;
