@@ -151,6 +151,12 @@ def cpu_baseline(cfg, hdr, prob_units, budgets, max_units=8):
                 one_thread_value=L0 / dt1, affinity_cores=affinity, cpu_model=cpu_model())
 
 
+def summed_traffic(kernel_file: str, kernels, workload: str):
+    """Sum of committed_traffic over a step's kernels (None if any is missing)."""
+    parts = [committed_traffic(kernel_file, k, workload) for k in kernels]
+    return None if any(x is None for x in parts) else sum(parts)
+
+
 def decode_bytes(cfg):
     """Algorithmic bytes of one decode step: per cache, K read once for the
     logits, the new token's queries, A_prev read, kept K and V rows read and
@@ -244,6 +250,8 @@ def bench_decode(args):
                                                    + cfg.gqa * cfg.head_dim * 2 + 12 * n + 4)
         i_gbs = ib / (in_ms * 1e-3) / 1e9
         inplace = {"us_per_step": round(in_ms * 1e3, 2),
+                   "traffic": summed_traffic("voxzip.hip", ("vz_logits_bf16_kernel", "vz_accum_kernel",
+                                                            "vz_slot_evict_kernel"), cfg.name),
                    "cache_rows_per_s": sum(int(n) for n in cfg.lens) * cfg.n_layers
                    * cfg.n_kv_heads / (in_ms * 1e-3),
                    "algorithmic_bytes_per_step": ib,
@@ -633,7 +641,9 @@ def bench_wnw(args):
             "chunk_scores": {"bound": "hbm", "kernel": "wnw_logits_kernel + wnw_lse_kernel + wnw_mass_kernel",
                              "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
-                             "traffic": None},
+                             "traffic": summed_traffic("wnw.hip", ("wnw_logits_kernel",
+                                                                   "wnw_lse_kernel",
+                                                                   "wnw_mass_kernel"), cfg.name)},
         },
     }
     if not args.no_cpu_baseline:
