@@ -12,7 +12,7 @@
 #define KVC_MAX_GW 256
 
 // Keys covered by one score workgroup (a "tile"); shorter rows use one tile.
-#define KVC_TILE_KEYS 1024
+#define KVC_TILE_KEYS 2048
 // Threads of the smoothing/selection workgroup (one workgroup per unit).
 #define KVC_SSS_THREADS 1024
 

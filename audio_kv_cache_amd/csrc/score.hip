@@ -8,7 +8,7 @@
 // the softmax taken over all L audio keys.
 //
 // Two passes over K, both GEMM-shaped (Q [G W, d] x K^T [d, keys]):
-//   stats  per query (max, sum of exp) of each 1024-key tile, folded per
+//   stats  per query (max, sum of exp) of each 2048-key tile, folded per
 //          unit into LSE (log2 units) by a small kernel after it
 //   pool   recompute the logits, p = exp2(l*c - LSE2), sum over the G*W
 //          queries, write s.

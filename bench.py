@@ -66,11 +66,15 @@ def algorithmic_bytes(cfg, hdr, budgets):
         # the fp32 score rows written
         pool=k_read + q_read + 4 * gw * n_units + 4 * tok,
         # statistics pass: K and queries read, one (max, sum) pair per query
-        # and 1024-key tile written
-        stats=k_read + q_read + 8 * gw * sum(-(-int(L) // 1024) for L in hdr.lengths)
+        # and score tile (SCORE_TILE_KEYS keys) written
+        stats=k_read + q_read + 8 * gw * sum(-(-int(L) // SCORE_TILE_KEYS) for L in hdr.lengths)
         * per_seq_units,
         # both passes: one G*W x d by d x L product per unit
         score_flops=2 * gw * d * tok)
+
+
+# keys per score workgroup in the library (KVC_TILE_KEYS)
+SCORE_TILE_KEYS = 2048
 
 
 def source_hash(*names):

@@ -81,9 +81,10 @@ int main(void) {
   CHECK(kvc_smooth(&p, &prm, NULL, fake, fake, NULL, 0, NULL) == KVC_ERR_INVALID_ARG);
   CHECK(kvc_select(&p, &prm, fake, NULL, fake, fake, NULL) == KVC_ERR_INVALID_ARG);
   CHECK(kvc_gather(&p, &prm, fake, fake, fake, fake, NULL, fake, NULL) == KVC_ERR_INVALID_ARG);
-  const int64_t st3[2] = {0, 65536};
-  const double r3[1] = {0.2};
-  kvc_problem big = prob(1, st3, r3, 48, 4, 8, 128, 65536);
+  /* two 65536-token sequences: a workspace beyond the static array */
+  const int64_t st3[3] = {0, 65536, 131072};
+  const double r3[2] = {0.2, 0.2};
+  kvc_problem big = prob(2, st3, r3, 48, 4, 8, 128, 131072);
   CHECK(kvc_compress_noalloc(&big, &prm, fake, fake, fake, fake, fake, fake, fake, fake, fake,
                              NULL) == KVC_ERR_WORKSPACE);
   for (int s = 0; s < 8; ++s) CHECK(kvc_status_str((kvc_status)s) != NULL);

@@ -421,7 +421,7 @@ def test_noalloc_entry_point_rejects_before_touching_the_device():
     # A problem whose workspace exceeds the static array, and null pointers,
     # are refused on the host (dummy pointers are never dereferenced).
     L = C.lib()
-    big = spec(seq_lens=[65536], retention=0.2)          # about 72 MiB of workspace
+    big = spec(seq_lens=[65536, 65536], retention=0.2)   # about 120 MiB of workspace
     prm = api.Params()
     assert api.kvc_plan(big, prm)[1] > C.KVC_NOALLOC_MAX_WORKSPACE
     fake = ctypes.c_void_p(1 << 20)

@@ -66,10 +66,11 @@ def test_noalloc_equals_compress_on_two_calls_in_a_row():
 
 
 def test_noalloc_rejects_problems_over_the_limit():
-    cfg = synth.CONFIGS["long64k"]            # about 72 MiB of workspace
+    cfg = synth.CONFIGS["long64k"]            # two of them: about 120 MiB of workspace
     hdr = synth.header(cfg)
     spec = api.Spec(n_layers=cfg.n_layers, n_kv_heads=cfg.n_kv_heads, gqa=cfg.gqa,
-                    head_dim=cfg.head_dim, seq_lens=hdr.lengths, retention=hdr.retention,
+                    head_dim=cfg.head_dim, seq_lens=list(hdr.lengths) * 2,
+                    retention=list(hdr.retention) * 2,
                     dtype=cfg.dtype, n_window=cfg.n_window)
     prm = api.Params(cfg.alpha, cfg.rho, cfg.window, cfg.base_ratio)
     assert api.kvc_plan(spec, prm)[1] > C.KVC_NOALLOC_MAX_WORKSPACE
