@@ -54,7 +54,6 @@ static constexpr float kSin32[16] = {
     0.83146961230254523708f, 0.70710678118654752440f, 0.55557023301960222474f,
     0.38268343236508977173f, 0.19509032201612826785f};
 
-__device__ __forceinline__ int phys(int a) { return a; }
 
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
   return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
@@ -170,50 +169,56 @@ __device__ __forceinline__ void exchange(float (&re)[V], float (&im)[V], float* 
                                          WF widx, RF ridx, Extra& x) {
   if (act) {
 #pragma unroll
-    for (int s = 0; s < V; ++s) lds[phys(widx(s))] = re[s];
-    if (x.xw >= 0) lds[phys(x.xw)] = x.wre;
+    for (int s = 0; s < V; ++s) lds[widx(s)] = re[s];
+    if (x.xw >= 0) lds[x.xw] = x.wre;
   }
   __syncthreads();
   if (act) {
 #pragma unroll
-    for (int s = 0; s < V; ++s) re[s] = lds[phys(ridx(s))];
-    if (x.xr >= 0) x.rre = lds[phys(x.xr)];
+    for (int s = 0; s < V; ++s) re[s] = lds[ridx(s)];
+    if (x.xr >= 0) x.rre = lds[x.xr];
   }
   __syncthreads();
   if (act) {
 #pragma unroll
-    for (int s = 0; s < V; ++s) lds[phys(widx(s))] = im[s];
-    if (x.xw >= 0) lds[phys(x.xw)] = x.wim;
+    for (int s = 0; s < V; ++s) lds[widx(s)] = im[s];
+    if (x.xw >= 0) lds[x.xw] = x.wim;
   }
   __syncthreads();
   if (act) {
 #pragma unroll
-    for (int s = 0; s < V; ++s) im[s] = lds[phys(ridx(s))];
-    if (x.xr >= 0) x.rim = lds[phys(x.xr)];
+    for (int s = 0; s < V; ++s) im[s] = lds[ridx(s)];
+    if (x.xr >= 0) x.rim = lds[x.xr];
   }
   __syncthreads();
 }
 
 // Same exchange with real and imaginary parts moved together (when the LDS
-// buffer holds N complex values): two barriers instead of four.
-template <int V, class WF, class RF>
+// buffer holds N complex values): two barriers instead of four.  PAD: see
+// xchg.
+template <int V, bool PAD, class WF, class RF>
 __device__ __forceinline__ void exchange2(float (&re)[V], float (&im)[V], float2* lds, bool act,
                                           WF widx, RF ridx, Extra& x) {
+  auto phys2 = [](int a) {
+    if constexpr (!PAD) return a;
+    asm volatile("" : "+v"(a));  // computed at its use, not shared across exchanges
+    return a + (a >> 4);
+  };
   if (act) {
 #pragma unroll
-    for (int s = 0; s < V; ++s) lds[widx(s)] = make_float2(re[s], im[s]);
-    if (x.xw >= 0) lds[x.xw] = make_float2(x.wre, x.wim);
+    for (int s = 0; s < V; ++s) lds[phys2(widx(s))] = make_float2(re[s], im[s]);
+    if (x.xw >= 0) lds[phys2(x.xw)] = make_float2(x.wre, x.wim);
   }
   __syncthreads();
   if (act) {
 #pragma unroll
     for (int s = 0; s < V; ++s) {
-      const float2 v = lds[ridx(s)];
+      const float2 v = lds[phys2(ridx(s))];
       re[s] = v.x;
       im[s] = v.y;
     }
     if (x.xr >= 0) {
-      const float2 v = lds[x.xr];
+      const float2 v = lds[phys2(x.xr)];
       x.rre = v.x;
       x.rim = v.y;
     }
@@ -226,14 +231,24 @@ __device__ __forceinline__ void exchange2(float (&re)[V], float (&im)[V], float2
 template <int N>
 struct Xbuf {
   static constexpr bool kPair = N <= 16384;
-  static constexpr int kFloats = kPair ? 2 * N : N;
+  static constexpr int kFloats = kPair ? 2 * N : N;            // positions, in floats
+  static constexpr int kPhys = kPair ? kFloats + kFloats / 16 : kFloats;  // with the pads
 };
 
-template <int N, int V, class WF, class RF>
+// PAD: the exchange's positions sit in LDS with one unused slot after every
+// 16 complex values (128 bytes, one pass over the banks).  A side of an
+// exchange that steps through positions 16 apart across lanes (a first
+// pass's output, natural chunks of 16) then falls on distinct banks instead
+// of on one, while runs of consecutive positions stay consecutive.  The
+// buffer holds data only within one exchange, so each exchange picks its
+// own layout.  Which exchanges take it is chosen per kernel: the padded
+// address costs registers, and these kernels sit at their register limit.
+template <int N, int V, bool PAD = false, class WF, class RF>
 __device__ __forceinline__ void xchg(float (&re)[V], float (&im)[V], float* lds, bool act, WF widx,
                                      RF ridx, Extra& x) {
+  static_assert(!PAD || Xbuf<N>::kPair, "the padded layout is for complex-pair buffers");
   if constexpr (Xbuf<N>::kPair)
-    exchange2<V>(re, im, reinterpret_cast<float2*>(lds), act, widx, ridx, x);
+    exchange2<V, PAD>(re, im, reinterpret_cast<float2*>(lds), act, widx, ridx, x);
   else
     exchange<V>(re, im, lds, act, widx, ridx, x);
 }
@@ -247,7 +262,9 @@ __host__ __device__ constexpr int fft_radix(int N, int V, int Ns, int RM) {
 // Forward complex FFT of length N = T V, passes from sub-length Ns on.  On
 // entry slot s holds x[in_index<fft_radix(N, V, 1, RM), T, N>(s)]; on exit
 // slot s holds X[ridx_final(s)] (plus the extra read of `xf`, if any).
-template <int N, int V, int Ns, int RM = 32, class RF>
+// PAD1: the first pass's exchange uses the padded layout, PADF: the last
+// one does (the buffer then needs Xbuf<N>::kPhys floats).
+template <int N, int V, int Ns, int RM = 32, bool PAD1 = false, bool PADF = false, class RF>
 __device__ __forceinline__ void fft_stages(float (&re)[V], float (&im)[V], float* lds, int t,
                                            bool act, RF ridx_final, Extra& xf) {
   constexpr int T = N / V;
@@ -256,12 +273,13 @@ __device__ __forceinline__ void fft_stages(float (&re)[V], float (&im)[V], float
   if (act) fft_pass<V, R, T, Ns>(re, im, t);
   auto wf = [&](int s) { return out_index<R, T, Ns>(s, t); };
   if constexpr (Nn >= N) {
-    xchg<N, V>(re, im, lds, act, wf, ridx_final, xf);
+    xchg<N, V, (PAD1 && Ns == 1) || PADF>(re, im, lds, act, wf, ridx_final, xf);
   } else {
     constexpr int R2 = fft_radix(N, V, Nn, RM);
     Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
-    xchg<N, V>(re, im, lds, act, wf, [&](int s) { return in_index<R2, T, N>(s, t); }, none);
-    fft_stages<N, V, Nn, RM>(re, im, lds, t, act, ridx_final, xf);
+    xchg<N, V, PAD1 && Ns == 1>(re, im, lds, act, wf,
+                                [&](int s) { return in_index<R2, T, N>(s, t); }, none);
+    fft_stages<N, V, Nn, RM, false, PADF>(re, im, lds, t, act, ridx_final, xf);
   }
 }
 
@@ -341,7 +359,7 @@ __device__ __forceinline__ void smooth_unit(const KvcDesc& D, int mode, int u, c
     return s < hv ? k : ((N - k) & (N - 1));
   };
   Extra xf{-1, (t == 0) ? N / 2 : -1, 0.f, 0.f, 0.f, 0.f};
-  fft_stages<N, V, 1, RM>(re, im, lds, t, act, pair_idx, xf);
+  fft_stages<N, V, 1, RM, Xbuf<N>::kPair>(re, im, lds, t, act, pair_idx, xf);
 
   // Real spectrum: F_k = A_k + e^{-2 pi i k/L} B_k with
   // A_k = (Z_k + conj Z_{N-k})/2, B_k = (Z_k - conj Z_{N-k})/(2i); the mirror
@@ -483,7 +501,8 @@ __device__ __forceinline__ void smooth_unit(const KvcDesc& D, int mode, int u, c
 #pragma unroll
   for (int s = 0; s < V; ++s) im[s] = -im[s];
   Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
-  fft_stages<N, V, 1, RM>(re, im, lds, t, act, [&](int s) { return t * V + s; }, none);
+  fft_stages<N, V, 1, RM, Xbuf<N>::kPair, Xbuf<N>::kPair>(re, im, lds, t, act,
+                                                          [&](int s) { return t * V + s; }, none);
 
   // Blend with the raw row: s_hat = (1 - alpha) s + alpha lowpass.
   const float invN = 1.0f / (float)N;
@@ -681,7 +700,7 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_select_kernel(
   constexpr int L = 2 * N;
   constexpr int V = kvc_sss_v(N);
   constexpr int T = N / V;
-  __shared__ __attribute__((aligned(16))) float lds[Xbuf<N>::kFloats];
+  __shared__ __attribute__((aligned(16))) float lds[Xbuf<N>::kPhys];
   __shared__ SssShared sh;
   // This launch covers the group's units, all of one length.
   const int u = kvc_group_unit(G, D.upseq, (int)blockIdx.x);
