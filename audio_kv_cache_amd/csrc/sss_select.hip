@@ -307,6 +307,54 @@ __device__ __forceinline__ X block_scan(X v, X* sw, X* total) {
   return before + incl - v;
 }
 
+// Wave sum and wave exclusive prefix of small non-negative ints (v <
+// 2^BITS), one ballot per bit of v: a few scalar and VALU instructions
+// instead of a chain of cross-lane permutes through LDS.  The sum is
+// wave-uniform.
+template <int BITS>
+__device__ __forceinline__ int wave_sum_small(int v) {
+  int s = 0;
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) s += __popcll(__ballot((v >> b) & 1)) << b;
+  return s;
+}
+template <int BITS>
+__device__ __forceinline__ int wave_prefix_small(int v, int* wave_total) {
+  int p = 0, s = 0;
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) {
+    const uint64_t m = __ballot((v >> b) & 1);
+    const int below = (int)__builtin_amdgcn_mbcnt_hi(
+        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    p += below << b;
+    s += __popcll(m) << b;
+  }
+  *wave_total = s;
+  return p;
+}
+// block_scan for ints in [0, 2^BITS).
+template <int BITS>
+__device__ __forceinline__ int block_scan_small(int v, int* sw, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int wt;
+  const int p = wave_prefix_small<BITS>(v, &wt);
+  if (lane == 0) sw[w] = wt;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < SSS_WAVES; ++i) {
+    const int x = sw[i];
+    if (i < w) before += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + p;
+}
+
+// Bits of a count of at most n.
+__host__ __device__ constexpr int count_bits(int n) { return n < 2 ? 1 : 1 + count_bits(n / 2); }
+
 __device__ __forceinline__ uint32_t order_key(float f) {
   if (f == 0.0f) f = 0.0f;  // -0 and +0 are equal
   const uint32_t b = __float_as_uint(f);
@@ -316,7 +364,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 struct SssShared {
   double sd[SSS_WAVES];
   int si[SSS_WAVES];
-  int s3[2][3][SSS_WAVES];
+  int bitcnt[32];   // per threshold bit: keys hit over the block
   int kstar;
 };
 
@@ -562,6 +610,15 @@ __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, int L, floa
   const int b = budgets[u];
   const int k = b - w;
   const int64_t off = offsets[u];
+  // A row kept whole (k >= ncand: every position) or down to its window
+  // (k <= 0: positions ncand .. L-1) is a run of consecutive positions:
+  // written directly, with no threshold search and no staging.
+  if (k >= ncand || k <= 0) {
+    const int lo = k >= ncand ? 0 : max(0, ncand);
+    const int n = min(b, L - lo);
+    for (int i = threadIdx.x; i < n; i += SSS_T) idx_out[off + i] = lo + i;
+    return;
+  }
   // Order-preserving keys of the thread's slots s (position p0 + s; slot
   // s is re[s/2] for even s, im[s/2] for odd s), transposed into planes per
   // group of 32 slots.  Slots past the row or the candidates never enter
@@ -588,37 +645,38 @@ __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, int L, floa
   }
 
   // Largest T with #{key >= T} >= k, bit by bit from the top; one barrier
-  // per bit (the reduction slots alternate between bits).  Per bit, the
-  // keys still equal to T's prefix with that bit set are `hit`: they stay
-  // equal if T takes the bit, else they are above T from then on.
-  if (k > 0 && k < ncand) {
-    int acnt = 0;
+  // per bit.  Per bit, the keys still equal to T's prefix with that bit set
+  // are `hit`: they stay equal if T takes the bit, else they are above T
+  // from then on.  Each wave adds its count of hits to the bit's LDS
+  // counter; `A` counts the keys above T so far over the whole block.  Both
+  // are wave-uniform (scalar registers), so the decision is a scalar
+  // branch.
+  constexpr int CB = count_bits(2 * V);  // a thread holds at most 2V keys
+  if (threadIdx.x < 32) sh.bitcnt[threadIdx.x] = 0;
+  __syncthreads();
+  int A = 0;
 #pragma unroll
-    for (int bit = 31; bit >= 0; --bit) {
-      uint32_t hit[NG];
-      int cnt = acnt;
+  for (int bit = 31; bit >= 0; --bit) {
+    uint32_t hit[NG];
+    int h = 0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      hit[g] = match[g] & P[g][bit];
+      h += __popc(hit[g]);
+    }
+    const int hw = wave_sum_small<CB>(h);
+    if ((threadIdx.x & 63) == 0) atomicAdd(&sh.bitcnt[bit], hw);
+    __syncthreads();
+    const int tot = A + __builtin_amdgcn_readfirstlane(sh.bitcnt[bit]);
+    if (tot >= k) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) match[g] = hit[g];
+    } else {
+      A = tot;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        hit[g] = match[g] & P[g][bit];
-        cnt += __popc(hit[g]);
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
-      if ((threadIdx.x & 63) == 0) sh.s3[bit & 1][0][threadIdx.x >> 6] = cnt;
-      __syncthreads();
-      int tot = 0;
-#pragma unroll
-      for (int i = 0; i < SSS_WAVES; ++i) tot += sh.s3[bit & 1][0][i];
-      if (tot >= k) {
-#pragma unroll
-        for (int g = 0; g < NG; ++g) match[g] = hit[g];
-      } else {
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          above[g] |= hit[g];
-          acnt += __popc(hit[g]);
-          match[g] &= ~P[g][bit];
-        }
+        above[g] |= hit[g];
+        match[g] &= ~P[g][bit];
       }
     }
   }
@@ -630,11 +688,9 @@ __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, int L, floa
     neq += __popc(match[g]);
   }
   int gt_total, eq_total;
-  const int eq_before = block_scan<int>(neq, sh.si, &eq_total);
-  block_scan<int>(ngt, sh.si, &gt_total);
+  const int eq_before = block_scan_small<CB>(neq, sh.si, &eq_total);
+  block_scan_small<CB>(ngt, sh.si, &gt_total);
   (void)eq_total;
-  const bool take_all = k >= ncand;
-  const bool take_none = k <= 0;
   const int need = k - gt_total;  // positions equal to thr to keep, lowest first
 
   int nsel = 0, er = eq_before;
@@ -647,8 +703,6 @@ __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, int L, floa
       const bool eq = (match[s >> 5] >> (s & 31)) & 1u;
       bool sel;
       if (p >= ncand) sel = p < L;
-      else if (take_all) sel = true;
-      else if (take_none) sel = false;
       else if (gt) sel = true;
       else if (eq) sel = (er++ < need);
       else sel = false;
@@ -660,19 +714,23 @@ __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, int L, floa
     }
   }
   int nsel_total;
-  const int base = block_scan<int>(nsel, sh.si, &nsel_total);
-  if (b <= kStage) {
+  const int base = block_scan_small<CB>(nsel, sh.si, &nsel_total);
+  // Staged output: position j of the segment at LDS int j + j/32, so that
+  // threads whose runs start 32 apart (dense selections) write to distinct
+  // banks.
+  auto sidx = [](int j) { return j + (j >> 5); };
+  if (b + (b >> 5) <= kStage) {
     // Compact into LDS, then one coalesced copy of the b positions.
     if (act) {
       int o = 0;
 #pragma unroll
       for (int s = 0; s < 2 * V; ++s) {
         const bool sel = (s < 32) ? ((selmask_lo >> s) & 1u) : ((selmask_hi >> (s - 32)) & 1u);
-        if (sel && base + o < b) stage[base + (o++)] = p0 + s;
+        if (sel && base + o < b) stage[sidx(base + (o++))] = p0 + s;
       }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < b; i += SSS_T) idx_out[off + i] = stage[i];
+    for (int i = threadIdx.x; i < b; i += SSS_T) idx_out[off + i] = stage[sidx(i)];
   } else if (act) {
     int o = 0;
 #pragma unroll
@@ -725,7 +783,7 @@ __global__ __launch_bounds__(SSS_T) void kvc_sss_select_kernel(
   if (mode & 2) {
     __syncthreads();  // the exchange buffer becomes the output staging area
     select_unit<V>(D, u, L, re, im, budgets, offsets, idx_out, sh, reinterpret_cast<int*>(lds),
-                   Xbuf<N>::kFloats, t, act);
+                   Xbuf<N>::kPhys, t, act);
   }
 }
 
