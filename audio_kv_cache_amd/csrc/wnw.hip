@@ -527,13 +527,28 @@ __global__ __launch_bounds__(256) void wnw_fixed_select_kernel(KvcDesc D, int se
     const uint32_t key = valid ? wnw_order_key(row[lo + lane]) : 0u;
     skey[wave][lane] = key;   // the wave's own row: no barrier needed
     __builtin_amdgcn_wave_barrier();
+    // Rank = keys above, then equal keys at lower positions.  The padding
+    // (key 0) is above no key, so the first count needs no bound.  Without
+    // equal keys the ranks of the segment are 0 .. len-1 once each, and
+    // equal keys share a rank, which lowers the sum: only then is the
+    // tie-breaking count run (a uniform branch).
     int rank = 0;
     for (int o = 0; o < len; o += 4) {
       const uint4 kq = *reinterpret_cast<const uint4*>(&skey[wave][o]);   // same for every lane
-      const uint32_t ko[4] = {kq.x, kq.y, kq.z, kq.w};
+      rank += (kq.x > key) + (kq.y > key) + (kq.z > key) + (kq.w > key);
+    }
+    int rsum = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        rank += (o + e < len) && ((ko[e] > key) || (ko[e] == key && o + e < lane));
+    for (int b = 0; b < 6; ++b) rsum += __popcll(__ballot(valid && ((rank >> b) & 1))) << b;
+    if (rsum != len * (len - 1) / 2) {
+      rank = 0;
+      for (int o = 0; o < len; o += 4) {
+        const uint4 kq = *reinterpret_cast<const uint4*>(&skey[wave][o]);
+        const uint32_t ko[4] = {kq.x, kq.y, kq.z, kq.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          rank += (o + e < len) && ((ko[e] > key) || (ko[e] == key && o + e < lane));
+      }
     }
     __builtin_amdgcn_wave_barrier();
     const bool take = valid && rank < quota;
