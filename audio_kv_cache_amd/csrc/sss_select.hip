@@ -238,8 +238,8 @@ struct Xbuf {
 // PAD: the exchange's positions sit in LDS with one unused slot after every
 // 16 complex values (128 bytes, one pass over the banks).  A side of an
 // exchange that steps through positions 16 apart across lanes (a first
-// pass's output, natural chunks of 16) then falls on distinct banks instead
-// of on one, while runs of consecutive positions stay consecutive.  The
+// radix-16 pass's output) then falls on distinct banks instead of on one,
+// while runs of consecutive positions stay consecutive.  The
 // buffer holds data only within one exchange, so each exchange picks its
 // own layout.  Which exchanges take it is chosen per kernel: the padded
 // address costs registers, and these kernels sit at their register limit.
@@ -262,9 +262,9 @@ __host__ __device__ constexpr int fft_radix(int N, int V, int Ns, int RM) {
 // Forward complex FFT of length N = T V, passes from sub-length Ns on.  On
 // entry slot s holds x[in_index<fft_radix(N, V, 1, RM), T, N>(s)]; on exit
 // slot s holds X[ridx_final(s)] (plus the extra read of `xf`, if any).
-// PAD1: the first pass's exchange uses the padded layout, PADF: the last
-// one does (the buffer then needs Xbuf<N>::kPhys floats).
-template <int N, int V, int Ns, int RM = 32, bool PAD1 = false, bool PADF = false, class RF>
+// PAD1: the first pass's exchange uses the padded layout (the buffer then
+// needs Xbuf<N>::kPhys floats).
+template <int N, int V, int Ns, int RM = 32, bool PAD1 = false, class RF>
 __device__ __forceinline__ void fft_stages(float (&re)[V], float (&im)[V], float* lds, int t,
                                            bool act, RF ridx_final, Extra& xf) {
   constexpr int T = N / V;
@@ -273,13 +273,13 @@ __device__ __forceinline__ void fft_stages(float (&re)[V], float (&im)[V], float
   if (act) fft_pass<V, R, T, Ns>(re, im, t);
   auto wf = [&](int s) { return out_index<R, T, Ns>(s, t); };
   if constexpr (Nn >= N) {
-    xchg<N, V, (PAD1 && Ns == 1) || PADF>(re, im, lds, act, wf, ridx_final, xf);
+    xchg<N, V, PAD1 && Ns == 1>(re, im, lds, act, wf, ridx_final, xf);
   } else {
     constexpr int R2 = fft_radix(N, V, Nn, RM);
     Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
     xchg<N, V, PAD1 && Ns == 1>(re, im, lds, act, wf,
                                 [&](int s) { return in_index<R2, T, N>(s, t); }, none);
-    fft_stages<N, V, Nn, RM, false, PADF>(re, im, lds, t, act, ridx_final, xf);
+    fft_stages<N, V, Nn, RM>(re, im, lds, t, act, ridx_final, xf);
   }
 }
 
@@ -549,8 +549,8 @@ __device__ __forceinline__ void smooth_unit(const KvcDesc& D, int mode, int u, c
 #pragma unroll
   for (int s = 0; s < V; ++s) im[s] = -im[s];
   Extra none{-1, -1, 0.f, 0.f, 0.f, 0.f};
-  fft_stages<N, V, 1, RM, Xbuf<N>::kPair, Xbuf<N>::kPair>(re, im, lds, t, act,
-                                                          [&](int s) { return t * V + s; }, none);
+  fft_stages<N, V, 1, RM, Xbuf<N>::kPair>(re, im, lds, t, act, [&](int s) { return t * V + s; },
+                                          none);
 
   // Blend with the raw row: s_hat = (1 - alpha) s + alpha lowpass.
   const float invN = 1.0f / (float)N;
