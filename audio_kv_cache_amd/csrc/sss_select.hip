@@ -605,6 +605,7 @@ __device__ __forceinline__ void select_unit(const KvcDesc& D, int u, int L, floa
                             float (&im)[V], const int32_t* budgets, const int64_t* offsets,
                             int32_t* idx_out, SssShared& sh, int* stage, int kStage, int t,
                             bool act) {
+  static_assert(2 * V <= 64, "the selection masks hold 64 positions per thread");
   const int w = D.window;
   const int ncand = L - w;
   const int b = budgets[u];
