@@ -366,6 +366,7 @@ struct SssShared {
   int si[SSS_WAVES];
   int bitcnt[32];   // per threshold bit: keys hit over the block
   int kstar;
+  int kstar2;       // the second unit's, where two units share a transform
 };
 
 // e^{i pi x} as (cos, sin); v_sin/v_cos take revolutions (x/2).
@@ -1110,11 +1111,86 @@ __device__ __forceinline__ float2 kvc_quarter(float2 v, int e, int S) {
                                                                     : make_float2(-v.y, v.x);
 }
 
+// Odd lengths have no half-length packing (L real values, Np = L), so two
+// units share each transform instead: the rows of the group's units 2p and
+// 2p + 1 are the real and imaginary parts of one length-L complex sequence
+// (the last unit of an odd count pairs with itself).  The DFT Z of
+// x1 + i x2 gives X1_k = (Z_k + conj Z_{L-k}) / 2 and
+// X2_k = (Z_k - conj Z_{L-k}) / (2i); the inverse of G1 + i G2 for two
+// Hermitian spectra is g1 + i g2 with both parts real.  Each row enters
+// scaled by 2^-e, e chosen so that its L2 norm is in [1, 2): the rounding
+// of one part then stays at the size of the other's (rows of very different
+// sizes would otherwise lose the smaller one's accuracy), and a power of
+// two commutes with every rounding, so the energies, k* and the low-pass
+// row (scaled back by 2^e) come out as without it.  A pair's values live in
+// the scratch slot of its first unit; every unit's exponent in the last
+// value of its own slot.  Even lengths: one unit per slot, no scaling.
+__host__ __device__ inline int kvc_big_items(int nwg, bool paired) {
+  return paired ? (nwg + 1) / 2 : nwg;
+}
+__host__ __device__ inline size_t kvc_big_exp_index(int Np, int M) {
+  return (size_t)M + 2 * (size_t)Np + 1;   // within the slot (BigScratch::ustride)
+}
+
 // Value n of the premultiplied sequence of the first forward transform:
-// a_n = in(n) conj(w_n), in(n) = (s_2n, s_2n+1) for even L, (s_n, 0) for odd.
-__device__ __forceinline__ float2 kvc_big_in(const float* srow, bool even, int n, float2 c) {
-  const float2 x = even ? make_float2(srow[2 * n], srow[2 * n + 1]) : make_float2(srow[n], 0.f);
+// a_n = in(n) conj(w_n), in(n) = (s_2n, s_2n+1) for even L,
+// (s_n 2^-e1, s2_n 2^-e2) for odd L (s2: the pair's second row).
+__device__ __forceinline__ float2 kvc_big_in(const float* srow, const float* srow2, bool even,
+                                             int n, float2 c, int e1, int e2) {
+  const float2 x = even ? make_float2(srow[2 * n], srow[2 * n + 1])
+                        : make_float2(ldexpf(srow[n], -e1), ldexpf(srow2[n], -e2));
   return cmul(x, c);
+}
+
+// The score row of group unit b.
+__device__ __forceinline__ const float* kvc_big_row(const KvcDesc& D, const KvcSeqGroup& G,
+                                                    const float* s_in, int b) {
+  const int u = kvc_group_unit(G, D.upseq, b);
+  const int seq = u / D.upseq, within = u - seq * D.upseq;
+  return s_in + D.srow_base[seq] + (int64_t)within * D.L[seq];
+}
+
+// Odd L: each unit's scale exponent e (L2 norm of the row times 2^-e in
+// [1, 2); 0 for a zero or non-finite norm), into the last value of its
+// slot.  One 1024-thread workgroup per unit, eight loads in flight per
+// thread.
+__global__ __launch_bounds__(SSS_T) void kvc_big_scale_kernel(KvcDesc D, KvcSeqGroup G, int Np,
+                                                              int M, const float* __restrict__ s_in,
+                                                              float2* __restrict__ base) {
+  __shared__ float part[SSS_WAVES];
+  const int b = (int)blockIdx.x;
+  const int L = D.L[G.seq[0]];
+  const float* srow = kvc_big_row(D, G, s_in, b);
+  float acc = 0.f;
+  for (int n0 = threadIdx.x; n0 < L; n0 += 8 * SSS_T) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = n0 + i * SSS_T;
+      v[i] = n < L ? srow[n] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(v[i], v[i], acc);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float ss = 0.f;
+    for (int w = 0; w < SSS_WAVES; ++w) ss += part[w];
+    int e = 0;
+    if (ss > 0.f && ss < INFINITY) {
+      frexpf(sqrtf(ss), &e);   // sqrt(ss) = f 2^e, f in [0.5, 1)
+      e -= 1;                  // 2^-e sqrt(ss) in [1, 2)
+    }
+    const BigScratch bs = kvc_big_scratch(Np, M);
+    float2* slot = base + bs.rows_off + (size_t)b * bs.ustride;
+    slot[kvc_big_exp_index(Np, M)] = make_float2(__int_as_float(e), 0.f);
+  }
+}
+__device__ __forceinline__ int kvc_big_exp(const float2* slot_base, int Np, int M) {
+  return __float_as_int(slot_base[kvc_big_exp_index(Np, M)].x);
 }
 
 // The radix-S split y_r[j] (r < S) of a length-M sequence given by `val`
@@ -1198,7 +1274,9 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_chirp_fft_kernel(float2* __rest
 // conjugation, the second H-point FFT (the decimation-in-time sub-transform
 // of the same sub-sequence), stored in place in natural order.  FROM_ROW:
 // the input is split on the fly from the unit's score row (the first
-// transform); else read from the unit's split values (the second).
+// transform); else read from the unit's split values (the second).  One
+// workgroup per (slot item, sub-sequence): units for even L, unit pairs for
+// odd L.
 template <int S, bool FROM_ROW>
 __global__ __launch_bounds__(SSS_T) void kvc_big_conv_kernel(KvcDesc D, KvcSeqGroup G, int Np,
                                                              const float* __restrict__ s_in,
@@ -1210,16 +1288,20 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_conv_kernel(KvcDesc D, KvcSeqGr
   const BigScratch bs = kvc_big_scratch(Np, M);
   const float2* bhat = base;
   const float2* cw = base + bs.cw_off;
-  const int slot = (int)blockIdx.x / S, r = (int)blockIdx.x % S;
+  const int nwg = G.n * (G.hi - G.lo);
+  const bool even = (D.L[G.seq[0]] & 1) == 0;   // (one length per group)
+  const int item = (int)blockIdx.x / S, r = (int)blockIdx.x % S;
+  const int slot = even ? item : 2 * item;
   float2* y = base + bs.rows_off + (size_t)slot * bs.ustride + (size_t)r * N;
   const int t = threadIdx.x;
   float re[V], im[V];
   if constexpr (FROM_ROW) {
-    const int u = kvc_group_unit(G, D.upseq, slot);
-    const int seq = u / D.upseq, within = u - seq * D.upseq;
-    const int L = D.L[seq];
-    const float* srow = s_in + D.srow_base[seq] + (int64_t)within * L;
-    const bool even = (L & 1) == 0;
+    const float* srow = kvc_big_row(D, G, s_in, slot);
+    const int slot2 = min(slot + 1, nwg - 1);
+    const float* srow2 = even ? srow : kvc_big_row(D, G, s_in, slot2);
+    const float2* slots = base + bs.rows_off;
+    const int e1 = even ? 0 : kvc_big_exp(slots + (size_t)slot * bs.ustride, Np, M);
+    const int e2 = even ? 0 : kvc_big_exp(slots + (size_t)slot2 * bs.ustride, Np, M);
 #pragma unroll
     for (int s = 0; s < V; ++s) {
       const int j = in_index<R0, T, N>(s, t);
@@ -1228,7 +1310,8 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_conv_kernel(KvcDesc D, KvcSeqGr
       for (int q = 0; q < S; ++q) {
         const int n = j + q * N;
         if (n < Np) {
-          const float2 v = kvc_quarter(kvc_big_in(srow, even, n, cw[n]), q * r, S);
+          const float2 v =
+              kvc_quarter(kvc_big_in(srow, srow2, even, n, cw[n], e1, e2), q * r, S);
           acc = make_float2(acc.x + v.x, acc.y + v.y);
         }
       }
@@ -1272,164 +1355,255 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_conv_kernel(KvcDesc D, KvcSeqGr
 template <int S>
 __host__ __device__ constexpr int kvc_big_batch() { return S >= 4 ? 4 : 8; }
 
-// Per unit, after the first convolution: the spectrum X_k (k < Np), the real
-// bins F_0 .. F_{L/2} with their fp64 energies, k*, the masked spectrum
-// merged back to the complex sequence, conjugated and premultiplied for the
-// inverse transform, and its split.  One 1024-thread workgroup per unit.
+// After the first convolution, per slot item (a unit for even L, a unit
+// pair for odd L), in three launches spread over the whole chip:
+//  A (kvc_big_bins_kernel): the real bins F_0 .. F_{L/2} (odd L: of both
+//    units), each from the spectrum values Z_k and Z_{Np-k} combined from the
+//    sub-transforms, and the fp64 energy sum of each of KVC_BIG_CH chunks of
+//    consecutive bins;
+//  B (kvc_big_kstar_kernel): k* from the chunk sums and a block scan of the
+//    one chunk in which the cumulative energy reaches rho of the total;
+//  C (kvc_big_merge_kernel): the masked spectrum merged back to the complex
+//    sequence the inverse transforms (G1 + i G2 for a pair), conjugated and
+//    premultiplied by conj(w_n), and its split into the sub-sequences.
+// In the item's slot: the chunk sums and k* from M on, the bins from
+// M + Np on.
+#define KVC_BIG_CH 16
+
+// Spectrum value k < Np of the first transform from the sub-transforms:
+// Z_k = conj(w_k) conj(sum_r W_M^{rk} E_r[k mod H]) / M.
 template <int S>
-__global__ __launch_bounds__(SSS_T) void kvc_big_spectrum_kernel(KvcDesc D, int mode,
-                                                                 KvcSeqGroup G, int Np,
-                                                                 float2* __restrict__ base,
-                                                                 int32_t* __restrict__ kstar_out) {
-  constexpr int M = S * KVC_BIG_H, H = KVC_BIG_H, KB = kvc_big_batch<S>();
-  __shared__ SssShared sh;
-  const int u = kvc_group_unit(G, D.upseq, (int)blockIdx.x);
-  const int seq = u / D.upseq;
-  const int L = D.L[seq];
-  const bool even = (L & 1) == 0;
-  const int t = threadIdx.x;
-  const BigScratch bs = kvc_big_scratch(Np, M);
-  const float2* cw = base + bs.cw_off;
-  float2* Y = base + bs.rows_off + (size_t)blockIdx.x * bs.ustride;
-  float2* X = Y + M;
-  float2* Fb = X + Np;
+__device__ __forceinline__ float2 kvc_big_spec(const float2* __restrict__ Y,
+                                               const float2* __restrict__ cw, int k, int M) {
+  const int kh = k & (KVC_BIG_H - 1);
+  float2 q = Y[kh];
+#pragma unroll
+  for (int r = 1; r < S; ++r) {
+    const float2 v = cmul(Y[(size_t)r * KVC_BIG_H + kh], kvc_twiddle(r * k, M));
+    q = make_float2(q.x + v.x, q.y + v.y);
+  }
   const float invM = 1.0f / (float)M;
-  // X_k = conj(w_k) conj(sum_r W_M^{rk} E_r[k mod H]) / M
-  for (int k0 = t; k0 < Np; k0 += KB * SSS_T) {
-    float2 e[KB][S], c[KB];
+  return cmul(cw[k], make_float2(q.x * invM, -q.y * invM));
+}
+
+// The slot of item `item`, the chunk sums (two per chunk: unit 1, unit 2)
+// and k* (two) within it.
+struct BigItem {
+  float2* Y;
+  float2* Fb;
+  float2* Fb2;
+  double* sums;
+  int* kst;
+};
+__device__ __forceinline__ BigItem kvc_big_item(float2* base, int Np, int M, int L, int slot) {
+  const BigScratch bs = kvc_big_scratch(Np, M);
+  BigItem it;
+  it.Y = base + bs.rows_off + (size_t)slot * bs.ustride;
+  it.Fb = it.Y + M + Np;
+  it.Fb2 = it.Fb + (L / 2 + 1);   // odd L: the second unit's bins (Np = L)
+  it.sums = reinterpret_cast<double*>(it.Y + M);
+  it.kst = reinterpret_cast<int*>(it.sums + 2 * KVC_BIG_CH);
+  return it;
+}
+
+template <int S>
+__global__ __launch_bounds__(256) void kvc_big_bins_kernel(KvcDesc D, KvcSeqGroup G, int Np,
+                                                           float2* __restrict__ base) {
+  constexpr int M = S * KVC_BIG_H, KB = 4;
+  __shared__ double part[2][4];
+  const int L = D.L[G.seq[0]];   // (one length per group)
+  const bool even = (L & 1) == 0;
+  const int item = (int)blockIdx.x / KVC_BIG_CH, c = (int)blockIdx.x % KVC_BIG_CH;
+  const BigItem it = kvc_big_item(base, Np, M, L, even ? item : 2 * item);
+  const float2* cw = base + kvc_big_scratch(Np, M).cw_off;
+  const int nb = L / 2 + 1, per = (nb + KVC_BIG_CH - 1) / KVC_BIG_CH;
+  const int k0 = min(nb, c * per), k1 = min(nb, k0 + per);
+  double e1 = 0.0, e2 = 0.0;
+  // (KB bins per thread at a time: their loads, then arithmetic and stores)
+  for (int kb = k0 + (int)threadIdx.x; kb < k1; kb += KB * 256) {
+    float2 zk[KB], zm[KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-      const int k = min(k0 + i * SSS_T, Np - 1);   // (clamped: every load in bounds)
-#pragma unroll
-      for (int r = 0; r < S; ++r) e[i][r] = Y[(size_t)r * H + (k & (H - 1))];
-      c[i] = cw[k];
+      const int k = min(kb + i * 256, k1 - 1);   // (clamped: every load in bounds)
+      zk[i] = kvc_big_spec<S>(it.Y, cw, k % Np, M);
+      zm[i] = kvc_big_spec<S>(it.Y, cw, (Np - k % Np) % Np, M);
     }
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-      const int k = k0 + i * SSS_T;
-      if (k >= Np) continue;
-      float2 q = e[i][0];
-#pragma unroll
-      for (int r = 1; r < S; ++r) {
-        const float2 v = cmul(e[i][r], kvc_twiddle(r * k, M));
-        q = make_float2(q.x + v.x, q.y + v.y);
+      const int k = kb + i * 256;
+      if (k >= k1) continue;
+      // A = (Z_k + conj Z_{Np-k}) / 2, B = (Z_k - conj Z_{Np-k}) / (2i)
+      const float2 A = make_float2(0.5f * (zk[i].x + zm[i].x), 0.5f * (zk[i].y - zm[i].y));
+      const float2 B = make_float2(0.5f * (zk[i].y + zm[i].y), -0.5f * (zk[i].x - zm[i].x));
+      if (even) {
+        const float2 WB = cmul(cispi(-2.0f * (float)k / (float)L), B);
+        const float2 F = make_float2(A.x + WB.x, A.y + WB.y);
+        it.Fb[k] = F;
+        e1 += (double)F.x * F.x + (double)F.y * F.y;
+      } else {
+        it.Fb[k] = A;    // the pair's first unit
+        it.Fb2[k] = B;   // and its second
+        e1 += (double)A.x * A.x + (double)A.y * A.y;
+        e2 += (double)B.x * B.x + (double)B.y * B.y;
       }
-      X[k] = cmul(c[i], make_float2(q.x * invM, -q.y * invM));
     }
   }
-  if (t == 0) sh.kstar = L / 2;  // the last bin, should rounding leave E short of rho E(L/2)
-  __syncthreads();
-  // Real bins (unpacked for even L) and their energies in fp64, in
-  // contiguous chunks per thread so that a block scan gives the prefixes.
-  const int nb = L / 2 + 1;
-  const int per = (nb + SSS_T - 1) / SSS_T;
-  const int k0 = min(nb, t * per), k1 = min(nb, k0 + per);
-  double esum = 0.0;
-  for (int kb = k0; kb < k1; kb += 8) {
-    float2 zk[8], zm[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kk = min(kb + i, k1 - 1);
-      if (even) {
-        zk[i] = X[kk % Np];
-        zm[i] = X[(Np - kk % Np) % Np];
-      } else {
-        zk[i] = X[kk];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kk = kb + i;
-      if (kk >= k1) continue;
-      float2 F;
-      if (even) {
-        const float2 A = make_float2(0.5f * (zk[i].x + zm[i].x), 0.5f * (zk[i].y - zm[i].y));
-        const float2 B = make_float2(0.5f * (zk[i].y + zm[i].y), -0.5f * (zk[i].x - zm[i].x));
-        const float2 WB = cmul(cispi(-2.0f * (float)kk / (float)L), B);
-        F = make_float2(A.x + WB.x, A.y + WB.y);
-      } else {
-        F = zk[i];
-      }
-      Fb[kk] = F;
-      esum += (double)F.x * F.x + (double)F.y * F.y;
-    }
+  for (int o = 32; o > 0; o >>= 1) {
+    e1 += __shfl_xor(e1, o);
+    e2 += __shfl_xor(e2, o);
   }
-  double total;
-  const double before = block_scan<double>(esum, sh.sd, &total);
-  const double target = (double)D.rho * total;
-  {
-    double e = before;
-    int cand = L;
-    for (int kb = k0; kb < k1; kb += 8) {
-      float2 F[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) F[i] = Fb[min(kb + i, k1 - 1)];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (kb + i >= k1) continue;
-        e += (double)F[i].x * F[i].x + (double)F[i].y * F[i].y;
-        if (e >= target && cand == L) cand = kb + i;
-      }
-    }
-    if (cand < L) atomicMin(&sh.kstar, cand);
+  if ((threadIdx.x & 63) == 0) {
+    part[0][threadIdx.x >> 6] = e1;
+    part[1][threadIdx.x >> 6] = e2;
   }
   __syncthreads();
-  const int kstar = sh.kstar;
-  if ((mode & 4) && t == 0) kstar_out[u] = kstar;
-  // Masked spectrum merged back to the complex sequence z the inverse
-  // transforms (as conj(DFT(conj z)) / Np), premultiplied by conj(w_n):
-  // a_n into X (free now), then split into Y.
+  if (threadIdx.x == 0) {
+    it.sums[2 * c] = ((part[0][0] + part[0][1]) + part[0][2]) + part[0][3];
+    it.sums[2 * c + 1] = ((part[1][0] + part[1][1]) + part[1][2]) + part[1][3];
+  }
+}
+
+// k* of each unit of the item: the first bin at which the cumulative fp64
+// energy reaches rho of the total (the last bin, should rounding leave the
+// total short).  One 1024-thread workgroup per item.
+template <int S>
+__global__ __launch_bounds__(SSS_T) void kvc_big_kstar_kernel(KvcDesc D, int mode, KvcSeqGroup G,
+                                                              int Np, float2* __restrict__ base,
+                                                              int32_t* __restrict__ kstar_out) {
+  constexpr int M = S * KVC_BIG_H;
+  __shared__ SssShared sh;
+  __shared__ double s_before;
+  __shared__ int s_chunk;
+  const int nwg = G.n * (G.hi - G.lo);
+  const int L = D.L[G.seq[0]];
+  const bool even = (L & 1) == 0;
+  const int slot = even ? (int)blockIdx.x : 2 * (int)blockIdx.x;
+  const int u = kvc_group_unit(G, D.upseq, slot);
+  const int u2 = even ? u : kvc_group_unit(G, D.upseq, min(slot + 1, nwg - 1));
+  const BigItem it = kvc_big_item(base, Np, M, L, slot);
+  const int nb = L / 2 + 1, per = (nb + KVC_BIG_CH - 1) / KVC_BIG_CH;
+  const int t = threadIdx.x;
+  int ks[2] = {L / 2, L / 2};
+  for (int part = 0; part < (even ? 1 : 2); ++part) {
+    const float2* F = part ? it.Fb2 : it.Fb;
+    // the chunk in which the cumulative energy reaches the target
+    if (t == 0) {
+      double total = 0.0;
+      for (int c = 0; c < KVC_BIG_CH; ++c) total += it.sums[2 * c + part];
+      const double target = (double)D.rho * total;
+      double cum = 0.0;
+      int cc = -1;
+      for (int c = 0; c < KVC_BIG_CH && cc < 0; ++c) {
+        if (cum + it.sums[2 * c + part] >= target) cc = c;
+        else cum += it.sums[2 * c + part];
+      }
+      s_chunk = cc;
+      s_before = cum;
+      // (the chunk's last bin, should the bin-by-bin sums fall short of the
+      // chunk's total by rounding)
+      sh.kstar = cc >= 0 ? min(nb, cc * per + per) - 1 : L / 2;
+      sh.sd[0] = target;
+    }
+    __syncthreads();
+    const int cc = s_chunk;
+    const double target = sh.sd[0], before0 = s_before;
+    __syncthreads();
+    if (cc >= 0) {
+      // contiguous runs of the chunk's bins per thread, a block scan of
+      // their energies, then each run walked in order
+      const int c0 = min(nb, cc * per), c1 = min(nb, c0 + per);
+      const int run = (c1 - c0 + SSS_T - 1) / SSS_T;
+      const int r0 = min(c1, c0 + t * run), r1 = min(c1, r0 + run);
+      double esum = 0.0;
+      for (int k = r0; k < r1; ++k) esum += (double)F[k].x * F[k].x + (double)F[k].y * F[k].y;
+      double tot;
+      double e = before0 + block_scan<double>(esum, sh.sd, &tot);
+      int cand = L;
+      for (int k = r0; k < r1 && cand == L; ++k) {
+        e += (double)F[k].x * F[k].x + (double)F[k].y * F[k].y;
+        if (e >= target) cand = k;
+      }
+      if (cand < L) atomicMin(&sh.kstar, cand);
+    }
+    __syncthreads();
+    ks[part] = sh.kstar;
+    __syncthreads();
+  }
+  if (t == 0) {
+    it.kst[0] = ks[0];
+    it.kst[1] = even ? ks[0] : ks[1];
+    if (mode & 4) {
+      kstar_out[u] = ks[0];
+      if (u2 != u) kstar_out[u2] = ks[1];
+    }
+  }
+}
+
+// The masked spectrum merged back and split: for the sub-sequence index j,
+// values n = j + q H (q < S) of the sequence the inverse transforms,
+// a_n = conj(z_n) conj(w_n) (z: the unit's complex sequence from its masked
+// bins, or G1 + i G2 for a pair), then the radix-S split.  Grid (item,
+// range of 1024 j).
+template <int S>
+__global__ __launch_bounds__(256) void kvc_big_merge_kernel(KvcDesc D, KvcSeqGroup G, int Np,
+                                                            float2* __restrict__ base) {
+  constexpr int M = S * KVC_BIG_H, H = KVC_BIG_H, JB = 4;
+  constexpr int PER_WG = 256 * JB, WGS = H / PER_WG;
+  const int L = D.L[G.seq[0]];
+  const bool even = (L & 1) == 0;
+  const int item = (int)blockIdx.x / WGS, jw = (int)blockIdx.x % WGS;
+  const BigItem it = kvc_big_item(base, Np, M, L, even ? item : 2 * item);
+  const float2* cw = base + kvc_big_scratch(Np, M).cw_off;
+  const int kstar = it.kst[0], kstar2 = it.kst[1];
   auto Fm = [&](int kk, float2 v) { return kk <= kstar ? v : make_float2(0.f, 0.f); };
-  for (int n0 = t; n0 < Np; n0 += 8 * SSS_T) {
-    float2 f1[8], f2[8], c[8];
+  auto Fm2 = [&](int kk, float2 v) { return kk <= kstar2 ? v : make_float2(0.f, 0.f); };
+  float2 f1[JB][S], f2[JB][S], c[JB][S];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int n = min(n0 + i * SSS_T, Np - 1);
-      // even: bins n and Np - n; odd: bin n or L - n
+  for (int i = 0; i < JB; ++i) {
+    const int j = jw * PER_WG + i * 256 + (int)threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+      const int n = min(j + q * H, Np - 1);   // (clamped: every load in bounds)
+      // even: bins n and Np - n; odd: bin n or L - n of each unit
       const int i1 = even ? n : (n <= (L - 1) / 2 ? n : L - n);
-      const int i2 = even ? Np - n : i1;
-      f1[i] = Fb[min(i1, kstar)];   // (masked below; the index kept in bounds)
-      f2[i] = Fb[min(i2, kstar)];
-      c[i] = cw[n];
+      f1[i][q] = it.Fb[min(i1, kstar)];   // (masked below; the indices kept in bounds)
+      f2[i][q] = even ? it.Fb[min(Np - n, kstar)] : it.Fb2[min(i1, kstar2)];
+      c[i][q] = cw[n];
     }
+  }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int n = n0 + i * SSS_T;
-      if (n >= Np) continue;
+  for (int i = 0; i < JB; ++i) {
+    const int j = jw * PER_WG + i * 256 + (int)threadIdx.x;
+    float2 a[S];
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+      const int n = j + q * H;
       float2 z;
       if (even) {
-        const float2 Fk = Fm(n, f1[i]), Fr = Fm(Np - n, f2[i]);
+        const float2 Fk = Fm(n, f1[i][q]), Fr = Fm(Np - n, f2[i][q]);
         const float2 A = make_float2(0.5f * (Fk.x + Fr.x), 0.5f * (Fk.y - Fr.y));
         const float2 Dd = make_float2(0.5f * (Fk.x - Fr.x), 0.5f * (Fk.y + Fr.y));
         const float2 B = cmul(cispi(2.0f * (float)n / (float)L), Dd);
         z = make_float2(A.x - B.y, A.y + B.x);
       } else {
-        z = n <= (L - 1) / 2 ? Fm(n, f1[i]) : conjf2(Fm(L - n, f1[i]));
+        // G1 + i G2, each unit's spectrum extended by conjugate symmetry
+        const bool lo = n <= (L - 1) / 2;
+        const float2 g1 = lo ? Fm(n, f1[i][q]) : conjf2(Fm(L - n, f1[i][q]));
+        const float2 g2 = lo ? Fm2(n, f2[i][q]) : conjf2(Fm2(L - n, f2[i][q]));
+        z = make_float2(g1.x - g2.y, g1.y + g2.x);
       }
-      X[n] = cmul(conjf2(z), c[i]);
+      a[q] = n < Np ? cmul(conjf2(z), c[i][q]) : make_float2(0.f, 0.f);
     }
-  }
-  __syncthreads();
-  for (int j0 = t; j0 < H; j0 += KB * SSS_T) {
-    float2 a[KB][S];
-#pragma unroll
-    for (int i = 0; i < KB; ++i)
-#pragma unroll
-      for (int q = 0; q < S; ++q) {
-        const int n = j0 + i * SSS_T + q * H;
-        a[i][q] = n < Np ? X[n] : make_float2(0.f, 0.f);
-      }
-#pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      const int j = j0 + i * SSS_T;
-      if (j < H) kvc_big_split<S>(Y, j, M, [&](int n) { return a[i][(n - j) / H]; });
-    }
+    kvc_big_split<S>(it.Y, j, M, [&](int n) { return a[(n - j) / H]; });
   }
 }
 
 // Per unit, after the second convolution: the low-pass row
 // lp = conj(conj(w_m) conj(sum_r ...) / M) / Np, the blend with the raw row,
 // and the selection on it.  mode without bit 0: selection on s_in as given.
+// Odd L: the unit's low-pass row is the real (first unit of the pair) or
+// imaginary (second) part of its pair's inverse.
 template <int S, int VS>
 __global__ __launch_bounds__(SSS_T) void kvc_big_finish_kernel(
     KvcDesc D, int mode, KvcSeqGroup G, int Np, const float* __restrict__ s_in,
@@ -1453,11 +1627,15 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_finish_kernel(
   if (mode & 1) {
     const BigScratch bs = kvc_big_scratch(Np, M);
     const float2* cw = base + bs.cw_off;
-    const float2* Y = base + bs.rows_off + (size_t)blockIdx.x * bs.ustride;
-    float* hs = reinterpret_cast<float*>(base + bs.rows_off + (size_t)blockIdx.x * bs.ustride + M);
+    const int b = (int)blockIdx.x, second = even ? 0 : (b & 1);
+    const float2* Y = base + bs.rows_off + (size_t)(b - second) * bs.ustride;
+    // (the unit's own slot past its M transform values: free here, and never
+    // the pair's transform values, which are in the first unit's slot below M)
+    float* hs = reinterpret_cast<float*>(base + bs.rows_off + (size_t)b * bs.ustride + M);
     float* hrow = (mode & 4) ? s_hat_out + row : nullptr;
     const float invM = 1.0f / (float)M, invNp = 1.0f / (float)Np;
     const float a = D.alpha, oma = 1.0f - D.alpha;
+    const int ex = even ? 0 : kvc_big_exp(base + bs.rows_off + (size_t)b * bs.ustride, Np, M);
     for (int m0 = t; m0 < Np; m0 += KB * SSS_T) {
       float2 e[KB][S], c[KB], sv[KB];
 #pragma unroll
@@ -1489,7 +1667,7 @@ __global__ __launch_bounds__(SSS_T) void kvc_big_finish_kernel(
             hrow[2 * m + 1] = h1;
           }
         } else {
-          const float h = oma * sv[i].x + a * lre;
+          const float h = oma * sv[i].x + a * ldexpf(second ? lim : lre, ex);
           hs[m] = h;
           if (hrow) hrow[m] = h;
         }
@@ -1541,12 +1719,21 @@ static hipError_t launch_big(const KvcDesc& D, const KvcSeqGroup& g, int nwg, in
     hipLaunchKernelGGL(kvc_big_chirp_split_kernel<S>, dim3(KVC_BIG_H / 256), dim3(256), 0, st,
                        Np, base);
     hipLaunchKernelGGL(kvc_big_chirp_fft_kernel<S>, dim3(S), dim3(SSS_T), 0, st, base);
-    hipLaunchKernelGGL((kvc_big_conv_kernel<S, true>), dim3(nwg * S), dim3(SSS_T), 0, st, D, g,
+    const bool paired = (D.L[g.seq[0]] & 1) != 0;
+    const int items = kvc_big_items(nwg, paired);
+    if (paired)
+      hipLaunchKernelGGL(kvc_big_scale_kernel, dim3(nwg), dim3(SSS_T), 0, st, D, g, Np, M,
+                         s_in, base);
+    hipLaunchKernelGGL((kvc_big_conv_kernel<S, true>), dim3(items * S), dim3(SSS_T), 0, st, D, g,
                        Np, s_in, base);
-    hipLaunchKernelGGL(kvc_big_spectrum_kernel<S>, dim3(nwg), dim3(SSS_T), 0, st, D, mode, g, Np,
+    hipLaunchKernelGGL(kvc_big_bins_kernel<S>, dim3(items * KVC_BIG_CH), dim3(256), 0, st, D, g,
+                       Np, base);
+    hipLaunchKernelGGL(kvc_big_kstar_kernel<S>, dim3(items), dim3(SSS_T), 0, st, D, mode, g, Np,
                        base, kstar_out);
-    hipLaunchKernelGGL((kvc_big_conv_kernel<S, false>), dim3(nwg * S), dim3(SSS_T), 0, st, D, g,
-                       Np, s_in, base);
+    hipLaunchKernelGGL(kvc_big_merge_kernel<S>, dim3(items * (KVC_BIG_H / 1024)), dim3(256), 0,
+                       st, D, g, Np, base);
+    hipLaunchKernelGGL((kvc_big_conv_kernel<S, false>), dim3(items * S), dim3(SSS_T), 0, st, D,
+                       g, Np, s_in, base);
   }
   if (D.L[g.seq[0]] > 32768)
     hipLaunchKernelGGL((kvc_big_finish_kernel<S, 32>), dim3(nwg), dim3(SSS_T), 0, st, D, mode, g,
