@@ -82,6 +82,33 @@ def test_smooth_long_lengths(L):
     assert P.rel_err(sh[3 * L:4 * L], rows[3]) <= 1e-5
 
 
+# Odd lengths past 16383 pair the units of a length group in each transform
+# (group units 2p and 2p + 1): an odd unit count leaves the last unit with
+# itself, and sequences of one length pair across their boundary.  Rows of
+# very different sizes side by side, and a constant row beside a large one.
+@pytest.mark.parametrize("n_seq,H,L", [(1, 3, 49999), (2, 3, 20001), (1, 1, 32767)])
+def test_smooth_long_odd_pairing(n_seq, H, L):
+    P.say(f"[smooth] pairs: {n_seq} x {H} units, L={L}")
+    cfg = P.small(n_seq=n_seq, n_layers=1, n_kv_heads=H, lengths=(L,) * n_seq, dtype="bf16",
+                  alpha=0.6, rho=0.7, retention=(0.9,) * n_seq, base_ratio=0.0)
+    D = Dev(synth.problem(cfg))
+    sink, cos, spiky, const = P._sss_rows(L, 4, np.random.default_rng(L + H))
+    pick = {(1, 3): [1e3 * spiky, const, sink],
+            (2, 3): [cos, 1e3 * spiky, const, 1e-2 * sink, const, spiky],
+            (1, 1): [sink]}[(n_seq, H)]
+    rows = [r.astype(np.float32) for r in pick]
+    sh, ks = D.smooth(np.concatenate(rows))
+    with ThreadPoolExecutor(len(rows)) as ex:
+        errs = list(ex.map(lambda h: check_smoothed_row(rows[h], sh[h * L:(h + 1) * L],
+                                                        int(ks[h]), 0.6, 0.7, "bf16"),
+                           range(len(rows))))
+    P.say(f"    k* {ks.tolist()}, s_hat errors {[f'{e[0]:.1e}' for e in errs]}")
+    for h, r in enumerate(rows):
+        if np.all(r == r[0]):
+            assert int(ks[h]) == 0
+            assert P.rel_err(sh[h * L:(h + 1) * L], r) <= 1e-5
+
+
 @pytest.mark.parametrize("dtype,d,gqa", [("bf16", 128, 8), ("bf16", 64, 2), ("f32", 64, 2),
                                          ("f32", 128, 1)])
 def test_scores_any_length(dtype, d, gqa):
