@@ -275,13 +275,18 @@ static kvc_status compress_range(const kvc_problem* prob, const kvc_params* para
   // retention), then one launch per step and sequence over the units of
   // layers [lb, le) (more, smaller launches cost more in launch and queue
   // latency than they save).
-  hipError_t e = kvc_launch_budget(D, head_scores, budgets, seg_offsets, s);
-  if (e != hipSuccess) return hip_status(e);
+  // Over every unit, the statistics pass of the scores takes the budget
+  // step along where it can (the budget pools' workgroups beside its tiles).
   const bool whole = lb == 0 && le == D.n_layers;
+  const bool hosted = whole && kvc_scores_host_budget(D);
+  hipError_t e = hipSuccess;
+  if (!hosted && (e = kvc_launch_budget(D, head_scores, budgets, seg_offsets, s)) != hipSuccess)
+    return hip_status(e);
   if (whole) {
     // one launch per pass over every sequence's tiles
-    if ((e = kvc_launch_scores(D, 0, D.n_units, q_window, k, c.srows, c.partials, c.lse2, s)) !=
-        hipSuccess)
+    const KvcBudgetArgs ba{head_scores, budgets, seg_offsets};
+    if ((e = kvc_launch_scores(D, 0, D.n_units, q_window, k, c.srows, c.partials, c.lse2, s, 3,
+                               hosted ? &ba : nullptr)) != hipSuccess)
       return hip_status(e);
   } else {
     for (int seq = 0; seq < D.n_seq; ++seq) {

@@ -69,9 +69,20 @@ hipError_t kvc_launch_budget(const KvcDesc& D, const float* S, int32_t* budgets,
 // score launches take any range, the smoothing/selection launches a range
 // within one sequence.
 // which: 1 = statistics pass (+ LSE fold), 2 = pooling pass, 3 = both.
+// The budget step's arguments, for a statistics pass that runs the budget
+// pools' workgroups beside its tiles (kvc_scores_host_budget).
+struct KvcBudgetArgs {
+  const float* S;
+  int32_t* budgets;
+  int64_t* offsets;
+};
 hipError_t kvc_launch_scores(const KvcDesc& D, int u0, int u1, const void* q, const void* k,
                              float* s, float2* partials, float* lse2, hipStream_t st,
-                             int which = 3);
+                             int which = 3, const KvcBudgetArgs* budget = nullptr);
+// Whether kvc_launch_scores over every unit can take the budget step along
+// (its statistics kernel then holds the budget's LDS without losing
+// occupancy); otherwise the caller launches kvc_launch_budget.
+bool kvc_scores_host_budget(const KvcDesc& D);
 // Smoothing/selection launch over several sequences of one length: units
 // seq[k] * upseq + lo .. seq[k] * upseq + hi - 1 for k < n (workgroup
 // b -> k = b / (hi - lo), unit lo + b % (hi - lo) of sequence seq[k]).

@@ -28,6 +28,7 @@
 // with margin.
 #include <type_traits>
 
+#include "budget.h"
 #include "kvc_internal.h"
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -714,15 +715,35 @@ __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_scor
 // wrong by overflowing, when a later key's logit exceeds the reference by
 // more than about 127 / c; the workgroup then recomputes the tile with the
 // exact online maximum.
-template <int D, int NBC>
+//
+// BUDGET: the first nbw workgroups (a multiple of 8, so that every tile
+// workgroup keeps its place on the XCDs) compute the budget pools instead
+// (step 3 needs only the head scores), sharing the workgroup's LDS with the
+// key chunks: the budget is then done within this pass instead of before it.
+template <int D, int NBC, bool BUDGET = false>
 __global__ __launch_bounds__(QsWaves<NBC>::NT, QsWaves<NBC>::MINB) void kvc_score_stats_qs_kernel(
     KvcDesc Dsc, int tile0, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    float2* __restrict__ partials) {
+    float2* __restrict__ partials, KvcBudgetArgs B, int nbw) {
   using C = QsCfg<D>;
   constexpr int NT = QsWaves<NBC>::NT, NK = C::NK;
-  __shared__ __attribute__((aligned(16))) char sK[2][C::CHUNK * C::RS];
+  constexpr int KBYTES = 2 * C::CHUNK * C::RS;
+  constexpr int SMEM =
+      BUDGET && (int)sizeof(KvcBudgetSmem) > KBYTES ? (int)sizeof(KvcBudgetSmem) : KBYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  char(*sK)[C::CHUNK * C::RS] = reinterpret_cast<char(*)[C::CHUNK * C::RS]>(smem);
   __shared__ int sRedo;
-  const int tile = tile0 + xcd_local_tile((int)blockIdx.x, (int)gridDim.x);
+  int bid = (int)blockIdx.x, nblk = (int)gridDim.x;
+  if constexpr (BUDGET) {
+    if (bid < nbw) {
+      if (bid < Dsc.n_seq * (Dsc.upseq / Dsc.pool_size))
+        kvc_budget_pool<NT>(Dsc, B.S, B.budgets, B.offsets, bid,
+                            *reinterpret_cast<KvcBudgetSmem*>(smem));
+      return;
+    }
+    bid -= nbw;
+    nblk -= nbw;
+  }
+  const int tile = tile0 + xcd_local_tile(bid, nblk);
   const TileInfo ti = tile_info(Dsc, tile);
   if (ti.tail) return;  // kvc_score_tail_kernel
   const int gw = NBC * 32;
@@ -1062,13 +1083,24 @@ static void launch_pair(const KvcDesc& D, int u0, int u1, const void* q, const v
 // Query-stationary bf16 passes; units [u0, u1) in one sequence.
 template <int Dm, int NBC>
 static void launch_qs(const KvcDesc& D, int u0, int u1, const void* q, const void* k, float* s,
-                      float2* partials, float* lse2, hipStream_t st, int which) {
+                      float2* partials, float* lse2, hipStream_t st, int which,
+                      const KvcBudgetArgs* budget) {
   const int t0 = tile_of_unit(D, u0);
   const int nt = tile_of_unit(D, u1) - t0;
   constexpr int NT = QsWaves<NBC>::NT;
   if (which & 1) {
-    hipLaunchKernelGGL((kvc_score_stats_qs_kernel<Dm, NBC>), dim3(nt), dim3(NT), 0, st, D, t0,
-                       (const uint16_t*)q, (const uint16_t*)k, partials);
+    if constexpr (QsWaves<NBC>::MINB <= 2) {
+      if (budget) {
+        const int nbw = (D.n_seq * (D.upseq / D.pool_size) + 7) & ~7;
+        hipLaunchKernelGGL((kvc_score_stats_qs_kernel<Dm, NBC, true>), dim3(nt + nbw), dim3(NT),
+                           0, st, D, t0, (const uint16_t*)q, (const uint16_t*)k, partials,
+                           *budget, nbw);
+      }
+    }
+    if (!budget || QsWaves<NBC>::MINB > 2)
+      hipLaunchKernelGGL((kvc_score_stats_qs_kernel<Dm, NBC, false>), dim3(nt), dim3(NT), 0, st,
+                         D, t0, (const uint16_t*)q, (const uint16_t*)k, partials,
+                         KvcBudgetArgs{nullptr, nullptr, nullptr}, 0);
     launch_tail<uint16_t, Dm>(D, u0, u1, 1, q, k, lse2, partials, s, st);
     hipLaunchKernelGGL(kvc_score_lse_kernel, dim3(u1 - u0), dim3(KVC_MAX_GW), 0, st, D, u0,
                        kLog2e / sqrtf((float)Dm), (const float2*)partials, lse2);
@@ -1084,24 +1116,38 @@ static void launch_qs(const KvcDesc& D, int u0, int u1, const void* q, const voi
 
 template <int Dm>
 static void launch_bf16(const KvcDesc& D, int u0, int u1, const void* q, const void* k, float* s,
-                        float2* partials, float* lse2, hipStream_t st, int which) {
+                        float2* partials, float* lse2, hipStream_t st, int which,
+                        const KvcBudgetArgs* b) {
   switch (D.gw / 32) {
-    case 1: launch_qs<Dm, 1>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    case 2: launch_qs<Dm, 2>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    case 3: launch_qs<Dm, 3>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    case 4: launch_qs<Dm, 4>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    case 5: launch_qs<Dm, 5>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    case 6: launch_qs<Dm, 6>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    case 7: launch_qs<Dm, 7>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
-    default: launch_qs<Dm, 8>(D, u0, u1, q, k, s, partials, lse2, st, which); break;
+    case 1: launch_qs<Dm, 1>(D, u0, u1, q, k, s, partials, lse2, st, which, b); break;
+    case 2: launch_qs<Dm, 2>(D, u0, u1, q, k, s, partials, lse2, st, which, b); break;
+    case 3: launch_qs<Dm, 3>(D, u0, u1, q, k, s, partials, lse2, st, which, b); break;
+    case 4: launch_qs<Dm, 4>(D, u0, u1, q, k, s, partials, lse2, st, which, b); break;
+    case 5: launch_qs<Dm, 5>(D, u0, u1, q, k, s, partials, lse2, st, which, b); break;
+    case 6: launch_qs<Dm, 6>(D, u0, u1, q, k, s, partials, lse2, st, which, b); break;
+    case 7: launch_qs<Dm, 7>(D, u0, u1, q, k, s, partials, lse2, st, which, b); break;
+    default: launch_qs<Dm, 8>(D, u0, u1, q, k, s, partials, lse2, st, which, b); break;
   }
 }
 
+bool kvc_scores_host_budget(const KvcDesc& D) {
+  // bf16, d = 128, seven or eight 32-query blocks: four waves per workgroup
+  // and two workgroups per CU with or without the budget's LDS (smaller
+  // kernels run more workgroups per CU than that LDS would allow)
+  const int nbc = D.gw / 32 < 8 ? D.gw / 32 : 8;
+  return D.dtype == 0 && D.d == 128 && nbc >= 7;
+}
+
 hipError_t kvc_launch_scores(const KvcDesc& D, int u0, int u1, const void* q, const void* k,
-                             float* s, float2* partials, float* lse2, hipStream_t st, int which) {
+                             float* s, float2* partials, float* lse2, hipStream_t st, int which,
+                             const KvcBudgetArgs* budget) {
   if (u1 <= u0) return hipSuccess;
-  if (D.dtype == 0 && D.d == 128) launch_bf16<128>(D, u0, u1, q, k, s, partials, lse2, st, which);
-  else if (D.dtype == 0 && D.d == 64) launch_bf16<64>(D, u0, u1, q, k, s, partials, lse2, st, which);
+  if (budget && (!kvc_scores_host_budget(D) || u0 != 0 || u1 != D.n_units || !(which & 1)))
+    return hipErrorInvalidValue;
+  if (D.dtype == 0 && D.d == 128)
+    launch_bf16<128>(D, u0, u1, q, k, s, partials, lse2, st, which, budget);
+  else if (D.dtype == 0 && D.d == 64)
+    launch_bf16<64>(D, u0, u1, q, k, s, partials, lse2, st, which, budget);
   else if (D.dtype == 1 && D.d == 128) launch_pair<TF64, 128, 0>(D, u0, u1, q, k, s, partials, lse2, st, which);
   else if (D.dtype == 1 && D.d == 64) launch_pair<TF64, 64, 0>(D, u0, u1, q, k, s, partials, lse2, st, which);
   else return hipErrorInvalidValue;
