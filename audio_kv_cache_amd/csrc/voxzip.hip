@@ -408,7 +408,8 @@ __global__ __launch_bounds__(VZ_SEL_THREADS) void vz_evict_kernel(
 // recent rows the M highest, and the middle row to drop is the one of
 // smallest A, the latest place among equal values (the complement of the
 // N kept).  The freed slot gets A = 0 and the next place, ready for the
-// next token's row.  One 256-thread workgroup per cache.
+// next token's row.  One 1024-thread workgroup per cache, eight slots' loads
+// in flight per thread in each pass.
 // ---------------------------------------------------------------------------
 __device__ inline void vz_min_pair(unsigned long long& k, int& s, unsigned long long k2, int s2) {
   if (k2 < k) {
@@ -417,12 +418,15 @@ __device__ inline void vz_min_pair(unsigned long long& k, int& s, unsigned long 
   }
 }
 
-__global__ __launch_bounds__(VZ_THREADS) void vz_slot_evict_kernel(VzDesc V, float* a,
+#define VZ_EVICT_T 1024
+#define VZ_EVICT_KB 8
+__global__ __launch_bounds__(VZ_EVICT_T) void vz_slot_evict_kernel(VzDesc V, float* a,
                                                                    int32_t* pos,
                                                                    int32_t* free_slot) {
-  __shared__ int s_min[VZ_THREADS / 64], s_max[VZ_THREADS / 64];
-  __shared__ unsigned long long s_key[VZ_THREADS / 64];
-  __shared__ int s_slot[VZ_THREADS / 64];
+  constexpr int NW = VZ_EVICT_T / 64, KB = VZ_EVICT_KB;
+  __shared__ int s_min[NW], s_max[NW];
+  __shared__ unsigned long long s_key[NW];
+  __shared__ int s_slot[NW];
   const int u = blockIdx.x, seq = u / V.upseq;
   const int n = V.len[seq], B = V.budget[seq];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -430,10 +434,15 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_slot_evict_kernel(VzDesc V, flo
   int32_t* pu = pos + (size_t)u * V.cap;
   // lowest and highest place
   int pmin = INT32_MAX, pmax = INT32_MIN;
-  for (int s = tid; s < n; s += VZ_THREADS) {
-    const int p = pu[s];
-    pmin = min(pmin, p);
-    pmax = max(pmax, p);
+  for (int s0 = tid; s0 < n; s0 += KB * VZ_EVICT_T) {
+    int p[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) p[i] = pu[min(s0 + i * VZ_EVICT_T, n - 1)];   // (clamped)
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      pmin = min(pmin, p[i]);
+      pmax = max(pmax, p[i]);
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -447,7 +456,7 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_slot_evict_kernel(VzDesc V, flo
   __syncthreads();
   pmin = s_min[0];
   pmax = s_max[0];
-  for (int w = 1; w < VZ_THREADS / 64; ++w) {
+  for (int w = 1; w < NW; ++w) {
     pmin = min(pmin, s_min[w]);
     pmax = max(pmax, s_max[w]);
   }
@@ -457,13 +466,24 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_slot_evict_kernel(VzDesc V, flo
     const int T = V.n_sink, M = V.recent[seq];
     unsigned long long best = ~0ull;
     int bslot = -1;
-    for (int s = tid; s < n; s += VZ_THREADS) {
-      const int p = pu[s];
-      if (p - pmin < T || p > pmax - M) continue;
-      // smallest A first; among equal A the latest place (largest p)
-      const unsigned long long key =
-          ((unsigned long long)vz_key(au[s]) << 32) | (unsigned long long)(~(uint32_t)p);
-      vz_min_pair(best, bslot, key, s);
+    for (int s0 = tid; s0 < n; s0 += KB * VZ_EVICT_T) {
+      int p[KB];
+      float av[KB];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const int s = min(s0 + i * VZ_EVICT_T, n - 1);   // (clamped; masked below)
+        p[i] = pu[s];
+        av[i] = au[s];
+      }
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const int s = s0 + i * VZ_EVICT_T;
+        if (s >= n || p[i] - pmin < T || p[i] > pmax - M) continue;
+        // smallest A first; among equal A the latest place (largest p)
+        const unsigned long long key =
+            ((unsigned long long)vz_key(av[i]) << 32) | (unsigned long long)(~(uint32_t)p[i]);
+        vz_min_pair(best, bslot, key, s);
+      }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -478,7 +498,7 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_slot_evict_kernel(VzDesc V, flo
     __syncthreads();
     best = s_key[0];
     bslot = s_slot[0];
-    for (int w = 1; w < VZ_THREADS / 64; ++w) vz_min_pair(best, bslot, s_key[w], s_slot[w]);
+    for (int w = 1; w < NW; ++w) vz_min_pair(best, bslot, s_key[w], s_slot[w]);
     out = bslot;
   } else if (n < V.cap) {
     out = n;                                  // the cache still grows: next slot
@@ -785,7 +805,7 @@ extern "C" kvc_status kvc_vz_step_inplace(const kvc_vz_problem* prob,
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e = vz_launch_accumulate(V, q, k, a, a, c, s);
   if (e == hipSuccess) {
-    hipLaunchKernelGGL(vz_slot_evict_kernel, dim3(V.n_units), dim3(VZ_THREADS), 0, s, V, a, pos,
+    hipLaunchKernelGGL(vz_slot_evict_kernel, dim3(V.n_units), dim3(VZ_EVICT_T), 0, s, V, a, pos,
                        free_slot);
     e = hipGetLastError();
   }
