@@ -69,6 +69,28 @@ hipError_t kvc_launch_budget(const KvcDesc& D, const float* S, int32_t* budgets,
 // score launches take any range, the smoothing/selection launches a range
 // within one sequence.
 // which: 1 = statistics pass (+ LSE fold), 2 = pooling pass, 3 = both.
+// Lane x of each 16-lane row rotated by R within the row (DPP row_ror: a
+// VALU operand modifier, no round trip through LDS).
+template <int R>
+__device__ __forceinline__ float kvc_ror16(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF, false));
+}
+// Max and sum over each 16-lane row of the wave, in every lane of the row
+// (the sum's order of additions differs between the row's lanes).
+__device__ __forceinline__ float kvc_row16_max(float x) {
+  x = fmaxf(x, kvc_ror16<1>(x));
+  x = fmaxf(x, kvc_ror16<2>(x));
+  x = fmaxf(x, kvc_ror16<4>(x));
+  return fmaxf(x, kvc_ror16<8>(x));
+}
+__device__ __forceinline__ float kvc_row16_sum(float x) {
+  x += kvc_ror16<1>(x);
+  x += kvc_ror16<2>(x);
+  x += kvc_ror16<4>(x);
+  return x + kvc_ror16<8>(x);
+}
+
 // The budget step's arguments, for a statistics pass that runs the budget
 // pools' workgroups beside its tiles (kvc_scores_host_budget).
 struct KvcBudgetArgs {

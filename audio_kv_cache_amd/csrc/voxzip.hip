@@ -147,6 +147,7 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_logits_bf16_kernel(
   // lane's four rows, then the 16 lanes of its group.
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
+    if (qb == 1 && !two) break;   // (uniform: no second block of heads)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int g = qb * 16 + grp * 4 + i;
@@ -160,14 +161,12 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_logits_bf16_kernel(
           if (g < G) lgu[(size_t)g * V.cap + j] = l2[kg];
         }
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      mx = kvc_row16_max(mx);
       float z = 0.f;
 #pragma unroll
       for (int kg = 0; kg < 4; ++kg)
         if (j0 + kg * 16 + col < n) z += exp2f(l2[kg] - mx);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o);
+      z = kvc_row16_sum(z);
       if (col == 0 && g < G) sst[g][wave] = make_float2(mx, z);
     }
   }

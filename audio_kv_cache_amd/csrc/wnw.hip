@@ -87,26 +87,6 @@ __device__ __forceinline__ void wnw_merge(float& m, float& z, float m2, float z2
 // Steps 1-2: anchor attention, block masses, chunk scores
 // ---------------------------------------------------------------------------
 
-// Lane x of each 16-lane row rotated by R within the row (DPP row_ror: a
-// VALU operand modifier, no round trip through LDS).
-template <int R>
-__device__ __forceinline__ float wnw_ror16(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF, false));
-}
-// Max and sum over each 16-lane row, in every lane of the row.
-__device__ __forceinline__ float wnw_row16_max(float x) {
-  x = fmaxf(x, wnw_ror16<1>(x));
-  x = fmaxf(x, wnw_ror16<2>(x));
-  x = fmaxf(x, wnw_ror16<4>(x));
-  return fmaxf(x, wnw_ror16<8>(x));
-}
-__device__ __forceinline__ float wnw_row16_sum(float x) {
-  x += wnw_ror16<1>(x);
-  x += wnw_ror16<2>(x);
-  x += wnw_ror16<4>(x);
-  return x + wnw_ror16<8>(x);
-}
 typedef __bf16 wnw_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float wnw_f4 __attribute__((ext_vector_type(4)));
 
@@ -197,12 +177,12 @@ __global__ __launch_bounds__(WNW_TILE) void wnw_logits_kernel(WnwDesc W, const u
           if (g < G) X.logits[((size_t)sa * G + g) * W.max_len + j] = l2[kg];
         }
       }
-      mx = wnw_row16_max(mx);
+      mx = kvc_row16_max(mx);
       float z = 0.f;
 #pragma unroll
       for (int kg = 0; kg < 4; ++kg)
         if (j0 + kg * 16 + col < n) z += __builtin_amdgcn_exp2f(l2[kg] - mx);
-      z = wnw_row16_sum(z);
+      z = kvc_row16_sum(z);
       if (col == 0 && g < G) sred[g][wave] = make_float2(mx, z);
     }
   }
