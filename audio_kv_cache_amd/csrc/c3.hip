@@ -970,6 +970,23 @@ __global__ __launch_bounds__(C3_BIG) void c3_span_part_kernel(C3Desc P, int par,
 // ---------------------------------------------------------------------------
 // Build: children ids and records, next depth's work lists
 // ---------------------------------------------------------------------------
+// Copy of N 16-byte pieces with every load issued before the first store.
+// Written as a plain copy, the compiler turns it into a memory copy whose
+// expansion waits on each load before its store, N latencies in a row; the
+// source is read once, so non-temporal loads suit it and keep the loads
+// apart from the stores.
+typedef unsigned int c3_u32x4 __attribute__((ext_vector_type(4)));
+template <int N>
+__device__ __forceinline__ void c3_copy_row(const uint4* src, uint4* dst) {
+  const c3_u32x4* s = reinterpret_cast<const c3_u32x4*>(src);
+  c3_u32x4* d = reinterpret_cast<c3_u32x4*>(dst);
+  c3_u32x4 r[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) r[i] = __builtin_nontemporal_load(s + i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) d[i] = r[i];
+}
+
 template <int D>
 __global__ __launch_bounds__(C3_BIG) void c3_ids_kernel(C3Desc P, int dep, C3Index X, C3Work W) {
   __shared__ int scan[C3_BIG / 64];
@@ -1005,9 +1022,8 @@ __global__ __launch_bounds__(C3_BIG) void c3_ids_kernel(C3Desc P, int dep, C3Ind
         X.left[y] = -1;
         X.parent[y] = x;
         X.depth[y] = dep + 1;
-        const uint4* src = reinterpret_cast<const uint4*>(W.cres + (ub + cs[side]) * D);
-        uint4* dst = reinterpret_cast<uint4*>(X.cent + y * D);
-        for (int i = 0; i < D / 8; ++i) dst[i] = src[i];
+        c3_copy_row<D / 8>(reinterpret_cast<const uint4*>(W.cres + (ub + cs[side]) * D),
+                           reinterpret_cast<uint4*>(X.cent + y * D));
         if (cm[side] > C3_LEAF) {
           ++cand;
           if (cm[side] <= C3_MLOC) {
