@@ -454,12 +454,18 @@ __device__ inline void c3_acc_rows(const unsigned char* sK, int r0, uint64_t lo,
 }
 
 // Hyperplane between two fp64 means for the 8 columns of piece gl (columns
-// 8 gl .. 8 gl + 7); the lanes of one node are LPN consecutive lanes, all
-// active together.  b is the fp32 sum of the rounded products in column
-// order: the node's lanes in turn, each lane's 8 columns in order.
+// 8 gl .. 8 gl + 7); the lanes of one node are LPN consecutive lanes of one
+// wave, all active together.  The normal w goes to the node's LDS row (row
+// [8 gl .. 8 gl + 7]) and b, the fp32 sum of the rounded products in column
+// order, is returned on every lane of the node: the products pass through
+// the same row (two stores per lane, then every lane reads the whole row,
+// the reads of one node broadcast) and each lane adds them one at a time.
+// Only the node's lanes touch the row here, and one wave's LDS operations
+// are done in order, so no barrier is needed.
 template <int LPN>
-__device__ inline float c3_bisect8(const double (&mu0)[8], const double (&mu1)[8], float (&w)[8]) {
-  float p[8];
+__device__ inline float c3_bisect8(const double (&mu0)[8], const double (&mu1)[8], float* row,
+                                   int gl) {
+  float w[8], p[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float wf = c3_round16((float)(mu1[i] - mu0[i]));
@@ -468,12 +474,20 @@ __device__ inline float c3_bisect8(const double (&mu0)[8], const double (&mu1)[8
     w[i] = wf;
     p[i] = wf * mf;
   }
-  const int first = (int)(threadIdx.x & 63) & ~(LPN - 1);
+  float4* r4 = reinterpret_cast<float4*>(row);
+  r4[2 * gl] = make_float4(p[0], p[1], p[2], p[3]);
+  r4[2 * gl + 1] = make_float4(p[4], p[5], p[6], p[7]);
   float s = 0.0f;
 #pragma unroll
-  for (int j = 0; j < LPN; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s = s + __shfl(p[i], first + j);
+  for (int c4 = 0; c4 < 2 * LPN; ++c4) {
+    const float4 v = r4[c4];
+    s = s + v.x;
+    s = s + v.y;
+    s = s + v.z;
+    s = s + v.w;
+  }
+  r4[2 * gl] = make_float4(w[0], w[1], w[2], w[3]);
+  r4[2 * gl + 1] = make_float4(w[4], w[5], w[6], w[7]);
   return s;
 }
 
@@ -584,7 +598,6 @@ __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Ind
     combine(pt, tot[rd]);
     if (valid && part == 0) {
       double m0[8], m1[8];
-      float w[8];
       const uint4 v0 = *reinterpret_cast<const uint4*>(sK + (r0 + sA0[j]) * RB + gl * 16);
       const uint4 v1 = *reinterpret_cast<const uint4*>(sK + (r0 + sA1[j]) * RB + gl * 16);
       const uint32_t h0[4] = {v0.x, v0.y, v0.z, v0.w}, h1[4] = {v1.x, v1.y, v1.z, v1.w};
@@ -595,9 +608,7 @@ __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Ind
         m1[2 * i] = (double)c3_bf(h1[i] & 0xFFFFu);
         m1[2 * i + 1] = (double)c3_bf(h1[i] >> 16);
       }
-      const float b = c3_bisect8<LPN>(m0, m1, w);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sW[j][gl * 8 + i] = w[i];
+      const float b = c3_bisect8<LPN>(m0, m1, &sW[j][0], gl);
       if (gl == 0) sB[j] = b;
     }
   }
@@ -663,10 +674,7 @@ __global__ __launch_bounds__(C3_T) void c3_local_kernel(C3Desc P, int dep, C3Ind
       if (same && gl == 0) sConv[j] = 1;
       if (!same && gl == 0) sLeft[it & 1] = 1;
       if (it + 1 < C3_ITERS && !same) {
-        float w[8];
-        const float b = c3_bisect8<LPN>(mu0, mu1, w);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sW[j][gl * 8 + i] = w[i];
+        const float b = c3_bisect8<LPN>(mu0, mu1, &sW[j][0], gl);
         if (gl == 0) sB[j] = b;
       } else {
         const int n0 = m - n1;
