@@ -1107,68 +1107,148 @@ __global__ __launch_bounds__(C3_BIG) void c3_frontier_kernel(C3Desc P, C3Index X
 // ---------------------------------------------------------------------------
 // Step: scores
 // ---------------------------------------------------------------------------
-// A thread per frontier entry: its centroid row is streamed from global
-// memory in 16-byte pieces (8 columns) and folded into the norm and the dot
-// products with every query head of the group (HPT >= G of them).
+// sigma = max over the group's query heads of cos(q_g, c) for every frontier
+// centroid c, on v_mfma_f32_16x16x32_bf16: the G query heads are the A rows
+// (16 per block, zero past G) and 16 frontier centroids the B columns; at
+// k-step ks lane l holds dims ks*32 + (l/16)*8 .. +7 of both operands, so a
+// centroid row is read as 64-byte runs, and all of a wave's loads (64
+// entries) are in flight before its first MFMA.  Output lane l holds entry
+// l % 16 for heads (l/16)*4 .. +3 of the block.  The centroid's squared norm
+// is summed by the four lanes holding its dims, then across them.
+typedef __bf16 c3_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float c3_f4 __attribute__((ext_vector_type(4)));
+
 template <int D, int HPT>
 __global__ __launch_bounds__(C3_T) void c3_score_kernel(C3Desc P, C3Index X, C3State S,
                                                         const uint16_t* __restrict__ q,
                                                         float* __restrict__ sigma) {
-  __shared__ __align__(16) float sQ[HPT][D];
+  constexpr int KS = D / 32, NQB = (HPT + 15) / 16, WPB = C3_T / 64;
   __shared__ float sQn[HPT];
   const int u = blockIdx.x / C3_SW, part = blockIdx.x - u * C3_SW;
   if (c3_n(P, u) <= c3_b(P, u)) return;
   const int G = P.gqa, A = S.count[u];
   const size_t ub = (size_t)u * P.cap, nb = (size_t)u * P.ncap;
-  for (int i = threadIdx.x; i < HPT * D; i += C3_T)
-    sQ[i / D][i % D] = i < G * D ? c3_bf(q[(size_t)u * G * D + i]) : 0.0f;
-  __syncthreads();
-  if (threadIdx.x < HPT) {
-    float s = 0.0f;
-    for (int c = 0; c < D; ++c) s = fmaf(sQ[threadIdx.x][c], sQ[threadIdx.x][c], s);
-    sQn[threadIdx.x] = sqrtf(s);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const uint16_t* qs = q + (size_t)u * G * D;
+  // Issue order: the wave's first 64 frontier indices, the query rows (the
+  // A operand, and for threads below HPT the row of their head's norm), then
+  // the first 64 centroid rows, so that only the index -> row dependence is
+  // serial (entries past A reload the last one and are not written).
+  uint4 kraw[4][KS];
+  int xs[4];
+  auto load_ids = [&](int b) {
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) xs[kg] = S.fr[ub + min(b + kg * 16 + col, A - 1)];
+  };
+  auto load_rows = [&]() {
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      const uint16_t* row = X.cent + (nb + xs[kg]) * D + grp * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kraw[kg][ks] = *reinterpret_cast<const uint4*>(row + ks * 32);
+    }
+  };
+  const int base0 = (part * WPB + wave) * 64;
+  int base = base0;
+  const bool any = base0 < A;
+  if (any) load_ids(base0);
+  uint4 qraw[NQB][KS];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[qb][ks] = *reinterpret_cast<const uint4*>(qs + (size_t)min(qb * 16 + col, G - 1) * D + ks * 32 + grp * 8);
+  const bool nthread = (int)threadIdx.x < HPT;
+  uint4 qr[D / 8];
+  if (nthread) {
+    const uint4* qrow = reinterpret_cast<const uint4*>(qs + (size_t)min((int)threadIdx.x, G - 1) * D);
+#pragma unroll
+    for (int p = 0; p < D / 8; ++p) qr[p] = qrow[p];
   }
-  __syncthreads();
-  for (int i = part * C3_T + threadIdx.x; i < A; i += C3_SW * C3_T) {
-    const int x = S.fr[ub + i];
-    const uint4* row = reinterpret_cast<const uint4*>(X.cent + (nb + x) * D);
-    float dot[HPT];
+  if (any) load_rows();
+  // query norms: a thread per head, the squares summed in dimension order
+  if (nthread) {
+    float s = 0.0f;
 #pragma unroll
-    for (int g = 0; g < HPT; ++g) dot[g] = 0.0f;
-    float cn = 0.0f;
-#pragma unroll 4
     for (int p = 0; p < D / 8; ++p) {
-      const uint4 v = row[p];
-      const float c[8] = {c3_bf(v.x & 0xFFFFu), c3_bf(v.x >> 16), c3_bf(v.y & 0xFFFFu),
-                          c3_bf(v.y >> 16),     c3_bf(v.z & 0xFFFFu), c3_bf(v.z >> 16),
-                          c3_bf(v.w & 0xFFFFu), c3_bf(v.w >> 16)};
+      const uint32_t w[4] = {qr[p].x, qr[p].y, qr[p].z, qr[p].w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) cn = fmaf(c[j], c[j], cn);
-#pragma unroll
-      for (int g = 0; g < HPT; ++g) {
-        const float4 q0 = *reinterpret_cast<const float4*>(&sQ[g][8 * p]);
-        const float4 q1 = *reinterpret_cast<const float4*>(&sQ[g][8 * p + 4]);
-        float d = dot[g];
-        d = fmaf(q0.x, c[0], d);
-        d = fmaf(q0.y, c[1], d);
-        d = fmaf(q0.z, c[2], d);
-        d = fmaf(q0.w, c[3], d);
-        d = fmaf(q1.x, c[4], d);
-        d = fmaf(q1.y, c[5], d);
-        d = fmaf(q1.z, c[6], d);
-        d = fmaf(q1.w, c[7], d);
-        dot[g] = d;
+      for (int j = 0; j < 4; ++j) {
+        const float lo = c3_bf(w[j] & 0xFFFFu), hi = c3_bf(w[j] >> 16);
+        s = fmaf(lo, lo, s);
+        s = fmaf(hi, hi, s);
       }
     }
-    cn = sqrtf(cn);
-    float best = -INFINITY;
+    sQn[threadIdx.x] = (int)threadIdx.x < G ? sqrtf(s) : 0.0f;
+  }
+  // A operand; heads past G: the last head's bits masked to zero
+  c3_bf16x8 qa[NQB][KS];
 #pragma unroll
-    for (int g = 0; g < HPT; ++g) {
-      if (g >= G) break;
-      const float den = sQn[g] * cn;
-      best = fmaxf(best, den > 0.0f ? dot[g] / den : 0.0f);
+  for (int qb = 0; qb < NQB; ++qb) {
+    const uint32_t keep = qb * 16 + col < G ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 raw = qraw[qb][ks];
+      raw.x &= keep;
+      raw.y &= keep;
+      raw.z &= keep;
+      raw.w &= keep;
+      __builtin_memcpy(&qa[qb][ks], &raw, 16);
     }
-    sigma[ub + i] = best;
+  }
+  __syncthreads();
+  float qn[NQB][4];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = qb * 16 + grp * 4 + i;
+      qn[qb][i] = h < G ? sQn[h] : 0.0f;
+    }
+  for (; base < A; base += C3_SW * C3_T) {
+    if (base != base0) {
+      load_ids(base);
+      load_rows();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      c3_bf16x8 kb[KS];
+      float cn = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        __builtin_memcpy(&kb[ks], &kraw[kg][ks], 16);
+        const uint32_t w[4] = {kraw[kg][ks].x, kraw[kg][ks].y, kraw[kg][ks].z, kraw[kg][ks].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = c3_bf(w[j] & 0xFFFFu), hi = c3_bf(w[j] >> 16);
+          cn = fmaf(lo, lo, cn);
+          cn = fmaf(hi, hi, cn);
+        }
+      }
+      cn += __shfl_xor(cn, 16);
+      cn += __shfl_xor(cn, 32);
+      cn = sqrtf(cn);
+      float best = -INFINITY;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        if (qb * 16 >= G) break;   // (uniform: no heads in this block)
+        c3_f4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[qb][ks], kb[ks], t, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (qb * 16 + grp * 4 + i < G) {
+            const float den = qn[qb][i] * cn;
+            best = fmaxf(best, den > 0.0f ? t[i] / den : 0.0f);
+          }
+      }
+      best = fmaxf(best, __shfl_xor(best, 16));
+      best = fmaxf(best, __shfl_xor(best, 32));
+      const int i = base + kg * 16 + col;
+      if (grp == 0 && i < A) sigma[ub + i] = best;
+    }
   }
 }
 
