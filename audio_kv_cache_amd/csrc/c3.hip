@@ -1606,8 +1606,8 @@ __global__ __launch_bounds__(C3_T) void c3_gather_kernel(C3Desc P, int bpc,
     if (t >= nl) continue;
     int s = idx[(size_t)u * P.kept_cap + t];
     if ((unsigned)s >= (unsigned)n) s = 0;
-    kv[p] = *reinterpret_cast<const uint4*>(k + u * P.ks[0] + (int64_t)s * P.ks[1] + pc * 8);
-    vv[p] = *reinterpret_cast<const uint4*>(v + u * P.vs[0] + (int64_t)s * P.vs[1] + pc * 8);
+    kv[p] = kvc_nt_load16(k + u * P.ks[0] + (int64_t)s * P.ks[1] + pc * 8);
+    vv[p] = kvc_nt_load16(v + u * P.vs[0] + (int64_t)s * P.vs[1] + pc * 8);
   }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {

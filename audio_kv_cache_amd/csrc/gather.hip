@@ -5,11 +5,13 @@
 // digest writes the same compaction as K_{t+1} = Concat(K[:T], K[I_hist],
 // K[-M:])).  Pure data movement: each lane moves 16-byte pieces, a 256-thread
 // workgroup moves a contiguous run of output rows, loads are issued for K and
-// V together so several 16-byte requests per lane are in flight, and the
-// output is written with non-temporal stores (it is not read again here).
+// V together so several 16-byte requests per lane are in flight, and both
+// sides bypass the caches' retention (non-temporal loads: each kept row is
+// read once; non-temporal stores: the output is not read again here).
 #include "kvc_internal.h"
 
 #define GATHER_THREADS 256
+#define GATHER_LDS_UNITS 1024
 
 template <int ROWB>
 __global__ __launch_bounds__(GATHER_THREADS) void kvc_gather_kernel(
@@ -22,7 +24,17 @@ __global__ __launch_bounds__(GATHER_THREADS) void kvc_gather_kernel(
   constexpr int ROWS_PER_BLOCK = ROWS_PER_PASS * PASSES;
   // Rows of units [u0, u1) are offsets[u0] .. offsets[u1]-1; the grid
   // strides over them.
-  const int64_t rbeg = offsets[u0], rend = offsets[u1];
+  // With at most GATHER_LDS_UNITS units the offsets are staged in LDS once
+  // (one round of loads), so finding a row's unit costs no global latency.
+  __shared__ int64_t soff[GATHER_LDS_UNITS + 1];
+  const int nu = u1 - u0;
+  const bool staged = nu <= GATHER_LDS_UNITS;
+  if (staged) {
+    for (int i = threadIdx.x; i <= nu; i += GATHER_THREADS) soff[i] = offsets[u0 + i];
+    __syncthreads();
+  }
+  auto off = [&](int uu) { return staged ? soff[uu - u0] : offsets[uu]; };
+  const int64_t rbeg = off(u0), rend = off(u1);
   const int esz = D.dtype == 0 ? 2 : 4;
   const int chunk = threadIdx.x % CH;
   for (int64_t r0 = rbeg + (int64_t)blockIdx.x * ROWS_PER_BLOCK; r0 < rend;
@@ -32,7 +44,7 @@ __global__ __launch_bounds__(GATHER_THREADS) void kvc_gather_kernel(
     int lo = u0, hi = u1 - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (offsets[mid] <= t0) lo = mid; else hi = mid - 1;
+      if (off(mid) <= t0) lo = mid; else hi = mid - 1;
     }
     int u = lo;
     uint4 kv[PASSES], vv[PASSES];
@@ -42,7 +54,7 @@ __global__ __launch_bounds__(GATHER_THREADS) void kvc_gather_kernel(
       const int64_t t = r0 + p * ROWS_PER_PASS + threadIdx.x / CH;
       rows[p] = t;
       if (t >= rend) continue;
-      while (u + 1 < u1 && offsets[u + 1] <= t) ++u;
+      while (u + 1 < u1 && off(u + 1) <= t) ++u;
       const int seq = u / D.upseq;
       const int within = u - seq * D.upseq;
       const int l = within / D.n_heads, h = within - l * D.n_heads;
@@ -50,8 +62,8 @@ __global__ __launch_bounds__(GATHER_THREADS) void kvc_gather_kernel(
       if ((unsigned)pos >= (unsigned)D.L[seq]) pos = 0;  // never read outside the row
       const char* ks = k + (kvc_kv_offset(D.ks, D, seq, l, h) + (int64_t)pos * D.ks[2]) * esz;
       const char* vs = v + (kvc_kv_offset(D.vs, D, seq, l, h) + (int64_t)pos * D.vs[2]) * esz;
-      kv[p] = *reinterpret_cast<const uint4*>(ks + chunk * 16);
-      vv[p] = *reinterpret_cast<const uint4*>(vs + chunk * 16);
+      kv[p] = kvc_nt_load16(ks + chunk * 16);
+      vv[p] = kvc_nt_load16(vs + chunk * 16);
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {

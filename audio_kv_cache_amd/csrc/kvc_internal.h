@@ -91,6 +91,14 @@ __device__ __forceinline__ float kvc_row16_sum(float x) {
   return x + kvc_ror16<8>(x);
 }
 
+// A 16-byte load that does not keep its line in the caches (each row a
+// gather reads is read once).
+typedef unsigned int kvc_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 kvc_nt_load16(const void* p) {
+  const kvc_u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const kvc_u32x4*>(p));
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
 // The budget step's arguments, for a statistics pass that runs the budget
 // pools' workgroups beside its tiles (kvc_scores_host_budget).
 struct KvcBudgetArgs {

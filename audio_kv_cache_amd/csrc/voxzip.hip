@@ -545,8 +545,8 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_gather_kernel(
     int s = ix[t];
     if ((unsigned)s >= (unsigned)n) s = 0;
     src[p] = s;
-    kv[p] = *reinterpret_cast<const uint4*>(k + (u * V.ks[0] + s * V.ks[1]) * esz + ch * 16);
-    vv[p] = *reinterpret_cast<const uint4*>(v + (u * V.vs[0] + s * V.vs[1]) * esz + ch * 16);
+    kv[p] = kvc_nt_load16(k + (u * V.ks[0] + s * V.ks[1]) * esz + ch * 16);
+    vv[p] = kvc_nt_load16(v + (u * V.vs[0] + s * V.vs[1]) * esz + ch * 16);
   }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {

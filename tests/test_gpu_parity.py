@@ -144,11 +144,18 @@ def test_budget_bitexact_hand_cases_and_random():
 # ---------------------------------------------------------------------------
 # Step 5: gather (bit-exact)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
-def test_gather_bitexact(dtype, d):
-    say(f"[gather] {dtype} d={d}")
-    cfg = small(dtype=dtype, head_dim=d, n_seq=3, lengths=(256, 1024, 128), retention=(0.5, 0.3, 0.9),
-                base_ratio=0.0)
+@pytest.mark.parametrize("dtype,d,many", [("bf16", 128, False), ("bf16", 64, False), ("f32", 64, False),
+                                           ("f32", 128, False), ("bf16", 128, True)])
+def test_gather_bitexact(dtype, d, many):
+    """many: 1152 units, more than the gather stages in LDS (it then looks up
+    each row's unit in global memory)."""
+    say(f"[gather] {dtype} d={d} many={many}")
+    if many:
+        cfg = small(dtype=dtype, head_dim=d, n_seq=3, n_layers=24, n_kv_heads=16, lengths=(64, 96, 128),
+                    retention=(0.5, 0.7, 0.4), base_ratio=0.0)
+    else:
+        cfg = small(dtype=dtype, head_dim=d, n_seq=3, lengths=(256, 1024, 128), retention=(0.5, 0.3, 0.9),
+                    base_ratio=0.0)
     D = Dev(synth.problem(cfg))
     b, off = D.budget()
     rng = np.random.default_rng(1)
