@@ -836,7 +836,7 @@ __global__ __launch_bounds__(C3_T) void c3_span_iter_kernel(C3Desc P, int par, i
     for (int p = 0; p < PER; ++p) {
       const int i = tid + p * C3_T, r = i / PPR, pc = i - r * PPR;
       if (r < rows)
-        buf[slot][p] = *reinterpret_cast<const uint4*>(
+        buf[slot][p] = kvc_nt_load16(
             k + u * P.ks[0] + (int64_t)sPerm[blk * C3_CH + r] * P.ks[1] + pc * 8);
     }
     oldf[slot] = (it > 0 && tid < rows) ? W.flags[ub + q0 + blk * C3_CH + tid] : 0;
