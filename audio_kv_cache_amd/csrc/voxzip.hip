@@ -82,12 +82,20 @@ typedef float vz_f4 __attribute__((ext_vector_type(4)));
 // ks*32 + (l/16)*8 .. +7 of both operands (so a row is read as 64-byte
 // runs); output lane l holds row l % 16 for heads (l/16)*4 .. +3 of the
 // block.  Rows past n read row n - 1 and are masked.
-template <int D>
+// STAGED (the in-place step, where nothing reads the rows again): every load
+// instruction reads whole rows (PPR lanes per row, full 128-byte lines) with
+// non-temporal loads into LDS, and each lane then reads its fragments in the
+// MFMA layout from rows padded by 16 bytes.  Otherwise (the compacting step,
+// whose gather re-reads nearly every row right after and finds part of them
+// still in the caches) each lane loads its fragments straight from memory.
+template <int D, bool STAGED>
 __global__ __launch_bounds__(VZ_THREADS) void vz_logits_bf16_kernel(
     VzDesc V, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     float* __restrict__ lg, float2* __restrict__ part) {
   constexpr int KS = D / 32;
   constexpr int NWV = VZ_THREADS / 64;
+  constexpr int PPR = D / 8, RPI = 64 / PPR, NLD = 64 / RPI;   // pieces per row, rows per load, loads
+  constexpr int RS = 2 * D + 16;                                 // padded LDS row stride, bytes
   __shared__ float2 sst[VZ_MAX_G][NWV];
   const int u = blockIdx.x, pi = blockIdx.y;
   const int seq = u / V.upseq;
@@ -119,15 +127,36 @@ __global__ __launch_bounds__(VZ_THREADS) void vz_logits_bf16_kernel(
   const uint16_t* kc = k + (int64_t)u * V.ks[0];
   float* lgu = lg + (size_t)u * G * V.cap;
   const int j0 = row0 + wave * 64;
+  // Rows past n reload row n - 1 (masked below).
   uint4 kraw[4][KS];
+  if constexpr (STAGED) {
+    __shared__ __attribute__((aligned(16))) char sKr[NWV][64 * RS];
+    const int pc = lane % PPR;
+    uint4 kl[NLD];
 #pragma unroll
-  for (int kg = 0; kg < 4; ++kg) {
-    const int j = min(j0 + kg * 16 + col, n - 1);
-    const uint16_t* kr = kc + (int64_t)j * V.ks[1] + grp * 8;
+    for (int i = 0; i < NLD; ++i) {
+      const int j = min(j0 + i * RPI + lane / PPR, n - 1);
+      kl[i] = kvc_nt_load16(kc + (int64_t)j * V.ks[1] + pc * 8);
+    }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kraw[kg][ks] = *reinterpret_cast<const uint4*>(kr + ks * 32);
+    for (int i = 0; i < NLD; ++i)
+      *reinterpret_cast<uint4*>(sKr[wave] + (i * RPI + lane / PPR) * RS + pc * 16) = kl[i];
+    __syncthreads();
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kraw[kg][ks] = *reinterpret_cast<const uint4*>(sKr[wave] + (kg * 16 + col) * RS + (ks * 32 + grp * 8) * 2);
+  } else {
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      const int j = min(j0 + kg * 16 + col, n - 1);
+      const uint16_t* kr = kc + (int64_t)j * V.ks[1] + grp * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kraw[kg][ks] = *reinterpret_cast<const uint4*>(kr + ks * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
   vz_f4 acc[2][4];
 #pragma unroll
   for (int kg = 0; kg < 4; ++kg) {
@@ -661,10 +690,15 @@ static hipError_t vz_launch_accumulate(const VzDesc& V, const void* q, const voi
   if (V.dtype == 0) {
     const uint16_t* qq = (const uint16_t*)q;
     const uint16_t* kk = (const uint16_t*)k;
-    if (V.d == 128)
-      hipLaunchKernelGGL((vz_logits_bf16_kernel<128>), pgrid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
+    const bool inplace = a_prev == a_t;
+    if (V.d == 128 && inplace)
+      hipLaunchKernelGGL((vz_logits_bf16_kernel<128, true>), pgrid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
+    else if (V.d == 128)
+      hipLaunchKernelGGL((vz_logits_bf16_kernel<128, false>), pgrid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
+    else if (inplace)
+      hipLaunchKernelGGL((vz_logits_bf16_kernel<64, true>), pgrid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
     else
-      hipLaunchKernelGGL((vz_logits_bf16_kernel<64>), pgrid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
+      hipLaunchKernelGGL((vz_logits_bf16_kernel<64, false>), pgrid, dim3(VZ_THREADS), 0, st, V, qq, kk, c.lg, c.part);
   } else {
     const float* qq = (const float*)q;
     const float* kk = (const float*)k;
