@@ -242,7 +242,7 @@ __device__ inline void c3_stage(const C3Desc& P, int u, const uint16_t* __restri
     const int i = threadIdx.x + p * C3_T;
     const int r = i / PPR, pc = i - r * PPR;
     if (r < rows && (valid == nullptr || valid[r] >= 0))
-      buf[p] = *reinterpret_cast<const uint4*>(k + u * P.ks[0] + (int64_t)src[r] * P.ks[1] + pc * 8);
+      buf[p] = kvc_nt_load16(k + u * P.ks[0] + (int64_t)src[r] * P.ks[1] + pc * 8);
   }
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(C3_T) void c3_root_sum_kernel(C3Desc P, C3Work W,
   for (int p = 0; p < PER; ++p) {
     const int r = rg + p * RG;
     if (r < rows)
-      buf[p] = *reinterpret_cast<const uint4*>(k + u * P.ks[0] + (int64_t)(base + r) * P.ks[1] + pc * 8);
+      buf[p] = kvc_nt_load16(k + u * P.ks[0] + (int64_t)(base + r) * P.ks[1] + pc * 8);
   }
   double acc[8];
 #pragma unroll
