@@ -109,7 +109,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(cfg, hdr, prob_units, budgets, max_units=8):
+def cpu_baseline(cfg, hdr, prob_units, budgets, max_units=16):
     """The fp64 oracle, as it stands, on a bounded sample of units: the
     first max_units units of sequence 0 (layer 0's KV heads, then layer 1's)
     on a thread pool of min(max_units, usable cores) threads, and the first
