@@ -248,12 +248,16 @@ def bench_decode(args):
         free = torch.empty(prob.n_units, dtype=torch.int32, device="cuda")
         in_ms = timed(lambda: api.kvc_vz_step_inplace(spec, prm, q, k, a_in, pos_in, free, ws,
                                                       stream))
+        in_scrub_ms = scrubbed_ms(lambda i: api.kvc_vz_step_inplace(spec, prm, q, k, a_in, pos_in,
+                                                                    free, ws, stream),
+                                  args.steps, stream)
         ib = 0
         for n in cfg.lens:
             ib += cfg.n_layers * cfg.n_kv_heads * (n * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
                                                    + cfg.gqa * cfg.head_dim * 2 + 12 * n + 4)
         i_gbs = ib / (in_ms * 1e-3) / 1e9
         inplace = {"us_per_step": round(in_ms * 1e3, 2),
+                   "us_per_step_scrubbed": round(in_scrub_ms * 1e3, 2),
                    "traffic": summed_traffic("voxzip.hip", ("vz_logits_bf16_kernel", "vz_accum_kernel",
                                                             "vz_slot_evict_kernel"), cfg.name),
                    "cache_rows_per_s": sum(int(n) for n in cfg.lens) * cfg.n_layers
@@ -261,14 +265,18 @@ def bench_decode(args):
                    "algorithmic_bytes_per_step": ib,
                    "path_hbm": {"achieved": round(i_gbs, 1), "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": round(i_gbs / HBM_PEAK_GBS, 4)}}
-        log(f"[bench] decode in place {in_ms * 1e3:.1f} us/step, path {i_gbs:.0f} GB/s")
+        log(f"[bench] decode in place {in_ms * 1e3:.1f} us/step, path {i_gbs:.0f} GB/s; "
+            f"{in_scrub_ms * 1e3:.1f} us after a cache scrub")
+    step_scrub_ms = scrubbed_ms(lambda i: api.kvc_vz_step(spec, prm, q, k, v, a_prev, ko, vo, ao,
+                                                          idx, ws, stream), args.steps, stream)
     ab = decode_bytes(cfg)
     units = prob.n_units
     rows = sum(int(n) for n in cfg.lens) * cfg.n_layers * cfg.n_kv_heads
     gbs = ab["total"] / (step_ms * 1e-3) / 1e9
     g_gbs = ab["gather"] / (stages["gather"] * 1e-3) / 1e9
     a_gbs = ab["logits"] / (stages["accumulate"] * 1e-3) / 1e9
-    log(f"[bench] decode {step_ms * 1e3:.1f} us/step, path {gbs:.0f} GB/s; stages " +
+    log(f"[bench] decode {step_ms * 1e3:.1f} us/step ({step_scrub_ms * 1e3:.1f} us after a cache "
+        f"scrub), path {gbs:.0f} GB/s; stages " +
         ", ".join(f"{n2} {t * 1e3:.1f} us" for n2, t in stages.items()))
     out = {
         "workload": f"{cfg.name}: {units} caches ({cfg.n_seq} seq x {cfg.n_layers} layers x "
@@ -276,6 +284,7 @@ def bench_decode(args):
                     f"{list(cfg.budgets)}, GQA {cfg.gqa}, head_dim {cfg.head_dim}, {cfg.dtype}, "
                     f"gamma {cfg.gamma}, T {cfg.n_sink}, recent {cfg.recent_frac}",
         "us_per_step": round(step_ms * 1e3, 2),
+        "us_per_step_scrubbed": round(step_scrub_ms * 1e3, 2),
         "cache_rows_per_s": rows / (step_ms * 1e-3),
         "algorithmic_bytes_per_step": ab["total"],
         "path_hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -402,6 +411,7 @@ def bench_c3(args):
     step_ms = timed(step, args.steps)
     # the same steps replayed from one captured graph
     graph_step_ms = graph_ms(lambda: [step(i, None) for i in range(args.steps)], args.steps)
+    scrub_step_ms = scrubbed_ms(step, args.steps, stream)
     si = o["state"][cur[0]]
     so = o["state"][1 - cur[0]]
     stages = {
@@ -417,7 +427,8 @@ def bench_c3(args):
     ab = c3_bytes(cfg, A_total, kept_total)
     gbs = {n2: ab[n3] / (stages[n2] * 1e-3) / 1e9 for n2, n3 in
            (("score", "score"), ("gather", "gather"))}
-    log(f"[bench] c3 step {step_ms * 1e3:.1f} us ({graph_step_ms * 1e3:.1f} us from a graph); stages " +
+    log(f"[bench] c3 step {step_ms * 1e3:.1f} us ({graph_step_ms * 1e3:.1f} us from a graph, "
+        f"{scrub_step_ms * 1e3:.1f} us after a cache scrub); stages " +
         ", ".join(f"{n2} {t * 1e3:.1f} us" for n2, t in stages.items()))
 
     def hbm(kernel, g, src):
@@ -439,6 +450,7 @@ def bench_c3(args):
         "nodes": int(nn.sum()), "frontier_entries": A_total,
         "us_per_step": round(step_ms * 1e3, 2),
         "us_per_step_graph": round(graph_step_ms * 1e3, 2),
+        "us_per_step_scrubbed": round(scrub_step_ms * 1e3, 2),
         "steps_per_s": 1e3 / step_ms,
         "algorithmic_bytes_per_step": ab["total"],
         "stage_us": {n2: round(t * 1e3, 2) for n2, t in stages.items()},
@@ -491,6 +503,27 @@ def graph_ms(issue, n):
     ev1.record(stream)
     torch.cuda.synchronize()
     return ev0.elapsed_time(ev1) / n
+
+
+_SCRUB = []
+
+
+def scrubbed_ms(fn, n, stream):
+    """Mean event time of n calls fn(i), each after a 512 MiB device-to-device
+    copy (1 GiB of traffic) that evicts the 256 MB memory-side cache, as the
+    other work of a serving step between two decode steps would."""
+    import torch
+    if not _SCRUB:
+        _SCRUB.extend(torch.empty(512 << 20, dtype=torch.uint8, device="cuda") for _ in range(2))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for i in range(n):
+        _SCRUB[1].copy_(_SCRUB[0])
+        evs[i][0].record(stream)
+        fn(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in evs) / n
 
 
 def bench_wnw(args):
@@ -576,6 +609,11 @@ def bench_wnw(args):
         step(t)
     graph_step_ms = graph_ms(lambda: [step(t, None) for t in range(args.warmup, n_steps)],
                              args.steps)
+    # Pass 4: the same timed steps from the same state, each after a cache scrub.
+    reset()
+    for t in range(args.warmup):
+        step(t)
+    scrub_step_ms = scrubbed_ms(lambda i: step(args.warmup + i), args.steps, stream)
 
     def timed(fn, n):
         torch.cuda.synchronize()
@@ -621,7 +659,8 @@ def bench_wnw(args):
     recall_gbs = cold_bytes / (recall_ms * 1e-3) / 1e9
     anchor_bytes = sum(int(n) for n in cfg.lens) * int(lay.n_anchor) * d * 2
     score_gbs = anchor_bytes / (stages["chunk_scores"] * 1e-3) / 1e9
-    log(f"[bench] wnw step {step_ms * 1e3:.1f} us ({graph_step_ms * 1e3:.1f} us from a graph), "
+    log(f"[bench] wnw step {step_ms * 1e3:.1f} us ({graph_step_ms * 1e3:.1f} us from a graph, "
+        f"{scrub_step_ms * 1e3:.1f} us after a cache scrub), "
         f"{bytes_per_step / 1e6:.3f} MB recalled per "
         f"step; chunk scores {stages['chunk_scores'] * 1e3:.1f} us, update "
         f"{stages['update'] * 1e3:.1f} us (stages from a graph); cold step {cold_ms * 1e3:.1f} us recalling "
@@ -634,6 +673,7 @@ def bench_wnw(args):
                     f"after {prm.release_after}",
         "us_per_step": round(step_ms * 1e3, 2),
         "us_per_step_graph": round(graph_step_ms * 1e3, 2),
+        "us_per_step_scrubbed": round(scrub_step_ms * 1e3, 2),
         "steps_per_s": 1e3 / step_ms,
         "recalled_bytes_per_step": bytes_per_step,
         "recalled_blocks": [b for b, _ in rec_blocks[args.warmup:]],
