@@ -29,6 +29,8 @@ import hashlib
 import json
 import os
 import pathlib
+import re
+import subprocess
 import sys
 import time
 
@@ -487,6 +489,44 @@ def bench_c3(args):
 PCIE_PEAK_GBS = 64.0        # PCIe 5.0 x16, one direction (the MI355X host link)
 
 
+def smi_sample():
+    """Socket power (W) and per-XCD shader clocks (MHz) as amd-smi reads them now,
+    or None where the tool is missing or prints neither."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
+                           timeout=30)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    power = re.search(r"SOCKET_POWER:\s*([\d.]+)\s*W", r.stdout)
+    clocks = [int(c) for c in re.findall(r"GFX_\d+:\s*CLK:\s*(\d+)\s*MHz", r.stdout)]
+    if power is None and not clocks:
+        return None
+    return {"socket_w": float(power.group(1)) if power else None, "gfx_mhz": clocks}
+
+
+def power_sample(calls, ms_each, seconds, sync):
+    """Keep each call looping on the GPU for about `seconds` and read socket power
+    and shader clocks halfway through: which stages run at the power cap and
+    at what clock.  Diagnostic only; nothing here is timed."""
+    res = {}
+    for name, fn in calls.items():
+        n = max(1, int(seconds * 1e3 / max(ms_each[name], 1e-3)))
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        time.sleep(max(0.0, seconds / 2 - (time.perf_counter() - t0)))
+        res[name] = smi_sample()
+        sync()
+        if res[name] is None:
+            log("[bench] power: amd-smi gave no reading")
+            return res
+        c = res[name]["gfx_mhz"]
+        log(f"[bench] power {name}: socket {res[name]['socket_w']} W, shader clocks "
+            f"{min(c) if c else '-'}-{max(c) if c else '-'} MHz over {len(c)} XCDs")
+        time.sleep(0.5)
+    return res
+
+
 def graph_ms(issue, n):
     """Capture issue() (n steps launched on the current stream) into one HIP
     graph, replay it once, and return the event time per step."""
@@ -735,6 +775,10 @@ def main():
     ap.add_argument("--wnw-config", default="wnw_voxtral3b")
     ap.add_argument("--wnw-only", action="store_true",
                     help="measure only the WnW leg and print its object")
+    ap.add_argument("--power-sample", type=float, default=0.0, metavar="SECONDS",
+                    help="after the stage timings, loop the two score passes, the gather "
+                         "and the whole step for SECONDS each and log amd-smi's socket "
+                         "power and shader clocks")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -879,6 +923,11 @@ def main():
             torch.cuda.synchronize()
             stages[name] = ev0.elapsed_time(ev1) / args.steps
         log("[bench] stage ms: " + ", ".join(f"{n} {t:.3f}" for n, t in stages.items()))
+        if args.power_sample > 0:
+            pc = {n: calls[n] for n in ("score_stats", "score_pool", "gather")}
+            pc["step"] = step
+            ms_each = dict(stages, step=ms)
+            power_sample(pc, ms_each, args.power_sample, torch.cuda.synchronize)
 
     # Rooflines.  The dominant kernel is the pooling pass of the scores; its
     # tighter bound is HBM (K must be streamed) unless the MFMA work takes

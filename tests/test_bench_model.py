@@ -67,3 +67,35 @@ def test_decode_bytes_closed_form():
     assert m["logits"] == units * (n * d * e + G * d * e + 4 * (n - 1))
     # gather: kept K and V rows read and written, A and positions out
     assert m["gather"] == units * (4 * B * d * e + 8 * B)
+
+
+_SMI_TEXT = """GPU: 0
+    POWER:
+        SOCKET_POWER: 1399 W
+        THROTTLE_STATUS: N/A
+    CLOCK:
+        GFX_0:
+            CLK: 1723 MHz
+            MIN_CLK: 500 MHz
+        GFX_1:
+            CLK: 1630 MHz
+            MIN_CLK: 500 MHz
+        MEM_0:
+            CLK: 2000 MHz
+"""
+
+
+def test_smi_sample_parses_power_and_xcd_clocks(monkeypatch):
+    """The power leg's reader takes the socket power and one clock per GFX
+    domain, not the memory clock or the limits."""
+    class R:
+        stdout, stderr, returncode = _SMI_TEXT, "", 0
+    monkeypatch.setattr(bench.subprocess, "run", lambda *a, **k: R())
+    assert bench.smi_sample() == {"socket_w": 1399.0, "gfx_mhz": [1723, 1630]}
+
+
+def test_smi_sample_missing_tool(monkeypatch):
+    def boom(*a, **k):
+        raise FileNotFoundError("amd-smi")
+    monkeypatch.setattr(bench.subprocess, "run", boom)
+    assert bench.smi_sample() is None
