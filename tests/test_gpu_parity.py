@@ -445,6 +445,29 @@ def test_compress_full_retention_identity():
     assert torch.equal(o["k_out"].view(4, 512, -1), D.k.reshape(4, 512, -1))
 
 
+@pytest.mark.parametrize("case,kw", [
+    # shortest length, no local window (every kept row comes from the top-k)
+    ("L64_w0", dict(lengths=(64,), window=0, retention=(0.5,))),
+    # mean budget equal to the window with no base share: the pool is empty
+    # and every unit keeps exactly its last 32 positions
+    ("budget_is_window", dict(lengths=(64,), window=32, retention=(0.5,), base_ratio=0.0)),
+    # two odd lengths, one query head per KV head, no window; some heads'
+    # budgets reach L (every position kept)
+    ("odd_w0_g1", dict(n_seq=2, lengths=(65, 97), window=0, retention=(0.3, 0.7), head_dim=128,
+                       gqa=1)),
+    # a one-position window, retention 0.9 beside 0.05 (budgets of 3 to 5 rows)
+    ("w1_extremes", dict(n_seq=2, lengths=(64, 127), window=1, retention=(0.9, 0.05),
+                         base_ratio=0.0)),
+])
+def test_compress_edge_shapes(case, kw):
+    say(f"[e2e] edge {case}")
+    cfg = small(name="edge", n_layers=3, n_kv_heads=2, **kw)
+    D = Dev(synth.problem(cfg))
+    o = _check_e2e(D, D.units())
+    if case == "budget_is_window":
+        assert np.array_equal(o["idx"].cpu().numpy(), np.tile(np.arange(32, 64), 6))
+
+
 def test_compress_deterministic():
     say("[e2e] determinism")
     D = dev("qwen7b")
